@@ -1,0 +1,392 @@
+"""Pins for the CPU oracle: values the pages print, closed forms derived from
+their inputs, invariants the mathematics fixes, and brute force on tiny inputs.
+
+Each test names what would break if the oracle held a plausible mistake (a
+dropped term, a wrong sign, index or operand order).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import awq_oracle as O
+import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# page 4's worked example ("Weight-Only Quantization: GPTQ and AWQ", 4. Tiny example)
+# ---------------------------------------------------------------------------
+class TestWorkedExample:
+    g = load("worked_example.json")
+
+    def arrays(self):
+        w = np.array([self.g["w"]], dtype=F32)
+        x = np.array(self.g["x"], dtype=F32)
+        s = np.array(self.g["scale"], dtype=F32)
+        return w, x, s
+
+    def test_exact_output(self):
+        w, x, _ = self.arrays()
+        assert round(float(w[0].astype(np.float64) @ x.astype(np.float64)), 3) == self.g["printed"]["exact"]
+
+    def test_naive_rtn_matches_print(self):
+        w, x, _ = self.arrays()
+        q, step, _ = O.group_quantize(w, None, 4)
+        assert q[0].tolist() == self.g["derived_from_page_inputs"]["naive_codes"]
+        wh = O.fake_quant(w, None, 4)[0]
+        assert [round(float(v), 3) for v in wh] == self.g["printed"]["naive_dequant"]
+        assert round(float(wh.astype(np.float64) @ x.astype(np.float64)), 3) == self.g["printed"]["naive_out"]
+
+    def test_awq_scaled_matches_print(self):
+        w, x, s = self.arrays()
+        q, step, _ = O.group_quantize(w, s, 4)
+        assert q[0].tolist() == self.g["derived_from_page_inputs"]["awq_codes"]
+        wh = O.fake_quant(w, s, 4)[0]
+        assert [round(float(v), 3) + 0.0 for v in wh] == self.g["printed"]["awq_dequant"]
+        assert round(float(wh.astype(np.float64) @ x.astype(np.float64)), 3) == self.g["printed"]["awq_out"]
+
+    def test_weight_error_closed_forms(self):
+        w, x, s = self.arrays()
+        d = self.g["derived_from_page_inputs"]
+        naive = O.weight_error(w, np.ones(4, F32), x, 4)
+        awq = O.weight_error(w, s, x, 4)
+        assert naive == pytest.approx(d["weight_err_naive"][0] / d["weight_err_naive"][1], rel=1e-6)
+        assert awq == pytest.approx(d["weight_err_awq"][0] / d["weight_err_awq"][1], rel=1e-5)
+
+    def test_output_error_closed_forms(self):
+        w, x, s = self.arrays()
+        d = self.g["derived_from_page_inputs"]
+        X = x[None, :].astype(np.float32)
+        naive = O.output_error(w, np.ones(4, F32), X, 4)
+        awq = O.output_error(w, s, X, 4)
+        assert naive == pytest.approx(d["output_err_naive"][0] / d["output_err_naive"][1], rel=1e-6)
+        assert awq == pytest.approx(d["output_err_awq"][0] / d["output_err_awq"][1], rel=1e-4)
+
+    def test_embedded_in_search(self):
+        """x_mean = [16,1,1,1] makes alpha = 0.5 give s = [2, .5, .5, .5] = [4,1,1,1]/2.
+
+        A power-of-two factor on s leaves codes and w_hat unchanged, so the page's
+        AWQ codes appear as candidate 10 and the page's naive codes as candidate 0.
+        Weight-mode errors (x weighted by [16,1,1,1]): 2314/4900 and 66/4900.
+        """
+        w, _, _ = self.arrays()
+        xm = np.array([16, 1, 1, 1], dtype=F32)
+        S = O.candidate_scales(xm, 20)
+        assert S[10].tolist() == [2.0, 0.5, 0.5, 0.5]
+        assert O.group_quantize(w, S[10], 4)[0][0].tolist() == self.g["derived_from_page_inputs"]["awq_codes"]
+        assert O.group_quantize(w, S[0], 4)[0][0].tolist() == self.g["derived_from_page_inputs"]["naive_codes"]
+        errs, kb, sb = O.search_scales([w], xm, 4, 20)
+        assert errs[0] == pytest.approx(2314 / 4900, rel=1e-6)
+        assert errs[10] == pytest.approx(66 / 4900, rel=1e-5)
+        assert errs[kb] <= errs[0]
+
+
+# ---------------------------------------------------------------------------
+# candidates ([cassindra] the scale search as code, non-duo branch)
+# ---------------------------------------------------------------------------
+class TestCandidates:
+    def test_alpha_zero_is_ones(self):
+        xm = np.array([0.0, 1e-9, 3.0, 250.0], dtype=F32)
+        S = O.candidate_scales(xm, 20)
+        assert np.array_equal(S[0], np.ones(4, F32))
+
+    def test_closed_form_two_level(self):
+        # x = [16, 1, ...]: t = [16^a, 1, ...], norm = 4^a -> s = [4^a, 4^-a, ...]
+        xm = np.array([16, 1, 1, 1, 1, 1, 1, 1], dtype=F32)
+        for k, a in enumerate(O.grid_alphas(20)):
+            s = O.candidate_scales(xm, 20)[k]
+            assert s[0] == pytest.approx(4.0 ** a, rel=1e-7)
+            assert np.allclose(s[1:], 4.0 ** (-a), rtol=1e-7)
+
+    def test_grid_is_k_over_n(self):
+        assert O.grid_alphas(20)[0] == 0.0 and O.grid_alphas(20)[19] == 0.95
+        assert O.grid_alphas(4) == [0.0, 0.25, 0.5, 0.75]
+
+    def test_normalised_max_times_min_is_one(self):
+        xm = WL.make_magnitudes(5, 512)
+        S = O.candidate_scales(xm, 20)
+        for k in range(20):
+            assert float(S[k].max()) * float(S[k].min()) == pytest.approx(1.0, rel=1e-6)
+
+    def test_clamp_before_normalisation(self):
+        # a zero channel: 0^a = 0 -> clamped to 1e-4 (not 0), for a > 0
+        xm = np.array([0.0, 1.0, 4.0, 4.0], dtype=F32)
+        s = O.candidate_scale(xm, 0.5)
+        t = np.array([1e-4, 1.0, 2.0, 2.0])
+        assert np.allclose(s, (t / math.sqrt(2.0 * 1e-4)).astype(F32), rtol=1e-7)
+
+    def test_scale_invariance_of_s(self):
+        # s depends on x only up to a positive factor (the normalisation cancels c^a)
+        xm = WL.make_magnitudes(9, 256) + 1.0
+        S1 = O.candidate_scales(xm, 20)
+        S2 = O.candidate_scales((xm * F32(8.0)).astype(F32), 20)
+        assert np.allclose(S1, S2, rtol=2e-7, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# quantizer ([konic] Group-wise symmetric INT4)
+# ---------------------------------------------------------------------------
+def nearest_code_exact(v: float, step: float) -> int:
+    """argmin over the 15 codes of |v - q step| in exact rational arithmetic, ties to even."""
+    fv, fs = Fraction(v), Fraction(step)
+    best = None
+    for q in range(-7, 8):
+        d = abs(fv - q * fs)
+        if best is None or d < best[0] or (d == best[0] and q % 2 == 0):
+            best = (d, q)
+    return best[1]
+
+
+class TestQuantizer:
+    def test_codes_are_nearest_grid_point(self):
+        g = np.random.default_rng(1)
+        W = (g.standard_normal((16, 64)) * 0.02).astype(np.float16)
+        s = (np.exp(g.standard_normal(64) * 0.7)).astype(F32)
+        q, step, v = O.group_quantize(W, s, 16)
+        n_mismatch = 0
+        for o in range(16):
+            for i in range(64):
+                st = float(step[o, i // 16])
+                e = nearest_code_exact(float(v[o, i]), st)
+                if e != int(q[o, i]):
+                    # only where the exact quotient sits within an fp32 ulp of a half-integer
+                    exact = Fraction(float(v[o, i])) / Fraction(st)
+                    frac = exact - math.floor(exact)
+                    assert abs(float(frac) - 0.5) < 1e-6
+                    n_mismatch += 1
+        assert n_mismatch <= 2
+
+    def test_code_range_and_zero_group(self):
+        W = np.zeros((8, 32), dtype=np.float16)
+        W[1, 5] = 0.5
+        q, step, _ = O.group_quantize(W, None, 16)
+        assert step[0, 0] == 0 and step[1, 1] == 0
+        assert np.all(q[0] == 0)
+        assert q[1, 5] == 7 and np.abs(q).max() <= 7
+        assert np.all(O.fake_quant(W, None, 16)[0] == 0)
+
+    def test_per_element_error_bound(self):
+        # |v - q step| <= step/2 (up to rounding) unclipped ([repro] Q5: the rounding
+        # error stays the same in the scaled domain; in W's domain it falls by 1/s)
+        g = np.random.default_rng(2)
+        W = (g.standard_normal((64, 256)) * 0.02).astype(np.float16)
+        s = (np.exp(g.standard_normal(256))).astype(F32)
+        q, step, v = O.group_quantize(W, s, 128)
+        st = np.repeat(step, 128, axis=1).astype(np.float64)
+        err = np.abs(v.astype(np.float64) - q * st)
+        assert np.all(err <= st * 0.5 * (1 + 1e-6))
+        wh = O.fake_quant(W, s, 128).astype(np.float64)
+        err_w = np.abs(W.astype(np.float64) - wh)
+        assert np.all(err_w <= st * 0.5 / s[None, :] * (1 + 1e-5) + 1e-12)
+
+    def test_power_of_two_scaling_of_w(self):
+        g = np.random.default_rng(3)
+        W = (g.standard_normal((16, 256)) * 0.02).astype(F32)
+        s = (np.exp(g.standard_normal(256))).astype(F32)
+        xm = np.abs(g.standard_normal(256)).astype(F32)
+        q1, st1, _ = O.group_quantize(W, s, 64)
+        q2, st2, _ = O.group_quantize((W * 8).astype(F32), s, 64)
+        assert np.array_equal(q1, q2) and np.array_equal(st2, st1 * 8)
+        e1 = O.weight_error(W, s, xm, 64)
+        e2 = O.weight_error((W * 8).astype(F32), s, xm, 64)
+        assert e2 == pytest.approx(64 * e1, rel=1e-12)
+
+    def test_unit_scale_equals_rtn(self):
+        W = WL.make_weight(4, 32, 256)
+        a = O.group_quantize(W, None, 128)
+        b = O.group_quantize(W, np.ones(256, F32), 128)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+    def test_clip_one_equals_unclipped_and_clip_clamps(self):
+        W = WL.make_weight(5, 16, 128)
+        a = O.group_quantize(W, None, 64)
+        b = O.group_quantize(W, None, 64, clip=np.ones(16, F32))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        c = O.group_quantize(W, None, 64, clip=np.full(16, 0.5, F32))
+        assert np.abs(c[0]).max() == 7 and (np.abs(c[0]) == 7).sum() > (np.abs(a[0]) == 7).sum()
+
+
+# ---------------------------------------------------------------------------
+# errors and search
+# ---------------------------------------------------------------------------
+class TestErrorsAndSearch:
+    def test_act_stats_closed_form(self):
+        X = np.array([[1.0, -2.0, 0.0], [-3.0, 2.0, 0.5]], dtype=np.float16)
+        assert O.act_stats(X).tolist() == [2.0, 2.0, 0.25]
+        Xb = WL.f32_to_bf16_bits(np.array([[-1.5, 4.0], [0.5, -4.0], [1.0, 1.0]], dtype=F32))
+        assert O.act_stats(Xb).tolist() == pytest.approx([1.0, 3.0])
+
+    def test_output_error_direct_difference(self):
+        # X W_hat^T - X W^T evaluated as two separate products equals the difference form
+        g = np.random.default_rng(6)
+        W = (g.standard_normal((24, 64)) * 0.02).astype(np.float16)
+        X = WL.make_activations(7, 9, 64, "bf16")
+        s = O.candidate_scale(O.act_stats(X), 0.45)
+        Xd = O.decode_activations(X)
+        wh = O.fake_quant(W, s, 32).astype(np.float64)
+        Y = Xd @ wh.T - Xd @ W.astype(np.float64).T
+        ref = float((Y * Y).mean())
+        assert O.output_error(W, s, X, 32) == pytest.approx(ref, rel=1e-9)
+
+    def test_diagonal_x_links_the_two_modes(self):
+        # X = diag(m): x_mean = m / T and E_out = (T / d_out) E_w; same argmin
+        d_in, d_out = 64, 16
+        m = WL.make_magnitudes(11, d_in)
+        X = np.diag(m).astype(np.float32)
+        W = WL.make_weight(12, d_out, d_in)
+        xm = O.act_stats(X)
+        assert np.allclose(xm, m / d_in, rtol=1e-7)
+        ew, kw, _ = O.search_scales([W], xm, 32, 20, "weight")
+        eo, ko, _ = O.search_scales([W], xm, 32, 20, "output", X=X)
+        assert np.allclose(eo, ew * d_in / d_out, rtol=1e-5)
+        assert kw == ko
+
+    def test_activation_scaling_invariance(self):
+        W = WL.make_weight(13, 32, 256)
+        xm = WL.make_magnitudes(14, 256)
+        e1, k1, s1 = O.search_scales([W], xm, 128, 20)
+        e2, k2, s2 = O.search_scales([W], (xm * F32(4)).astype(F32), 128, 20)
+        assert k1 == k2
+        assert np.allclose(e2, 16 * e1, rtol=1e-5)
+
+    def test_never_worse_than_rtn(self):
+        for seed in range(3):
+            W = WL.make_weight(20 + seed, 64, 256)
+            X = WL.make_activations(30 + seed, 32, 256)
+            xm = O.act_stats(X)
+            errs, kb, _ = O.search_scales([W], xm, 128, 20)
+            assert errs[kb] <= errs[0]
+            assert errs[kb] == errs.min()
+            erro, ko, _ = O.search_scales([W], xm, 128, 20, "output", X=X)
+            assert erro[ko] <= erro[0]
+
+    def test_outliers_pull_alpha_up(self):
+        # with outlier channels the chosen alpha is > 0 and the error falls well below RTN
+        W = WL.make_weight(2001, 256, 512)
+        X = WL.make_activations(2002, 64, 512, "f16")
+        errs, kb, _ = O.search_scales([W], O.act_stats(X), 128, 20)
+        assert kb > 0 and errs[kb] < 0.8 * errs[0]
+
+    def test_first_argmin_keeps_first_tie(self):
+        assert O.first_argmin([3.0, 1.0, 1.0, 2.0]) == 1
+        assert O.first_argmin([1.0, 1.0]) == 0
+
+    def test_group_rows_concatenate(self):
+        W1 = WL.make_weight(40, 16, 128)
+        W2 = WL.make_weight(41, 8, 128)
+        xm = WL.make_magnitudes(42, 128)
+        e_parts, _, _ = O.search_scales([W1, W2], xm, 64, 20)
+        e_cat, _, _ = O.search_scales([np.concatenate([W1, W2])], xm, 64, 20)
+        S = O.candidate_scales(xm, 20)
+        e_sum = [O.weight_error(W1, S[k], xm, 64) + O.weight_error(W2, S[k], xm, 64) for k in range(20)]
+        assert np.array_equal(e_parts, e_cat) and np.allclose(e_parts, e_sum, rtol=1e-12)
+
+    def test_brute_force_tiny_search(self):
+        """8x16 W, G=8, T=5: every candidate's error from exact nearest-code
+        quantization (rational arithmetic on the fp32 operands) matches."""
+        W = WL.make_weight(50, 8, 16)
+        X = WL.make_activations(51, 5, 16, "bf16")
+        xm = O.act_stats(X)
+        errs, kb, _ = O.search_scales([W], xm, 8, 20)
+        S = O.candidate_scales(xm, 20)
+        for k in range(20):
+            tot = 0.0
+            for o in range(8):
+                for g0 in range(0, 16, 8):
+                    v = [float(F32(float(W[o, i])) * S[k][i]) for i in range(g0, g0 + 8)]
+                    a = max(abs(t) for t in v)
+                    st = float(F32(a) / F32(7))
+                    for j, i in enumerate(range(g0, g0 + 8)):
+                        q = nearest_code_exact(v[j], st)
+                        wh = float(F32(F32(q) * F32(st)) / S[k][i])
+                        tot += ((float(W[o, i]) - wh) * float(xm[i])) ** 2
+            assert errs[k] == pytest.approx(tot, rel=1e-12)
+        assert kb == int(np.argmin(errs))
+
+
+# ---------------------------------------------------------------------------
+# clip search ([cassindra] pipeline step 5)
+# ---------------------------------------------------------------------------
+class TestClip:
+    def test_ratios(self):
+        r = O.clip_ratios(20, 0.5)
+        assert r[0] == 1.0 and r[-1] == 0.5 and len(r) == 20
+        assert np.all(np.diff(r) < 0)
+
+    def test_hand_example_picks_point_seven(self):
+        # row [1, .1, .1, .1], channel 0 unused by X: the best step is 0.1, i.e. ratio 0.7
+        W = np.tile(np.array([[1.0, 0.1, 0.1, 0.1]], dtype=F32), (8, 1))
+        X = np.diag([0.0, 1.0, 1.0, 1.0]).astype(F32)
+        E, c = O.clip_search(W, np.ones(4, F32), X, 4, n_clip=6, clip_lo=0.5)
+        assert np.all(c == F32(0.7))
+        assert np.all(E[:, 3] < 1e-12) and np.all(E[:, 0] > 5e-3)
+
+    def test_ratio_one_is_unclipped(self):
+        W = WL.make_weight(60, 16, 64)
+        X = WL.make_activations(61, 7, 64)
+        s = O.candidate_scale(O.act_stats(X), 0.3)
+        E, _ = O.clip_search(W, s, X, 32, n_clip=4)
+        assert np.array_equal(E[:, 0], O.output_error_rows(W, s, X, 32))
+
+
+# ---------------------------------------------------------------------------
+# packing ([konic] AutoAWQ / HF-AWQ GEMM on-disk format; exporter step 4)
+# ---------------------------------------------------------------------------
+class TestPack:
+    g = load("pack_order.json")
+
+    def test_order_golden_word(self):
+        u = np.tile((np.arange(16) % 8).astype(np.uint8)[:, None], (1, 4))
+        words = O.pack_codes(u)
+        assert words.shape == (4, 2)
+        assert np.all(words == np.uint32(int(self.g["word_when_code_equals_row_mod_8"], 16)))
+
+    def test_orientation_golden(self):
+        u = np.tile(np.minimum(np.arange(16), 14).astype(np.uint8)[None, :], (8, 1))
+        words = O.pack_codes(u)          # [d_in=16, d_out/8=1]
+        for i in range(16):
+            assert int(words[i, 0]) == int(f"{min(i, 14):x}" * 8, 16)
+
+    def test_pack_shapes_zero_point_and_roundtrip(self):
+        W = WL.make_weight(70, 64, 256)
+        s = (np.exp(np.random.default_rng(0).standard_normal(256) * 0.3)).astype(F32)
+        qw, sc, qz, q, step = O.quantize_pack(W, s, 128)
+        assert qw.shape == (256, 8) and sc.shape == (2, 64) and qz.shape == (2, 8)
+        assert sc.dtype == np.float16
+        assert np.all(qz == np.uint32(int(self.g["qzeros_word"], 16)))
+        u = O.unpack_codes(qw, 64)
+        assert u.max() <= 14 and np.array_equal(u.astype(np.int16) - 7, q.astype(np.int16))
+        # (u - zero) * scale reproduces q * fp16(step) exactly
+        deq = O.unpack_dequant(qw, sc, qz, 64, 128)
+        ref = (q.astype(F32) * np.repeat(step.astype(np.float16).astype(F32), 128, axis=1)).astype(F32)
+        assert np.array_equal(deq, ref)
+        assert np.array_equal(O.unpack_dequant(qw, sc, None, 64, 128), deq)
+
+    def test_fp16_rne_golden(self):
+        for hx, bits in load("fp16_rne.json")["cases"]:
+            v = np.array([float.fromhex(hx)], dtype=F32)
+            with np.errstate(over="ignore"):
+                got = int(O.f32_to_f16(v).view(np.uint16)[0])
+            assert got == int(bits, 16), hx
+
+    def test_size_accounting(self):
+        # Qwen3-8B linears: 13.9 GB in fp16 -> 3.5 GB of INT4 codes (4.0x);
+        # 4 + 16/128 + 4/128 = 4.16 bits per weight with scales and zeros
+        n = WL.qwen3_8b_linear_params()
+        assert n == 36 * 192_937_984 == 6_945_767_424
+        assert round(2 * n / 1e9, 1) == 13.9
+        assert round(n / 2 / 1e9, 1) == 3.5
+        assert round((2 * n) / (n / 2), 1) == 4.0
+        bits = 4 + 16 / 128 + 4 / 128
+        assert round(bits, 2) == 4.16
