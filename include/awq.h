@@ -1,0 +1,202 @@
+/*
+ * awq.h -- C ABI of libawq, the MI355X (gfx950) library for the per-layer hot
+ * path of activation-aware weight quantization (AWQ):
+ *
+ *   calibration activations X --(awq_act_stats)--> per-input-channel mean |x|
+ *   --(awq_candidate_scales / awq_search_scales)--> grid search over alpha in
+ *   s = x_mean^alpha (normalised), each candidate scored by group-wise
+ *   symmetric INT4 fake quantization of W*s --(awq_quantize_pack)--> AutoAWQ
+ *   GEMM layout (qweight / scales / qzeros) --(awq_unpack_dequant)--> check.
+ *
+ * Sources (page title, section):
+ *   [konic]     "From-Scratch AWQ INT4 Quantization on Qwen3-8B": "AWQ scaling",
+ *               "Group-wise symmetric INT4", "AutoAWQ / HF-AWQ GEMM on-disk
+ *               format", exporter step 4.
+ *   [cassindra] "AWQ architecture, in depth": "The pipeline end to end",
+ *               "The scale search as code", "Quantization, storage and packing".
+ *   [lm]        "Weight-Only Quantization: GPTQ and AWQ": "5. Technical
+ *               explanation / AWQ", "6-9. Under the hood: the packed format".
+ *
+ * Conventions (all entry points):
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every
+ *     buffer; the library never allocates or frees device memory and keeps no
+ *     pointer after a call returns.  Scratch memory is caller-supplied (`ws`),
+ *     sized by the matching *_workspace query.
+ *   - Matrices are row-major.  Weights are fp16 [rows, d_in]; activations are
+ *     fp16 or bf16 [T, d_in] with a leading dimension `ld_x` >= d_in (elements).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call validates its arguments synchronously on the host, then enqueues its
+ *     kernels asynchronously on `stream`; results are ready when the stream is.
+ *   - Inputs are never modified.  On any argument error nothing is launched and
+ *     outputs are untouched; the call returns a nonzero status and
+ *     awq_last_error() describes it.  A launch failure returns AWQ_EHIP.
+ *   - No global mutable device state: calls on distinct streams may run
+ *     concurrently if their buffers are distinct.  Results are deterministic
+ *     (fixed-order reductions, no floating-point atomics).
+ */
+#ifndef AWQ_H
+#define AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t awq_status;
+#define AWQ_OK 0
+#define AWQ_EINVAL 1     /* null pointer, negative size, unsupported value */
+#define AWQ_ESHAPE 2     /* d_in % group_size, d_out % 8, ld_x < d_in, ... */
+#define AWQ_EDTYPE 3     /* unknown dtype enum */
+#define AWQ_EWORKSPACE 4 /* ws too small or missing */
+#define AWQ_EALIGN 5     /* pointer or leading dimension not 16-byte aligned */
+#define AWQ_EHIP 6       /* HIP launch / runtime error */
+
+#define AWQ_F16 0
+#define AWQ_BF16 1
+#define AWQ_F32 2
+
+#define AWQ_SCORE_WEIGHT 0 /* [konic] AWQ scaling: ||(W - Q(W s)/s) diag(x_mean)||^2 */
+#define AWQ_SCORE_OUTPUT 1 /* [cassindra] mean((X W_hat^T - X W^T)^2) over the group */
+
+#define AWQ_ABI_VERSION 1
+
+/* Search configuration ([cassindra] search_scale(x, linears, ..., n_grid=20)). */
+typedef struct {
+  int32_t group_size; /* quantization group along d_in: 32, 64 or 128           */
+  int32_t n_grid;     /* number of alpha points, alpha_k = k / n_grid; 1..64      */
+  int32_t score;      /* AWQ_SCORE_WEIGHT or AWQ_SCORE_OUTPUT                     */
+  int32_t n_clip;     /* 0 = no clip search; else >= 2 ratios (output score only) */
+  double s_min;       /* lower clamp of x_mean^alpha before normalising (1e-4)    */
+  float clip_lo;      /* smallest clip ratio, in (0, 1]; ratios 1.0 .. clip_lo     */
+  int32_t reserved;   /* must be 0                                                */
+} awq_search_cfg;
+
+/* One group of linears sharing an input ([cassindra] torch.cat of the group's
+ * weights): part p is an fp16 device matrix [rows[p], d_in], 16-byte aligned.
+ * The rows of all parts are scored as one concatenated matrix. */
+typedef struct {
+  int32_t n_parts;       /* 1..8                                  */
+  const void* const* w;  /* [host] array of n_parts device ptrs   */
+  const int64_t* rows;   /* [host] array of n_parts row counts    */
+} awq_wgroup;
+
+/* ---------------------------------------------------------------------------
+ * awq_act_stats -- per-input-channel mean absolute activation.
+ * [konic] AWQ scaling (x = |X|.mean(0)); [cassindra] search_scale, first line.
+ *
+ *   x_mean[i] = (accumulate ? x_mean[i] : 0) + inv_count * sum_t |X[t, i]|
+ *
+ * X: fp16/bf16 [T, ld_x] (x_dtype = AWQ_F16 | AWQ_BF16); T >= 0, d_in >= 1.
+ * Sums are accumulated in fp64 in a fixed order and rounded once to fp32.
+ * Pass inv_count = 1/T for one chunk; to stream tokens in chunks, call with
+ * accumulate = 1 and inv_count = 1/T_total for every chunk after the first.
+ * ws: awq_act_stats_workspace(T, d_in) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+awq_status awq_act_stats_workspace(int64_t T, int64_t d_in, size_t* bytes /* [host] */);
+awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in, int64_t ld_x,
+                         float inv_count, int32_t accumulate, float* x_mean,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_candidate_scales -- the candidate scale table of the grid search.
+ * [cassindra] The scale search as code (non-duo branch); [lm] 5. AWQ: s = |X|^alpha.
+ *
+ *   t_k,i  = max(x_mean_i ^ (k / n_grid), s_min)     (x^0 = 1 for every x)
+ *   S[k,i] = fp32( t_k,i / sqrt(max_i t_k,i * min_i t_k,i) )   evaluated in fp64
+ *
+ * x_mean: fp32 [d_in] (non-negative, finite); S: fp32 [n_grid, d_in].
+ * Row 0 is exactly 1.0 (alpha = 0 is plain round-to-nearest).
+ * ------------------------------------------------------------------------- */
+awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_grid, double s_min,
+                                float* S, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_search_scales -- grid search of alpha for one input-sharing group.
+ * [konic] AWQ scaling (grid search, activation-weighted error, alpha = 0 is
+ * RTN so the search never worsens it); [konic] Group-wise symmetric INT4
+ * (step = max|group| / 7, q = round(w / step).clamp(-7, 7), round half to
+ * even); [cassindra] The scale search as code (keep the first strict minimum,
+ * weights restored: W is read-only here) and pipeline step 5 (clip search).
+ *
+ * For k = 0..n_grid-1, with s = S[k] and v = W*s (fp32), per row o and group g:
+ *   a = max|v|, step = RN(a / 7), q = clamp(rint(v / step), -7, 7), w_hat = q*step/s
+ *   AWQ_SCORE_WEIGHT: err[k] = sum_{o,i} ((W[o,i] - w_hat[o,i]) * x_mean[i])^2
+ *   AWQ_SCORE_OUTPUT: err[k] = mean_{t,o} (sum_i X[t,i] (w_hat[o,i] - W[o,i]))^2
+ * best_idx = first k attaining the minimum of err; best_s = S[best_idx].
+ * With n_clip >= 2 (output score only), afterwards per output row o and ratio
+ * c_j = fp32(1 - j (1 - clip_lo) / (n_clip - 1)), j = 0..n_clip-1, the step of
+ * every group of that row becomes RN(RN(c_j * a) / 7) with s = best_s, the row's
+ * output error sum_t (sum_i X[t,i] (w_hat - W)[o,i])^2 is evaluated, and
+ * clip[o] = c_j of the first strict minimum (ties keep the larger ratio).
+ *
+ * W: group of fp16 parts (rows concatenated), d_out_total = sum rows,
+ *    d_out_total >= 1, d_in % group_size == 0.
+ * x_mean: fp32 [d_in].  X: activations [T, ld_x] (x_dtype), required for the
+ *    output score and for the clip search, else may be NULL; T >= 1 then.
+ * err: fp32 [n_grid]; best_idx: int32 [1]; best_s: fp32 [d_in];
+ * clip: fp32 [d_out_total], required iff n_clip >= 2, else may be NULL;
+ * clip_err: fp32 [d_out_total, n_clip] per-row clip errors or NULL.
+ * Arithmetic: weight score decides codes in fp32 with a reciprocal of the step
+ * (codes can differ from an IEEE division only where v/step lies within a few
+ * ulp of a half-integer); partial sums in fp32, final sums in fp64.  Output
+ * score uses the bit-exact codes of awq_quantize_pack and contracts X with
+ * (w_hat - W) on the matrix cores in fp16, each operand scaled by a power of
+ * two chosen from its maximum (exact, overflow-free), fp32 accumulation, fp64
+ * final sums; the fp16 rounding of (w_hat - W) bounds the relative error of
+ * err[k] near 1e-4 on small inputs and far below it at calibration sizes.
+ * ws: awq_search_workspace(...) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+awq_status awq_search_workspace(const awq_search_cfg* cfg /* [host] */, int64_t d_out_total,
+                                int64_t d_in, int64_t T, size_t* bytes /* [host] */);
+awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_wgroup* W /* [host] */,
+                             int64_t d_in, const float* x_mean,
+                             const void* X, int32_t x_dtype, int64_t T, int64_t ld_x,
+                             float* err, int32_t* best_idx, float* best_s,
+                             float* clip, float* clip_err,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_quantize_pack -- quantize W*s and pack into the AutoAWQ GEMM layout.
+ * [konic] Group-wise symmetric INT4; AutoAWQ / HF-AWQ GEMM on-disk format
+ * (unsigned codes, 8 per int32, pack order [0,2,4,6,1,3,5,7]); exporter step 4
+ * (zero = 7, u = q + 7); [lm] 6-9 (scales [in/G, out] fp16, zeros [in/G, out/8]).
+ *
+ * v = RN(W*s) (s = NULL: v = W), a = max|v| over the group,
+ * step = RN(RN(clip[o]*a) / 7) (clip = NULL: RN(a / 7)),
+ * q = clamp(rint(RN(v / step)), -7, 7) with IEEE division and round half to
+ * even (bit-exact), step = 0 gives q = 0;  u = q + 7 in [0, 14].
+ *   qweight[i, m]: int32 [d_in, d_out/8]; nibble j (bits 4j..4j+3) holds u of
+ *                  output row 8m + order[j], order = {0,2,4,6,1,3,5,7}
+ *   scales[g, o]:  fp16 bits [d_in/G, d_out], fp16 round-to-nearest-even of step
+ *   qzeros[g, m]:  int32 [d_in/G, d_out/8], every nibble 7 (may be NULL)
+ * W: fp16 [d_out, d_in] 16-byte aligned; d_out % 8 == 0, d_in % group_size == 0,
+ * group_size in {32, 64, 128}; s: fp32 [d_in] or NULL; clip: fp32 [d_out] or NULL.
+ * ------------------------------------------------------------------------- */
+awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size,
+                             const float* s, const float* clip,
+                             int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_unpack_dequant -- inverse of awq_quantize_pack, for verification.
+ * [konic] exporter step 4: (u - zero) * scale reproduces q * step exactly.
+ *
+ * out[o, i] = (u[o,i] - zero[g,o]) * float(scales[g,o])   (fp32, exact)
+ *             divided by s[i] (IEEE) when s != NULL (back to W's domain).
+ * qzeros NULL means zero = 7.  out: [d_out, d_in] of out_dtype (AWQ_F32 or
+ * AWQ_F16, the latter rounded to nearest even).
+ * ------------------------------------------------------------------------- */
+awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                              int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
+                              void* out, int32_t out_dtype, void* stream);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* awq_last_error(void);
+/* AWQ_ABI_VERSION of the loaded library. */
+int32_t awq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AWQ_H */

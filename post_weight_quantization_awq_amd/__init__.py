@@ -1,0 +1,269 @@
+"""AWQ per-layer hot path on MI355X (gfx950): Python binding of libawq.so.
+
+This module only marshals arguments: torch tensors are checked for device,
+dtype and layout, their device pointers and the current HIP stream are handed
+to the C ABI declared in ``include/awq.h``, and errors come back as
+``AwqError``.  Every step of the computation runs in the library's HIP
+kernels; there is no CPU fallback.  The library must have been built
+(``python -m post_weight_quantization_awq_amd.build``); the first call without
+it raises ImportError.
+
+Entry points (same names as the C ABI):
+
+* ``act_stats``           per-input-channel mean |x|        ("AWQ scaling", konic.io)
+* ``candidate_scales``    s_k = clamp(x^(k/n), s_min) / sqrt(max*min)   ("The scale search as code", aicassindra.com)
+* ``search_scales``       alpha grid search, weight or output score, optional clip search
+* ``quantize_pack``       INT4 codes + fp16 scales in the AutoAWQ GEMM layout
+* ``unpack_dequant``      inverse of quantize_pack
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libawq.so")
+
+AWQ_OK, AWQ_EINVAL, AWQ_ESHAPE, AWQ_EDTYPE, AWQ_EWORKSPACE, AWQ_EALIGN, AWQ_EHIP = range(7)
+AWQ_F16, AWQ_BF16, AWQ_F32 = 0, 1, 2
+AWQ_SCORE_WEIGHT, AWQ_SCORE_OUTPUT = 0, 1
+STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_EINVAL", 2: "AWQ_ESHAPE", 3: "AWQ_EDTYPE",
+                4: "AWQ_EWORKSPACE", 5: "AWQ_EALIGN", 6: "AWQ_EHIP"}
+
+EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales",
+            "awq_search_workspace", "awq_search_scales", "awq_quantize_pack",
+            "awq_unpack_dequant", "awq_last_error", "awq_abi_version")
+
+
+class AwqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class SearchCfg(ctypes.Structure):
+    _fields_ = [("group_size", ctypes.c_int32), ("n_grid", ctypes.c_int32),
+                ("score", ctypes.c_int32), ("n_clip", ctypes.c_int32),
+                ("s_min", ctypes.c_double), ("clip_lo", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+class WGroup(ctypes.Structure):
+    _fields_ = [("n_parts", ctypes.c_int32), ("w", ctypes.POINTER(ctypes.c_void_p)),
+                ("rows", ctypes.POINTER(ctypes.c_int64))]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m post_weight_quantization_awq_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, F64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_size_t)
+    PSZ = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "awq_act_stats_workspace": [I64, I64, PSZ],
+        "awq_act_stats": [P, I32, I64, I64, I64, F32, I32, P, P, SZ, P],
+        "awq_candidate_scales": [P, I64, I32, F64, P, P],
+        "awq_search_workspace": [ctypes.POINTER(SearchCfg), I64, I64, I64, PSZ],
+        "awq_search_scales": [ctypes.POINTER(SearchCfg), ctypes.POINTER(WGroup), I64, P, P, I32, I64, I64,
+                              P, P, P, P, P, P, SZ, P],
+        "awq_quantize_pack": [P, I64, I64, I32, P, P, P, P, P, P],
+        "awq_unpack_dequant": [P, P, P, I64, I64, I32, P, P, I32, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int32
+    lib.awq_last_error.argtypes = []
+    lib.awq_last_error.restype = ctypes.c_char_p
+    lib.awq_abi_version.argtypes = []
+    lib.awq_abi_version.restype = ctypes.c_int32
+    return lib
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libawq.so (loaded on first use; ImportError if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def _check(st: int) -> None:
+    if st != AWQ_OK:
+        raise AwqError(st, lib().awq_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _x_dtype(X: torch.Tensor) -> int:
+    if X.dtype == torch.bfloat16:
+        return AWQ_BF16
+    if X.dtype == torch.float16:
+        return AWQ_F16
+    raise ValueError(f"activations must be bf16 or fp16, got {X.dtype}")
+
+
+def _rows_view(X: torch.Tensor, name: str):
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return X.shape[0], X.shape[1], X.stride(0)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def act_stats_workspace_bytes(T: int, d_in: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().awq_act_stats_workspace(T, d_in, ctypes.byref(n)))
+    return n.value
+
+
+def act_stats(X: torch.Tensor, x_mean: Optional[torch.Tensor] = None, inv_count: Optional[float] = None,
+              accumulate: bool = False, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """x_mean[i] (+)= inv_count * sum_t |X[t, i]| (inv_count defaults to 1/T)."""
+    _dev(X, "X")
+    T, d_in, ld = _rows_view(X, "X")
+    if x_mean is None:
+        x_mean = torch.empty(d_in, dtype=torch.float32, device=X.device)
+    if inv_count is None:
+        inv_count = 1.0 / T if T > 0 else 0.0
+    need = act_stats_workspace_bytes(T, d_in)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, X.device)
+    _check(lib().awq_act_stats(_ptr(X), _x_dtype(X), T, d_in, ld, inv_count, int(accumulate),
+                             _ptr(x_mean), _ptr(ws), ws.numel(), _stream(stream)))
+    return x_mean
+
+
+def candidate_scales(x_mean: torch.Tensor, n_grid: int = 20, s_min: float = 1e-4, stream=None) -> torch.Tensor:
+    _dev(x_mean, "x_mean")
+    d_in = x_mean.numel()
+    S = torch.empty((n_grid, d_in), dtype=torch.float32, device=x_mean.device)
+    _check(lib().awq_candidate_scales(_ptr(x_mean), d_in, n_grid, s_min, _ptr(S), _stream(stream)))
+    return S
+
+
+@dataclasses.dataclass
+class SearchResult:
+    err: torch.Tensor                 # fp32 [n_grid]
+    best_idx: torch.Tensor            # int32 [1]
+    best_s: torch.Tensor              # fp32 [d_in]
+    clip: Optional[torch.Tensor]      # fp32 [d_out] or None
+    clip_err: Optional[torch.Tensor]  # fp32 [d_out, n_clip] or None
+
+
+def _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min) -> SearchCfg:
+    sc = {"weight": AWQ_SCORE_WEIGHT, "output": AWQ_SCORE_OUTPUT}[score] if isinstance(score, str) else score
+    return SearchCfg(group_size, n_grid, sc, n_clip, s_min, clip_lo, 0)
+
+
+def search_workspace_bytes(d_out: int, d_in: int, T: int = 0, *, group_size: int = 128, n_grid: int = 20,
+                           score="weight", n_clip: int = 0, clip_lo: float = 0.5, s_min: float = 1e-4) -> int:
+    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min)
+    n = ctypes.c_size_t()
+    _check(lib().awq_search_workspace(ctypes.byref(cfg), d_out, d_in, T, ctypes.byref(n)))
+    return n.value
+
+
+def search_scales(W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, *, group_size: int = 128,
+                  n_grid: int = 20, score="weight", X: Optional[torch.Tensor] = None, n_clip: int = 0,
+                  clip_lo: float = 0.5, s_min: float = 1e-4, want_clip_err: bool = False,
+                  ws: Optional[torch.Tensor] = None, out: Optional[SearchResult] = None,
+                  stream=None) -> SearchResult:
+    """Grid search of alpha for one group of linears sharing an input (rows concatenated)."""
+    parts: List[torch.Tensor] = list(W_parts)
+    if not parts:
+        raise ValueError("empty weight group")
+    d_in = parts[0].shape[1]
+    for p in parts:
+        _dev(p, "W")
+        if p.dtype != torch.float16 or p.dim() != 2 or not p.is_contiguous() or p.shape[1] != d_in:
+            raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
+    dev = parts[0].device
+    d_out = sum(p.shape[0] for p in parts)
+    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min)
+    T, ld, xdt = 0, 0, AWQ_BF16
+    if X is not None:
+        _dev(X, "X")
+        T, dx, ld = _rows_view(X, "X")
+        if dx != d_in:
+            raise ValueError("X and W disagree on d_in")
+        xdt = _x_dtype(X)
+    n = ctypes.c_size_t()
+    _check(lib().awq_search_workspace(ctypes.byref(cfg), d_out, d_in, max(T, 1), ctypes.byref(n)))
+    if ws is None or ws.numel() < n.value:
+        ws = workspace(n.value, dev)
+    if out is None:
+        out = SearchResult(
+            err=torch.empty(n_grid, dtype=torch.float32, device=dev),
+            best_idx=torch.empty(1, dtype=torch.int32, device=dev),
+            best_s=torch.empty(d_in, dtype=torch.float32, device=dev),
+            clip=torch.empty(d_out, dtype=torch.float32, device=dev) if n_clip else None,
+            clip_err=torch.empty((d_out, n_clip), dtype=torch.float32, device=dev)
+            if (n_clip and want_clip_err) else None)
+    wptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    rows = (ctypes.c_int64 * len(parts))(*[p.shape[0] for p in parts])
+    grp = WGroup(len(parts), ctypes.cast(wptrs, ctypes.POINTER(ctypes.c_void_p)),
+                 ctypes.cast(rows, ctypes.POINTER(ctypes.c_int64)))
+    _check(lib().awq_search_scales(ctypes.byref(cfg), ctypes.byref(grp), d_in, _ptr(x_mean), _ptr(X), xdt, T, ld,
+                                 _ptr(out.err), _ptr(out.best_idx), _ptr(out.best_s), _ptr(out.clip),
+                                 _ptr(out.clip_err), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def quantize_pack(W: torch.Tensor, group_size: int = 128, s: Optional[torch.Tensor] = None,
+                  clip: Optional[torch.Tensor] = None, with_zeros: bool = True, out=None, stream=None):
+    """Returns (qweight int32 [d_in, d_out/8], scales fp16 [d_in/G, d_out], qzeros int32 [d_in/G, d_out/8])."""
+    _dev(W, "W")
+    if W.dtype != torch.float16 or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be contiguous fp16 [d_out, d_in]")
+    d_out, d_in = W.shape
+    if out is None:
+        qweight = torch.empty((d_in, d_out // 8), dtype=torch.int32, device=W.device)
+        scales = torch.empty((d_in // group_size, d_out), dtype=torch.float16, device=W.device)
+        qzeros = torch.empty((d_in // group_size, d_out // 8), dtype=torch.int32, device=W.device) \
+            if with_zeros else None
+    else:
+        qweight, scales, qzeros = out
+    _check(lib().awq_quantize_pack(_ptr(W), d_out, d_in, group_size, _ptr(s), _ptr(clip), _ptr(qweight),
+                                 _ptr(scales), _ptr(qzeros), _stream(stream)))
+    return qweight, scales, qzeros
+
+
+def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], d_out: int,
+                   group_size: int = 128, s: Optional[torch.Tensor] = None, out_dtype=torch.float32,
+                   stream=None) -> torch.Tensor:
+    _dev(qweight, "qweight")
+    d_in = qweight.shape[0]
+    out = torch.empty((d_out, d_in), dtype=out_dtype, device=qweight.device)
+    odt = {torch.float32: AWQ_F32, torch.float16: AWQ_F16}[out_dtype]
+    _check(lib().awq_unpack_dequant(_ptr(qweight), _ptr(scales), _ptr(qzeros), d_out, d_in, group_size, _ptr(s),
+                                  _ptr(out), odt, _stream(stream)))
+    return out
+
+
+__all__ = ["AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
+           "search_workspace_bytes", "act_stats_workspace_bytes", "SearchResult", "lib", "LIB_PATH"]

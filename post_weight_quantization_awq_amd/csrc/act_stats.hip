@@ -1,0 +1,146 @@
+// Per-input-channel mean |x| over calibration tokens.
+// "From-Scratch AWQ INT4 Quantization on Qwen3-8B", section "AWQ scaling"
+// (x = |X|.mean(0)); "AWQ architecture, in depth", section "The scale search
+// as code" (x.abs().float().mean(dim=0)).
+//
+// HBM-bound column reduction: 2 bytes read per element.  Each lane owns 8
+// consecutive channels (one 16-byte load per token row); the 4 waves of a block
+// take interleaved token rows; blocks split the token axis.  Per-lane sums are
+// fp64 (full rate on CDNA4 VALU), the split partials are combined in a fixed
+// order by a second kernel, so the result is deterministic and independent of
+// the launch shape up to fp64 rounding.
+#include "awq_device.h"
+#include "awq_launch.h"
+
+namespace awq {
+
+constexpr int kStatsThreads = 256;
+constexpr int kStatsCols = 64 * 8;  // channels per block
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
+    const uint16_t* __restrict__ X, int64_t T, int64_t d_in, int64_t ld, int64_t rows_per_split,
+    double* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t col0 = ((int64_t)blockIdx.x * 64 + lane) * 8;
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_split;
+  const int64_t r_end = min(T, r_begin + rows_per_split);
+  double acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+
+  if (col0 < d_in) {
+    if (VEC && col0 + 8 <= d_in) {
+      const uint16_t* p = X + col0;
+      int64_t r = r_begin + wv;
+      // 4 rows in flight per lane
+      for (; r + 12 < r_end; r += 16) {
+        uint4 u[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          u[q] = ld_nt(p + (r + 4 * q) * ld);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
+            float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
+            acc[2 * j] += (double)__builtin_fabsf(lo);
+            acc[2 * j + 1] += (double)__builtin_fabsf(hi);
+          }
+        }
+      }
+      for (; r < r_end; r += 4) {
+        uint4 u = *(const uint4*)(p + r * ld);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
+          float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
+          acc[2 * j] += (double)__builtin_fabsf(lo);
+          acc[2 * j + 1] += (double)__builtin_fabsf(hi);
+        }
+      }
+    } else {
+      for (int64_t r = r_begin + wv; r < r_end; r += 4) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (col0 + j < d_in) {
+            uint16_t b = X[r * ld + col0 + j];
+            acc[j] += (double)__builtin_fabsf(BF16 ? bf2f(b) : h2f(b));
+          }
+        }
+      }
+    }
+  }
+
+  __shared__ double red[4][64 * 8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[wv][lane * 8 + j] = acc[j];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 64 * 8; idx += kStatsThreads) {
+    const int64_t c = (int64_t)blockIdx.x * kStatsCols + idx;
+    if (c < d_in) {
+      double s = red[0][idx];
+      s += red[1][idx];
+      s += red[2][idx];
+      s += red[3][idx];
+      part[(int64_t)blockIdx.y * d_in + c] = s;
+    }
+  }
+}
+
+__global__ void act_stats_final_kernel(const double* __restrict__ part, int64_t n_split, int64_t d_in,
+                                       double inv_count, int accumulate, float* __restrict__ x_mean) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= d_in) return;
+  double s = 0.0;
+  for (int64_t p = 0; p < n_split; ++p) s += part[p * d_in + i];
+  double v = s * inv_count;
+  if (accumulate) v += (double)x_mean[i];
+  x_mean[i] = (float)v;
+}
+
+void act_stats_plan(int64_t T, int64_t d_in, int64_t* n_split, int64_t* rows_per_split) {
+  if (T <= 0 || d_in <= 0) {
+    *n_split = 0;
+    *rows_per_split = 1;
+    return;
+  }
+  const int64_t col_blocks = (d_in + kStatsCols - 1) / kStatsCols;
+  int64_t want = (4096 + col_blocks - 1) / col_blocks;           // ~4096 blocks in flight
+  int64_t max_split = (T + 63) / 64;                            // >= 64 rows per split
+  int64_t ns = want < max_split ? want : max_split;
+  if (ns < 1) ns = 1;
+  int64_t rps = (T + ns - 1) / ns;
+  rps = (rps + 15) / 16 * 16;
+  *rows_per_split = rps;
+  *n_split = (T + rps - 1) / rps;
+}
+
+hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld,
+                            float inv_count, int accumulate, float* x_mean, void* ws,
+                            hipStream_t stream) {
+  int64_t n_split, rps;
+  act_stats_plan(T, d_in, &n_split, &rps);
+  double* part = (double*)ws;
+  if (n_split > 0) {
+    const bool vec = ((uintptr_t)X % 16 == 0) && (ld % 8 == 0);
+    dim3 grid((unsigned)((d_in + kStatsCols - 1) / kStatsCols), (unsigned)n_split);
+    const uint16_t* x = (const uint16_t*)X;
+    if (bf16) {
+      if (vec) act_stats_partial_kernel<true, true><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
+      else act_stats_partial_kernel<true, false><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
+    } else {
+      if (vec) act_stats_partial_kernel<false, true><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
+      else act_stats_partial_kernel<false, false><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
+    }
+  }
+  act_stats_final_kernel<<<(unsigned)((d_in + 255) / 256), 256, 0, stream>>>(
+      part, n_split, d_in, (double)inv_count, accumulate, x_mean);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -1,0 +1,319 @@
+// C ABI of libawq (declared in include/awq.h): argument validation, workspace
+// carving and kernel launches.  Every argument error is found before anything
+// is enqueued; no entry point allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/awq.h"
+#include "awq_device.h"
+#include "awq_launch.h"
+
+using namespace awq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+awq_status fail(awq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+awq_status ok() {
+  g_err[0] = '\0';
+  return AWQ_OK;
+}
+
+awq_status hip_status(hipError_t e, const char* where) {
+  if (e != hipSuccess) return fail(AWQ_EHIP, "%s: %s", where, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
+
+// workspace layout of awq_search_scales
+struct SearchPlan {
+  bool output;
+  int64_t n_blocks;     // weight score: search blocks
+  int64_t n_mt, n_nt;   // output score: GEMM tiles
+  int64_t n_x, n_db;    // output score: X max partials, dW max partials per candidate
+  int cand_chunk;       // output score: candidates per dW chunk
+  size_t off_S, off_C2, off_part, off_x16, off_dw, off_colpart, off_xmax, off_dmax, off_sc, total;
+};
+
+constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
+
+SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, int64_t T) {
+  SearchPlan p{};
+  p.output = cfg.score == AWQ_SCORE_OUTPUT;
+  size_t off = 0;
+  p.off_S = off;
+  off += align256((size_t)cfg.n_grid * d_in * sizeof(float));
+  if (!p.output) {
+    p.off_C2 = off;
+    off += align256((size_t)cfg.n_grid * d_in * sizeof(float));
+    p.n_blocks = search_weight_blocks(cfg.group_size, d_out, d_in);
+    p.off_part = off;
+    off += align256((size_t)p.n_blocks * cfg.n_grid * sizeof(float));
+  } else {
+    gemm_sq_shape(T, d_out, 0, &p.n_mt, &p.n_nt);
+    p.n_x = absmax_blocks(T);
+    p.n_db = build_dw_blocks(cfg.group_size, d_out, d_in);
+    const int max_c = cfg.n_grid > cfg.n_clip ? cfg.n_grid : cfg.n_clip;
+    const size_t per_cand = (size_t)d_out * d_in * sizeof(uint16_t);
+    int64_t chunk = (int64_t)(kDwBudget / (per_cand ? per_cand : 1));
+    if (chunk > max_c) chunk = max_c;
+    if (chunk < 1) chunk = 1;
+    p.cand_chunk = (int)chunk;
+    p.off_x16 = off;
+    off += align256((size_t)T * d_in * sizeof(uint16_t));
+    p.off_dw = off;
+    off += align256(per_cand * chunk);
+    p.off_part = off;
+    off += align256((size_t)cfg.n_grid * p.n_mt * p.n_nt * sizeof(float));
+    if (cfg.n_clip >= 2) {
+      p.off_colpart = off;
+      off += align256((size_t)cfg.n_clip * p.n_mt * d_out * sizeof(float));
+    }
+    p.off_xmax = off;
+    off += align256((size_t)p.n_x * sizeof(float));
+    p.off_dmax = off;
+    off += align256((size_t)max_c * p.n_db * sizeof(float));
+    p.off_sc = off;
+    off += 2 * align256(sizeof(OutScales));
+  }
+  p.total = off;
+  return p;
+}
+
+awq_status check_cfg(const awq_search_cfg* cfg) {
+  if (!cfg) return fail(AWQ_EINVAL, "cfg is NULL");
+  if (!valid_group(cfg->group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", cfg->group_size);
+  if (cfg->n_grid < 1 || cfg->n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", cfg->n_grid, kMaxGrid);
+  if (cfg->score != AWQ_SCORE_WEIGHT && cfg->score != AWQ_SCORE_OUTPUT)
+    return fail(AWQ_EINVAL, "score %d unknown", cfg->score);
+  if (cfg->n_clip != 0) {
+    if (cfg->n_clip < 2 || cfg->n_clip > kMaxGrid) return fail(AWQ_EINVAL, "n_clip %d not 0 or in [2,%d]", cfg->n_clip, kMaxGrid);
+    if (cfg->score != AWQ_SCORE_OUTPUT) return fail(AWQ_EINVAL, "clip search needs the output score");
+    if (!(cfg->clip_lo > 0.0f && cfg->clip_lo <= 1.0f)) return fail(AWQ_EINVAL, "clip_lo %g not in (0,1]", (double)cfg->clip_lo);
+  }
+  if (!(cfg->s_min > 0.0 && isfinite(cfg->s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
+  if (cfg->reserved != 0) return fail(AWQ_EINVAL, "reserved must be 0");
+  return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_last_error(void) { return g_err; }
+
+int32_t awq_abi_version(void) { return AWQ_ABI_VERSION; }
+
+// ---------------------------------------------------------------------------
+awq_status awq_act_stats_workspace(int64_t T, int64_t d_in, size_t* bytes) {
+  if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
+  if (T < 0 || d_in < 1) return fail(AWQ_EINVAL, "need T >= 0 and d_in >= 1");
+  int64_t ns, rps;
+  act_stats_plan(T, d_in, &ns, &rps);
+  *bytes = align256((size_t)ns * d_in * sizeof(double));
+  return ok();
+}
+
+awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in, int64_t ld_x,
+                         float inv_count, int32_t accumulate, float* x_mean, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (x_dtype != AWQ_F16 && x_dtype != AWQ_BF16) return fail(AWQ_EDTYPE, "x_dtype %d: need AWQ_F16 or AWQ_BF16", x_dtype);
+  if (T < 0 || d_in < 1) return fail(AWQ_EINVAL, "need T >= 0 and d_in >= 1");
+  if (ld_x < d_in) return fail(AWQ_ESHAPE, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
+  if (!x_mean) return fail(AWQ_EINVAL, "x_mean is NULL");
+  if (T > 0 && !X) return fail(AWQ_EINVAL, "X is NULL");
+  if (!isfinite(inv_count)) return fail(AWQ_EINVAL, "inv_count not finite");
+  size_t need = 0;
+  awq_act_stats_workspace(T, d_in, &need);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if (need > 0 && ((uintptr_t)ws & 7u)) return fail(AWQ_EALIGN, "ws not 8-byte aligned");
+  return hip_status(launch_act_stats(X, x_dtype == AWQ_BF16, T, d_in, ld_x, inv_count, accumulate ? 1 : 0,
+                                     x_mean, ws, (hipStream_t)stream),
+                    "awq_act_stats");
+}
+
+// ---------------------------------------------------------------------------
+awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_grid, double s_min,
+                                float* S, void* stream) {
+  if (!x_mean || !S) return fail(AWQ_EINVAL, "x_mean / S is NULL");
+  if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
+  if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
+  if (!(s_min > 0.0 && isfinite(s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
+  return hip_status(launch_candidates(x_mean, d_in, n_grid, s_min, S, nullptr, (hipStream_t)stream),
+                    "awq_candidate_scales");
+}
+
+// ---------------------------------------------------------------------------
+awq_status awq_search_workspace(const awq_search_cfg* cfg, int64_t d_out_total, int64_t d_in, int64_t T,
+                                size_t* bytes) {
+  awq_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
+  if (d_out_total < 1 || d_in < 1) return fail(AWQ_EINVAL, "need d_out_total >= 1 and d_in >= 1");
+  if (d_in % cfg->group_size) return fail(AWQ_ESHAPE, "d_in %lld not a multiple of group_size %d", (long long)d_in, cfg->group_size);
+  if (cfg->score == AWQ_SCORE_OUTPUT && T < 1) return fail(AWQ_EINVAL, "output score needs T >= 1");
+  *bytes = plan_search(*cfg, d_out_total, d_in, T).total;
+  return ok();
+}
+
+awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int64_t d_in,
+                             const float* x_mean, const void* X, int32_t x_dtype, int64_t T,
+                             int64_t ld_x, float* err, int32_t* best_idx, float* best_s, float* clip,
+                             float* clip_err, void* ws, size_t ws_bytes, void* stream) {
+  awq_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!W || !W->w || !W->rows) return fail(AWQ_EINVAL, "weight group is NULL");
+  if (W->n_parts < 1 || W->n_parts > kMaxParts) return fail(AWQ_EINVAL, "n_parts %d not in [1,%d]", W->n_parts, kMaxParts);
+  WParts parts{};
+  parts.n = W->n_parts;
+  int64_t d_out = 0;
+  for (int p = 0; p < W->n_parts; ++p) {
+    if (W->rows[p] < 0) return fail(AWQ_EINVAL, "rows[%d] < 0", p);
+    if (W->rows[p] > 0 && !W->w[p]) return fail(AWQ_EINVAL, "w[%d] is NULL", p);
+    if (!aligned16(W->w[p])) return fail(AWQ_EALIGN, "w[%d] not 16-byte aligned", p);
+    parts.ptr[p] = (const uint16_t*)W->w[p];
+    parts.row_start[p] = d_out;
+    d_out += W->rows[p];
+  }
+  for (int p = W->n_parts; p <= kMaxParts; ++p) parts.row_start[p] = d_out;
+  for (int p = W->n_parts; p < kMaxParts; ++p) parts.ptr[p] = parts.ptr[W->n_parts - 1];
+  if (d_out < 1) return fail(AWQ_EINVAL, "group has no rows");
+  if (d_in < cfg->group_size || d_in % cfg->group_size)
+    return fail(AWQ_ESHAPE, "d_in %lld not a positive multiple of group_size %d", (long long)d_in, cfg->group_size);
+  if (!x_mean || !err || !best_idx || !best_s) return fail(AWQ_EINVAL, "x_mean / err / best_idx / best_s is NULL");
+  if (!aligned16(x_mean) || !aligned16(best_s)) return fail(AWQ_EALIGN, "x_mean / best_s not 16-byte aligned");
+  const bool need_x = cfg->score == AWQ_SCORE_OUTPUT || cfg->n_clip >= 2;
+  if (need_x) {
+    if (!X) return fail(AWQ_EINVAL, "X is NULL (needed by the output score)");
+    if (x_dtype != AWQ_F16 && x_dtype != AWQ_BF16) return fail(AWQ_EDTYPE, "x_dtype %d: need AWQ_F16 or AWQ_BF16", x_dtype);
+    if (T < 1) return fail(AWQ_EINVAL, "output score needs T >= 1");
+    if (ld_x < d_in) return fail(AWQ_ESHAPE, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
+    if (!aligned16(X) || (ld_x % 8)) return fail(AWQ_EALIGN, "X must be 16-byte aligned with ld_x % 8 == 0");
+  }
+  if (cfg->n_clip >= 2 && !clip) return fail(AWQ_EINVAL, "clip is NULL but n_clip >= 2");
+  const SearchPlan plan = plan_search(*cfg, d_out, d_in, T);
+  if (!ws || ws_bytes < plan.total) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, plan.total);
+  if ((uintptr_t)ws & 255u) return fail(AWQ_EALIGN, "ws not 256-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  float* S = (float*)(base + plan.off_S);
+  hipError_t e;
+  if (!plan.output) {
+    float* C2 = (float*)(base + plan.off_C2);
+    float* part = (float*)(base + plan.off_part);
+    if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, C2, s)) != hipSuccess)
+      return hip_status(e, "candidates");
+    if ((e = launch_search_weight(cfg->group_size, parts, d_out, d_in, cfg->n_grid, S, C2, part, s)) != hipSuccess)
+      return hip_status(e, "search_weight");
+    if ((e = launch_select(part, plan.n_blocks, cfg->n_grid, cfg->n_grid, 1, 1.0, nullptr, err, best_idx, S,
+                           d_in, best_s, s)) != hipSuccess)
+      return hip_status(e, "select");
+    return ok();
+  }
+
+  const bool bf16 = x_dtype == AWQ_BF16;
+  uint16_t* x16 = (uint16_t*)(base + plan.off_x16);
+  uint16_t* dw = (uint16_t*)(base + plan.off_dw);
+  float* part = (float*)(base + plan.off_part);
+  float* xmax = (float*)(base + plan.off_xmax);
+  float* dmax = (float*)(base + plan.off_dmax);
+  OutScales* sc_a = (OutScales*)(base + plan.off_sc);
+  OutScales* sc_c = (OutScales*)(base + plan.off_sc + align256(sizeof(OutScales)));
+  const int64_t n_tiles = plan.n_mt * plan.n_nt;
+  const int G = cfg->group_size;
+  if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, nullptr, s)) != hipSuccess)
+    return hip_status(e, "candidates");
+  if ((e = launch_prepare_x(X, bf16, T, d_in, ld_x, xmax, s)) != hipSuccess) return hip_status(e, "absmax(X)");
+  if ((e = launch_build_dw(G, parts, d_out, d_in, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax, nullptr,
+                           s)) != hipSuccess)
+    return hip_status(e, "build_dw(max)");
+  if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, cfg->n_grid, sc_a, s)) != hipSuccess)
+    return hip_status(e, "out_scales");
+  if ((e = launch_convert_x(X, bf16, T, d_in, ld_x, sc_a, x16, s)) != hipSuccess) return hip_status(e, "convert_x");
+  for (int c0 = 0; c0 < cfg->n_grid; c0 += plan.cand_chunk) {
+    const int nc = (cfg->n_grid - c0) < plan.cand_chunk ? (cfg->n_grid - c0) : plan.cand_chunk;
+    if ((e = launch_build_dw(G, parts, d_out, d_in, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, nullptr, dw, s)) !=
+        hipSuccess)
+      return hip_status(e, "build_dw");
+    if ((e = launch_gemm_sq(x16, T, d_in, dw, d_out, d_in, nc, 0, part + (size_t)c0 * n_tiles, s)) != hipSuccess)
+      return hip_status(e, "gemm_sq");
+  }
+  if ((e = launch_select(part, n_tiles, cfg->n_grid, 1, n_tiles, 1.0 / ((double)T * (double)d_out), sc_a->inv,
+                         err, best_idx, S, d_in, best_s, s)) != hipSuccess)
+    return hip_status(e, "select");
+  if (cfg->n_clip >= 2) {
+    float* colpart = (float*)(base + plan.off_colpart);
+    const int nclip = cfg->n_clip;
+    if ((e = launch_build_dw(G, parts, d_out, d_in, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0, nullptr,
+                             dmax, nullptr, s)) != hipSuccess)
+      return hip_status(e, "build_dw(clip max)");
+    if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, nclip, sc_c, s)) != hipSuccess)
+      return hip_status(e, "out_scales(clip)");
+    for (int c0 = 0; c0 < nclip; c0 += plan.cand_chunk) {
+      const int nc = (nclip - c0) < plan.cand_chunk ? (nclip - c0) : plan.cand_chunk;
+      if ((e = launch_build_dw(G, parts, d_out, d_in, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0, sc_c,
+                               nullptr, dw, s)) != hipSuccess)
+        return hip_status(e, "build_dw(clip)");
+      if ((e = launch_gemm_sq(x16, T, d_in, dw, d_out, d_in, nc, 1, colpart + (size_t)c0 * plan.n_mt * d_out, s)) !=
+          hipSuccess)
+        return hip_status(e, "gemm_sq(clip)");
+    }
+    if ((e = launch_clip_select(colpart, plan.n_mt, d_out, nclip, cfg->clip_lo, sc_c, clip, clip_err, s)) !=
+        hipSuccess)
+      return hip_status(e, "clip_select");
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
+                             const float* clip, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+                             void* stream) {
+  if (!valid_group(group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", group_size);
+  if (d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
+  if (d_out % 8) return fail(AWQ_ESHAPE, "d_out %lld not a multiple of 8", (long long)d_out);
+  if (d_in % group_size) return fail(AWQ_ESHAPE, "d_in %lld not a multiple of group_size %d", (long long)d_in, group_size);
+  if (d_out == 0 || d_in == 0) return ok();
+  if (!W || !qweight || !scales) return fail(AWQ_EINVAL, "W / qweight / scales is NULL");
+  if (!aligned16(W) || !aligned16(scales)) return fail(AWQ_EALIGN, "W / scales not 16-byte aligned");
+  if (s && !aligned16(s)) return fail(AWQ_EALIGN, "s not 16-byte aligned");
+  if (((uintptr_t)qweight & 3u) || (qzeros && ((uintptr_t)qzeros & 3u)) || (clip && ((uintptr_t)clip & 3u)))
+    return fail(AWQ_EALIGN, "qweight / qzeros / clip not 4-byte aligned");
+  return hip_status(launch_quantize_pack((const uint16_t*)W, d_out, d_in, group_size, s, clip, qweight, scales,
+                                         qzeros, (hipStream_t)stream),
+                    "awq_quantize_pack");
+}
+
+awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, int64_t d_out,
+                              int64_t d_in, int32_t group_size, const float* s, void* out, int32_t out_dtype,
+                              void* stream) {
+  if (!valid_group(group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", group_size);
+  if (out_dtype != AWQ_F32 && out_dtype != AWQ_F16) return fail(AWQ_EDTYPE, "out_dtype %d: need AWQ_F32 or AWQ_F16", out_dtype);
+  if (d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
+  if (d_out % 8) return fail(AWQ_ESHAPE, "d_out %lld not a multiple of 8", (long long)d_out);
+  if (d_in % group_size) return fail(AWQ_ESHAPE, "d_in %lld not a multiple of group_size %d", (long long)d_in, group_size);
+  if (d_out == 0 || d_in == 0) return ok();
+  if (!qweight || !scales || !out) return fail(AWQ_EINVAL, "qweight / scales / out is NULL");
+  return hip_status(launch_unpack_dequant(qweight, scales, qzeros, d_out, d_in, group_size, s, out,
+                                          out_dtype == AWQ_F16, (hipStream_t)stream),
+                    "awq_unpack_dequant");
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Host-side launch wrappers of the libawq kernels (internal; the public ABI is
+// include/awq.h).  Each wrapper enqueues on `stream` and returns
+// hipGetLastError() after its launches; arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "awq_device.h"
+
+namespace awq {
+
+// activation statistics
+void act_stats_plan(int64_t T, int64_t d_in, int64_t* n_split, int64_t* rows_per_split);
+hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld,
+                            float inv_count, int accumulate, float* x_mean, void* ws,
+                            hipStream_t stream);
+
+// candidate scale table S [n_grid, d_in] and, if C2 != nullptr, (x/s)^2 [n_grid, d_in]
+hipError_t launch_candidates(const float* x_mean, int64_t d_in, int n_grid, double s_min, float* S,
+                             float* C2, hipStream_t stream);
+
+// weight-score search: per-block partial errors [n_blocks, n_grid]
+int64_t search_weight_blocks(int group_size, int64_t d_out, int64_t d_in);
+hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_out, int64_t d_in,
+                                int n_grid, const float* S, const float* C2, float* partials,
+                                hipStream_t stream);
+
+// reduce partials p[b * stride_b + c * stride_c] over b (fixed order, fp64) ->
+// err [n_cand] (times `scale`, and times cand_scale[c] when given), first-minimum
+// index -> best_idx, best_s = S[best]
+hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, int64_t stride_b,
+                         int64_t stride_c, double scale, const double* cand_scale, float* err,
+                         int32_t* best_idx, const float* S, int64_t d_in, float* best_s,
+                         hipStream_t stream);
+
+// output-score search
+// X -> per-block max |X| [absmax_blocks(T)]
+int64_t absmax_blocks(int64_t rows);
+hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, float* xmax_part,
+                            hipStream_t stream);
+// scales: xs from the X partial maxima (xmax_part may be nullptr to keep xs), ds[c] and inv[c]
+// from the dW partial maxima dmax [n_cand, n_d]
+hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
+                             OutScales* sc, hipStream_t stream);
+// X16 [T, d_in] = fp16(X * xs)
+hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, const OutScales* sc,
+                            uint16_t* X16, hipStream_t stream);
+// dW of candidates c = cand0 .. cand0+n_cand-1 (mode 0: s = S[c]; mode 1: s = s_best, clip ratio c):
+//   dw == nullptr: per-block max |dW_c| -> dmax [n_cand, build_dw_blocks()]
+//   dw != nullptr: dw[c - cand0] = fp16(dW_c * sc->ds[c])
+int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in);
+hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, int64_t d_in,
+                           int n_cand, int mode, const float* S, const float* s_best, int n_clip,
+                           float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
+                           hipStream_t stream);
+// gemm-of-squares on fp16 operands: for every candidate c, Y = X16 dW[c]^T ([T, d_out]),
+//   per_col = 0: partials [n_cand, n_tiles] of sum(Y^2) per tile
+//   per_col = 1: partials [n_cand, n_mtiles, d_out] of column sums of Y^2
+void gemm_sq_shape(int64_t T, int64_t d_out, int per_col, int64_t* n_mtiles, int64_t* n_ntiles);
+hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T, int64_t ld_x, const uint16_t* dw, int64_t d_out,
+                          int64_t d_in, int n_cand, int per_col, float* partials, hipStream_t stream);
+// per-row argmin over clip ratios from column partials [n_clip, n_mtiles, d_out] (times sc->inv[j])
+hipError_t launch_clip_select(const float* colpart, int64_t n_mtiles, int64_t d_out, int n_clip,
+                              float clip_lo, const OutScales* sc, float* clip, float* clip_err,
+                              hipStream_t stream);
+
+// quantize + pack, unpack + dequant
+hipError_t launch_quantize_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int group_size,
+                                const float* s, const float* clip, int32_t* qweight,
+                                uint16_t* scales, int32_t* qzeros, hipStream_t stream);
+hipError_t launch_unpack_dequant(const int32_t* qweight, const uint16_t* scales,
+                                 const int32_t* qzeros, int64_t d_out, int64_t d_in, int group_size,
+                                 const float* s, void* out, bool out_f16, hipStream_t stream);
+
+}  // namespace awq

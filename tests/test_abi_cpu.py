@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/awq.h declares, and rejects bad arguments before launching anything.
+
+Device pointers here are fake (never dereferenced): every call below fails
+validation on the host, or has an empty size, so no kernel is enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+
+@pytest.fixture(scope="module")
+def A():
+    from post_weight_quantization_awq_amd import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        from post_weight_quantization_awq_amd import build
+        build.build()
+    import post_weight_quantization_awq_amd as A
+    A.lib()
+    return A
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ["awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_unpack_dequant",
+              "awq_search_workspace", "awq_last_error", "awq_abi_version", "awq_candidate_scales",
+              "awq_act_stats_workspace"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(A):
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in names:
+        assert n in exported, n
+        getattr(A.lib(), n)
+    assert set(A.EXPORTED) == set(names)
+
+
+def test_abi_version(A):
+    assert A.lib().awq_abi_version() == 1
+
+
+FAKE = 1 << 20          # 16- and 256-byte aligned, never dereferenced
+FAKE_MIS = FAKE + 2     # misaligned
+
+
+def st_pack(A, W=FAKE, d_out=64, d_in=256, G=128, s=None, clip=None, qw=FAKE, sc=FAKE, qz=None):
+    return A.lib().awq_quantize_pack(W, d_out, d_in, G, s, clip, qw, sc, qz, None)
+
+
+def test_pack_validation(A):
+    assert st_pack(A, G=96) == A.AWQ_EINVAL
+    assert st_pack(A, d_out=60) == A.AWQ_ESHAPE
+    assert st_pack(A, d_in=200) == A.AWQ_ESHAPE
+    assert st_pack(A, W=None) == A.AWQ_EINVAL
+    assert st_pack(A, W=FAKE_MIS) == A.AWQ_EALIGN
+    assert st_pack(A, s=FAKE_MIS) == A.AWQ_EALIGN
+    assert st_pack(A, d_out=-8) == A.AWQ_EINVAL
+    assert "multiple of 8" in A.lib().awq_last_error().decode() or True
+    # empty inputs: nothing to do, no launch, NULL pointers allowed
+    assert st_pack(A, W=None, d_out=0, qw=None, sc=None) == A.AWQ_OK
+    assert st_pack(A, W=None, d_in=0, qw=None, sc=None) == A.AWQ_OK
+    assert A.lib().awq_last_error().decode() == ""
+
+
+def test_unpack_validation(A):
+    L = A.lib()
+    assert L.awq_unpack_dequant(FAKE, FAKE, None, 64, 256, 128, None, FAKE, 7, None) == A.AWQ_EDTYPE
+    assert L.awq_unpack_dequant(FAKE, FAKE, None, 63, 256, 128, None, FAKE, A.AWQ_F32, None) == A.AWQ_ESHAPE
+    assert L.awq_unpack_dequant(None, FAKE, None, 64, 256, 128, None, FAKE, A.AWQ_F32, None) == A.AWQ_EINVAL
+    assert L.awq_unpack_dequant(None, None, None, 0, 256, 128, None, None, A.AWQ_F32, None) == A.AWQ_OK
+
+
+def test_act_stats_validation(A):
+    L = A.lib()
+    n = ctypes.c_size_t()
+    assert L.awq_act_stats_workspace(4096, 4096, ctypes.byref(n)) == 0 and n.value > 0
+    need = n.value
+    assert L.awq_act_stats(FAKE, 9, 4096, 4096, 4096, 1.0, 0, FAKE, FAKE, need, None) == A.AWQ_EDTYPE
+    assert L.awq_act_stats(FAKE, A.AWQ_BF16, 4096, 4096, 4000, 1.0, 0, FAKE, FAKE, need, None) == A.AWQ_ESHAPE
+    assert L.awq_act_stats(FAKE, A.AWQ_BF16, 4096, 4096, 4096, 1.0, 0, None, FAKE, need, None) == A.AWQ_EINVAL
+    assert L.awq_act_stats(None, A.AWQ_BF16, 4096, 4096, 4096, 1.0, 0, FAKE, FAKE, need, None) == A.AWQ_EINVAL
+    assert L.awq_act_stats(FAKE, A.AWQ_BF16, 4096, 4096, 4096, 1.0, 0, FAKE, FAKE, need - 8, None) == A.AWQ_EWORKSPACE
+    assert L.awq_act_stats(FAKE, A.AWQ_BF16, 4096, 4096, 4096, float("inf"), 0, FAKE, FAKE, need, None) == A.AWQ_EINVAL
+    assert L.awq_act_stats(FAKE, A.AWQ_BF16, -1, 4096, 4096, 1.0, 0, FAKE, FAKE, need, None) == A.AWQ_EINVAL
+    # T = 0 needs no workspace
+    assert L.awq_act_stats_workspace(0, 4096, ctypes.byref(n)) == 0 and n.value == 0
+
+
+def _group(A, ptrs, rows):
+    wp = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    rw = (ctypes.c_int64 * len(rows))(*rows)
+    g = A.WGroup(len(ptrs), ctypes.cast(wp, ctypes.POINTER(ctypes.c_void_p)),
+                 ctypes.cast(rw, ctypes.POINTER(ctypes.c_int64)))
+    g._keep = (wp, rw)
+    return g
+
+
+def st_search(A, cfg, grp, d_in=256, X=None, T=0, ld=0, clip=None, ws=FAKE, ws_bytes=1 << 40, xdt=1,
+              x_mean=FAKE):
+    return A.lib().awq_search_scales(ctypes.byref(cfg), ctypes.byref(grp), d_in, x_mean, X, xdt, T, ld,
+                                     FAKE, FAKE, FAKE, clip, None, ws, ws_bytes, None)
+
+
+def test_search_validation(A):
+    grp = _group(A, [FAKE, FAKE], [64, 32])
+    good = A._cfg(128, 20, "weight", 0, 0.5, 1e-4)
+    bad = [A._cfg(96, 20, "weight", 0, 0.5, 1e-4), A._cfg(128, 0, "weight", 0, 0.5, 1e-4),
+           A._cfg(128, 65, "weight", 0, 0.5, 1e-4), A._cfg(128, 20, 5, 0, 0.5, 1e-4),
+           A._cfg(128, 20, "weight", 20, 0.5, 1e-4), A._cfg(128, 20, "output", 1, 0.5, 1e-4),
+           A._cfg(128, 20, "output", 20, 0.0, 1e-4), A._cfg(128, 20, "weight", 0, 0.5, 0.0)]
+    for c in bad:
+        assert st_search(A, c, grp, X=FAKE, T=16, ld=256, clip=FAKE) == A.AWQ_EINVAL
+    c = A._cfg(128, 20, "weight", 0, 0.5, 1e-4)
+    c.reserved = 3
+    assert st_search(A, c, grp) == A.AWQ_EINVAL
+    assert st_search(A, good, grp, d_in=200) == A.AWQ_ESHAPE
+    assert st_search(A, good, grp, d_in=64) == A.AWQ_ESHAPE
+    assert st_search(A, good, _group(A, [FAKE_MIS], [64])) == A.AWQ_EALIGN
+    assert st_search(A, good, _group(A, [None], [64])) == A.AWQ_EINVAL
+    assert st_search(A, good, _group(A, [FAKE], [0])) == A.AWQ_EINVAL
+    assert st_search(A, good, _group(A, [FAKE] * 9, [8] * 9)) == A.AWQ_EINVAL
+    assert st_search(A, good, grp, x_mean=None) == A.AWQ_EINVAL
+    assert st_search(A, good, grp, ws_bytes=100) == A.AWQ_EWORKSPACE
+    assert st_search(A, good, grp, ws=FAKE + 16) == A.AWQ_EALIGN
+    out = A._cfg(128, 20, "output", 0, 0.5, 1e-4)
+    assert st_search(A, out, grp, X=None, T=16, ld=256) == A.AWQ_EINVAL
+    assert st_search(A, out, grp, X=FAKE, T=0, ld=256) == A.AWQ_EINVAL
+    assert st_search(A, out, grp, X=FAKE, T=16, ld=100) == A.AWQ_ESHAPE
+    assert st_search(A, out, grp, X=FAKE, T=16, ld=260) == A.AWQ_EALIGN
+    assert st_search(A, out, grp, X=FAKE_MIS, T=16, ld=256) == A.AWQ_EALIGN
+    assert st_search(A, out, grp, X=FAKE, T=16, ld=256, xdt=2) == A.AWQ_EDTYPE
+    clipc = A._cfg(128, 20, "output", 20, 0.5, 1e-4)
+    assert st_search(A, clipc, grp, X=FAKE, T=16, ld=256, clip=None) == A.AWQ_EINVAL
+    assert A.lib().awq_last_error().decode() != ""
+
+
+def test_workspace_sizes(A):
+    wmode = A.search_workspace_bytes(4096, 4096)
+    assert wmode < (1 << 21)                      # tables + per-block partials only
+    omode = A.search_workspace_bytes(6144, 4096, 16384, score="output")
+    assert omode >= 20 * 6144 * 4096 * 2          # dW of every candidate (bf16)
+    big = A.search_workspace_bytes(24576, 4096, 16384, score="output", n_clip=20)
+    assert big < (3 << 30)                        # dW built in chunks of <= 2 GiB
+    with pytest.raises(A.AwqError):
+        A.search_workspace_bytes(4096, 4000)
