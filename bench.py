@@ -1,0 +1,406 @@
+#!/usr/bin/env python3
+"""Benchmark of the AWQ per-layer hot path on one MI355X.
+
+One step = the whole path on one linear group with its inputs resident in HBM:
+activation statistics -> candidate scales -> grid search over alpha (20
+points) -> selection -> INT4 quantize + pack of the winner.  The default
+workload is a Qwen3-8B q_proj-shaped linear (W 4096 x 4096 fp16, X 4096
+tokens x 4096 bf16, group size 128, weight-domain activation-weighted error).
+
+Prints ONE JSON line.  `value` is weight-elements x grid-points per second of
+the whole step; per-kernel times come from HIP events recorded by the library
+around its main kernels on the stream they run on; `roofline` describes the
+dominant kernel; `cpu_baseline` times the CPU oracle on a bounded sample.
+
+Other workloads (--workload) measure the remaining rows: the output-score
+search on the matrix cores (fused QKV, MLP with clip search) and the full
+Qwen3-8B-shaped sweep of 144 linear groups.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "scale-search weight-elems×grid-pts/s + pack GB/s; % of HBM roofline, 1 MI355X"
+# MI355X published peaks and unit counts
+HBM_PEAK_GBPS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+VALU_LANE_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.32 T fp32 lane-ops/s (no packed math)
+# fp32 lane operations that one element x candidate needs in the weight score:
+# scale (mul), group max (max), v / step (mul by reciprocal), round (rndne),
+# residual v - q*step (fma), square-accumulate (fma)
+SEARCH_OPS_PER_ELEM_PT = 6
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs through the HIP runtime already loaded by torch."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e)
+
+    def ms(self, a: int, b: int) -> float:
+        assert self.hip.hipEventSynchronize(self.ev[b]) == 0
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        return out.value
+
+    def h(self, i: int) -> int:
+        return self.ev[i].value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def pack_bytes(d_out: int, d_in: int, G: int) -> int:
+    n = d_out * d_in
+    return 2 * n + n // 2 + 2 * n // G + n // (2 * G) + 4 * d_in
+
+
+def cpu_baseline_weight(W, X, G, budget_s: float):
+    """Times the CPU oracle on the same group: statistics over all tokens, then
+    search (20 points) + pack on consecutive row chunks until the time budget
+    or the rows run out; the step time is scaled to all rows."""
+    from oracle import awq_oracle as O
+    d_out, d_in = W.shape
+    t0, c0 = time.perf_counter(), time.process_time()
+    xm = O.act_stats(X)
+    t_stats = time.perf_counter() - t0
+    done, t_rows, chunk = 0, 0.0, 256
+    while done < d_out and t_stats + t_rows < budget_s:
+        Wr = W[done:done + chunk]
+        t1 = time.perf_counter()
+        _, _, s = O.search_scales([Wr], xm, G, 20)
+        O.quantize_pack(Wr, s, G)
+        t_rows += time.perf_counter() - t1
+        done += Wr.shape[0]
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    step_s = t_stats + t_rows * d_out / done
+    return {
+        "value": d_out * d_in * 20 / step_s,
+        "unit": "weight-elem*grid-pt/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"act_stats over all {X.shape[0]} tokens, search (20 points) + pack of {done} of {d_out} "
+                  f"rows, step time scaled to all rows ({wall:.1f} s wall)",
+    }
+
+
+def bench_weight(args, wl_name: str):
+    import numpy as np
+    import torch
+    import post_weight_quantization_awq_amd as A
+    import workloads as WL
+
+    wl = WL.WORKLOADS[wl_name]
+    grp = wl.groups[0]
+    G = args.group_size or wl.group_sizes[0]
+    parts_h, X_h = WL.host_group_inputs(wl, 0, 0)
+    W_h = np.concatenate(parts_h, axis=0)
+    dev = torch.device("cuda:0")
+    Ws = [torch.from_numpy(p).to(dev) for p in parts_h]
+    if X_h.dtype == np.uint16:
+        X = torch.from_numpy(X_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(X_h).to(dev)
+    d_out, d_in, T = grp.d_out, grp.d_in, X.shape[0]
+    n_w = d_out * d_in
+
+    # preallocated outputs and workspaces: the timed step allocates nothing
+    xm = torch.empty(d_in, dtype=torch.float32, device=dev)
+    ws_stats = A.workspace(A.act_stats_workspace_bytes(T, d_in), dev)
+    ws_search = A.workspace(A.search_workspace_bytes(d_out, d_in, 1, group_size=G), dev)
+    res = A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+                         torch.empty(d_in, device=dev), None, None)
+    packs = [(torch.empty((d_in, p.shape[0] // 8), dtype=torch.int32, device=dev),
+              torch.empty((d_in // G, p.shape[0]), dtype=torch.float16, device=dev),
+              torch.empty((d_in // G, p.shape[0] // 8), dtype=torch.int32, device=dev)) for p in Ws]
+    K = args.steps
+    ev = HipEvents(6 * K)
+
+    def step(i: int = -1):
+        if i >= 0:
+            A.set_timing_events(ev.h(6 * i), ev.h(6 * i + 1))
+        A.act_stats(X, x_mean=xm, ws=ws_stats)
+        if i >= 0:
+            A.set_timing_events(ev.h(6 * i + 2), ev.h(6 * i + 3))
+        A.search_scales(Ws, xm, group_size=G, ws=ws_search, out=res)
+        if i >= 0:
+            A.set_timing_events(ev.h(6 * i + 4), ev.h(6 * i + 5))
+        for p, o in zip(Ws, packs):
+            A.quantize_pack(p, G, res.best_s, out=o)
+        if i >= 0:
+            A.set_timing_events(None, None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    k_ms = {"act_stats": 0.0, "search_weight": 0.0, "quantize_pack": 0.0}
+    for i in range(K):
+        k_ms["act_stats"] += ev.ms(6 * i, 6 * i + 1) / K
+        k_ms["search_weight"] += ev.ms(6 * i + 2, 6 * i + 3) / K
+        k_ms["quantize_pack"] += ev.ms(6 * i + 4, 6 * i + 5) / K
+    ev.close()
+
+    elem_pts = n_w * 20
+    t_search = k_ms["search_weight"] * 1e-3
+    achieved_ops = SEARCH_OPS_PER_ELEM_PT * elem_pts / t_search / 1e12
+    pk_bytes = sum(pack_bytes(p.shape[0], d_in, G) for p in Ws)
+    out = {
+        "metric": METRIC,
+        "value": elem_pts / (ms_step * 1e-3),
+        "unit": "weight-elem*grid-pt/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl_name, "d_out": d_out, "d_in": d_in, "tokens": T, "group_size": G,
+                   "n_grid": 20, "score": "weight", "x_dtype": grp.x_dtype},
+        "search_elem_pts_per_s": elem_pts / t_search,
+        "search_hbm_equiv_GBps": 2.0 * elem_pts / t_search / 1e9,
+        "pack_GBps": pk_bytes / (k_ms["quantize_pack"] * 1e-3) / 1e9,
+        "act_stats_GBps": (2 * T * d_in + 4 * d_in) / (k_ms["act_stats"] * 1e-3) / 1e9,
+        "kernel_us": {k: v * 1e3 for k, v in k_ms.items()},
+        "roofline": {"bound": "alu", "achieved": achieved_ops, "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s",
+                     "frac": achieved_ops / VALU_LANE_OPS_PEAK_T, "traffic": None,
+                     "kernel": "search_weight_kernel",
+                     "ops_per_elem_pt": SEARCH_OPS_PER_ELEM_PT},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_weight(W_h, X_h, G, args.cpu_seconds)
+    return out
+
+
+def bench_output(args, wl_name: str):
+    import numpy as np
+    import torch
+    import post_weight_quantization_awq_amd as A
+    import workloads as WL
+
+    wl = WL.WORKLOADS[wl_name]
+    G = args.group_size or wl.group_sizes[0]
+    dev = torch.device("cuda:0")
+    groups = []
+    for gi, grp in enumerate(wl.groups):
+        parts = [WL.torch_weight(wl.seed(0, gi, 1 + 1000 * p), r, grp.d_in, dev) for p, r in enumerate(grp.parts)]
+        if grp.x_from == "mlp_down":
+            Xsrc = groups[gi - 1][1]
+            X = WL.torch_down_input(Xsrc, groups[gi - 1][0][0], groups[gi - 1][0][1])
+        else:
+            X = WL.torch_activations(wl.seed(0, gi, 2), grp.T, grp.d_in, dev)
+        groups.append((parts, X, grp))
+    torch.cuda.synchronize()
+    plans = []
+    for parts, X, grp in groups:
+        d_out = grp.d_out
+        xm = torch.empty(grp.d_in, dtype=torch.float32, device=dev)
+        ws_stats = A.workspace(A.act_stats_workspace_bytes(X.shape[0], grp.d_in), dev)
+        ws = A.workspace(A.search_workspace_bytes(d_out, grp.d_in, X.shape[0], group_size=G, score="output",
+                                                  n_clip=wl.n_clip), dev)
+        res = A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+                             torch.empty(grp.d_in, device=dev),
+                             torch.empty(d_out, device=dev) if wl.n_clip else None, None)
+        packs = [(torch.empty((grp.d_in, p.shape[0] // 8), dtype=torch.int32, device=dev),
+                  torch.empty((grp.d_in // G, p.shape[0]), dtype=torch.float16, device=dev),
+                  torch.empty((grp.d_in // G, p.shape[0] // 8), dtype=torch.int32, device=dev)) for p in parts]
+        plans.append((parts, X, grp, xm, ws_stats, ws, res, packs))
+    K = args.steps
+    n_pl = len(plans)
+    ev = HipEvents(2 * n_pl * K)
+
+    def step(k: int = -1):
+        for i, (parts, X, grp, xm, ws_stats, ws, res, packs) in enumerate(plans):
+            A.act_stats(X, x_mean=xm, ws=ws_stats)
+            if k >= 0:
+                A.set_timing_events(ev.h(2 * (k * n_pl + i)), ev.h(2 * (k * n_pl + i) + 1))
+            A.search_scales(parts, xm, group_size=G, score="output", X=X, n_clip=wl.n_clip, ws=ws, out=res)
+            if k >= 0:
+                A.set_timing_events(None, None)
+            off = 0
+            for p, o in zip(parts, packs):
+                clip = res.clip[off:off + p.shape[0]] if res.clip is not None else None
+                A.quantize_pack(p, G, res.best_s, clip, out=o)
+                off += p.shape[0]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(K):
+        step(k)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t1) * 1e3 / K
+    gemm_ms = [sum(ev.ms(2 * (k * n_pl + i), 2 * (k * n_pl + i) + 1) for k in range(K)) / K for i in range(n_pl)]
+    ev.close()
+    n_elem_pts = sum(g.d_out * g.d_in for _, _, g, *_ in plans) * 20
+    flops_alpha = [2.0 * X.shape[0] * g.d_out * g.d_in * 20 for _, X, g, *_ in plans]
+    # the events bracket the alpha-search GEMMs (with their dW builds when chunked)
+    tflops = sum(flops_alpha) / (sum(gemm_ms) * 1e-3) / 1e12
+    n_gemm = 20 + (wl.n_clip or 0)
+    total_flops = sum(2.0 * X.shape[0] * g.d_out * g.d_in * n_gemm for _, X, g, *_ in plans)
+    return {
+        "metric": METRIC,
+        "value": n_elem_pts / (ms_step * 1e-3),
+        "unit": "weight-elem*grid-pt/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16-mfma/f32", "data": "synthetic",
+        "config": {"workload": wl_name, "groups": [[g.name, g.d_out, g.d_in, X.shape[0]] for _, X, g, *_ in plans],
+                   "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip},
+        "step_TFLOPs_algorithmic": total_flops / (ms_step * 1e-3) / 1e12,
+        "gemm_ms": gemm_ms,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": None, "kernel": "gemm_sq_kernel"},
+    }
+
+
+def bench_sweep(args):
+    import torch
+    import post_weight_quantization_awq_amd as A
+    import workloads as WL
+
+    wl = WL.WORKLOADS["qwen3_8b_sweep"]
+    dev = torch.device("cuda:0")
+    blocks = args.blocks
+    # one calibration input per group kind (the 36 blocks share their statistics' shape)
+    Xs = [WL.torch_activations(wl.seed(0, gi, 2), g.T, g.d_in, dev) for gi, g in enumerate(wl.groups)]
+    Ws = []
+    for b in range(blocks):
+        Ws.append([[WL.torch_weight(wl.seed(b, gi, 1 + 1000 * p), r, g.d_in, dev) for p, r in enumerate(g.parts)]
+                   for gi, g in enumerate(wl.groups)])
+    torch.cuda.synchronize()
+    out_all = {}
+    for G in wl.group_sizes:
+        xms = [torch.empty(g.d_in, device=dev) for g in wl.groups]
+        ws_stats = [A.workspace(A.act_stats_workspace_bytes(g.T, g.d_in), dev) for g in wl.groups]
+        ws = [A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G), dev) for g in wl.groups]
+        res = [A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+                              torch.empty(g.d_in, device=dev), None, None) for g in wl.groups]
+        packs = [[(torch.empty((g.d_in, r // 8), dtype=torch.int32, device=dev),
+                   torch.empty((g.d_in // G, r), dtype=torch.float16, device=dev),
+                   torch.empty((g.d_in // G, r // 8), dtype=torch.int32, device=dev)) for r in g.parts]
+                 for g in wl.groups]
+        K = args.steps
+        per = 6 * 4 * blocks
+        ev = HipEvents(per * K)
+
+        def step(k=-1):
+            n = k * per
+            for b in range(blocks):
+                for gi, g in enumerate(wl.groups):
+                    if k >= 0:
+                        A.set_timing_events(ev.h(n), ev.h(n + 1))
+                    A.act_stats(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi])
+                    if k >= 0:
+                        A.set_timing_events(ev.h(n + 2), ev.h(n + 3))
+                    A.search_scales(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi])
+                    if k >= 0:
+                        A.set_timing_events(ev.h(n + 4), ev.h(n + 5))
+                    for p, o in zip(Ws[b][gi], packs[gi]):
+                        A.quantize_pack(p, G, res[gi].best_s, out=o)
+                    n += 6
+            if k >= 0:
+                A.set_timing_events(None, None)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for k in range(K):
+            step(k)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t1) * 1e3 / K
+        sums = [0.0, 0.0, 0.0]
+        for n in range(0, per * K, 6):
+            sums[0] += ev.ms(n, n + 1)
+            sums[1] += ev.ms(n + 2, n + 3)
+            sums[2] += ev.ms(n + 4, n + 5)
+        ev.close()
+        sums = [s / args.steps for s in sums]
+        n_w = blocks * sum(g.d_out * g.d_in for g in wl.groups)
+        pk = blocks * sum(pack_bytes(r, g.d_in, G) for g in wl.groups for r in g.parts)
+        xb = blocks * sum(2 * g.T * g.d_in for g in wl.groups)
+        out_all[f"G{G}"] = {
+            "ms_per_step": ms_step, "elem_pts_per_s": n_w * 20 / (ms_step * 1e-3),
+            "search_ms": sums[1], "search_elem_pts_per_s": n_w * 20 / (sums[1] * 1e-3),
+            "search_hbm_equiv_GBps": 2.0 * n_w * 20 / (sums[1] * 1e-3) / 1e9,
+            "search_alu_frac": SEARCH_OPS_PER_ELEM_PT * n_w * 20 / (sums[1] * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T,
+            "pack_ms": sums[2], "pack_GBps": pk / (sums[2] * 1e-3) / 1e9,
+            "act_stats_ms": sums[0], "act_stats_GBps": xb / (sums[0] * 1e-3) / 1e9,
+        }
+    n_w = blocks * sum(g.d_out * g.d_in for g in wl.groups)
+    first = out_all[f"G{wl.group_sizes[0]}"]
+    return {
+        "metric": METRIC, "value": first["elem_pts_per_s"], "unit": "weight-elem*grid-pt/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": first["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_sweep", "blocks": blocks, "weights": n_w, "n_grid": 20,
+                   "group_sizes": list(wl.group_sizes), "score": "weight"},
+        "per_group_size": out_all,
+        "roofline": {"bound": "alu", "achieved": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T,
+                     "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s", "frac": first["search_alu_frac"],
+                     "traffic": None, "kernel": "search_weight_kernel"},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="q_proj_4096x4096",
+                    choices=["single_linear_256x512", "q_proj_4096x4096", "qkv_6144x4096_output",
+                             "mlp_output_clip", "qwen3_8b_sweep"])
+    ap.add_argument("--group-size", type=int, default=None)
+    ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the AWQ search and pack run per linear group on a single device; "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from post_weight_quantization_awq_amd import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        from post_weight_quantization_awq_amd import build
+        build.build()
+    torch.cuda.set_device(0)
+    if args.workload in ("single_linear_256x512", "q_proj_4096x4096"):
+        out = bench_weight(args, args.workload)
+    elif args.workload == "qwen3_8b_sweep":
+        out = bench_sweep(args)
+    else:
+        out = bench_output(args, args.workload)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

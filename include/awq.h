@@ -108,9 +108,11 @@ awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in
  *
  * x_mean: fp32 [d_in] (non-negative, finite); S: fp32 [n_grid, d_in].
  * Row 0 is exactly 1.0 (alpha = 0 is plain round-to-nearest).
+ * ws: awq_candidate_scales_workspace(d_in, n_grid) bytes, 8-byte aligned.
  * ------------------------------------------------------------------------- */
+awq_status awq_candidate_scales_workspace(int64_t d_in, int32_t n_grid, size_t* bytes /* [host] */);
 awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_grid, double s_min,
-                                float* S, void* stream);
+                                float* S, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * awq_search_scales -- grid search of alpha for one input-sharing group.
@@ -190,6 +192,17 @@ awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t
 awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                               int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
                               void* out, int32_t out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_set_timing_events -- benchmark hook.  While set, every later call on
+ * this host thread records `before` and `after` (hipEvent_t handles passed as
+ * void*, created by the caller) on the call's stream immediately around its
+ * main kernel launches: the partial-sum kernel of awq_act_stats; the search
+ * kernel (weight score) or the chunked dW-build + GEMM launches (output score)
+ * of awq_search_scales; the pack kernel of awq_quantize_pack.  Pass NULL, NULL
+ * to clear.  The library records the events and nothing else.
+ * ------------------------------------------------------------------------- */
+awq_status awq_set_timing_events(void* before, void* after);
 
 /* Message of the last failing call on this host thread ("" if none). */
 const char* awq_last_error(void);

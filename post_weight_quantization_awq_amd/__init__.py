@@ -34,9 +34,9 @@ AWQ_SCORE_WEIGHT, AWQ_SCORE_OUTPUT = 0, 1
 STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_EINVAL", 2: "AWQ_ESHAPE", 3: "AWQ_EDTYPE",
                 4: "AWQ_EWORKSPACE", 5: "AWQ_EALIGN", 6: "AWQ_EHIP"}
 
-EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales",
+EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales_workspace", "awq_candidate_scales",
             "awq_search_workspace", "awq_search_scales", "awq_quantize_pack",
-            "awq_unpack_dequant", "awq_last_error", "awq_abi_version")
+            "awq_unpack_dequant", "awq_last_error", "awq_abi_version", "awq_set_timing_events")
 
 
 class AwqError(RuntimeError):
@@ -67,12 +67,14 @@ def _load() -> ctypes.CDLL:
     sig = {
         "awq_act_stats_workspace": [I64, I64, PSZ],
         "awq_act_stats": [P, I32, I64, I64, I64, F32, I32, P, P, SZ, P],
-        "awq_candidate_scales": [P, I64, I32, F64, P, P],
+        "awq_candidate_scales_workspace": [I64, I32, PSZ],
+        "awq_candidate_scales": [P, I64, I32, F64, P, P, SZ, P],
         "awq_search_workspace": [ctypes.POINTER(SearchCfg), I64, I64, I64, PSZ],
         "awq_search_scales": [ctypes.POINTER(SearchCfg), ctypes.POINTER(WGroup), I64, P, P, I32, I64, I64,
                               P, P, P, P, P, P, SZ, P],
         "awq_quantize_pack": [P, I64, I64, I32, P, P, P, P, P, P],
         "awq_unpack_dequant": [P, P, P, I64, I64, I32, P, P, I32, P],
+        "awq_set_timing_events": [P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -162,7 +164,11 @@ def candidate_scales(x_mean: torch.Tensor, n_grid: int = 20, s_min: float = 1e-4
     _dev(x_mean, "x_mean")
     d_in = x_mean.numel()
     S = torch.empty((n_grid, d_in), dtype=torch.float32, device=x_mean.device)
-    _check(lib().awq_candidate_scales(_ptr(x_mean), d_in, n_grid, s_min, _ptr(S), _stream(stream)))
+    n = ctypes.c_size_t()
+    _check(lib().awq_candidate_scales_workspace(d_in, n_grid, ctypes.byref(n)))
+    ws = workspace(n.value, x_mean.device)
+    _check(lib().awq_candidate_scales(_ptr(x_mean), d_in, n_grid, s_min, _ptr(S), _ptr(ws), ws.numel(),
+                                      _stream(stream)))
     return S
 
 
@@ -265,5 +271,10 @@ def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional
     return out
 
 
-__all__ = ["AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
+def set_timing_events(before: Optional[int], after: Optional[int]) -> None:
+    """Record raw hipEvent_t handles around the main kernel of every later call (None clears)."""
+    _check(lib().awq_set_timing_events(before, after))
+
+
+__all__ = ["set_timing_events", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
            "search_workspace_bytes", "act_stats_workspace_bytes", "SearchResult", "lib", "LIB_PATH"]

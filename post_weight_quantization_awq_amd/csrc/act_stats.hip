@@ -92,15 +92,27 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
   }
 }
 
-__global__ void act_stats_final_kernel(const double* __restrict__ part, int64_t n_split, int64_t d_in,
-                                       double inv_count, int accumulate, float* __restrict__ x_mean) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= d_in) return;
+// 32 channels x 8 split-slices per block: each thread sums every 8th split
+// partial of one channel, the 8 slice sums are then added in a fixed order.
+__global__ __launch_bounds__(256) void act_stats_final_kernel(const double* __restrict__ part, int64_t n_split,
+                                                             int64_t d_in, double inv_count, int accumulate,
+                                                             float* __restrict__ x_mean) {
+  const int lane = threadIdx.x & 31, slice = threadIdx.x >> 5;
+  const int64_t i = (int64_t)blockIdx.x * 32 + lane;
   double s = 0.0;
-  for (int64_t p = 0; p < n_split; ++p) s += part[p * d_in + i];
-  double v = s * inv_count;
-  if (accumulate) v += (double)x_mean[i];
-  x_mean[i] = (float)v;
+  if (i < d_in)
+    for (int64_t p = slice; p < n_split; p += 8) s += part[p * d_in + i];
+  __shared__ double red[8][32];
+  red[slice][lane] = s;
+  __syncthreads();
+  if (slice == 0 && i < d_in) {
+    double t = red[0][lane];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) t += red[q][lane];
+    double v = t * inv_count;
+    if (accumulate) v += (double)x_mean[i];
+    x_mean[i] = (float)v;
+  }
 }
 
 void act_stats_plan(int64_t T, int64_t d_in, int64_t* n_split, int64_t* rows_per_split) {
@@ -138,7 +150,7 @@ hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, i
       else act_stats_partial_kernel<false, false><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
     }
   }
-  act_stats_final_kernel<<<(unsigned)((d_in + 255) / 256), 256, 0, stream>>>(
+  act_stats_final_kernel<<<(unsigned)((d_in + 31) / 32), 256, 0, stream>>>(
       part, n_split, d_in, (double)inv_count, accumulate, x_mean);
   return hipGetLastError();
 }

@@ -15,6 +15,14 @@ using namespace awq;
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
+
+// records the timing events, if set, on `stream`
+void mark(bool before, hipStream_t stream) {
+  hipEvent_t e = before ? g_ev_before : g_ev_after;
+  if (e != nullptr) (void)hipEventRecord(e, stream);
+}
 
 awq_status fail(awq_status st, const char* fmt, ...) {
   va_list ap;
@@ -44,10 +52,10 @@ bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
 struct SearchPlan {
   bool output;
   int64_t n_blocks;     // weight score: search blocks
-  int64_t n_mt, n_nt;   // output score: GEMM tiles
+  int64_t T_pad, d_out_pad, K_pad, n_mt, ldc;  // output score: padded GEMM shapes, token tiles, partial ld
   int64_t n_x, n_db;    // output score: X max partials, dW max partials per candidate
   int cand_chunk;       // output score: candidates per dW chunk
-  size_t off_S, off_C2, off_part, off_x16, off_dw, off_colpart, off_xmax, off_dmax, off_sc, total;
+  size_t off_S, off_C2, off_cand, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, total;
 };
 
 constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
@@ -58,6 +66,10 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
   size_t off = 0;
   p.off_S = off;
   off += align256((size_t)cfg.n_grid * d_in * sizeof(float));
+  p.off_cand = off;
+  off += align256(candidates_workspace_bytes(d_in, cfg.n_grid));
+  p.off_tot = off;
+  off += align256((size_t)kMaxGrid * sizeof(double));
   if (!p.output) {
     p.off_C2 = off;
     off += align256((size_t)cfg.n_grid * d_in * sizeof(float));
@@ -65,25 +77,23 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     p.off_part = off;
     off += align256((size_t)p.n_blocks * cfg.n_grid * sizeof(float));
   } else {
-    gemm_sq_shape(T, d_out, 0, &p.n_mt, &p.n_nt);
+    gemm_sq_pad(T, d_out, d_in, &p.T_pad, &p.d_out_pad, &p.K_pad);
+    p.n_mt = p.T_pad / 256;
     p.n_x = absmax_blocks(T);
     p.n_db = build_dw_blocks(cfg.group_size, d_out, d_in);
     const int max_c = cfg.n_grid > cfg.n_clip ? cfg.n_grid : cfg.n_clip;
-    const size_t per_cand = (size_t)d_out * d_in * sizeof(uint16_t);
-    int64_t chunk = (int64_t)(kDwBudget / (per_cand ? per_cand : 1));
+    p.ldc = (int64_t)max_c * p.d_out_pad;
+    const size_t per_cand = (size_t)p.d_out_pad * p.K_pad * sizeof(uint16_t);
+    int64_t chunk = (int64_t)(kDwBudget / per_cand);
     if (chunk > max_c) chunk = max_c;
     if (chunk < 1) chunk = 1;
     p.cand_chunk = (int)chunk;
     p.off_x16 = off;
-    off += align256((size_t)T * d_in * sizeof(uint16_t));
+    off += align256((size_t)p.T_pad * p.K_pad * sizeof(uint16_t));
     p.off_dw = off;
     off += align256(per_cand * chunk);
     p.off_part = off;
-    off += align256((size_t)cfg.n_grid * p.n_mt * p.n_nt * sizeof(float));
-    if (cfg.n_clip >= 2) {
-      p.off_colpart = off;
-      off += align256((size_t)cfg.n_clip * p.n_mt * d_out * sizeof(float));
-    }
+    off += align256((size_t)p.n_mt * p.ldc * sizeof(float));
     p.off_xmax = off;
     off += align256((size_t)p.n_x * sizeof(float));
     p.off_dmax = off;
@@ -117,6 +127,13 @@ extern "C" {
 
 const char* awq_last_error(void) { return g_err; }
 
+awq_status awq_set_timing_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return fail(AWQ_EINVAL, "set both events or neither");
+  g_ev_before = (hipEvent_t)before;
+  g_ev_after = (hipEvent_t)after;
+  return ok();
+}
+
 int32_t awq_abi_version(void) { return AWQ_ABI_VERSION; }
 
 // ---------------------------------------------------------------------------
@@ -143,19 +160,32 @@ awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   if (need > 0 && ((uintptr_t)ws & 7u)) return fail(AWQ_EALIGN, "ws not 8-byte aligned");
-  return hip_status(launch_act_stats(X, x_dtype == AWQ_BF16, T, d_in, ld_x, inv_count, accumulate ? 1 : 0,
-                                     x_mean, ws, (hipStream_t)stream),
-                    "awq_act_stats");
+  mark(true, (hipStream_t)stream);
+  hipError_t e = launch_act_stats(X, x_dtype == AWQ_BF16, T, d_in, ld_x, inv_count, accumulate ? 1 : 0, x_mean,
+                                  ws, (hipStream_t)stream);
+  mark(false, (hipStream_t)stream);
+  return hip_status(e, "awq_act_stats");
 }
 
 // ---------------------------------------------------------------------------
+awq_status awq_candidate_scales_workspace(int64_t d_in, int32_t n_grid, size_t* bytes) {
+  if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
+  if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
+  if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
+  *bytes = align256(candidates_workspace_bytes(d_in, n_grid));
+  return ok();
+}
+
 awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_grid, double s_min,
-                                float* S, void* stream) {
+                                float* S, void* ws, size_t ws_bytes, void* stream) {
   if (!x_mean || !S) return fail(AWQ_EINVAL, "x_mean / S is NULL");
   if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
   if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
   if (!(s_min > 0.0 && isfinite(s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
-  return hip_status(launch_candidates(x_mean, d_in, n_grid, s_min, S, nullptr, (hipStream_t)stream),
+  const size_t need = candidates_workspace_bytes(d_in, n_grid);
+  if (!ws || ws_bytes < need) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 7u) return fail(AWQ_EALIGN, "ws not 8-byte aligned");
+  return hip_status(launch_candidates(x_mean, d_in, n_grid, s_min, S, nullptr, ws, (hipStream_t)stream),
                     "awq_candidate_scales");
 }
 
@@ -218,12 +248,14 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   if (!plan.output) {
     float* C2 = (float*)(base + plan.off_C2);
     float* part = (float*)(base + plan.off_part);
-    if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, C2, s)) != hipSuccess)
+    if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, C2, base + plan.off_cand, s)) != hipSuccess)
       return hip_status(e, "candidates");
-    if ((e = launch_search_weight(cfg->group_size, parts, d_out, d_in, cfg->n_grid, S, C2, part, s)) != hipSuccess)
-      return hip_status(e, "search_weight");
-    if ((e = launch_select(part, plan.n_blocks, cfg->n_grid, cfg->n_grid, 1, 1.0, nullptr, err, best_idx, S,
-                           d_in, best_s, s)) != hipSuccess)
+    mark(true, s);
+    e = launch_search_weight(cfg->group_size, parts, d_out, d_in, cfg->n_grid, S, C2, part, s);
+    mark(false, s);
+    if (e != hipSuccess) return hip_status(e, "search_weight");
+    if ((e = launch_select(part, plan.n_blocks, cfg->n_grid, 1, plan.n_blocks, 1.0, nullptr,
+                           (double*)(base + plan.off_tot), err, best_idx, S, d_in, best_s, s)) != hipSuccess)
       return hip_status(e, "select");
     return ok();
   }
@@ -231,52 +263,60 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   const bool bf16 = x_dtype == AWQ_BF16;
   uint16_t* x16 = (uint16_t*)(base + plan.off_x16);
   uint16_t* dw = (uint16_t*)(base + plan.off_dw);
-  float* part = (float*)(base + plan.off_part);
+  float* colpart = (float*)(base + plan.off_part);
   float* xmax = (float*)(base + plan.off_xmax);
   float* dmax = (float*)(base + plan.off_dmax);
+  double* tot = (double*)(base + plan.off_tot);
   OutScales* sc_a = (OutScales*)(base + plan.off_sc);
   OutScales* sc_c = (OutScales*)(base + plan.off_sc + align256(sizeof(OutScales)));
-  const int64_t n_tiles = plan.n_mt * plan.n_nt;
   const int G = cfg->group_size;
-  if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, nullptr, s)) != hipSuccess)
+  const int64_t dop = plan.d_out_pad, kp = plan.K_pad;
+  if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, nullptr, base + plan.off_cand, s)) != hipSuccess)
     return hip_status(e, "candidates");
   if ((e = launch_prepare_x(X, bf16, T, d_in, ld_x, xmax, s)) != hipSuccess) return hip_status(e, "absmax(X)");
-  if ((e = launch_build_dw(G, parts, d_out, d_in, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax, nullptr,
-                           s)) != hipSuccess)
+  if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax,
+                           nullptr, s)) != hipSuccess)
     return hip_status(e, "build_dw(max)");
   if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, cfg->n_grid, sc_a, s)) != hipSuccess)
     return hip_status(e, "out_scales");
-  if ((e = launch_convert_x(X, bf16, T, d_in, ld_x, sc_a, x16, s)) != hipSuccess) return hip_status(e, "convert_x");
+  if ((e = launch_convert_x(X, bf16, T, d_in, ld_x, plan.T_pad, kp, sc_a, x16, s)) != hipSuccess)
+    return hip_status(e, "convert_x");
+  const bool one_chunk = plan.cand_chunk >= cfg->n_grid;
+  if (!one_chunk) mark(true, s);
   for (int c0 = 0; c0 < cfg->n_grid; c0 += plan.cand_chunk) {
     const int nc = (cfg->n_grid - c0) < plan.cand_chunk ? (cfg->n_grid - c0) : plan.cand_chunk;
-    if ((e = launch_build_dw(G, parts, d_out, d_in, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, nullptr, dw, s)) !=
+    if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, nullptr, dw, s)) !=
         hipSuccess)
       return hip_status(e, "build_dw");
-    if ((e = launch_gemm_sq(x16, T, d_in, dw, d_out, d_in, nc, 0, part + (size_t)c0 * n_tiles, s)) != hipSuccess)
-      return hip_status(e, "gemm_sq");
+    if (one_chunk) mark(true, s);
+    e = launch_gemm_sq(x16, plan.T_pad, kp, dw, (int64_t)nc * dop, colpart + (int64_t)c0 * dop, plan.ldc, s);
+    if (one_chunk) mark(false, s);
+    if (e != hipSuccess) return hip_status(e, "gemm_sq");
   }
-  if ((e = launch_select(part, n_tiles, cfg->n_grid, 1, n_tiles, 1.0 / ((double)T * (double)d_out), sc_a->inv,
-                         err, best_idx, S, d_in, best_s, s)) != hipSuccess)
-    return hip_status(e, "select");
+  if (!one_chunk) mark(false, s);
+  if ((e = launch_reduce_cols(colpart, plan.n_mt, plan.ldc, d_out, dop, cfg->n_grid, 1.0 / ((double)T * (double)d_out),
+                              sc_a, tot, s)) != hipSuccess)
+    return hip_status(e, "reduce_cols");
+  if ((e = launch_argmin(tot, cfg->n_grid, err, best_idx, S, d_in, best_s, s)) != hipSuccess)
+    return hip_status(e, "argmin");
   if (cfg->n_clip >= 2) {
-    float* colpart = (float*)(base + plan.off_colpart);
     const int nclip = cfg->n_clip;
-    if ((e = launch_build_dw(G, parts, d_out, d_in, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0, nullptr,
-                             dmax, nullptr, s)) != hipSuccess)
+    if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0,
+                             nullptr, dmax, nullptr, s)) != hipSuccess)
       return hip_status(e, "build_dw(clip max)");
     if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, nclip, sc_c, s)) != hipSuccess)
       return hip_status(e, "out_scales(clip)");
     for (int c0 = 0; c0 < nclip; c0 += plan.cand_chunk) {
       const int nc = (nclip - c0) < plan.cand_chunk ? (nclip - c0) : plan.cand_chunk;
-      if ((e = launch_build_dw(G, parts, d_out, d_in, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0, sc_c,
+      if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0, sc_c,
                                nullptr, dw, s)) != hipSuccess)
         return hip_status(e, "build_dw(clip)");
-      if ((e = launch_gemm_sq(x16, T, d_in, dw, d_out, d_in, nc, 1, colpart + (size_t)c0 * plan.n_mt * d_out, s)) !=
+      if ((e = launch_gemm_sq(x16, plan.T_pad, kp, dw, (int64_t)nc * dop, colpart + (int64_t)c0 * dop, plan.ldc, s)) !=
           hipSuccess)
         return hip_status(e, "gemm_sq(clip)");
     }
-    if ((e = launch_clip_select(colpart, plan.n_mt, d_out, nclip, cfg->clip_lo, sc_c, clip, clip_err, s)) !=
-        hipSuccess)
+    if ((e = launch_clip_select(colpart, plan.n_mt, plan.ldc, d_out, dop, nclip, cfg->clip_lo, sc_c, clip, clip_err,
+                                s)) != hipSuccess)
       return hip_status(e, "clip_select");
   }
   return ok();
@@ -296,9 +336,11 @@ awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t
   if (s && !aligned16(s)) return fail(AWQ_EALIGN, "s not 16-byte aligned");
   if (((uintptr_t)qweight & 3u) || (qzeros && ((uintptr_t)qzeros & 3u)) || (clip && ((uintptr_t)clip & 3u)))
     return fail(AWQ_EALIGN, "qweight / qzeros / clip not 4-byte aligned");
-  return hip_status(launch_quantize_pack((const uint16_t*)W, d_out, d_in, group_size, s, clip, qweight, scales,
-                                         qzeros, (hipStream_t)stream),
-                    "awq_quantize_pack");
+  mark(true, (hipStream_t)stream);
+  hipError_t e = launch_quantize_pack((const uint16_t*)W, d_out, d_in, group_size, s, clip, qweight, scales, qzeros,
+                                      (hipStream_t)stream);
+  mark(false, (hipStream_t)stream);
+  return hip_status(e, "awq_quantize_pack");
 }
 
 awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, int64_t d_out,

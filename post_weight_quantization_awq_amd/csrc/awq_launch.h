@@ -17,11 +17,13 @@ hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, i
                             float inv_count, int accumulate, float* x_mean, void* ws,
                             hipStream_t stream);
 
-// candidate scale table S [n_grid, d_in] and, if C2 != nullptr, (x/s)^2 [n_grid, d_in]
+// candidate scale table S [n_grid, d_in] and, if C2 != nullptr, (x/s)^2 [n_grid, d_in];
+// ws: candidates_workspace_bytes(d_in, n_grid) bytes (8-byte aligned)
+size_t candidates_workspace_bytes(int64_t d_in, int n_grid);
 hipError_t launch_candidates(const float* x_mean, int64_t d_in, int n_grid, double s_min, float* S,
-                             float* C2, hipStream_t stream);
+                             float* C2, void* ws, hipStream_t stream);
 
-// weight-score search: per-block partial errors [n_blocks, n_grid]
+// weight-score search: per-block partial errors, candidate-major [n_grid, n_blocks]
 int64_t search_weight_blocks(int group_size, int64_t d_out, int64_t d_in);
 hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_out, int64_t d_in,
                                 int n_grid, const float* S, const float* C2, float* partials,
@@ -30,8 +32,12 @@ hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_o
 // reduce partials p[b * stride_b + c * stride_c] over b (fixed order, fp64) ->
 // err [n_cand] (times `scale`, and times cand_scale[c] when given), first-minimum
 // index -> best_idx, best_s = S[best]
+// first minimum of tot [n_cand] -> err (fp32), best_idx, best_s = S[best]
+hipError_t launch_argmin(const double* tot, int n_cand, float* err, int32_t* best_idx, const float* S, int64_t d_in,
+                         float* best_s, hipStream_t stream);
+// tot: [n_cand] fp64 scratch
 hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, int64_t stride_b,
-                         int64_t stride_c, double scale, const double* cand_scale, float* err,
+                         int64_t stride_c, double scale, const double* cand_scale, double* tot, float* err,
                          int32_t* best_idx, const float* S, int64_t d_in, float* best_s,
                          hipStream_t stream);
 
@@ -44,26 +50,29 @@ hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 // from the dW partial maxima dmax [n_cand, n_d]
 hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
                              OutScales* sc, hipStream_t stream);
-// X16 [T, d_in] = fp16(X * xs)
-hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, const OutScales* sc,
-                            uint16_t* X16, hipStream_t stream);
+// padded GEMM shapes: T_pad, d_out_pad multiples of 256, K_pad of 64
+void gemm_sq_pad(int64_t T, int64_t d_out, int64_t d_in, int64_t* T_pad, int64_t* d_out_pad, int64_t* K_pad);
+// X16 [T_pad, K_pad] = fp16(X * xs), zero padded
+hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,
+                            int64_t K_pad, const OutScales* sc, uint16_t* X16, hipStream_t stream);
 // dW of candidates c = cand0 .. cand0+n_cand-1 (mode 0: s = S[c]; mode 1: s = s_best, clip ratio c):
-//   dw == nullptr: per-block max |dW_c| -> dmax [n_cand, build_dw_blocks()]
-//   dw != nullptr: dw[c - cand0] = fp16(dW_c * sc->ds[c])
+//   dw == nullptr: per-block max |dW_c| -> dmax [n_cand, build_dw_blocks(G, d_out, d_in)]
+//   dw != nullptr: dw[c - cand0] = fp16(dW_c * sc->ds[c]), [d_out_pad, K_pad] each, zero padded
 int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in);
-hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, int64_t d_in,
-                           int n_cand, int mode, const float* S, const float* s_best, int n_clip,
+hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, int64_t d_in, int64_t d_out_pad,
+                           int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best, int n_clip,
                            float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
                            hipStream_t stream);
-// gemm-of-squares on fp16 operands: for every candidate c, Y = X16 dW[c]^T ([T, d_out]),
-//   per_col = 0: partials [n_cand, n_tiles] of sum(Y^2) per tile
-//   per_col = 1: partials [n_cand, n_mtiles, d_out] of column sums of Y^2
-void gemm_sq_shape(int64_t T, int64_t d_out, int per_col, int64_t* n_mtiles, int64_t* n_ntiles);
-hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T, int64_t ld_x, const uint16_t* dw, int64_t d_out,
-                          int64_t d_in, int n_cand, int per_col, float* partials, hipStream_t stream);
-// per-row argmin over clip ratios from column partials [n_clip, n_mtiles, d_out] (times sc->inv[j])
-hipError_t launch_clip_select(const float* colpart, int64_t n_mtiles, int64_t d_out, int n_clip,
-                              float clip_lo, const OutScales* sc, float* clip, float* clip_err,
+// gemm of squares on fp16 operands: Y = X16 [T_pad, K_pad] dw^T (dw: [n_cols, K_pad]);
+// colpart[mt * ldc + n] = sum over the 256 tokens of tile mt of Y[t, n]^2
+hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
+                          float* colpart, int64_t ldc, hipStream_t stream);
+// tot[c] = scale * sc->inv[c] * sum_mt sum_{o < d_out} colpart[mt * ldc + c * d_out_pad + o]
+hipError_t launch_reduce_cols(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
+                              int n_cand, double scale, const OutScales* sc, double* tot, hipStream_t stream);
+// per-row argmin over clip ratios: E[o, j] = sc->inv[j] * sum_mt colpart[mt * ldc + j * d_out_pad + o]
+hipError_t launch_clip_select(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
+                              int n_clip, float clip_lo, const OutScales* sc, float* clip, float* clip_err,
                               hipStream_t stream);
 
 // quantize + pack, unpack + dequant

@@ -4,9 +4,11 @@
 // divided by sqrt(max(s) * min(s)) so the scales stay centred near 1.
 // "Weight-Only Quantization: GPTQ and AWQ", section 5 (AWQ): s = |X|^alpha.
 //
-// One block per grid point; the values are evaluated in fp64 and rounded once
-// to fp32.  alpha = 0 is special-cased (x^0 = 1 for every x, including 0), so
-// row 0 is exactly 1.0 and candidate 0 is plain round-to-nearest.  For the
+// Two fully parallel passes over (grid point, channel): the first evaluates
+// t = max(x^alpha, s_min) in fp64 and keeps the extrema per block, the second
+// evaluates t again, normalises and rounds once to fp32.  alpha = 0 is
+// special-cased (x^0 = 1 for every x, including 0), so row 0 is exactly 1.0
+// and candidate 0 is plain round-to-nearest.  For the
 // weight score the kernel also stores (x / s)^2 in fp32, the per-column weight
 // of the squared error in the scaled domain: (w - q*step/s) * x = (v - q*step) * x/s.
 #include "awq_device.h"
@@ -19,43 +21,79 @@ __device__ __forceinline__ double cand_t(float x, int k, double alpha, double s_
   return t > s_min ? t : s_min;
 }
 
-__global__ __launch_bounds__(256) void candidates_kernel(const float* __restrict__ x_mean, int64_t d_in,
-                                                         int n_grid, double s_min, float* __restrict__ S,
-                                                         float* __restrict__ C2) {
-  const int k = blockIdx.x;
+constexpr int kCandThreads = 256;
+
+// pass 1: per-block max / min of t[k, i]
+__global__ __launch_bounds__(kCandThreads) void cand_ext_kernel(const float* __restrict__ x_mean, int64_t d_in,
+                                                               int n_grid, double s_min, double* __restrict__ bmax,
+                                                               double* __restrict__ bmin) {
+  const int k = blockIdx.y;
   const double alpha = (double)k / (double)n_grid;
-  double tmax = 0.0, tmin = __builtin_inf();
-  for (int64_t i = threadIdx.x; i < d_in; i += blockDim.x) {
-    double t = cand_t(x_mean[i], k, alpha, s_min);
-    tmax = t > tmax ? t : tmax;
-    tmin = t < tmin ? t : tmin;
+  const int64_t i = (int64_t)blockIdx.x * kCandThreads + threadIdx.x;
+  double vmax = 0.0, vmin = __builtin_inf();
+  if (i < d_in) {
+    vmax = cand_t(x_mean[i], k, alpha, s_min);
+    vmin = vmax;
   }
-  __shared__ double smax[256], smin[256];
-  smax[threadIdx.x] = tmax;
-  smin[threadIdx.x] = tmin;
+  __shared__ double smax[kCandThreads], smin[kCandThreads];
+  smax[threadIdx.x] = vmax;
+  smin[threadIdx.x] = vmin;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
+  for (int w = kCandThreads / 2; w >= 1; w >>= 1) {
     if ((int)threadIdx.x < w) {
       smax[threadIdx.x] = smax[threadIdx.x] > smax[threadIdx.x + w] ? smax[threadIdx.x] : smax[threadIdx.x + w];
       smin[threadIdx.x] = smin[threadIdx.x] < smin[threadIdx.x + w] ? smin[threadIdx.x] : smin[threadIdx.x + w];
     }
     __syncthreads();
   }
-  const double norm = sqrt(smax[0] * smin[0]);
-  for (int64_t i = threadIdx.x; i < d_in; i += blockDim.x) {
-    const float x = x_mean[i];
-    const float s = (float)(cand_t(x, k, alpha, s_min) / norm);
-    S[(int64_t)k * d_in + i] = s;
-    if (C2) {
-      const float c = x / s;
-      C2[(int64_t)k * d_in + i] = c * c;
-    }
+  if (threadIdx.x == 0) {
+    bmax[(int64_t)k * gridDim.x + blockIdx.x] = smax[0];
+    bmin[(int64_t)k * gridDim.x + blockIdx.x] = smin[0];
   }
 }
 
-hipError_t launch_candidates(const float* x_mean, int64_t d_in, int n_grid, double s_min, float* S,
-                             float* C2, hipStream_t stream) {
-  candidates_kernel<<<n_grid, 256, 0, stream>>>(x_mean, d_in, n_grid, s_min, S, C2);
+// pass 2: norm_k = sqrt(max t * min t) from the block extrema; S = fp32(t / norm)
+__global__ __launch_bounds__(kCandThreads) void cand_s_kernel(const float* __restrict__ x_mean, int64_t d_in,
+                                                             int n_grid, double s_min,
+                                                             const double* __restrict__ bmax,
+                                                             const double* __restrict__ bmin, int n_blk,
+                                                             float* __restrict__ S, float* __restrict__ C2) {
+  const int k = blockIdx.y;
+  __shared__ double norm_sh;
+  if (threadIdx.x == 0) {
+    double mx = 0.0, mn = __builtin_inf();
+    for (int b = 0; b < n_blk; ++b) {
+      const double a = bmax[(int64_t)k * n_blk + b], c = bmin[(int64_t)k * n_blk + b];
+      mx = a > mx ? a : mx;
+      mn = c < mn ? c : mn;
+    }
+    norm_sh = sqrt(mx * mn);
+  }
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * kCandThreads + threadIdx.x;
+  if (i >= d_in) return;
+  const double alpha = (double)k / (double)n_grid;
+  const float s = (float)(cand_t(x_mean[i], k, alpha, s_min) / norm_sh);
+  S[(int64_t)k * d_in + i] = s;
+  if (C2) {
+    const float c = x_mean[i] / s;
+    C2[(int64_t)k * d_in + i] = c * c;
+  }
+}
+
+size_t candidates_workspace_bytes(int64_t d_in, int n_grid) {
+  const int64_t n_blk = (d_in + kCandThreads - 1) / kCandThreads;
+  return (size_t)n_grid * 2 * n_blk * sizeof(double);
+}
+
+hipError_t launch_candidates(const float* x_mean, int64_t d_in, int n_grid, double s_min, float* S, float* C2,
+                             void* ws, hipStream_t stream) {
+  const int n_blk = (int)((d_in + kCandThreads - 1) / kCandThreads);
+  double* bmax = (double*)ws;
+  double* bmin = bmax + (int64_t)n_grid * n_blk;
+  dim3 grid((unsigned)n_blk, (unsigned)n_grid);
+  cand_ext_kernel<<<grid, kCandThreads, 0, stream>>>(x_mean, d_in, n_grid, s_min, bmax, bmin);
+  cand_s_kernel<<<grid, kCandThreads, 0, stream>>>(x_mean, d_in, n_grid, s_min, bmax, bmin, n_blk, S, C2);
   return hipGetLastError();
 }
 

@@ -10,18 +10,21 @@
 // so each candidate c costs one GEMM of X [T, d_in] with dW_c = W_hat_c - W
 // [d_out, d_in], and only the sum of squares of the product is kept:
 //   1. absmax + convert_x: X is copied once to fp16 scaled by a power of two
-//      (exact for bf16 inputs in range, overflow-free);
+//      (exact for bf16 inputs in range, overflow-free), padded with zeros to
+//      whole GEMM tiles;
 //   2. build_dw (max pass, then write pass): dW_c with the same bit-exact codes
 //      as the pack kernel, scaled by a power of two from its exact maximum and
 //      rounded to fp16 -- 3 more mantissa bits than bf16 at the same matrix-core
 //      rate, which keeps the relative error of the errors near 1e-4 even for
 //      a few tokens and rows (one pass over W per candidate, negligible next to
 //      the GEMM);
-//   3. gemm_sq: fp16 MFMA 32x32x16 GEMM, fp32 accumulation; the epilogue squares
-//      the tile and reduces it (whole tile, or per output column for the clip
-//      search), so the T x d_out product never reaches memory;
-//   4. select / clip_select: fixed-order fp64 sums of the tile partials, times
-//      the exact inverse of the squared operand scales.
+//   3. gemm_sq: fp16 MFMA 32x32x16 GEMM over all candidates of a chunk at once
+//      (their dW stacked along N), fp32 accumulation; the epilogue squares the
+//      tile and sums each column over the tile's tokens, so the T x d_out
+//      product never reaches memory;
+//   4. reduce_cols / clip_select: fixed-order fp64 sums of the column partials
+//      (per candidate, or per row and clip ratio), times the exact inverse of
+//      the squared operand scales.
 #include "awq_device.h"
 #include "awq_launch.h"
 
@@ -38,10 +41,12 @@ __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_lo) {
 
 // WRITE = false: per-block max |dW_c| -> dmax[(c - cand0) * gridDim.x + block]
 // WRITE = true:  dW16[c - cand0] = fp16(dW_c * ds[c])
+//   dW16 rows are d_out_pad apart per candidate and K_pad elements long; rows
+//   d_out .. d_out_pad-1 and columns d_in .. K_pad-1 are written as zeros.
 template <int G, bool WRITE>
 __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
-    const WParts P, int64_t d_out, int64_t d_in, int mode, const float* __restrict__ S,
-    const float* __restrict__ s_best, int n_clip, float clip_lo, int cand0,
+    const WParts P, int64_t d_out, int64_t d_in, int64_t d_out_pad, int64_t K_pad, int mode,
+    const float* __restrict__ S, const float* __restrict__ s_best, int n_clip, float clip_lo, int cand0,
     const OutScales* __restrict__ sc, float* __restrict__ dmax, uint16_t* __restrict__ dw) {
   constexpr int LPG = G / 16;
   constexpr int RS = kDwThreads / LPG;
@@ -101,10 +106,21 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
     }
   }
   if constexpr (WRITE) {
-    if (!valid) return;
-    uint4* dst = (uint4*)(dw + (int64_t)blockIdx.y * d_out * d_in + row * d_in + col);
+    if (row >= d_out_pad) return;
+    uint16_t* rowp = dw + (int64_t)blockIdx.y * d_out_pad * K_pad + row * K_pad;
+    uint4* dst = (uint4*)(rowp + col);
+    if (!valid) {
+      for (int j = 0; j < 8; ++j) outw[j] = 0u;
+    }
     dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
     dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+    if (K_pad > d_in && gcol == n_gcol - 1) {  // zero K padding (at most one group wide)
+      uint4* pad = (uint4*)(rowp + col + G);
+      if (col + G < K_pad) {
+        pad[0] = make_uint4(0u, 0u, 0u, 0u);
+        pad[1] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
   } else {
     mx = wave_max(mx);
     if ((tid & 63) == 0) red[tid >> 6] = mx;
@@ -122,16 +138,17 @@ int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in) {
   return (d_in / group_size) * ((d_out + rs - 1) / rs);
 }
 
-hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, int64_t d_in,
-                           int n_cand, int mode, const float* S, const float* s_best, int n_clip,
+hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, int64_t d_in, int64_t d_out_pad,
+                           int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best, int n_clip,
                            float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
                            hipStream_t stream) {
-  dim3 grid((unsigned)build_dw_blocks(group_size, d_out, d_in), (unsigned)n_cand);
+  // max pass: d_out rows; write pass: d_out_pad rows (zeros past d_out)
+  dim3 grid((unsigned)build_dw_blocks(group_size, dw == nullptr ? d_out : d_out_pad, d_in), (unsigned)n_cand);
 #define AWQ_DW(G)                                                                             \
   if (dw == nullptr) build_dw_kernel<G, false><<<grid, kDwThreads, 0, stream>>>(                \
-      parts, d_out, d_in, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw);               \
+      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw); \
   else build_dw_kernel<G, true><<<grid, kDwThreads, 0, stream>>>(                               \
-      parts, d_out, d_in, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw);
+      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw);
   switch (group_size) {
     case 32: AWQ_DW(32) break;
     case 64: AWQ_DW(64) break;
@@ -209,25 +226,28 @@ __global__ __launch_bounds__(256) void out_scales_kernel(const float* __restrict
   }
 }
 
+// X16 [T_pad, K_pad] = fp16(X * xs), zeros in rows >= T and columns >= d_in
 template <bool BF16>
 __global__ __launch_bounds__(256) void convert_x_kernel(const uint16_t* __restrict__ X, int64_t rows, int64_t cols,
-                                                       int64_t ld, const OutScales* __restrict__ sc,
-                                                       uint16_t* __restrict__ X16) {
+                                                       int64_t ld, int64_t rows_pad, int64_t cols_pad,
+                                                       const OutScales* __restrict__ sc, uint16_t* __restrict__ X16) {
   const float xs = sc->xs;
-  const int64_t chunks = cols / 8;
-  const int64_t n = rows * chunks;
+  const int64_t chunks = cols_pad / 8;
+  const int64_t n = rows_pad * chunks;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
     const int64_t r = idx / chunks, c = (idx % chunks) * 8;
-    const uint4 u = ld_nt(X + r * ld + c);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    uint32_t o[4];
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (r < rows && c < cols) {
+      const uint4 u = ld_nt(X + r * ld + c);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
-      const float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
-      o[j] = (uint32_t)f2h_bits(lo * xs) | ((uint32_t)f2h_bits(hi * xs) << 16);
+      for (int j = 0; j < 4; ++j) {
+        const float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
+        const float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
+        o[j] = (uint32_t)f2h_bits(lo * xs) | ((uint32_t)f2h_bits(hi * xs) << 16);
+      }
     }
-    *(uint4*)(X16 + r * cols + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)(X16 + r * cols_pad + c) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -247,147 +267,172 @@ hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* d
   return hipGetLastError();
 }
 
-hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, const OutScales* sc,
-                            uint16_t* X16, hipStream_t stream) {
-  const int64_t n = T * (d_in / 8);
+hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,
+                            int64_t K_pad, const OutScales* sc, uint16_t* X16, hipStream_t stream) {
+  const int64_t n = T_pad * (K_pad / 8);
   int64_t nb = (n + 255) / 256;
   if (nb > 8192) nb = 8192;
-  if (bf16) convert_x_kernel<true><<<(unsigned)nb, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, sc, X16);
-  else convert_x_kernel<false><<<(unsigned)nb, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, sc, X16);
+  if (bf16) convert_x_kernel<true><<<(unsigned)nb, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, T_pad, K_pad, sc, X16);
+  else convert_x_kernel<false><<<(unsigned)nb, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, T_pad, K_pad, sc, X16);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// 2. GEMM of squares: Y = X dW^T, keep sum(Y^2) per tile or per column.
-//    Block tile 128 (tokens) x 128 (output rows) x 64 (inputs), 4 waves in a
-//    2 x 2 arrangement, each wave 64 x 64 = 2 x 2 MFMA 32x32x16 tiles.
-//    Operands are K-contiguous in memory and in LDS (row stride padded to
-//    72 elements against bank conflicts); each lane feeds the MFMA 8
-//    consecutive K values of one row (A: token row, B: output row).
+// 2. GEMM of squares: Y = X16 dW^T over the concatenated candidates
+//    (N_total = n_cand * d_out_pad columns, each candidate padded to a multiple
+//    of the tile with zero rows; M and K padded likewise with zeros), and per
+//    column the sum over the block's 256 tokens of Y^2 -> colpart[mt][n].
+//
+//    Block tile 256 x 256 x 64, 8 waves (2 along M x 4 along N), wave tile
+//    128 x 64 = 4 x 2 MFMA 32x32x16 f16 tiles, fp32 accumulators.  Operands go
+//    global -> LDS with global_load_lds_dwordx4 (no register staging), two
+//    stages; 16-byte K-chunks are XOR-swizzled by row so that the fragment
+//    reads of 32 consecutive rows hit distinct banks.  The block order is
+//    remapped so that each XCD owns a contiguous range of tiles, walked in
+//    groups of 8 M-tiles: concurrent blocks of one XCD share A and B tiles in
+//    its L2.
 // ---------------------------------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kBK = 64, kLdsW = kBK + 8;
-constexpr int kGemmThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kGemmThreads = 512;
+constexpr int kGroupM = 8;
+constexpr int kXcds = 8;
 
-void gemm_sq_shape(int64_t T, int64_t d_out, int per_col, int64_t* n_mtiles, int64_t* n_ntiles) {
-  (void)per_col;
-  *n_mtiles = (T + kBM - 1) / kBM;
-  *n_ntiles = (d_out + kBN - 1) / kBN;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
+
+__device__ __forceinline__ void load_tile_lds(const uint16_t* __restrict__ src, int64_t ld, int64_t row0, int64_t k0,
+                                              uint16_t* lds_tile, int wave, int lane) {
+  // 256 rows x 64 K = 32 KiB = 32 wave-loads of 1 KiB (8 rows each); wave w issues 4.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int u = wave * 4 + q;
+    const int row = u * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ (lane >> 3);           // logical chunk stored at slot lane & 7
+    const uint16_t* g = src + (row0 + row) * ld + k0 + kc * 8;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)(lds_tile + u * 512), 16, 0, 0);
+  }
 }
 
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma32(const uint4 a, const uint4 b, f32x16 c) {
-  if constexpr (BF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+__device__ __forceinline__ uint4 frag(const uint16_t* lds_tile, int row, int kc) {
+  return *(const uint4*)(lds_tile + row * kBK + ((kc ^ (row & 7)) << 3));
 }
 
-template <bool BF16, int PER_COL>
-__global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(
-    const uint16_t* __restrict__ X, int64_t T, int64_t ldx, const uint16_t* __restrict__ DW,
-    int64_t N, int64_t K, int64_t n_mt, int64_t n_nt, float* __restrict__ partials) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLdsW];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdsW];
+__device__ __forceinline__ f32x16 mfma_f16(const uint4 a, const uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
+__global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                              const uint16_t* __restrict__ B, int64_t ldb,
+                                                              int64_t K, int64_t n_mt, int64_t n_nt,
+                                                              float* __restrict__ colpart, int64_t ldc) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kBM * kBK];  // [stage][A|B]
   __shared__ float red[2][kBN];
 
-  const int cand = blockIdx.y;
-  const uint16_t* B = DW + (int64_t)cand * N * K;
-  const int64_t nt = blockIdx.x % n_nt;
-  const int64_t mt = blockIdx.x / n_nt;
+  // XCD-contiguous, M-grouped tile order
+  const int64_t nblk = (int64_t)gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid % kXcds, pos = bid / kXcds;
+  const int64_t q = nblk / kXcds, r = nblk % kXcds;
+  const int64_t id = (xcd < r) ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+  const int64_t per_group = (int64_t)kGroupM * n_nt;
+  const int64_t first_m = (id / per_group) * kGroupM;
+  const int64_t gsz = (n_mt - first_m) < kGroupM ? (n_mt - first_m) : kGroupM;
+  const int64_t mt = first_m + (id % per_group) % gsz;
+  const int64_t nt = (id % per_group) / gsz;
   const int64_t m0 = mt * kBM, n0 = nt * kBN;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
-  f32x16 acc[2][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
+
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-  uint4 ra[4], rb[4];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kGemmThreads * i;
-      const int r = c >> 3, kc = c & 7;
-      const int64_t kk = k0 + kc * 8;
-      const int64_t gm = m0 + r, gn = n0 + r;
-      ra[i] = (gm < T && kk < K) ? *(const uint4*)(X + gm * ldx + kk) : zero4;
-      rb[i] = (gn < N && kk < K) ? *(const uint4*)(B + gn * K + kk) : zero4;
+  const int nk = (int)(K / kBK);
+  load_tile_lds(A, lda, m0, 0, lds[0][0], wave, lane);
+  load_tile_lds(B, ldb, n0, 0, lds[0][1], wave, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage kt have landed
+    __syncthreads();                 // ... and every wave's; stage kt^1 is free again
+    const int st = kt & 1;
+    if (kt + 1 < nk) {
+      load_tile_lds(A, lda, m0, (int64_t)(kt + 1) * kBK, lds[st ^ 1][0], wave, lane);
+      load_tile_lds(B, ldb, n0, (int64_t)(kt + 1) * kBK, lds[st ^ 1][1], wave, lane);
     }
-  };
-  gload(0);
-  for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-    __syncthreads();
+    const uint16_t* As = lds[st][0];
+    const uint16_t* Bs = lds[st][1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kGemmThreads * i;
-      const int r = c >> 3, kc = c & 7;
-      *(uint4*)(As + r * kLdsW + kc * 8) = ra[i];
-      *(uint4*)(Bs + r * kLdsW + kc * 8) = rb[i];
-    }
-    __syncthreads();
-    if (k0 + kBK < K) gload(k0 + kBK);
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int kc = 2 * ks + (lane >> 5);
+      uint4 a[4], b[2];
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      uint4 a[2], b[2];
+      for (int i = 0; i < 4; ++i) a[i] = frag(As, wm * 128 + i * 32 + (lane & 31), kc);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *(const uint4*)(As + (wm * 64 + i * 32 + (lane & 31)) * kLdsW + kk + (lane >> 5) * 8);
+      for (int j = 0; j < 2; ++j) b[j] = frag(Bs, wn * 64 + j * 32 + (lane & 31), kc);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *(const uint4*)(Bs + (wn * 64 + j * 32 + (lane & 31)) * kLdsW + kk + (lane >> 5) * 8);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<BF16>(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
     }
   }
 
-  if constexpr (PER_COL == 0) {
-    float sq = 0.0f;
+  // epilogue: column c of a 32x32 tile lives in lanes c and c + 32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j) {
+    float cs = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sq = __builtin_fmaf(acc[i][j][e], acc[i][j][e], sq);
-    sq = wave_sum(sq);
-    if (lane == 0) red[0][wave] = sq;
-    __syncthreads();
-    if (tid == 0)
-      partials[(int64_t)cand * (n_mt * n_nt) + blockIdx.x] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-  } else {
-    // D column of a 32x32 MFMA tile = lane % 32; lanes l and l + 32 hold other rows
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float cs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
-      cs += __shfl_xor(cs, 32, kWave);
-      if (lane < 32) red[wm][wn * 64 + j * 32 + lane] = cs;
-    }
-    __syncthreads();
-    if (tid < kBN && n0 + tid < N)
-      partials[((int64_t)cand * n_mt + mt) * N + n0 + tid] = red[0][tid] + red[1][tid];
+      for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
+    cs += __shfl_xor(cs, 32, kWave);
+    if (lane < 32) red[wm][wn * 64 + j * 32 + lane] = cs;
   }
+  __syncthreads();
+  if (tid < kBN) colpart[mt * ldc + n0 + tid] = red[0][tid] + red[1][tid];
 }
 
-hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T, int64_t ld_x, const uint16_t* dw, int64_t d_out,
-                          int64_t d_in, int n_cand, int per_col, float* partials, hipStream_t stream) {
-  int64_t n_mt, n_nt;
-  gemm_sq_shape(T, d_out, per_col, &n_mt, &n_nt);
-  dim3 grid((unsigned)(n_mt * n_nt), (unsigned)n_cand);
-  if (per_col) gemm_sq_kernel<false, 1><<<grid, kGemmThreads, 0, stream>>>(X16, T, ld_x, dw, d_out, d_in, n_mt, n_nt, partials);
-  else gemm_sq_kernel<false, 0><<<grid, kGemmThreads, 0, stream>>>(X16, T, ld_x, dw, d_out, d_in, n_mt, n_nt, partials);
+void gemm_sq_pad(int64_t T, int64_t d_out, int64_t d_in, int64_t* T_pad, int64_t* d_out_pad, int64_t* K_pad) {
+  *T_pad = (T + kBM - 1) / kBM * kBM;
+  *d_out_pad = (d_out + kBN - 1) / kBN * kBN;
+  *K_pad = (d_in + kBK - 1) / kBK * kBK;
+}
+
+hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
+                          float* colpart, int64_t ldc, hipStream_t stream) {
+  const int64_t n_mt = T_pad / kBM, n_nt = n_cols / kBN;
+  gemm_sq_kernel<<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(X16, K_pad, dw, K_pad, K_pad, n_mt, n_nt,
+                                                                      colpart, ldc);
+  return hipGetLastError();
+}
+
+// per-candidate totals: tot[c] = scale * inv[c] * sum_mt sum_{o < d_out} colpart[mt][c * d_out_pad + o]
+__global__ __launch_bounds__(256) void reduce_cols_kernel(const float* __restrict__ colpart, int64_t n_mt, int64_t ldc,
+                                                         int64_t d_out, int64_t d_out_pad, double scale,
+                                                         const OutScales* __restrict__ sc, double* __restrict__ tot) {
+  const int c = blockIdx.x;
+  double acc = 0.0;
+  for (int64_t o = threadIdx.x; o < d_out; o += 256) {
+    const float* p = colpart + (int64_t)c * d_out_pad + o;
+    for (int64_t mt = 0; mt < n_mt; ++mt) acc += (double)p[mt * ldc];
+  }
+  __shared__ double red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tot[c] = red[0] * scale * sc->inv[c];
+}
+
+hipError_t launch_reduce_cols(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
+                              int n_cand, double scale, const OutScales* sc, double* tot, hipStream_t stream) {
+  reduce_cols_kernel<<<n_cand, 256, 0, stream>>>(colpart, n_mt, ldc, d_out, d_out_pad, scale, sc, tot);
   return hipGetLastError();
 }
 
@@ -395,8 +440,8 @@ hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T, int64_t ld_x, const ui
 // 3. per-row clip selection: E[o, j] = sum over token tiles (fixed order, fp64);
 //    ratio of the first strict minimum over j = 0 (1.0) .. n_clip-1 (clip_lo).
 // ---------------------------------------------------------------------------
-__global__ void clip_select_kernel(const float* __restrict__ colpart, int64_t n_mt, int64_t d_out,
-                                   int n_clip, float clip_lo, const OutScales* __restrict__ sc,
+__global__ void clip_select_kernel(const float* __restrict__ colpart, int64_t n_mt, int64_t ldc, int64_t d_out,
+                                   int64_t d_out_pad, int n_clip, float clip_lo, const OutScales* __restrict__ sc,
                                    float* __restrict__ clip, float* __restrict__ clip_err) {
   const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (o >= d_out) return;
@@ -404,7 +449,7 @@ __global__ void clip_select_kernel(const float* __restrict__ colpart, int64_t n_
   double be = 0.0;
   for (int j = 0; j < n_clip; ++j) {
     double e = 0.0;
-    for (int64_t mt = 0; mt < n_mt; ++mt) e += (double)colpart[((int64_t)j * n_mt + mt) * d_out + o];
+    for (int64_t mt = 0; mt < n_mt; ++mt) e += (double)colpart[mt * ldc + (int64_t)j * d_out_pad + o];
     e *= sc->inv[j];
     if (clip_err != nullptr) clip_err[o * n_clip + j] = (float)e;
     if (j == 0 || e < be) { be = e; best = j; }
@@ -412,11 +457,11 @@ __global__ void clip_select_kernel(const float* __restrict__ colpart, int64_t n_
   clip[o] = clip_ratio(best, n_clip, clip_lo);
 }
 
-hipError_t launch_clip_select(const float* colpart, int64_t n_mt, int64_t d_out, int n_clip,
-                              float clip_lo, const OutScales* sc, float* clip, float* clip_err,
+hipError_t launch_clip_select(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
+                              int n_clip, float clip_lo, const OutScales* sc, float* clip, float* clip_err,
                               hipStream_t stream) {
-  clip_select_kernel<<<(unsigned)((d_out + 255) / 256), 256, 0, stream>>>(colpart, n_mt, d_out, n_clip,
-                                                                          clip_lo, sc, clip, clip_err);
+  clip_select_kernel<<<(unsigned)((d_out + 255) / 256), 256, 0, stream>>>(colpart, n_mt, ldc, d_out, d_out_pad,
+                                                                          n_clip, clip_lo, sc, clip, clip_err);
   return hipGetLastError();
 }
 

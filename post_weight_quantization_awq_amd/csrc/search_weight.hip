@@ -114,8 +114,8 @@ __global__ __launch_bounds__(kSearchThreads) void search_weight_kernel(
     if ((tid & 63) == 0) red[k][tid >> 6] = e;
   }
   __syncthreads();
-  if (tid < n_grid)
-    partials[(int64_t)blockIdx.x * n_grid + tid] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
+  if (tid < n_grid)  // candidate-major: partials[k * n_blocks + block]
+    partials[(int64_t)tid * gridDim.x + blockIdx.x] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
 }
 
 int64_t search_weight_blocks(int group_size, int64_t d_out, int64_t d_in) {
@@ -152,35 +152,38 @@ hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_o
 
 // ---------------------------------------------------------------------------
 // Selection ("AWQ architecture, in depth", "The scale search as code": keep the
-// candidate when err < best, i.e. the first minimum).  Partials are summed in
-// a fixed order in fp64; the winner's scale row is copied out.
+// candidate when err < best, i.e. the first minimum).  One block per candidate
+// sums its partials in a fixed order in fp64; one block then picks the first
+// minimum and copies the winner's scale row.
 // ---------------------------------------------------------------------------
-constexpr int kSelThreads = 1024;
+constexpr int kRedThreads = 256;
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ partials,
-                                                            int64_t n_blocks, int n_cand, int64_t stride_b,
-                                                            int64_t stride_c, double scale,
-                                                            const double* __restrict__ cand_scale,
+__global__ __launch_bounds__(kRedThreads) void reduce_cand_kernel(const float* __restrict__ partials,
+                                                                 int64_t n_blocks, int64_t stride_b,
+                                                                 int64_t stride_c, double scale,
+                                                                 const double* __restrict__ cand_scale,
+                                                                 double* __restrict__ tot) {
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* p = partials + (int64_t)c * stride_c;
+  double acc = 0.0;
+  for (int64_t b = tid; b < n_blocks; b += kRedThreads) acc += (double)p[b * stride_b];
+  __shared__ double red[kRedThreads];
+  red[tid] = acc;
+  __syncthreads();
+  for (int w = kRedThreads / 2; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) tot[c] = red[0] * scale * (cand_scale != nullptr ? cand_scale[c] : 1.0);
+}
+
+__global__ __launch_bounds__(kRedThreads) void argmin_kernel(const double* __restrict__ tot, int n_cand,
                                                             float* __restrict__ err, int32_t* __restrict__ best_idx,
                                                             const float* __restrict__ S, int64_t d_in,
                                                             float* __restrict__ best_s) {
-  __shared__ double tot[kMaxGrid];
-  __shared__ double red[kSelThreads];
   __shared__ int best_sh;
-  const int tid = threadIdx.x;
-  for (int c = 0; c < n_cand; ++c) {
-    double acc = 0.0;
-    for (int64_t b = tid; b < n_blocks; b += kSelThreads) acc += (double)partials[b * stride_b + c * stride_c];
-    red[tid] = acc;
-    __syncthreads();
-    for (int w = kSelThreads / 2; w >= 1; w >>= 1) {
-      if (tid < w) red[tid] += red[tid + w];
-      __syncthreads();
-    }
-    if (tid == 0) tot[c] = red[0] * scale * (cand_scale != nullptr ? cand_scale[c] : 1.0);
-    __syncthreads();
-  }
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     int b = 0;
     double be = tot[0];
     for (int c = 0; c < n_cand; ++c) {
@@ -193,16 +196,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   __syncthreads();
   if (S != nullptr) {
     const float* src = S + (int64_t)best_sh * d_in;
-    for (int64_t i = tid; i < d_in; i += kSelThreads) best_s[i] = src[i];
+    for (int64_t i = threadIdx.x; i < d_in; i += kRedThreads) best_s[i] = src[i];
   }
 }
 
+hipError_t launch_argmin(const double* tot, int n_cand, float* err, int32_t* best_idx, const float* S, int64_t d_in,
+                         float* best_s, hipStream_t stream) {
+  argmin_kernel<<<1, kRedThreads, 0, stream>>>(tot, n_cand, err, best_idx, S, d_in, best_s);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, int64_t stride_b,
-                         int64_t stride_c, double scale, const double* cand_scale, float* err,
+                         int64_t stride_c, double scale, const double* cand_scale, double* tot, float* err,
                          int32_t* best_idx, const float* S, int64_t d_in, float* best_s,
                          hipStream_t stream) {
-  select_kernel<<<1, kSelThreads, 0, stream>>>(partials, n_blocks, n_cand, stride_b, stride_c, scale,
-                                               cand_scale, err, best_idx, S, d_in, best_s);
+  reduce_cand_kernel<<<n_cand, kRedThreads, 0, stream>>>(partials, n_blocks, stride_b, stride_c, scale,
+                                                         cand_scale, tot);
+  argmin_kernel<<<1, kRedThreads, 0, stream>>>(tot, n_cand, err, best_idx, S, d_in, best_s);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_unpack_dequant",
               "awq_search_workspace", "awq_last_error", "awq_abi_version", "awq_candidate_scales",
-              "awq_act_stats_workspace"]:
+              "awq_act_stats_workspace", "awq_candidate_scales_workspace", "awq_set_timing_events"]:
         assert n in names
 
 
@@ -147,6 +147,18 @@ def test_search_validation(A):
     clipc = A._cfg(128, 20, "output", 20, 0.5, 1e-4)
     assert st_search(A, clipc, grp, X=FAKE, T=16, ld=256, clip=None) == A.AWQ_EINVAL
     assert A.lib().awq_last_error().decode() != ""
+
+
+def test_candidate_validation(A):
+    L = A.lib()
+    n = ctypes.c_size_t()
+    assert L.awq_candidate_scales_workspace(4096, 20, ctypes.byref(n)) == 0 and n.value > 0
+    assert L.awq_candidate_scales(FAKE, 4096, 20, 1e-4, FAKE, FAKE, n.value - 8, None) == A.AWQ_EWORKSPACE
+    assert L.awq_candidate_scales(FAKE, 4096, 0, 1e-4, FAKE, FAKE, n.value, None) == A.AWQ_EINVAL
+    assert L.awq_candidate_scales(FAKE, 4096, 20, 0.0, FAKE, FAKE, n.value, None) == A.AWQ_EINVAL
+    assert L.awq_candidate_scales(None, 4096, 20, 1e-4, FAKE, FAKE, n.value, None) == A.AWQ_EINVAL
+    assert L.awq_set_timing_events(FAKE, None) == A.AWQ_EINVAL
+    assert L.awq_set_timing_events(None, None) == A.AWQ_OK
 
 
 def test_workspace_sizes(A):

@@ -206,6 +206,8 @@ def test_unpack_roundtrip(A, G, out_f16, with_s):
     ([96, 40, 64], 256, 129, 64, "bf16"),
     ([136], 512, 200, 128, "f16"),
     ([72], 384, 77, 32, "bf16"),
+    ([40], 96, 70, 32, "bf16"),            # K padded to the 64-wide GEMM step
+    ([300, 220], 512, 600, 128, "bf16"),   # several token and row tiles, ragged edges
 ])
 def test_search_output(A, parts, d_in, T, G, xdt):
     say(f"search output parts={parts} d_in={d_in} T={T} G={G} {xdt}")
@@ -253,3 +255,19 @@ def test_deterministic(A):
     c = A.search_scales([dev_f16(W)], xm, score="output", X=dev_x(X))
     d = A.search_scales([dev_f16(W)], xm, score="output", X=dev_x(X))
     assert np.array_equal(host(c.err), host(d.err))
+
+
+def test_search_output_full_size_row_sample(A):
+    """Fused QKV at its calibration size (16384 tokens x 4096 inputs): the first
+    64 rows of each of q, k, v form the scored group (the oracle evaluates
+    every candidate exactly on them)."""
+    import workloads as WL
+    wl = WL.WORKLOADS["qkv_6144x4096_output"]
+    say("search output qkv full size, 3 x 64 rows")
+    parts, X = WL.host_group_inputs(wl, 0, 0, rows_limit=64)
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in parts], dev_f32(xm), group_size=128, score="output", X=dev_x(X))
+    errs, k, _ = O.search_scales(parts, xm, 128, 20, "output", X=X)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
+    np.testing.assert_allclose(host(A.act_stats(dev_x(X))), xm, rtol=1e-6)
