@@ -136,17 +136,21 @@ def bench_weight(args, wl_name: str):
     K = args.steps
     ev = HipEvents(6 * K)
 
+    stats_plan = A.ActStatsPlan(X, x_mean=xm, ws=ws_stats)
+    search_plan = A.SearchPlan(Ws, xm, group_size=G, ws=ws_search, out=res)
+    pack_plans = [A.PackPlan(p, G, res.best_s, out=o) for p, o in zip(Ws, packs)]
+
     def step(i: int = -1):
         if i >= 0:
             A.set_timing_events(ev.h(6 * i), ev.h(6 * i + 1))
-        A.act_stats(X, x_mean=xm, ws=ws_stats)
+        stats_plan.launch()
         if i >= 0:
             A.set_timing_events(ev.h(6 * i + 2), ev.h(6 * i + 3))
-        A.search_scales(Ws, xm, group_size=G, ws=ws_search, out=res)
+        search_plan.launch()
         if i >= 0:
             A.set_timing_events(ev.h(6 * i + 4), ev.h(6 * i + 5))
-        for p, o in zip(Ws, packs):
-            A.quantize_pack(p, G, res.best_s, out=o)
+        for pp in pack_plans:
+            pp.launch()
         if i >= 0:
             A.set_timing_events(None, None)
 
@@ -226,24 +230,28 @@ def bench_output(args, wl_name: str):
         packs = [(torch.empty((grp.d_in, p.shape[0] // 8), dtype=torch.int32, device=dev),
                   torch.empty((grp.d_in // G, p.shape[0]), dtype=torch.float16, device=dev),
                   torch.empty((grp.d_in // G, p.shape[0] // 8), dtype=torch.int32, device=dev)) for p in parts]
-        plans.append((parts, X, grp, xm, ws_stats, ws, res, packs))
+        sp = A.ActStatsPlan(X, x_mean=xm, ws=ws_stats)
+        qp = A.SearchPlan(parts, xm, group_size=G, score="output", X=X, n_clip=wl.n_clip, ws=ws, out=res)
+        pps, off = [], 0
+        for p, o in zip(parts, packs):
+            clip = res.clip[off:off + p.shape[0]] if res.clip is not None else None
+            pps.append(A.PackPlan(p, G, res.best_s, clip, out=o))
+            off += p.shape[0]
+        plans.append((parts, X, grp, sp, qp, pps))
     K = args.steps
     n_pl = len(plans)
     ev = HipEvents(2 * n_pl * K)
 
     def step(k: int = -1):
-        for i, (parts, X, grp, xm, ws_stats, ws, res, packs) in enumerate(plans):
-            A.act_stats(X, x_mean=xm, ws=ws_stats)
+        for i, (parts, X, grp, sp, qp, pps) in enumerate(plans):
+            sp.launch()
             if k >= 0:
                 A.set_timing_events(ev.h(2 * (k * n_pl + i)), ev.h(2 * (k * n_pl + i) + 1))
-            A.search_scales(parts, xm, group_size=G, score="output", X=X, n_clip=wl.n_clip, ws=ws, out=res)
+            qp.launch()
             if k >= 0:
                 A.set_timing_events(None, None)
-            off = 0
-            for p, o in zip(parts, packs):
-                clip = res.clip[off:off + p.shape[0]] if res.clip is not None else None
-                A.quantize_pack(p, G, res.best_s, clip, out=o)
-                off += p.shape[0]
+            for pp in pps:
+                pp.launch()
 
     for _ in range(args.warmup):
         step()
@@ -306,6 +314,11 @@ def bench_sweep(args):
         K = args.steps
         per = 6 * 4 * blocks
         ev = HipEvents(per * K)
+        st_plans = [A.ActStatsPlan(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi]) for gi in range(len(wl.groups))]
+        se_plans = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi])
+                     for gi in range(len(wl.groups))] for b in range(blocks)]
+        pk_plans = [[[A.PackPlan(p, G, res[gi].best_s, out=o) for p, o in zip(Ws[b][gi], packs[gi])]
+                     for gi in range(len(wl.groups))] for b in range(blocks)]
 
         def step(k=-1):
             n = k * per
@@ -313,14 +326,14 @@ def bench_sweep(args):
                 for gi, g in enumerate(wl.groups):
                     if k >= 0:
                         A.set_timing_events(ev.h(n), ev.h(n + 1))
-                    A.act_stats(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi])
+                    st_plans[gi].launch()
                     if k >= 0:
                         A.set_timing_events(ev.h(n + 2), ev.h(n + 3))
-                    A.search_scales(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi])
+                    se_plans[b][gi].launch()
                     if k >= 0:
                         A.set_timing_events(ev.h(n + 4), ev.h(n + 5))
-                    for p, o in zip(Ws[b][gi], packs[gi]):
-                        A.quantize_pack(p, G, res[gi].best_s, out=o)
+                    for pp in pk_plans[b][gi]:
+                        pp.launch()
                     n += 6
             if k >= 0:
                 A.set_timing_events(None, None)
@@ -366,6 +379,26 @@ def bench_sweep(args):
     }
 
 
+def bench_copy(args):
+    """Plain device copy of 512 MiB (torch), the calibration of the HBM byte counters."""
+    import torch
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"metric": "device copy bandwidth (counter calibration)", "value": 2 * n / (ms * 1e-3) / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": {"workload": "copy_512MiB", "bytes_read": n, "bytes_written": n}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,7 +406,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="q_proj_4096x4096",
                     choices=["single_linear_256x512", "q_proj_4096x4096", "qkv_6144x4096_output",
-                             "mlp_output_clip", "qwen3_8b_sweep"])
+                             "mlp_output_clip", "qwen3_8b_sweep", "copy_512MiB"])
     ap.add_argument("--group-size", type=int, default=None)
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -396,6 +429,8 @@ def main() -> int:
         out = bench_weight(args, args.workload)
     elif args.workload == "qwen3_8b_sweep":
         out = bench_sweep(args)
+    elif args.workload == "copy_512MiB":
+        out = bench_copy(args)
     else:
         out = bench_output(args, args.workload)
     print(json.dumps(out), flush=True)

@@ -137,27 +137,53 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 # ---------------------------------------------------------------------------
+# Prepared calls: the ctypes argument tuple is built once; run() is one call
+# into the library (no allocation, no size queries), so repeated use costs a
+# few microseconds of host time.
+# ---------------------------------------------------------------------------
+class _Prepared:
+    _fn = ""
+
+    def _bind(self, *args) -> None:
+        self._f = getattr(lib(), self._fn)
+        self._args = args
+
+    def launch(self) -> None:
+        _check(self._f(*self._args))
+
+
 def act_stats_workspace_bytes(T: int, d_in: int) -> int:
     n = ctypes.c_size_t()
     _check(lib().awq_act_stats_workspace(T, d_in, ctypes.byref(n)))
     return n.value
 
 
+class ActStatsPlan(_Prepared):
+    """x_mean[i] (+)= inv_count * sum_t |X[t, i]| (inv_count defaults to 1/T)."""
+    _fn = "awq_act_stats"
+
+    def __init__(self, X: torch.Tensor, x_mean: Optional[torch.Tensor] = None, inv_count: Optional[float] = None,
+                 accumulate: bool = False, ws: Optional[torch.Tensor] = None, stream=None):
+        _dev(X, "X")
+        T, d_in, ld = _rows_view(X, "X")
+        self.x_mean = torch.empty(d_in, dtype=torch.float32, device=X.device) if x_mean is None else x_mean
+        if inv_count is None:
+            inv_count = 1.0 / T if T > 0 else 0.0
+        need = act_stats_workspace_bytes(T, d_in)
+        self.ws = workspace(need, X.device) if (ws is None or ws.numel() < need) else ws
+        self._keep = (X,)
+        self._bind(_ptr(X), _x_dtype(X), T, d_in, ld, inv_count, int(accumulate), _ptr(self.x_mean),
+                   _ptr(self.ws), self.ws.numel(), _stream(stream))
+
+    def run(self) -> torch.Tensor:
+        self.launch()
+        return self.x_mean
+
+
 def act_stats(X: torch.Tensor, x_mean: Optional[torch.Tensor] = None, inv_count: Optional[float] = None,
               accumulate: bool = False, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """x_mean[i] (+)= inv_count * sum_t |X[t, i]| (inv_count defaults to 1/T)."""
-    _dev(X, "X")
-    T, d_in, ld = _rows_view(X, "X")
-    if x_mean is None:
-        x_mean = torch.empty(d_in, dtype=torch.float32, device=X.device)
-    if inv_count is None:
-        inv_count = 1.0 / T if T > 0 else 0.0
-    need = act_stats_workspace_bytes(T, d_in)
-    if ws is None or ws.numel() < need:
-        ws = workspace(need, X.device)
-    _check(lib().awq_act_stats(_ptr(X), _x_dtype(X), T, d_in, ld, inv_count, int(accumulate),
-                             _ptr(x_mean), _ptr(ws), ws.numel(), _stream(stream)))
-    return x_mean
+    return ActStatsPlan(X, x_mean, inv_count, accumulate, ws, stream).run()
 
 
 def candidate_scales(x_mean: torch.Tensor, n_grid: int = 20, s_min: float = 1e-4, stream=None) -> torch.Tensor:
@@ -194,69 +220,95 @@ def search_workspace_bytes(d_out: int, d_in: int, T: int = 0, *, group_size: int
     return n.value
 
 
-def search_scales(W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, *, group_size: int = 128,
-                  n_grid: int = 20, score="weight", X: Optional[torch.Tensor] = None, n_clip: int = 0,
-                  clip_lo: float = 0.5, s_min: float = 1e-4, want_clip_err: bool = False,
-                  ws: Optional[torch.Tensor] = None, out: Optional[SearchResult] = None,
-                  stream=None) -> SearchResult:
+class SearchPlan(_Prepared):
     """Grid search of alpha for one group of linears sharing an input (rows concatenated)."""
-    parts: List[torch.Tensor] = list(W_parts)
-    if not parts:
-        raise ValueError("empty weight group")
-    d_in = parts[0].shape[1]
-    for p in parts:
-        _dev(p, "W")
-        if p.dtype != torch.float16 or p.dim() != 2 or not p.is_contiguous() or p.shape[1] != d_in:
-            raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
-    dev = parts[0].device
-    d_out = sum(p.shape[0] for p in parts)
-    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min)
-    T, ld, xdt = 0, 0, AWQ_BF16
-    if X is not None:
-        _dev(X, "X")
-        T, dx, ld = _rows_view(X, "X")
-        if dx != d_in:
-            raise ValueError("X and W disagree on d_in")
-        xdt = _x_dtype(X)
-    n = ctypes.c_size_t()
-    _check(lib().awq_search_workspace(ctypes.byref(cfg), d_out, d_in, max(T, 1), ctypes.byref(n)))
-    if ws is None or ws.numel() < n.value:
-        ws = workspace(n.value, dev)
-    if out is None:
-        out = SearchResult(
-            err=torch.empty(n_grid, dtype=torch.float32, device=dev),
-            best_idx=torch.empty(1, dtype=torch.int32, device=dev),
-            best_s=torch.empty(d_in, dtype=torch.float32, device=dev),
-            clip=torch.empty(d_out, dtype=torch.float32, device=dev) if n_clip else None,
-            clip_err=torch.empty((d_out, n_clip), dtype=torch.float32, device=dev)
-            if (n_clip and want_clip_err) else None)
-    wptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
-    rows = (ctypes.c_int64 * len(parts))(*[p.shape[0] for p in parts])
-    grp = WGroup(len(parts), ctypes.cast(wptrs, ctypes.POINTER(ctypes.c_void_p)),
-                 ctypes.cast(rows, ctypes.POINTER(ctypes.c_int64)))
-    _check(lib().awq_search_scales(ctypes.byref(cfg), ctypes.byref(grp), d_in, _ptr(x_mean), _ptr(X), xdt, T, ld,
-                                 _ptr(out.err), _ptr(out.best_idx), _ptr(out.best_s), _ptr(out.clip),
-                                 _ptr(out.clip_err), _ptr(ws), ws.numel(), _stream(stream)))
-    return out
+    _fn = "awq_search_scales"
+
+    def __init__(self, W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, *, group_size: int = 128,
+                 n_grid: int = 20, score="weight", X: Optional[torch.Tensor] = None, n_clip: int = 0,
+                 clip_lo: float = 0.5, s_min: float = 1e-4, want_clip_err: bool = False,
+                 ws: Optional[torch.Tensor] = None, out: Optional[SearchResult] = None, stream=None):
+        parts: List[torch.Tensor] = list(W_parts)
+        if not parts:
+            raise ValueError("empty weight group")
+        d_in = parts[0].shape[1]
+        for p in parts:
+            _dev(p, "W")
+            if p.dtype != torch.float16 or p.dim() != 2 or not p.is_contiguous() or p.shape[1] != d_in:
+                raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
+        dev = parts[0].device
+        d_out = sum(p.shape[0] for p in parts)
+        self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min)
+        T, ld, xdt = 0, 0, AWQ_BF16
+        if X is not None:
+            _dev(X, "X")
+            T, dx, ld = _rows_view(X, "X")
+            if dx != d_in:
+                raise ValueError("X and W disagree on d_in")
+            xdt = _x_dtype(X)
+        n = ctypes.c_size_t()
+        _check(lib().awq_search_workspace(ctypes.byref(self.cfg), d_out, d_in, max(T, 1), ctypes.byref(n)))
+        self.ws = workspace(n.value, dev) if (ws is None or ws.numel() < n.value) else ws
+        if out is None:
+            out = SearchResult(
+                err=torch.empty(n_grid, dtype=torch.float32, device=dev),
+                best_idx=torch.empty(1, dtype=torch.int32, device=dev),
+                best_s=torch.empty(d_in, dtype=torch.float32, device=dev),
+                clip=torch.empty(d_out, dtype=torch.float32, device=dev) if n_clip else None,
+                clip_err=torch.empty((d_out, n_clip), dtype=torch.float32, device=dev)
+                if (n_clip and want_clip_err) else None)
+        self.out = out
+        self._wptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+        self._rows = (ctypes.c_int64 * len(parts))(*[p.shape[0] for p in parts])
+        self.grp = WGroup(len(parts), ctypes.cast(self._wptrs, ctypes.POINTER(ctypes.c_void_p)),
+                          ctypes.cast(self._rows, ctypes.POINTER(ctypes.c_int64)))
+        self._keep = (parts, x_mean, X)
+        self._bind(ctypes.byref(self.cfg), ctypes.byref(self.grp), d_in, _ptr(x_mean), _ptr(X), xdt, T, ld,
+                   _ptr(out.err), _ptr(out.best_idx), _ptr(out.best_s), _ptr(out.clip), _ptr(out.clip_err),
+                   _ptr(self.ws), self.ws.numel(), _stream(stream))
+
+    def run(self) -> SearchResult:
+        self.launch()
+        return self.out
+
+
+def search_scales(W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, **kw) -> SearchResult:
+    """Grid search of alpha for one group of linears sharing an input (rows concatenated)."""
+    return SearchPlan(W_parts, x_mean, **kw).run()
+
+
+class PackPlan(_Prepared):
+    """INT4 quantize + pack of W*s: qweight int32 [d_in, d_out/8], scales fp16 [d_in/G, d_out],
+    qzeros int32 [d_in/G, d_out/8] (or None)."""
+    _fn = "awq_quantize_pack"
+
+    def __init__(self, W: torch.Tensor, group_size: int = 128, s: Optional[torch.Tensor] = None,
+                 clip: Optional[torch.Tensor] = None, with_zeros: bool = True, out=None, stream=None):
+        _dev(W, "W")
+        if W.dtype != torch.float16 or W.dim() != 2 or not W.is_contiguous():
+            raise ValueError("W must be contiguous fp16 [d_out, d_in]")
+        d_out, d_in = W.shape
+        if out is None:
+            qweight = torch.empty((d_in, d_out // 8), dtype=torch.int32, device=W.device)
+            scales = torch.empty((d_in // group_size, d_out), dtype=torch.float16, device=W.device)
+            qzeros = torch.empty((d_in // group_size, d_out // 8), dtype=torch.int32, device=W.device) \
+                if with_zeros else None
+            out = (qweight, scales, qzeros)
+        self.out = out
+        self._keep = (W, s, clip)
+        qweight, scales, qzeros = out
+        self._bind(_ptr(W), d_out, d_in, group_size, _ptr(s), _ptr(clip), _ptr(qweight), _ptr(scales),
+                   _ptr(qzeros), _stream(stream))
+
+    def run(self):
+        self.launch()
+        return self.out
 
 
 def quantize_pack(W: torch.Tensor, group_size: int = 128, s: Optional[torch.Tensor] = None,
                   clip: Optional[torch.Tensor] = None, with_zeros: bool = True, out=None, stream=None):
     """Returns (qweight int32 [d_in, d_out/8], scales fp16 [d_in/G, d_out], qzeros int32 [d_in/G, d_out/8])."""
-    _dev(W, "W")
-    if W.dtype != torch.float16 or W.dim() != 2 or not W.is_contiguous():
-        raise ValueError("W must be contiguous fp16 [d_out, d_in]")
-    d_out, d_in = W.shape
-    if out is None:
-        qweight = torch.empty((d_in, d_out // 8), dtype=torch.int32, device=W.device)
-        scales = torch.empty((d_in // group_size, d_out), dtype=torch.float16, device=W.device)
-        qzeros = torch.empty((d_in // group_size, d_out // 8), dtype=torch.int32, device=W.device) \
-            if with_zeros else None
-    else:
-        qweight, scales, qzeros = out
-    _check(lib().awq_quantize_pack(_ptr(W), d_out, d_in, group_size, _ptr(s), _ptr(clip), _ptr(qweight),
-                                 _ptr(scales), _ptr(qzeros), _stream(stream)))
-    return qweight, scales, qzeros
+    return PackPlan(W, group_size, s, clip, with_zeros, out, stream).run()
 
 
 def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], d_out: int,
@@ -267,7 +319,7 @@ def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional
     out = torch.empty((d_out, d_in), dtype=out_dtype, device=qweight.device)
     odt = {torch.float32: AWQ_F32, torch.float16: AWQ_F16}[out_dtype]
     _check(lib().awq_unpack_dequant(_ptr(qweight), _ptr(scales), _ptr(qzeros), d_out, d_in, group_size, _ptr(s),
-                                  _ptr(out), odt, _stream(stream)))
+                                    _ptr(out), odt, _stream(stream)))
     return out
 
 
@@ -276,5 +328,5 @@ def set_timing_events(before: Optional[int], after: Optional[int]) -> None:
     _check(lib().awq_set_timing_events(before, after))
 
 
-__all__ = ["set_timing_events", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
+__all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "PackPlan", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
            "search_workspace_bytes", "act_stats_workspace_bytes", "SearchResult", "lib", "LIB_PATH"]

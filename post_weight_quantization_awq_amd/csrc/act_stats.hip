@@ -4,8 +4,9 @@
 // as code" (x.abs().float().mean(dim=0)).
 //
 // HBM-bound column reduction: 2 bytes read per element.  Each lane owns 8
-// consecutive channels (one 16-byte load per token row); the 4 waves of a block
-// take interleaved token rows; blocks split the token axis.  Per-lane sums are
+// consecutive channels (one 16-byte load per token row) and keeps 16 row loads
+// in flight; the 4 waves of a block take 16-row slices; blocks split the token
+// axis.  Per-lane sums are
 // fp64 (full rate on CDNA4 VALU), the split partials are combined in a fixed
 // order by a second kernel, so the result is deterministic and independent of
 // the launch shape up to fp64 rounding.
@@ -17,6 +18,23 @@ namespace awq {
 constexpr int kStatsThreads = 256;
 constexpr int kStatsCols = 64 * 8;  // channels per block
 
+constexpr int kRowsPerWaveIter = 16;  // rows whose loads one lane keeps in flight
+
+template <bool BF16>
+__device__ __forceinline__ void acc8(const uint4 u, double* acc) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
+    const float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
+    acc[2 * j] += (double)__builtin_fabsf(lo);
+    acc[2 * j + 1] += (double)__builtin_fabsf(hi);
+  }
+}
+
+// Block: 64 lanes x 8 channels wide, 4 waves; the block's token range is walked
+// in 64-row steps, wave w taking rows w*16 .. w*16+15 of each step with all 16
+// loads issued before any is used.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
     const uint16_t* __restrict__ X, int64_t T, int64_t d_in, int64_t ld, int64_t rows_per_split,
@@ -33,43 +51,23 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
   if (col0 < d_in) {
     if (VEC && col0 + 8 <= d_in) {
       const uint16_t* p = X + col0;
-      int64_t r = r_begin + wv;
-      // 4 rows in flight per lane
-      for (; r + 12 < r_end; r += 16) {
-        uint4 u[4];
+      for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += 4 * kRowsPerWaveIter) {
+        uint4 u[kRowsPerWaveIter];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          u[q] = ld_nt(p + (r + 4 * q) * ld);
+        for (int q = 0; q < kRowsPerWaveIter; ++q)
+          u[q] = (base + q < r_end) ? ld_nt(p + (base + q) * ld) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
-            float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
-            acc[2 * j] += (double)__builtin_fabsf(lo);
-            acc[2 * j + 1] += (double)__builtin_fabsf(hi);
-          }
-        }
-      }
-      for (; r < r_end; r += 4) {
-        uint4 u = *(const uint4*)(p + r * ld);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
-          float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
-          acc[2 * j] += (double)__builtin_fabsf(lo);
-          acc[2 * j + 1] += (double)__builtin_fabsf(hi);
-        }
+        for (int q = 0; q < kRowsPerWaveIter; ++q) acc8<BF16>(u[q], acc);
       }
     } else {
-      for (int64_t r = r_begin + wv; r < r_end; r += 4) {
+      for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += 4 * kRowsPerWaveIter) {
+        for (int64_t r = base; r < base + kRowsPerWaveIter && r < r_end; ++r) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (col0 + j < d_in) {
-            uint16_t b = X[r * ld + col0 + j];
-            acc[j] += (double)__builtin_fabsf(BF16 ? bf2f(b) : h2f(b));
+          for (int j = 0; j < 8; ++j) {
+            if (col0 + j < d_in) {
+              const uint16_t b = X[r * ld + col0 + j];
+              acc[j] += (double)__builtin_fabsf(BF16 ? bf2f(b) : h2f(b));
+            }
           }
         }
       }
@@ -118,16 +116,14 @@ __global__ __launch_bounds__(256) void act_stats_final_kernel(const double* __re
 void act_stats_plan(int64_t T, int64_t d_in, int64_t* n_split, int64_t* rows_per_split) {
   if (T <= 0 || d_in <= 0) {
     *n_split = 0;
-    *rows_per_split = 1;
+    *rows_per_split = 64;
     return;
   }
-  const int64_t col_blocks = (d_in + kStatsCols - 1) / kStatsCols;
-  int64_t want = (4096 + col_blocks - 1) / col_blocks;           // ~4096 blocks in flight
-  int64_t max_split = (T + 63) / 64;                            // >= 64 rows per split
-  int64_t ns = want < max_split ? want : max_split;
-  if (ns < 1) ns = 1;
-  int64_t rps = (T + ns - 1) / ns;
-  rps = (rps + 15) / 16 * 16;
+  // 64 token rows per split (one row step of the 4 waves) up to 512 for long
+  // calibration sets, keeping the fp64 partials a few percent of X
+  int64_t rps = T / 256;
+  rps = rps < 64 ? 64 : (rps > 512 ? 512 : rps);
+  rps = (rps + 63) / 64 * 64;
   *rows_per_split = rps;
   *n_split = (T + rps - 1) / rps;
 }

@@ -55,7 +55,7 @@ struct SearchPlan {
   int64_t T_pad, d_out_pad, K_pad, n_mt, ldc;  // output score: padded GEMM shapes, token tiles, partial ld
   int64_t n_x, n_db;    // output score: X max partials, dW max partials per candidate
   int cand_chunk;       // output score: candidates per dW chunk
-  size_t off_S, off_C2, off_cand, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, total;
+  size_t off_S, off_C2, off_cand, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
 };
 
 constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
@@ -100,6 +100,8 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     off += align256((size_t)max_c * p.n_db * sizeof(float));
     p.off_sc = off;
     off += 2 * align256(sizeof(OutScales));
+    p.off_chunk = off;
+    off += align256((size_t)max_c * reduce_cols_chunks(d_out) * sizeof(double));
   }
   p.total = off;
   return p;
@@ -295,7 +297,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   }
   if (!one_chunk) mark(false, s);
   if ((e = launch_reduce_cols(colpart, plan.n_mt, plan.ldc, d_out, dop, cfg->n_grid, 1.0 / ((double)T * (double)d_out),
-                              sc_a, tot, s)) != hipSuccess)
+                              sc_a, (double*)(base + plan.off_chunk), tot, s)) != hipSuccess)
     return hip_status(e, "reduce_cols");
   if ((e = launch_argmin(tot, cfg->n_grid, err, best_idx, S, d_in, best_s, s)) != hipSuccess)
     return hip_status(e, "argmin");

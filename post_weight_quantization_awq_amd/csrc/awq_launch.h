@@ -46,8 +46,7 @@ hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, in
 int64_t absmax_blocks(int64_t rows);
 hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, float* xmax_part,
                             hipStream_t stream);
-// scales: xs from the X partial maxima (xmax_part may be nullptr to keep xs), ds[c] and inv[c]
-// from the dW partial maxima dmax [n_cand, n_d]
+// scales: xs from the X partial maxima, ds[c] and inv[c] from the dW partial maxima dmax [n_cand, n_d]
 hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
                              OutScales* sc, hipStream_t stream);
 // padded GEMM shapes: T_pad, d_out_pad multiples of 256, K_pad of 64
@@ -67,9 +66,12 @@ hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, i
 // colpart[mt * ldc + n] = sum over the 256 tokens of tile mt of Y[t, n]^2
 hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                           float* colpart, int64_t ldc, hipStream_t stream);
-// tot[c] = scale * sc->inv[c] * sum_mt sum_{o < d_out} colpart[mt * ldc + c * d_out_pad + o]
+// tot[c] = scale * sc->inv[c] * sum_mt sum_{o < d_out} colpart[mt * ldc + c * d_out_pad + o];
+// chunk_sum: [n_cand, reduce_cols_chunks(d_out)] fp64 scratch
+int64_t reduce_cols_chunks(int64_t d_out);
 hipError_t launch_reduce_cols(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
-                              int n_cand, double scale, const OutScales* sc, double* tot, hipStream_t stream);
+                              int n_cand, double scale, const OutScales* sc, double* chunk_sum, double* tot,
+                              hipStream_t stream);
 // per-row argmin over clip ratios: E[o, j] = sc->inv[j] * sum_mt colpart[mt * ldc + j * d_out_pad + o]
 hipError_t launch_clip_select(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
                               int n_clip, float clip_lo, const OutScales* sc, float* clip, float* clip_err,

@@ -189,40 +189,35 @@ __global__ __launch_bounds__(256) void absmax_rows_kernel(const uint16_t* __rest
     out[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
-// xmax: [n_x] partial maxima of |X| (nullptr: keep sc->xs); dmax: [n_cand, n_d].
+__device__ float block_max256(const float* __restrict__ a, int64_t n, float* red) {
+  const int tid = threadIdx.x;
+  float m = 0.0f;
+  for (int64_t i = tid; i < n; i += 256) m = __builtin_fmaxf(m, a[i]);
+  red[tid] = m;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] = __builtin_fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// xmax: [n_x] partial maxima of |X|; dmax: [n_cand, n_d].  Block c sets ds[c]
+// and inv[c] (every block derives the same xs from the X partials).
 __global__ __launch_bounds__(256) void out_scales_kernel(const float* __restrict__ xmax, int64_t n_x,
                                                         const float* __restrict__ dmax, int64_t n_d, int n_cand,
                                                         OutScales* __restrict__ sc) {
   __shared__ float red[256];
-  const int tid = threadIdx.x;
-  if (xmax != nullptr) {
-    float m = 0.0f;
-    for (int64_t i = tid; i < n_x; i += 256) m = __builtin_fmaxf(m, xmax[i]);
-    red[tid] = m;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-      if (tid < w) red[tid] = __builtin_fmaxf(red[tid], red[tid + w]);
-      __syncthreads();
-    }
-    if (tid == 0) sc->xs = pow2_scale_for(red[0]);
-    __syncthreads();
-  }
-  for (int c = 0; c < n_cand; ++c) {
-    float m = 0.0f;
-    for (int64_t i = tid; i < n_d; i += 256) m = __builtin_fmaxf(m, dmax[(int64_t)c * n_d + i]);
-    red[tid] = m;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-      if (tid < w) red[tid] = __builtin_fmaxf(red[tid], red[tid + w]);
-      __syncthreads();
-    }
-    if (tid == 0) {
-      const float ds = pow2_scale_for(red[0]);
-      sc->ds[c] = ds;
-      const double p = (double)sc->xs * (double)ds;
-      sc->inv[c] = 1.0 / (p * p);
-    }
-    __syncthreads();
+  const int c = blockIdx.x;
+  const float xs = pow2_scale_for(block_max256(xmax, n_x, red));
+  const float ds = pow2_scale_for(block_max256(dmax + (int64_t)c * n_d, n_d, red));
+  if (threadIdx.x == 0) {
+    if (c == 0) sc->xs = xs;
+    sc->ds[c] = ds;
+    const double p = (double)xs * (double)ds;
+    sc->inv[c] = 1.0 / (p * p);
   }
 }
 
@@ -263,7 +258,7 @@ hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 
 hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
                              OutScales* sc, hipStream_t stream) {
-  out_scales_kernel<<<1, 256, 0, stream>>>(xmax_part, n_x, dmax, n_d, n_cand, sc);
+  out_scales_kernel<<<n_cand, 256, 0, stream>>>(xmax_part, n_x, dmax, n_d, n_cand, sc);
   return hipGetLastError();
 }
 
@@ -284,10 +279,11 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 //    column the sum over the block's 256 tokens of Y^2 -> colpart[mt][n].
 //
 //    Block tile 256 x 256 x 64, 8 waves (2 along M x 4 along N), wave tile
-//    128 x 64 = 4 x 2 MFMA 32x32x16 f16 tiles, fp32 accumulators.  Operands go
-//    global -> LDS with global_load_lds_dwordx4 (no register staging), two
-//    stages; 16-byte K-chunks are XOR-swizzled by row so that the fragment
-//    reads of 32 consecutive rows hit distinct banks.  The block order is
+//    128 x 64 = 4 x 2 MFMA 32x32x16 f16 tiles, fp32 accumulators.  Two LDS
+//    stages; the next stage's operands are loaded into registers while the
+//    current one computes, then stored to the free stage (one barrier per
+//    stage).  16-byte K-chunks are XOR-swizzled by row so that fragment reads
+//    are free of bank conflicts.  The block order is
 //    remapped so that each XCD owns a contiguous range of tiles, walked in
 //    groups of 8 M-tiles: concurrent blocks of one XCD share A and B tiles in
 //    its L2.
@@ -297,29 +293,56 @@ constexpr int kGemmThreads = 512;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
+// 16-byte K-chunk kc of tile row `row` sits at chunk slot kc ^ swz(row): the
+// 16 rows read by one quarter-wave land in 16 distinct 16-byte bank slots of a
+// 256-byte window, and any 8 consecutive rows in 8 slots of a 128-byte window.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ void load_tile_lds(const uint16_t* __restrict__ src, int64_t ld, int64_t row0, int64_t k0,
-                                              uint16_t* lds_tile, int wave, int lane) {
-  // 256 rows x 64 K = 32 KiB = 32 wave-loads of 1 KiB (8 rows each); wave w issues 4.
+__device__ __forceinline__ uint4 frag(const uint16_t* lds_tile, int row, int kc) {
+  return *(const uint4*)(lds_tile + row * kBK + ((kc ^ swz(row)) << 3));
+}
+
+// global -> registers: 256 rows x 64 K of one operand = 2048 chunks of 16 B,
+// 4 per thread; thread t takes chunks t + 512 i (8 threads cover one row)
+__device__ __forceinline__ void gload(const uint16_t* __restrict__ src, int64_t ld, int64_t row0, int64_t k0,
+                                      int tid, uint4 (&r)[4]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int u = wave * 4 + q;
-    const int row = u * 8 + (lane >> 3);
-    const int kc = (lane & 7) ^ (lane >> 3);           // logical chunk stored at slot lane & 7
-    const uint16_t* g = src + (row0 + row) * ld + k0 + kc * 8;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)(lds_tile + u * 512), 16, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kGemmThreads * i;
+    r[i] = *(const uint4*)(src + (row0 + (c >> 3)) * ld + k0 + (c & 7) * 8);
   }
 }
 
-__device__ __forceinline__ uint4 frag(const uint16_t* lds_tile, int row, int kc) {
-  return *(const uint4*)(lds_tile + row * kBK + ((kc ^ (row & 7)) << 3));
+__device__ __forceinline__ void lstore(uint16_t* lds_tile, int tid, const uint4 (&r)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kGemmThreads * i;
+    const int row = c >> 3, kc = c & 7;
+    *(uint4*)(lds_tile + row * kBK + ((kc ^ swz(row)) << 3)) = r[i];
+  }
 }
 
 __device__ __forceinline__ f32x16 mfma_f16(const uint4 a, const uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
                                                 0);
+}
+
+// One 64-wide K stage of MFMAs from LDS tiles As/Bs into acc.
+__device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane,
+                                           f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) {
+    const int kc = 2 * ks + (lane >> 5);
+    uint4 a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = frag(As, wm * 128 + i * 32 + (lane & 31), kc);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = frag(Bs, wn * 64 + j * 32 + (lane & 31), kc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
+  }
 }
 
 __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
@@ -354,32 +377,33 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)(K / kBK);
-  load_tile_lds(A, lda, m0, 0, lds[0][0], wave, lane);
-  load_tile_lds(B, ldb, n0, 0, lds[0][1], wave, lane);
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage kt have landed
-    __syncthreads();                 // ... and every wave's; stage kt^1 is free again
+  uint4 ra[4], rb[4];
+  gload(A, lda, m0, 0, tid, ra);
+  gload(B, ldb, n0, 0, tid, rb);
+  lstore(lds[0][0], tid, ra);
+  lstore(lds[0][1], tid, rb);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) {
-      load_tile_lds(A, lda, m0, (int64_t)(kt + 1) * kBK, lds[st ^ 1][0], wave, lane);
-      load_tile_lds(B, ldb, n0, (int64_t)(kt + 1) * kBK, lds[st ^ 1][1], wave, lane);
-    }
-    const uint16_t* As = lds[st][0];
-    const uint16_t* Bs = lds[st][1];
+    // next stage in flight while this one computes
+    gload(A, lda, m0, (int64_t)(kt + 1) * kBK, tid, ra);
+    gload(B, ldb, n0, (int64_t)(kt + 1) * kBK, tid, rb);
+    mfma_stage(lds[st][0], lds[st][1], wm, wn, lane, acc);
+    // stage st ^ 1 was last read before the previous barrier
+    lstore(lds[st ^ 1][0], tid, ra);
+    lstore(lds[st ^ 1][1], tid, rb);
+    // schedule: the 8 global loads first (they then run under the MFMAs),
+    // each k16 step's 6 fragment reads ahead of its 8 MFMAs, the stores last
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int kc = 2 * ks + (lane >> 5);
-      uint4 a[4], b[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = frag(As, wm * 128 + i * 32 + (lane & 31), kc);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = frag(Bs, wn * 64 + j * 32 + (lane & 31), kc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
+    __syncthreads();
   }
+  mfma_stage(lds[(nk - 1) & 1][0], lds[(nk - 1) & 1][1], wm, wn, lane, acc);
 
   // epilogue: column c of a 32x32 tile lives in lanes c and c + 32
 #pragma unroll
@@ -411,28 +435,56 @@ hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, con
 }
 
 // per-candidate totals: tot[c] = scale * inv[c] * sum_mt sum_{o < d_out} colpart[mt][c * d_out_pad + o]
-__global__ __launch_bounds__(256) void reduce_cols_kernel(const float* __restrict__ colpart, int64_t n_mt, int64_t ldc,
-                                                         int64_t d_out, int64_t d_out_pad, double scale,
-                                                         const OutScales* __restrict__ sc, double* __restrict__ tot) {
-  const int c = blockIdx.x;
+// stage 1: block (chunk, c) sums 256 columns over all token tiles -> chunk_sum[c][chunk]
+// stage 2: one thread per candidate adds its chunk sums in order
+constexpr int kColChunk = 256;
+
+__global__ __launch_bounds__(kColChunk) void reduce_cols_kernel(const float* __restrict__ colpart, int64_t n_mt,
+                                                               int64_t ldc, int64_t d_out, int64_t d_out_pad,
+                                                               double* __restrict__ chunk_sum) {
+  const int c = blockIdx.y;
+  const int64_t o = (int64_t)blockIdx.x * kColChunk + threadIdx.x;
   double acc = 0.0;
-  for (int64_t o = threadIdx.x; o < d_out; o += 256) {
+  if (o < d_out) {
     const float* p = colpart + (int64_t)c * d_out_pad + o;
-    for (int64_t mt = 0; mt < n_mt; ++mt) acc += (double)p[mt * ldc];
+    int64_t mt = 0;
+    for (; mt + 8 <= n_mt; mt += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = p[(mt + q) * ldc];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += (double)v[q];
+    }
+    for (; mt < n_mt; ++mt) acc += (double)p[mt * ldc];
   }
-  __shared__ double red[256];
+  __shared__ double red[kColChunk];
   red[threadIdx.x] = acc;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
+  for (int w = kColChunk / 2; w >= 1; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) tot[c] = red[0] * scale * sc->inv[c];
+  if (threadIdx.x == 0) chunk_sum[(int64_t)c * gridDim.x + blockIdx.x] = red[0];
 }
 
+__global__ void sum_chunks_kernel(const double* __restrict__ chunk_sum, int64_t n_chunk, int n_cand, double scale,
+                                  const OutScales* __restrict__ sc, double* __restrict__ tot) {
+  const int c = threadIdx.x;
+  if (c >= n_cand) return;
+  double t = 0.0;
+  for (int64_t k = 0; k < n_chunk; ++k) t += chunk_sum[(int64_t)c * n_chunk + k];
+  tot[c] = t * scale * sc->inv[c];
+}
+
+int64_t reduce_cols_chunks(int64_t d_out) { return (d_out + kColChunk - 1) / kColChunk; }
+
 hipError_t launch_reduce_cols(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
-                              int n_cand, double scale, const OutScales* sc, double* tot, hipStream_t stream) {
-  reduce_cols_kernel<<<n_cand, 256, 0, stream>>>(colpart, n_mt, ldc, d_out, d_out_pad, scale, sc, tot);
+                              int n_cand, double scale, const OutScales* sc, double* chunk_sum, double* tot,
+                              hipStream_t stream) {
+  const int64_t nch = reduce_cols_chunks(d_out);
+  reduce_cols_kernel<<<dim3((unsigned)nch, (unsigned)n_cand), kColChunk, 0, stream>>>(colpart, n_mt, ldc, d_out,
+                                                                                      d_out_pad, chunk_sum);
+  sum_chunks_kernel<<<1, 64, 0, stream>>>(chunk_sum, nch, n_cand, scale, sc, tot);
   return hipGetLastError();
 }
 

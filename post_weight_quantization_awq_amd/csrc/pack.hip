@@ -9,7 +9,8 @@
 //
 // Codes are bit-exact with IEEE fp32: the step is RN(a / 7) (exact divide by 7
 // sequence), the code is rint(RN(v / step)) through a reciprocal fast path
-// that falls back to the IEEE division near half-integers.
+// that falls back to the IEEE division near half-integers.  Unclipped, |v| is
+// at most the group maximum, so |rint(v / step)| <= 7 needs no clamp.
 //
 // HBM-bound: 2 bytes read and ~0.53 bytes written per weight.  A lane owns an
 // 8 x 8 tile (8 consecutive output rows, 8 consecutive inputs): its 8 rows at
@@ -37,7 +38,17 @@ struct PackShape {
   static constexpr int MW = ROWS_B / 8;          // words per input column per block
 };
 
-template <int G>
+// Per element: cvt, scale, max (half a max3), v * rcp(step), rint, the
+// near-half check, cvt to int and a shift-add into the word (~8.5 VALU ops).
+// Codes accumulate as signed nibbles: sum_r q_r * 16^nib(r) + 0x77777777 equals
+// sum_r (q_r + 7) * 16^nib(r) exactly, since every q_r + 7 lies in [0, 14].
+// A row whose fast codes might differ from rint(RN(v / step)) (|r0 - rint r0|
+// within 2^-15 of 1/2, or r0 not finite) recomputes its 8 codes with the IEEE
+// division.  The bound on |r0 - v/step| (rcp within 1 ulp, one rounding) is
+// below 8e-6 for |v/step| < 32; unclipped |v/step| <= 7, and with clipping a
+// larger quotient can only mis-round to a code that the clamp maps to +-7
+// either way for |v/step| >= 32 (ratios >= 7/32).
+template <int G, bool HAS_S, bool HAS_CLIP>
 __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ W, int64_t d_out, int64_t d_in, const float* __restrict__ s,
     const float* __restrict__ clip, int32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
@@ -56,44 +67,56 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
   const bool valid = row0 < d_out;  // d_out % 8 == 0: all 8 rows or none
 
   float sv[8];
-  if (s != nullptr) {
+  if constexpr (HAS_S) {
     const float4 a = *(const float4*)(s + col0);
     const float4 b = *(const float4*)(s + col0 + 4);
     sv[0] = a.x; sv[1] = a.y; sv[2] = a.z; sv[3] = a.w;
     sv[4] = b.x; sv[5] = b.y; sv[6] = b.z; sv[7] = b.w;
   }
-  uint32_t words[8];
+  uint4 raw[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) words[j] = 0u;
+  for (int r = 0; r < 8; ++r)
+    raw[r] = valid ? ld_nt(W + (row0 + r) * d_in + col0) : make_uint4(0u, 0u, 0u, 0u);
+
+  int32_t words[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) words[j] = 0;
   uint32_t sbits[4];
 
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     float v[8];
-    if (valid) {
-      const uint4 u = ld_nt(W + (row0 + r) * d_in + col0);
-      unpack8_f16(u, v);
-      if (s != nullptr) {
+    unpack8_f16(raw[r], v);
+    if constexpr (HAS_S) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = v[j] * sv[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+      for (int j = 0; j < 8; ++j) v[j] = v[j] * sv[j];
     }
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
     m = group_max<SH::LPG>(m);
-    const float a = (clip != nullptr && valid) ? clip[row0 + r] * m : m;
+    float a = m;
+    if constexpr (HAS_CLIP) a = valid ? clip[row0 + r] * m : m;
     const float step = div7(a);
     const float inv = __builtin_amdgcn_rcpf(step);
+    float n[8];
+    bool near = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float r0 = v[j] * inv;
+      n[j] = __builtin_rintf(r0);
+      near |= !(__builtin_fabsf(r0 - n[j]) < 0.5f - 0x1p-15f);  // also true for inf / NaN
+    }
+    if (near) {  // rare: exact codes for this lane's 8 elements of row r
+#pragma unroll
+      for (int j = 0; j < 8; ++j) n[j] = step > 0.0f ? __builtin_rintf(v[j] / step) : 0.0f;
+    }
     const int sh = 4 * nibble_of_row(r);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float n = step > 0.0f ? code_exact(v[j], step, inv) : 0.0f;
-      n = __builtin_fminf(__builtin_fmaxf(n, -7.0f), 7.0f);
-      words[j] |= (uint32_t)((int)n + 7) << sh;
+      float q = n[j];
+      if constexpr (HAS_CLIP) q = __builtin_amdgcn_fmed3f(q, -7.0f, 7.0f);
+      words[j] += (int32_t)q << sh;
     }
     const uint32_t hb = f2h_bits(step);
     if (r & 1) sbits[r >> 1] |= hb << 16;
@@ -101,7 +124,7 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
   }
 
 #pragma unroll
-  for (int j = 0; j < 8; ++j) wt[lg * 8 + j][m_local] = words[j];
+  for (int j = 0; j < 8; ++j) wt[lg * 8 + j][m_local] = (uint32_t)words[j] + 0x77777777u;
   if (valid && lg == 0) {
     *(uint4*)(scales + gcol * d_out + row0) = make_uint4(sbits[0], sbits[1], sbits[2], sbits[3]);
     if (qzeros != nullptr) qzeros[gcol * (d_out / 8) + row0 / 8] = 0x77777777;
@@ -121,22 +144,27 @@ static int64_t pack_blocks(int64_t d_out, int64_t d_in) {
   return (d_in / G) * ((d_out + PackShape<G>::ROWS_B - 1) / PackShape<G>::ROWS_B);
 }
 
+template <int G>
+static void launch_pack_g(const uint16_t* W, int64_t d_out, int64_t d_in, const float* s, const float* clip,
+                          int32_t* qweight, uint16_t* scales, int32_t* qzeros, hipStream_t stream) {
+  const unsigned nb = (unsigned)pack_blocks<G>(d_out, d_in);
+  if (s != nullptr && clip != nullptr)
+    quantize_pack_kernel<G, true, true><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+  else if (s != nullptr)
+    quantize_pack_kernel<G, true, false><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+  else if (clip != nullptr)
+    quantize_pack_kernel<G, false, true><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+  else
+    quantize_pack_kernel<G, false, false><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+}
+
 hipError_t launch_quantize_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int group_size,
                                 const float* s, const float* clip, int32_t* qweight,
                                 uint16_t* scales, int32_t* qzeros, hipStream_t stream) {
   switch (group_size) {
-    case 32:
-      quantize_pack_kernel<32><<<(unsigned)pack_blocks<32>(d_out, d_in), kPackThreads, 0, stream>>>(
-          W, d_out, d_in, s, clip, qweight, scales, qzeros);
-      break;
-    case 64:
-      quantize_pack_kernel<64><<<(unsigned)pack_blocks<64>(d_out, d_in), kPackThreads, 0, stream>>>(
-          W, d_out, d_in, s, clip, qweight, scales, qzeros);
-      break;
-    default:
-      quantize_pack_kernel<128><<<(unsigned)pack_blocks<128>(d_out, d_in), kPackThreads, 0, stream>>>(
-          W, d_out, d_in, s, clip, qweight, scales, qzeros);
-      break;
+    case 32: launch_pack_g<32>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream); break;
+    case 64: launch_pack_g<64>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream); break;
+    default: launch_pack_g<128>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream); break;
   }
   return hipGetLastError();
 }
