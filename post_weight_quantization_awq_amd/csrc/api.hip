@@ -237,6 +237,11 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
     if (T < 1) return fail(AWQ_EINVAL, "output score needs T >= 1");
     if (ld_x < d_in) return fail(AWQ_ESHAPE, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
     if (!aligned16(X) || (ld_x % 8)) return fail(AWQ_EALIGN, "X must be 16-byte aligned with ld_x % 8 == 0");
+    // the matrix-core operands are addressed with 32-bit byte offsets
+    int64_t tp, dp, kp;
+    gemm_sq_pad(T, d_out, d_in, &tp, &dp, &kp);
+    if ((double)tp * (double)kp * 2.0 >= 4294967296.0 || (double)dp * (double)kp * 2.0 * 2.0 >= 4294967296.0)
+      return fail(AWQ_ESHAPE, "output score needs T*d_in and d_out*d_in below 2^31 elements");
   }
   if (cfg->n_clip >= 2 && !clip) return fail(AWQ_EINVAL, "clip is NULL but n_clip >= 2");
   const SearchPlan plan = plan_search(*cfg, d_out, d_in, T);

@@ -278,20 +278,22 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 //    of the tile with zero rows; M and K padded likewise with zeros), and per
 //    column the sum over the block's 256 tokens of Y^2 -> colpart[mt][n].
 //
-//    Block tile 256 x 256 x 64, 8 waves (2 along M x 4 along N), wave tile
-//    128 x 64 = 4 x 2 MFMA 32x32x16 f16 tiles, fp32 accumulators.  Two LDS
-//    stages; the next stage's operands are loaded into registers while the
-//    current one computes, then stored to the free stage (one barrier per
-//    stage).  16-byte K-chunks are XOR-swizzled by row so that fragment reads
-//    are free of bank conflicts.  The block order is
-//    remapped so that each XCD owns a contiguous range of tiles, walked in
-//    groups of 8 M-tiles: concurrent blocks of one XCD share A and B tiles in
-//    its L2.
+//    Block tile 256 x 256 x 64, 4 waves (2 x 2), wave tile 128 x 128 =
+//    4 x 4 MFMA 32x32x16 f16 tiles; the 256 fp32 accumulators per lane live in
+//    AGPRs (one wave per SIMD).  A wave reads 8 fragments (8 KiB of LDS) per
+//    16 MFMAs.  Two LDS stages and two register stages: the operands of
+//    stage kt + 2 are loaded at the top of stage kt, under its MFMAs, and
+//    reach LDS at the end of stage kt + 1 (one barrier per stage).  16-byte K-chunks are
+//    XOR-swizzled by row so that fragment reads are free of bank conflicts.
+//    The block order is remapped so that each XCD owns a contiguous range of
+//    tiles, walked in groups of 8 M-tiles: concurrent blocks of one XCD share
+//    A and B tiles in its L2.
 // ---------------------------------------------------------------------------
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kGemmThreads = 512;
+constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
+constexpr int kLoads = (kBM * kBK / 8) / kGemmThreads;  // 16-byte chunks per thread per operand: 8
 
 // 16-byte K-chunk kc of tile row `row` sits at chunk slot kc ^ swz(row): the
 // 16 rows read by one quarter-wave land in 16 distinct 16-byte bank slots of a
@@ -302,24 +304,30 @@ __device__ __forceinline__ uint4 frag(const uint16_t* lds_tile, int row, int kc)
   return *(const uint4*)(lds_tile + row * kBK + ((kc ^ swz(row)) << 3));
 }
 
-// global -> registers: 256 rows x 64 K of one operand = 2048 chunks of 16 B,
-// 4 per thread; thread t takes chunks t + 512 i (8 threads cover one row)
-__device__ __forceinline__ void gload(const uint16_t* __restrict__ src, int64_t ld, int64_t row0, int64_t k0,
-                                      int tid, uint4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + kGemmThreads * i;
-    r[i] = *(const uint4*)(src + (row0 + (c >> 3)) * ld + k0 + (c & 7) * 8);
-  }
+// global -> registers through a buffer resource: 256 rows x 64 K of one
+// operand = 2048 chunks of 16 B; thread t takes chunks t + 256 i (8 threads
+// cover one row): rows t/8 + 32 i.  The lane's byte offset `voff` in its first
+// row is the same for every stage and both operands (one VGPR); the tile row,
+// stage and i offsets are wave-uniform (SGPR soffset).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void lstore(uint16_t* lds_tile, int tid, const uint4 (&r)[4]) {
+__device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t row32_bytes,
+                                      uint4 (&r)[kLoads]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + kGemmThreads * i;
-    const int row = c >> 3, kc = c & 7;
-    *(uint4*)(lds_tile + row * kBK + ((kc ^ swz(row)) << 3)) = r[i];
-  }
+  for (int i = 0; i < kLoads; ++i)
+    r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff + i * row32_bytes, 0));
+}
+
+// registers -> LDS: row t/8 + 32 i, chunk t % 8; swz(row) does not depend on i
+__device__ __forceinline__ void lstore(uint16_t* lds_tile, int tid, const uint4 (&r)[kLoads]) {
+  const int row = tid >> 3, kc = tid & 7;
+  uint16_t* p = lds_tile + row * kBK + ((kc ^ swz(row)) << 3);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) *(uint4*)(p + i * 32 * kBK) = r[i];
 }
 
 __device__ __forceinline__ f32x16 mfma_f16(const uint4 a, const uint4 b, f32x16 c) {
@@ -327,28 +335,29 @@ __device__ __forceinline__ f32x16 mfma_f16(const uint4 a, const uint4 b, f32x16 
                                                 0);
 }
 
-// One 64-wide K stage of MFMAs from LDS tiles As/Bs into acc.
+// One 64-wide K stage: 4 k16 steps of 8 fragment reads and 16 MFMAs.
 __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane,
-                                           f32x16 (&acc)[4][2]) {
+                                           f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
     const int kc = 2 * ks + (lane >> 5);
-    uint4 a[4], b[2];
+    uint4 a[4], b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = frag(As, wm * 128 + i * 32 + (lane & 31), kc);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = frag(Bs, wn * 64 + j * 32 + (lane & 31), kc);
+    for (int j = 0; j < 4; ++j) b[j] = frag(Bs, wn * 128 + j * 32 + (lane & 31), kc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
   }
 }
 
+// A: [n_mt * 256, lda] (a_bytes in all), B: [n_nt * 256, ldb] (b_bytes); both < 4 GiB
 __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
-                                                              const uint16_t* __restrict__ B, int64_t ldb,
-                                                              int64_t K, int64_t n_mt, int64_t n_nt,
-                                                              float* __restrict__ colpart, int64_t ldc) {
+                                                              uint32_t a_bytes, const uint16_t* __restrict__ B,
+                                                              int64_t ldb, uint32_t b_bytes, int64_t K, int64_t n_mt,
+                                                              int64_t n_nt, float* __restrict__ colpart, int64_t ldc) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kBM * kBK];  // [stage][A|B]
   __shared__ float red[2][kBN];
 
@@ -366,55 +375,96 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
   const int64_t m0 = mt * kBM, n0 = nt * kBN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
+  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Stage kt is computed from lds[kt & 1].  Stage kt + 1 is in registers
+  // (loaded during stage kt - 1) and is stored to the other buffer after the
+  // MFMAs; the loads of stage kt + 2 are issued before them, so every global
+  // load has two stages of MFMA time to arrive.
   const int nk = (int)(K / kBK);
-  uint4 ra[4], rb[4];
-  gload(A, lda, m0, 0, tid, ra);
-  gload(B, ldb, n0, 0, tid, rb);
-  lstore(lds[0][0], tid, ra);
-  lstore(lds[0][1], tid, rb);
-  __syncthreads();
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int st = kt & 1;
-    // next stage in flight while this one computes
-    gload(A, lda, m0, (int64_t)(kt + 1) * kBK, tid, ra);
-    gload(B, ldb, n0, (int64_t)(kt + 1) * kBK, tid, rb);
-    mfma_stage(lds[st][0], lds[st][1], wm, wn, lane, acc);
-    // stage st ^ 1 was last read before the previous barrier
-    lstore(lds[st ^ 1][0], tid, ra);
-    lstore(lds[st ^ 1][1], tid, rb);
-    // schedule: the 8 global loads first (they then run under the MFMAs),
-    // each k16 step's 6 fragment reads ahead of its 8 MFMAs, the stores last
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
-    __syncthreads();
+  // A and B share the leading dimension (K padded), hence the lane offset
+  const uint32_t voff = (uint32_t)(((tid >> 3) * lda + (tid & 7) * 8) * 2);
+  const uint32_t row32 = (uint32_t)(32 * lda * 2);
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, a_bytes);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, b_bytes);
+  const uint32_t sA = (uint32_t)(m0 * lda * 2), sB = (uint32_t)(n0 * ldb * 2);
+  uint4 ra0[kLoads], rb0[kLoads], ra1[kLoads], rb1[kLoads];
+  gload(rsA, voff, sA, row32, ra0);
+  gload(rsB, voff, sB, row32, rb0);
+  lstore(lds[0][0], tid, ra0);
+  lstore(lds[0][1], tid, rb0);
+  {
+    const uint32_t k1 = (uint32_t)(nk > 1 ? kBK * 2 : 0);
+    gload(rsA, voff, sA + k1, row32, ra1);
+    gload(rsB, voff, sB + k1, row32, rb1);
   }
-  mfma_stage(lds[(nk - 1) & 1][0], lds[(nk - 1) & 1][1], wm, wn, lane, acc);
+  __syncthreads();
+
+// one stage: loads of kt + 2 (or a harmless in-bounds re-read) into (RA, RB),
+// MFMAs on lds[ST], store of kt + 1 from (SA, SB) into lds[ST ^ 1] (free since
+// the previous barrier; its registers arrived a stage ago) spread over the
+// first half of the MFMAs, barrier
+#define AWQ_STAGE(ST, RA, RB, SA, SB)                                          \
+  {                                                                            \
+    const uint32_t k2 = (uint32_t)((kt + 2 < nk ? kt + 2 : kt + 1) * kBK * 2); \
+    gload(rsA, voff, sA + k2, row32, RA);                                      \
+    gload(rsB, voff, sB + k2, row32, RB);                                      \
+    mfma_stage(lds[ST][0], lds[ST][1], wm, wn, lane, acc);                     \
+    lstore(lds[(ST) ^ 1][0], tid, SA);                                         \
+    lstore(lds[(ST) ^ 1][1], tid, SB);                                         \
+    /* order: the 16 loads; step 0's 8 fragment reads; steps 0-1: each     */ \
+    /* pair of MFMAs followed by one store of stage kt + 1 and one read of  */ \
+    /* the next step; step 2: pairs of MFMAs and reads; step 3: MFMAs       */ \
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * kLoads, 0);                \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                         \
+    for (int ks = 0; ks < 2; ++ks) {                                           \
+      for (int u = 0; u < 8; ++u) {                                            \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                     \
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     \
+      }                                                                        \
+    }                                                                          \
+    for (int u = 0; u < 8; ++u) {                                              \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                       \
+    }                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);                        \
+    __syncthreads();                                                           \
+  }
+
+  int kt = 0;
+  // every stage but the last has a successor to store
+  for (; kt + 2 < nk; kt += 2) {
+    AWQ_STAGE(0, ra0, rb0, ra1, rb1)
+    ++kt;
+    AWQ_STAGE(1, ra1, rb1, ra0, rb0)
+    --kt;
+  }
+  if (kt + 1 < nk) {  // two stages left: kt (buffer 0), then kt + 1
+    AWQ_STAGE(0, ra0, rb0, ra1, rb1)
+    ++kt;
+  }
+  mfma_stage(lds[kt & 1][0], lds[kt & 1][1], wm, wn, lane, acc);
+#undef AWQ_STAGE
 
   // epilogue: column c of a 32x32 tile lives in lanes c and c + 32
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 4; ++j) {
     float cs = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
     cs += __shfl_xor(cs, 32, kWave);
-    if (lane < 32) red[wm][wn * 64 + j * 32 + lane] = cs;
+    if (lane < 32) red[wm][wn * 128 + j * 32 + lane] = cs;
   }
   __syncthreads();
   if (tid < kBN) colpart[mt * ldc + n0 + tid] = red[0][tid] + red[1][tid];
@@ -429,8 +479,9 @@ void gemm_sq_pad(int64_t T, int64_t d_out, int64_t d_in, int64_t* T_pad, int64_t
 hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                           float* colpart, int64_t ldc, hipStream_t stream) {
   const int64_t n_mt = T_pad / kBM, n_nt = n_cols / kBN;
-  gemm_sq_kernel<<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(X16, K_pad, dw, K_pad, K_pad, n_mt, n_nt,
-                                                                      colpart, ldc);
+  const uint32_t a_bytes = (uint32_t)(T_pad * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
+  gemm_sq_kernel<<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(X16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad,
+                                                                      n_mt, n_nt, colpart, ldc);
   return hipGetLastError();
 }
 
