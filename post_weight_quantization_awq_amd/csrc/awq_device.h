@@ -133,6 +133,36 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Same for non-negative finite floats: their bit patterns order like the
+// values, so the unsigned max folds into one DPP-modified VALU op per step
+// (a float max would first canonicalize the permuted operand).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+template <int N>
+__device__ __forceinline__ float group_max_nonneg(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if constexpr (N >= 2) u = max(u, dpp_u<0xB1>(u));
+  if constexpr (N >= 4) u = max(u, dpp_u<0x4E>(u));
+  if constexpr (N >= 8) u = max(u, dpp_u<0x141>(u));
+  if constexpr (N >= 16) u = max(u, dpp_u<0x140>(u));
+  return __builtin_bit_cast(float, u);
+}
+// Sum over each aligned row of 16 lanes (every lane of the row gets it);
+// fixed pairing, so the result does not depend on scheduling.
+template <int CTRL>
+__device__ __forceinline__ float dpp_m(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_m<0xB1>(x);
+  x += dpp_m<0x4E>(x);
+  x += dpp_m<0x141>(x);
+  x += dpp_m<0x140>(x);
+  return x;
+}
+
 // Sum over the 64 lanes of a wave, fixed pairing (deterministic).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

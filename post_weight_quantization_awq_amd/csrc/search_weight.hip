@@ -13,32 +13,45 @@
 // domain (w - q*step/s) * x = (v - q*step) * (x/s), so each lane accumulates
 // d^2 per column over its rows and weights the column sums by (x/s)^2 once.
 //
-// Tile: one quantization group column (G inputs) by 32*R rows (G = 128); each
-// lane holds 16 consecutive inputs of R rows; the G/16 lanes of a row combine
-// their maxima with DPP row permutes.  The candidate scales and (x/s)^2 of the
-// block's columns are staged in LDS.
+// Tile: one quantization group column (G inputs) by 8192*R/G rows (256 rows
+// for G = 128): each
+// lane holds 32 inputs of R rows as packed fp16 (four 16-byte chunks,
+// interleaved with the other G/32 lanes of the row so that one load
+// instruction reads G/32 * 16 contiguous bytes of a row); v = w*s is formed
+// straight from the fp16 halves with a mixed-precision fma.  The G/32 lanes
+// of a row combine their maxima with DPP row permutes.  The candidate scales
+// and (x/s)^2 of the block's columns are staged in LDS.  Two blocks share a
+// compute unit (one wave per SIMD each), so VGPRs stay under 256.
 #include "awq_device.h"
 #include "awq_launch.h"
 
 namespace awq {
 
 constexpr int kSearchThreads = 256;
-constexpr int kSearchR = 4;  // rows per lane
+constexpr int kSearchE = 32;  // inputs per lane per row
+constexpr int kSearchR = 4;   // rows per lane
+// Initial value of a group's running max: zero groups then get a tiny positive
+// step, so q = 0 and d = 0 exactly without a select (any group whose max is
+// below it contributes less than 2^-200 to the score).
+constexpr float kTinyMax = 0x1p-100f;
 
 template <int G>
-constexpr int search_rows_per_block() { return (kSearchThreads / (G / 16)) * kSearchR; }
+constexpr int search_rows_per_block() { return (kSearchThreads / (G / kSearchE)) * kSearchR; }
 
-template <int G, int R>
-__global__ __launch_bounds__(kSearchThreads) void search_weight_kernel(
+template <int G>
+__global__ __launch_bounds__(kSearchThreads, 2) void search_weight_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int n_grid, const float* __restrict__ S,
     const float* __restrict__ C2, float* __restrict__ partials) {
-  constexpr int LPG = G / 16;                  // lanes per group row
+  constexpr int R = kSearchR;
+  constexpr int LPG = G / kSearchE;            // lanes per group row (1, 2 or 4)
   constexpr int RS = kSearchThreads / LPG;     // row slots per block
   constexpr int RB = RS * R;                   // rows per block
+  constexpr int NC = kSearchE / 8;             // 16-byte chunks per lane and row
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   extern __shared__ float lds[];               // s [n_grid][G], then (x/s)^2 [n_grid][G]
   float* s_l = lds;
   float* c_l = lds + n_grid * G;
-  __shared__ float red[kMaxGrid][4];
+  __shared__ float red[kMaxGrid][kSearchThreads / 16];
 
   const int64_t n_gcol = d_in / G;
   const int64_t gcol = blockIdx.x % n_gcol;
@@ -54,48 +67,52 @@ __global__ __launch_bounds__(kSearchThreads) void search_weight_kernel(
 
   const int lg = tid % LPG;
   const int slot = tid / LPG;
-  const int cc = lg * 16;
-  float w[R][16];
+  // chunk c of this lane covers group columns (c * LPG + lg) * 8 .. + 7
+  uint4 w[R][NC];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t row = rblk * RB + slot + (int64_t)RS * r;
     if (row < d_out) {
-      const uint4* p = (const uint4*)(row_ptr(P, row, d_in) + c0 + cc);
-      const uint4 a = ld_nt(p);
-      const uint4 b = ld_nt(p + 1);
-      unpack8_f16(a, w[r]);
-      unpack8_f16(b, w[r] + 8);
+      const uint4* p = (const uint4*)(row_ptr(P, row, d_in) + c0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) w[r][c] = ld_nt(p + c * LPG + lg);
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) w[r][j] = 0.0f;
+      for (int c = 0; c < NC; ++c) w[r][c] = make_uint4(0, 0, 0, 0);
     }
   }
   __syncthreads();
 
   for (int k = 0; k < n_grid; ++k) {
-    float s[16];
+    float s[kSearchE];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 t = ((const float4*)(s_l + k * G + cc))[j];
-      s[4 * j] = t.x; s[4 * j + 1] = t.y; s[4 * j + 2] = t.z; s[4 * j + 3] = t.w;
+    for (int c = 0; c < NC; ++c) {
+      const float4* sp = (const float4*)(s_l + k * G + (c * LPG + lg) * 8);
+      const float4 t0 = sp[0], t1 = sp[1];
+      s[8 * c + 0] = t0.x; s[8 * c + 1] = t0.y; s[8 * c + 2] = t0.z; s[8 * c + 3] = t0.w;
+      s[8 * c + 4] = t1.x; s[8 * c + 5] = t1.y; s[8 * c + 6] = t1.z; s[8 * c + 7] = t1.w;
     }
-    float acc[16];
+    float acc[kSearchE];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+    for (int j = 0; j < kSearchE; ++j) acc[j] = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float v[16];
-      float m = 0.0f;
+      float v[kSearchE];
+      float m = kTinyMax;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        v[j] = w[r][j] * s[j];
-        m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+      for (int c = 0; c < NC; ++c) {
+        const h8 h = __builtin_bit_cast(h8, w[r][c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[8 * c + e] = __builtin_fmaf((float)h[e], s[8 * c + e], 0.0f);
+          m = __builtin_fmaxf(m, __builtin_fabsf(v[8 * c + e]));
+        }
       }
-      m = group_max<LPG>(m);
+      m = group_max_nonneg<LPG>(m);
       const float step = div7(m);
-      const float inv = m > 0.0f ? __builtin_amdgcn_rcpf(step) : 0.0f;
+      const float inv = __builtin_amdgcn_rcpf(step);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < kSearchE; ++j) {
         const float q = __builtin_rintf(v[j] * inv);
         const float d = __builtin_fmaf(-step, q, v[j]);
         acc[j] = __builtin_fmaf(d, d, acc[j]);
@@ -103,19 +120,29 @@ __global__ __launch_bounds__(kSearchThreads) void search_weight_kernel(
     }
     float e = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 t = ((const float4*)(c_l + k * G + cc))[j];
-      e = __builtin_fmaf(t.x, acc[4 * j], e);
-      e = __builtin_fmaf(t.y, acc[4 * j + 1], e);
-      e = __builtin_fmaf(t.z, acc[4 * j + 2], e);
-      e = __builtin_fmaf(t.w, acc[4 * j + 3], e);
+    for (int c = 0; c < NC; ++c) {
+      const float4* cp = (const float4*)(c_l + k * G + (c * LPG + lg) * 8);
+      const float4 t0 = cp[0], t1 = cp[1];
+      e = __builtin_fmaf(t0.x, acc[8 * c + 0], e);
+      e = __builtin_fmaf(t0.y, acc[8 * c + 1], e);
+      e = __builtin_fmaf(t0.z, acc[8 * c + 2], e);
+      e = __builtin_fmaf(t0.w, acc[8 * c + 3], e);
+      e = __builtin_fmaf(t1.x, acc[8 * c + 4], e);
+      e = __builtin_fmaf(t1.y, acc[8 * c + 5], e);
+      e = __builtin_fmaf(t1.z, acc[8 * c + 6], e);
+      e = __builtin_fmaf(t1.w, acc[8 * c + 7], e);
     }
-    e = wave_sum(e);
-    if ((tid & 63) == 0) red[k][tid >> 6] = e;
+    e = row16_sum(e);
+    if ((tid & 15) == 0) red[k][tid >> 4] = e;
   }
   __syncthreads();
-  if (tid < n_grid)  // candidate-major: partials[k * n_blocks + block]
-    partials[(int64_t)tid * gridDim.x + blockIdx.x] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
+  if (tid < n_grid) {  // candidate-major: partials[k * n_blocks + block]
+    const float* q = red[tid];
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = q[2 * i] + q[2 * i + 1];
+    partials[(int64_t)tid * gridDim.x + blockIdx.x] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+  }
 }
 
 int64_t search_weight_blocks(int group_size, int64_t d_out, int64_t d_in) {
@@ -135,15 +162,15 @@ hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_o
   const size_t shm = (size_t)2 * n_grid * group_size * sizeof(float);
   switch (group_size) {
     case 32:
-      search_weight_kernel<32, kSearchR><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
+      search_weight_kernel<32><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
           parts, d_out, d_in, n_grid, S, C2, partials);
       break;
     case 64:
-      search_weight_kernel<64, kSearchR><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
+      search_weight_kernel<64><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
           parts, d_out, d_in, n_grid, S, C2, partials);
       break;
     default:
-      search_weight_kernel<128, kSearchR><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
+      search_weight_kernel<128><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
           parts, d_out, d_in, n_grid, S, C2, partials);
       break;
   }
