@@ -157,11 +157,18 @@ def bench_weight(args, wl_name: str):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # step time: K steps with nothing else on the stream (an event record
+    # costs several microseconds of GPU timeline, which would be charged to
+    # the method)
     t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    # kernel durations: the same K steps again, events around each kernel
     for i in range(K):
         step(i)
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / K
     k_ms = {"act_stats": 0.0, "search_weight": 0.0, "quantize_pack": 0.0}
     for i in range(K):
         k_ms["act_stats"] += ev.ms(6 * i, 6 * i + 1) / K
@@ -342,10 +349,13 @@ def bench_sweep(args):
             step()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for k in range(K):
-            step(k)
+        for _ in range(K):
+            step()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t1) * 1e3 / K
+        for k in range(K):  # kernel durations: same steps again with events around each kernel
+            step(k)
+        torch.cuda.synchronize()
         sums = [0.0, 0.0, 0.0]
         for n in range(0, per * K, 6):
             sums[0] += ev.ms(n, n + 1)

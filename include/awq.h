@@ -108,7 +108,8 @@ awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in
  *
  * x_mean: fp32 [d_in] (non-negative, finite); S: fp32 [n_grid, d_in].
  * Row 0 is exactly 1.0 (alpha = 0 is plain round-to-nearest).
- * ws: awq_candidate_scales_workspace(d_in, n_grid) bytes, 8-byte aligned.
+ * ws: awq_candidate_scales_workspace(d_in, n_grid) bytes; that is 0 in this
+ * version, so ws may be NULL (the argument is kept for later versions).
  * ------------------------------------------------------------------------- */
 awq_status awq_candidate_scales_workspace(int64_t d_in, int32_t n_grid, size_t* bytes /* [host] */);
 awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_grid, double s_min,

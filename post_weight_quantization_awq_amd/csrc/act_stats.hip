@@ -21,14 +21,14 @@ constexpr int kStatsCols = 64 * 8;  // channels per block
 constexpr int kRowsPerWaveIter = 16;  // rows whose loads one lane keeps in flight
 
 template <bool BF16>
-__device__ __forceinline__ void acc8(const uint4 u, double* acc) {
+__device__ __forceinline__ void acc8(const uint4 u, bool in, double* acc) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
     const float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
-    acc[2 * j] += (double)__builtin_fabsf(lo);
-    acc[2 * j + 1] += (double)__builtin_fabsf(hi);
+    acc[2 * j] += in ? (double)__builtin_fabsf(lo) : 0.0;
+    acc[2 * j + 1] += in ? (double)__builtin_fabsf(hi) : 0.0;
   }
 }
 
@@ -52,12 +52,18 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
     if (VEC && col0 + 8 <= d_in) {
       const uint16_t* p = X + col0;
       for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += 4 * kRowsPerWaveIter) {
+        // unconditional loads of a clamped row (rows past r_end add nothing):
+        // no branch between the loads and their uses, all 16 issue first and
+        // each use waits for its own load only
         uint4 u[kRowsPerWaveIter];
 #pragma unroll
-        for (int q = 0; q < kRowsPerWaveIter; ++q)
-          u[q] = (base + q < r_end) ? ld_nt(p + (base + q) * ld) : make_uint4(0u, 0u, 0u, 0u);
+        for (int q = 0; q < kRowsPerWaveIter; ++q) {
+          const int64_t r = base + q < r_end ? base + q : r_end - 1;
+          u[q] = ld_nt(p + r * ld);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < kRowsPerWaveIter; ++q) acc8<BF16>(u[q], acc);
+        for (int q = 0; q < kRowsPerWaveIter; ++q) acc8<BF16>(u[q], base + q < r_end, acc);
       }
     } else {
       for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += 4 * kRowsPerWaveIter) {
@@ -92,14 +98,26 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
 
 // 32 channels x 8 split-slices per block: each thread sums every 8th split
 // partial of one channel, the 8 slice sums are then added in a fixed order.
+constexpr int kFinalBatch = 8;
 __global__ __launch_bounds__(256) void act_stats_final_kernel(const double* __restrict__ part, int64_t n_split,
                                                              int64_t d_in, double inv_count, int accumulate,
                                                              float* __restrict__ x_mean) {
   const int lane = threadIdx.x & 31, slice = threadIdx.x >> 5;
   const int64_t i = (int64_t)blockIdx.x * 32 + lane;
   double s = 0.0;
-  if (i < d_in)
-    for (int64_t p = slice; p < n_split; p += 8) s += part[p * d_in + i];
+  if (i < d_in) {
+    for (int64_t p0 = slice; p0 < n_split; p0 += 8 * kFinalBatch) {
+      double v[kFinalBatch];  // loads in flight (clamped index), added in increasing p
+#pragma unroll
+      for (int u = 0; u < kFinalBatch; ++u) {
+        const int64_t p = p0 + 8 * (int64_t)u;
+        v[u] = part[(p < n_split ? p : n_split - 1) * d_in + i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kFinalBatch; ++u) s += p0 + 8 * (int64_t)u < n_split ? v[u] : 0.0;
+    }
+  }
   __shared__ double red[8][32];
   red[slice][lane] = s;
   __syncthreads();

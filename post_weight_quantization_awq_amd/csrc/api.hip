@@ -55,7 +55,7 @@ struct SearchPlan {
   int64_t T_pad, d_out_pad, K_pad, n_mt, ldc;  // output score: padded GEMM shapes, token tiles, partial ld
   int64_t n_x, n_db;    // output score: X max partials, dW max partials per candidate
   int cand_chunk;       // output score: candidates per dW chunk
-  size_t off_S, off_C2, off_cand, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
+  size_t off_S, off_C2, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
 };
 
 constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
@@ -66,8 +66,6 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
   size_t off = 0;
   p.off_S = off;
   off += align256((size_t)cfg.n_grid * d_in * sizeof(float));
-  p.off_cand = off;
-  off += align256(candidates_workspace_bytes(d_in, cfg.n_grid));
   p.off_tot = off;
   off += align256((size_t)kMaxGrid * sizeof(double));
   if (!p.output) {
@@ -174,7 +172,7 @@ awq_status awq_candidate_scales_workspace(int64_t d_in, int32_t n_grid, size_t* 
   if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
   if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
   if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
-  *bytes = align256(candidates_workspace_bytes(d_in, n_grid));
+  *bytes = 0;  // the table needs no scratch
   return ok();
 }
 
@@ -184,10 +182,9 @@ awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_gri
   if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
   if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
   if (!(s_min > 0.0 && isfinite(s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
-  const size_t need = candidates_workspace_bytes(d_in, n_grid);
-  if (!ws || ws_bytes < need) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
-  if ((uintptr_t)ws & 7u) return fail(AWQ_EALIGN, "ws not 8-byte aligned");
-  return hip_status(launch_candidates(x_mean, d_in, n_grid, s_min, S, nullptr, ws, (hipStream_t)stream),
+  (void)ws;
+  (void)ws_bytes;
+  return hip_status(launch_candidates(x_mean, d_in, n_grid, s_min, S, nullptr, (hipStream_t)stream),
                     "awq_candidate_scales");
 }
 
@@ -255,14 +252,14 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   if (!plan.output) {
     float* C2 = (float*)(base + plan.off_C2);
     float* part = (float*)(base + plan.off_part);
-    if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, C2, base + plan.off_cand, s)) != hipSuccess)
+    if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, C2, s)) != hipSuccess)
       return hip_status(e, "candidates");
     mark(true, s);
     e = launch_search_weight(cfg->group_size, parts, d_out, d_in, cfg->n_grid, S, C2, part, s);
     mark(false, s);
     if (e != hipSuccess) return hip_status(e, "search_weight");
-    if ((e = launch_select(part, plan.n_blocks, cfg->n_grid, 1, plan.n_blocks, 1.0, nullptr,
-                           (double*)(base + plan.off_tot), err, best_idx, S, d_in, best_s, s)) != hipSuccess)
+    if ((e = launch_select(part, plan.n_blocks, cfg->n_grid, 1.0, nullptr, (double*)(base + plan.off_tot), err,
+                           best_idx, S, d_in, best_s, s)) != hipSuccess)
       return hip_status(e, "select");
     return ok();
   }
@@ -278,7 +275,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   OutScales* sc_c = (OutScales*)(base + plan.off_sc + align256(sizeof(OutScales)));
   const int G = cfg->group_size;
   const int64_t dop = plan.d_out_pad, kp = plan.K_pad;
-  if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, nullptr, base + plan.off_cand, s)) != hipSuccess)
+  if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, nullptr, s)) != hipSuccess)
     return hip_status(e, "candidates");
   if ((e = launch_prepare_x(X, bf16, T, d_in, ld_x, xmax, s)) != hipSuccess) return hip_status(e, "absmax(X)");
   if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax,
@@ -301,11 +298,13 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
     if (e != hipSuccess) return hip_status(e, "gemm_sq");
   }
   if (!one_chunk) mark(false, s);
-  if ((e = launch_reduce_cols(colpart, plan.n_mt, plan.ldc, d_out, dop, cfg->n_grid, 1.0 / ((double)T * (double)d_out),
-                              sc_a, (double*)(base + plan.off_chunk), tot, s)) != hipSuccess)
+  double* chunk_sum = (double*)(base + plan.off_chunk);
+  const int64_t nch = reduce_cols_chunks(d_out);
+  if ((e = launch_reduce_cols(colpart, plan.n_mt, plan.ldc, d_out, dop, cfg->n_grid, chunk_sum, s)) != hipSuccess)
     return hip_status(e, "reduce_cols");
-  if ((e = launch_argmin(tot, cfg->n_grid, err, best_idx, S, d_in, best_s, s)) != hipSuccess)
-    return hip_status(e, "argmin");
+  if ((e = launch_select(chunk_sum, nch, cfg->n_grid, 1.0 / ((double)T * (double)d_out), sc_a->inv, tot, err,
+                         best_idx, S, d_in, best_s, s)) != hipSuccess)
+    return hip_status(e, "select");
   if (cfg->n_clip >= 2) {
     const int nclip = cfg->n_clip;
     if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0,

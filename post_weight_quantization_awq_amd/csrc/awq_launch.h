@@ -17,11 +17,9 @@ hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, i
                             float inv_count, int accumulate, float* x_mean, void* ws,
                             hipStream_t stream);
 
-// candidate scale table S [n_grid, d_in] and, if C2 != nullptr, (x/s)^2 [n_grid, d_in];
-// ws: candidates_workspace_bytes(d_in, n_grid) bytes (8-byte aligned)
-size_t candidates_workspace_bytes(int64_t d_in, int n_grid);
+// candidate scale table S [n_grid, d_in] and, if C2 != nullptr, (x/s)^2 [n_grid, d_in]
 hipError_t launch_candidates(const float* x_mean, int64_t d_in, int n_grid, double s_min, float* S,
-                             float* C2, void* ws, hipStream_t stream);
+                             float* C2, hipStream_t stream);
 
 // weight-score search: per-block partial errors, candidate-major [n_grid, n_blocks]
 int64_t search_weight_blocks(int group_size, int64_t d_out, int64_t d_in);
@@ -29,17 +27,16 @@ hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_o
                                 int n_grid, const float* S, const float* C2, float* partials,
                                 hipStream_t stream);
 
-// reduce partials p[b * stride_b + c * stride_c] over b (fixed order, fp64) ->
-// err [n_cand] (times `scale`, and times cand_scale[c] when given), first-minimum
-// index -> best_idx, best_s = S[best]
-// first minimum of tot [n_cand] -> err (fp32), best_idx, best_s = S[best]
-hipError_t launch_argmin(const double* tot, int n_cand, float* err, int32_t* best_idx, const float* S, int64_t d_in,
-                         float* best_s, hipStream_t stream);
-// tot: [n_cand] fp64 scratch
-hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, int64_t stride_b,
-                         int64_t stride_c, double scale, const double* cand_scale, double* tot, float* err,
-                         int32_t* best_idx, const float* S, int64_t d_in, float* best_s,
-                         hipStream_t stream);
+// reduce partials p[c * n_blocks + b] over b (fixed order, fp64), times `scale`
+// and cand_scale[c] when given -> tot [n_cand] (fp64) and err [n_cand] (fp32);
+// smallest index attaining the minimum -> best_idx; if S is given,
+// best_s = S[best] [d_in].  One launch.
+hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, double scale,
+                         const double* cand_scale, double* tot, float* err, int32_t* best_idx, const float* S,
+                         int64_t d_in, float* best_s, hipStream_t stream);
+hipError_t launch_select(const double* partials, int64_t n_blocks, int n_cand, double scale,
+                         const double* cand_scale, double* tot, float* err, int32_t* best_idx, const float* S,
+                         int64_t d_in, float* best_s, hipStream_t stream);
 
 // output-score search
 // X -> per-block max |X| [absmax_blocks(T)]
@@ -66,12 +63,11 @@ hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, i
 // colpart[mt * ldc + n] = sum over the 256 tokens of tile mt of Y[t, n]^2
 hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                           float* colpart, int64_t ldc, hipStream_t stream);
-// tot[c] = scale * sc->inv[c] * sum_mt sum_{o < d_out} colpart[mt * ldc + c * d_out_pad + o];
-// chunk_sum: [n_cand, reduce_cols_chunks(d_out)] fp64 scratch
+// chunk_sum[c, ch] = sum_mt sum_{o in chunk ch, o < d_out} colpart[mt * ldc + c * d_out_pad + o]
+// (fp64, fixed order), [n_cand, reduce_cols_chunks(d_out)]
 int64_t reduce_cols_chunks(int64_t d_out);
 hipError_t launch_reduce_cols(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
-                              int n_cand, double scale, const OutScales* sc, double* chunk_sum, double* tot,
-                              hipStream_t stream);
+                              int n_cand, double* chunk_sum, hipStream_t stream);
 // per-row argmin over clip ratios: E[o, j] = sc->inv[j] * sum_mt colpart[mt * ldc + j * d_out_pad + o]
 hipError_t launch_clip_select(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
                               int n_clip, float clip_lo, const OutScales* sc, float* clip, float* clip_err,

@@ -518,24 +518,13 @@ __global__ __launch_bounds__(kColChunk) void reduce_cols_kernel(const float* __r
   if (threadIdx.x == 0) chunk_sum[(int64_t)c * gridDim.x + blockIdx.x] = red[0];
 }
 
-__global__ void sum_chunks_kernel(const double* __restrict__ chunk_sum, int64_t n_chunk, int n_cand, double scale,
-                                  const OutScales* __restrict__ sc, double* __restrict__ tot) {
-  const int c = threadIdx.x;
-  if (c >= n_cand) return;
-  double t = 0.0;
-  for (int64_t k = 0; k < n_chunk; ++k) t += chunk_sum[(int64_t)c * n_chunk + k];
-  tot[c] = t * scale * sc->inv[c];
-}
-
 int64_t reduce_cols_chunks(int64_t d_out) { return (d_out + kColChunk - 1) / kColChunk; }
 
 hipError_t launch_reduce_cols(const float* colpart, int64_t n_mt, int64_t ldc, int64_t d_out, int64_t d_out_pad,
-                              int n_cand, double scale, const OutScales* sc, double* chunk_sum, double* tot,
-                              hipStream_t stream) {
+                              int n_cand, double* chunk_sum, hipStream_t stream) {
   const int64_t nch = reduce_cols_chunks(d_out);
   reduce_cols_kernel<<<dim3((unsigned)nch, (unsigned)n_cand), kColChunk, 0, stream>>>(colpart, n_mt, ldc, d_out,
                                                                                       d_out_pad, chunk_sum);
-  sum_chunks_kernel<<<1, 64, 0, stream>>>(chunk_sum, nch, n_cand, scale, sc, tot);
   return hipGetLastError();
 }
 

@@ -73,10 +73,17 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
     sv[0] = a.x; sv[1] = a.y; sv[2] = a.z; sv[3] = a.w;
     sv[4] = b.x; sv[5] = b.y; sv[6] = b.z; sv[7] = b.w;
   }
+  // Unconditional loads (a lane past d_out reads rows 0..7 and stores
+  // nothing), so the wait before row r covers only rows 0..r.
+  const int64_t lrow = valid ? row0 : 0;
+  float cl[8];
+  if constexpr (HAS_CLIP) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) cl[r] = clip[lrow + r];
+  }
   uint4 raw[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-    raw[r] = valid ? ld_nt(W + (row0 + r) * d_in + col0) : make_uint4(0u, 0u, 0u, 0u);
+  for (int r = 0; r < 8; ++r) raw[r] = ld_nt(W + (lrow + r) * d_in + col0);
 
   int32_t words[8];
 #pragma unroll
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
     for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
     m = group_max<SH::LPG>(m);
     float a = m;
-    if constexpr (HAS_CLIP) a = valid ? clip[row0 + r] * m : m;
+    if constexpr (HAS_CLIP) a = cl[r] * m;
     const float step = div7(a);
     const float inv = __builtin_amdgcn_rcpf(step);
     float n[8];
@@ -121,6 +128,9 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
     const uint32_t hb = f2h_bits(step);
     if (r & 1) sbits[r >> 1] |= hb << 16;
     else sbits[r >> 1] = hb;
+    // keep rows apart: row r then waits only for its own load, so the
+    // arithmetic of early rows overlaps the loads of later ones
+    __builtin_amdgcn_sched_barrier(0);
   }
 
 #pragma unroll

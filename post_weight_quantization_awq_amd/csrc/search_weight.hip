@@ -38,6 +38,89 @@ constexpr float kTinyMax = 0x1p-100f;
 template <int G>
 constexpr int search_rows_per_block() { return (kSearchThreads / (G / kSearchE)) * kSearchR; }
 
+// ---------------------------------------------------------------------------
+// Selection ("AWQ architecture, in depth", "The scale search as code": keep the
+// candidate when err < best, i.e. the first minimum), run by one whole block.
+// Wave w owns candidates w, w + NW, ...; lane l sums blocks b = l, l + 64, ...
+// of each in fp64, in increasing b, then a fixed shuffle tree finishes the
+// candidate's sum, so the result does not depend on scheduling.  Loads are
+// issued kSelBatch at a time across the wave's candidates to keep many in
+// flight.  Wave 0 then picks the smallest index attaining the minimum and the
+// block copies the winner's scale row.
+// ---------------------------------------------------------------------------
+constexpr int kSelBatch = 32;
+
+template <typename TP, int NT>
+__device__ __forceinline__ void select_block(const TP* __restrict__ part, int n_blocks, int n_cand, double scale,
+                                             const double* __restrict__ cand_scale, double* __restrict__ tot,
+                                             float* __restrict__ err, int32_t* __restrict__ best_idx,
+                                             const float* __restrict__ S, int64_t d_in,
+                                             float* __restrict__ best_s, double* tot_sh, int* best_sh) {
+  constexpr int NW = NT / kWave;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int n_u = (n_blocks + kWave - 1) / kWave;                  // loads per lane and candidate
+  const int my_c = wave < n_cand ? (n_cand - wave + NW - 1) / NW : 0;
+  const int total = my_c * n_u;
+  double acc = 0.0;
+  int ci = 0, uu = 0;  // position of load j0: candidate wave + ci * NW, lane block uu * 64 + lane
+  for (int j0 = 0; j0 < total; j0 += kSelBatch) {
+    TP v[kSelBatch];
+    bool ok[kSelBatch];
+    int c = ci, q = uu;
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {  // unconditional loads (clamped), masked when added
+      const int b = q * kWave + lane;
+      ok[u] = j0 + u < total && b < n_blocks;
+      v[u] = part[ok[u] ? (int64_t)(wave + c * NW) * n_blocks + b : 0];
+      if (++q == n_u) {
+        q = 0;
+        ++c;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      if (j0 + u < total) {
+        acc += ok[u] ? (double)v[u] : 0.0;
+        if (++uu == n_u) {  // last load of this candidate (uniform over the wave)
+          const double t = wave_sum_d(acc);
+          const int cc = wave + ci * NW;
+          if (lane == 0) tot_sh[cc] = t * scale * (cand_scale != nullptr ? cand_scale[cc] : 1.0);
+          acc = 0.0;
+          uu = 0;
+          ++ci;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool live = lane < n_cand;
+    const double t = live ? tot_sh[lane] : __builtin_inf();
+    if (live) {
+      tot[lane] = t;
+      err[lane] = (float)t;
+    }
+    double mn = t;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const double o = __shfl_xor(mn, m, kWave);
+      mn = o < mn ? o : mn;
+    }
+    const unsigned long long hit = __ballot(live && t == mn);
+    const int b = hit ? __ffsll((long long)hit) - 1 : 0;
+    if (lane == 0) {
+      best_idx[0] = b;
+      *best_sh = b;
+    }
+  }
+  __syncthreads();
+  if (S != nullptr) {
+    const float* src = S + (int64_t)*best_sh * d_in;
+    for (int64_t i = threadIdx.x; i < d_in; i += NT) best_s[i] = src[i];
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(kSearchThreads, 2) void search_weight_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int n_grid, const float* __restrict__ S,
@@ -177,69 +260,35 @@ hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_o
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Selection ("AWQ architecture, in depth", "The scale search as code": keep the
-// candidate when err < best, i.e. the first minimum).  One block per candidate
-// sums its partials in a fixed order in fp64; one block then picks the first
-// minimum and copies the winner's scale row.
-// ---------------------------------------------------------------------------
-constexpr int kRedThreads = 256;
+// Selection kernel: one block of kSelThreads.
+constexpr int kSelThreads = 1024;
 
-__global__ __launch_bounds__(kRedThreads) void reduce_cand_kernel(const float* __restrict__ partials,
-                                                                 int64_t n_blocks, int64_t stride_b,
-                                                                 int64_t stride_c, double scale,
-                                                                 const double* __restrict__ cand_scale,
-                                                                 double* __restrict__ tot) {
-  const int c = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float* p = partials + (int64_t)c * stride_c;
-  double acc = 0.0;
-  for (int64_t b = tid; b < n_blocks; b += kRedThreads) acc += (double)p[b * stride_b];
-  __shared__ double red[kRedThreads];
-  red[tid] = acc;
-  __syncthreads();
-  for (int w = kRedThreads / 2; w >= 1; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) tot[c] = red[0] * scale * (cand_scale != nullptr ? cand_scale[c] : 1.0);
-}
-
-__global__ __launch_bounds__(kRedThreads) void argmin_kernel(const double* __restrict__ tot, int n_cand,
-                                                            float* __restrict__ err, int32_t* __restrict__ best_idx,
+template <typename TP>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const TP* __restrict__ part, int n_blocks, int n_cand,
+                                                            double scale, const double* __restrict__ cand_scale,
+                                                            double* __restrict__ tot, float* __restrict__ err,
+                                                            int32_t* __restrict__ best_idx,
                                                             const float* __restrict__ S, int64_t d_in,
                                                             float* __restrict__ best_s) {
+  __shared__ double tot_sh[kMaxGrid];
   __shared__ int best_sh;
-  if (threadIdx.x == 0) {
-    int b = 0;
-    double be = tot[0];
-    for (int c = 0; c < n_cand; ++c) {
-      err[c] = (float)tot[c];
-      if (tot[c] < be) { be = tot[c]; b = c; }
-    }
-    best_idx[0] = b;
-    best_sh = b;
-  }
-  __syncthreads();
-  if (S != nullptr) {
-    const float* src = S + (int64_t)best_sh * d_in;
-    for (int64_t i = threadIdx.x; i < d_in; i += kRedThreads) best_s[i] = src[i];
-  }
+  select_block<TP, kSelThreads>(part, n_blocks, n_cand, scale, cand_scale, tot, err, best_idx, S, d_in, best_s,
+                                tot_sh, &best_sh);
 }
 
-hipError_t launch_argmin(const double* tot, int n_cand, float* err, int32_t* best_idx, const float* S, int64_t d_in,
-                         float* best_s, hipStream_t stream) {
-  argmin_kernel<<<1, kRedThreads, 0, stream>>>(tot, n_cand, err, best_idx, S, d_in, best_s);
+hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, double scale,
+                         const double* cand_scale, double* tot, float* err, int32_t* best_idx, const float* S,
+                         int64_t d_in, float* best_s, hipStream_t stream) {
+  select_kernel<float><<<1, kSelThreads, 0, stream>>>(partials, (int)n_blocks, n_cand, scale, cand_scale, tot, err,
+                                                      best_idx, S, d_in, best_s);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, int64_t stride_b,
-                         int64_t stride_c, double scale, const double* cand_scale, double* tot, float* err,
-                         int32_t* best_idx, const float* S, int64_t d_in, float* best_s,
-                         hipStream_t stream) {
-  reduce_cand_kernel<<<n_cand, kRedThreads, 0, stream>>>(partials, n_blocks, stride_b, stride_c, scale,
-                                                         cand_scale, tot);
-  argmin_kernel<<<1, kRedThreads, 0, stream>>>(tot, n_cand, err, best_idx, S, d_in, best_s);
+hipError_t launch_select(const double* partials, int64_t n_blocks, int n_cand, double scale,
+                         const double* cand_scale, double* tot, float* err, int32_t* best_idx, const float* S,
+                         int64_t d_in, float* best_s, hipStream_t stream) {
+  select_kernel<double><<<1, kSelThreads, 0, stream>>>(partials, (int)n_blocks, n_cand, scale, cand_scale, tot, err,
+                                                       best_idx, S, d_in, best_s);
   return hipGetLastError();
 }
 

@@ -152,8 +152,9 @@ def test_search_validation(A):
 def test_candidate_validation(A):
     L = A.lib()
     n = ctypes.c_size_t()
-    assert L.awq_candidate_scales_workspace(4096, 20, ctypes.byref(n)) == 0 and n.value > 0
-    assert L.awq_candidate_scales(FAKE, 4096, 20, 1e-4, FAKE, FAKE, n.value - 8, None) == A.AWQ_EWORKSPACE
+    # the table needs no scratch: zero bytes, ws may be NULL
+    assert L.awq_candidate_scales_workspace(4096, 20, ctypes.byref(n)) == 0 and n.value == 0
+    assert L.awq_candidate_scales_workspace(4096, 65, ctypes.byref(n)) == A.AWQ_EINVAL
     assert L.awq_candidate_scales(FAKE, 4096, 0, 1e-4, FAKE, FAKE, n.value, None) == A.AWQ_EINVAL
     assert L.awq_candidate_scales(FAKE, 4096, 20, 0.0, FAKE, FAKE, n.value, None) == A.AWQ_EINVAL
     assert L.awq_candidate_scales(None, 4096, 20, 1e-4, FAKE, FAKE, n.value, None) == A.AWQ_EINVAL
