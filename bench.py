@@ -8,9 +8,13 @@ workload is a Qwen3-8B q_proj-shaped linear (W 4096 x 4096 fp16, X 4096
 tokens x 4096 bf16, group size 128, weight-domain activation-weighted error).
 
 Prints ONE JSON line.  `value` is weight-elements x grid-points per second of
-the whole step; per-kernel times come from HIP events recorded by the library
-around its main kernels on the stream they run on; `roofline` describes the
-dominant kernel; `cpu_baseline` times the CPU oracle on a bounded sample.
+the whole step, timed over K steps with nothing else on the stream; per-kernel
+times come from a second pass over the same K steps in which the library
+records HIP events around its main kernels on the stream they run on (an event
+record costs microseconds of GPU timeline, so it stays out of the step time);
+`roofline` describes the dominant kernel (traffic from committed counter runs,
+null once its sources change); `cpu_baseline` times the CPU oracle on a
+bounded sample.
 
 Other workloads (--workload) measure the remaining rows: the output-score
 search on the matrix cores (fused QKV, MLP with clip search) and the full
@@ -20,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +43,40 @@ VALU_LANE_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.32 T fp32 lane-ops/s (
 # scale (mul), group max (max), v / step (mul by reciprocal), round (rndne),
 # residual v - q*step (fma), square-accumulate (fma)
 SEARCH_OPS_PER_ELEM_PT = 6
+# HBM bytes per launch of the dominant kernels, from `rocprofv3 --pmc FETCH_SIZE`
+# and `--pmc WRITE_SIZE` runs of this script (commands and tables in
+# profiles/search_weight_q_proj_4096x4096.md and
+# profiles/gemm_sq_qkv_6144x4096_output.md): KiB per dispatch, scaled by what
+# the same counters read for a plain copy of known size
+# (profiles/copy_512MiB_calibration.md).  Each entry records the sha256 of the
+# sources its kernel is built from; once those change, the counters describe
+# another kernel and traffic is reported as null.
+FETCH_CAL, WRITE_CAL = 2.0, 1.0
+PMC_TRAFFIC = {
+    ("search_weight_kernel", "q_proj_4096x4096"): {
+        "fetch_kib": 16782.3, "write_kib": 320.0,
+        "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
+        "sha256": "d47104ef2d0a585d2ea4bd48bb967ba2a5fb19377a914f3e53282dc4c07e176d"},
+    ("gemm_sq_kernel", "qkv_6144x4096_output"): {
+        "fetch_kib": 12857120.5, "write_kib": 30720.0,
+        "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
+        "sha256": "e101829c07f90125bc6936008a391cfb3491b79eadcb8a3d2777ca96012d3aaa"},
+}
+
+
+def pmc_traffic(kernel: str, workload: str):
+    """Calibrated HBM bytes per launch, or None (no counters for this kernel and
+    workload, or sources changed since they were taken)."""
+    e = PMC_TRAFFIC.get((kernel, workload))
+    if e is None:
+        return None
+    h = hashlib.sha256()
+    for rel in e["sources"]:
+        with open(os.path.join(ROOT, "post_weight_quantization_awq_amd", rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != e["sha256"]:
+        return None
+    return 1024.0 * (FETCH_CAL * e["fetch_kib"] + WRITE_CAL * e["write_kib"])
 
 
 class HipEvents:
@@ -196,7 +235,8 @@ def bench_weight(args, wl_name: str):
         "act_stats_GBps": (2 * T * d_in + 4 * d_in) / (k_ms["act_stats"] * 1e-3) / 1e9,
         "kernel_us": {k: v * 1e3 for k, v in k_ms.items()},
         "roofline": {"bound": "alu", "achieved": achieved_ops, "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s",
-                     "frac": achieved_ops / VALU_LANE_OPS_PEAK_T, "traffic": None,
+                     "frac": achieved_ops / VALU_LANE_OPS_PEAK_T,
+                     "traffic": pmc_traffic("search_weight_kernel", wl_name),
                      "kernel": "search_weight_kernel",
                      "ops_per_elem_pt": SEARCH_OPS_PER_ELEM_PT},
     }
@@ -264,10 +304,13 @@ def bench_output(args, wl_name: str):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for k in range(K):
-        step(k)
+    for _ in range(K):
+        step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t1) * 1e3 / K
+    for k in range(K):  # GEMM durations: same steps again with events around the GEMMs
+        step(k)
+    torch.cuda.synchronize()
     gemm_ms = [sum(ev.ms(2 * (k * n_pl + i), 2 * (k * n_pl + i) + 1) for k in range(K)) / K for i in range(n_pl)]
     ev.close()
     n_elem_pts = sum(g.d_out * g.d_in for _, _, g, *_ in plans) * 20
@@ -288,7 +331,8 @@ def bench_output(args, wl_name: str):
         "step_TFLOPs_algorithmic": total_flops / (ms_step * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": None, "kernel": "gemm_sq_kernel"},
+                     "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": pmc_traffic("gemm_sq_kernel", wl_name),
+                     "kernel": "gemm_sq_kernel"},
     }
 
 
