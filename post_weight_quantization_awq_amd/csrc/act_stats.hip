@@ -4,24 +4,41 @@
 // as code" (x.abs().float().mean(dim=0)).
 //
 // HBM-bound column reduction: 2 bytes read per element.  Each lane owns 8
-// consecutive channels (one 16-byte load per token row) and keeps 16 row loads
-// in flight; the 4 waves of a block take 16-row slices; blocks split the token
-// axis.  Per-lane sums are
-// fp64 (full rate on CDNA4 VALU), the split partials are combined in a fixed
-// order by a second kernel, so the result is deterministic and independent of
-// the launch shape up to fp64 rounding.
+// consecutive channels (one 16-byte load per token row); a block is 64 lanes
+// wide and 4 waves tall, the 4 waves taking 16-row slices of each 64-row
+// step; blocks split the token axis.  Per-lane sums are fp64 (full rate on
+// CDNA4 VALU), the split partials are combined in a fixed order by a second
+// kernel, so the result is deterministic and independent of the launch shape
+// up to fp64 rounding.
+//
+// The token axis is cut into whole splits of a multiple of 64 rows, streamed
+// by the main kernel (no bounds logic: every 16-row batch is full), and the
+// leftover rows, cut into 64-row splits for the generic kernel, which also
+// covers unaligned inputs.
 #include "awq_device.h"
 #include "awq_launch.h"
 
 namespace awq {
 
 constexpr int kStatsThreads = 256;
-constexpr int kStatsCols = 64 * 8;  // channels per block
-
-constexpr int kRowsPerWaveIter = 16;  // rows whose loads one lane keeps in flight
+constexpr int kStatsCols = 64 * 8;    // channels per block
+constexpr int kRowsPerWaveIter = 16;  // rows per batch of one wave
+constexpr int64_t kStepRows = 4 * kRowsPerWaveIter;
 
 template <bool BF16>
-__device__ __forceinline__ void acc8(const uint4 u, bool in, double* acc) {
+__device__ __forceinline__ void acc8(const uint4 u, double* acc) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
+    const float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
+    acc[2 * j] += (double)__builtin_fabsf(lo);
+    acc[2 * j + 1] += (double)__builtin_fabsf(hi);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void acc8_masked(const uint4 u, bool in, double* acc) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -32,18 +49,68 @@ __device__ __forceinline__ void acc8(const uint4 u, bool in, double* acc) {
   }
 }
 
-// Block: 64 lanes x 8 channels wide, 4 waves; the block's token range is walked
-// in 64-row steps, wave w taking rows w*16 .. w*16+15 of each step with all 16
-// loads issued before any is used.
+// The WAVES waves' 8 channel sums of the block -> part[split][channel], added
+// in wave order.
+template <int WAVES>
+__device__ __forceinline__ void store_partials(const double* acc, int wv, int lane, int64_t split, int64_t d_in,
+                                               double* __restrict__ part) {
+  __shared__ double red[WAVES][64 * 8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[wv][lane * 8 + j] = acc[j];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 64 * 8; idx += WAVES * 64) {
+    const int64_t c = (int64_t)blockIdx.x * kStatsCols + idx;
+    if (c < d_in) {
+      double s = red[0][idx];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) s += red[w][idx];
+      part[split * d_in + c] = s;
+    }
+  }
+}
+
+// Main kernel: a block of 4 waves covers rows [y * 4 ROWS, (y + 1) * 4 ROWS),
+// all inside X (X 16-byte aligned, ld and d_in multiples of 8); every wave
+// issues its ROWS row loads at once and adds them as they arrive.  One batch
+// per wave and small blocks dispatched split by split keep the rows read at
+// any moment contiguous in memory and leave several blocks per CU to cover
+// each other's reduction tails: measured on a 512 MB input this runs at
+// ~7 TB/s, where waves that stream several batches each (two register sets,
+// a rolling prefetch) or 16-wave blocks (one per CU) reach 4.7-6 TB/s.
+template <bool BF16, int ROWS>
+__global__ __launch_bounds__(kStatsThreads) void act_stats_main_kernel(const uint16_t* __restrict__ X, int64_t d_in,
+                                                                      int64_t ld, double* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int64_t col0 = ((int64_t)blockIdx.x * 64 + lane) * 8;
+  double acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+  if (col0 < d_in) {
+    const uint16_t* p = X + ((int64_t)blockIdx.y * (4 * ROWS) + wv * ROWS) * ld + col0;
+    uint4 u[ROWS];
+#pragma unroll
+    for (int q = 0; q < ROWS; ++q) u[q] = ld_nt(p + q * ld);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < ROWS; ++q) acc8<BF16>(u[q], acc);
+  }
+  store_partials<4>(acc, wv, lane, blockIdx.y, d_in, part);
+}
+
+// Generic kernel: split y covers rows [row0 + y * rps, min(T, ... + rps)) and
+// writes partial row split0 + y.  Rows past the end load a clamped row and add
+// nothing (no branch between the 16 loads and their uses); unaligned inputs
+// take scalar loads.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
-    const uint16_t* __restrict__ X, int64_t T, int64_t d_in, int64_t ld, int64_t rows_per_split,
+    const uint16_t* __restrict__ X, int64_t T, int64_t d_in, int64_t ld, int64_t row0, int64_t rps, int64_t split0,
     double* __restrict__ part) {
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t col0 = ((int64_t)blockIdx.x * 64 + lane) * 8;
-  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_split;
-  const int64_t r_end = min(T, r_begin + rows_per_split);
+  const int64_t r_begin = row0 + (int64_t)blockIdx.y * rps;
+  const int64_t r_end = min(T, r_begin + rps);
   double acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0;
@@ -51,10 +118,7 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
   if (col0 < d_in) {
     if (VEC && col0 + 8 <= d_in) {
       const uint16_t* p = X + col0;
-      for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += 4 * kRowsPerWaveIter) {
-        // unconditional loads of a clamped row (rows past r_end add nothing):
-        // no branch between the loads and their uses, all 16 issue first and
-        // each use waits for its own load only
+      for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += kStepRows) {
         uint4 u[kRowsPerWaveIter];
 #pragma unroll
         for (int q = 0; q < kRowsPerWaveIter; ++q) {
@@ -63,10 +127,10 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < kRowsPerWaveIter; ++q) acc8<BF16>(u[q], base + q < r_end, acc);
+        for (int q = 0; q < kRowsPerWaveIter; ++q) acc8_masked<BF16>(u[q], base + q < r_end, acc);
       }
     } else {
-      for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += 4 * kRowsPerWaveIter) {
+      for (int64_t base = r_begin + wv * kRowsPerWaveIter; base < r_end; base += kStepRows) {
         for (int64_t r = base; r < base + kRowsPerWaveIter && r < r_end; ++r) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -79,21 +143,7 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_partial_kernel(
       }
     }
   }
-
-  __shared__ double red[4][64 * 8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) red[wv][lane * 8 + j] = acc[j];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 64 * 8; idx += kStatsThreads) {
-    const int64_t c = (int64_t)blockIdx.x * kStatsCols + idx;
-    if (c < d_in) {
-      double s = red[0][idx];
-      s += red[1][idx];
-      s += red[2][idx];
-      s += red[3][idx];
-      part[(int64_t)blockIdx.y * d_in + c] = s;
-    }
-  }
+  store_partials<4>(acc, wv, lane, split0 + blockIdx.y, d_in, part);
 }
 
 // 32 channels x 8 split-slices per block: each thread sums every 8th split
@@ -131,19 +181,59 @@ __global__ __launch_bounds__(256) void act_stats_final_kernel(const double* __re
   }
 }
 
+// Whole splits of rps rows for the main kernel: 128 rows (32 per wave, fp64
+// partials at 1/32 of X's bytes) when that still gives at least 1024 blocks,
+// else 64; then the T % rps leftover rows in 64-row splits for the generic
+// kernel.
+static void stats_split(int64_t T, int64_t d_in, int64_t* rps, int64_t* n_main, int64_t* n_tail) {
+  const int64_t n_cb = (d_in + kStatsCols - 1) / kStatsCols;
+  *rps = (T / (2 * kStepRows)) * n_cb >= 1024 ? 2 * kStepRows : kStepRows;
+  *n_main = T / *rps;
+  *n_tail = (T - *n_main * *rps + kStepRows - 1) / kStepRows;
+}
+
 void act_stats_plan(int64_t T, int64_t d_in, int64_t* n_split, int64_t* rows_per_split) {
   if (T <= 0 || d_in <= 0) {
     *n_split = 0;
-    *rows_per_split = 64;
+    *rows_per_split = kStepRows;
     return;
   }
-  // 64 token rows per split (one row step of the 4 waves) up to 512 for long
-  // calibration sets, keeping the fp64 partials a few percent of X
-  int64_t rps = T / 256;
-  rps = rps < 64 ? 64 : (rps > 512 ? 512 : rps);
-  rps = (rps + 63) / 64 * 64;
+  int64_t rps, n_main, n_tail;
+  stats_split(T, d_in, &rps, &n_main, &n_tail);
   *rows_per_split = rps;
-  *n_split = (T + rps - 1) / rps;
+  *n_split = n_main + n_tail;
+}
+
+template <bool BF16>
+static void launch_stats_t(const uint16_t* x, int64_t T, int64_t d_in, int64_t ld, double* part,
+                           hipStream_t stream) {
+  int64_t rps, n_main, n_tail;
+  stats_split(T, d_in, &rps, &n_main, &n_tail);
+  const unsigned n_cb = (unsigned)((d_in + kStatsCols - 1) / kStatsCols);
+  const bool vec = ((uintptr_t)x % 16 == 0) && (ld % 8 == 0);
+  if (vec) {
+    if (n_main > 0) {
+      const dim3 grid(n_cb, (unsigned)n_main);
+      if (d_in % 8 == 0) {
+        if (rps == kStepRows)
+          act_stats_main_kernel<BF16, 16><<<grid, kStatsThreads, 0, stream>>>(x, d_in, ld, part);
+        else
+          act_stats_main_kernel<BF16, 32><<<grid, kStatsThreads, 0, stream>>>(x, d_in, ld, part);
+      } else
+        act_stats_partial_kernel<BF16, true><<<dim3(n_cb, (unsigned)n_main), kStatsThreads, 0, stream>>>(
+            x, T, d_in, ld, 0, rps, 0, part);
+    }
+    if (n_tail > 0)
+      act_stats_partial_kernel<BF16, true><<<dim3(n_cb, (unsigned)n_tail), kStatsThreads, 0, stream>>>(
+          x, T, d_in, ld, n_main * rps, kStepRows, n_main, part);
+  } else {
+    if (n_main > 0)
+      act_stats_partial_kernel<BF16, false><<<dim3(n_cb, (unsigned)n_main), kStatsThreads, 0, stream>>>(
+          x, T, d_in, ld, 0, rps, 0, part);
+    if (n_tail > 0)
+      act_stats_partial_kernel<BF16, false><<<dim3(n_cb, (unsigned)n_tail), kStatsThreads, 0, stream>>>(
+          x, T, d_in, ld, n_main * rps, kStepRows, n_main, part);
+  }
 }
 
 hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld,
@@ -153,16 +243,8 @@ hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, i
   act_stats_plan(T, d_in, &n_split, &rps);
   double* part = (double*)ws;
   if (n_split > 0) {
-    const bool vec = ((uintptr_t)X % 16 == 0) && (ld % 8 == 0);
-    dim3 grid((unsigned)((d_in + kStatsCols - 1) / kStatsCols), (unsigned)n_split);
-    const uint16_t* x = (const uint16_t*)X;
-    if (bf16) {
-      if (vec) act_stats_partial_kernel<true, true><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
-      else act_stats_partial_kernel<true, false><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
-    } else {
-      if (vec) act_stats_partial_kernel<false, true><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
-      else act_stats_partial_kernel<false, false><<<grid, kStatsThreads, 0, stream>>>(x, T, d_in, ld, rps, part);
-    }
+    if (bf16) launch_stats_t<true>((const uint16_t*)X, T, d_in, ld, part, stream);
+    else launch_stats_t<false>((const uint16_t*)X, T, d_in, ld, part, stream);
   }
   act_stats_final_kernel<<<(unsigned)((d_in + 31) / 32), 256, 0, stream>>>(
       part, n_split, d_in, (double)inv_count, accumulate, x_mean);
