@@ -410,8 +410,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
 
 // one stage: loads of kt + 2 (or a harmless in-bounds re-read) into (RA, RB),
 // MFMAs on lds[ST], store of kt + 1 from (SA, SB) into lds[ST ^ 1] (free since
-// the previous barrier; its registers arrived a stage ago) spread over the
-// first half of the MFMAs, barrier
+// the previous barrier) spread over the second half of the MFMAs, barrier.
+// Storing late gives the loads of kt + 1 (issued at the start of stage kt - 1)
+// about 1.5 stages to arrive before a store waits for them: measured 3-5%
+// faster than storing in the first half.
 #define AWQ_STAGE(ST, RA, RB, SA, SB)                                          \
   {                                                                            \
     const uint32_t k2 = (uint32_t)((kt + 2 < nk ? kt + 2 : kt + 1) * kBK * 2); \
@@ -421,22 +423,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
     lstore(lds[(ST) ^ 1][0], tid, SA);                                         \
     lstore(lds[(ST) ^ 1][1], tid, SB);                                         \
     /* order: the 16 loads; step 0's 8 fragment reads; steps 0-1: each     */ \
-    /* pair of MFMAs followed by one store of stage kt + 1 and one read of  */ \
-    /* the next step; step 2: pairs of MFMAs and reads; step 3: MFMAs       */ \
+    /* pair of MFMAs followed by one read of the next step; step 2: pairs   */ \
+    /* of MFMAs, each followed by a read of step 3 and a store of stage     */ \
+    /* kt + 1; step 3: pairs of MFMAs, each followed by a store             */ \
     __builtin_amdgcn_sched_group_barrier(0x020, 2 * kLoads, 0);                \
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                         \
-    for (int ks = 0; ks < 2; ++ks) {                                           \
-      for (int u = 0; u < 8; ++u) {                                            \
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                     \
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                     \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     \
-      }                                                                        \
+    for (int u = 0; u < 16; ++u) {                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                       \
     }                                                                          \
     for (int u = 0; u < 8; ++u) {                                              \
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                       \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                       \
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                       \
     }                                                                          \
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);                        \
+    for (int u = 0; u < 8; ++u) {                                              \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                       \
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                       \
+    }                                                                          \
     __syncthreads();                                                           \
   }
 
