@@ -278,10 +278,12 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 //    of the tile with zero rows; M and K padded likewise with zeros), and per
 //    column the sum over the block's 256 tokens of Y^2 -> colpart[mt][n].
 //
-//    Block tile 256 x 256, 4 waves (2 x 2), wave tile 128 x 128 = 4 x 4 MFMA
-//    32x32x16 f16 tiles; the 256 fp32 accumulators per lane live in AGPRs
-//    (one wave per SIMD).  A wave reads 8 fragments (8 KiB of LDS) per 16
-//    MFMAs.  K advances in stages of 32 through a ring of 4 LDS slots, one
+//    Block tile 256 x 256, 8 waves (2 x 4), wave tile 128 x 64 = 4 x 2 MFMA
+//    32x32x16 f16 tiles; 128 fp32 accumulators per lane, 168 registers in
+//    all, so two waves share a SIMD and one issues MFMAs while the other
+//    waits (measured 4-5% faster than 4 waves of 128 x 128 tiles with one
+//    wave per SIMD, 1.5% faster than 16 waves of 64 x 64).  A wave reads 6
+//    fragments (6 KiB of LDS) per 8 MFMAs.  K advances in stages of 32 through a ring of 4 LDS slots, one
 //    distinct array per slot and operand: the operands go from global memory
 //    straight into LDS (buffer loads with the LDS bit, 16 bytes per lane, no
 //    staging registers and no LDS store instructions), three stages ahead of
@@ -300,7 +302,7 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 //    A and B tiles in its L2.
 // ---------------------------------------------------------------------------
 constexpr int kBM = 256, kBN = 256, kBK = 32;
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 512;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
@@ -329,34 +331,34 @@ __shared__ __attribute__((aligned(1024))) uint16_t sB2[kBN * kBK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB3[kBN * kBK];
 
 // one operand tile (256 rows x 32 K) straight into LDS: wave w fetches rows
-// 64w .. 64w+63 in 4 loads of 16 rows; lane i lands in row 64w + 16n + i/4,
+// 32w .. 32w+31 in 2 loads of 16 rows; lane i lands in row 32w + 16n + i/4,
 // slot i%4, and fetches chunk (i%4) ^ swz(row) = (i%4) ^ ((i/16) & 3)
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* dst, int wave, uint32_t vo,
                                          uint32_t soff, uint32_t row16_bytes) {
 #pragma unroll
-  for (int n = 0; n < 4; ++n)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (64 * wave + 16 * n) * kBK), 16, vo,
+  for (int n = 0; n < 2; ++n)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (32 * wave + 16 * n) * kBK), 16, vo,
                                              soff + (uint32_t)n * row16_bytes, 0, 0);
 }
 
 __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane,
-                                           f32x16 (&acc)[4][4]) {
+                                           f32x16 (&acc)[4][2]) {
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
     const int kc = 2 * ks + (lane >> 5);
-    uint4 a[4], b[4];
+    uint4 a[4], b[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = frag(As, wm * 128 + i * 32 + (lane & 31), kc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = frag(Bs, wn * 128 + j * 32 + (lane & 31), kc);
+    for (int j = 0; j < 2; ++j) b[j] = frag(Bs, wn * 64 + j * 32 + (lane & 31), kc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
   }
 }
 
-__global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                               uint32_t a_bytes, const uint16_t* __restrict__ B,
                                                               int64_t ldb, uint32_t b_bytes, int64_t K, int64_t n_mt,
                                                               int64_t n_nt, float* __restrict__ colpart, int64_t ldc) {
@@ -375,13 +377,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
   const uint32_t row16 = 16 * ld2;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, a_bytes);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, b_bytes);
-  const uint32_t sA = (uint32_t)((m0 + 64 * wave) * lda * 2), sB = (uint32_t)((n0 + 64 * wave) * ldb * 2);
+  const uint32_t sA = (uint32_t)((m0 + 32 * wave) * lda * 2), sB = (uint32_t)((n0 + 32 * wave) * ldb * 2);
   // k-tile t (clamped: past the end the ring re-fetches the last tile into a free buffer)
   auto koff = [&](int t) { return (uint32_t)((t < nk ? t : nk - 1) * kBK * 2); };
 
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
   dma_tile(rsB, sB1, wave, vo, sB + koff(1), row16);
   dma_tile(rsA, sA2, wave, vo, sA + koff(2), row16);
   dma_tile(rsB, sB2, wave, vo, sB + koff(2), row16);
-  __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) lgkmcnt(0): this wave's stage-0 loads are in LDS
+  __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): this wave's stage-0 loads are in LDS
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
     dma_tile(rsA, sA##SN, wave, vo, sA + koff(kt + 3), row16);                  \
     dma_tile(rsB, sB##SN, wave, vo, sB + koff(kt + 3), row16);                  \
     mfma_stage(sA##S, sB##S, wm, wn, lane, acc);                                \
-    __builtin_amdgcn_s_waitcnt(0x4070);                                         \
+    __builtin_amdgcn_s_waitcnt(0x0078);                                         \
     asm volatile("" ::: "memory");                                              \
     __builtin_amdgcn_s_barrier();                                               \
     asm volatile("" ::: "memory");                                              \
@@ -437,14 +439,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_sq_kernel(const uint16_t* _
   __builtin_amdgcn_s_waitcnt(0x0070);  // no load in flight past this point
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     float cs = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
     cs += __shfl_xor(cs, 32, kWave);
-    if (lane < 32) red[wm][wn * 128 + j * 32 + lane] = cs;
+    if (lane < 32) red[wm][wn * 64 + j * 32 + lane] = cs;
   }
   __syncthreads();
   if (tid < kBN) colpart[mt * ldc + n0 + tid] = red[0][tid] + red[1][tid];
