@@ -58,9 +58,9 @@ PMC_TRAFFIC = {
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
         "sha256": "d47104ef2d0a585d2ea4bd48bb967ba2a5fb19377a914f3e53282dc4c07e176d"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 12857120.5, "write_kib": 30720.0,
+        "fetch_kib": 11797862.7, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "e101829c07f90125bc6936008a391cfb3491b79eadcb8a3d2777ca96012d3aaa"},
+        "sha256": "a9268af91445dad27351e35a37d5ecf1e9e694ecbb0a61a04557d9af80d2f0f0"},
 }
 
 
