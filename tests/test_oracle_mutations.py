@@ -1,0 +1,188 @@
+"""The oracle's pins are strong enough: each plausible single mistake planted in
+the oracle (a dropped term, a wrong sign, index, constant, rounding mode or
+operand order) makes at least one pin in test_oracle_pins.py fail.
+
+Mistakes are planted by monkeypatching the oracle module on the CPU; the pins
+are then run in-process, stopping at the first one that fails.
+"""
+import inspect
+
+import numpy as np
+import pytest
+
+from oracle import awq_oracle as O
+import test_oracle_pins as PINS
+
+F32, F64 = np.float32, np.float64
+
+
+def _pins():
+    out = []
+    for _, cls in inspect.getmembers(PINS, inspect.isclass):
+        if cls.__name__.startswith("Test") and cls.__module__ == PINS.__name__:
+            for name, fn in inspect.getmembers(cls, inspect.isfunction):
+                if name.startswith("test_"):
+                    out.append((f"{cls.__name__}.{name}", cls, name))
+    return out
+
+
+def _first_failing_pin():
+    for label, cls, name in _pins():
+        try:
+            getattr(cls(), name)()
+        except Exception:      # an assertion, or the mutant breaking a shape or type
+            return label
+    return None
+
+
+# ---------------------------------------------------------------------------
+# mutants: name -> list of (attribute, replacement)
+# ---------------------------------------------------------------------------
+def _act_stats_signed(X):
+    Xd = O.decode_activations(X)
+    return (Xd.sum(axis=0) / Xd.shape[0]).astype(F32)
+
+
+def _act_stats_max(X):
+    return np.abs(O.decode_activations(X)).max(axis=0).astype(F32)
+
+
+def _act_stats_sum(X):
+    return np.abs(O.decode_activations(X)).sum(axis=0).astype(F32)
+
+
+def _grid_incl_one(n):
+    return [k / (n - 1) for k in range(n)]
+
+
+def _cand(x_mean, alpha, s_min=O.S_MIN, norm="geo", clamp_after=False):
+    x = x_mean.astype(F64)
+    t = np.ones_like(x) if alpha == 0.0 else np.power(x, alpha)
+    if not clamp_after:
+        t = np.maximum(t, s_min)
+    d = np.sqrt(t.max() * t.min()) if norm == "geo" else t.max()
+    t = t / d
+    if clamp_after:
+        t = np.maximum(t, s_min)
+    return t.astype(F32)
+
+
+def _gq(W, s, G, clip=None, rnd=np.rint, lo=-7, hi=7, div=7.0, use_s=True):
+    Wf = np.asarray(W).astype(F32)
+    d_out, d_in = Wf.shape
+    v = Wf if (s is None or not use_s) else (Wf * s.astype(F32)[None, :]).astype(F32)
+    vg = v.reshape(d_out, d_in // G, G)
+    amax = np.abs(vg).max(axis=2)
+    if clip is not None:
+        amax = (clip.astype(F32)[:, None] * amax).astype(F32)
+    step = (amax / F32(div)).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (vg / step[:, :, None]).astype(F32)
+    ratio = np.where(step[:, :, None] > 0, ratio, F32(0))
+    q = np.clip(rnd(ratio), lo, hi).astype(np.int8)
+    return q.reshape(d_out, d_in), step, v
+
+
+def _round_half_away(r):
+    return np.sign(r) * np.floor(np.abs(r) + 0.5)
+
+
+def _dequant(q, step, s, G, mode):
+    d_out, d_in = q.shape
+    qs = (q.astype(F32).reshape(d_out, -1, G) * step[:, :, None]).astype(F32).reshape(d_out, d_in)
+    if s is None or mode == "none":
+        return qs
+    return (qs * s.astype(F32)[None, :]).astype(F32)   # mode "mul"
+
+
+def _werr(W, s, x_mean, G, mode):
+    w_hat = O.fake_quant(W, s, G)
+    d = np.asarray(W).astype(F64) - w_hat.astype(F64)
+    if mode == "x":
+        return float(np.sum(d * d * x_mean.astype(F64)[None, :]))
+    return float(np.sum(np.abs(d * x_mean.astype(F64)[None, :])))   # "l1"
+
+
+def _oerr_rows_sum_first(W, s, X, G, clip=None):
+    Xd = O.decode_activations(X)
+    D = O.fake_quant(W, s, G, clip).astype(F64) - np.asarray(W).astype(F64)
+    Y = Xd @ D.T
+    return np.sum(Y, axis=0) ** 2
+
+
+def _argmin_last(errors):
+    best_i, best_e = -1, float("inf")
+    for i, e in enumerate(errors):
+        if e <= best_e:
+            best_i, best_e = i, e
+    return best_i
+
+
+def _clip_ratios_rev(n, lo=0.5):
+    return np.array([lo + j * (1.0 - lo) / (n - 1) for j in range(n)], dtype=F64).astype(F32)
+
+
+def _clip_ratios_excl(n, lo=0.5):
+    return np.array([1.0 - j * (1.0 - lo) / n for j in range(n)], dtype=F64).astype(F32)
+
+
+_pack_codes_original = O.pack_codes   # captured before any test patches the module
+
+
+def _pack_along_d_in(u):
+    """codes packed 8 per word along the input axis: [d_in/8, d_out] words"""
+    return _pack_codes_original(u.T.copy()).T.copy()
+
+
+def _f16_trunc(x):
+    b = np.asarray(x, dtype=F32).view(np.uint32)
+    sign = (b >> 16) & 0x8000
+    a = np.abs(np.asarray(x, dtype=F32)).astype(F64)
+    h = np.asarray(a.astype(np.float16), dtype=np.float16)            # RNE magnitude
+    over = h.astype(F64) > a                                          # rounded up -> step down
+    hb = h.view(np.uint16) - over.astype(np.uint16)
+    return (hb | sign.astype(np.uint16)).view(np.float16)
+
+
+MUTANTS = {
+    "act_stats: signed mean": [("act_stats", _act_stats_signed)],
+    "act_stats: max |x|": [("act_stats", _act_stats_max)],
+    "act_stats: sum, not mean": [("act_stats", _act_stats_sum)],
+    "grid: k / (n - 1)": [("grid_alphas", _grid_incl_one)],
+    "scales: divide by max": [("candidate_scale", lambda x, a, s_min=O.S_MIN: _cand(x, a, s_min, norm="max"))],
+    "scales: clamp after normalising": [("candidate_scale",
+                                         lambda x, a, s_min=O.S_MIN: _cand(x, a, s_min, clamp_after=True))],
+    "quant: round half away from zero": [("group_quantize", lambda W, s, G, clip=None: _gq(W, s, G, clip,
+                                                                                          rnd=_round_half_away))],
+    "quant: truncate": [("group_quantize", lambda W, s, G, clip=None: _gq(W, s, G, clip, rnd=np.trunc))],
+    "quant: clamp to [-8, 7]": [("group_quantize", lambda W, s, G, clip=None: _gq(W, s, G, clip, lo=-8))],
+    "quant: step = max / 8": [("group_quantize", lambda W, s, G, clip=None: _gq(W, s, G, clip, div=8.0))],
+    "quant: step = max / 15": [("group_quantize", lambda W, s, G, clip=None: _gq(W, s, G, clip, div=15.0))],
+    "quant: scale s ignored": [("group_quantize", lambda W, s, G, clip=None: _gq(W, s, G, clip, use_s=False))],
+    "dequant: no division by s": [("dequantize", lambda q, st, s, G: _dequant(q, st, s, G, "none"))],
+    "dequant: multiply by s": [("dequantize", lambda q, st, s, G: _dequant(q, st, s, G, "mul"))],
+    "weight error: x not squared": [("weight_error", lambda W, s, x, G: _werr(W, s, x, G, "x"))],
+    "weight error: L1": [("weight_error", lambda W, s, x, G: _werr(W, s, x, G, "l1"))],
+    "output error: sum before squaring": [("output_error_rows", _oerr_rows_sum_first)],
+    "selection: last minimum": [("first_argmin", _argmin_last)],
+    "selection: maximum": [("first_argmin", lambda e: int(np.argmax(np.asarray(e))))],
+    "clip ratios: from clip_lo up": [("clip_ratios", _clip_ratios_rev)],
+    "clip ratios: clip_lo never reached": [("clip_ratios", _clip_ratios_excl)],
+    "pack: order 0..7": [("PACK_ORDER", [0, 1, 2, 3, 4, 5, 6, 7])],
+    "pack: inverse order": [("PACK_ORDER", [0, 4, 1, 5, 2, 6, 3, 7])],
+    "pack: zero point 8": [("ZERO_POINT", 8)],
+    "pack: fp16 scales truncated": [("f32_to_f16", _f16_trunc)],
+    "pack: qweight along d_in": [("pack_codes", _pack_along_d_in)],
+}
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _first_failing_pin() is None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    for attr, repl in MUTANTS[name]:
+        monkeypatch.setattr(O, attr, repl)
+    caught = _first_failing_pin()
+    assert caught is not None, f"no pin fails with the mistake '{name}' planted in the oracle"

@@ -167,6 +167,15 @@ class TestQuantizer:
                     n_mismatch += 1
         assert n_mismatch <= 2
 
+    def test_exact_ties_round_to_even(self):
+        # a group whose max is 7 has step 7 / 7 = 1 exactly, so these fp16
+        # values sit exactly on half-integers: round half to even (not away
+        # from zero, not toward zero, not up)
+        W = np.array([[7.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -6.5]], dtype=np.float16)
+        q, step, _ = O.group_quantize(W, None, 8)
+        assert step[0, 0] == 1.0
+        assert q[0].tolist() == [7, 2, 4, -2, 0, 0, 2, -6]
+
     def test_code_range_and_zero_group(self):
         W = np.zeros((8, 32), dtype=np.float16)
         W[1, 5] = 0.5
