@@ -95,8 +95,11 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
   for (int j = 0; j < 16; ++j) {
     float n = step > 0.0f ? code_exact(v[j], step, inv) : 0.0f;
     n = __builtin_fminf(__builtin_fmaxf(n, -7.0f), 7.0f);
-    const float wh = (n * step) / sv[j];          // RN(RN(q * step) / s)
-    const float d = wh - w[j];
+    // w_hat - w = (q * step - w * s) / s, formed in the scaled domain with one
+    // fma and the hardware reciprocal of s: within a few fp32 ulp of
+    // RN(RN(q * step) / s) - w, far below the fp16 rounding of the operand
+    // (the codes q themselves are exact)
+    const float d = __builtin_fmaf(n, step, -v[j]) * __builtin_amdgcn_rcpf(sv[j]);
     if constexpr (WRITE) {
       const uint32_t b = f2h_bits(d * dsc);       // exact scaling by 2^e, one rounding
       if (j & 1) outw[j >> 1] |= b << 16;
