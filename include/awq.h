@@ -176,6 +176,8 @@ awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_w
  *   qzeros[g, m]:  int32 [d_in/G, d_out/8], every nibble 7 (may be NULL)
  * W: fp16 [d_out, d_in] 16-byte aligned; d_out % 8 == 0, d_in % group_size == 0,
  * group_size in {32, 64, 128}; s: fp32 [d_in] or NULL; clip: fp32 [d_out] or NULL.
+ * W, s and clip are expected to be finite (s > 0, clip in (0, 1]); codes of
+ * non-finite weights are unspecified (nothing faults).
  * ------------------------------------------------------------------------- */
 awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size,
                              const float* s, const float* clip,

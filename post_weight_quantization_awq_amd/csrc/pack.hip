@@ -24,11 +24,6 @@ namespace awq {
 
 constexpr int kPackThreads = 512;  // 8 waves
 
-// nibble that holds row r of an 8-row run: order = {0,2,4,6,1,3,5,7} => inverse {0,4,1,5,2,6,3,7}
-__device__ __forceinline__ constexpr int nibble_of_row(int r) {
-  return (r & 1) ? 4 + (r >> 1) : (r >> 1);
-}
-
 template <int G>
 struct PackShape {
   static constexpr int LPG = G / 8;              // lanes per group row
@@ -38,16 +33,21 @@ struct PackShape {
   static constexpr int MW = ROWS_B / 8;          // words per input column per block
 };
 
-// Per element: cvt, scale, max (half a max3), v * rcp(step), rint, the
-// near-half check, cvt to int and a shift-add into the word (~8.5 VALU ops).
-// Codes accumulate as signed nibbles: sum_r q_r * 16^nib(r) + 0x77777777 equals
-// sum_r (q_r + 7) * 16^nib(r) exactly, since every q_r + 7 lies in [0, 14].
-// A row whose fast codes might differ from rint(RN(v / step)) (|r0 - rint r0|
-// within 2^-15 of 1/2, or r0 not finite) recomputes its 8 codes with the IEEE
-// division.  The bound on |r0 - v/step| (rcp within 1 ulp, one rounding) is
-// below 8e-6 for |v/step| < 32; unclipped |v/step| <= 7, and with clipping a
-// larger quotient can only mis-round to a code that the clamp maps to +-7
-// either way for |v/step| >= 32 (ratios >= 7/32).
+// Per element: the scaled value straight from the fp16 half (mixed-precision
+// fma), max (half a max3), v * rcp(step), rint, r0 - rint(r0) into a running
+// max (half a max3), and one exact fp32 fma into the word (~5.5 VALU ops).
+// Codes accumulate as small signed integers in fp32, even rows into the low
+// 16-bit half of the word and odd rows into the high half (the pack order puts
+// rows 0, 2, 4, 6 in nibbles 0-3 and rows 1, 3, 5, 7 in nibbles 4-7):
+// sum_k q * 16^k is an integer of magnitude <= 7 * 0x1111, exact in fp32, and
+// adding 0x7777 gives sum_k (q + 7) * 16^k since every q + 7 lies in [0, 14].
+// A row whose fast codes might differ from rint(RN(v / step)) (some
+// |r0 - rint r0| within 2^-15 of 1/2), or whose step is not a positive finite
+// number, recomputes its 8 codes with the IEEE division.  The bound on
+// |r0 - v/step| (rcp within 1 ulp, one rounding) is below 8e-6 for
+// |v/step| < 32; unclipped |v/step| <= 7, and with clipping a larger quotient
+// can only mis-round to a code that the clamp maps to +-7 either way for
+// |v/step| >= 32 (ratios >= 7/32).  Weights are expected to be finite.
 template <int G, bool HAS_S, bool HAS_CLIP>
 __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ W, int64_t d_out, int64_t d_in, const float* __restrict__ s,
@@ -85,45 +85,48 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
 #pragma unroll
   for (int r = 0; r < 8; ++r) raw[r] = ld_nt(W + (lrow + r) * d_in + col0);
 
-  int32_t words[8];
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  float lo[8], hi[8];  // codes of even / odd rows as exact fp32 sums of q * 16^k
 #pragma unroll
-  for (int j = 0; j < 8; ++j) words[j] = 0;
+  for (int j = 0; j < 8; ++j) lo[j] = hi[j] = 0.0f;
   uint32_t sbits[4];
 
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
+    const h8 hv = __builtin_bit_cast(h8, raw[r]);
     float v[8];
-    unpack8_f16(raw[r], v);
-    if constexpr (HAS_S) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = v[j] * sv[j];
-    }
     float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
-    m = group_max<SH::LPG>(m);
+    for (int j = 0; j < 8; ++j) {
+      v[j] = HAS_S ? __builtin_fmaf((float)hv[j], sv[j], 0.0f) : (float)hv[j];
+      m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+    }
+    m = group_max_nonneg<SH::LPG>(m);
     float a = m;
     if constexpr (HAS_CLIP) a = cl[r] * m;
     const float step = div7(a);
     const float inv = __builtin_amdgcn_rcpf(step);
     float n[8];
-    bool near = false;
+    float dev = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float r0 = v[j] * inv;
       n[j] = __builtin_rintf(r0);
-      near |= !(__builtin_fabsf(r0 - n[j]) < 0.5f - 0x1p-15f);  // also true for inf / NaN
+      dev = __builtin_fmaxf(dev, __builtin_fabsf(r0 - n[j]));
     }
-    if (near) {  // rare: exact codes for this lane's 8 elements of row r
+    if (!(dev < 0.5f - 0x1p-15f) || !(step > 0.0f && step < __builtin_inff())) {
+      // rare: exact codes for this lane's 8 elements of row r
 #pragma unroll
       for (int j = 0; j < 8; ++j) n[j] = step > 0.0f ? __builtin_rintf(v[j] / step) : 0.0f;
     }
-    const int sh = 4 * nibble_of_row(r);
+    constexpr float kWeight[4] = {1.0f, 16.0f, 256.0f, 4096.0f};
+    const float wgt = kWeight[r >> 1];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float q = n[j];
       if constexpr (HAS_CLIP) q = __builtin_amdgcn_fmed3f(q, -7.0f, 7.0f);
-      words[j] += (int32_t)q << sh;
+      if (r & 1) hi[j] = __builtin_fmaf(q, wgt, hi[j]);
+      else lo[j] = __builtin_fmaf(q, wgt, lo[j]);
     }
     const uint32_t hb = f2h_bits(step);
     if (r & 1) sbits[r >> 1] |= hb << 16;
@@ -134,7 +137,10 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
   }
 
 #pragma unroll
-  for (int j = 0; j < 8; ++j) wt[lg * 8 + j][m_local] = (uint32_t)words[j] + 0x77777777u;
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t wlo = (uint32_t)((int32_t)lo[j] + 0x7777), whi = (uint32_t)((int32_t)hi[j] + 0x7777);
+    wt[lg * 8 + j][m_local] = (whi << 16) | wlo;
+  }
   if (valid && lg == 0) {
     *(uint4*)(scales + gcol * d_out + row0) = make_uint4(sbits[0], sbits[1], sbits[2], sbits[3]);
     if (qzeros != nullptr) qzeros[gcol * (d_out / 8) + row0 / 8] = 0x77777777;
