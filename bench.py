@@ -58,9 +58,9 @@ PMC_TRAFFIC = {
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
         "sha256": "d47104ef2d0a585d2ea4bd48bb967ba2a5fb19377a914f3e53282dc4c07e176d"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11797862.7, "write_kib": 30720.0,
+        "fetch_kib": 11797599.2, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "a9268af91445dad27351e35a37d5ecf1e9e694ecbb0a61a04557d9af80d2f0f0"},
+        "sha256": "63067e4e2f84e2980324f45636889da93bb0ddc46c8e8c293c11bd17cee62491"},
 }
 
 
