@@ -38,7 +38,10 @@ METRIC = "scale-search weight-elems×grid-pts/s + pack GB/s; % of HBM roofline, 
 # MI355X published peaks and unit counts
 HBM_PEAK_GBPS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0
-VALU_LANE_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.32 T fp32 lane-ops/s (no packed math)
+# fp32 vector: 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 32 lane-ops per clock x 2 flops
+# (FMA) x 2.4 GHz, i.e. 78.6 T lane-operations/s; a SIMD issues up to two
+# wave64 VALU instructions per 4 clocks when they come from different classes
+VALU_LANE_OPS_PEAK_T = 256 * 4 * 32 * 2.4e9 / 1e12   # 78.64 T fp32 lane-ops/s
 # fp32 lane operations that one element x candidate needs in the weight score:
 # scale (mul), group max (max), v / step (mul by reciprocal), round (rndne),
 # residual v - q*step (fma), square-accumulate (fma)

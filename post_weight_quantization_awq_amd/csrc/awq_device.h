@@ -36,12 +36,20 @@ struct WParts {
   int32_t n;
 };
 
+// Start of global row `row` of the concatenated parts.  The part's pointer and
+// first row are chosen by selects over constant indices, so the kernel-argument
+// arrays stay in scalar registers (indexing them by a per-lane part number
+// would read the argument block with vector loads and wait on them).
 __device__ __forceinline__ const uint16_t* row_ptr(const WParts& P, int64_t row, int64_t d_in) {
-  int p = 0;
+  const uint16_t* base = P.ptr[0];
+  int64_t r0 = 0;
 #pragma unroll
-  for (int j = 1; j < kMaxParts; ++j)
-    if (j < P.n && row >= P.row_start[j]) p = j;
-  return P.ptr[p] + (row - P.row_start[p]) * d_in;
+  for (int j = 1; j < kMaxParts; ++j) {
+    const bool in = j < P.n && row >= P.row_start[j];
+    base = in ? P.ptr[j] : base;
+    r0 = in ? P.row_start[j] : r0;
+  }
+  return base + (row - r0) * d_in;
 }
 
 // Power-of-two operand scales of the output-score GEMM (in the workspace):

@@ -13,15 +13,17 @@
 // domain (w - q*step/s) * x = (v - q*step) * (x/s), so each lane accumulates
 // d^2 per column over its rows and weights the column sums by (x/s)^2 once.
 //
-// Tile: one quantization group column (G inputs) by 8192*R/G rows (256 rows
-// for G = 128): each
-// lane holds 32 inputs of R rows as packed fp16 (four 16-byte chunks,
-// interleaved with the other G/32 lanes of the row so that one load
-// instruction reads G/32 * 16 contiguous bytes of a row); v = w*s is formed
-// straight from the fp16 halves with a mixed-precision fma.  The G/32 lanes
-// of a row combine their maxima with DPP row permutes.  The candidate scales
-// and (x/s)^2 of the block's columns are staged in LDS.  Two blocks share a
-// compute unit (one wave per SIMD each), so VGPRs stay under 256.
+// Tile: one quantization group column (G inputs) by 8192*R/G rows (128 rows
+// for G = 128, R = 2).  Each lane holds 32 inputs of R rows, loaded as packed
+// fp16 (four 16-byte chunks, interleaved with the other G/32 lanes of the row
+// so that one load instruction reads G/32 * 16 contiguous bytes of a row) and
+// widened to fp32 once, outside the candidate loop.  The G/32 lanes of a row
+// combine their maxima with DPP row permutes.  The candidate scales and
+// (x/s)^2 of the block's columns are staged in LDS.  Each row's chain (group
+// max, step, reciprocal) is serial, so the kernel is sized for three resident
+// blocks per compute unit (three waves per SIMD, at most 168 VGPRs): with two
+// rows per lane that measured 9-14% faster than four rows at two waves per
+// SIMD.
 #include "awq_device.h"
 #include "awq_launch.h"
 
@@ -29,7 +31,8 @@ namespace awq {
 
 constexpr int kSearchThreads = 256;
 constexpr int kSearchE = 32;  // inputs per lane per row
-constexpr int kSearchR = 4;   // rows per lane
+constexpr int kSearchR = 2;   // rows per lane
+constexpr int kStageV = 4;    // float4 per candidate table and thread per staging batch
 // Initial value of a group's running max: zero groups then get a tiny positive
 // step, so q = 0 and d = 0 exactly without a select (any group whose max is
 // below it contributes less than 2^-200 to the score).
@@ -122,7 +125,7 @@ __device__ __forceinline__ void select_block(const TP* __restrict__ part, int n_
 }
 
 template <int G>
-__global__ __launch_bounds__(kSearchThreads, 2) void search_weight_kernel(
+__global__ __launch_bounds__(kSearchThreads, 3) void search_weight_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int n_grid, const float* __restrict__ S,
     const float* __restrict__ C2, float* __restrict__ partials) {
   constexpr int R = kSearchR;
@@ -136,35 +139,56 @@ __global__ __launch_bounds__(kSearchThreads, 2) void search_weight_kernel(
   float* c_l = lds + n_grid * G;
   __shared__ float red[kMaxGrid][kSearchThreads / 16];
 
-  const int64_t n_gcol = d_in / G;
-  const int64_t gcol = blockIdx.x % n_gcol;
+  const uint32_t n_gcol = (uint32_t)(d_in / G);
+  const uint32_t gcol = blockIdx.x % n_gcol;
   const int64_t rblk = blockIdx.x / n_gcol;
-  const int64_t c0 = gcol * G;
+  const int64_t c0 = (int64_t)gcol * G;
   const int tid = threadIdx.x;
 
-  for (int idx = tid; idx < n_grid * (G / 4); idx += kSearchThreads) {
-    const int k = idx / (G / 4), j = idx % (G / 4);
-    ((float4*)s_l)[idx] = *(const float4*)(S + (int64_t)k * d_in + c0 + 4 * j);
-    ((float4*)c_l)[idx] = *(const float4*)(C2 + (int64_t)k * d_in + c0 + 4 * j);
-  }
-
+  // W tile first: it is the bulk of the kernel's traffic.  Every lane loads a
+  // row that exists (rows past d_out read row d_out - 1) and those rows are
+  // cleared once all loads have landed, so no load waits behind a branch.
   const int lg = tid % LPG;
   const int slot = tid / LPG;
   // chunk c of this lane covers group columns (c * LPG + lg) * 8 .. + 7
   uint4 w[R][NC];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t row = rblk * RB + slot + (int64_t)RS * r;
-    if (row < d_out) {
-      const uint4* p = (const uint4*)(row_ptr(P, row, d_in) + c0);
+    const int64_t row = min(rblk * RB + slot + (int64_t)RS * r, d_out - 1);
+    const uint4* p = (const uint4*)(row_ptr(P, row, d_in) + c0);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) w[r][c] = ld_nt(p + c * LPG + lg);
-    } else {
+    for (int c = 0; c < NC; ++c) w[r][c] = ld_nt(p + c * LPG + lg);
+  }
+  // Candidate scales and (x/s)^2 of the block's columns into LDS, issued
+  // while the W loads are in flight, kStageV float4 per table and thread at a
+  // time.  Indices past the table are clamped to its last entry, for the loads
+  // and the stores alike (those lanes write the value that entry holds), so
+  // no load sits behind a branch and waits alone.
+  const int n_st = n_grid * (G / 4);
+  for (int base = 0; base < n_st; base += kStageV * kSearchThreads) {
+    float4 a[kStageV], b[kStageV];
+    int ix[kStageV];
+#pragma unroll
+    for (int u = 0; u < kStageV; ++u) {
+      ix[u] = min(base + u * kSearchThreads + tid, n_st - 1);
+      const int64_t off = (int64_t)(ix[u] / (G / 4)) * d_in + c0 + 4 * (ix[u] % (G / 4));
+      a[u] = *(const float4*)(S + off);
+      b[u] = *(const float4*)(C2 + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kStageV; ++u) {
+      ((float4*)s_l)[ix[u]] = a[u];
+      ((float4*)c_l)[ix[u]] = b[u];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (rblk * RB + slot + (int64_t)RS * r >= d_out) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) w[r][c] = make_uint4(0, 0, 0, 0);
     }
   }
-  __syncthreads();
 
   for (int k = 0; k < n_grid; ++k) {
     float s[kSearchE];
