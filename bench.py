@@ -57,13 +57,13 @@ SEARCH_OPS_PER_ELEM_PT = 6
 FETCH_CAL, WRITE_CAL = 2.0, 1.0
 PMC_TRAFFIC = {
     ("search_weight_kernel", "q_proj_4096x4096"): {
-        "fetch_kib": 16782.3, "write_kib": 320.0,
+        "fetch_kib": 16756.2, "write_kib": 640.0,
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
-        "sha256": "d47104ef2d0a585d2ea4bd48bb967ba2a5fb19377a914f3e53282dc4c07e176d"},
+        "sha256": "68f36a6a380370dd3d87aafbc2ab63c401bdf8d1d0934c5c4ea72de3ef432c72"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11797599.2, "write_kib": 30720.0,
+        "fetch_kib": 11797777.8, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "63067e4e2f84e2980324f45636889da93bb0ddc46c8e8c293c11bd17cee62491"},
+        "sha256": "2b503c378c5e6c431b26ff4c04308976c9b7583824b9c64387e6f897876c8588"},
 }
 
 
