@@ -99,6 +99,9 @@ def _search_case(A, parts, X, G, n_grid=20):
     ("qkv_parts_ragged", [96, 40, 64], 256, 50, 64, "bf16"),
     ("g32_ragged_rows", [200], 384, 33, 32, "bf16"),
     ("one_row", [1], 128, 9, 128, "bf16"),
+    # all eight parts, one empty, blocks straddling part boundaries
+    ("eight_parts_one_empty", [130, 8, 0, 120, 1, 64, 70, 7], 256, 40, 128, "bf16"),
+    ("eight_parts_g64", [33, 0, 95, 2, 128, 17, 5, 60], 192, 21, 64, "bf16"),
 ])
 def test_search_weight(A, name, parts, d_in, T, G, xdt):
     say(f"search weight {name} parts={parts} d_in={d_in} G={G}")
@@ -208,6 +211,7 @@ def test_unpack_roundtrip(A, G, out_f16, with_s):
     ([72], 384, 77, 32, "bf16"),
     ([40], 96, 70, 32, "bf16"),            # K padded to the 64-wide GEMM step
     ([300, 220], 512, 600, 128, "bf16"),   # several token and row tiles, ragged edges
+    ([40, 0, 24, 8, 16, 33, 7, 16], 256, 90, 64, "bf16"),  # eight parts, one empty
 ])
 def test_search_output(A, parts, d_in, T, G, xdt):
     say(f"search output parts={parts} d_in={d_in} T={T} G={G} {xdt}")
@@ -221,14 +225,17 @@ def test_search_output(A, parts, d_in, T, G, xdt):
     assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
 
 
-@pytest.mark.parametrize("d_out,d_in,T,G", [(64, 256, 150, 128), (136, 384, 70, 64)])
-def test_clip_search(A, d_out, d_in, T, G):
-    say(f"clip search d_out={d_out} d_in={d_in} T={T} G={G}")
-    W = WL.make_weight(700 + d_out, d_out, d_in)
+@pytest.mark.parametrize("parts,d_in,T,G", [([64], 256, 150, 128), ([136], 384, 70, 64),
+                                            ([24, 0, 40], 256, 60, 128)])
+def test_clip_search(A, parts, d_in, T, G):
+    d_out = sum(parts)
+    say(f"clip search parts={parts} d_in={d_in} T={T} G={G}")
+    Ws = [WL.make_weight(700 + d_out + 3 * i, r, d_in) for i, r in enumerate(parts)]
+    W = np.concatenate(Ws, axis=0)
     X = WL.make_activations(800 + d_out, T, d_in, "bf16")
     xm = O.act_stats(X)
-    res = A.search_scales([dev_f16(W)], dev_f32(xm), group_size=G, score="output", X=dev_x(X), n_clip=20,
-                          want_clip_err=True)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          n_clip=20, want_clip_err=True)
     _, k, s = O.search_scales([W], xm, G, 20, "output", X=X)
     assert ulp_dist(host(res.best_s), s) <= 2 or int(host(res.best_idx)[0]) != k
     E, c = O.clip_search(W, s, X, G, 20, 0.5)
