@@ -30,7 +30,7 @@ hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_o
 // reduce partials p[c * n_blocks + b] over b (fixed order, fp64), times `scale`
 // and cand_scale[c] when given -> tot [n_cand] (fp64) and err [n_cand] (fp32);
 // smallest index attaining the minimum -> best_idx; if S is given,
-// best_s = S[best] [d_in].  One launch.
+// best_s = S[best] [d_in].  One launch (ceil(d_in / 1024) blocks).
 hipError_t launch_select(const float* partials, int64_t n_blocks, int n_cand, double scale,
                          const double* cand_scale, double* tot, float* err, int32_t* best_idx, const float* S,
                          int64_t d_in, float* best_s, hipStream_t stream);
