@@ -57,11 +57,11 @@ SEARCH_OPS_PER_ELEM_PT = 6
 FETCH_CAL, WRITE_CAL = 2.0, 1.0
 PMC_TRAFFIC = {
     ("search_weight_kernel", "q_proj_4096x4096"): {
-        "fetch_kib": 16756.2, "write_kib": 640.0,
+        "fetch_kib": 16756.3, "write_kib": 640.0,
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
-        "sha256": "68f36a6a380370dd3d87aafbc2ab63c401bdf8d1d0934c5c4ea72de3ef432c72"},
+        "sha256": "22dc4325fa32c158c87346270825f677711ba5a78d2bff255613a72e5d89ec6d"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11797777.8, "write_kib": 30720.0,
+        "fetch_kib": 11797803.2, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
         "sha256": "2b503c378c5e6c431b26ff4c04308976c9b7583824b9c64387e6f897876c8588"},
 }
