@@ -74,9 +74,10 @@ __device__ __forceinline__ void store_partials(const double* acc, int wv, int la
 // issues its ROWS row loads at once and adds them as they arrive.  One batch
 // per wave and small blocks dispatched split by split keep the rows read at
 // any moment contiguous in memory and leave several blocks per CU to cover
-// each other's reduction tails: measured on a 512 MB input this runs at
-// ~7 TB/s, where waves that stream several batches each (two register sets,
-// a rolling prefetch) or 16-wave blocks (one per CU) reach 4.7-6 TB/s.
+// each other's reduction tails: on 0.5-1.6 GB inputs this streams ~6.2 TB/s
+// (a plain streaming read reaches ~7.1), where waves that stream several
+// batches each (two register sets, a rolling prefetch) or 16-wave blocks (one
+// per CU) reached 4.7-6 TB/s.
 template <bool BF16, int ROWS>
 __global__ __launch_bounds__(kStatsThreads) void act_stats_main_kernel(const uint16_t* __restrict__ X, int64_t d_in,
                                                                       int64_t ld, double* __restrict__ part) {
