@@ -368,16 +368,30 @@ def bench_sweep(args):
         K = args.steps
         per = 6 * 4 * blocks
         ev = HipEvents(per * K)
-        st_plans = [A.ActStatsPlan(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi]) for gi in range(len(wl.groups))]
-        se_plans = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi])
-                     for gi in range(len(wl.groups))] for b in range(blocks)]
-        pk_plans = [[[A.PackPlan(p, G, res[gi].best_s, out=o) for p, o in zip(Ws[b][gi], packs[gi])]
-                     for gi in range(len(wl.groups))] for b in range(blocks)]
+        ng = len(wl.groups)
+        # The groups of a block are independent chains (own statistics, search and
+        # packing; own workspaces and outputs): the timed steps put each group
+        # kind on a stream of its own, joined to the main stream at both ends.
+        # Kernel durations come from the same steps on the main stream alone.
+        main = torch.cuda.current_stream()
+        streams = [torch.cuda.Stream() for _ in range(args.streams)]
 
-        def step(k=-1):
+        def plans(stream_of):
+            st = [A.ActStatsPlan(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi], stream=stream_of(gi)) for gi in range(ng)]
+            se = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi], stream=stream_of(gi))
+                   for gi in range(ng)] for b in range(blocks)]
+            pk = [[[A.PackPlan(p, G, res[gi].best_s, out=o, stream=stream_of(gi)) for p, o in zip(Ws[b][gi], packs[gi])]
+                   for gi in range(ng)] for b in range(blocks)]
+            return st, se, pk
+
+        par = plans(lambda gi: streams[gi % len(streams)])
+        ser = plans(lambda gi: main)
+
+        def step(pl, k=-1):
+            st_plans, se_plans, pk_plans = pl
             n = k * per
             for b in range(blocks):
-                for gi, g in enumerate(wl.groups):
+                for gi in range(ng):
                     if k >= 0:
                         A.set_timing_events(ev.h(n), ev.h(n + 1))
                     st_plans[gi].launch()
@@ -392,16 +406,27 @@ def bench_sweep(args):
             if k >= 0:
                 A.set_timing_events(None, None)
 
+        def step_streams():
+            start = torch.cuda.Event()
+            start.record(main)
+            for s_ in streams:
+                s_.wait_event(start)
+            step(par)
+            for s_ in streams:
+                done = torch.cuda.Event()
+                done.record(s_)
+                main.wait_event(done)
+
         for _ in range(args.warmup):
-            step()
+            step_streams()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(K):
-            step()
+            step_streams()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t1) * 1e3 / K
-        for k in range(K):  # kernel durations: same steps again with events around each kernel
-            step(k)
+        for k in range(K):  # kernel durations: same steps again, one stream, events around each kernel
+            step(ser, k)
         torch.cuda.synchronize()
         sums = [0.0, 0.0, 0.0]
         for n in range(0, per * K, 6):
@@ -428,7 +453,7 @@ def bench_sweep(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": first["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "qwen3_8b_sweep", "blocks": blocks, "weights": n_w, "n_grid": 20,
-                   "group_sizes": list(wl.group_sizes), "score": "weight"},
+                   "group_sizes": list(wl.group_sizes), "score": "weight", "streams": args.streams},
         "per_group_size": out_all,
         "roofline": {"bound": "alu", "achieved": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T,
                      "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s", "frac": first["search_alu_frac"],
@@ -466,6 +491,8 @@ def main() -> int:
                              "mlp_output_clip", "qwen3_8b_sweep", "copy_512MiB"])
     ap.add_argument("--group-size", type=int, default=None)
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
+    ap.add_argument("--streams", type=int, default=4,
+                    help="streams the sweep's group kinds are spread over in the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
