@@ -114,6 +114,19 @@ def test_search_weight(A, name, parts, d_in, T, G, xdt):
     assert ulp_dist(g_s, O.candidate_scales(O.act_stats(X), 20)[g_k]) <= 2
 
 
+@pytest.mark.parametrize("n_grid", [2, 33, 64])
+def test_search_weight_grid_sizes(A, n_grid):
+    """Smallest and largest grids, and one just past the 32 candidates whose
+    scales the selection loads together with the partial errors."""
+    say(f"search weight n_grid={n_grid}")
+    Ws = [WL.make_weight(7300 + n_grid, 300, 512)]
+    X = WL.make_activations(8300 + n_grid, 70, 512, "bf16")
+    g_err, g_k, g_s, errs, k, s, xm = _search_case(A, Ws, X, 128, n_grid=n_grid)
+    np.testing.assert_allclose(g_err, errs, rtol=1e-3, atol=0)
+    assert argmin_ok(g_k, errs, k), (g_k, k)
+    assert ulp_dist(g_s, O.candidate_scales(xm, n_grid)[g_k]) <= 2
+
+
 def test_search_worked_example_embedded(A):
     """The page-4 worked example row inside a 128-wide group: x_mean [16,1,1,...]
     makes candidate 10 scale channel 0 by 2 and the rest by 1/2 (= [4,1,1,1]/2)."""
