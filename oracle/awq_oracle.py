@@ -52,6 +52,10 @@ its reason in the design notes of the repository):
   of output row 8m + order[j], order = [0, 2, 4, 6, 1, 3, 5, 7];
   scales[g, o] = fp16(step), qzeros[g, m] = 0x77777777.
 
+Norm-group export: the shared scale is the per-channel geometric mean of the
+member scales, evaluated as exp(mean(ln s)) in fp64 and rounded once to fp32;
+the folded norm is the IEEE fp32 quotient rounded once to the norm's dtype.
+
 Parity unpinned: the nibble-order reading and the qweight orientation against
 a real INT4 runtime (no runtime or checkpoint is available to compare with),
 and the clip-search semantics beyond "ratio 1.0 reproduces the unclipped
@@ -339,3 +343,67 @@ def unpack_dequant(qweight: np.ndarray, scales: np.ndarray, qzeros: Optional[np.
     if s is not None:
         w = (w / s.astype(F32)[None, :]).astype(F32)
     return w
+
+
+# ---------------------------------------------------------------------------
+# O9: norm-group export ([konic] "AutoAWQ / HF-AWQ GEMM on-disk format", the
+#     exporter's steps 1-3: q/k/v share input_layernorm and gate/up share
+#     post_attention_layernorm, so their per-linear scales become one shared
+#     scale per norm group -- the geometric mean over the member linears --
+#     folded into that norm as norm.weight /= s_shared; the norm-following
+#     linears are re-quantized with the shared scale, and o_proj / down_proj,
+#     which have no preceding norm, are exported as plain RTN, s = 1)
+# ---------------------------------------------------------------------------
+def shared_scale(s_members: Sequence[np.ndarray]) -> np.ndarray:
+    """s_shared[i] = (prod_m s_m[i]) ** (1/M), evaluated as the exponential of
+    the mean natural logarithm in fp64 and rounded once to fp32."""
+    S = np.stack([np.asarray(s, dtype=F32).astype(F64) for s in s_members])   # [M, d_in]
+    return np.exp(np.mean(np.log(S), axis=0)).astype(F32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit pattern (uint16), round to nearest, ties to even: the
+    two bf16 neighbours of x (mantissa truncated toward zero, and one unit
+    further from zero) are compared with x in exact fp64 arithmetic."""
+    x = np.asarray(x, dtype=F32)
+    toward0 = x.view(np.uint32) >> np.uint32(16)
+    away = toward0 + np.uint32(1)
+    v0 = (toward0 << np.uint32(16)).view(F32).astype(F64)
+    v1 = (away << np.uint32(16)).view(F32).astype(F64)
+    xd = x.astype(F64)
+    d0, d1 = np.abs(xd - v0), np.abs(v1 - xd)
+    pick_away = (d1 < d0) | ((d1 == d0) & ((toward0 & np.uint32(1)) == 1))
+    return np.where(pick_away, away, toward0).astype(np.uint16)
+
+
+def decode_norm(norm_w: np.ndarray) -> np.ndarray:
+    """fp16, bf16 (uint16 bit patterns) or fp32 norm weight -> exact fp32 values."""
+    if norm_w.dtype == np.uint16:
+        return (norm_w.astype(np.uint32) << np.uint32(16)).view(F32)
+    if norm_w.dtype in (np.float16, np.float32):
+        return norm_w.astype(F32)
+    raise TypeError(norm_w.dtype)
+
+
+def fold_norm(norm_w: np.ndarray, s_shared: np.ndarray) -> np.ndarray:
+    """norm.weight /= s_shared: the IEEE fp32 quotient, rounded once to the
+    norm's own dtype (the in-place division of an fp16 / bf16 tensor)."""
+    q = (decode_norm(norm_w) / np.asarray(s_shared, dtype=F32)).astype(F32)
+    if norm_w.dtype == np.float16:
+        return q.astype(np.float16)
+    if norm_w.dtype == np.uint16:
+        return f32_to_bf16_bits(q)
+    return q
+
+
+def export_norm_group(W_members: Sequence[np.ndarray], s_members: Sequence[np.ndarray],
+                      norm_w: np.ndarray, group_size: int):
+    """Steps 1-2 for one norm group: (s_shared, folded norm, [quantize_pack of
+    every member with s_shared])."""
+    s_sh = shared_scale(s_members)
+    return s_sh, fold_norm(norm_w, s_sh), [quantize_pack(W, s_sh, group_size) for W in W_members]
+
+
+def export_rtn(W: np.ndarray, group_size: int):
+    """Step 3: o_proj / down_proj at plain round-to-nearest (s = 1)."""
+    return quantize_pack(W, None, group_size)

@@ -144,6 +144,29 @@ def _f16_trunc(x):
     return (hb | sign.astype(np.uint16)).view(np.float16)
 
 
+def _shared_arith(s_members):
+    S = np.stack([np.asarray(x, dtype=F32).astype(F64) for x in s_members])
+    return S.mean(axis=0).astype(F32)
+
+
+def _shared_f32(s_members):
+    S = np.stack([np.asarray(x, dtype=F32) for x in s_members])
+    return np.exp(np.mean(np.log(S), axis=0, dtype=F32)).astype(F32)
+
+
+def _fold_multiply(norm_w, s_shared):
+    q = (O.decode_norm(norm_w) * np.asarray(s_shared, dtype=F32)).astype(F32)
+    if norm_w.dtype == np.float16:
+        return q.astype(np.float16)
+    if norm_w.dtype == np.uint16:
+        return O.f32_to_bf16_bits(q)
+    return q
+
+
+def _bf16_truncate(x):
+    return (np.asarray(x, dtype=F32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 MUTANTS = {
     "act_stats: signed mean": [("act_stats", _act_stats_signed)],
     "act_stats: max |x|": [("act_stats", _act_stats_max)],
@@ -173,6 +196,12 @@ MUTANTS = {
     "pack: zero point 8": [("ZERO_POINT", 8)],
     "pack: fp16 scales truncated": [("f32_to_f16", _f16_trunc)],
     "pack: qweight along d_in": [("pack_codes", _pack_along_d_in)],
+    "export: arithmetic mean of the scales": [("shared_scale", _shared_arith)],
+    "export: first member's scale": [("shared_scale", lambda s_members: np.asarray(s_members[0], dtype=F32))],
+    "export: logarithms in fp32": [("shared_scale", _shared_f32)],
+    "export: norm multiplied by s": [("fold_norm", _fold_multiply)],
+    "export: bf16 by truncation": [("f32_to_bf16_bits", _bf16_truncate)],
+    "export: o/down with the shared scale": [("export_rtn", lambda W, G: O.quantize_pack(W, np.full(W.shape[1], 2.0, F32), G))],
 }
 
 

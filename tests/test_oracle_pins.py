@@ -17,6 +17,7 @@ import workloads as WL
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 F32 = np.float32
+F64 = np.float64
 
 
 def load(name):
@@ -399,3 +400,92 @@ class TestPack:
         assert round((2 * n) / (n / 2), 1) == 4.0
         bits = 4 + 16 / 128 + 4 / 128
         assert round(bits, 2) == 4.16
+
+
+def ulps32(a, b) -> int:
+    """Distance in fp32 units in the last place (same-sign finite values)."""
+    ia = np.asarray(a, dtype=F32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, dtype=F32).view(np.int32).astype(np.int64)
+    return int(np.max(np.abs(ia - ib)))
+
+
+class TestNormGroupExport:
+    """[konic] exporter steps 1-3: one shared scale per norm group (geometric
+    mean of the member linears' scales) folded into the norm, the members
+    re-quantized with it, o_proj / down_proj at RTN."""
+
+    def test_geometric_mean_closed_forms(self):
+        a = lambda *v: np.array(v, dtype=F32)
+        assert np.array_equal(O.shared_scale([a(2.0, 0.5, 3.0), a(8.0, 2.0, 3.0)]), a(4.0, 1.0, 3.0))
+        assert np.array_equal(O.shared_scale([a(1.0), a(4.0), a(16.0)]), a(4.0))
+        assert np.array_equal(O.shared_scale([a(3.0), a(12.0), a(48.0)]), a(12.0))   # 1728 = 12^3
+        assert np.array_equal(O.shared_scale([a(2.0), a(32.0)]), a(8.0))
+        s = np.exp(np.random.default_rng(5).uniform(-5, 5, 300)).astype(F32)
+        assert np.array_equal(O.shared_scale([s]), s)                              # one member
+        assert np.array_equal(O.shared_scale([s, s, s]), s)                        # equal members
+
+    def test_matches_root_of_product(self):
+        rng = np.random.default_rng(6)
+        for M in range(2, 9):
+            S = np.exp(rng.uniform(-4, 4, (M, 64))).astype(F32)
+            got = O.shared_scale(list(S))
+            ref = np.array([math.prod(float(v) for v in S[:, i]) ** (1.0 / M) for i in range(64)])
+            assert ulps32(got, ref.astype(F32)) <= 1, M
+
+    def test_scaling_and_order(self):
+        rng = np.random.default_rng(7)
+        S = [np.exp(rng.uniform(-3, 3, 128)).astype(F32) for _ in range(3)]
+        base = O.shared_scale(S)
+        for c in (2.0 ** 7, 2.0 ** -9):
+            assert np.array_equal(O.shared_scale([(x * F32(c)).astype(F32) for x in S]), (base * F32(c)).astype(F32))
+        assert ulps32(O.shared_scale(S[::-1]), base) == 0
+        # a member and its reciprocal cancel (exactly for powers of two)
+        assert np.array_equal(O.shared_scale([np.full(4, 8.0, F32), np.full(4, 0.125, F32)]), np.ones(4, F32))
+
+    def test_fold_closed_forms(self):
+        s = np.array([2.0, 3.0, 1.0, 0.25], dtype=F32)
+        assert np.array_equal(O.fold_norm(np.array([6.0, 1.0, -5.5, 1.5], F32), s),
+                              np.array([3.0, F32(1.0) / F32(3.0), -5.5, 6.0], F32))
+        h = O.fold_norm(np.array([1.0, 6.0], np.float16), np.array([3.0, 2.0], F32))
+        assert h.dtype == np.float16 and [hex(v) for v in h.view(np.uint16)] == ["0x3555", "0x4200"]
+        b = O.fold_norm(np.array([0x3F80, 0x4040], np.uint16), np.array([4.0, 1.0], F32))   # bf16 1.0, 3.0
+        assert b.dtype == np.uint16 and [hex(v) for v in b] == ["0x3e80", "0x4040"]
+
+    def test_bf16_rounding_against_library(self):
+        import torch
+        ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20, 1.5], F32)
+        assert [hex(v) for v in O.f32_to_bf16_bits(ties)] == ["0x3f80", "0x3f82", "0xbf80", "0x3f81", "0x3fc0"]
+        x = (np.random.default_rng(8).standard_normal(4096) * np.exp(np.random.default_rng(9).uniform(-20, 20, 4096)))
+        x = x.astype(F32)
+        lib = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(O.f32_to_bf16_bits(x), lib)
+
+    def test_fold_identity_and_inverse(self):
+        rng = np.random.default_rng(10)
+        n32 = rng.uniform(0.2, 3.0, 500).astype(F32)
+        for n in (n32, n32.astype(np.float16), O.f32_to_bf16_bits(n32)):
+            assert np.array_equal(O.fold_norm(n, np.ones(500, F32)), n)
+        s = np.exp(rng.uniform(-2, 2, 500)).astype(F32)
+        back = (O.fold_norm(n32, s) * s).astype(F32)
+        assert np.max(np.abs(back / n32 - 1)) < 2.5e-7
+
+    def test_folding_reproduces_weight_dequantization(self):
+        """Norm-folding (store Q(W s), divide the activation by s in the norm)
+        and weight-dequantization (Q(W s)/s) give the same product up to the
+        fp32 rounding of the folded norm ([konic] the two application
+        strategies are the same mathematics)."""
+        rng = np.random.default_rng(11)
+        W = WL.make_weight(90, 64, 256)
+        s = np.exp(rng.uniform(-1, 1, 256)).astype(F32)
+        norm = rng.uniform(0.5, 2.0, 256).astype(F32)
+        x = rng.standard_normal((5, 256)).astype(F32)
+        s_sh, folded, packs = O.export_norm_group([W], [s], norm, 128)
+        qw, sc, qz, _, _ = packs[0]
+        deq = O.unpack_dequant(qw, sc, qz, 64, 128).astype(F64)                   # Q(W s), no 1/s
+        y_fold = (x.astype(F64) * folded.astype(F64)) @ deq.T
+        y_wd = (x.astype(F64) * norm.astype(F64)) @ (deq / s_sh.astype(F64)).T
+        np.testing.assert_allclose(y_fold, y_wd, rtol=1e-5, atol=1e-6 * np.abs(y_wd).max())
+        # o_proj / down_proj: RTN, the same as a unit scale
+        r = O.export_rtn(W, 128)
+        u = O.quantize_pack(W, np.ones(256, F32), 128)
+        assert all(np.array_equal(a, b) for a, b in zip(r, u))
