@@ -6,12 +6,14 @@
  *   --(awq_candidate_scales / awq_search_scales)--> grid search over alpha in
  *   s = x_mean^alpha (normalised), each candidate scored by group-wise
  *   symmetric INT4 fake quantization of W*s --(awq_quantize_pack)--> AutoAWQ
- *   GEMM layout (qweight / scales / qzeros) --(awq_unpack_dequant)--> check.
+ *   GEMM layout (qweight / scales / qzeros) --(awq_unpack_dequant)--> check;
+ *   for export, awq_norm_group_fold shares one scale per norm group and folds
+ *   it into the norm.
  *
  * Sources (page title, section):
  *   [konic]     "From-Scratch AWQ INT4 Quantization on Qwen3-8B": "AWQ scaling",
  *               "Group-wise symmetric INT4", "AutoAWQ / HF-AWQ GEMM on-disk
- *               format", exporter step 4.
+ *               format", exporter steps 1-4.
  *   [cassindra] "AWQ architecture, in depth": "The pipeline end to end",
  *               "The scale search as code", "Quantization, storage and packing".
  *   [lm]        "Weight-Only Quantization: GPTQ and AWQ": "5. Technical
@@ -182,6 +184,31 @@ awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_w
 awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size,
                              const float* s, const float* clip,
                              int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_norm_group_fold -- shared scale of a norm group and the folded norm.
+ * [konic] exporter steps 1-3: q/k/v share input_layernorm and gate/up share
+ * post_attention_layernorm; the member linears' scales become one shared
+ * scale (their per-channel geometric mean) folded into the norm
+ * (norm.weight /= s_shared); the members are then packed with s = s_shared
+ * (awq_quantize_pack) and o_proj / down_proj with s = NULL (plain RTN).
+ *
+ *   s_shared[i] = RN_fp32(exp((1/M) sum_m ln s[m][i]))   fp64 logarithms, summed
+ *                                                         in member order
+ *   norm_out[i] = RN_dtype(norm[i] / s_shared[i])         IEEE fp32 quotient
+ *
+ * s: [host] array of n_members (1..8) device pointers, each fp32 [d_in] with
+ * finite positive entries (the s_k rows awq_search_scales returns).
+ * norm: [d_in] of norm_dtype (AWQ_F16, AWQ_BF16 or AWQ_F32), aligned to its
+ * element size, or NULL (then norm_out must be NULL and only s_shared is
+ * produced).  norm_out: [d_in] of the same dtype; it may equal norm (in
+ * place: each element is read before it is written).
+ * s_shared: fp32 [d_in], 4-byte aligned.  d_in = 0 returns AWQ_OK at once.
+ * No workspace.
+ * ------------------------------------------------------------------------- */
+awq_status awq_norm_group_fold(const float* const* s /* [host] */, int32_t n_members, int64_t d_in,
+                               const void* norm, int32_t norm_dtype, void* norm_out, float* s_shared,
+                               void* stream);
 
 /* ---------------------------------------------------------------------------
  * awq_unpack_dequant -- inverse of awq_quantize_pack, for verification.

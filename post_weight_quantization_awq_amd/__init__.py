@@ -36,7 +36,8 @@ STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_EINVAL", 2: "AWQ_ESHAPE", 3: "AWQ_EDTYPE",
 
 EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales_workspace", "awq_candidate_scales",
             "awq_search_workspace", "awq_search_scales", "awq_quantize_pack",
-            "awq_unpack_dequant", "awq_last_error", "awq_abi_version", "awq_set_timing_events")
+            "awq_unpack_dequant", "awq_norm_group_fold", "awq_last_error", "awq_abi_version",
+            "awq_set_timing_events")
 
 
 class AwqError(RuntimeError):
@@ -74,6 +75,7 @@ def _load() -> ctypes.CDLL:
                               P, P, P, P, P, P, SZ, P],
         "awq_quantize_pack": [P, I64, I64, I32, P, P, P, P, P, P],
         "awq_unpack_dequant": [P, P, P, I64, I64, I32, P, P, I32, P],
+        "awq_norm_group_fold": [ctypes.POINTER(ctypes.c_void_p), I32, I64, P, I32, P, P, P],
         "awq_set_timing_events": [P, P],
     }
     for name, args in sig.items():
@@ -323,10 +325,53 @@ def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional
     return out
 
 
+class FoldPlan(_Prepared):
+    """Shared scale of a norm group (per-channel geometric mean of the members'
+    scales) and the norm folded with it (norm / s_shared in the norm's dtype)."""
+    _fn = "awq_norm_group_fold"
+
+    def __init__(self, s_members: Sequence[torch.Tensor], norm: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, s_shared: Optional[torch.Tensor] = None, stream=None):
+        members = list(s_members)
+        if not members:
+            raise ValueError("no member scales")
+        d_in = members[0].numel()
+        for t in members:
+            _dev(t, "s")
+            if t.dtype != torch.float32 or t.numel() != d_in or not t.is_contiguous():
+                raise ValueError("member scales must be contiguous fp32 [d_in] with one d_in")
+        dev = members[0].device
+        ndt = 0
+        if norm is not None:
+            _dev(norm, "norm")
+            if norm.numel() != d_in or not norm.is_contiguous():
+                raise ValueError("norm must be contiguous [d_in]")
+            ndt = {torch.float16: AWQ_F16, torch.bfloat16: AWQ_BF16, torch.float32: AWQ_F32}[norm.dtype]
+            if out is None:
+                out = torch.empty_like(norm)
+        self.s_shared = torch.empty(d_in, dtype=torch.float32, device=dev) if s_shared is None else s_shared
+        self.norm_out = out
+        self._sptrs = (ctypes.c_void_p * len(members))(*[t.data_ptr() for t in members])
+        self._keep = (members, norm)
+        self._bind(ctypes.cast(self._sptrs, ctypes.POINTER(ctypes.c_void_p)), len(members), d_in, _ptr(norm), ndt,
+                   _ptr(out), _ptr(self.s_shared), _stream(stream))
+
+    def run(self):
+        self.launch()
+        return self.s_shared, self.norm_out
+
+
+def norm_group_fold(s_members: Sequence[torch.Tensor], norm: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, s_shared: Optional[torch.Tensor] = None, stream=None):
+    """Returns (s_shared fp32 [d_in], norm_out or None): the geometric mean of the
+    member scales and norm / s_shared (out may be norm itself, in place)."""
+    return FoldPlan(s_members, norm, out, s_shared, stream).run()
+
+
 def set_timing_events(before: Optional[int], after: Optional[int]) -> None:
     """Record raw hipEvent_t handles around the main kernel of every later call (None clears)."""
     _check(lib().awq_set_timing_events(before, after))
 
 
-__all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "PackPlan", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
+__all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "PackPlan", "FoldPlan", "norm_group_fold", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
            "search_workspace_bytes", "act_stats_workspace_bytes", "SearchResult", "lib", "LIB_PATH"]

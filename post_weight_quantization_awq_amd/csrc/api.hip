@@ -349,6 +349,35 @@ awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t
   return hip_status(e, "awq_quantize_pack");
 }
 
+awq_status awq_norm_group_fold(const float* const* s, int32_t n_members, int64_t d_in, const void* norm,
+                               int32_t norm_dtype, void* norm_out, float* s_shared, void* stream) {
+  if (!s) return fail(AWQ_EINVAL, "s is NULL");
+  if (n_members < 1 || n_members > kMaxParts)
+    return fail(AWQ_EINVAL, "n_members %d not in [1,%d]", n_members, kMaxParts);
+  if (d_in < 0) return fail(AWQ_EINVAL, "negative size");
+  if (norm && norm_dtype != AWQ_F16 && norm_dtype != AWQ_BF16 && norm_dtype != AWQ_F32)
+    return fail(AWQ_EDTYPE, "norm_dtype %d: need AWQ_F16, AWQ_BF16 or AWQ_F32", norm_dtype);
+  if (norm && !norm_out) return fail(AWQ_EINVAL, "norm given but norm_out is NULL");
+  if (!norm && norm_out) return fail(AWQ_EINVAL, "norm_out given but norm is NULL");
+  if (d_in == 0) return ok();
+  if (!s_shared) return fail(AWQ_EINVAL, "s_shared is NULL");
+  ScaleSet S{};
+  S.n = n_members;
+  for (int m = 0; m < n_members; ++m) {
+    if (!s[m]) return fail(AWQ_EINVAL, "s[%d] is NULL", m);
+    S.p[m] = s[m];
+  }
+  for (int m = n_members; m < kMaxParts; ++m) S.p[m] = s[0];
+  const size_t esz = norm_dtype == AWQ_F32 ? 4 : 2;
+  if (norm && ((uintptr_t)norm % esz || (uintptr_t)norm_out % esz))
+    return fail(AWQ_EALIGN, "norm / norm_out not aligned to their element size");
+  if ((uintptr_t)s_shared & 3u) return fail(AWQ_EALIGN, "s_shared not 4-byte aligned");
+  mark(true, (hipStream_t)stream);
+  hipError_t e = launch_norm_group_fold(S, d_in, norm, norm_dtype, norm_out, s_shared, (hipStream_t)stream);
+  mark(false, (hipStream_t)stream);
+  return hip_status(e, "awq_norm_group_fold");
+}
+
 awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, int64_t d_out,
                               int64_t d_in, int32_t group_size, const float* s, void* out, int32_t out_dtype,
                               void* stream) {

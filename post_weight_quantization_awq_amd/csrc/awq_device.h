@@ -30,6 +30,12 @@ __device__ __forceinline__ uint4 ld_nt(const void* p) {
 }
 
 // Row-concatenated group of fp16 weight matrices, passed by value to kernels.
+// The member scale vectors of a norm group: n device pointers to fp32 [d_in].
+struct ScaleSet {
+  const float* p[kMaxParts];
+  int32_t n;
+};
+
 struct WParts {
   const uint16_t* ptr[kMaxParts];
   int64_t row_start[kMaxParts + 1];  // prefix sums of rows; row_start[n] = d_out

@@ -81,4 +81,10 @@ hipError_t launch_unpack_dequant(const int32_t* qweight, const uint16_t* scales,
                                  const int32_t* qzeros, int64_t d_out, int64_t d_in, int group_size,
                                  const float* s, void* out, bool out_f16, hipStream_t stream);
 
+// s_shared = fp32 geometric mean of the n member scales (fp64 logs), and
+// norm_out = norm / s_shared in the norm's dtype (0 fp16, 1 bf16, 2 fp32);
+// norm may be null (then only s_shared).
+hipError_t launch_norm_group_fold(const ScaleSet& S, int64_t d_in, const void* norm, int norm_dtype, void* norm_out,
+                                  float* s_shared, hipStream_t stream);
+
 }  // namespace awq

@@ -171,3 +171,24 @@ def test_workspace_sizes(A):
     assert big < (3 << 30)                        # dW built in chunks of <= 2 GiB
     with pytest.raises(A.AwqError):
         A.search_workspace_bytes(4096, 4000)
+
+
+def test_norm_group_fold_validation(A):
+    L = A.lib()
+    ptrs = lambda *p: ctypes.cast((ctypes.c_void_p * len(p))(*p), ctypes.POINTER(ctypes.c_void_p))
+    s3 = ptrs(FAKE, FAKE, FAKE)
+    f = lambda s=s3, n=3, d=4096, norm=FAKE, dt=A.AWQ_F16, out=FAKE, ssh=FAKE: \
+        L.awq_norm_group_fold(s, n, d, norm, dt, out, ssh, None)
+    assert f(s=None) == A.AWQ_EINVAL
+    assert f(n=0) == A.AWQ_EINVAL and f(n=9) == A.AWQ_EINVAL
+    assert f(s=ptrs(FAKE, None, FAKE)) == A.AWQ_EINVAL
+    assert f(d=-1) == A.AWQ_EINVAL
+    assert f(dt=7) == A.AWQ_EDTYPE
+    assert f(out=None) == A.AWQ_EINVAL            # norm without norm_out
+    assert f(norm=None) == A.AWQ_EINVAL           # norm_out without norm
+    assert f(ssh=None) == A.AWQ_EINVAL
+    assert f(norm=FAKE + 1) == A.AWQ_EALIGN       # fp16 norm at an odd address
+    assert f(dt=A.AWQ_F32, out=FAKE + 2) == A.AWQ_EALIGN
+    assert f(ssh=FAKE + 2) == A.AWQ_EALIGN
+    assert f(d=0, norm=None, out=None, ssh=None) == A.AWQ_OK
+    assert L.awq_last_error().decode() == ""
