@@ -461,6 +461,133 @@ def bench_sweep(args):
     }
 
 
+def bench_export(args):
+    """Norm-group export of the 36 blocks ("From-Scratch AWQ INT4 Quantization
+    on Qwen3-8B", exporter steps 1-3): per block the statistics of the two
+    norm groups' inputs, per-linear weight-score searches of q/k/v and
+    gate/up, the two norm folds (shared scale + folded norm), q/k/v and
+    gate/up packed with their group's shared scale, o/down packed at RTN."""
+    import torch
+    import post_weight_quantization_awq_amd as A
+    import workloads as WL
+
+    wl = WL.WORKLOADS["qwen3_8b_export"]
+    dev = torch.device("cuda:0")
+    blocks, G, K = args.blocks, wl.group_sizes[0], args.steps
+    grp = wl.groups                      # qkv, o, gate_up, down
+    NORMED, RTN = (0, 2), (1, 3)         # groups behind a norm / without one
+    Xs = {gi: WL.torch_activations(wl.seed(0, gi, 2), grp[gi].T, grp[gi].d_in, dev) for gi in NORMED}
+    Ws = [[[WL.torch_weight(wl.seed(b, gi, 1 + 1000 * p), r, g.d_in, dev) for p, r in enumerate(g.parts)]
+           for gi, g in enumerate(grp)] for b in range(blocks)]
+    norms = [{gi: WL.torch_norm(wl.seed(b, gi, 3), grp[gi].d_in, dev) for gi in NORMED} for b in range(blocks)]
+    torch.cuda.synchronize()
+    xms = {gi: torch.empty(grp[gi].d_in, device=dev) for gi in NORMED}
+    ws_st = {gi: A.workspace(A.act_stats_workspace_bytes(grp[gi].T, grp[gi].d_in), dev) for gi in NORMED}
+    members = [(gi, p) for gi in NORMED for p in range(len(grp[gi].parts))]
+    ws_se = {m: A.workspace(A.search_workspace_bytes(grp[m[0]].parts[m[1]], grp[m[0]].d_in, 1, group_size=G), dev)
+             for m in members}
+    res = {m: A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+                             torch.empty(grp[m[0]].d_in, device=dev), None, None) for m in members}
+    s_sh = {gi: torch.empty(grp[gi].d_in, device=dev) for gi in NORMED}
+    n_out = {gi: torch.empty(grp[gi].d_in, dtype=torch.float16, device=dev) for gi in NORMED}
+    packs = {(gi, p): (torch.empty((g.d_in, r // 8), dtype=torch.int32, device=dev),
+                       torch.empty((g.d_in // G, r), dtype=torch.float16, device=dev),
+                       torch.empty((g.d_in // G, r // 8), dtype=torch.int32, device=dev))
+             for gi, g in enumerate(grp) for p, r in enumerate(g.parts)}
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(args.streams)]
+    chain_of = {0: 0, 2: 1, 1: 2, 3: 3}  # attention group, MLP group, o_proj, down_proj
+
+    def plans(stream_of):
+        """Per block, the calls in order, each tagged with its kernel kind."""
+        st = {gi: A.ActStatsPlan(Xs[gi], x_mean=xms[gi], ws=ws_st[gi], stream=stream_of(chain_of[gi])) for gi in NORMED}
+        out = []
+        for b in range(blocks):
+            calls = []
+            for gi in NORMED:
+                sp = stream_of(chain_of[gi])
+                calls.append(("act_stats", st[gi]))
+                for p in range(len(grp[gi].parts)):
+                    calls.append(("search", A.SearchPlan([Ws[b][gi][p]], xms[gi], group_size=G, ws=ws_se[(gi, p)],
+                                                         out=res[(gi, p)], stream=sp)))
+                calls.append(("fold", A.FoldPlan([res[(gi, p)].best_s for p in range(len(grp[gi].parts))],
+                                                 norms[b][gi], out=n_out[gi], s_shared=s_sh[gi], stream=sp)))
+                for p in range(len(grp[gi].parts)):
+                    calls.append(("pack", A.PackPlan(Ws[b][gi][p], G, s_sh[gi], out=packs[(gi, p)], stream=sp)))
+            for gi in RTN:
+                for p in range(len(grp[gi].parts)):
+                    calls.append(("pack", A.PackPlan(Ws[b][gi][p], G, None, out=packs[(gi, p)],
+                                                     stream=stream_of(chain_of[gi]))))
+            out.append(calls)
+        return out
+
+    par = plans(lambda c: streams[c % len(streams)])
+    ser = plans(lambda c: main)
+    n_calls = sum(len(c) for c in ser)
+    ev = HipEvents(2 * n_calls * K)
+
+    def step(pl, k=-1):
+        n, kinds = k * 2 * n_calls, []
+        for calls in pl:
+            for kind, c in calls:
+                if k >= 0:
+                    A.set_timing_events(ev.h(n), ev.h(n + 1))
+                    kinds.append((kind, n))
+                    n += 2
+                c.launch()
+        if k >= 0:
+            A.set_timing_events(None, None)
+        return kinds
+
+    def step_streams():
+        start = torch.cuda.Event()
+        start.record(main)
+        for s_ in streams:
+            s_.wait_event(start)
+        step(par)
+        for s_ in streams:
+            done = torch.cuda.Event()
+            done.record(s_)
+            main.wait_event(done)
+
+    for _ in range(args.warmup):
+        step_streams()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(K):
+        step_streams()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t1) * 1e3 / K
+    tagged = []
+    for k in range(K):  # kernel durations: the same steps on one stream, events around each call's main kernel
+        tagged += step(ser, k)
+    torch.cuda.synchronize()
+    sums, counts = {}, {}
+    for kind, n in tagged:
+        sums[kind] = sums.get(kind, 0.0) + ev.ms(n, n + 1)
+        counts[kind] = counts.get(kind, 0) + 1
+    ev.close()
+    per_step = {kk: v / K for kk, v in sums.items()}
+    n_search = blocks * sum(grp[gi].d_out * grp[gi].d_in for gi in NORMED)
+    n_all = blocks * sum(g.d_out * g.d_in for g in grp)
+    pk = blocks * sum(pack_bytes(r, g.d_in, G) for g in grp for r in g.parts)
+    frac = SEARCH_OPS_PER_ELEM_PT * n_search * 20 / (per_step["search"] * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T
+    return {
+        "metric": METRIC, "value": n_search * 20 / (ms_step * 1e-3), "unit": "weight-elem*grid-pt/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_export", "blocks": blocks, "searched_weights": n_search,
+                   "exported_weights": n_all, "n_grid": 20, "group_size": G, "score": "weight",
+                   "streams": args.streams},
+        "weights_exported_per_s": n_all / (ms_step * 1e-3),
+        "kernel_ms_per_step": per_step,
+        "fold_us_per_call": sums["fold"] / counts["fold"] * 1e3,
+        "pack_GBps": pk / (per_step["pack"] * 1e-3) / 1e9,
+        "roofline": {"bound": "alu", "achieved": frac * VALU_LANE_OPS_PEAK_T, "peak": VALU_LANE_OPS_PEAK_T,
+                     "unit": "TOP/s", "frac": frac, "traffic": None, "kernel": "search_weight_kernel"},
+    }
+
+
 def bench_copy(args):
     """Plain device copy of 512 MiB (torch), the calibration of the HBM byte counters."""
     import torch
@@ -488,7 +615,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="q_proj_4096x4096",
                     choices=["single_linear_256x512", "q_proj_4096x4096", "qkv_6144x4096_output",
-                             "mlp_output_clip", "qwen3_8b_sweep", "copy_512MiB"])
+                             "mlp_output_clip", "qwen3_8b_sweep", "qwen3_8b_export", "copy_512MiB"])
     ap.add_argument("--group-size", type=int, default=None)
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
     ap.add_argument("--streams", type=int, default=4,
@@ -513,6 +640,8 @@ def main() -> int:
         out = bench_weight(args, args.workload)
     elif args.workload == "qwen3_8b_sweep":
         out = bench_sweep(args)
+    elif args.workload == "qwen3_8b_export":
+        out = bench_export(args)
     elif args.workload == "copy_512MiB":
         out = bench_copy(args)
     else:

@@ -12,7 +12,8 @@ Workloads are the Qwen3-8B-shaped linear groups that the scale search runs on:
   random 1% of the channels (round(0.01 * d_in)) is multiplied by 50 to model
   the outlier channels whose weights AWQ protects;
 * the down-projection input of an MLP is SiLU(X W_gate^T) * (X W_up^T),
-  evaluated in fp32 from the fp16 weights and rounded to bf16.
+  evaluated in fp32 from the fp16 weights and rounded to bf16;
+* norm weights (the export's RMSNorm gains) g_i = 1 + 0.1 * N(0, 1), fp16.
 
 bf16 tensors are carried as ``uint16`` arrays holding the bit pattern, since
 numpy has no bf16 dtype.  Large device-resident workloads (the full-model sweep)
@@ -103,6 +104,21 @@ def torch_weight(seed: int, d_out: int, d_in: int, device):
     g.manual_seed(seed)
     z = torch.randn((d_out, d_in), generator=g, device=device, dtype=torch.float32)
     return (z * WEIGHT_STD).to(torch.float16)
+
+
+NORM_STD = 0.1
+
+
+def make_norm(seed: int, d: int) -> np.ndarray:
+    """Norm weight [d] fp16 ~ 1 + N(0, 0.1^2)."""
+    return (1.0 + rng(seed).standard_normal(d, dtype=np.float32) * np.float32(NORM_STD)).astype(np.float16)
+
+
+def torch_norm(seed: int, d: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (1.0 + torch.randn(d, generator=g, device=device, dtype=torch.float32) * NORM_STD).to(torch.float16)
 
 
 def torch_activations(seed: int, T: int, d_in: int, device, dtype: str = "bf16"):
@@ -197,6 +213,10 @@ WORKLOADS = {
         [128], score="output", n_clip=20, seed_base=4000),
     "qwen3_8b_sweep": Workload(
         "qwen3_8b_sweep", QWEN3_8B_BLOCK, [128, 64], blocks=36, seed_base=5000),
+    # export of the same blocks: per-linear searches of q/k/v and gate/up, the
+    # two norm folds, packing with the shared scales, o/down at RTN
+    "qwen3_8b_export": Workload(
+        "qwen3_8b_export", QWEN3_8B_BLOCK, [128], blocks=36, seed_base=6000),
 }
 
 
