@@ -59,11 +59,11 @@ PMC_TRAFFIC = {
     ("search_weight_kernel", "q_proj_4096x4096"): {
         "fetch_kib": 16756.3, "write_kib": 640.0,
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
-        "sha256": "22dc4325fa32c158c87346270825f677711ba5a78d2bff255613a72e5d89ec6d"},
+        "sha256": "71df8f03ac5773c1afe4f65fedbed4389fa7c4d28b6b47f13f5f9406ace6694d"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11797803.2, "write_kib": 30720.0,
+        "fetch_kib": 11797735.3, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "2b503c378c5e6c431b26ff4c04308976c9b7583824b9c64387e6f897876c8588"},
+        "sha256": "10a16ec891483e54946f7ed520cafaef1a86138a04c2cf42f08085a00623413c"},
 }
 
 
