@@ -52,6 +52,10 @@ its reason in the design notes of the repository):
   of output row 8m + order[j], order = [0, 2, 4, 6, 1, 3, 5, 7];
   scales[g, o] = fp16(step), qzeros[g, m] = 0x77777777.
 
+Duo scaling: w_mean is the mean over the group's rows of |w| / rowmax|w|
+(quotients in fp32, sums in fp64, all-zero rows contributing 0), and
+t = max(x^r / (w_mean^(1-r) + 1e-4), 1e-4) before the same normalisation.
+
 Norm-group export: the shared scale is the per-channel geometric mean of the
 member scales, evaluated as exp(mean(ln s)) in fp64 and rounded once to fp32;
 the folded norm is the IEEE fp32 quotient rounded once to the norm's dtype.
@@ -133,8 +137,49 @@ def candidate_scale(x_mean: np.ndarray, alpha: float, s_min: float = S_MIN) -> n
     return (t / norm).astype(F32)
 
 
-def candidate_scales(x_mean: np.ndarray, n_grid: int = 20, s_min: float = S_MIN) -> np.ndarray:
+def candidate_scales(x_mean: np.ndarray, n_grid: int = 20, s_min: float = S_MIN,
+                     w_mean: Optional[np.ndarray] = None) -> np.ndarray:
+    """Rows s_k for alpha_k = k / n_grid; with w_mean given, the duo-scaling
+    candidates (candidate_scale_duo)."""
+    if w_mean is not None:
+        return np.stack([candidate_scale_duo(x_mean, w_mean, a, s_min) for a in grid_alphas(n_grid)])
     return np.stack([candidate_scale(x_mean, a, s_min) for a in grid_alphas(n_grid)])
+
+
+# ---------------------------------------------------------------------------
+# O2b: duo scaling ([cassindra] The scale search as code, duo_scaling=True:
+#      w_mean = (|W| / rowmax |W|).mean over rows, per input channel, of the
+#      group's concatenated weights; s = x_mean^r / (w_mean^(1-r) + 1e-4),
+#      then the same clamp and normalisation as the plain candidates)
+# ---------------------------------------------------------------------------
+DUO_EPS = 1e-4
+
+
+def weight_channel_mean(W_parts: Sequence[np.ndarray]) -> np.ndarray:
+    """w_mean[i] = (1/d_out) sum_o |W[o, i]| / max_j |W[o, j]| over the
+    concatenated rows: each quotient in IEEE fp32, the sum over rows in fp64
+    (row order), the mean rounded once to fp32.  A row whose entries are all
+    zero contributes 0 (its quotients would be 0/0)."""
+    W = np.concatenate([decode_weight(w) for w in W_parts], axis=0)       # exact fp32
+    A = np.abs(W)
+    rmax = A.max(axis=1)
+    total = np.zeros(W.shape[1], dtype=F64)
+    for o in range(W.shape[0]):
+        if rmax[o] > 0:
+            total += (A[o] / rmax[o]).astype(F32).astype(F64)
+    return (total / W.shape[0]).astype(F32)
+
+
+def candidate_scale_duo(x_mean: np.ndarray, w_mean: np.ndarray, alpha: float,
+                        s_min: float = S_MIN) -> np.ndarray:
+    """t = max(x^alpha / (w^(1-alpha) + 1e-4), s_min), s = t / sqrt(max t * min t),
+    in fp64, rounded once to fp32.  pow(v, 0) = 1 for every v (R5)."""
+    x, w = x_mean.astype(F64), w_mean.astype(F64)
+    num = np.ones_like(x) if alpha == 0.0 else np.power(x, alpha)
+    den = np.power(w, 1.0 - alpha) + DUO_EPS
+    t = np.maximum(num / den, s_min)
+    norm = np.sqrt(t.max() * t.min())
+    return (t / norm).astype(F32)
 
 
 # ---------------------------------------------------------------------------
@@ -230,14 +275,15 @@ def first_argmin(errors: Sequence[float]) -> int:
 
 def search_scales(W_parts: Sequence[np.ndarray], x_mean: np.ndarray, group_size: int,
                   n_grid: int = 20, score: str = "weight", X: Optional[np.ndarray] = None,
-                  s_min: float = S_MIN):
+                  s_min: float = S_MIN, duo: bool = False):
     """Returns (errors [n_grid] fp64, best index, best s fp32 [d_in]).
 
     The linears of one input-sharing group are scored together, their rows
-    concatenated ([cassindra] torch.cat of the group's weights).
+    concatenated ([cassindra] torch.cat of the group's weights); duo = True
+    takes the duo-scaling candidates of those rows.
     """
     W = np.concatenate([np.asarray(w) for w in W_parts], axis=0)
-    S = candidate_scales(x_mean, n_grid, s_min)
+    S = candidate_scales(x_mean, n_grid, s_min, weight_channel_mean(W_parts) if duo else None)
     errs = []
     for k in range(n_grid):
         if score == "weight":

@@ -167,6 +167,27 @@ def _bf16_truncate(x):
     return (np.asarray(x, dtype=F32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def _wmean_unnormalised(W_parts):
+    W = np.concatenate([O.decode_weight(w) for w in W_parts], axis=0)
+    return np.abs(W).astype(F64).mean(axis=0).astype(F32)
+
+
+def _wmean_colmax(W_parts):
+    W = np.abs(np.concatenate([O.decode_weight(w) for w in W_parts], axis=0))
+    cmax = W.max(axis=0)
+    q = np.where(cmax > 0, W / np.where(cmax > 0, cmax, 1), 0).astype(F32)
+    return q.astype(F64).mean(axis=0).astype(F32)
+
+
+def _duo(x_mean, w_mean, alpha, s_min=O.S_MIN, swap=False, eps_outside=False):
+    x, w = x_mean.astype(F64), w_mean.astype(F64)
+    num = np.ones_like(x) if alpha == 0.0 else np.power(x, alpha)
+    e = alpha if swap else 1.0 - alpha
+    t = num / np.power(w, e) + O.DUO_EPS if eps_outside else num / (np.power(w, e) + O.DUO_EPS)
+    t = np.maximum(t, s_min)
+    return (t / np.sqrt(t.max() * t.min())).astype(F32)
+
+
 MUTANTS = {
     "act_stats: signed mean": [("act_stats", _act_stats_signed)],
     "act_stats: max |x|": [("act_stats", _act_stats_max)],
@@ -196,6 +217,11 @@ MUTANTS = {
     "pack: zero point 8": [("ZERO_POINT", 8)],
     "pack: fp16 scales truncated": [("f32_to_f16", _f16_trunc)],
     "pack: qweight along d_in": [("pack_codes", _pack_along_d_in)],
+    "duo: w_mean not row-normalised": [("weight_channel_mean", _wmean_unnormalised)],
+    "duo: w_mean normalised by column max": [("weight_channel_mean", _wmean_colmax)],
+    "duo: exponents swapped": [("candidate_scale_duo", lambda x, w, a, s_min=O.S_MIN: _duo(x, w, a, s_min, swap=True))],
+    "duo: 1e-4 added outside the quotient": [("candidate_scale_duo",
+                                              lambda x, w, a, s_min=O.S_MIN: _duo(x, w, a, s_min, eps_outside=True))],
     "export: arithmetic mean of the scales": [("shared_scale", _shared_arith)],
     "export: first member's scale": [("shared_scale", lambda s_members: np.asarray(s_members[0], dtype=F32))],
     "export: logarithms in fp32": [("shared_scale", _shared_f32)],

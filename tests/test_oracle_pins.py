@@ -489,3 +489,53 @@ class TestNormGroupExport:
         r = O.export_rtn(W, 128)
         u = O.quantize_pack(W, np.ones(256, F32), 128)
         assert all(np.array_equal(a, b) for a, b in zip(r, u))
+
+
+class TestDuoScaling:
+    """[cassindra] The scale search as code, duo_scaling=True."""
+
+    def test_weight_mean_closed_forms(self):
+        f16 = lambda a: np.array(a, dtype=np.float16)
+        assert np.array_equal(O.weight_channel_mean([f16(np.full((5, 8), -0.25))]), np.ones(8, F32))
+        W = np.zeros((4, 6), np.float16)
+        for o in range(4):
+            W[o, o] = 0.5 * (o + 1)                   # one nonzero per row
+        wm = O.weight_channel_mean([W])
+        assert np.array_equal(wm, np.array([0.25, 0.25, 0.25, 0.25, 0, 0], F32))
+        # an all-zero row counts in the mean with 0; row [1, -2] gives [0.5, 1]
+        assert np.array_equal(O.weight_channel_mean([f16([[0, 0]]), f16([[1, -2]])]), np.array([0.25, 0.5], F32))
+
+    def test_weight_mean_invariances(self):
+        W = WL.make_weight(31, 40, 256)
+        wm = O.weight_channel_mean([W])
+        assert np.all(wm > 0) and np.all(wm <= 1)
+        Ws = W.copy()
+        Ws[::3] = (Ws[::3].astype(F32) * 4).astype(np.float16)      # power-of-two row scaling
+        assert np.array_equal(O.weight_channel_mean([Ws]), wm)
+        assert ulps32(O.weight_channel_mean([W[::-1]]), wm) <= 1        # row order
+        assert np.array_equal(O.weight_channel_mean([W[:10], W[10:]]), wm)   # parts concatenate
+
+    def test_candidates_closed_forms(self):
+        x = np.full(16, 3.0, F32)
+        for k in range(20):
+            assert np.array_equal(O.candidate_scale_duo(x, np.full(16, 0.4, F32), k / 20), np.ones(16, F32))
+        # w_mean = 1: the denominator is the constant 1 + 1e-4, which the
+        # normalisation removes: the plain candidates (away from the clamp)
+        xm = np.exp(np.random.default_rng(12).normal(0, 1, 300)).astype(F32)
+        for a in (0.0, 0.35, 0.95):
+            assert ulps32(O.candidate_scale_duo(xm, np.ones(300, F32), a), O.candidate_scale(xm, a)) <= 1
+
+    def test_candidates_normalised_and_elementwise(self):
+        rng = np.random.default_rng(13)
+        xm = np.exp(rng.normal(0, 1, 64)).astype(F32)
+        wm = rng.uniform(0.05, 0.6, 64).astype(F32)
+        for a in (0.0, 0.25, 0.6):
+            s = O.candidate_scale_duo(xm, wm, a)
+            t = [max((float(xv) ** a if a else 1.0) / (float(wv) ** (1 - a) + 1e-4), 1e-4) for xv, wv in zip(xm, wm)]
+            norm = math.sqrt(max(t) * min(t))
+            assert ulps32(s, np.array([v / norm for v in t]).astype(F32)) <= 1
+            assert abs(float(s.astype(F64).max()) * float(s.astype(F64).min()) - 1.0) < 1e-6
+        # alpha = 0 is not RTN under duo scaling: s is proportional to 1 / (w_mean + 1e-4)
+        s0 = O.candidate_scale_duo(xm, wm, 0.0).astype(F64)
+        r = s0 * (wm.astype(F64) + 1e-4)
+        assert np.allclose(r, r[0], rtol=1e-6)
