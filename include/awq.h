@@ -72,8 +72,14 @@ typedef struct {
   int32_t n_clip;     /* 0 = no clip search; else >= 2 ratios (output score only) */
   double s_min;       /* lower clamp of x_mean^alpha before normalising (1e-4)    */
   float clip_lo;      /* smallest clip ratio, in (0, 1]; ratios 1.0 .. clip_lo     */
-  int32_t reserved;   /* must be 0                                                */
+  int32_t flags;      /* AWQ_FLAG_DUO: duo-scaling candidates; other bits 0        */
 } awq_search_cfg;
+
+/* [cassindra] The scale search as code, duo_scaling=True: the candidates are
+ * s = x_mean^r / (w_mean^(1-r) + 1e-4) (then the same clamp and
+ * normalisation), w_mean the row-normalised mean |w| of the group's rows per
+ * input channel (awq_weight_channel_mean). */
+#define AWQ_FLAG_DUO 1
 
 /* One group of linears sharing an input ([cassindra] torch.cat of the group's
  * weights): part p is an fp16 device matrix [rows[p], d_in], 16-byte aligned.
@@ -118,13 +124,50 @@ awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_gri
                                 float* S, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * awq_weight_channel_mean -- duo scaling's weight statistic.
+ * [cassindra] The scale search as code:
+ *   w_mean = (w_cat.abs() / w_cat.abs().amax(dim=1)).mean(dim=0)
+ *
+ *   w_mean[i] = (1/d_out) sum_o |W[o, i]| / max_j |W[o, j]|
+ *
+ * over the concatenated rows of W (each quotient an IEEE fp32 division, an
+ * all-zero row contributing 0; sums in fp64 in a fixed order, rounded once to
+ * fp32).  W: as awq_search_scales, d_in a positive multiple of 8.
+ * w_mean: fp32 [d_in].  ws: awq_weight_channel_mean_workspace(d_out_total,
+ * d_in) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+awq_status awq_weight_channel_mean_workspace(int64_t d_out_total, int64_t d_in, size_t* bytes /* [host] */);
+awq_status awq_weight_channel_mean(const awq_wgroup* W /* [host] */, int64_t d_in, float* w_mean, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_candidate_scales_duo -- the duo-scaling candidate table.
+ * [cassindra] The scale search as code (duo_scaling=True):
+ *
+ *   t_k[i] = max(x_mean[i]^r / (w_mean[i]^(1-r) + 1e-4), s_min),  r = k / n_grid
+ *   S[k, i] = RN_fp32(t_k[i] / sqrt(max_i t_k[i] * min_i t_k[i]))
+ *
+ * evaluated in fp64 (pow(v, 0) = 1; r = 0 gives 1 / (w_mean + 1e-4), which is
+ * not plain RTN).  x_mean, w_mean: fp32 [d_in], finite, >= 0.  S: fp32
+ * [n_grid, d_in].  ws: awq_candidate_scales_duo_workspace(d_in, n_grid) bytes,
+ * 256-byte aligned (the fp64 table and per-block extrema).
+ * ------------------------------------------------------------------------- */
+awq_status awq_candidate_scales_duo_workspace(int64_t d_in, int32_t n_grid, size_t* bytes /* [host] */);
+awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, int64_t d_in, int32_t n_grid,
+                                    double s_min, float* S, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * awq_search_scales -- grid search of alpha for one input-sharing group.
  * [konic] AWQ scaling (grid search, activation-weighted error, alpha = 0 is
- * RTN so the search never worsens it); [konic] Group-wise symmetric INT4
+ * RTN so the search never worsens it -- for the plain candidates; with
+ * cfg->flags & AWQ_FLAG_DUO the table is awq_candidate_scales_duo's over
+ * awq_weight_channel_mean of the group, and alpha = 0 is not RTN); [konic]
+ * Group-wise symmetric INT4
  * (step = max|group| / 7, q = round(w / step).clamp(-7, 7), round half to
  * even); [cassindra] The scale search as code (keep the first strict minimum,
  * weights restored: W is read-only here) and pipeline step 5 (clip search).
  *
+ * S is the awq_candidate_scales table (or, duo, awq_candidate_scales_duo's).
  * For k = 0..n_grid-1, with s = S[k] and v = W*s (fp32), per row o and group g:
  *   a = max|v|, step = RN(a / 7), q = clamp(rint(v / step), -7, 7), w_hat = q*step/s
  *   AWQ_SCORE_WEIGHT: err[k] = sum_{o,i} ((W[o,i] - w_hat[o,i]) * x_mean[i])^2

@@ -31,13 +31,15 @@ LIB_PATH = os.path.join(_HERE, "libawq.so")
 AWQ_OK, AWQ_EINVAL, AWQ_ESHAPE, AWQ_EDTYPE, AWQ_EWORKSPACE, AWQ_EALIGN, AWQ_EHIP = range(7)
 AWQ_F16, AWQ_BF16, AWQ_F32 = 0, 1, 2
 AWQ_SCORE_WEIGHT, AWQ_SCORE_OUTPUT = 0, 1
+AWQ_FLAG_DUO = 1
 STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_EINVAL", 2: "AWQ_ESHAPE", 3: "AWQ_EDTYPE",
                 4: "AWQ_EWORKSPACE", 5: "AWQ_EALIGN", 6: "AWQ_EHIP"}
 
 EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales_workspace", "awq_candidate_scales",
             "awq_search_workspace", "awq_search_scales", "awq_quantize_pack",
-            "awq_unpack_dequant", "awq_norm_group_fold", "awq_last_error", "awq_abi_version",
-            "awq_set_timing_events")
+            "awq_unpack_dequant", "awq_norm_group_fold", "awq_weight_channel_mean_workspace",
+            "awq_weight_channel_mean", "awq_candidate_scales_duo_workspace", "awq_candidate_scales_duo",
+            "awq_last_error", "awq_abi_version", "awq_set_timing_events")
 
 
 class AwqError(RuntimeError):
@@ -50,7 +52,7 @@ class SearchCfg(ctypes.Structure):
     _fields_ = [("group_size", ctypes.c_int32), ("n_grid", ctypes.c_int32),
                 ("score", ctypes.c_int32), ("n_clip", ctypes.c_int32),
                 ("s_min", ctypes.c_double), ("clip_lo", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
 
 class WGroup(ctypes.Structure):
@@ -76,6 +78,10 @@ def _load() -> ctypes.CDLL:
         "awq_quantize_pack": [P, I64, I64, I32, P, P, P, P, P, P],
         "awq_unpack_dequant": [P, P, P, I64, I64, I32, P, P, I32, P],
         "awq_norm_group_fold": [ctypes.POINTER(ctypes.c_void_p), I32, I64, P, I32, P, P, P],
+        "awq_weight_channel_mean_workspace": [I64, I64, PSZ],
+        "awq_weight_channel_mean": [ctypes.POINTER(WGroup), I64, P, P, SZ, P],
+        "awq_candidate_scales_duo_workspace": [I64, I32, PSZ],
+        "awq_candidate_scales_duo": [P, P, I64, I32, F64, P, P, SZ, P],
         "awq_set_timing_events": [P, P],
     }
     for name, args in sig.items():
@@ -200,6 +206,47 @@ def candidate_scales(x_mean: torch.Tensor, n_grid: int = 20, s_min: float = 1e-4
     return S
 
 
+def _wgroup(parts):
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    rows = (ctypes.c_int64 * len(parts))(*[p.shape[0] for p in parts])
+    return WGroup(len(parts), ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)),
+                  ctypes.cast(rows, ctypes.POINTER(ctypes.c_int64))), (ptrs, rows)
+
+
+def weight_channel_mean(W_parts: Sequence[torch.Tensor], stream=None) -> torch.Tensor:
+    """Duo scaling's w_mean: row-normalised mean |w| per input channel of the
+    group's concatenated rows (fp32 [d_in])."""
+    parts = list(W_parts)
+    for p in parts:
+        _dev(p, "W")
+        if p.dtype != torch.float16 or p.dim() != 2 or not p.is_contiguous() or p.shape[1] != parts[0].shape[1]:
+            raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
+    d_in, dev = parts[0].shape[1], parts[0].device
+    d_out = sum(p.shape[0] for p in parts)
+    n = ctypes.c_size_t()
+    _check(lib().awq_weight_channel_mean_workspace(d_out, d_in, ctypes.byref(n)))
+    ws = workspace(n.value, dev)
+    out = torch.empty(d_in, dtype=torch.float32, device=dev)
+    grp, keep = _wgroup(parts)
+    _check(lib().awq_weight_channel_mean(ctypes.byref(grp), d_in, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def candidate_scales_duo(x_mean: torch.Tensor, w_mean: torch.Tensor, n_grid: int = 20, s_min: float = 1e-4,
+                         stream=None) -> torch.Tensor:
+    """Duo-scaling candidate table S [n_grid, d_in]."""
+    _dev(x_mean, "x_mean")
+    _dev(w_mean, "w_mean")
+    d_in = x_mean.numel()
+    S = torch.empty((n_grid, d_in), dtype=torch.float32, device=x_mean.device)
+    n = ctypes.c_size_t()
+    _check(lib().awq_candidate_scales_duo_workspace(d_in, n_grid, ctypes.byref(n)))
+    ws = workspace(n.value, x_mean.device)
+    _check(lib().awq_candidate_scales_duo(_ptr(x_mean), _ptr(w_mean), d_in, n_grid, s_min, _ptr(S), _ptr(ws),
+                                          ws.numel(), _stream(stream)))
+    return S
+
+
 @dataclasses.dataclass
 class SearchResult:
     err: torch.Tensor                 # fp32 [n_grid]
@@ -209,14 +256,15 @@ class SearchResult:
     clip_err: Optional[torch.Tensor]  # fp32 [d_out, n_clip] or None
 
 
-def _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min) -> SearchCfg:
+def _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo=False) -> SearchCfg:
     sc = {"weight": AWQ_SCORE_WEIGHT, "output": AWQ_SCORE_OUTPUT}[score] if isinstance(score, str) else score
-    return SearchCfg(group_size, n_grid, sc, n_clip, s_min, clip_lo, 0)
+    return SearchCfg(group_size, n_grid, sc, n_clip, s_min, clip_lo, AWQ_FLAG_DUO if duo else 0)
 
 
 def search_workspace_bytes(d_out: int, d_in: int, T: int = 0, *, group_size: int = 128, n_grid: int = 20,
-                           score="weight", n_clip: int = 0, clip_lo: float = 0.5, s_min: float = 1e-4) -> int:
-    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min)
+                           score="weight", n_clip: int = 0, clip_lo: float = 0.5, s_min: float = 1e-4,
+                           duo: bool = False) -> int:
+    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo)
     n = ctypes.c_size_t()
     _check(lib().awq_search_workspace(ctypes.byref(cfg), d_out, d_in, T, ctypes.byref(n)))
     return n.value
@@ -229,7 +277,8 @@ class SearchPlan(_Prepared):
     def __init__(self, W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, *, group_size: int = 128,
                  n_grid: int = 20, score="weight", X: Optional[torch.Tensor] = None, n_clip: int = 0,
                  clip_lo: float = 0.5, s_min: float = 1e-4, want_clip_err: bool = False,
-                 ws: Optional[torch.Tensor] = None, out: Optional[SearchResult] = None, stream=None):
+                 ws: Optional[torch.Tensor] = None, out: Optional[SearchResult] = None, stream=None,
+                 duo: bool = False):
         parts: List[torch.Tensor] = list(W_parts)
         if not parts:
             raise ValueError("empty weight group")
@@ -240,7 +289,7 @@ class SearchPlan(_Prepared):
                 raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
         dev = parts[0].device
         d_out = sum(p.shape[0] for p in parts)
-        self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min)
+        self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo)
         T, ld, xdt = 0, 0, AWQ_BF16
         if X is not None:
             _dev(X, "X")
@@ -373,5 +422,6 @@ def set_timing_events(before: Optional[int], after: Optional[int]) -> None:
     _check(lib().awq_set_timing_events(before, after))
 
 
-__all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "PackPlan", "FoldPlan", "norm_group_fold", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
+__all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "PackPlan", "FoldPlan", "norm_group_fold",
+           "weight_channel_mean", "candidate_scales_duo", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
            "search_workspace_bytes", "act_stats_workspace_bytes", "SearchResult", "lib", "LIB_PATH"]

@@ -252,4 +252,10 @@ hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, i
   return hipGetLastError();
 }
 
+hipError_t launch_split_mean(const double* part, int64_t n_split, int64_t d_in, double inv_count, float* out,
+                             hipStream_t stream) {
+  act_stats_final_kernel<<<(unsigned)((d_in + 31) / 32), 256, 0, stream>>>(part, n_split, d_in, inv_count, 0, out);
+  return hipGetLastError();
+}
+
 }  // namespace awq

@@ -56,7 +56,24 @@ struct SearchPlan {
   int64_t n_x, n_db;    // output score: X max partials, dW max partials per candidate
   int cand_chunk;       // output score: candidates per dW chunk
   size_t off_S, off_C2, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
+  bool duo;                   // duo-scaling candidates: w_mean, its scratch, the fp64 table
+  size_t off_wmean, off_rmax, off_wpart, off_T, off_ext;
 };
+
+// scratch of the duo candidates, from `off` on
+size_t plan_duo(SearchPlan& p, int64_t d_out, int64_t d_in, int n_grid, size_t off) {
+  p.off_wmean = off;
+  off += align256((size_t)d_in * sizeof(float));
+  p.off_rmax = off;
+  off += align256((size_t)d_out * sizeof(float));
+  p.off_wpart = off;
+  off += align256((size_t)wmean_splits(d_out) * d_in * sizeof(double));
+  p.off_T = off;
+  off += align256((size_t)n_grid * d_in * sizeof(double));
+  p.off_ext = off;
+  off += align256((size_t)n_grid * duo_cand_blocks(d_in) * 2 * sizeof(double));
+  return off;
+}
 
 constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
 
@@ -101,8 +118,22 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     p.off_chunk = off;
     off += align256((size_t)max_c * reduce_cols_chunks(d_out) * sizeof(double));
   }
+  p.duo = (cfg.flags & AWQ_FLAG_DUO) != 0;
+  if (p.duo) off = plan_duo(p, d_out, d_in, cfg.n_grid, off);
   p.total = off;
   return p;
+}
+
+// the candidate table of a search: plain, or duo scaling over the group's rows
+hipError_t launch_cands(const awq_search_cfg& cfg, const SearchPlan& plan, const WParts& parts, int64_t d_out,
+                        int64_t d_in, const float* x_mean, char* base, float* S, float* C2, hipStream_t s) {
+  if (!plan.duo) return launch_candidates(x_mean, d_in, cfg.n_grid, cfg.s_min, S, C2, s);
+  float* w_mean = (float*)(base + plan.off_wmean);
+  hipError_t e = launch_weight_channel_mean(parts, d_out, d_in, (float*)(base + plan.off_rmax),
+                                            (double*)(base + plan.off_wpart), w_mean, s);
+  if (e != hipSuccess) return e;
+  return launch_candidates_duo(x_mean, w_mean, d_in, cfg.n_grid, cfg.s_min, (double*)(base + plan.off_T),
+                               (double*)(base + plan.off_ext), S, C2, s);
 }
 
 awq_status check_cfg(const awq_search_cfg* cfg) {
@@ -117,7 +148,7 @@ awq_status check_cfg(const awq_search_cfg* cfg) {
     if (!(cfg->clip_lo > 0.0f && cfg->clip_lo <= 1.0f)) return fail(AWQ_EINVAL, "clip_lo %g not in (0,1]", (double)cfg->clip_lo);
   }
   if (!(cfg->s_min > 0.0 && isfinite(cfg->s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
-  if (cfg->reserved != 0) return fail(AWQ_EINVAL, "reserved must be 0");
+  if (cfg->flags & ~AWQ_FLAG_DUO) return fail(AWQ_EINVAL, "flags 0x%x: unknown bits", (unsigned)cfg->flags);
   return AWQ_OK;
 }
 
@@ -189,6 +220,87 @@ awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_gri
 }
 
 // ---------------------------------------------------------------------------
+// group parts of an awq_wgroup (validated), d_out in *d_out
+static awq_status read_group(const awq_wgroup* W, WParts* parts, int64_t* d_out) {
+  if (!W || !W->w || !W->rows) return fail(AWQ_EINVAL, "weight group is NULL");
+  if (W->n_parts < 1 || W->n_parts > kMaxParts) return fail(AWQ_EINVAL, "n_parts %d not in [1,%d]", W->n_parts, kMaxParts);
+  *parts = WParts{};
+  parts->n = W->n_parts;
+  int64_t n = 0;
+  for (int p = 0; p < W->n_parts; ++p) {
+    if (W->rows[p] < 0) return fail(AWQ_EINVAL, "rows[%d] < 0", p);
+    if (W->rows[p] > 0 && !W->w[p]) return fail(AWQ_EINVAL, "w[%d] is NULL", p);
+    if (!aligned16(W->w[p])) return fail(AWQ_EALIGN, "w[%d] not 16-byte aligned", p);
+    parts->ptr[p] = (const uint16_t*)W->w[p];
+    parts->row_start[p] = n;
+    n += W->rows[p];
+  }
+  for (int p = W->n_parts; p <= kMaxParts; ++p) parts->row_start[p] = n;
+  for (int p = W->n_parts; p < kMaxParts; ++p) parts->ptr[p] = parts->ptr[W->n_parts - 1];
+  if (n < 1) return fail(AWQ_EINVAL, "group has no rows");
+  *d_out = n;
+  return AWQ_OK;
+}
+
+static size_t wmean_ws(int64_t d_out, int64_t d_in) {
+  return align256((size_t)d_out * sizeof(float)) + align256((size_t)wmean_splits(d_out) * d_in * sizeof(double));
+}
+
+awq_status awq_weight_channel_mean_workspace(int64_t d_out_total, int64_t d_in, size_t* bytes) {
+  if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
+  if (d_out_total < 1 || d_in < 1) return fail(AWQ_EINVAL, "need d_out_total >= 1 and d_in >= 1");
+  *bytes = wmean_ws(d_out_total, d_in);
+  return ok();
+}
+
+awq_status awq_weight_channel_mean(const awq_wgroup* W, int64_t d_in, float* w_mean, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  WParts parts;
+  int64_t d_out = 0;
+  awq_status st = read_group(W, &parts, &d_out);
+  if (st) return st;
+  if (d_in < 8 || d_in % 8) return fail(AWQ_ESHAPE, "d_in %lld not a positive multiple of 8", (long long)d_in);
+  if (!w_mean) return fail(AWQ_EINVAL, "w_mean is NULL");
+  const size_t need = wmean_ws(d_out, d_in);
+  if (!ws || ws_bytes < need) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255u) return fail(AWQ_EALIGN, "ws not 256-byte aligned");
+  char* base = (char*)ws;
+  return hip_status(launch_weight_channel_mean(parts, d_out, d_in, (float*)base,
+                                               (double*)(base + align256((size_t)d_out * sizeof(float))), w_mean,
+                                               (hipStream_t)stream),
+                    "awq_weight_channel_mean");
+}
+
+static size_t duo_cand_ws(int64_t d_in, int n_grid) {
+  return align256((size_t)n_grid * d_in * sizeof(double)) +
+         align256((size_t)n_grid * duo_cand_blocks(d_in) * 2 * sizeof(double));
+}
+
+awq_status awq_candidate_scales_duo_workspace(int64_t d_in, int32_t n_grid, size_t* bytes) {
+  if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
+  if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
+  if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
+  *bytes = duo_cand_ws(d_in, n_grid);
+  return ok();
+}
+
+awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, int64_t d_in, int32_t n_grid,
+                                    double s_min, float* S, void* ws, size_t ws_bytes, void* stream) {
+  if (!x_mean || !w_mean || !S) return fail(AWQ_EINVAL, "x_mean / w_mean / S is NULL");
+  if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
+  if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
+  if (!(s_min > 0.0 && isfinite(s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
+  const size_t need = duo_cand_ws(d_in, n_grid);
+  if (!ws || ws_bytes < need) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255u) return fail(AWQ_EALIGN, "ws not 256-byte aligned");
+  char* base = (char*)ws;
+  return hip_status(launch_candidates_duo(x_mean, w_mean, d_in, n_grid, s_min, (double*)base,
+                                          (double*)(base + align256((size_t)n_grid * d_in * sizeof(double))), S,
+                                          nullptr, (hipStream_t)stream),
+                    "awq_candidate_scales_duo");
+}
+
+// ---------------------------------------------------------------------------
 awq_status awq_search_workspace(const awq_search_cfg* cfg, int64_t d_out_total, int64_t d_in, int64_t T,
                                 size_t* bytes) {
   awq_status st = check_cfg(cfg);
@@ -252,7 +364,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   if (!plan.output) {
     float* C2 = (float*)(base + plan.off_C2);
     float* part = (float*)(base + plan.off_part);
-    if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, C2, s)) != hipSuccess)
+    if ((e = launch_cands(*cfg, plan, parts, d_out, d_in, x_mean, base, S, C2, s)) != hipSuccess)
       return hip_status(e, "candidates");
     mark(true, s);
     e = launch_search_weight(cfg->group_size, parts, d_out, d_in, cfg->n_grid, S, C2, part, s);
@@ -275,7 +387,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   OutScales* sc_c = (OutScales*)(base + plan.off_sc + align256(sizeof(OutScales)));
   const int G = cfg->group_size;
   const int64_t dop = plan.d_out_pad, kp = plan.K_pad;
-  if ((e = launch_candidates(x_mean, d_in, cfg->n_grid, cfg->s_min, S, nullptr, s)) != hipSuccess)
+  if ((e = launch_cands(*cfg, plan, parts, d_out, d_in, x_mean, base, S, nullptr, s)) != hipSuccess)
     return hip_status(e, "candidates");
   if ((e = launch_prepare_x(X, bf16, T, d_in, ld_x, xmax, s)) != hipSuccess) return hip_status(e, "absmax(X)");
   if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax,

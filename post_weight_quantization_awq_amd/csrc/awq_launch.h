@@ -87,4 +87,21 @@ hipError_t launch_unpack_dequant(const int32_t* qweight, const uint16_t* scales,
 hipError_t launch_norm_group_fold(const ScaleSet& S, int64_t d_in, const void* norm, int norm_dtype, void* norm_out,
                                   float* s_shared, hipStream_t stream);
 
+// out[i] = inv_count * (sum over the n_split rows of part[split][i], in
+// split order, fp64) rounded to fp32 (the statistics' final combine)
+hipError_t launch_split_mean(const double* part, int64_t n_split, int64_t d_in, double inv_count, float* out,
+                             hipStream_t stream);
+
+// Duo scaling ([cassindra] The scale search as code, duo_scaling=True).
+// w_mean of the group's rows: rmax [d_out] and part [wmean_splits(d_out)][d_in]
+// are scratch.
+int64_t wmean_splits(int64_t d_out);
+hipError_t launch_weight_channel_mean(const WParts& parts, int64_t d_out, int64_t d_in, float* rmax, double* part,
+                                      float* w_mean, hipStream_t stream);
+// duo candidate table: T [n_grid][d_in] fp64 and ext [n_grid][duo_cand_blocks][2]
+// fp64 are scratch; S [n_grid][d_in], C2 (optional) as launch_candidates
+int64_t duo_cand_blocks(int64_t d_in);
+hipError_t launch_candidates_duo(const float* x_mean, const float* w_mean, int64_t d_in, int n_grid, double s_min,
+                                 double* T, double* ext, float* S, float* C2, hipStream_t stream);
+
 }  // namespace awq

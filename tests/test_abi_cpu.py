@@ -126,7 +126,7 @@ def test_search_validation(A):
     for c in bad:
         assert st_search(A, c, grp, X=FAKE, T=16, ld=256, clip=FAKE) == A.AWQ_EINVAL
     c = A._cfg(128, 20, "weight", 0, 0.5, 1e-4)
-    c.reserved = 3
+    c.flags = 2
     assert st_search(A, c, grp) == A.AWQ_EINVAL
     assert st_search(A, good, grp, d_in=200) == A.AWQ_ESHAPE
     assert st_search(A, good, grp, d_in=64) == A.AWQ_ESHAPE
@@ -192,3 +192,30 @@ def test_norm_group_fold_validation(A):
     assert f(ssh=FAKE + 2) == A.AWQ_EALIGN
     assert f(d=0, norm=None, out=None, ssh=None) == A.AWQ_OK
     assert L.awq_last_error().decode() == ""
+
+
+def test_duo_entry_validation(A):
+    L = A.lib()
+    n = ctypes.c_size_t()
+    assert L.awq_weight_channel_mean_workspace(0, 256, ctypes.byref(n)) == A.AWQ_EINVAL
+    assert L.awq_weight_channel_mean_workspace(64, 256, ctypes.byref(n)) == A.AWQ_OK and n.value > 0
+    need = n.value
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+    rows = (ctypes.c_int64 * 1)(64)
+    grp = A.WGroup(1, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), ctypes.cast(rows, ctypes.POINTER(ctypes.c_int64)))
+    wcm = lambda d_in=256, out=FAKE, ws=FAKE, nb=need: L.awq_weight_channel_mean(ctypes.byref(grp), d_in, out, ws, nb, None)
+    assert wcm(d_in=100) == A.AWQ_ESHAPE
+    assert wcm(out=None) == A.AWQ_EINVAL
+    assert wcm(nb=need - 1) == A.AWQ_EWORKSPACE
+    assert wcm(ws=FAKE + 16) == A.AWQ_EALIGN
+    assert L.awq_weight_channel_mean(None, 256, FAKE, FAKE, need, None) == A.AWQ_EINVAL
+    assert L.awq_candidate_scales_duo_workspace(256, 65, ctypes.byref(n)) == A.AWQ_EINVAL
+    assert L.awq_candidate_scales_duo_workspace(256, 20, ctypes.byref(n)) == A.AWQ_OK and n.value > 0
+    need = n.value
+    cd = lambda x=FAKE, w=FAKE, s_min=1e-4, nb=need: L.awq_candidate_scales_duo(x, w, 256, 20, s_min, FAKE, FAKE, nb, None)
+    assert cd(w=None) == A.AWQ_EINVAL
+    assert cd(s_min=0.0) == A.AWQ_EINVAL
+    assert cd(nb=0) == A.AWQ_EWORKSPACE
+    # the duo flag enlarges the search workspace by the weight statistic and the fp64 table
+    plain = A.search_workspace_bytes(64, 256, 1)
+    assert A.search_workspace_bytes(64, 256, 1, duo=True) > plain
