@@ -116,7 +116,7 @@ def pack_bytes(d_out: int, d_in: int, G: int) -> int:
     return 2 * n + n // 2 + 2 * n // G + n // (2 * G) + 4 * d_in
 
 
-def cpu_baseline_weight(W, X, G, budget_s: float):
+def cpu_baseline_weight(W, X, G, budget_s: float, duo: bool = False):
     """Times the CPU oracle on the same group: statistics over all tokens, then
     search (20 points) + pack on consecutive row chunks until the time budget
     or the rows run out; the step time is scaled to all rows."""
@@ -129,7 +129,7 @@ def cpu_baseline_weight(W, X, G, budget_s: float):
     while done < d_out and t_stats + t_rows < budget_s:
         Wr = W[done:done + chunk]
         t1 = time.perf_counter()
-        _, _, s = O.search_scales([Wr], xm, G, 20)
+        _, _, s = O.search_scales([Wr], xm, G, 20, duo=duo)
         O.quantize_pack(Wr, s, G)
         t_rows += time.perf_counter() - t1
         done += Wr.shape[0]
@@ -169,7 +169,7 @@ def bench_weight(args, wl_name: str):
     # preallocated outputs and workspaces: the timed step allocates nothing
     xm = torch.empty(d_in, dtype=torch.float32, device=dev)
     ws_stats = A.workspace(A.act_stats_workspace_bytes(T, d_in), dev)
-    ws_search = A.workspace(A.search_workspace_bytes(d_out, d_in, 1, group_size=G), dev)
+    ws_search = A.workspace(A.search_workspace_bytes(d_out, d_in, 1, group_size=G, duo=args.duo), dev)
     res = A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                          torch.empty(d_in, device=dev), None, None)
     packs = [(torch.empty((d_in, p.shape[0] // 8), dtype=torch.int32, device=dev),
@@ -179,7 +179,7 @@ def bench_weight(args, wl_name: str):
     ev = HipEvents(6 * K)
 
     stats_plan = A.ActStatsPlan(X, x_mean=xm, ws=ws_stats)
-    search_plan = A.SearchPlan(Ws, xm, group_size=G, ws=ws_search, out=res)
+    search_plan = A.SearchPlan(Ws, xm, group_size=G, ws=ws_search, out=res, duo=args.duo)
     pack_plans = [A.PackPlan(p, G, res.best_s, out=o) for p, o in zip(Ws, packs)]
 
     def step(i: int = -1):
@@ -231,7 +231,7 @@ def bench_weight(args, wl_name: str):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl_name, "d_out": d_out, "d_in": d_in, "tokens": T, "group_size": G,
-                   "n_grid": 20, "score": "weight", "x_dtype": grp.x_dtype},
+                   "n_grid": 20, "score": "weight", "x_dtype": grp.x_dtype, "duo": args.duo},
         "search_elem_pts_per_s": elem_pts / t_search,
         "search_hbm_equiv_GBps": 2.0 * elem_pts / t_search / 1e9,
         "pack_GBps": pk_bytes / (k_ms["quantize_pack"] * 1e-3) / 1e9,
@@ -244,7 +244,7 @@ def bench_weight(args, wl_name: str):
                      "ops_per_elem_pt": SEARCH_OPS_PER_ELEM_PT},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_weight(W_h, X_h, G, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_weight(W_h, X_h, G, args.cpu_seconds, args.duo)
     return out
 
 
@@ -273,7 +273,7 @@ def bench_output(args, wl_name: str):
         xm = torch.empty(grp.d_in, dtype=torch.float32, device=dev)
         ws_stats = A.workspace(A.act_stats_workspace_bytes(X.shape[0], grp.d_in), dev)
         ws = A.workspace(A.search_workspace_bytes(d_out, grp.d_in, X.shape[0], group_size=G, score="output",
-                                                  n_clip=wl.n_clip), dev)
+                                                  n_clip=wl.n_clip, duo=args.duo), dev)
         res = A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                              torch.empty(grp.d_in, device=dev),
                              torch.empty(d_out, device=dev) if wl.n_clip else None, None)
@@ -281,7 +281,8 @@ def bench_output(args, wl_name: str):
                   torch.empty((grp.d_in // G, p.shape[0]), dtype=torch.float16, device=dev),
                   torch.empty((grp.d_in // G, p.shape[0] // 8), dtype=torch.int32, device=dev)) for p in parts]
         sp = A.ActStatsPlan(X, x_mean=xm, ws=ws_stats)
-        qp = A.SearchPlan(parts, xm, group_size=G, score="output", X=X, n_clip=wl.n_clip, ws=ws, out=res)
+        qp = A.SearchPlan(parts, xm, group_size=G, score="output", X=X, n_clip=wl.n_clip, ws=ws, out=res,
+                          duo=args.duo)
         pps, off = [], 0
         for p, o in zip(parts, packs):
             clip = res.clip[off:off + p.shape[0]] if res.clip is not None else None
@@ -330,7 +331,7 @@ def bench_output(args, wl_name: str):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16-mfma/f32", "data": "synthetic",
         "config": {"workload": wl_name, "groups": [[g.name, g.d_out, g.d_in, X.shape[0]] for _, X, g, *_ in plans],
-                   "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip},
+                   "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip, "duo": args.duo},
         "step_TFLOPs_algorithmic": total_flops / (ms_step * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -358,7 +359,8 @@ def bench_sweep(args):
     for G in wl.group_sizes:
         xms = [torch.empty(g.d_in, device=dev) for g in wl.groups]
         ws_stats = [A.workspace(A.act_stats_workspace_bytes(g.T, g.d_in), dev) for g in wl.groups]
-        ws = [A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G), dev) for g in wl.groups]
+        ws = [A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G, duo=args.duo), dev)
+              for g in wl.groups]
         res = [A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                               torch.empty(g.d_in, device=dev), None, None) for g in wl.groups]
         packs = [[(torch.empty((g.d_in, r // 8), dtype=torch.int32, device=dev),
@@ -378,7 +380,8 @@ def bench_sweep(args):
 
         def plans(stream_of):
             st = [A.ActStatsPlan(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi], stream=stream_of(gi)) for gi in range(ng)]
-            se = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi], stream=stream_of(gi))
+            se = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi], stream=stream_of(gi),
+                                 duo=args.duo)
                    for gi in range(ng)] for b in range(blocks)]
             pk = [[[A.PackPlan(p, G, res[gi].best_s, out=o, stream=stream_of(gi)) for p, o in zip(Ws[b][gi], packs[gi])]
                    for gi in range(ng)] for b in range(blocks)]
@@ -453,7 +456,8 @@ def bench_sweep(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": first["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "qwen3_8b_sweep", "blocks": blocks, "weights": n_w, "n_grid": 20,
-                   "group_sizes": list(wl.group_sizes), "score": "weight", "streams": args.streams},
+                   "group_sizes": list(wl.group_sizes), "score": "weight", "streams": args.streams,
+                   "duo": args.duo},
         "per_group_size": out_all,
         "roofline": {"bound": "alu", "achieved": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T,
                      "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s", "frac": first["search_alu_frac"],
@@ -620,6 +624,8 @@ def main() -> int:
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
     ap.add_argument("--streams", type=int, default=4,
                     help="streams the sweep's group kinds are spread over in the timed steps")
+    ap.add_argument("--duo", action="store_true",
+                    help="duo-scaling candidates (x_mean^r / (w_mean^(1-r) + 1e-4)) in the search workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()

@@ -21,23 +21,45 @@ constexpr int kDuoCols = 64 * 8;    // channels per column block (8 per lane)
 constexpr int kDuoSplitRows = 64;   // rows per split (16 per wave)
 
 // one wave per row: the largest |w| of the row (fp16 magnitudes order like
-// their bit patterns with the sign cleared; weights are finite)
+// their bit patterns with the sign cleared; weights are finite).  A lane's
+// loads of a stretch of 8 chunks are all issued before the first max.
 __global__ __launch_bounds__(kDuoThreads) void row_absmax_kernel(const WParts P, int64_t d_out, int64_t d_in,
                                                                  float* __restrict__ rmax) {
+  constexpr int kU = 8;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kDuoThreads / kWave) + (threadIdx.x >> 6);
   if (row >= d_out) return;  // uniform over the wave
   const uint4* p = (const uint4*)row_ptr(P, row, d_in);
+  const int n = (int)(d_in / 8);
   uint32_t m = 0;
-  for (int64_t c = lane; c < d_in / 8; c += kWave) {
-    const uint4 u = p[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int c0 = 0; c0 < n; c0 += kU * kWave) {
+    uint4 u[kU];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    for (int j = 0; j < kU; ++j) {
+      const int c = c0 + j * kWave + lane;
+      u[j] = c < n ? p[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+    }
   }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, kWave));
   if (lane == 0) rmax[row] = h2f((uint16_t)m);
+}
+
+// IEEE fp32 quotient a / b of fp16 magnitudes 0 <= a <= b, b > 0, given y
+// within one ulp of 1/b: q0 = a*y, the residual a - q0*b is exact in one FMA
+// (b has 11 significant bits), and one correction step rounds to the IEEE
+// quotient.  Checked on the host for every such pair of finite fp16 values
+// and each of the three y (RN(1/b) and its two neighbours).
+__device__ __forceinline__ float div_f16_mag(float a, float b, float y) {
+  const float q0 = a * y;
+  const float r = __builtin_fmaf(-q0, b, a);
+  return __builtin_fmaf(r, y, q0);
 }
 
 // split y, column block x: sum over the split's rows of |w| / rowmax for 8
@@ -66,11 +88,12 @@ __global__ __launch_bounds__(kDuoThreads) void wmean_partial_kernel(const WParts
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const bool use = r0 + 4 * i < d_out && m[i] > 0.0f;
+      const float y = __builtin_amdgcn_rcpf(m[i]);  // v_rcp_f32: within 1 ulp
       const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float lo = h2f((uint16_t)(w[j] & 0x7FFFu)) / m[i];
-        const float hi = h2f((uint16_t)((w[j] >> 16) & 0x7FFFu)) / m[i];
+        const float lo = div_f16_mag(h2f((uint16_t)(w[j] & 0x7FFFu)), m[i], y);
+        const float hi = div_f16_mag(h2f((uint16_t)((w[j] >> 16) & 0x7FFFu)), m[i], y);
         acc[2 * j] += use ? (double)lo : 0.0;
         acc[2 * j + 1] += use ? (double)hi : 0.0;
       }
