@@ -56,6 +56,13 @@ Duo scaling: w_mean is the mean over the group's rows of |w| / rowmax|w|
 (quotients in fp32, sums in fp64, all-zero rows contributing 0), and
 t = max(x^r / (w_mean^(1-r) + 1e-4), 1e-4) before the same normalisation.
 
+Asymmetric INT4: per group and output row the range [lo, hi] = [min(0, min v),
+max(0, max v)], step = RN(RN(hi - lo) / 15), zero point z = clamp(rint(RN(-lo /
+step)), 0, 15), code u = clamp(rint(RN(v / step)) + z, 0, 15), reconstruction
+(u - z) * step; an all-zero group has step 0, z = 0, u = 0.  A clip ratio c
+shrinks both ends (RN(c lo), RN(c hi)).  qzeros hold z in the qweight nibble
+order.
+
 Norm-group export: the shared scale is the per-channel geometric mean of the
 member scales, evaluated as exp(mean(ln s)) in fp64 and rounded once to fp32;
 the folded norm is the IEEE fp32 quotient rounded once to the norm's dtype.
@@ -75,6 +82,7 @@ F32 = np.float32
 F64 = np.float64
 
 QMAX = 7                      # symmetric signed grid [-7, 7] ([konic] Group-wise symmetric INT4)
+UMAX = 15                     # asymmetric unsigned grid [0, 15] ([cassindra] 4-bit zero point, step ~ range / 15)
 ZERO_POINT = 7                # u = q + 7 ([konic] exporter step 4)
 PACK_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)   # [konic] AutoAWQ / HF-AWQ GEMM on-disk format
 S_MIN = 1e-4                  # [cassindra] clamp(min=1e-4)
@@ -230,11 +238,74 @@ def fake_quant(W: np.ndarray, s: Optional[np.ndarray], group_size: int,
 
 
 # ---------------------------------------------------------------------------
+# O3a: group-wise asymmetric INT4 ([cassindra] "Why it works" worked example:
+#      values up to 0.5 in a group give a step of about 1/15 and a worst
+#      rounding error of about half that; "Quantization, storage and packing":
+#      one 16-bit scale and one 4-bit zero point per group and output channel,
+#      4 + (16 + 4) / 128 bits per weight; "The recipe": W4A16_ASYM)
+# ---------------------------------------------------------------------------
+def group_quantize_asym(W: np.ndarray, s: Optional[np.ndarray], group_size: int,
+                        clip: Optional[np.ndarray] = None):
+    """Asymmetric quantization of v = RN(w * s) group-wise along the input axis.
+
+    The range of a group is [lo, hi] = [min(0, min v), max(0, max v)] (zero
+    inside, so it is representable and z is an integer code), optionally
+    shrunk by the row's clip ratio c to [RN(c lo), RN(c hi)];
+    step = RN(RN(hi - lo) / 15); z = clamp(rint(RN(-lo / step)), 0, 15);
+    u = clamp(rint(RN(v / step)) + z, 0, 15).  An all-zero group has step 0,
+    z = 0 and u = 0.
+    Returns (u uint8 [d_out, d_in], z uint8 [d_out, d_in/G], step fp32 [d_out, d_in/G], v fp32).
+    """
+    Wf = np.asarray(W).astype(F32)
+    d_out, d_in = Wf.shape
+    assert d_in % group_size == 0
+    n_groups = d_in // group_size
+    v = Wf if s is None else (Wf * s.astype(F32)[None, :]).astype(F32)
+    vg = v.reshape(d_out, n_groups, group_size)
+    hi = np.maximum(vg.max(axis=2), F32(0))                          # exact
+    lo = np.minimum(vg.min(axis=2), F32(0))
+    if clip is not None:
+        c = clip.astype(F32)[:, None]
+        hi, lo = (c * hi).astype(F32), (c * lo).astype(F32)          # RN(c hi), RN(c lo)
+    step = ((hi - lo).astype(F32) / F32(UMAX)).astype(F32)          # RN(RN(hi - lo) / 15)
+    live = step > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        zr = (-lo / step).astype(F32)                                # RN(-lo / step)
+        ratio = (vg / step[:, :, None]).astype(F32)                  # RN(v / step)
+    z = np.where(live, np.clip(np.rint(zr), 0, UMAX), 0).astype(np.int16)
+    n = np.where(live[:, :, None], np.rint(ratio), 0).astype(np.int64)
+    u = np.clip(n + z[:, :, None], 0, UMAX).astype(np.uint8)
+    return u.reshape(d_out, d_in), z.astype(np.uint8), step, v
+
+
+def dequantize_asym(u: np.ndarray, z: np.ndarray, step: np.ndarray, s: Optional[np.ndarray],
+                    group_size: int) -> np.ndarray:
+    """w_hat = RN(RN((u - z) * step) / s) in fp32."""
+    d_out, d_in = u.shape
+    qs = u.astype(np.int16).reshape(d_out, -1, group_size) - z.astype(np.int16)[:, :, None]
+    r = (qs.astype(F32) * step[:, :, None]).astype(F32).reshape(d_out, d_in)
+    if s is None:
+        return r
+    return (r / s.astype(F32)[None, :]).astype(F32)
+
+
+def fake_quant_asym(W: np.ndarray, s: Optional[np.ndarray], group_size: int,
+                    clip: Optional[np.ndarray] = None) -> np.ndarray:
+    u, z, step, _ = group_quantize_asym(W, s, group_size, clip)
+    return dequantize_asym(u, z, step, s, group_size)
+
+
+def _fq(W, s, group_size, clip=None, asym=False):
+    return fake_quant_asym(W, s, group_size, clip) if asym else fake_quant(W, s, group_size, clip)
+
+
+# ---------------------------------------------------------------------------
 # O4w: activation-weighted reconstruction error ([konic] AWQ scaling:
 #      || (W - Q(W s)/s) diag(x) ||^2)
 # ---------------------------------------------------------------------------
-def weight_error(W: np.ndarray, s: np.ndarray, x_mean: np.ndarray, group_size: int) -> float:
-    w_hat = fake_quant(W, s, group_size)
+def weight_error(W: np.ndarray, s: np.ndarray, x_mean: np.ndarray, group_size: int,
+                 asym: bool = False) -> float:
+    w_hat = _fq(W, s, group_size, None, asym)
     d = (np.asarray(W).astype(F64) - w_hat.astype(F64)) * x_mean.astype(F64)[None, :]
     return float(np.sum(d * d))
 
@@ -245,17 +316,17 @@ def weight_error(W: np.ndarray, s: np.ndarray, x_mean: np.ndarray, group_size: i
 #      output error is X (W - W_hat))
 # ---------------------------------------------------------------------------
 def output_error_rows(W: np.ndarray, s: Optional[np.ndarray], X: np.ndarray, group_size: int,
-                      clip: Optional[np.ndarray] = None) -> np.ndarray:
+                      clip: Optional[np.ndarray] = None, asym: bool = False) -> np.ndarray:
     """Per output row o: sum_t (sum_i X[t,i] (w_hat[o,i] - W[o,i]))^2, fp64."""
     Xd = decode_activations(X)
-    w_hat = fake_quant(W, s, group_size, clip)
+    w_hat = _fq(W, s, group_size, clip, asym)
     D = w_hat.astype(F64) - np.asarray(W).astype(F64)              # [d_out, d_in]
     Y = Xd @ D.T                                                    # [T, d_out]
     return np.sum(Y * Y, axis=0)
 
 
-def output_error(W: np.ndarray, s: np.ndarray, X: np.ndarray, group_size: int) -> float:
-    rows = output_error_rows(W, s, X, group_size)
+def output_error(W: np.ndarray, s: np.ndarray, X: np.ndarray, group_size: int, asym: bool = False) -> float:
+    rows = output_error_rows(W, s, X, group_size, None, asym) if asym else output_error_rows(W, s, X, group_size)
     T = X.shape[0]
     return float(rows.sum() / (T * np.asarray(W).shape[0]))
 
@@ -275,21 +346,24 @@ def first_argmin(errors: Sequence[float]) -> int:
 
 def search_scales(W_parts: Sequence[np.ndarray], x_mean: np.ndarray, group_size: int,
                   n_grid: int = 20, score: str = "weight", X: Optional[np.ndarray] = None,
-                  s_min: float = S_MIN, duo: bool = False):
+                  s_min: float = S_MIN, duo: bool = False, asym: bool = False):
     """Returns (errors [n_grid] fp64, best index, best s fp32 [d_in]).
 
     The linears of one input-sharing group are scored together, their rows
     concatenated ([cassindra] torch.cat of the group's weights); duo = True
-    takes the duo-scaling candidates of those rows.
+    takes the duo-scaling candidates of those rows; asym = True scores the
+    asymmetric quantizer (O3a).
     """
     W = np.concatenate([np.asarray(w) for w in W_parts], axis=0)
     S = candidate_scales(x_mean, n_grid, s_min, weight_channel_mean(W_parts) if duo else None)
     errs = []
     for k in range(n_grid):
         if score == "weight":
-            errs.append(weight_error(W, S[k], x_mean, group_size))
+            errs.append(weight_error(W, S[k], x_mean, group_size, asym=True) if asym
+                        else weight_error(W, S[k], x_mean, group_size))
         elif score == "output":
-            errs.append(output_error(W, S[k], X, group_size))
+            errs.append(output_error(W, S[k], X, group_size, asym=True) if asym
+                        else output_error(W, S[k], X, group_size))
         else:
             raise ValueError(score)
     k_best = first_argmin(errs)
@@ -308,14 +382,15 @@ def clip_ratios(n_clip: int, clip_lo: float = 0.5) -> np.ndarray:
 
 
 def clip_search(W: np.ndarray, s: np.ndarray, X: np.ndarray, group_size: int,
-                n_clip: int = 20, clip_lo: float = 0.5):
+                n_clip: int = 20, clip_lo: float = 0.5, asym: bool = False):
     """Returns (E [d_out, n_clip] fp64, chosen ratio [d_out] fp32)."""
     Wa = np.asarray(W)
     ratios = clip_ratios(n_clip, clip_lo)
     E = np.zeros((Wa.shape[0], n_clip), dtype=F64)
     for j, c in enumerate(ratios):
         clip = np.full(Wa.shape[0], c, dtype=F32)
-        E[:, j] = output_error_rows(Wa, s, X, group_size, clip)
+        E[:, j] = output_error_rows(Wa, s, X, group_size, clip, asym) if asym \
+            else output_error_rows(Wa, s, X, group_size, clip)
     best = np.array([first_argmin(E[o]) for o in range(Wa.shape[0])])
     return E, ratios[best]
 
@@ -368,6 +443,19 @@ def quantize_pack(W: np.ndarray, s: Optional[np.ndarray], group_size: int,
         zword |= np.uint32(ZERO_POINT) << np.uint32(4 * j)
     qzeros = np.full((step.shape[1], d_out // 8), zword, dtype=np.uint32)
     return qweight, scales, qzeros, q, step
+
+
+def quantize_pack_asym(W: np.ndarray, s: Optional[np.ndarray], group_size: int,
+                       clip: Optional[np.ndarray] = None):
+    """Asymmetric codes (O3a) in the same layout: qweight nibbles hold u,
+    scales fp16(step), and qzeros [d_in/G, d_out/8] hold z in the qweight
+    nibble order (word (g, m), nibble j: row 8m + PACK_ORDER[j]).
+    Returns (qweight, scales, qzeros, u [d_out, d_in], z [d_out, d_in/G], step)."""
+    u, z, step, _ = group_quantize_asym(W, s, group_size, clip)
+    qweight = pack_codes(u)
+    scales = f32_to_f16(step.T)
+    qzeros = pack_codes(z)                                           # [d_in/G, d_out/8]
+    return qweight, scales, qzeros, u, z, step
 
 
 # ---------------------------------------------------------------------------

@@ -188,6 +188,42 @@ def _duo(x_mean, w_mean, alpha, s_min=O.S_MIN, swap=False, eps_outside=False):
     return (t / np.sqrt(t.max() * t.min())).astype(F32)
 
 
+def _gqa(W, s, G, clip=None, div=15.0, zround=np.rint, zsign=1.0, with_zero=True, umax=15):
+    Wf = np.asarray(W).astype(F32)
+    d_out, d_in = Wf.shape
+    v = Wf if s is None else (Wf * s.astype(F32)[None, :]).astype(F32)
+    vg = v.reshape(d_out, d_in // G, G)
+    hi, lo = vg.max(axis=2), vg.min(axis=2)
+    if with_zero:
+        hi, lo = np.maximum(hi, F32(0)), np.minimum(lo, F32(0))
+    if clip is not None:
+        c = clip.astype(F32)[:, None]
+        hi, lo = (c * hi).astype(F32), (c * lo).astype(F32)
+    step = ((hi - lo).astype(F32) / F32(div)).astype(F32)
+    live = step > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        zr = (F32(-zsign) * lo / step).astype(F32)
+        ratio = (vg / step[:, :, None]).astype(F32)
+    z = np.where(live, np.clip(zround(zr), 0, 15), 0).astype(np.int16)
+    n = np.where(live[:, :, None], np.rint(ratio), 0).astype(np.int64)
+    u = np.clip(n + z[:, :, None], 0, umax).astype(np.uint8)
+    return u.reshape(d_out, d_in), z.astype(np.uint8), step, v
+
+
+def _deq_asym_no_zero(u, z, step, s, G):
+    d_out, d_in = u.shape
+    r = (u.astype(F32).reshape(d_out, -1, G) * step[:, :, None]).astype(F32).reshape(d_out, d_in)
+    return r if s is None else (r / s.astype(F32)[None, :]).astype(F32)
+
+
+def _pack_asym_zeros_row_order(W, s, G, clip=None):
+    u, z, step, _ = O.group_quantize_asym(W, s, G, clip)
+    qz = np.zeros((z.shape[1], z.shape[0] // 8), dtype=np.uint32)
+    for j in range(8):
+        qz |= z[j::8, :].astype(np.uint32).T << np.uint32(4 * j)
+    return O.pack_codes(u), O.f32_to_f16(step.T), qz, u, z, step
+
+
 MUTANTS = {
     "act_stats: signed mean": [("act_stats", _act_stats_signed)],
     "act_stats: max |x|": [("act_stats", _act_stats_max)],
@@ -227,6 +263,16 @@ MUTANTS = {
     "export: logarithms in fp32": [("shared_scale", _shared_f32)],
     "export: norm multiplied by s": [("fold_norm", _fold_multiply)],
     "export: bf16 by truncation": [("f32_to_bf16_bits", _bf16_truncate)],
+    "asym: step = range / 16": [("group_quantize_asym", lambda W, s, G, clip=None: _gqa(W, s, G, clip, div=16.0))],
+    "asym: zero point rounded down": [("group_quantize_asym", lambda W, s, G, clip=None: _gqa(W, s, G, clip,
+                                                                                          zround=np.floor))],
+    "asym: zero point with the wrong sign": [("group_quantize_asym",
+                                              lambda W, s, G, clip=None: _gqa(W, s, G, clip, zsign=-1.0))],
+    "asym: range need not contain zero": [("group_quantize_asym",
+                                           lambda W, s, G, clip=None: _gqa(W, s, G, clip, with_zero=False))],
+    "asym: codes clamped to [0, 14]": [("group_quantize_asym", lambda W, s, G, clip=None: _gqa(W, s, G, clip, umax=14))],
+    "asym: dequant ignores the zero point": [("dequantize_asym", _deq_asym_no_zero)],
+    "asym: qzeros in row order": [("quantize_pack_asym", _pack_asym_zeros_row_order)],
     "export: o/down with the shared scale": [("export_rtn", lambda W, G: O.quantize_pack(W, np.full(W.shape[1], 2.0, F32), G))],
 }
 

@@ -539,3 +539,129 @@ class TestDuoScaling:
         s0 = O.candidate_scale_duo(xm, wm, 0.0).astype(F64)
         r = s0 * (wm.astype(F64) + 1e-4)
         assert np.allclose(r, r[0], rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# asymmetric INT4 ("AWQ architecture, in depth": the worked example in "Why it
+# works" -- values up to 0.5 give a step of about 1/15 and a worst rounding
+# error of about 0.033 -- and "Quantization, storage and packing": one 16-bit
+# scale and one 4-bit zero point per group and output channel, about 4.16
+# bits per weight)
+# ---------------------------------------------------------------------------
+class TestAsymmetricInt4:
+    def test_worked_example_step_and_error(self):
+        rng = np.random.default_rng(11)
+        w = rng.uniform(-0.5, 0.5, 128).astype(F32)
+        w[3], w[77] = -0.5, 0.5
+        w[5] = 0.2                               # the channel scaled by 2 stays inside the range
+        W = w[None, :]
+        u, z, step, _ = O.group_quantize_asym(W, None, 128)
+        assert step[0, 0] == F32(1.0) / F32(15)  # range 1 over 15 steps
+        assert round(float(step[0, 0]), 3) == 0.067
+        err = np.abs(O.fake_quant_asym(W, None, 128) - W)
+        half = float(step[0, 0]) / 2
+        assert err.max() <= half * (1 + 2 ** -20) and round(half, 3) == 0.033
+        # activation 20 on that channel: 20 x 0.033 = 0.67 per output at worst;
+        # scaling the weight by 2 (and the activation by 1/2) halves it
+        assert round(20 * half, 2) == 0.67
+        s = np.ones(128, F32)
+        s[5] = 2.0
+        u2, z2, step2, _ = O.group_quantize_asym(W, s, 128)
+        assert step2[0, 0] == step[0, 0] and z2[0, 0] == z[0, 0]
+        e5 = abs(float(O.fake_quant_asym(W, s, 128)[0, 5]) - 0.2)
+        assert e5 <= half / 2 * (1 + 2 ** -20) and round(20 * half / 2, 2) == 0.33
+
+    def test_grid_values_reconstruct_exactly(self):
+        rng = np.random.default_rng(12)
+        d = 2.0 ** -7
+        for zz in range(16):
+            k = np.concatenate([np.arange(16), rng.integers(0, 16, 16)])
+            rng.shuffle(k)
+            vals = ((k - zz) * d).astype(F32)[None, :]
+            u, z, step, _ = O.group_quantize_asym(vals, None, 32)
+            assert step[0, 0] == F32(d) and int(z[0, 0]) == zz
+            assert np.array_equal(u[0].astype(np.int64), k)
+            assert np.array_equal(O.fake_quant_asym(vals, None, 32), vals)
+
+    def test_codes_are_nearest_level(self):
+        rng = np.random.default_rng(13)
+        W = (rng.standard_normal((24, 64)) * 0.05).astype(np.float16)
+        W[3] = np.abs(W[3])                      # one-signed rows
+        W[4] = -np.abs(W[4])
+        W[5, :32] += np.float16(0.08)            # off-centre group
+        s = np.exp(rng.standard_normal(64) * 0.4).astype(F32)
+        u, z, step, v = O.group_quantize_asym(W, s, 32)
+        for o in range(W.shape[0]):
+            for g in range(2):
+                st = float(step[o, g])
+                vg = v[o, 32 * g:32 * (g + 1)].astype(F64)
+                lo, hi = min(0.0, vg.min()), max(0.0, vg.max())
+                assert abs(-lo / st - int(z[o, g])) <= 0.5 + 1e-6
+                levels = (np.arange(16) - int(z[o, g])) * st
+                dist = np.abs(vg[:, None] - levels[None, :])
+                chosen = dist[np.arange(32), u[o, 32 * g:32 * (g + 1)].astype(np.int64)]
+                assert np.all(chosen <= dist.min(axis=1) + 1e-6 * st)
+                # the integer zero point shifts the grid by at most half a step
+                assert levels[0] <= lo + (0.5 + 1e-6) * st and levels[15] >= hi - (0.5 + 1e-6) * st
+
+    def test_one_signed_and_degenerate_groups(self):
+        rng = np.random.default_rng(14)
+        pos = rng.uniform(0.01, 0.3, 32).astype(F32)
+        W = np.stack([pos, -pos, np.zeros(32, F32), np.full(32, 0.3, F32)])
+        u, z, step, _ = O.group_quantize_asym(W, None, 32)
+        assert int(z[0, 0]) == 0 and u[0].max() == 15 and u[0][np.argmax(pos)] == 15
+        assert int(z[1, 0]) == 15 and u[1].min() == 0 and u[1][np.argmax(pos)] == 0
+        assert step[2, 0] == 0 and int(z[2, 0]) == 0 and not u[2].any()
+        assert int(z[3, 0]) == 0 and np.all(u[3] == 15)
+        w_hat = O.fake_quant_asym(W, None, 32)
+        assert not w_hat[2].any()
+        assert np.all(w_hat[3] == F32(15) * (F32(0.3) / F32(15)))
+        assert ulps32(w_hat[3], W[3]) <= 1
+
+    def test_pack_zero_points_and_roundtrip(self):
+        W = WL.make_weight(71, 64, 256)
+        s = (np.exp(np.random.default_rng(1).standard_normal(256) * 0.3)).astype(F32)
+        qw, sc, qz, u, z, step = O.quantize_pack_asym(W, s, 128)
+        assert qw.shape == (256, 8) and sc.shape == (2, 64) and qz.shape == (2, 8)
+        assert np.array_equal(O.unpack_codes(qw, 64), u)
+        assert np.array_equal(O.unpack_codes(qz, 64), z)
+        # qzeros use the qweight nibble order: zero point = row mod 8 gives the golden word
+        zz = np.tile((np.arange(16) % 8).astype(np.uint8)[:, None], (1, 2))
+        assert np.all(O.pack_codes(zz) == np.uint32(int(load("pack_order.json")["word_when_code_equals_row_mod_8"], 16)))
+        deq = O.unpack_dequant(qw, sc, qz, 64, 128)
+        ref = ((u.astype(np.int16) - np.repeat(z.astype(np.int16), 128, axis=1)).astype(F32)
+               * np.repeat(step.astype(np.float16).astype(F32), 128, axis=1)).astype(F32)
+        assert np.array_equal(deq, ref)
+
+    def test_storage_bits_from_packed_sizes(self):
+        W = WL.make_weight(72, 64, 1024)
+        qw, sc, qz, *_ = O.quantize_pack_asym(W, None, 128)
+        bits = 8 * (qw.nbytes + sc.nbytes + qz.nbytes) / W.size
+        assert bits == 4 + (16 + 4) / 128 and round(bits, 2) == 4.16
+
+    def test_search_asym_alpha_zero_is_rtn(self):
+        W = WL.make_weight(73, 48, 256)
+        X = WL.make_activations(74, 40, 256, "bf16")
+        xm = O.act_stats(X)
+        errs, k, s = O.search_scales([W], xm, 128, 20, asym=True)
+        w_rtn = O.fake_quant_asym(W, None, 128)
+        d = (W.astype(F64) - w_rtn.astype(F64)) * xm.astype(F64)[None, :]
+        assert errs[0] == np.sum(d * d)
+        assert errs[k] <= errs[0] and k == O.first_argmin(errs)
+        eo, ko, _ = O.search_scales([W], xm, 128, 20, "output", X=X, asym=True)
+        Y = O.decode_activations(X) @ (w_rtn.astype(F64) - W.astype(F64)).T
+        assert abs(eo[0] - np.mean(Y * Y)) <= 1e-12 * np.mean(Y * Y)
+
+    def test_clip_asym(self):
+        rng = np.random.default_rng(15)
+        d = 2.0 ** -6
+        k = rng.integers(0, 16, (4, 32))
+        k[:, 0], k[:, 1] = 0, 15
+        W = ((k - 6) * d).astype(F32)           # range [-6d, 9d], step d, z = 6
+        u1, z1, st1, _ = O.group_quantize_asym(W, None, 32, np.ones(4, F32))
+        u0, z0, st0, _ = O.group_quantize_asym(W, None, 32)
+        assert np.array_equal(u1, u0) and np.array_equal(z1, z0) and np.array_equal(st1, st0)
+        uh, zh, sth, _ = O.group_quantize_asym(W, None, 32, np.full(4, 0.5, F32))
+        assert np.all(sth == F32(d / 2)) and np.all(zh == 6)
+        # values beyond the shrunk range saturate at the end codes
+        assert np.array_equal(uh, np.clip(2 * (k - 6) + 6, 0, 15))
