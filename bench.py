@@ -46,6 +46,10 @@ VALU_LANE_OPS_PEAK_T = 256 * 4 * 32 * 2.4e9 / 1e12   # 78.64 T fp32 lane-ops/s
 # scale (mul), group max (max), v / step (mul by reciprocal), round (rndne),
 # residual v - q*step (fma), square-accumulate (fma)
 SEARCH_OPS_PER_ELEM_PT = 6
+# the asymmetric grid adds a second running extremum (max(-v), half an op with
+# the max3 pairing, plus the max of v no longer folding |.|) and the clamp of
+# the code to [-z, 15 - z] (med3): 7
+SEARCH_OPS_PER_ELEM_PT_ASYM = 7
 # HBM bytes per launch of the dominant kernels, from `rocprofv3 --pmc FETCH_SIZE`
 # and `--pmc WRITE_SIZE` runs of this script (commands and tables in
 # profiles/search_weight_q_proj_4096x4096.md and
@@ -57,19 +61,22 @@ SEARCH_OPS_PER_ELEM_PT = 6
 FETCH_CAL, WRITE_CAL = 2.0, 1.0
 PMC_TRAFFIC = {
     ("search_weight_kernel", "q_proj_4096x4096"): {
-        "fetch_kib": 16756.3, "write_kib": 640.0,
+        "fetch_kib": 16756.4, "write_kib": 640.0,
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
-        "sha256": "71df8f03ac5773c1afe4f65fedbed4389fa7c4d28b6b47f13f5f9406ace6694d"},
+        "sha256": "a50efc3064248ff2a52008c134db172bb304f7eb4089c634d900bf16206b9b13"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11797735.3, "write_kib": 30720.0,
+        "fetch_kib": 11797502.5, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "10a16ec891483e54946f7ed520cafaef1a86138a04c2cf42f08085a00623413c"},
+        "sha256": "694cb7a3b501509768c9ce468c13db421cf19ad44e50f1b2f92caf9c141469fb"},
 }
 
 
-def pmc_traffic(kernel: str, workload: str):
+def pmc_traffic(kernel: str, workload: str, args=None):
     """Calibrated HBM bytes per launch, or None (no counters for this kernel and
-    workload, or sources changed since they were taken)."""
+    workload, or sources changed since they were taken).  The counters were
+    taken on the symmetric-grid instantiation; the asymmetric one has none."""
+    if args is not None and getattr(args, "asym", False):
+        return None
     e = PMC_TRAFFIC.get((kernel, workload))
     if e is None:
         return None
@@ -116,7 +123,7 @@ def pack_bytes(d_out: int, d_in: int, G: int) -> int:
     return 2 * n + n // 2 + 2 * n // G + n // (2 * G) + 4 * d_in
 
 
-def cpu_baseline_weight(W, X, G, budget_s: float, duo: bool = False):
+def cpu_baseline_weight(W, X, G, budget_s: float, duo: bool = False, asym: bool = False):
     """Times the CPU oracle on the same group: statistics over all tokens, then
     search (20 points) + pack on consecutive row chunks until the time budget
     or the rows run out; the step time is scaled to all rows."""
@@ -129,8 +136,11 @@ def cpu_baseline_weight(W, X, G, budget_s: float, duo: bool = False):
     while done < d_out and t_stats + t_rows < budget_s:
         Wr = W[done:done + chunk]
         t1 = time.perf_counter()
-        _, _, s = O.search_scales([Wr], xm, G, 20, duo=duo)
-        O.quantize_pack(Wr, s, G)
+        _, _, s = O.search_scales([Wr], xm, G, 20, duo=duo, asym=asym)
+        if asym:
+            O.quantize_pack_asym(Wr, s, G)
+        else:
+            O.quantize_pack(Wr, s, G)
         t_rows += time.perf_counter() - t1
         done += Wr.shape[0]
     wall = time.perf_counter() - t0
@@ -169,7 +179,8 @@ def bench_weight(args, wl_name: str):
     # preallocated outputs and workspaces: the timed step allocates nothing
     xm = torch.empty(d_in, dtype=torch.float32, device=dev)
     ws_stats = A.workspace(A.act_stats_workspace_bytes(T, d_in), dev)
-    ws_search = A.workspace(A.search_workspace_bytes(d_out, d_in, 1, group_size=G, duo=args.duo), dev)
+    ws_search = A.workspace(A.search_workspace_bytes(d_out, d_in, 1, group_size=G, duo=args.duo, asym=args.asym),
+                            dev)
     res = A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                          torch.empty(d_in, device=dev), None, None)
     packs = [(torch.empty((d_in, p.shape[0] // 8), dtype=torch.int32, device=dev),
@@ -179,8 +190,8 @@ def bench_weight(args, wl_name: str):
     ev = HipEvents(6 * K)
 
     stats_plan = A.ActStatsPlan(X, x_mean=xm, ws=ws_stats)
-    search_plan = A.SearchPlan(Ws, xm, group_size=G, ws=ws_search, out=res, duo=args.duo)
-    pack_plans = [A.PackPlan(p, G, res.best_s, out=o) for p, o in zip(Ws, packs)]
+    search_plan = A.SearchPlan(Ws, xm, group_size=G, ws=ws_search, out=res, duo=args.duo, asym=args.asym)
+    pack_plans = [A.PackPlan(p, G, res.best_s, out=o, asym=args.asym) for p, o in zip(Ws, packs)]
 
     def step(i: int = -1):
         if i >= 0:
@@ -220,7 +231,8 @@ def bench_weight(args, wl_name: str):
 
     elem_pts = n_w * 20
     t_search = k_ms["search_weight"] * 1e-3
-    achieved_ops = SEARCH_OPS_PER_ELEM_PT * elem_pts / t_search / 1e12
+    ops = SEARCH_OPS_PER_ELEM_PT_ASYM if args.asym else SEARCH_OPS_PER_ELEM_PT
+    achieved_ops = ops * elem_pts / t_search / 1e12
     pk_bytes = sum(pack_bytes(p.shape[0], d_in, G) for p in Ws)
     out = {
         "metric": METRIC,
@@ -231,7 +243,8 @@ def bench_weight(args, wl_name: str):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl_name, "d_out": d_out, "d_in": d_in, "tokens": T, "group_size": G,
-                   "n_grid": 20, "score": "weight", "x_dtype": grp.x_dtype, "duo": args.duo},
+                   "n_grid": 20, "score": "weight", "x_dtype": grp.x_dtype, "duo": args.duo,
+                   "asym": args.asym},
         "search_elem_pts_per_s": elem_pts / t_search,
         "search_hbm_equiv_GBps": 2.0 * elem_pts / t_search / 1e9,
         "pack_GBps": pk_bytes / (k_ms["quantize_pack"] * 1e-3) / 1e9,
@@ -239,12 +252,12 @@ def bench_weight(args, wl_name: str):
         "kernel_us": {k: v * 1e3 for k, v in k_ms.items()},
         "roofline": {"bound": "alu", "achieved": achieved_ops, "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s",
                      "frac": achieved_ops / VALU_LANE_OPS_PEAK_T,
-                     "traffic": pmc_traffic("search_weight_kernel", wl_name),
+                     "traffic": pmc_traffic("search_weight_kernel", wl_name, args),
                      "kernel": "search_weight_kernel",
-                     "ops_per_elem_pt": SEARCH_OPS_PER_ELEM_PT},
+                     "ops_per_elem_pt": ops},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_weight(W_h, X_h, G, args.cpu_seconds, args.duo)
+        out["cpu_baseline"] = cpu_baseline_weight(W_h, X_h, G, args.cpu_seconds, args.duo, args.asym)
     return out
 
 
@@ -273,7 +286,7 @@ def bench_output(args, wl_name: str):
         xm = torch.empty(grp.d_in, dtype=torch.float32, device=dev)
         ws_stats = A.workspace(A.act_stats_workspace_bytes(X.shape[0], grp.d_in), dev)
         ws = A.workspace(A.search_workspace_bytes(d_out, grp.d_in, X.shape[0], group_size=G, score="output",
-                                                  n_clip=wl.n_clip, duo=args.duo), dev)
+                                                  n_clip=wl.n_clip, duo=args.duo, asym=args.asym), dev)
         res = A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                              torch.empty(grp.d_in, device=dev),
                              torch.empty(d_out, device=dev) if wl.n_clip else None, None)
@@ -282,11 +295,11 @@ def bench_output(args, wl_name: str):
                   torch.empty((grp.d_in // G, p.shape[0] // 8), dtype=torch.int32, device=dev)) for p in parts]
         sp = A.ActStatsPlan(X, x_mean=xm, ws=ws_stats)
         qp = A.SearchPlan(parts, xm, group_size=G, score="output", X=X, n_clip=wl.n_clip, ws=ws, out=res,
-                          duo=args.duo)
+                          duo=args.duo, asym=args.asym)
         pps, off = [], 0
         for p, o in zip(parts, packs):
             clip = res.clip[off:off + p.shape[0]] if res.clip is not None else None
-            pps.append(A.PackPlan(p, G, res.best_s, clip, out=o))
+            pps.append(A.PackPlan(p, G, res.best_s, clip, out=o, asym=args.asym))
             off += p.shape[0]
         plans.append((parts, X, grp, sp, qp, pps))
     K = args.steps
@@ -331,11 +344,12 @@ def bench_output(args, wl_name: str):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16-mfma/f32", "data": "synthetic",
         "config": {"workload": wl_name, "groups": [[g.name, g.d_out, g.d_in, X.shape[0]] for _, X, g, *_ in plans],
-                   "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip, "duo": args.duo},
+                   "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip, "duo": args.duo,
+                   "asym": args.asym},
         "step_TFLOPs_algorithmic": total_flops / (ms_step * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": pmc_traffic("gemm_sq_kernel", wl_name),
+                     "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": pmc_traffic("gemm_sq_kernel", wl_name, args),
                      "kernel": "gemm_sq_kernel"},
     }
 
@@ -359,7 +373,7 @@ def bench_sweep(args):
     for G in wl.group_sizes:
         xms = [torch.empty(g.d_in, device=dev) for g in wl.groups]
         ws_stats = [A.workspace(A.act_stats_workspace_bytes(g.T, g.d_in), dev) for g in wl.groups]
-        ws = [A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G, duo=args.duo), dev)
+        ws = [A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G, duo=args.duo, asym=args.asym), dev)
               for g in wl.groups]
         res = [A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                               torch.empty(g.d_in, device=dev), None, None) for g in wl.groups]
@@ -381,9 +395,10 @@ def bench_sweep(args):
         def plans(stream_of):
             st = [A.ActStatsPlan(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi], stream=stream_of(gi)) for gi in range(ng)]
             se = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi], stream=stream_of(gi),
-                                 duo=args.duo)
+                                 duo=args.duo, asym=args.asym)
                    for gi in range(ng)] for b in range(blocks)]
-            pk = [[[A.PackPlan(p, G, res[gi].best_s, out=o, stream=stream_of(gi)) for p, o in zip(Ws[b][gi], packs[gi])]
+            pk = [[[A.PackPlan(p, G, res[gi].best_s, out=o, stream=stream_of(gi), asym=args.asym)
+                    for p, o in zip(Ws[b][gi], packs[gi])]
                    for gi in range(ng)] for b in range(blocks)]
             return st, se, pk
 
@@ -445,7 +460,8 @@ def bench_sweep(args):
             "ms_per_step": ms_step, "elem_pts_per_s": n_w * 20 / (ms_step * 1e-3),
             "search_ms": sums[1], "search_elem_pts_per_s": n_w * 20 / (sums[1] * 1e-3),
             "search_hbm_equiv_GBps": 2.0 * n_w * 20 / (sums[1] * 1e-3) / 1e9,
-            "search_alu_frac": SEARCH_OPS_PER_ELEM_PT * n_w * 20 / (sums[1] * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T,
+            "search_alu_frac": (SEARCH_OPS_PER_ELEM_PT_ASYM if args.asym else SEARCH_OPS_PER_ELEM_PT)
+            * n_w * 20 / (sums[1] * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T,
             "pack_ms": sums[2], "pack_GBps": pk / (sums[2] * 1e-3) / 1e9,
             "act_stats_ms": sums[0], "act_stats_GBps": xb / (sums[0] * 1e-3) / 1e9,
         }
@@ -457,7 +473,7 @@ def bench_sweep(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "qwen3_8b_sweep", "blocks": blocks, "weights": n_w, "n_grid": 20,
                    "group_sizes": list(wl.group_sizes), "score": "weight", "streams": args.streams,
-                   "duo": args.duo},
+                   "duo": args.duo, "asym": args.asym},
         "per_group_size": out_all,
         "roofline": {"bound": "alu", "achieved": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T,
                      "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s", "frac": first["search_alu_frac"],
@@ -626,6 +642,8 @@ def main() -> int:
                     help="streams the sweep's group kinds are spread over in the timed steps")
     ap.add_argument("--duo", action="store_true",
                     help="duo-scaling candidates (x_mean^r / (w_mean^(1-r) + 1e-4)) in the search workloads")
+    ap.add_argument("--asym", action="store_true",
+                    help="asymmetric INT4 (zero point per group) in the search and pack of the search workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()

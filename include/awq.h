@@ -72,7 +72,7 @@ typedef struct {
   int32_t n_clip;     /* 0 = no clip search; else >= 2 ratios (output score only) */
   double s_min;       /* lower clamp of x_mean^alpha before normalising (1e-4)    */
   float clip_lo;      /* smallest clip ratio, in (0, 1]; ratios 1.0 .. clip_lo     */
-  int32_t flags;      /* AWQ_FLAG_DUO: duo-scaling candidates; other bits 0        */
+  int32_t flags;      /* AWQ_FLAG_DUO | AWQ_FLAG_ASYM; other bits 0                 */
 } awq_search_cfg;
 
 /* [cassindra] The scale search as code, duo_scaling=True: the candidates are
@@ -80,6 +80,12 @@ typedef struct {
  * normalisation), w_mean the row-normalised mean |w| of the group's rows per
  * input channel (awq_weight_channel_mean). */
 #define AWQ_FLAG_DUO 1
+
+/* [cassindra] Why it works (worked example: step about range / 15) and
+ * Quantization, storage and packing (one 16-bit scale and one 4-bit zero point
+ * per group and output channel; the recipe's W4A16_ASYM): score the
+ * asymmetric grid of awq_quantize_pack_asym instead of the symmetric one. */
+#define AWQ_FLAG_ASYM 2
 
 /* One group of linears sharing an input ([cassindra] torch.cat of the group's
  * weights): part p is an fp16 device matrix [rows[p], d_in], 16-byte aligned.
@@ -173,6 +179,10 @@ awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, in
  *   AWQ_SCORE_WEIGHT: err[k] = sum_{o,i} ((W[o,i] - w_hat[o,i]) * x_mean[i])^2
  *   AWQ_SCORE_OUTPUT: err[k] = mean_{t,o} (sum_i X[t,i] (w_hat[o,i] - W[o,i]))^2
  * best_idx = first k attaining the minimum of err; best_s = S[best_idx].
+ * With cfg->flags & AWQ_FLAG_ASYM the quantizer is awq_quantize_pack_asym's:
+ *   lo = min(0, min v), hi = max(0, max v), step = RN(RN(hi - lo) / 15),
+ *   z = clamp(rint(RN(-lo / step)), 0, 15), w_hat = (clamp(rint(v / step) + z,
+ *   0, 15) - z) * step / s; the clip ratio multiplies both lo and hi.
  * With n_clip >= 2 (output score only), afterwards per output row o and ratio
  * c_j = fp32(1 - j (1 - clip_lo) / (n_clip - 1)), j = 0..n_clip-1, the step of
  * every group of that row becomes RN(RN(c_j * a) / 7) with s = best_s, the row's
@@ -227,6 +237,29 @@ awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_w
 awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size,
                              const float* s, const float* clip,
                              int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_quantize_pack_asym -- asymmetric INT4 codes in the same layout.
+ * [cassindra] Why it works (range / 15 steps) and Quantization, storage and
+ * packing (16-bit scale and 4-bit zero point per group and output channel,
+ * about 4.16 bits per weight); [konic] AutoAWQ / HF-AWQ GEMM on-disk format
+ * for the nibble order.
+ *
+ * v = RN(W*s), per row o and group g: lo = min(0, min v), hi = max(0, max v),
+ * with clip: lo = RN(clip[o]*lo), hi = RN(clip[o]*hi);
+ * step = RN(RN(hi - lo) / 15); z = clamp(rint(RN(-lo / step)), 0, 15);
+ * u = clamp(rint(RN(v / step)) + z, 0, 15) (IEEE division, round half to
+ * even, bit-exact); step = 0 (all-zero group) gives z = 0, u = 0.
+ *   qweight[i, m]: as awq_quantize_pack, nibbles hold u
+ *   scales[g, o]:  fp16 round-to-nearest-even of step
+ *   qzeros[g, m]:  int32 [d_in/G, d_out/8], nibble j holds z of row 8m + order[j]
+ *                  (required, 4-byte aligned)
+ * awq_unpack_dequant with these qzeros gives (u - z) * fp16(step).
+ * Shapes, alignment and errors as awq_quantize_pack; qzeros NULL is AWQ_EINVAL.
+ * ------------------------------------------------------------------------- */
+awq_status awq_quantize_pack_asym(const void* W, int64_t d_out, int64_t d_in, int32_t group_size,
+                                  const float* s, const float* clip,
+                                  int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
 
 /* ---------------------------------------------------------------------------
  * awq_norm_group_fold -- shared scale of a norm group and the folded norm.

@@ -32,11 +32,12 @@ AWQ_OK, AWQ_EINVAL, AWQ_ESHAPE, AWQ_EDTYPE, AWQ_EWORKSPACE, AWQ_EALIGN, AWQ_EHIP
 AWQ_F16, AWQ_BF16, AWQ_F32 = 0, 1, 2
 AWQ_SCORE_WEIGHT, AWQ_SCORE_OUTPUT = 0, 1
 AWQ_FLAG_DUO = 1
+AWQ_FLAG_ASYM = 2
 STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_EINVAL", 2: "AWQ_ESHAPE", 3: "AWQ_EDTYPE",
                 4: "AWQ_EWORKSPACE", 5: "AWQ_EALIGN", 6: "AWQ_EHIP"}
 
 EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales_workspace", "awq_candidate_scales",
-            "awq_search_workspace", "awq_search_scales", "awq_quantize_pack",
+            "awq_search_workspace", "awq_search_scales", "awq_quantize_pack", "awq_quantize_pack_asym",
             "awq_unpack_dequant", "awq_norm_group_fold", "awq_weight_channel_mean_workspace",
             "awq_weight_channel_mean", "awq_candidate_scales_duo_workspace", "awq_candidate_scales_duo",
             "awq_last_error", "awq_abi_version", "awq_set_timing_events")
@@ -76,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "awq_search_scales": [ctypes.POINTER(SearchCfg), ctypes.POINTER(WGroup), I64, P, P, I32, I64, I64,
                               P, P, P, P, P, P, SZ, P],
         "awq_quantize_pack": [P, I64, I64, I32, P, P, P, P, P, P],
+        "awq_quantize_pack_asym": [P, I64, I64, I32, P, P, P, P, P, P],
         "awq_unpack_dequant": [P, P, P, I64, I64, I32, P, P, I32, P],
         "awq_norm_group_fold": [ctypes.POINTER(ctypes.c_void_p), I32, I64, P, I32, P, P, P],
         "awq_weight_channel_mean_workspace": [I64, I64, PSZ],
@@ -256,15 +258,16 @@ class SearchResult:
     clip_err: Optional[torch.Tensor]  # fp32 [d_out, n_clip] or None
 
 
-def _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo=False) -> SearchCfg:
+def _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo=False, asym=False) -> SearchCfg:
     sc = {"weight": AWQ_SCORE_WEIGHT, "output": AWQ_SCORE_OUTPUT}[score] if isinstance(score, str) else score
-    return SearchCfg(group_size, n_grid, sc, n_clip, s_min, clip_lo, AWQ_FLAG_DUO if duo else 0)
+    flags = (AWQ_FLAG_DUO if duo else 0) | (AWQ_FLAG_ASYM if asym else 0)
+    return SearchCfg(group_size, n_grid, sc, n_clip, s_min, clip_lo, flags)
 
 
 def search_workspace_bytes(d_out: int, d_in: int, T: int = 0, *, group_size: int = 128, n_grid: int = 20,
                            score="weight", n_clip: int = 0, clip_lo: float = 0.5, s_min: float = 1e-4,
-                           duo: bool = False) -> int:
-    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo)
+                           duo: bool = False, asym: bool = False) -> int:
+    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo, asym)
     n = ctypes.c_size_t()
     _check(lib().awq_search_workspace(ctypes.byref(cfg), d_out, d_in, T, ctypes.byref(n)))
     return n.value
@@ -278,7 +281,7 @@ class SearchPlan(_Prepared):
                  n_grid: int = 20, score="weight", X: Optional[torch.Tensor] = None, n_clip: int = 0,
                  clip_lo: float = 0.5, s_min: float = 1e-4, want_clip_err: bool = False,
                  ws: Optional[torch.Tensor] = None, out: Optional[SearchResult] = None, stream=None,
-                 duo: bool = False):
+                 duo: bool = False, asym: bool = False):
         parts: List[torch.Tensor] = list(W_parts)
         if not parts:
             raise ValueError("empty weight group")
@@ -289,7 +292,7 @@ class SearchPlan(_Prepared):
                 raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
         dev = parts[0].device
         d_out = sum(p.shape[0] for p in parts)
-        self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo)
+        self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo, asym)
         T, ld, xdt = 0, 0, AWQ_BF16
         if X is not None:
             _dev(X, "X")
@@ -330,11 +333,15 @@ def search_scales(W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, **kw) -
 
 class PackPlan(_Prepared):
     """INT4 quantize + pack of W*s: qweight int32 [d_in, d_out/8], scales fp16 [d_in/G, d_out],
-    qzeros int32 [d_in/G, d_out/8] (or None)."""
+    qzeros int32 [d_in/G, d_out/8] (or None; always written for the asymmetric grid)."""
     _fn = "awq_quantize_pack"
 
     def __init__(self, W: torch.Tensor, group_size: int = 128, s: Optional[torch.Tensor] = None,
-                 clip: Optional[torch.Tensor] = None, with_zeros: bool = True, out=None, stream=None):
+                 clip: Optional[torch.Tensor] = None, with_zeros: bool = True, out=None, stream=None,
+                 asym: bool = False):
+        if asym:
+            self._fn = "awq_quantize_pack_asym"
+            with_zeros = True
         _dev(W, "W")
         if W.dtype != torch.float16 or W.dim() != 2 or not W.is_contiguous():
             raise ValueError("W must be contiguous fp16 [d_out, d_in]")
@@ -357,9 +364,11 @@ class PackPlan(_Prepared):
 
 
 def quantize_pack(W: torch.Tensor, group_size: int = 128, s: Optional[torch.Tensor] = None,
-                  clip: Optional[torch.Tensor] = None, with_zeros: bool = True, out=None, stream=None):
-    """Returns (qweight int32 [d_in, d_out/8], scales fp16 [d_in/G, d_out], qzeros int32 [d_in/G, d_out/8])."""
-    return PackPlan(W, group_size, s, clip, with_zeros, out, stream).run()
+                  clip: Optional[torch.Tensor] = None, with_zeros: bool = True, out=None, stream=None,
+                  asym: bool = False):
+    """Returns (qweight int32 [d_in, d_out/8], scales fp16 [d_in/G, d_out], qzeros int32 [d_in/G, d_out/8]);
+    asym = True: the asymmetric grid with data zero points."""
+    return PackPlan(W, group_size, s, clip, with_zeros, out, stream, asym).run()
 
 
 def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], d_out: int,

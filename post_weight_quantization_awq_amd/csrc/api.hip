@@ -148,7 +148,8 @@ awq_status check_cfg(const awq_search_cfg* cfg) {
     if (!(cfg->clip_lo > 0.0f && cfg->clip_lo <= 1.0f)) return fail(AWQ_EINVAL, "clip_lo %g not in (0,1]", (double)cfg->clip_lo);
   }
   if (!(cfg->s_min > 0.0 && isfinite(cfg->s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
-  if (cfg->flags & ~AWQ_FLAG_DUO) return fail(AWQ_EINVAL, "flags 0x%x: unknown bits", (unsigned)cfg->flags);
+  if (cfg->flags & ~(AWQ_FLAG_DUO | AWQ_FLAG_ASYM))
+    return fail(AWQ_EINVAL, "flags 0x%x: unknown bits", (unsigned)cfg->flags);
   return AWQ_OK;
 }
 
@@ -360,6 +361,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
   float* S = (float*)(base + plan.off_S);
+  const bool asym = (cfg->flags & AWQ_FLAG_ASYM) != 0;
   hipError_t e;
   if (!plan.output) {
     float* C2 = (float*)(base + plan.off_C2);
@@ -367,7 +369,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
     if ((e = launch_cands(*cfg, plan, parts, d_out, d_in, x_mean, base, S, C2, s)) != hipSuccess)
       return hip_status(e, "candidates");
     mark(true, s);
-    e = launch_search_weight(cfg->group_size, parts, d_out, d_in, cfg->n_grid, S, C2, part, s);
+    e = launch_search_weight(cfg->group_size, asym, parts, d_out, d_in, cfg->n_grid, S, C2, part, s);
     mark(false, s);
     if (e != hipSuccess) return hip_status(e, "search_weight");
     if ((e = launch_select(part, plan.n_blocks, cfg->n_grid, 1.0, nullptr, (double*)(base + plan.off_tot), err,
@@ -390,7 +392,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   if ((e = launch_cands(*cfg, plan, parts, d_out, d_in, x_mean, base, S, nullptr, s)) != hipSuccess)
     return hip_status(e, "candidates");
   if ((e = launch_prepare_x(X, bf16, T, d_in, ld_x, xmax, s)) != hipSuccess) return hip_status(e, "absmax(X)");
-  if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax,
+  if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax,
                            nullptr, s)) != hipSuccess)
     return hip_status(e, "build_dw(max)");
   if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, cfg->n_grid, sc_a, s)) != hipSuccess)
@@ -401,7 +403,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   if (!one_chunk) mark(true, s);
   for (int c0 = 0; c0 < cfg->n_grid; c0 += plan.cand_chunk) {
     const int nc = (cfg->n_grid - c0) < plan.cand_chunk ? (cfg->n_grid - c0) : plan.cand_chunk;
-    if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, nullptr, dw, s)) !=
+    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, nullptr, dw, s)) !=
         hipSuccess)
       return hip_status(e, "build_dw");
     if (one_chunk) mark(true, s);
@@ -419,14 +421,14 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
     return hip_status(e, "select");
   if (cfg->n_clip >= 2) {
     const int nclip = cfg->n_clip;
-    if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0,
+    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0,
                              nullptr, dmax, nullptr, s)) != hipSuccess)
       return hip_status(e, "build_dw(clip max)");
     if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, nclip, sc_c, s)) != hipSuccess)
       return hip_status(e, "out_scales(clip)");
     for (int c0 = 0; c0 < nclip; c0 += plan.cand_chunk) {
       const int nc = (nclip - c0) < plan.cand_chunk ? (nclip - c0) : plan.cand_chunk;
-      if ((e = launch_build_dw(G, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0, sc_c,
+      if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0, sc_c,
                                nullptr, dw, s)) != hipSuccess)
         return hip_status(e, "build_dw(clip)");
       if ((e = launch_gemm_sq(x16, plan.T_pad, kp, dw, (int64_t)nc * dop, colpart + (int64_t)c0 * dop, plan.ldc, s)) !=
@@ -441,24 +443,39 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
 }
 
 // ---------------------------------------------------------------------------
-awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
-                             const float* clip, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
-                             void* stream) {
+static awq_status quantize_pack_impl(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, bool asym,
+                                     const float* s, const float* clip, int32_t* qweight, uint16_t* scales,
+                                     int32_t* qzeros, void* stream, const char* name) {
   if (!valid_group(group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", group_size);
   if (d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
   if (d_out % 8) return fail(AWQ_ESHAPE, "d_out %lld not a multiple of 8", (long long)d_out);
   if (d_in % group_size) return fail(AWQ_ESHAPE, "d_in %lld not a multiple of group_size %d", (long long)d_in, group_size);
   if (d_out == 0 || d_in == 0) return ok();
   if (!W || !qweight || !scales) return fail(AWQ_EINVAL, "W / qweight / scales is NULL");
+  if (asym && !qzeros) return fail(AWQ_EINVAL, "qzeros is NULL (asymmetric zero points are data)");
   if (!aligned16(W) || !aligned16(scales)) return fail(AWQ_EALIGN, "W / scales not 16-byte aligned");
   if (s && !aligned16(s)) return fail(AWQ_EALIGN, "s not 16-byte aligned");
   if (((uintptr_t)qweight & 3u) || (qzeros && ((uintptr_t)qzeros & 3u)) || (clip && ((uintptr_t)clip & 3u)))
     return fail(AWQ_EALIGN, "qweight / qzeros / clip not 4-byte aligned");
   mark(true, (hipStream_t)stream);
-  hipError_t e = launch_quantize_pack((const uint16_t*)W, d_out, d_in, group_size, s, clip, qweight, scales, qzeros,
-                                      (hipStream_t)stream);
+  hipError_t e = launch_quantize_pack((const uint16_t*)W, d_out, d_in, group_size, asym, s, clip, qweight, scales,
+                                      qzeros, (hipStream_t)stream);
   mark(false, (hipStream_t)stream);
-  return hip_status(e, "awq_quantize_pack");
+  return hip_status(e, name);
+}
+
+awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
+                             const float* clip, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+                             void* stream) {
+  return quantize_pack_impl(W, d_out, d_in, group_size, false, s, clip, qweight, scales, qzeros, stream,
+                            "awq_quantize_pack");
+}
+
+awq_status awq_quantize_pack_asym(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
+                                  const float* clip, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+                                  void* stream) {
+  return quantize_pack_impl(W, d_out, d_in, group_size, true, s, clip, qweight, scales, qzeros, stream,
+                            "awq_quantize_pack_asym");
 }
 
 awq_status awq_norm_group_fold(const float* const* s, int32_t n_members, int64_t d_in, const void* norm,

@@ -3,7 +3,11 @@
 // Quantizer conventions follow "From-Scratch AWQ INT4 Quantization on
 // Qwen3-8B", section "Group-wise symmetric INT4": the step of a group is
 // max|group| / 7 and codes are round(v / step) clamped to [-7, 7], rounding
-// half to even; the whole library decides codes in fp32.
+// half to even; the whole library decides codes in fp32.  The asymmetric
+// variant ("AWQ architecture, in depth": a 4-bit zero point per group, step
+// about range / 15) takes the range [min(0, min v), max(0, max v)], step
+// RN(range / 15), zero point z = rint(-min / step) in [0, 15] and codes
+// rint(v / step) + z clamped to [0, 15].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -116,6 +120,17 @@ __device__ __forceinline__ float div7(float a) {
   float r = __builtin_fmaf(-7.0f, q0, a);
   return __builtin_fmaf(r, z, q0);
 }
+
+// ---- exact step of the asymmetric grid: RN(a / 15) ---------------------------
+// Same sequence with RN(1/15); checked on the host against IEEE division for
+// every finite non-negative float.
+__device__ __forceinline__ float div15(float a) {
+  const float z = 1.0f / 15.0f;
+  float q0 = a * z;
+  float r = __builtin_fmaf(-15.0f, q0, a);
+  return __builtin_fmaf(r, z, q0);
+}
+constexpr int kUMax = 15;  // asymmetric codes 0..15
 
 // ---- code of v for a step (fp32, round half to even) -------------------------
 // Fast path: r0 = v * rcp(step) lies within 8e-6 of v/step for |v/step| < 32,

@@ -23,7 +23,8 @@ hipError_t launch_candidates(const float* x_mean, int64_t d_in, int n_grid, doub
 
 // weight-score search: per-block partial errors, candidate-major [n_grid, n_blocks]
 int64_t search_weight_blocks(int group_size, int64_t d_out, int64_t d_in);
-hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_out, int64_t d_in,
+// asym: the asymmetric grid (zero point per group row)
+hipError_t launch_search_weight(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
                                 int n_grid, const float* S, const float* C2, float* partials,
                                 hipStream_t stream);
 
@@ -55,9 +56,9 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 //   dw == nullptr: per-block max |dW_c| -> dmax [n_cand, build_dw_blocks(G, d_out, d_in)]
 //   dw != nullptr: dw[c - cand0] = fp16(dW_c * sc->ds[c]), [d_out_pad, K_pad] each, zero padded
 int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in);
-hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, int64_t d_in, int64_t d_out_pad,
-                           int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best, int n_clip,
-                           float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
+hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
+                           int64_t d_out_pad, int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best,
+                           int n_clip, float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
                            hipStream_t stream);
 // gemm of squares on fp16 operands: Y = X16 [T_pad, K_pad] dw^T (dw: [n_cols, K_pad]);
 // colpart[mt * ldc + n] = sum over the 256 tokens of tile mt of Y[t, n]^2
@@ -74,7 +75,8 @@ hipError_t launch_clip_select(const float* colpart, int64_t n_mt, int64_t ldc, i
                               hipStream_t stream);
 
 // quantize + pack, unpack + dequant
-hipError_t launch_quantize_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int group_size,
+// asym: unsigned codes with per-(group, row) zero points written to qzeros (required)
+hipError_t launch_quantize_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int group_size, bool asym,
                                 const float* s, const float* clip, int32_t* qweight,
                                 uint16_t* scales, int32_t* qzeros, hipStream_t stream);
 hipError_t launch_unpack_dequant(const int32_t* qweight, const uint16_t* scales,

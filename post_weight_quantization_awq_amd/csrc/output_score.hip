@@ -41,9 +41,12 @@ __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_lo) {
 
 // WRITE = false: per-block max |dW_c| -> dmax[(c - cand0) * gridDim.x + block]
 // WRITE = true:  dW16[c - cand0] = fp16(dW_c * ds[c])
+// ASYM: codes of the asymmetric grid (range [min(0, min v), max(0, max v)],
+//   both ends times the clip ratio in mode 1, step RN(range / 15), exact zero
+//   point and codes; the signed code clamp(n, -z, 15 - z) times the step)
 //   dW16 rows are d_out_pad apart per candidate and K_pad elements long; rows
 //   d_out .. d_out_pad-1 and columns d_in .. K_pad-1 are written as zeros.
-template <int G, bool WRITE>
+template <int G, bool WRITE, bool ASYM>
 __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int64_t d_out_pad, int64_t K_pad, int mode,
     const float* __restrict__ S, const float* __restrict__ s_best, int n_clip, float clip_lo, int cand0,
@@ -78,23 +81,40 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
     const float4 t = ((const float4*)(s + col))[j];
     sv[4 * j] = t.x; sv[4 * j + 1] = t.y; sv[4 * j + 2] = t.z; sv[4 * j + 3] = t.w;
   }
-  float m = 0.0f;
+  float m = 0.0f, mn = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     v[j] = w[j] * sv[j];
-    m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+    if constexpr (ASYM) {
+      m = __builtin_fmaxf(m, v[j]);
+      mn = __builtin_fmaxf(mn, -v[j]);
+    } else {
+      m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+    }
   }
   m = group_max<LPG>(m);
-  const float a = (mode == 1) ? clip_ratio(c, n_clip, clip_lo) * m : m;
-  const float step = div7(a);
+  float a = m, an = 0.0f;
+  if constexpr (ASYM) an = group_max<LPG>(mn);
+  if (mode == 1) {
+    const float cr = clip_ratio(c, n_clip, clip_lo);
+    a = cr * a;
+    an = cr * an;
+  }
+  const float step = ASYM ? div15(a + an) : div7(a);
   const float inv = __builtin_amdgcn_rcpf(step);
+  float qlo = -7.0f, qhi = 7.0f;
+  if constexpr (ASYM) {
+    const float z = step > 0.0f ? __builtin_amdgcn_fmed3f(code_exact(an, step, inv), 0.0f, (float)kUMax) : 0.0f;
+    qlo = -z;
+    qhi = (float)kUMax - z;
+  }
   const float dsc = WRITE ? sc->ds[c] : 1.0f;
   uint32_t outw[8];
   float mx = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     float n = step > 0.0f ? code_exact(v[j], step, inv) : 0.0f;
-    n = __builtin_fminf(__builtin_fmaxf(n, -7.0f), 7.0f);
+    n = __builtin_fminf(__builtin_fmaxf(n, qlo), qhi);
     // w_hat - w = (q * step - w * s) / s, formed in the scaled domain with one
     // fma and the hardware reciprocal of s: within a few fp32 ulp of
     // RN(RN(q * step) / s) - w, far below the fp16 rounding of the operand
@@ -141,23 +161,26 @@ int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in) {
   return (d_in / group_size) * ((d_out + rs - 1) / rs);
 }
 
-hipError_t launch_build_dw(int group_size, const WParts& parts, int64_t d_out, int64_t d_in, int64_t d_out_pad,
-                           int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best, int n_clip,
-                           float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
+hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
+                           int64_t d_out_pad, int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best,
+                           int n_clip, float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
                            hipStream_t stream) {
   // max pass: d_out rows; write pass: d_out_pad rows (zeros past d_out)
   dim3 grid((unsigned)build_dw_blocks(group_size, dw == nullptr ? d_out : d_out_pad, d_in), (unsigned)n_cand);
-#define AWQ_DW(G)                                                                             \
-  if (dw == nullptr) build_dw_kernel<G, false><<<grid, kDwThreads, 0, stream>>>(                \
+#define AWQ_DW2(G, A)                                                                         \
+  if (dw == nullptr) build_dw_kernel<G, false, A><<<grid, kDwThreads, 0, stream>>>(             \
       parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw); \
-  else build_dw_kernel<G, true><<<grid, kDwThreads, 0, stream>>>(                               \
+  else build_dw_kernel<G, true, A><<<grid, kDwThreads, 0, stream>>>(                            \
       parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw);
+#define AWQ_DW(G) \
+  if (asym) { AWQ_DW2(G, true) } else { AWQ_DW2(G, false) }
   switch (group_size) {
     case 32: AWQ_DW(32) break;
     case 64: AWQ_DW(64) break;
     default: AWQ_DW(128) break;
   }
 #undef AWQ_DW
+#undef AWQ_DW2
   return hipGetLastError();
 }
 

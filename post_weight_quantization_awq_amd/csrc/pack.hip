@@ -12,6 +12,13 @@
 // that falls back to the IEEE division near half-integers.  Unclipped, |v| is
 // at most the group maximum, so |rint(v / step)| <= 7 needs no clamp.
 //
+// ASYM ("AWQ architecture, in depth": a 4-bit zero point per group and output
+// channel, step about range / 15): range [min(0, min v), max(0, max v)] (both
+// ends times the clip ratio), step RN(range / 15) (exact divide by 15), zero
+// point z = clamp(rint(RN(-min / step)), 0, 15) by the IEEE division (once
+// per row), code u = clamp(rint(RN(v / step)) + z, 0, 15); qzeros carry the
+// eight rows' z in the qweight nibble order.
+//
 // HBM-bound: 2 bytes read and ~0.53 bytes written per weight.  A lane owns an
 // 8 x 8 tile (8 consecutive output rows, 8 consecutive inputs): its 8 rows at
 // one input column form exactly one qweight word, so packing happens in
@@ -48,7 +55,7 @@ struct PackShape {
 // |v/step| < 32; unclipped |v/step| <= 7, and with clipping a larger quotient
 // can only mis-round to a code that the clamp maps to +-7 either way for
 // |v/step| >= 32 (ratios >= 7/32).  Weights are expected to be finite.
-template <int G, bool HAS_S, bool HAS_CLIP>
+template <int G, bool HAS_S, bool HAS_CLIP, bool ASYM>
 __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ W, int64_t d_out, int64_t d_in, const float* __restrict__ s,
     const float* __restrict__ clip, int32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
@@ -90,21 +97,31 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) lo[j] = hi[j] = 0.0f;
   uint32_t sbits[4];
+  uint32_t zword = 0;  // ASYM: zero points of the 8 rows, nibble order of the codes
 
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const h8 hv = __builtin_bit_cast(h8, raw[r]);
     float v[8];
-    float m = 0.0f;
+    float m = 0.0f, mn = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       v[j] = HAS_S ? __builtin_fmaf((float)hv[j], sv[j], 0.0f) : (float)hv[j];
-      m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+      if constexpr (ASYM) {
+        m = __builtin_fmaxf(m, v[j]);
+        mn = __builtin_fmaxf(mn, -v[j]);
+      } else {
+        m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+      }
     }
     m = group_max_nonneg<SH::LPG>(m);
-    float a = m;
-    if constexpr (HAS_CLIP) a = cl[r] * m;
-    const float step = div7(a);
+    float a = m, an = 0.0f;
+    if constexpr (ASYM) an = group_max_nonneg<SH::LPG>(mn);
+    if constexpr (HAS_CLIP) {
+      a = cl[r] * a;
+      an = cl[r] * an;
+    }
+    const float step = ASYM ? div15(a + an) : div7(a);
     const float inv = __builtin_amdgcn_rcpf(step);
     float n[8];
     float dev = 0.0f;
@@ -121,10 +138,16 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
     }
     constexpr float kWeight[4] = {1.0f, 16.0f, 256.0f, 4096.0f};
     const float wgt = kWeight[r >> 1];
+    float zf = 0.0f;
+    if constexpr (ASYM) {
+      zf = step > 0.0f ? __builtin_amdgcn_fmed3f(__builtin_rintf(an / step), 0.0f, (float)kUMax) : 0.0f;
+      zword |= (uint32_t)zf << (4 * ((r & 1) ? 4 + (r >> 1) : (r >> 1)));
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float q = n[j];
-      if constexpr (HAS_CLIP) q = __builtin_amdgcn_fmed3f(q, -7.0f, 7.0f);
+      if constexpr (ASYM) q = __builtin_amdgcn_fmed3f(q, -zf, (float)kUMax - zf) + zf;  // u in [0, 15]
+      else if constexpr (HAS_CLIP) q = __builtin_amdgcn_fmed3f(q, -7.0f, 7.0f);
       if (r & 1) hi[j] = __builtin_fmaf(q, wgt, hi[j]);
       else lo[j] = __builtin_fmaf(q, wgt, lo[j]);
     }
@@ -138,12 +161,13 @@ __global__ __launch_bounds__(kPackThreads) void quantize_pack_kernel(
 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint32_t wlo = (uint32_t)((int32_t)lo[j] + 0x7777), whi = (uint32_t)((int32_t)hi[j] + 0x7777);
+    constexpr int32_t kOff = ASYM ? 0 : 0x7777;  // symmetric codes are q + 7
+    const uint32_t wlo = (uint32_t)((int32_t)lo[j] + kOff), whi = (uint32_t)((int32_t)hi[j] + kOff);
     wt[lg * 8 + j][m_local] = (whi << 16) | wlo;
   }
   if (valid && lg == 0) {
     *(uint4*)(scales + gcol * d_out + row0) = make_uint4(sbits[0], sbits[1], sbits[2], sbits[3]);
-    if (qzeros != nullptr) qzeros[gcol * (d_out / 8) + row0 / 8] = 0x77777777;
+    if (qzeros != nullptr) qzeros[gcol * (d_out / 8) + row0 / 8] = ASYM ? (int32_t)zword : 0x77777777;
   }
   __syncthreads();
   const int64_t words_per_col = d_out / 8;
@@ -160,28 +184,32 @@ static int64_t pack_blocks(int64_t d_out, int64_t d_in) {
   return (d_in / G) * ((d_out + PackShape<G>::ROWS_B - 1) / PackShape<G>::ROWS_B);
 }
 
-template <int G>
+template <int G, bool ASYM>
 static void launch_pack_g(const uint16_t* W, int64_t d_out, int64_t d_in, const float* s, const float* clip,
                           int32_t* qweight, uint16_t* scales, int32_t* qzeros, hipStream_t stream) {
   const unsigned nb = (unsigned)pack_blocks<G>(d_out, d_in);
   if (s != nullptr && clip != nullptr)
-    quantize_pack_kernel<G, true, true><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+    quantize_pack_kernel<G, true, true, ASYM><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
   else if (s != nullptr)
-    quantize_pack_kernel<G, true, false><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+    quantize_pack_kernel<G, true, false, ASYM><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
   else if (clip != nullptr)
-    quantize_pack_kernel<G, false, true><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+    quantize_pack_kernel<G, false, true, ASYM><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
   else
-    quantize_pack_kernel<G, false, false><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
+    quantize_pack_kernel<G, false, false, ASYM><<<nb, kPackThreads, 0, stream>>>(W, d_out, d_in, s, clip, qweight, scales, qzeros);
 }
 
-hipError_t launch_quantize_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int group_size,
+hipError_t launch_quantize_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int group_size, bool asym,
                                 const float* s, const float* clip, int32_t* qweight,
                                 uint16_t* scales, int32_t* qzeros, hipStream_t stream) {
+#define AWQ_PK(G) \
+  if (asym) launch_pack_g<G, true>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream); \
+  else launch_pack_g<G, false>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream);
   switch (group_size) {
-    case 32: launch_pack_g<32>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream); break;
-    case 64: launch_pack_g<64>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream); break;
-    default: launch_pack_g<128>(W, d_out, d_in, s, clip, qweight, scales, qzeros, stream); break;
+    case 32: AWQ_PK(32) break;
+    case 64: AWQ_PK(64) break;
+    default: AWQ_PK(128) break;
   }
+#undef AWQ_PK
   return hipGetLastError();
 }
 

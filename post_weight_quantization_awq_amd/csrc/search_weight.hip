@@ -24,6 +24,12 @@
 // blocks per compute unit (three waves per SIMD, at most 168 VGPRs): with two
 // rows per lane that measured 9-14% faster than four rows at two waves per
 // SIMD.
+//
+// ASYM: the asymmetric grid ("AWQ architecture, in depth", a 4-bit zero point
+// per group, step ~ range / 15).  Each row tracks max(v) and max(-v) (both
+// start non-negative, so the range contains 0), step = RN(range / 15), the
+// zero point z = rint(-min / step) (exact), and per element the signed code
+// clamp(rint(v / step), -z, 15 - z) (one med3): 7 lane-ops per element·point.
 #include "awq_device.h"
 #include "awq_launch.h"
 
@@ -41,7 +47,7 @@ constexpr float kTinyMax = 0x1p-100f;
 template <int G>
 constexpr int search_rows_per_block() { return (kSearchThreads / (G / kSearchE)) * kSearchR; }
 
-template <int G>
+template <int G, bool ASYM>
 __global__ __launch_bounds__(kSearchThreads, 3) void search_weight_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int n_grid, const float* __restrict__ S,
     const float* __restrict__ C2, float* __restrict__ partials) {
@@ -123,23 +129,43 @@ __global__ __launch_bounds__(kSearchThreads, 3) void search_weight_kernel(
     for (int r = 0; r < R; ++r) {
       float v[kSearchE];
       float m = kTinyMax;
+      float mn = 0.0f;  // ASYM: max(-v), the range's lower end negated
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const h8 h = __builtin_bit_cast(h8, w[r][c]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           v[8 * c + e] = __builtin_fmaf((float)h[e], s[8 * c + e], 0.0f);
-          m = __builtin_fmaxf(m, __builtin_fabsf(v[8 * c + e]));
+          if constexpr (ASYM) {
+            m = __builtin_fmaxf(m, v[8 * c + e]);
+            mn = __builtin_fmaxf(mn, -v[8 * c + e]);
+          } else {
+            m = __builtin_fmaxf(m, __builtin_fabsf(v[8 * c + e]));
+          }
         }
       }
       m = group_max_nonneg<LPG>(m);
-      const float step = div7(m);
-      const float inv = __builtin_amdgcn_rcpf(step);
+      if constexpr (ASYM) {
+        mn = group_max_nonneg<LPG>(mn);
+        const float step = div15(m + mn);
+        const float inv = __builtin_amdgcn_rcpf(step);
+        const float z = __builtin_amdgcn_fmed3f(code_exact(mn, step, inv), 0.0f, (float)kUMax);
+        const float zl = -z, zh = (float)kUMax - z;
 #pragma unroll
-      for (int j = 0; j < kSearchE; ++j) {
-        const float q = __builtin_rintf(v[j] * inv);
-        const float d = __builtin_fmaf(-step, q, v[j]);
-        acc[j] = __builtin_fmaf(d, d, acc[j]);
+        for (int j = 0; j < kSearchE; ++j) {
+          const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(v[j] * inv), zl, zh);
+          const float d = __builtin_fmaf(-step, q, v[j]);
+          acc[j] = __builtin_fmaf(d, d, acc[j]);
+        }
+      } else {
+        const float step = div7(m);
+        const float inv = __builtin_amdgcn_rcpf(step);
+#pragma unroll
+        for (int j = 0; j < kSearchE; ++j) {
+          const float q = __builtin_rintf(v[j] * inv);
+          const float d = __builtin_fmaf(-step, q, v[j]);
+          acc[j] = __builtin_fmaf(d, d, acc[j]);
+        }
       }
     }
     float e = 0.0f;
@@ -179,25 +205,29 @@ int64_t search_weight_blocks(int group_size, int64_t d_out, int64_t d_in) {
   return (d_in / group_size) * ((d_out + rb - 1) / rb);
 }
 
-hipError_t launch_search_weight(int group_size, const WParts& parts, int64_t d_out, int64_t d_in,
-                                int n_grid, const float* S, const float* C2, float* partials,
-                                hipStream_t stream) {
-  const int64_t nb = search_weight_blocks(group_size, d_out, d_in);
+template <bool ASYM>
+static void launch_search_weight_t(int group_size, const WParts& parts, int64_t d_out, int64_t d_in, int n_grid,
+                                   const float* S, const float* C2, float* partials, hipStream_t stream) {
+  const unsigned nb = (unsigned)search_weight_blocks(group_size, d_out, d_in);
   const size_t shm = (size_t)2 * n_grid * group_size * sizeof(float);
   switch (group_size) {
     case 32:
-      search_weight_kernel<32><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
-          parts, d_out, d_in, n_grid, S, C2, partials);
+      search_weight_kernel<32, ASYM><<<nb, kSearchThreads, shm, stream>>>(parts, d_out, d_in, n_grid, S, C2, partials);
       break;
     case 64:
-      search_weight_kernel<64><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
-          parts, d_out, d_in, n_grid, S, C2, partials);
+      search_weight_kernel<64, ASYM><<<nb, kSearchThreads, shm, stream>>>(parts, d_out, d_in, n_grid, S, C2, partials);
       break;
     default:
-      search_weight_kernel<128><<<(unsigned)nb, kSearchThreads, shm, stream>>>(
-          parts, d_out, d_in, n_grid, S, C2, partials);
+      search_weight_kernel<128, ASYM><<<nb, kSearchThreads, shm, stream>>>(parts, d_out, d_in, n_grid, S, C2, partials);
       break;
   }
+}
+
+hipError_t launch_search_weight(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
+                                int n_grid, const float* S, const float* C2, float* partials,
+                                hipStream_t stream) {
+  if (asym) launch_search_weight_t<true>(group_size, parts, d_out, d_in, n_grid, S, C2, partials, stream);
+  else launch_search_weight_t<false>(group_size, parts, d_out, d_in, n_grid, S, C2, partials, stream);
   return hipGetLastError();
 }
 

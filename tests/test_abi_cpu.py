@@ -77,6 +77,19 @@ def test_pack_validation(A):
     assert A.lib().awq_last_error().decode() == ""
 
 
+def test_pack_asym_validation(A):
+    L = A.lib()
+    pk = lambda qz=FAKE, G=128, d_out=64, W=FAKE: L.awq_quantize_pack_asym(W, d_out, 256, G, None, None, FAKE, FAKE,
+                                                                          qz, None)
+    assert pk(qz=None) == A.AWQ_EINVAL          # zero points are data: qzeros required
+    assert "qzeros" in L.awq_last_error().decode()
+    assert pk(G=96) == A.AWQ_EINVAL
+    assert pk(d_out=60) == A.AWQ_ESHAPE
+    assert pk(W=FAKE_MIS) == A.AWQ_EALIGN
+    assert pk(qz=FAKE + 1) == A.AWQ_EALIGN
+    assert pk(qz=None, d_out=0, W=None) == A.AWQ_OK
+
+
 def test_unpack_validation(A):
     L = A.lib()
     assert L.awq_unpack_dequant(FAKE, FAKE, None, 64, 256, 128, None, FAKE, 7, None) == A.AWQ_EDTYPE
@@ -126,7 +139,7 @@ def test_search_validation(A):
     for c in bad:
         assert st_search(A, c, grp, X=FAKE, T=16, ld=256, clip=FAKE) == A.AWQ_EINVAL
     c = A._cfg(128, 20, "weight", 0, 0.5, 1e-4)
-    c.flags = 2
+    c.flags = 4
     assert st_search(A, c, grp) == A.AWQ_EINVAL
     assert st_search(A, good, grp, d_in=200) == A.AWQ_ESHAPE
     assert st_search(A, good, grp, d_in=64) == A.AWQ_ESHAPE

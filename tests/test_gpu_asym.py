@@ -1,0 +1,172 @@
+"""Asymmetric INT4 on the GPU against the oracle ("AWQ architecture, in depth":
+a 4-bit zero point per group and output channel, step about range / 15):
+bit-exact codes, fp16 scales and packed zero points; the unpacked weights;
+weight- and output-score searches and the clip search on the asymmetric grid."""
+import numpy as np
+import pytest
+
+from oracle import awq_oracle as O
+import workloads as WL
+from tests._util import argmin_ok, dev_f16, dev_f32, dev_x, host, say, ulp_dist
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def A():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import post_weight_quantization_awq_amd as A
+    A.lib()
+    return A
+
+
+def _special_rows(W, G):
+    """All-zero, one-signed and constant groups, and a group off centre."""
+    W[3, :G] = 0
+    W[4, :G] = np.abs(W[4, :G])
+    W[5, :G] = -np.abs(W[5, :G])
+    W[6, :G] = np.float16(0.0123)
+    W[7, :G] = W[7, :G] + np.float16(0.05)
+    return W
+
+
+def _pack_compare(A, W, G, s, clip):
+    qw, sc, qz = A.quantize_pack(dev_f16(W), G, None if s is None else dev_f32(s),
+                                 None if clip is None else dev_f32(clip), asym=True)
+    rqw, rsc, rqz, u, z, step = O.quantize_pack_asym(W, s, G, clip)
+    g_qw, g_sc, g_qz = host(qw), host(sc), host(qz)
+    assert np.array_equal(g_qw, rqw), "qweight"
+    assert np.array_equal(g_sc.view(np.uint16), rsc.view(np.uint16)), "scales"
+    assert np.array_equal(g_qz, rqz), "qzeros"
+    return qw, sc, qz
+
+
+@pytest.mark.parametrize("d_out,d_in,G,with_s,with_clip", [
+    (256, 512, 128, True, False),
+    (4096, 4096, 128, True, False),
+    (4096, 4096, 128, False, False),
+    (264, 384, 64, True, True),
+    (1032, 256, 32, True, True),
+    (8, 128, 128, True, False),
+    (16, 96, 32, False, True),
+])
+def test_quantize_pack_asym_bit_exact(A, d_out, d_in, G, with_s, with_clip):
+    say(f"pack asym d_out={d_out} d_in={d_in} G={G} s={with_s} clip={with_clip}")
+    W = _special_rows(WL.make_weight(9100 + d_out + G, d_out, d_in), G)
+    s = (np.exp(np.random.default_rng(d_in + 1).standard_normal(d_in) * 0.8)).astype(F32) if with_s else None
+    clip = None
+    if with_clip:
+        r = O.clip_ratios(20, 0.5)
+        clip = r[np.random.default_rng(d_out + 1).integers(0, 20, d_out)]
+    _pack_compare(A, W, G, s, clip)
+
+
+def test_pack_asym_grid_values(A):
+    """Values on the grid (k - z) * 2^-7 with both end codes present decode to
+    themselves: step 2^-7, zero point z, codes k."""
+    say("pack asym grid values")
+    rng = np.random.default_rng(5)
+    rows = []
+    for z in range(16):
+        k = np.concatenate([[0, 15], rng.integers(0, 16, 126)])
+        rng.shuffle(k)
+        rows.append((k - z) * 2.0 ** -7)
+    W = np.array(rows * 1, dtype=np.float16)          # 16 rows, one 128-group
+    qw, sc, qz = _pack_compare(A, W, 128, None, None)
+    assert np.all(host(sc).astype(F32) == F32(2.0 ** -7))
+    assert np.array_equal(O.unpack_codes(host(qz), 16)[:, 0], np.arange(16))
+    import torch
+    out = A.unpack_dequant(qw, sc, qz, 16, 128, None, torch.float32)
+    assert np.array_equal(host(out), W.astype(F32))
+
+
+@pytest.mark.parametrize("G,with_s", [(128, True), (64, False), (32, True)])
+def test_unpack_asym(A, G, with_s):
+    import torch
+    say(f"unpack asym G={G} s={with_s}")
+    d_out, d_in = 136, 512
+    W = _special_rows(WL.make_weight(41 + G, d_out, d_in), G)
+    s = (np.exp(np.random.default_rng(G).standard_normal(d_in) * 0.5)).astype(F32)
+    qw, sc, qz = _pack_compare(A, W, G, s, None)
+    sdev = dev_f32(s) if with_s else None
+    got = host(A.unpack_dequant(qw, sc, qz, d_out, G, sdev, torch.float32))
+    ref = O.unpack_dequant(host(qw), host(sc), host(qz), d_out, G, s if with_s else None)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name,parts,d_in,T,G", [
+    ("single_256x512", [256], 512, 64, 128),
+    ("q_proj_4096x4096", [4096], 4096, 4096, 128),
+    ("qkv_parts_ragged", [96, 40, 64], 256, 50, 64),
+    ("g32_ragged_rows", [200], 384, 33, 32),
+    ("eight_parts_one_empty", [130, 8, 0, 120, 1, 64, 70, 7], 256, 40, 128),
+])
+def test_search_weight_asym(A, name, parts, d_in, T, G):
+    say(f"search weight asym {name}")
+    Ws = [WL.make_weight(7100 + 13 * i + d_in, r, d_in) for i, r in enumerate(parts)]
+    if Ws[0].shape[0] > 8:
+        _special_rows(Ws[0], G)
+    X = WL.make_activations(8100 + d_in, T, d_in, "bf16")
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, asym=True)
+    errs, k, s = O.search_scales(Ws, xm, G, 20, asym=True)
+    g_err = host(res.err).astype(np.float64)
+    np.testing.assert_allclose(g_err, errs, rtol=1e-3, atol=0)
+    g_k = int(host(res.best_idx)[0])
+    assert argmin_ok(g_k, errs, k), (g_k, k)
+    assert g_err[g_k] <= g_err[0]                         # alpha = 0 is RTN on the asymmetric grid
+    assert ulp_dist(host(res.best_s), O.candidate_scales(xm, 20)[g_k]) <= 2
+
+
+def test_search_weight_asym_duo(A):
+    say("search weight asym + duo")
+    Ws = [WL.make_weight(7400 + i, r, 384) for i, r in enumerate([72, 56])]
+    X = WL.make_activations(8400, 60, 384, "bf16")
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=128, asym=True, duo=True)
+    errs, k, _ = O.search_scales(Ws, xm, 128, 20, asym=True, duo=True)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
+
+
+@pytest.mark.parametrize("parts,d_in,T,G", [([64], 256, 300, 128), ([96, 40, 64], 256, 129, 64),
+                                            ([72], 384, 77, 32)])
+def test_search_output_asym(A, parts, d_in, T, G):
+    say(f"search output asym parts={parts} d_in={d_in} T={T} G={G}")
+    Ws = [WL.make_weight(510 + 7 * i + T, r, d_in) for i, r in enumerate(parts)]
+    _special_rows(Ws[0], G)
+    X = WL.make_activations(610 + T, T, d_in, "bf16")
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          asym=True)
+    errs, k, _ = O.search_scales(Ws, xm, G, 20, "output", X=X, asym=True)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
+
+
+@pytest.mark.parametrize("parts,d_in,T,G", [([64], 256, 150, 128), ([24, 0, 40], 256, 60, 64)])
+def test_clip_search_asym(A, parts, d_in, T, G):
+    d_out = sum(parts)
+    say(f"clip search asym parts={parts} d_in={d_in} T={T} G={G}")
+    Ws = [WL.make_weight(710 + d_out + 3 * i, r, d_in) for i, r in enumerate(parts)]
+    W = np.concatenate(Ws, axis=0)
+    X = WL.make_activations(810 + d_out, T, d_in, "bf16")
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          n_clip=20, want_clip_err=True, asym=True)
+    errs, k, _ = O.search_scales([W], xm, G, 20, "output", X=X, asym=True)
+    g_k = int(host(res.best_idx)[0])
+    assert argmin_ok(g_k, errs, k)
+    s = O.candidate_scales(xm, 20)[g_k]          # the clip search runs on the chosen row
+    assert ulp_dist(host(res.best_s), s) <= 2
+    E, c = O.clip_search(W, s, X, G, 20, 0.5, asym=True)
+    np.testing.assert_allclose(host(res.clip_err).astype(np.float64), E, rtol=2e-3)
+    g_c = host(res.clip)
+    ratios = O.clip_ratios(20, 0.5)
+    for o in range(d_out):
+        gj = int(np.nonzero(ratios == g_c[o])[0][0])
+        assert argmin_ok(gj, E[o], O.first_argmin(E[o]), rel=2e-3), o
+    _pack_compare(A, W, G, s, c)
