@@ -63,6 +63,10 @@ step)), 0, 15), code u = clamp(rint(RN(v / step)) + z, 0, 15), reconstruction
 shrinks both ends (RN(c lo), RN(c hi)).  qzeros hold z in the qweight nibble
 order.
 
+W4A16 product: Y = X W_hat^T in fp64 with W_hat the exact fp32 dequantization
+(u - z) * fp16 scale of the packed layout (the stored, scaled domain: the
+activations are the ones that already carry the folded 1/s).
+
 Norm-group export: the shared scale is the per-channel geometric mean of the
 member scales, evaluated as exp(mean(ln s)) in fp64 and rounded once to fp32;
 the folded norm is the IEEE fp32 quotient rounded once to the norm's dtype.
@@ -477,6 +481,27 @@ def unpack_dequant(qweight: np.ndarray, scales: np.ndarray, qzeros: Optional[np.
     if s is not None:
         w = (w / s.astype(F32)[None, :]).astype(F32)
     return w
+
+
+# ---------------------------------------------------------------------------
+# O10: W4A16 product on the packed layout ([cassindra] "Kernels: why W4A16 is
+#      fast at decode": the packed 4-bit weights are dequantized with the
+#      group's scale and zero point and multiplied with 16-bit activations;
+#      decode is bound by reading the weights; [lm] "The kernels": W4A16 GEMM)
+# ---------------------------------------------------------------------------
+def w4a16_matmul(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray, qzeros: Optional[np.ndarray],
+                 d_out: int, group_size: int) -> np.ndarray:
+    """Y [M, d_out] = X [M, d_in] W_hat^T, fp64, where W_hat [d_out, d_in] is
+    unpack_dequant of the packed tensors (exact fp32 values); X is fp16 (or
+    bf16 bits), decoded exactly."""
+    W_hat = unpack_dequant(qweight, scales, qzeros, d_out, group_size)   # [d_out, d_in]
+    return decode_activations(X) @ W_hat.astype(F64).T
+
+
+def w4a16_bytes(d_out: int, d_in: int, group_size: int) -> int:
+    """Bytes a W4A16 product reads for its weights: 4-bit codes, fp16 scales
+    and 4-bit zero points per group and output channel."""
+    return d_out * d_in // 2 + 2 * d_out * (d_in // group_size) + d_out * (d_in // group_size) // 2
 
 
 # ---------------------------------------------------------------------------

@@ -224,6 +224,22 @@ def _pack_asym_zeros_row_order(W, s, G, clip=None):
     return O.pack_codes(u), O.f32_to_f16(step.T), qz, u, z, step
 
 
+
+def _w4a16_no_zero(X, qweight, scales, qzeros, d_out, G):
+    return O.w4a16_matmul(X, qweight, scales, None, d_out, G)
+
+
+def _w4a16_first_group_scales(X, qweight, scales, qzeros, d_out, G):
+    sc = np.repeat(np.asarray(scales)[:1], np.asarray(scales).shape[0], axis=0)
+    return _ORIG_W4A16(X, qweight, sc, qzeros, d_out, G)
+
+
+def _w4a16_fp16_accumulate(X, qweight, scales, qzeros, d_out, G):
+    W_hat = O.unpack_dequant(qweight, scales, qzeros, d_out, G).astype(np.float16)
+    return (np.asarray(X, dtype=np.float16) @ W_hat.T).astype(F64)
+
+
+_ORIG_W4A16 = O.w4a16_matmul
 MUTANTS = {
     "act_stats: signed mean": [("act_stats", _act_stats_signed)],
     "act_stats: max |x|": [("act_stats", _act_stats_max)],
@@ -273,6 +289,9 @@ MUTANTS = {
     "asym: codes clamped to [0, 14]": [("group_quantize_asym", lambda W, s, G, clip=None: _gqa(W, s, G, clip, umax=14))],
     "asym: dequant ignores the zero point": [("dequantize_asym", _deq_asym_no_zero)],
     "asym: qzeros in row order": [("quantize_pack_asym", _pack_asym_zeros_row_order)],
+    "w4a16: zero points ignored": [("w4a16_matmul", _w4a16_no_zero)],
+    "w4a16: first group's scales everywhere": [("w4a16_matmul", _w4a16_first_group_scales)],
+    "w4a16: fp16 accumulation": [("w4a16_matmul", _w4a16_fp16_accumulate)],
     "export: o/down with the shared scale": [("export_rtn", lambda W, G: O.quantize_pack(W, np.full(W.shape[1], 2.0, F32), G))],
 }
 

@@ -665,3 +665,64 @@ class TestAsymmetricInt4:
         assert np.all(sth == F32(d / 2)) and np.all(zh == 6)
         # values beyond the shrunk range saturate at the end codes
         assert np.array_equal(uh, np.clip(2 * (k - 6) + 6, 0, 15))
+
+
+# ---------------------------------------------------------------------------
+# W4A16 product on the packed layout ("AWQ architecture, in depth", "Kernels:
+# why W4A16 is fast at decode"; "Weight-Only Quantization: GPTQ and AWQ",
+# "The kernels" and "4. Tiny example")
+# ---------------------------------------------------------------------------
+class TestW4A16:
+    g = load("worked_example.json")
+
+    def test_worked_example_through_the_packed_layout(self):
+        """The page's outputs (naive 4.629, AWQ 5.057) from the packed codes: the
+        runtime multiplies x / s (fp16) with the stored q * fp16(step), so each
+        result carries the fp16 roundings of the step and of x / s (2^-11
+        relative each) on top of the page's 3-decimal print."""
+        w = np.tile(np.array(self.g["w"], dtype=np.float16), (8, 1))          # 8 rows, one group of 4
+        x = np.array(self.g["x"], dtype=F64)
+        s = np.array(self.g["scale"], dtype=F32)
+        for sv, key in [(None, "naive_out"), (s, "awq_out")]:
+            qw, sc, qz, q, step = O.quantize_pack(w, sv, 4)
+            xs = (x if sv is None else x / sv).astype(np.float16)[None, :]   # 1/s folded into the input
+            y = O.w4a16_matmul(xs, qw, sc, qz, 8, 4)
+            assert y.shape == (1, 8) and np.all(y == y[0, 0])
+            assert abs(y[0, 0] - self.g["printed"][key]) <= 5e-4 + 3 * 2 ** -11 * abs(y[0, 0])
+
+    def test_one_hot_rows_read_back_the_weights(self):
+        W = WL.make_weight(80, 16, 64)
+        qw, sc, qz, *_ = O.quantize_pack_asym(W, None, 32)
+        eye = np.eye(64, dtype=np.float16)
+        Y = O.w4a16_matmul(eye, qw, sc, qz, 16, 32)                       # Y[i, o] = W_hat[o, i]
+        W_hat = O.unpack_dequant(qw, sc, qz, 16, 32)
+        assert np.array_equal(Y, W_hat.T.astype(F64))
+        Y2 = O.w4a16_matmul(eye[:3] * np.float16(2), qw, sc, qz, 16, 32)
+        assert np.array_equal(Y2, 2 * W_hat.T[:3].astype(F64))
+
+    def test_scaled_domain_equals_weight_domain(self):
+        """(x / s) . W_hat_s = x . (W_hat_s / s): the packed product with the
+        folded input reproduces the search's fake-quantized weights."""
+        rng = np.random.default_rng(81)
+        s = np.exp2(rng.integers(-2, 3, 128)).astype(F32)     # powers of two: the fold is exact
+        # every group's max |w s| is 7 * 2^-6, so its step 2^-6 is stored exactly in fp16
+        V = rng.uniform(-0.99, 0.99, (24, 128)) * 7 * 2.0 ** -6
+        V[:, 5], V[:, 70] = 7 * 2.0 ** -6, -7 * 2.0 ** -6
+        W = (V / s).astype(np.float16)
+        X = (rng.standard_normal((3, 128)) * 4).astype(np.float16)
+        qw, sc, qz, q, step = O.quantize_pack(W, s, 64)
+        assert np.all(step == F32(2.0 ** -6))
+        Y = O.w4a16_matmul((X.astype(F32) / s).astype(np.float16), qw, sc, qz, 24, 64)
+        ref = X.astype(F64) @ O.fake_quant(W, s, 64).astype(F64).T
+        np.testing.assert_allclose(Y, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+    def test_bytes_and_decode_speedup_bound(self):
+        # weights at 4 + (16 + 4) / 128 bits against 16: the bandwidth-bound
+        # speedup at batch 1 approaches 3 to 4 times
+        n, k = 4096, 4096
+        b = O.w4a16_bytes(n, k, 128)
+        assert 8 * b / (n * k) == 4 + 20 / 128
+        assert 3.0 < 2 * n * k / b < 4.0
+        W = WL.make_weight(83, 64, 256)
+        qw, sc, qz, *_ = O.quantize_pack_asym(W, None, 128)
+        assert qw.nbytes + sc.nbytes + qz.nbytes == O.w4a16_bytes(64, 256, 128)
