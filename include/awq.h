@@ -300,6 +300,34 @@ awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, co
                               void* out, int32_t out_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * awq_w4a16_matmul -- the W4A16 product on the packed layout (decode GEMV).
+ * [cassindra] Kernels: why W4A16 is fast at decode (packed 4-bit weights
+ * dequantized in registers with the group's scale and zero point, multiplied
+ * with 16-bit activations; bound by reading the weights at a few tokens);
+ * [lm] The kernels, 6-9 (layout).
+ *
+ *   Y[t, o] = sum_i X[t, i] * (u[o, i] - z[g, o]) * scales[g, o],  g = i / G
+ *
+ * with u, z the nibbles of qweight / qzeros as written by awq_quantize_pack or
+ * awq_quantize_pack_asym (qzeros NULL means z = 7), i.e. the weights in the
+ * stored (scaled) domain: X must already carry the folded 1/s.
+ * X: fp16 [M, ld_x], ld_x >= d_in, 2-byte aligned.  qweight int32 [d_in, d_out/8]
+ * and qzeros int32 [d_in/G, d_out/8] 4-byte aligned; scales fp16 [d_in/G, d_out]
+ * 16-byte aligned.  Y: [M, ld_y] of y_dtype (AWQ_F16, rounded to nearest even
+ * once, or AWQ_F32), ld_y >= d_out and a multiple of 4, 8-byte (fp16) or
+ * 16-byte (fp32) aligned.  d_out % 8 == 0, d_in % group_size == 0.
+ * Arithmetic: u * x exact in fp32, fp32 sums over 32 input rows, then the zero
+ * point and scale, then fixed-order fp32 sums (deterministic).  Tokens are
+ * processed 4 at a time (the weights are read once per 4 tokens).
+ * ws: awq_w4a16_workspace(M, d_out, d_in) bytes, 256-byte aligned.  M = 0 or
+ * d_out = 0 returns AWQ_OK at once.
+ * ------------------------------------------------------------------------- */
+awq_status awq_w4a16_workspace(int64_t M, int64_t d_out, int64_t d_in, size_t* bytes /* [host] */);
+awq_status awq_w4a16_matmul(const void* X, int64_t M, int64_t ld_x, const int32_t* qweight, const uint16_t* scales,
+                            const int32_t* qzeros, int64_t d_out, int64_t d_in, int32_t group_size, void* Y,
+                            int64_t ld_y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * awq_set_timing_events -- benchmark hook.  While set, every later call on
  * this host thread records `before` and `after` (hipEvent_t handles passed as
  * void*, created by the caller) on the call's stream immediately around its

@@ -40,6 +40,7 @@ EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales_wo
             "awq_search_workspace", "awq_search_scales", "awq_quantize_pack", "awq_quantize_pack_asym",
             "awq_unpack_dequant", "awq_norm_group_fold", "awq_weight_channel_mean_workspace",
             "awq_weight_channel_mean", "awq_candidate_scales_duo_workspace", "awq_candidate_scales_duo",
+            "awq_w4a16_workspace", "awq_w4a16_matmul",
             "awq_last_error", "awq_abi_version", "awq_set_timing_events")
 
 
@@ -84,6 +85,8 @@ def _load() -> ctypes.CDLL:
         "awq_weight_channel_mean": [ctypes.POINTER(WGroup), I64, P, P, SZ, P],
         "awq_candidate_scales_duo_workspace": [I64, I32, PSZ],
         "awq_candidate_scales_duo": [P, P, I64, I32, F64, P, P, SZ, P],
+        "awq_w4a16_workspace": [I64, I64, I64, PSZ],
+        "awq_w4a16_matmul": [P, I64, I64, P, P, P, I64, I64, I32, P, I64, I32, P, SZ, P],
         "awq_set_timing_events": [P, P],
     }
     for name, args in sig.items():
@@ -371,6 +374,41 @@ def quantize_pack(W: torch.Tensor, group_size: int = 128, s: Optional[torch.Tens
     return PackPlan(W, group_size, s, clip, with_zeros, out, stream, asym).run()
 
 
+class W4A16Plan(_Prepared):
+    """Y [M, d_out] = X [M, d_in] (fp16, carrying the folded 1/s) times the
+    dequantized packed weights, transposed (the decode GEMV)."""
+    _fn = "awq_w4a16_matmul"
+
+    def __init__(self, X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
+                 qzeros: Optional[torch.Tensor], d_out: int, group_size: int = 128, out_dtype=torch.float16,
+                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+        _dev(X, "X")
+        _dev(qweight, "qweight")
+        if X.dtype != torch.float16:
+            raise ValueError("X must be fp16")
+        M, d_in, ld = _rows_view(X, "X")
+        if qweight.shape != (d_in, d_out // 8):
+            raise ValueError("qweight must be [d_in, d_out/8]")
+        n = ctypes.c_size_t()
+        _check(lib().awq_w4a16_workspace(M, d_out, d_in, ctypes.byref(n)))
+        self.ws = workspace(n.value, X.device) if (ws is None or ws.numel() < n.value) else ws
+        self.out = torch.empty((M, d_out), dtype=out_dtype, device=X.device) if out is None else out
+        ydt = {torch.float32: AWQ_F32, torch.float16: AWQ_F16}[self.out.dtype]
+        self._keep = (X, qweight, scales, qzeros)
+        self._bind(_ptr(X), M, ld, _ptr(qweight), _ptr(scales), _ptr(qzeros), d_out, d_in, group_size,
+                   _ptr(self.out), self.out.stride(0), ydt, _ptr(self.ws), self.ws.numel(), _stream(stream))
+
+    def run(self) -> torch.Tensor:
+        self.launch()
+        return self.out
+
+
+def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor],
+                 d_out: int, group_size: int = 128, out_dtype=torch.float16, stream=None) -> torch.Tensor:
+    """Y = X W_hat^T on the packed layout (W_hat = (u - z) * scale in the stored domain)."""
+    return W4A16Plan(X, qweight, scales, qzeros, d_out, group_size, out_dtype, stream=stream).run()
+
+
 def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], d_out: int,
                    group_size: int = 128, s: Optional[torch.Tensor] = None, out_dtype=torch.float32,
                    stream=None) -> torch.Tensor:
@@ -432,5 +470,5 @@ def set_timing_events(before: Optional[int], after: Optional[int]) -> None:
 
 
 __all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "PackPlan", "FoldPlan", "norm_group_fold",
-           "weight_channel_mean", "candidate_scales_duo", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
+           "weight_channel_mean", "candidate_scales_duo", "W4A16Plan", "w4a16_matmul", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
            "search_workspace_bytes", "act_stats_workspace_bytes", "SearchResult", "lib", "LIB_PATH"]

@@ -478,6 +478,44 @@ awq_status awq_quantize_pack_asym(const void* W, int64_t d_out, int64_t d_in, in
                             "awq_quantize_pack_asym");
 }
 
+// ---------------------------------------------------------------------------
+static int w4a16_mt(int64_t M) { return M >= 3 ? 4 : (int)M; }
+
+awq_status awq_w4a16_workspace(int64_t M, int64_t d_out, int64_t d_in, size_t* bytes) {
+  if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
+  if (M < 0 || d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
+  *bytes = align256((size_t)w4a16_slices(d_in) * (size_t)w4a16_mt(M) * (size_t)d_out * sizeof(float));
+  return ok();
+}
+
+awq_status awq_w4a16_matmul(const void* X, int64_t M, int64_t ld_x, const int32_t* qweight, const uint16_t* scales,
+                            const int32_t* qzeros, int64_t d_out, int64_t d_in, int32_t group_size, void* Y,
+                            int64_t ld_y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_group(group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", group_size);
+  if (M < 0 || d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
+  if (d_out % 8) return fail(AWQ_ESHAPE, "d_out %lld not a multiple of 8", (long long)d_out);
+  if (d_in % group_size) return fail(AWQ_ESHAPE, "d_in %lld not a multiple of group_size %d", (long long)d_in, group_size);
+  if (y_dtype != AWQ_F16 && y_dtype != AWQ_F32) return fail(AWQ_EDTYPE, "y_dtype %d: need AWQ_F16 or AWQ_F32", y_dtype);
+  if (M == 0 || d_out == 0) return ok();
+  if (d_in == 0) return fail(AWQ_ESHAPE, "d_in is 0 with M, d_out > 0");
+  if (ld_x < d_in) return fail(AWQ_ESHAPE, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
+  if (ld_y < d_out || ld_y % 4) return fail(AWQ_ESHAPE, "ld_y %lld: need >= d_out and a multiple of 4", (long long)ld_y);
+  if (!X || !qweight || !scales || !Y) return fail(AWQ_EINVAL, "X / qweight / scales / Y is NULL");
+  if (((uintptr_t)X & 1u) || ((uintptr_t)qweight & 3u) || (qzeros && ((uintptr_t)qzeros & 3u)))
+    return fail(AWQ_EALIGN, "X / qweight / qzeros misaligned");
+  if (!aligned16(scales)) return fail(AWQ_EALIGN, "scales not 16-byte aligned");
+  if ((uintptr_t)Y & (y_dtype == AWQ_F16 ? 7u : 15u)) return fail(AWQ_EALIGN, "Y misaligned for vector stores");
+  size_t need = 0;
+  awq_w4a16_workspace(M, d_out, d_in, &need);
+  if (!ws || ws_bytes < need) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255u) return fail(AWQ_EALIGN, "ws not 256-byte aligned");
+  mark(true, (hipStream_t)stream);
+  hipError_t e = launch_w4a16((const uint16_t*)X, M, ld_x, (const uint32_t*)qweight, scales, (const uint32_t*)qzeros,
+                              d_out, d_in, group_size, Y, ld_y, y_dtype == AWQ_F16, (float*)ws, (hipStream_t)stream);
+  mark(false, (hipStream_t)stream);
+  return hip_status(e, "awq_w4a16_matmul");
+}
+
 awq_status awq_norm_group_fold(const float* const* s, int32_t n_members, int64_t d_in, const void* norm,
                                int32_t norm_dtype, void* norm_out, float* s_shared, void* stream) {
   if (!s) return fail(AWQ_EINVAL, "s is NULL");

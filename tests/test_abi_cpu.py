@@ -29,7 +29,7 @@ def A():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(awq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_abi():
@@ -232,3 +232,30 @@ def test_duo_entry_validation(A):
     # the duo flag enlarges the search workspace by the weight statistic and the fp64 table
     plain = A.search_workspace_bytes(64, 256, 1)
     assert A.search_workspace_bytes(64, 256, 1, duo=True) > plain
+
+
+def test_w4a16_validation(A):
+    L = A.lib()
+    n = ctypes.c_size_t()
+    assert L.awq_w4a16_workspace(1, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 32 * 4096 * 4
+    assert L.awq_w4a16_workspace(3, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 32 * 4 * 4096 * 4
+    assert L.awq_w4a16_workspace(-1, 8, 128, ctypes.byref(n)) == A.AWQ_EINVAL
+    need = 32 * 4096 * 4
+
+    def mm(X=FAKE, M=1, ld_x=4096, qw=FAKE, sc=FAKE, qz=None, d_out=4096, d_in=4096, G=128, Y=FAKE, ld_y=4096,
+           ydt=A.AWQ_F16, ws=FAKE, nb=need):
+        return L.awq_w4a16_matmul(X, M, ld_x, qw, sc, qz, d_out, d_in, G, Y, ld_y, ydt, ws, nb, None)
+
+    assert mm(G=96) == A.AWQ_EINVAL
+    assert mm(d_out=4092) == A.AWQ_ESHAPE
+    assert mm(d_in=4000) == A.AWQ_ESHAPE
+    assert mm(ld_x=4095) == A.AWQ_ESHAPE
+    assert mm(ld_y=4094) == A.AWQ_ESHAPE
+    assert mm(ydt=A.AWQ_BF16) == A.AWQ_EDTYPE
+    assert mm(X=None) == A.AWQ_EINVAL
+    assert mm(sc=FAKE + 8) == A.AWQ_EALIGN
+    assert mm(Y=FAKE + 4) == A.AWQ_EALIGN
+    assert mm(Y=FAKE + 8, ydt=A.AWQ_F32) == A.AWQ_EALIGN
+    assert mm(nb=need - 1) == A.AWQ_EWORKSPACE
+    assert mm(ws=FAKE + 16) == A.AWQ_EALIGN
+    assert mm(M=0, X=None, Y=None) == A.AWQ_OK

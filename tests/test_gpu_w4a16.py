@@ -1,0 +1,137 @@
+"""W4A16 product on the packed layout against the oracle ("AWQ architecture, in
+depth", "Kernels: why W4A16 is fast at decode").
+
+Packed inputs come from the oracle's pack or from random codes (never from the
+HIP path).  Tolerance, from the arithmetic: products u * x are exact in fp32;
+a wave adds 32 of them and the 32 activations in fp32, folds the zero point
+and the scale (3 roundings), then 4 waves and n_slices row slices are added in
+fp32.  With B = sum_i |x_i| (u_i + z) scale the fp32 result lies within
+2^-24 (32 + 8 + 4 + n_slices) B of the exact product; an fp16 output adds one
+rounding (at most one fp16 ulp here, taken at the larger magnitude)."""
+import numpy as np
+import pytest
+
+from oracle import awq_oracle as O
+import workloads as WL
+from tests._util import dev_f16, host, say
+
+pytestmark = pytest.mark.gpu
+
+F32, F64 = np.float32, np.float64
+
+
+@pytest.fixture(scope="module")
+def A():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import post_weight_quantization_awq_amd as A
+    A.lib()
+    return A
+
+
+def _random_packed(seed, d_out, d_in, G, zeros=True):
+    rng = np.random.default_rng(seed)
+    qw = rng.integers(0, 2 ** 32, (d_in, d_out // 8), dtype=np.uint64).astype(np.uint32)
+    sc = (rng.uniform(0.002, 0.03, (d_in // G, d_out))).astype(np.float16)
+    qz = rng.integers(0, 2 ** 32, (d_in // G, d_out // 8), dtype=np.uint64).astype(np.uint32) if zeros else None
+    return qw, sc, qz
+
+
+def _dev_i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
+
+
+def _bound(X, qw, sc, qz, d_out, G, n_slices):
+    u = O.unpack_codes(qw, d_out).astype(F64)                         # [d_out, d_in]
+    z = (O.unpack_codes(qz, d_out).astype(F64) if qz is not None
+         else np.full((d_out, qw.shape[0] // G), 7.0))
+    zz = np.repeat(z, G, axis=1)
+    ss = np.repeat(sc.astype(F64).T, G, axis=1)
+    B = np.abs(O.decode_activations(X)) @ ((u + zz) * ss).T
+    return 2.0 ** -24 * (32 + 8 + 4 + n_slices) * B
+
+
+def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
+    import torch
+    M, d_in = X.shape
+    Xp = X if ld_x is None else np.pad(X, ((0, 0), (0, ld_x - d_in)))
+    Xd = dev_f16(Xp)[:, :d_in]
+    tdt = torch.float16 if out_dtype == "f16" else torch.float32
+    out = None
+    if ld_y is not None:
+        out = torch.full((M, ld_y), 7.0, dtype=tdt, device="cuda")[:, :d_out]
+    plan = A.W4A16Plan(Xd, _dev_i32(qw), dev_f16(sc), None if qz is None else _dev_i32(qz), d_out, G, tdt, out=out)
+    Y = host(plan.run()).astype(F64)
+    ref = O.w4a16_matmul(X, qw, sc, qz, d_out, G)
+    tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 127) // 128)
+    if out_dtype == "f16":
+        tol = tol + np.spacing(np.abs(ref).astype(np.float16) * np.float16(1.002)).astype(F64)
+    err = np.abs(Y - ref)
+    assert np.all(err <= tol), (float((err - tol).max()), float(err.max()))
+    if ld_y is not None:   # the padding columns are untouched
+        assert np.all(host(plan.out.as_strided((M, ld_y), (ld_y, 1)))[:, d_out:] == 7.0)
+    return Y
+
+
+@pytest.mark.parametrize("name,d_out,d_in,G,zeros", [
+    ("q_proj_4096x4096", 4096, 4096, 128, False),
+    ("gate_up_24576x4096", 24576, 4096, 128, True),
+    ("down_4096x12288", 4096, 12288, 128, True),
+    ("k_proj_1024x4096_g64", 1024, 4096, 64, True),
+])
+def test_w4a16_decode_full_size(A, name, d_out, d_in, G, zeros):
+    say(f"w4a16 {name} M=1")
+    qw, sc, qz = _random_packed(d_out + d_in + G, d_out, d_in, G, zeros)
+    X = (np.random.default_rng(d_in).standard_normal((1, d_in))).astype(np.float16)
+    _check(A, X, qw, sc, qz, d_out, G)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("d_out,d_in,G,out_dtype", [(1032, 384, 64, "f16"), (520, 96, 32, "f32"),
+                                                    (16, 256, 128, "f32")])
+def test_w4a16_tokens_and_ragged_shapes(A, M, d_out, d_in, G, out_dtype):
+    say(f"w4a16 M={M} d_out={d_out} d_in={d_in} G={G} {out_dtype}")
+    qw, sc, qz = _random_packed(7 * M + d_out, d_out, d_in, G, True)
+    X = (np.random.default_rng(M + d_in).standard_normal((M, d_in)) * 3).astype(np.float16)
+    _check(A, X, qw, sc, qz, d_out, G, out_dtype)
+
+
+def test_w4a16_strides(A):
+    say("w4a16 strided X and Y")
+    qw, sc, qz = _random_packed(11, 264, 256, 64, True)
+    X = (np.random.default_rng(12).standard_normal((3, 256))).astype(np.float16)
+    _check(A, X, qw, sc, qz, 264, 64, "f16", ld_x=264, ld_y=272)
+    _check(A, X, qw, sc, qz, 264, 64, "f32", ld_x=300, ld_y=268)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_w4a16_on_oracle_packed_weights(A, asym):
+    """A quantized linear: the folded input x / s times the packed W * s
+    reproduces x times the fake-quantized weights within the fp16 roundings."""
+    say(f"w4a16 oracle-packed asym={asym}")
+    W = WL.make_weight(90 + asym, 512, 1024)
+    s = (np.exp(np.random.default_rng(91).standard_normal(1024) * 0.4)).astype(F32)
+    if asym:
+        qw, sc, qz, *_ = O.quantize_pack_asym(W, s, 128)
+    else:
+        qw, sc, qz, *_ = O.quantize_pack(W, s, 128)
+    X = WL.make_activations(92, 4, 1024, "bf16")
+    Xs = (O.decode_activations(X) / s.astype(F64)).astype(np.float16)
+    Y = _check(A, Xs, qw, sc, qz, 512, 128, "f32")
+    fq = O.fake_quant_asym(W, s, 128) if asym else O.fake_quant(W, s, 128)
+    ref = O.decode_activations(X) @ fq.astype(F64).T
+    # each term differs by the fp16 roundings of x / s and of the stored step
+    # (2^-11 relative each) and the fp32 roundings of the fake quantization
+    B2 = np.abs(O.decode_activations(X)) @ np.abs(fq.astype(F64)).T
+    assert np.all(np.abs(Y - ref) <= (2.0 ** -10 + 2.0 ** -20) * B2)
+
+
+def test_w4a16_deterministic(A):
+    say("w4a16 determinism")
+    import torch
+    qw, sc, qz = _random_packed(13, 4096, 4096, 128, True)
+    X = dev_f16((np.random.default_rng(14).standard_normal((2, 4096))).astype(np.float16))
+    a = A.w4a16_matmul(X, _dev_i32(qw), dev_f16(sc), _dev_i32(qz), 4096, 128, torch.float32)
+    b = A.w4a16_matmul(X, _dev_i32(qw), dev_f16(sc), _dev_i32(qz), 4096, 128, torch.float32)
+    assert torch.equal(a, b)
