@@ -608,6 +608,152 @@ def bench_export(args):
     }
 
 
+def cpu_baseline_w4a16(layers_h, M, budget_s: float):
+    """Times the CPU oracle's W4A16 product on the first layers of the step
+    (host copies of the same packed tensors) until the budget runs out; the
+    rate is packed bytes per second."""
+    from oracle import awq_oracle as O
+    t0, c0 = time.perf_counter(), time.process_time()
+    done_b, done_l = 0, 0
+    for qw, sc, qz, x, d_out, G in layers_h:
+        O.w4a16_matmul(x, qw, sc, qz, d_out, G)
+        done_b += O.w4a16_bytes(d_out, qw.shape[0], G)
+        done_l += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {"value": done_b / wall / 1e9, "unit": "GB/s", "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"{done_l} layers of the step at M = {M} ({done_b / 1e9:.2f} GB of packed weights, "
+                      f"{wall:.1f} s wall)"}
+
+
+def bench_w4a16(args):
+    import numpy as np
+    import torch
+    import post_weight_quantization_awq_amd as A
+    import workloads as WL
+
+    wl = WL.WORKLOADS["qwen3_8b_decode_w4a16"]
+    G = args.group_size or wl.group_sizes[0]
+    M = args.tokens
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed_base)
+    lo, hi = -2 ** 31, 2 ** 31 - 1
+    layers = []
+    for b in range(args.blocks):
+        for g in wl.groups:
+            d_out, d_in = g.d_out, g.d_in
+            qw = torch.randint(lo, hi, (d_in, d_out // 8), dtype=torch.int32, device=dev, generator=gen)
+            sc = (torch.rand((d_in // G, d_out), device=dev, generator=gen) * 0.028 + 0.002).half()
+            qz = torch.randint(lo, hi, (d_in // G, d_out // 8), dtype=torch.int32, device=dev, generator=gen)
+            x = torch.randn((M, d_in), device=dev, generator=gen).half()
+            y = torch.empty((M, d_out), dtype=torch.float16, device=dev)
+            layers.append((qw, sc, qz, x, y, d_out, d_in))
+    n, ws_bytes = ctypes.c_size_t(), 0
+    for g in wl.groups:   # one workspace for every call of the step (stream-ordered)
+        A.lib().awq_w4a16_workspace(M, g.d_out, g.d_in, ctypes.byref(n))
+        ws_bytes = max(ws_bytes, n.value)
+    ws = A.workspace(ws_bytes, dev)
+    # a decode step is a fixed sequence of launches: captured once as a HIP
+    # graph (default-priority side stream) and replayed, as a serving loop does
+    s = torch.cuda.Stream()
+    plans = [A.W4A16Plan(x, qw, sc, qz, d_out, G, out=y, ws=ws, stream=s)
+             for qw, sc, qz, x, y, d_out, d_in in layers]
+    # fp16 reference: the same shapes through torch's fp16 linear (hipBLASLt)
+    w16 = [torch.randn((d_out, d_in), device=dev, generator=gen).half() * 0.02
+           for qw, sc, qz, x, y, d_out, d_in in layers]
+    y16 = [torch.empty((M, d_out), dtype=torch.float16, device=dev) for *_, d_out, d_in in layers]
+    torch.cuda.synchronize()
+    K = args.steps
+
+    def step():
+        for p in plans:
+            p.launch()
+
+    def step16():
+        for (qw, sc, qz, x, y, d_out, d_in), w, o in zip(layers, w16, y16):
+            torch.mm(x, w.t(), out=o)
+
+    def timed(fn):
+        s.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            fn()
+        s.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            step()
+            step16()
+        ms_eager = timed(step)
+        ms16_eager = timed(step16)
+        ref_y = [y.clone() for *_, y, d_out, d_in in layers[:8]]
+        g, g16 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        with torch.cuda.graph(g16, stream=s):
+            step16()
+        for _ in range(args.warmup):
+            g.replay()
+            g16.replay()
+        ms = timed(g.replay)
+        ms16 = timed(g16.replay)
+        s.synchronize()
+        for r, (*_, y, d_out, d_in) in zip(ref_y, layers[:8]):   # replays reproduce the eager results
+            if not torch.equal(r, y):
+                raise RuntimeError("graph replay differs from the eager W4A16 result")
+    # per-call durations (the GEMV and its reduction) with events on the call's stream
+    n_l = len(plans)
+    ev = HipEvents(2 * n_l * K)
+    with torch.cuda.stream(s):
+        for k in range(K):
+            for i, p in enumerate(plans):
+                A.set_timing_events(ev.h(2 * (k * n_l + i)), ev.h(2 * (k * n_l + i) + 1))
+                p.launch()
+            A.set_timing_events(None, None)
+    s.synchronize()
+    call_ms = [sum(ev.ms(2 * (k * n_l + i), 2 * (k * n_l + i) + 1) for k in range(K)) / K for i in range(n_l)]
+    ev.close()
+
+    def alg_bytes(d_out, d_in):
+        return d_out * d_in // 2 + 2 * d_out * (d_in // G) + d_out * (d_in // G) // 2 + 2 * M * (d_in + d_out)
+
+    tot_b = sum(alg_bytes(d_out, d_in) for *_, d_out, d_in in layers)
+    achieved = tot_b / (sum(call_ms) * 1e-3) / 1e9
+    kinds = {}
+    for (qw, sc, qz, x, y, d_out, d_in), t in zip(layers, call_ms):
+        key = f"{d_out}x{d_in}"
+        kb = kinds.setdefault(key, [0.0, 0.0, 0])
+        kb[0] += t
+        kb[1] += alg_bytes(d_out, d_in)
+        kb[2] += 1
+    out = {
+        "metric": "W4A16 decode through packed linears: weight bytes/s", "value": tot_b / (ms * 1e-3) / 1e9,
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16-in/u4-w/f32-acc",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_decode_w4a16", "blocks": args.blocks, "tokens": M, "group_size": G,
+                   "linears_per_block": [f"{g.d_out}x{g.d_in}" for g in wl.groups]},
+        "fp16_ms_per_step": ms16, "speedup_vs_fp16": ms16 / ms,
+        "eager_ms_per_step": ms_eager, "fp16_eager_ms_per_step": ms16_eager,
+        "per_shape_GBps": {k: v[1] / (v[0] * 1e-3) / 1e9 for k, v in kinds.items()},
+        "per_shape_us": {k: 1e3 * v[0] / v[2] for k, v in kinds.items()},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "w4a16_gemv_kernel + w4a16_reduce_kernel (per call)"},
+    }
+    if not args.no_cpu_baseline:
+        hl = []
+        for qw, sc, qz, x, y, d_out, d_in in layers[:8]:
+            hl.append((qw.cpu().numpy().view(np.uint32), sc.cpu().numpy(), qz.cpu().numpy().view(np.uint32),
+                       x.cpu().numpy(), d_out, G))
+        out["cpu_baseline"] = cpu_baseline_w4a16(hl, M, min(args.cpu_seconds, 20.0))
+    return out
+
+
 def bench_copy(args):
     """Plain device copy of 512 MiB (torch), the calibration of the HBM byte counters."""
     import torch
@@ -635,7 +781,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="q_proj_4096x4096",
                     choices=["single_linear_256x512", "q_proj_4096x4096", "qkv_6144x4096_output",
-                             "mlp_output_clip", "qwen3_8b_sweep", "qwen3_8b_export", "copy_512MiB"])
+                             "mlp_output_clip", "qwen3_8b_sweep", "qwen3_8b_export", "qwen3_8b_decode_w4a16",
+                             "copy_512MiB"])
     ap.add_argument("--group-size", type=int, default=None)
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
     ap.add_argument("--streams", type=int, default=4,
@@ -644,6 +791,7 @@ def main() -> int:
                     help="duo-scaling candidates (x_mean^r / (w_mean^(1-r) + 1e-4)) in the search workloads")
     ap.add_argument("--asym", action="store_true",
                     help="asymmetric INT4 (zero point per group) in the search and pack of the search workloads")
+    ap.add_argument("--tokens", type=int, default=1, help="tokens per decode step of the W4A16 workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -666,6 +814,8 @@ def main() -> int:
         out = bench_sweep(args)
     elif args.workload == "qwen3_8b_export":
         out = bench_export(args)
+    elif args.workload == "qwen3_8b_decode_w4a16":
+        out = bench_w4a16(args)
     elif args.workload == "copy_512MiB":
         out = bench_copy(args)
     else:

@@ -237,10 +237,11 @@ def test_duo_entry_validation(A):
 def test_w4a16_validation(A):
     L = A.lib()
     n = ctypes.c_size_t()
-    assert L.awq_w4a16_workspace(1, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 32 * 4096 * 4
-    assert L.awq_w4a16_workspace(3, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 32 * 4 * 4096 * 4
+    assert L.awq_w4a16_workspace(1, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value > 0
+    need = n.value                      # fp32 partials of one token per input slice and output
+    assert need % (4096 * 4) == 0
+    assert L.awq_w4a16_workspace(3, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 4 * need
     assert L.awq_w4a16_workspace(-1, 8, 128, ctypes.byref(n)) == A.AWQ_EINVAL
-    need = 32 * 4096 * 4
 
     def mm(X=FAKE, M=1, ld_x=4096, qw=FAKE, sc=FAKE, qz=None, d_out=4096, d_in=4096, G=128, Y=FAKE, ld_y=4096,
            ydt=A.AWQ_F16, ws=FAKE, nb=need):

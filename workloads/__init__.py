@@ -217,6 +217,11 @@ WORKLOADS = {
     # two norm folds, packing with the shared scales, o/down at RTN
     "qwen3_8b_export": Workload(
         "qwen3_8b_export", QWEN3_8B_BLOCK, [128], blocks=36, seed_base=6000),
+    # decode through the packed linears of the same blocks (fused QKV and
+    # gate/up as a serving engine runs them): random codes, scales and zero
+    # points of the packed layout, fp16 activations of a few tokens
+    "qwen3_8b_decode_w4a16": Workload(
+        "qwen3_8b_decode_w4a16", QWEN3_8B_BLOCK, [128], blocks=36, seed_base=7000),
 }
 
 
