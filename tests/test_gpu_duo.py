@@ -59,7 +59,8 @@ def test_candidate_scales_duo(A, d_in, n_grid):
     assert ulp_dist(S, O.candidate_scales(xm, n_grid, w_mean=wm)) <= 2
 
 
-@pytest.mark.parametrize("rows,d_in,T,G", [([256], 512, 64, 128), ([96, 40, 64], 256, 50, 64), ([200], 384, 33, 32)])
+@pytest.mark.parametrize("rows,d_in,T,G", [([256], 512, 64, 128), ([96, 40, 64], 256, 50, 64), ([200], 384, 33, 32),
+                                            ([4096], 4096, 4096, 128)])     # q_proj at full size
 def test_search_weight_duo(A, rows, d_in, T, G):
     say(f"duo weight search rows={rows} d_in={d_in} G={G}")
     Ws = _parts(rows, d_in, 960 + d_in, (3,))
