@@ -723,6 +723,9 @@ def bench_w4a16(args):
 
     tot_b = sum(alg_bytes(d_out, d_in) for *_, d_out, d_in in layers)
     achieved = tot_b / (sum(call_ms) * 1e-3) / 1e9
+    # 32 tokens or more run the matrix-core GEMM: quoted against the fp16 MFMA peak
+    gemm = M >= 32
+    tflops = 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (sum(call_ms) * 1e-3) / 1e12
     kinds = {}
     for (qw, sc, qz, x, y, d_out, d_in), t in zip(layers, call_ms):
         key = f"{d_out}x{d_in}"
@@ -741,9 +744,14 @@ def bench_w4a16(args):
         "eager_ms_per_step": ms_eager, "fp16_eager_ms_per_step": ms16_eager,
         "per_shape_GBps": {k: v[1] / (v[0] * 1e-3) / 1e9 for k, v in kinds.items()},
         "per_shape_us": {k: 1e3 * v[0] / v[2] for k, v in kinds.items()},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "w4a16_gemv_kernel + w4a16_reduce_kernel (per call)"},
+        "roofline": ({"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": None, "kernel": "w4a16_gemm_kernel"}
+                     if gemm else
+                     {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                      "kernel": "w4a16_gemv_kernel + w4a16_reduce_kernel (per call)"}),
+        "step_TFLOPs": 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (ms * 1e-3) / 1e12,
+        "fp16_step_TFLOPs": 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (ms16 * 1e-3) / 1e12,
     }
     if not args.no_cpu_baseline:
         hl = []

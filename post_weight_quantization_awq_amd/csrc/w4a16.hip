@@ -54,6 +54,16 @@ __device__ __forceinline__ uint32_t and_opaque(uint32_t a, uint32_t b) {
   return r;
 }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// (a & m) | c in one VALU op (the compiler otherwise emits an and and an or);
+// m and c are held in VGPRs (a VOP3 op reads at most one scalar operand here)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+
 template <int MT>
 __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ X, int64_t ld_x, int m_valid, int64_t d_in, const uint32_t* __restrict__ qweight,
@@ -221,9 +231,190 @@ __global__ __launch_bounds__(kRdCols * kRdSplit) void w4a16_reduce_kernel(const 
 
 int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 
+// ---------------------------------------------------------------------------
+// Prefill: the W4A16 GEMM on the matrix cores ("AWQ architecture, in depth",
+// "Kernels: why W4A16 is fast at decode": at prefill sizes the product is
+// compute-bound and dequantization is extra work).  Block tile 128 tokens x
+// 128 outputs, 8 waves of 64 x 32 (2 x 1 v_mfma_f32_32x32x16_f16; a group's
+// own accumulators and the result's fit 2 waves per SIMD), K in stages of 32
+// through two LDS buffers.  X goes to LDS as it is; the codes are
+// dequantized on their way to LDS into exact fp16 (u - z): two K rows at a
+// time, one byte permute puts the same byte of both rows side by side, one
+// and-or makes 1024 + u (even nibbles) or 1024 + 16 u (odd nibbles) and one
+// packed fp16 add subtracts 1024 + z (or 1024 + 16 z).  The MFMAs therefore
+// accumulate exact products (u - z) x (16x for the odd-nibble outputs, whose
+// scale takes the 1/16); a group of G rows accumulates alone and is added to
+// the result times the fp32 scale of its column, so no fp16 rounding touches
+// a dequantized weight.  16-byte K-chunks of an LDS tile row are swizzled by
+// the row so that fragment reads are conflict-free.
+// ---------------------------------------------------------------------------
+constexpr int kQBM = 128, kQBN = 128, kQBK = 32;
+constexpr int kQThreads = 512;
+constexpr int kQDepth = 8;           // stages of loads in flight (a register ring)
+constexpr int kGemmMinTokens = 32;  // below this the GEMV reads the weights fewer times
+
+// 16-byte K-chunk kc (0..3) of an LDS tile row.  X rows are swizzled by bits
+// 2-3 of the row, code rows by bits 3-4: the codes are written as 4-byte
+// pairs to rows 8 m + c, and those rows must not share banks.
+__device__ __forceinline__ int qoff_a(int row, int kc) { return row * kQBK + ((kc ^ ((row >> 2) & 3)) << 3); }
+__device__ __forceinline__ int qoff_b(int row, int kc) { return row * kQBK + ((kc ^ ((row >> 3) & 3)) << 3); }
+
+template <bool Y16>
+__global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
+    const uint16_t* __restrict__ X, int64_t ld_x, int64_t M, int64_t d_in, const uint32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros, int64_t d_out, int group_size,
+    void* __restrict__ Y, int64_t ld_y) {
+  __shared__ __align__(16) uint16_t sA[2][kQBM * kQBK];
+  __shared__ __align__(16) uint16_t sB[2][kQBN * kQBK];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;  // wave tile rows 64 wm.., columns 32 wn..
+  const int64_t n0 = (int64_t)blockIdx.x * kQBN, m0 = (int64_t)blockIdx.y * kQBM;
+  const uint32_t n_words = (uint32_t)(d_out / 8);
+  const int nk = (int)(d_in / kQBK);
+  const int spg = group_size / kQBK;  // stages per quantization group
+  const uint32_t kLoMask = 0x000F000Fu, kHiMask = 0x00F000F0u, kMagic = 0x64006400u;
+  constexpr int kOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+
+  // X: one 16-byte chunk per thread (rows past M read row 0 and store zeros)
+  const int arow = tid >> 2, akc = tid & 3;
+  const bool alive = m0 + arow < M;
+  const uint16_t* xrow = X + (alive ? (m0 + arow) : 0) * ld_x + akc * 8;
+  // codes: word column bm, K rows 2 bp and 2 bp + 1 of the stage (threads 256..511 load the
+  // same words as 0..255, so that every thread issues the same loads, and store nothing);
+  // a column past d_out re-reads the last one: its outputs are never stored
+  const bool bthr = tid < (kQBN / 8) * (kQBK / 2);
+  const int bm = tid & 15, bp = (tid >> 4) & 15;
+  const int64_t wcol = n0 / 8 + bm;
+  const uint32_t wc = wcol < (int64_t)n_words ? (uint32_t)wcol : n_words - 1;
+  const uint32_t* qw0 = qweight + (uint64_t)(2 * bp) * n_words + wc;
+  // zero points: the symmetric layout (qzeros NULL) loads a code word and uses 7
+  const bool has_z = qzeros != nullptr;
+  const uint32_t* zp = has_z ? qzeros + wc : qweight + wc;
+  const uint32_t zstride = has_z ? n_words : 0u;
+  // scale of this lane's output column (1/16 for odd-nibble outputs); past d_out: column 0, unused
+  const int64_t my_col = n0 + wn * 32 + (lane & 31);
+  const bool col_live = my_col < d_out;
+  const float sc_mul = (my_col & 2) ? 0.0625f : 1.0f;
+  const uint16_t* sp = scales + (col_live ? my_col : 0);
+
+  // register ring: slot i holds the global data of stage kt with kt % kQDepth == i.  Every
+  // thread issues the same five loads per stage (stages past the end re-load the last one).
+  uint4 ra[kQDepth];
+  uint32_t rwa[kQDepth], rwb[kQDepth], rz[kQDepth];
+  uint16_t rs[kQDepth];
+  auto issue = [&](int slot, int kt) {
+    const int ktc = kt < nk ? kt : nk - 1;
+    const uint32_t k0 = (uint32_t)ktc * kQBK;
+    const uint32_t g = (uint32_t)(ktc / spg);
+    ra[slot] = *(const uint4*)(xrow + k0);
+    rwa[slot] = qw0[k0 * n_words];
+    rwb[slot] = qw0[(k0 + 1) * n_words];
+    rz[slot] = zp[g * zstride];
+    rs[slot] = sp[(uint64_t)g * d_out];
+  };
+  auto store = [&](int slot, int buf) {
+    *(uint4*)&sA[buf][qoff_a(arow, akc)] = alive ? ra[slot] : make_uint4(0, 0, 0, 0);
+    if (!bthr) return;
+    const uint32_t zw = has_z ? rz[slot] : 0x77777777u;
+    const int k2 = 2 * bp;  // the pair's first K row within the stage
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
+      const uint32_t pb = __builtin_amdgcn_perm(rwb[slot], rwa[slot], sel);  // bytes [rwa.b, 0, rwb.b, 0]
+      const uint32_t ze = 0x64006400u + 0x00010001u * ((zw >> (8 * b)) & 0xFu);      // fp16 1024 + z, both halves
+      const uint32_t zo = 0x64006400u + 0x00100010u * ((zw >> (8 * b + 4)) & 0xFu);  // fp16 1024 + 16 z
+      const h2 ev = __builtin_bit_cast(h2, and_or(pb, kLoMask, kMagic)) - __builtin_bit_cast(h2, ze);
+      const h2 od = __builtin_bit_cast(h2, and_or(pb, kHiMask, kMagic)) - __builtin_bit_cast(h2, zo);
+      const int ne = 8 * bm + kOrder[2 * b], no = 8 * bm + kOrder[2 * b + 1];
+      *(h2*)&sB[buf][qoff_b(ne, k2 >> 3) + (k2 & 7)] = ev;
+      *(h2*)&sB[buf][qoff_b(no, k2 >> 3) + (k2 & 7)] = od;
+    }
+  };
+
+  f32x16 acc[2], accg[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = accg[i][e] = 0.0f;
+
+#pragma unroll
+  for (int i = 0; i < kQDepth; ++i) issue(i, i);
+  store(0, 0);
+  __syncthreads();
+  // stage kt: loads of stage kt + depth into the slot stage kt held; MFMAs on
+  // LDS buffer kt % 2; stage kt + 1 from its slot into the other buffer
+  int kt = 0;
+  auto run_stage = [&](const int i, const bool has_next) {
+    const int buf = i & 1;  // kQDepth is even, so kt % 2 == i % 2
+    const float scv = h2f(rs[i]) * sc_mul;  // this stage's group scale, before the slot is reused
+    issue(i, kt + kQDepth);
+#pragma unroll
+    for (int ks = 0; ks < kQBK / 16; ++ks) {
+      const int kc = 2 * ks + (lane >> 5);
+      uint4 a[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) a[r] = *(const uint4*)&sA[buf][qoff_a(wm * 64 + r * 32 + (lane & 31), kc)];
+      const uint4 bb = *(const uint4*)&sB[buf][qoff_b(wn * 32 + (lane & 31), kc)];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        accg[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[r]),
+                                                         __builtin_bit_cast(f16x8, bb), accg[r], 0, 0, 0);
+    }
+    if ((kt + 1) % spg == 0) {  // the group is complete: scale it into the result
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          acc[r][e] = __builtin_fmaf(accg[r][e], scv, acc[r][e]);
+          accg[r][e] = 0.0f;
+        }
+    }
+    if (has_next) store((i + 1) % kQDepth, buf ^ 1);
+    __syncthreads();
+    ++kt;
+  };
+  // full trips of kQDepth stages, each with a successor: no branch around the
+  // ring's loads, so its registers stay put across trips and the compiler's
+  // in-order waits leave the later stages in flight
+  for (; kt + kQDepth < nk;) {
+#pragma unroll
+    for (int i = 0; i < kQDepth; ++i) run_stage(i, true);
+  }
+#pragma unroll
+  for (int i = 0; i < kQDepth; ++i) {  // the last 1..kQDepth stages
+    if (kt < nk) run_stage(i, kt + 1 < nk);
+  }
+  // lane l holds rows 8 (e / 4) + 4 (l / 32) + e % 4 of column l % 32 of each 32 x 32 tile
+  if (!col_live) return;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t row = m0 + wm * 64 + r * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (row >= M) continue;
+      if constexpr (Y16) ((uint16_t*)Y)[row * ld_y + my_col] = f2h_bits(acc[r][e]);
+      else ((float*)Y)[row * ld_y + my_col] = acc[r][e];
+    }
+}
+
+bool w4a16_uses_gemm(const void* X, int64_t M, int64_t ld_x, int64_t d_in) {
+  return M >= kGemmMinTokens && ((uintptr_t)X & 15u) == 0 && ld_x % 8 == 0 && d_in % kQBK == 0;
+}
+
 hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* qzeros, int64_t d_out, int64_t d_in, int group_size, void* Y, int64_t ld_y,
                         bool y_f16, float* part, hipStream_t stream) {
+  if (w4a16_uses_gemm(X, M, ld_x, d_in)) {
+    const dim3 g((unsigned)((d_out + kQBN - 1) / kQBN), (unsigned)((M + kQBM - 1) / kQBM));
+    if (y_f16)
+      w4a16_gemm_kernel<true><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
+                                                            group_size, Y, ld_y);
+    else
+      w4a16_gemm_kernel<false><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
+                                                             group_size, Y, ld_y);
+    return hipGetLastError();
+  }
   const int64_t n_slices = w4a16_slices(d_in);
   const dim3 grid((unsigned)w4a16_cols(d_out), (unsigned)n_slices);
   for (int64_t t0 = 0; t0 < M; t0 += 4) {

@@ -2,12 +2,16 @@
 depth", "Kernels: why W4A16 is fast at decode").
 
 Packed inputs come from the oracle's pack or from random codes (never from the
-HIP path).  Tolerance, from the arithmetic: products u * x are exact in fp32;
-a wave adds 32 of them and the 32 activations in fp32, folds the zero point
-and the scale (3 roundings), then 4 waves and n_slices row slices are added in
-fp32.  With B = sum_i |x_i| (u_i + z) scale the fp32 result lies within
-2^-24 (32 + 8 + 4 + n_slices) B of the exact product; an fp16 output adds one
-rounding (at most one fp16 ulp here, taken at the larger magnitude)."""
+HIP path).  Tolerance, from the arithmetic, with B = sum_i |x_i| (u_i + z) scale:
+* decode GEMV (fewer than 32 tokens, or X not 16-byte aligned): products u * x
+  are exact in fp32; a wave adds 32 of them and the 32 activations in fp32,
+  folds the zero point and the scale (3 roundings), then 8 waves and n_slices
+  row slices are added in fp32: within 2^-24 (32 + 8 + 8 + n_slices) B;
+* prefill GEMM (32 tokens or more): the matrix cores add G exact products
+  (u - z) x of a group in fp32, one fma applies the scale, d_in / G groups are
+  added: within 2^-24 (G + 2 + d_in / G) B.
+An fp16 output adds one rounding (at most one fp16 ulp, taken at the larger
+magnitude)."""
 import numpy as np
 import pytest
 
@@ -42,17 +46,19 @@ def _dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
 
 
-def _bound(X, qw, sc, qz, d_out, G, n_slices):
+def _bound(X, qw, sc, qz, d_out, G, n_slices, gemm=False):
     u = O.unpack_codes(qw, d_out).astype(F64)                         # [d_out, d_in]
     z = (O.unpack_codes(qz, d_out).astype(F64) if qz is not None
          else np.full((d_out, qw.shape[0] // G), 7.0))
     zz = np.repeat(z, G, axis=1)
     ss = np.repeat(sc.astype(F64).T, G, axis=1)
     B = np.abs(O.decode_activations(X)) @ ((u + zz) * ss).T
-    return 2.0 ** -24 * (32 + 8 + 4 + n_slices) * B
+    d_in = qw.shape[0]
+    return 2.0 ** -24 * ((G + 2 + d_in // G) if gemm else (32 + 8 + 8 + n_slices)) * B
 
 
 def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
+    """The kernel is the GEMM at 32 tokens or more when X rows are 16-byte aligned, else the GEMV."""
     import torch
     M, d_in = X.shape
     Xp = X if ld_x is None else np.pad(X, ((0, 0), (0, ld_x - d_in)))
@@ -64,7 +70,9 @@ def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
     plan = A.W4A16Plan(Xd, _dev_i32(qw), dev_f16(sc), None if qz is None else _dev_i32(qz), d_out, G, tdt, out=out)
     Y = host(plan.run()).astype(F64)
     ref = O.w4a16_matmul(X, qw, sc, qz, d_out, G)
-    tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 127) // 128)
+    ldx = d_in if ld_x is None else ld_x
+    gemm = M >= 32 and ldx % 8 == 0
+    tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 255) // 256, gemm)
     if out_dtype == "f16":
         tol = tol + np.spacing(np.abs(ref).astype(np.float16) * np.float16(1.002)).astype(F64)
     err = np.abs(Y - ref)
@@ -135,3 +143,36 @@ def test_w4a16_deterministic(A):
     a = A.w4a16_matmul(X, _dev_i32(qw), dev_f16(sc), _dev_i32(qz), 4096, 128, torch.float32)
     b = A.w4a16_matmul(X, _dev_i32(qw), dev_f16(sc), _dev_i32(qz), 4096, 128, torch.float32)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("M", [32, 100, 257, 1024])
+@pytest.mark.parametrize("d_out,d_in,G,out_dtype,zeros", [(1032, 384, 64, "f16", True), (520, 256, 32, "f32", False),
+                                                          (4096, 4096, 128, "f16", True)])
+def test_w4a16_prefill_gemm(A, M, d_out, d_in, G, out_dtype, zeros):
+    """Prefill sizes on the matrix cores: ragged token and output tiles, every group size."""
+    say(f"w4a16 gemm M={M} d_out={d_out} d_in={d_in} G={G} {out_dtype}")
+    qw, sc, qz = _random_packed(31 * M + d_out, d_out, d_in, G, zeros)
+    X = (np.random.default_rng(M + 7 * d_in).standard_normal((M, d_in)) * 2).astype(np.float16)
+    _check(A, X, qw, sc, qz, d_out, G, out_dtype)
+
+
+def test_w4a16_prefill_strides_and_fallback(A):
+    say("w4a16 gemm strides; unaligned X falls back to the GEMV")
+    qw, sc, qz = _random_packed(41, 264, 256, 64, True)
+    X = (np.random.default_rng(42).standard_normal((70, 256))).astype(np.float16)
+    _check(A, X, qw, sc, qz, 264, 64, "f32", ld_x=264, ld_y=300)     # GEMM, padded rows
+    _check(A, X, qw, sc, qz, 264, 64, "f16", ld_x=259, ld_y=264)     # rows not 16-byte aligned: GEMV
+
+
+def test_w4a16_prefill_on_oracle_packed_weights(A):
+    say("w4a16 gemm oracle-packed asym")
+    W = WL.make_weight(95, 384, 512)
+    s = (np.exp(np.random.default_rng(96).standard_normal(512) * 0.4)).astype(F32)
+    qw, sc, qz, *_ = O.quantize_pack_asym(W, s, 128)
+    X = WL.make_activations(97, 300, 512, "bf16")
+    Xs = (O.decode_activations(X) / s.astype(F64)).astype(np.float16)
+    Y = _check(A, Xs, qw, sc, qz, 384, 128, "f32")
+    fq = O.fake_quant_asym(W, s, 128)
+    ref = O.decode_activations(X) @ fq.astype(F64).T
+    B2 = np.abs(O.decode_activations(X)) @ np.abs(fq.astype(F64)).T
+    assert np.all(np.abs(Y - ref) <= (2.0 ** -10 + 2.0 ** -20) * B2)
