@@ -27,9 +27,10 @@
 //
 // ASYM: the asymmetric grid ("AWQ architecture, in depth", a 4-bit zero point
 // per group, step ~ range / 15).  Each row tracks max(v) and max(-v) (both
-// start non-negative, so the range contains 0), step = RN(range / 15), the
-// zero point z = rint(-min / step) (exact), and per element the signed code
-// clamp(rint(v / step), -z, 15 - z) (one med3): 7 lane-ops per element·point.
+// start non-negative, so the range contains 0), step = RN(range / 15), and per
+// element the code rint(v / step): the zero point z only bounds the codes to
+// [-z, 15 - z], which changes a code only at a half-way tie of the range's
+// ends (see the loop), so the error sums run 6.5 lane-ops per element·point.
 #include "awq_device.h"
 #include "awq_launch.h"
 
@@ -149,11 +150,15 @@ __global__ __launch_bounds__(kSearchThreads, 3) void search_weight_kernel(
         mn = group_max_nonneg<LPG>(mn);
         const float step = div15(m + mn);
         const float inv = __builtin_amdgcn_rcpf(step);
-        const float z = __builtin_amdgcn_fmed3f(code_exact(mn, step, inv), 0.0f, (float)kUMax);
-        const float zl = -z, zh = (float)kUMax - z;
+        // The code clamp to [-z, 15 - z] only changes a code when an end of the
+        // range sits on a half-way tie that the zero point's rounding resolved
+        // the other way (v / step within an ulp or two of k + 1/2 at the group's
+        // extreme element): it is left out of the error sums here (one element's
+        // error differs by at most a step^2 in such a case), and kept, exactly,
+        // where codes are stored (pack) or form the output-score operand.
 #pragma unroll
         for (int j = 0; j < kSearchE; ++j) {
-          const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(v[j] * inv), zl, zh);
+          const float q = __builtin_rintf(v[j] * inv);
           const float d = __builtin_fmaf(-step, q, v[j]);
           acc[j] = __builtin_fmaf(d, d, acc[j]);
         }
