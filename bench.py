@@ -61,11 +61,11 @@ SEARCH_OPS_PER_ELEM_PT_ASYM = 7
 FETCH_CAL, WRITE_CAL = 2.0, 1.0
 PMC_TRAFFIC = {
     ("search_weight_kernel", "q_proj_4096x4096"): {
-        "fetch_kib": 16756.4, "write_kib": 640.0,
+        "fetch_kib": 16758.4, "write_kib": 640.0,
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
-        "sha256": "a50efc3064248ff2a52008c134db172bb304f7eb4089c634d900bf16206b9b13"},
+        "sha256": "defe0c2e9940a8e54a9e9e972d928a3348712ea21d6d59d02dfc4e145d6bede3"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11797502.5, "write_kib": 30720.0,
+        "fetch_kib": 11797680.2, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
         "sha256": "694cb7a3b501509768c9ce468c13db421cf19ad44e50f1b2f92caf9c141469fb"},
 }

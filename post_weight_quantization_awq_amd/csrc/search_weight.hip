@@ -48,6 +48,16 @@ constexpr float kTinyMax = 0x1p-100f;
 template <int G>
 constexpr int search_rows_per_block() { return (kSearchThreads / (G / kSearchE)) * kSearchR; }
 
+// rint(v * inv) for |v * inv| < 2^22: fma(v, inv, 1.5 * 2^23) rounds the exact
+// product to an integer (the sum's ulp is 1; ties to even, 1.5 * 2^23 being
+// even), and subtracting 1.5 * 2^23 is exact.  Two dual-issue operations in
+// place of a multiply and the single-pipe round (measured 2% faster on the
+// sweep); it differs from rint(RN(v * inv)) only when the rounding of the
+// product would cross a half-way point.
+__device__ __forceinline__ float round_scaled(float v, float inv) {
+  return __builtin_fmaf(v, inv, 12582912.0f) - 12582912.0f;
+}
+
 template <int G, bool ASYM>
 __global__ __launch_bounds__(kSearchThreads, 3) void search_weight_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int n_grid, const float* __restrict__ S,
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(kSearchThreads, 3) void search_weight_kernel(
         // where codes are stored (pack) or form the output-score operand.
 #pragma unroll
         for (int j = 0; j < kSearchE; ++j) {
-          const float q = __builtin_rintf(v[j] * inv);
+          const float q = round_scaled(v[j], inv);
           const float d = __builtin_fmaf(-step, q, v[j]);
           acc[j] = __builtin_fmaf(d, d, acc[j]);
         }
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(kSearchThreads, 3) void search_weight_kernel(
         const float inv = __builtin_amdgcn_rcpf(step);
 #pragma unroll
         for (int j = 0; j < kSearchE; ++j) {
-          const float q = __builtin_rintf(v[j] * inv);
+          const float q = round_scaled(v[j], inv);
           const float d = __builtin_fmaf(-step, q, v[j]);
           acc[j] = __builtin_fmaf(d, d, acc[j]);
         }
