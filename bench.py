@@ -723,8 +723,8 @@ def bench_w4a16(args):
 
     tot_b = sum(alg_bytes(d_out, d_in) for *_, d_out, d_in in layers)
     achieved = tot_b / (sum(call_ms) * 1e-3) / 1e9
-    # 32 tokens or more run the matrix-core GEMM: quoted against the fp16 MFMA peak
-    gemm = M >= 32
+    # 9 tokens or more run the matrix-core GEMM: quoted against the fp16 MFMA peak
+    gemm = M >= 9
     tflops = 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (sum(call_ms) * 1e-3) / 1e12
     kinds = {}
     for (qw, sc, qz, x, y, d_out, d_in), t in zip(layers, call_ms):
@@ -745,7 +745,8 @@ def bench_w4a16(args):
         "per_shape_GBps": {k: v[1] / (v[0] * 1e-3) / 1e9 for k, v in kinds.items()},
         "per_shape_us": {k: 1e3 * v[0] / v[2] for k, v in kinds.items()},
         "roofline": ({"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": None, "kernel": "w4a16_gemm_kernel"}
+                      "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
+                      "kernel": "w4a16_gemm_kernel (+ w4a16_reduce_kernel where K is split, per call)"}
                      if gemm else
                      {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": achieved / HBM_PEAK_GBPS, "traffic": None,

@@ -316,13 +316,16 @@ awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, co
  * 16-byte aligned.  Y: [M, ld_y] of y_dtype (AWQ_F16, rounded to nearest even
  * once, or AWQ_F32), ld_y >= d_out and a multiple of 4, 8-byte (fp16) or
  * 16-byte (fp32) aligned.  d_out % 8 == 0, d_in % group_size == 0.
- * Arithmetic: fewer than 32 tokens (or X rows not 16-byte aligned, or d_in
- * not a multiple of 128): the decode GEMV -- u * x exact in fp32, fp32 sums
- * over 32 input rows, then the zero point and scale, then fixed-order fp32
- * sums, tokens 4 at a time (the weights are read once per 4 tokens).  32
- * tokens or more: the matrix-core GEMM -- exact fp16 (u - z) times X
- * accumulated in fp32 per quantization group, times the fp32 scale, groups
- * added in order.  Both are deterministic.
+ * Arithmetic: fewer than 9 tokens (or X rows not 16-byte aligned, ld_x not a
+ * multiple of 8, or d_in not a multiple of 32): the decode GEMV -- u * x
+ * exact in fp32, fp32 sums over 32 input rows, then the zero point and scale,
+ * then fixed-order fp32 sums, tokens 4 at a time (the weights are read once
+ * per 4 tokens).  9 tokens or more: the matrix-core GEMM -- exact fp16
+ * (u - z) times X accumulated in fp32 per quantization group, times the fp32
+ * scale, groups added in order; when the 128 x 128 output tiles are fewer
+ * than the compute units, K is cut at multiples of 128 inputs into up to 8
+ * ranges whose fp32 results are added in range order.  Both are
+ * deterministic.
  * ws: awq_w4a16_workspace(M, d_out, d_in) bytes, 256-byte aligned.  M = 0 or
  * d_out = 0 returns AWQ_OK at once.
  * ------------------------------------------------------------------------- */

@@ -484,7 +484,9 @@ static int w4a16_mt(int64_t M) { return M >= 3 ? 4 : (int)M; }
 awq_status awq_w4a16_workspace(int64_t M, int64_t d_out, int64_t d_in, size_t* bytes) {
   if (!bytes) return fail(AWQ_EINVAL, "bytes is NULL");
   if (M < 0 || d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
-  *bytes = align256((size_t)w4a16_slices(d_in) * (size_t)w4a16_mt(M) * (size_t)d_out * sizeof(float));
+  const size_t gemv = (size_t)w4a16_slices(d_in) * (size_t)w4a16_mt(M) * (size_t)d_out;
+  const size_t gemm = (size_t)w4a16_gemm_part_floats(M, d_out, d_in);
+  *bytes = align256((gemv > gemm ? gemv : gemm) * sizeof(float));
   return ok();
 }
 

@@ -87,6 +87,8 @@ hipError_t launch_unpack_dequant(const int32_t* qweight, const uint16_t* scales,
 // ld_y) = X [M, d_in] (fp16, row stride ld_x) W_hat^T; part: fp32 scratch of
 // w4a16_slices(d_in) * min(4, M rounded up to 1, 2, 4) * d_out floats
 int64_t w4a16_slices(int64_t d_in);
+// floats of the prefill GEMM's K-split partials (0 when it runs unsplit or M is below the GEMM's range)
+int64_t w4a16_gemm_part_floats(int64_t M, int64_t d_out, int64_t d_in);
 int64_t w4a16_cols(int64_t d_out);
 hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* qzeros, int64_t d_out, int64_t d_in, int group_size, void* Y, int64_t ld_y,

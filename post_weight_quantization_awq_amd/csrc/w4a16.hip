@@ -237,7 +237,10 @@ int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 // compute-bound and dequantization is extra work).  Block tile 128 tokens x
 // 128 outputs, 8 waves of 64 x 32 (2 x 1 v_mfma_f32_32x32x16_f16; a group's
 // own accumulators and the result's fit 2 waves per SIMD), K in stages of 32
-// through two LDS buffers.  X goes to LDS as it is; the codes are
+// through a ring of four LDS buffers: a stage's tiles are stored two stages
+// ahead of its MFMAs and its fragments read one stage ahead, so neither the
+// stores nor the fragment reads sit between a barrier and the MFMAs that
+// follow it (2% faster than two buffers).  X goes to LDS as it is; the codes are
 // dequantized on their way to LDS into exact fp16 (u - z): two K rows at a
 // time, one byte permute puts the same byte of both rows side by side, one
 // and-or makes 1024 + u (even nibbles) or 1024 + 16 u (odd nibbles) and one
@@ -251,7 +254,10 @@ int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 constexpr int kQBM = 128, kQBN = 128, kQBK = 32;
 constexpr int kQThreads = 512;
 constexpr int kQDepth = 8;           // stages of loads in flight (a register ring)
-constexpr int kGemmMinTokens = 32;  // below this the GEMV reads the weights fewer times
+constexpr int kQBufs = 4;            // LDS stage buffers: stores run two stages ahead of the MFMAs
+// from 9 tokens on, one 128-token tile (split over K when the tile grid is small)
+// costs less than the three or more passes of the 4-token GEMV
+constexpr int kGemmMinTokens = 9;
 
 // 16-byte K-chunk kc (0..3) of an LDS tile row.  X rows are swizzled by bits
 // 2-3 of the row, code rows by bits 3-4: the codes are written as 4-byte
@@ -263,40 +269,43 @@ template <bool Y16>
 __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ld_x, int64_t M, int64_t d_in, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros, int64_t d_out, int group_size,
-    void* __restrict__ Y, int64_t ld_y) {
-  __shared__ __align__(16) uint16_t sA[2][kQBM * kQBK];
-  __shared__ __align__(16) uint16_t sB[2][kQBN * kQBK];
+    void* __restrict__ Y, int64_t ld_y, int split_stages, float* __restrict__ part) {
+  __shared__ __align__(16) uint16_t sA[kQBufs][kQBM * kQBK];
+  __shared__ __align__(16) uint16_t sB[kQBufs][kQBN * kQBK];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // wave tile rows 64 wm.., columns 32 wn..
   const int64_t n0 = (int64_t)blockIdx.x * kQBN, m0 = (int64_t)blockIdx.y * kQBM;
   const uint32_t n_words = (uint32_t)(d_out / 8);
-  const int nk = (int)(d_in / kQBK);
+  // K split z covers stages [z * split_stages, ...): a multiple of every group's stage count
+  const int ks0 = (int)blockIdx.z * split_stages;
+  const int nk = min((int)(d_in / kQBK) - ks0, split_stages);
   const int spg = group_size / kQBK;  // stages per quantization group
+  const int64_t g0 = ks0 / spg;       // first group of the split
   const uint32_t kLoMask = 0x000F000Fu, kHiMask = 0x00F000F0u, kMagic = 0x64006400u;
   constexpr int kOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 
   // X: one 16-byte chunk per thread (rows past M read row 0 and store zeros)
   const int arow = tid >> 2, akc = tid & 3;
   const bool alive = m0 + arow < M;
-  const uint16_t* xrow = X + (alive ? (m0 + arow) : 0) * ld_x + akc * 8;
-  // codes: word column bm, K rows 2 bp and 2 bp + 1 of the stage (threads 256..511 load the
-  // same words as 0..255, so that every thread issues the same loads, and store nothing);
-  // a column past d_out re-reads the last one: its outputs are never stored
-  const bool bthr = tid < (kQBN / 8) * (kQBK / 2);
+  const uint16_t* xrow = X + (alive ? (m0 + arow) : 0) * ld_x + akc * 8 + (int64_t)ks0 * kQBK;
+  // codes: word column bm, K rows 2 bp and 2 bp + 1 of the stage; threads 0..255 expand bytes
+  // 0-1 of the two words, threads 256..511 bytes 2-3 (both halves load the same words); a
+  // column past d_out re-reads the last one: its outputs are never stored
   const int bm = tid & 15, bp = (tid >> 4) & 15;
+  const int bh = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int64_t wcol = n0 / 8 + bm;
   const uint32_t wc = wcol < (int64_t)n_words ? (uint32_t)wcol : n_words - 1;
-  const uint32_t* qw0 = qweight + (uint64_t)(2 * bp) * n_words + wc;
+  const uint32_t* qw0 = qweight + (uint64_t)(2 * bp + ks0 * kQBK) * n_words + wc;
   // zero points: the symmetric layout (qzeros NULL) loads a code word and uses 7
   const bool has_z = qzeros != nullptr;
-  const uint32_t* zp = has_z ? qzeros + wc : qweight + wc;
+  const uint32_t* zp = has_z ? qzeros + (uint64_t)g0 * n_words + wc : qweight + wc;
   const uint32_t zstride = has_z ? n_words : 0u;
   // scale of this lane's output column (1/16 for odd-nibble outputs); past d_out: column 0, unused
   const int64_t my_col = n0 + wn * 32 + (lane & 31);
   const bool col_live = my_col < d_out;
   const float sc_mul = (my_col & 2) ? 0.0625f : 1.0f;
-  const uint16_t* sp = scales + (col_live ? my_col : 0);
+  const uint16_t* sp = scales + g0 * d_out + (col_live ? my_col : 0);
 
   // register ring: slot i holds the global data of stage kt with kt % kQDepth == i.  Every
   // thread issues the same five loads per stage (stages past the end re-load the last one).
@@ -315,11 +324,11 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
   };
   auto store = [&](int slot, int buf) {
     *(uint4*)&sA[buf][qoff_a(arow, akc)] = alive ? ra[slot] : make_uint4(0, 0, 0, 0);
-    if (!bthr) return;
     const uint32_t zw = has_z ? rz[slot] : 0x77777777u;
     const int k2 = 2 * bp;  // the pair's first K row within the stage
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * bh + bb;
       const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
       const uint32_t pb = __builtin_amdgcn_perm(rwb[slot], rwa[slot], sel);  // bytes [rwa.b, 0, rwb.b, 0]
       const uint32_t ze = 0x64006400u + 0x00010001u * ((zw >> (8 * b)) & 0xFu);      // fp16 1024 + z, both halves
@@ -340,27 +349,40 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
 
 #pragma unroll
   for (int i = 0; i < kQDepth; ++i) issue(i, i);
-  store(0, 0);
-  __syncthreads();
-  // stage kt: loads of stage kt + depth into the slot stage kt held; MFMAs on
-  // LDS buffer kt % 2; stage kt + 1 from its slot into the other buffer
-  int kt = 0;
-  auto run_stage = [&](const int i, const bool has_next) {
-    const int buf = i & 1;  // kQDepth is even, so kt % 2 == i % 2
-    const float scv = h2f(rs[i]) * sc_mul;  // this stage's group scale, before the slot is reused
-    issue(i, kt + kQDepth);
+  // fragments of one stage: per 16-deep K step, two X rows blocks and one code block
+  struct Frags {
+    uint4 a[2][2], b[2];
+  };
+  auto load_frags = [&](Frags& f, int buf) {
 #pragma unroll
     for (int ks = 0; ks < kQBK / 16; ++ks) {
       const int kc = 2 * ks + (lane >> 5);
-      uint4 a[2];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) a[r] = *(const uint4*)&sA[buf][qoff_a(wm * 64 + r * 32 + (lane & 31), kc)];
-      const uint4 bb = *(const uint4*)&sB[buf][qoff_b(wn * 32 + (lane & 31), kc)];
+      for (int r = 0; r < 2; ++r) f.a[ks][r] = *(const uint4*)&sA[buf][qoff_a(wm * 64 + r * 32 + (lane & 31), kc)];
+      f.b[ks] = *(const uint4*)&sB[buf][qoff_b(wn * 32 + (lane & 31), kc)];
+    }
+  };
+  store(0, 0);
+  if (nk > 1) store(1, 1);
+  __syncthreads();
+  Frags fr[2];
+  load_frags(fr[0], 0);
+  // stage kt (ring slot i = kt % kQDepth, LDS buffer kt % kQBufs, fragments fr[kt % 2]):
+  // loads of stage kt + depth into slot i; fragment reads of stage kt + 1 (stored two
+  // stages back, visible since the last barrier); MFMAs of stage kt; stage kt + 2 from
+  // its slot into its buffer, whose last reads (stage kt - 2) ended before the last barrier
+  int kt = 0;
+  auto run_stage = [&](const int i, const bool has_next, const bool has_next2) {
+    const float scv = h2f(rs[i]) * sc_mul;  // this stage's group scale, before the slot is reused
+    issue(i, kt + kQDepth);
+    if (has_next) load_frags(fr[(i + 1) & 1], (i + 1) % kQBufs);
+    const Frags& f = fr[i & 1];
+#pragma unroll
+    for (int ks = 0; ks < kQBK / 16; ++ks)
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        accg[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[r]),
-                                                         __builtin_bit_cast(f16x8, bb), accg[r], 0, 0, 0);
-    }
+        accg[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, f.a[ks][r]),
+                                                         __builtin_bit_cast(f16x8, f.b[ks]), accg[r], 0, 0, 0);
     if ((kt + 1) % spg == 0) {  // the group is complete: scale it into the result
 #pragma unroll
       for (int r = 0; r < 2; ++r)
@@ -370,20 +392,21 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
           accg[r][e] = 0.0f;
         }
     }
-    if (has_next) store((i + 1) % kQDepth, buf ^ 1);
+    if (has_next2) store((i + 2) % kQDepth, (i + 2) % kQBufs);
     __syncthreads();
     ++kt;
   };
-  // full trips of kQDepth stages, each with a successor: no branch around the
+  // full trips of kQDepth stages, each with two successors: no branch around the
   // ring's loads, so its registers stay put across trips and the compiler's
-  // in-order waits leave the later stages in flight
-  for (; kt + kQDepth < nk;) {
+  // in-order waits leave the later stages in flight (kQDepth is a multiple of
+  // kQBufs and of 2, so slot, buffer and fragment set follow i)
+  for (; kt + kQDepth + 1 < nk;) {
 #pragma unroll
-    for (int i = 0; i < kQDepth; ++i) run_stage(i, true);
+    for (int i = 0; i < kQDepth; ++i) run_stage(i, true, true);
   }
 #pragma unroll
-  for (int i = 0; i < kQDepth; ++i) {  // the last 1..kQDepth stages
-    if (kt < nk) run_stage(i, kt + 1 < nk);
+  for (int i = 0; i < kQDepth + 1; ++i) {  // the last 2..kQDepth + 1 stages
+    if (kt < nk) run_stage(i % kQDepth, kt + 1 < nk, kt + 2 < nk);
   }
   // lane l holds rows 8 (e / 4) + 4 (l / 32) + e % 4 of column l % 32 of each 32 x 32 tile
   if (!col_live) return;
@@ -393,9 +416,33 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
     for (int e = 0; e < 16; ++e) {
       const int64_t row = m0 + wm * 64 + r * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       if (row >= M) continue;
-      if constexpr (Y16) ((uint16_t*)Y)[row * ld_y + my_col] = f2h_bits(acc[r][e]);
+      if (part != nullptr) part[((int64_t)blockIdx.z * M + row) * d_out + my_col] = acc[r][e];
+      else if constexpr (Y16) ((uint16_t*)Y)[row * ld_y + my_col] = f2h_bits(acc[r][e]);
       else ((float*)Y)[row * ld_y + my_col] = acc[r][e];
     }
+}
+
+// K splits of the GEMM, so that a small tile grid still gives every compute
+// unit a block (one block per CU): split boundaries fall on multiples of 128
+// inputs (a group boundary at every group size); at most 8 splits and at most
+// half as many as there are 128-input units.  The split partials [z][M][d_out]
+// are added in split order by the reduction kernel.
+static int gemm_split_stages(int64_t M, int64_t d_out, int64_t d_in) {
+  const int nk = (int)(d_in / kQBK);
+  const int64_t tiles = ((d_out + kQBN - 1) / kQBN) * ((M + kQBM - 1) / kQBM);
+  const int units = (nk + 3) / 4;  // 128-input units, the last one possibly partial
+  int64_t s = (256 + tiles - 1) / tiles;
+  s = s < 8 ? s : 8;
+  s = s < units / 2 ? s : units / 2;
+  if (s <= 1) return nk;
+  return (int)((units + s - 1) / s) * 4;
+}
+
+int64_t w4a16_gemm_part_floats(int64_t M, int64_t d_out, int64_t d_in) {
+  if (M < kGemmMinTokens || d_in % kQBK) return 0;
+  const int nk = (int)(d_in / kQBK), ss = gemm_split_stages(M, d_out, d_in);
+  const int64_t n_split = (nk + ss - 1) / ss;
+  return n_split > 1 ? n_split * M * d_out : 0;
 }
 
 bool w4a16_uses_gemm(const void* X, int64_t M, int64_t ld_x, int64_t d_in) {
@@ -406,13 +453,21 @@ hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32
                         const uint32_t* qzeros, int64_t d_out, int64_t d_in, int group_size, void* Y, int64_t ld_y,
                         bool y_f16, float* part, hipStream_t stream) {
   if (w4a16_uses_gemm(X, M, ld_x, d_in)) {
-    const dim3 g((unsigned)((d_out + kQBN - 1) / kQBN), (unsigned)((M + kQBM - 1) / kQBM));
+    const int nk = (int)(d_in / kQBK), ss = gemm_split_stages(M, d_out, d_in);
+    const int n_split = (nk + ss - 1) / ss;
+    float* gp = n_split > 1 ? part : nullptr;
+    const dim3 g((unsigned)((d_out + kQBN - 1) / kQBN), (unsigned)((M + kQBM - 1) / kQBM), (unsigned)n_split);
     if (y_f16)
       w4a16_gemm_kernel<true><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
-                                                            group_size, Y, ld_y);
+                                                            group_size, Y, ld_y, ss, gp);
     else
       w4a16_gemm_kernel<false><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
-                                                             group_size, Y, ld_y);
+                                                             group_size, Y, ld_y, ss, gp);
+    if (n_split > 1) {
+      const dim3 rgrid((unsigned)((d_out / 4 + kRdCols - 1) / kRdCols), (unsigned)M);
+      w4a16_reduce_kernel<<<rgrid, kRdCols * kRdSplit, 0, stream>>>(part, n_split, (int)M, d_out, Y, ld_y,
+                                                                    y_f16 ? 1 : 0);
+    }
     return hipGetLastError();
   }
   const int64_t n_slices = w4a16_slices(d_in);

@@ -3,13 +3,15 @@ depth", "Kernels: why W4A16 is fast at decode").
 
 Packed inputs come from the oracle's pack or from random codes (never from the
 HIP path).  Tolerance, from the arithmetic, with B = sum_i |x_i| (u_i + z) scale:
-* decode GEMV (fewer than 32 tokens, or X not 16-byte aligned): products u * x
+* decode GEMV (fewer than 9 tokens, or X not 16-byte aligned): products u * x
   are exact in fp32; a wave adds 32 of them and the 32 activations in fp32,
   folds the zero point and the scale (3 roundings), then 8 waves and n_slices
   row slices are added in fp32: within 2^-24 (32 + 8 + 8 + n_slices) B;
-* prefill GEMM (32 tokens or more): the matrix cores add G exact products
+* prefill GEMM (9 tokens or more): the matrix cores add G exact products
   (u - z) x of a group in fp32, one fma applies the scale, d_in / G groups are
-  added: within 2^-24 (G + 2 + d_in / G) B.
+  added: within 2^-24 (G + 2 + d_in / G) B.  Split over K into S ranges of
+  at least two 128-input units, a range adds at most d_in / G / S + 1 groups
+  and S range results are added after it, which stays within the same count.
 An fp16 output adds one rounding (at most one fp16 ulp, taken at the larger
 magnitude)."""
 import numpy as np
@@ -58,7 +60,7 @@ def _bound(X, qw, sc, qz, d_out, G, n_slices, gemm=False):
 
 
 def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
-    """The kernel is the GEMM at 32 tokens or more when X rows are 16-byte aligned, else the GEMV."""
+    """The kernel is the GEMM at 9 tokens or more when X rows are 16-byte aligned, else the GEMV."""
     import torch
     M, d_in = X.shape
     Xp = X if ld_x is None else np.pad(X, ((0, 0), (0, ld_x - d_in)))
@@ -71,7 +73,7 @@ def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
     Y = host(plan.run()).astype(F64)
     ref = O.w4a16_matmul(X, qw, sc, qz, d_out, G)
     ldx = d_in if ld_x is None else ld_x
-    gemm = M >= 32 and ldx % 8 == 0
+    gemm = M >= 9 and ldx % 8 == 0
     tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 255) // 256, gemm)
     if out_dtype == "f16":
         tol = tol + np.spacing(np.abs(ref).astype(np.float16) * np.float16(1.002)).astype(F64)
@@ -145,7 +147,7 @@ def test_w4a16_deterministic(A):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("M", [32, 100, 257, 1024])
+@pytest.mark.parametrize("M", [9, 32, 100, 257, 1024])
 @pytest.mark.parametrize("d_out,d_in,G,out_dtype,zeros", [(1032, 384, 64, "f16", True), (520, 256, 32, "f32", False),
                                                           (4096, 4096, 128, "f16", True)])
 def test_w4a16_prefill_gemm(A, M, d_out, d_in, G, out_dtype, zeros):
@@ -154,6 +156,18 @@ def test_w4a16_prefill_gemm(A, M, d_out, d_in, G, out_dtype, zeros):
     qw, sc, qz = _random_packed(31 * M + d_out, d_out, d_in, G, zeros)
     X = (np.random.default_rng(M + 7 * d_in).standard_normal((M, d_in)) * 2).astype(np.float16)
     _check(A, X, qw, sc, qz, d_out, G, out_dtype)
+
+
+@pytest.mark.parametrize("M,d_out,d_in,G,out_dtype,ld_y", [(64, 1032, 2112, 64, "f16", 1040),
+                                                           (40, 520, 1056, 32, "f32", 520),
+                                                           (300, 264, 4096, 128, "f32", 272)])
+def test_w4a16_prefill_split_k(A, M, d_out, d_in, G, out_dtype, ld_y):
+    """Small tile grids split K over several blocks (6, 3 and 8 splits here, the last
+    ones shorter) and add the split partials in order."""
+    say(f"w4a16 gemm split-K M={M} d_out={d_out} d_in={d_in} G={G} {out_dtype} ld_y={ld_y}")
+    qw, sc, qz = _random_packed(53 * M + d_in, d_out, d_in, G, True)
+    X = (np.random.default_rng(M + d_out).standard_normal((M, d_in))).astype(np.float16)
+    _check(A, X, qw, sc, qz, d_out, G, out_dtype, ld_y=ld_y)
 
 
 def test_w4a16_prefill_strides_and_fallback(A):
