@@ -340,8 +340,9 @@ awq_status awq_w4a16_matmul(const void* X, int64_t M, int64_t ld_x, const int32_
  * void*, created by the caller) on the call's stream immediately around its
  * main kernel launches: the partial-sum kernel of awq_act_stats; the search
  * kernel (weight score) or the chunked dW-build + GEMM launches (output score)
- * of awq_search_scales; the pack kernel of awq_quantize_pack.  Pass NULL, NULL
- * to clear.  The library records the events and nothing else.
+ * of awq_search_scales; the pack kernel of awq_quantize_pack; every launch of
+ * awq_w4a16_matmul (GEMV or GEMM and, where used, the reduction).  Pass NULL,
+ * NULL to clear.  The library records the events and nothing else.
  * ------------------------------------------------------------------------- */
 awq_status awq_set_timing_events(void* before, void* after);
 
