@@ -322,10 +322,10 @@ awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, co
  * then fixed-order fp32 sums, tokens 4 at a time (the weights are read once
  * per 4 tokens).  9 tokens or more: the matrix-core GEMM -- exact fp16
  * (u - z) times X accumulated in fp32 per quantization group, times the fp32
- * scale, groups added in order; when the 128 x 128 output tiles are fewer
- * than the compute units, K is cut at multiples of 128 inputs into up to 8
- * ranges whose fp32 results are added in range order.  Both are
- * deterministic.
+ * scale, groups added in order; when the output tiles (256 tokens x 128
+ * outputs, or 128 x 128 for at most 128 tokens) are fewer than the compute
+ * units, K is cut at multiples of 128 inputs into up to 8 ranges whose fp32
+ * results are added in range order.  Both are deterministic.
  * ws: awq_w4a16_workspace(M, d_out, d_in) bytes, 256-byte aligned.  M = 0 or
  * d_out = 0 returns AWQ_OK at once.
  * ------------------------------------------------------------------------- */

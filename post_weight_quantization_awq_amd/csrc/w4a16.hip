@@ -234,13 +234,14 @@ int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 // ---------------------------------------------------------------------------
 // Prefill: the W4A16 GEMM on the matrix cores ("AWQ architecture, in depth",
 // "Kernels: why W4A16 is fast at decode": at prefill sizes the product is
-// compute-bound and dequantization is extra work).  Block tile 128 tokens x
-// 128 outputs, 8 waves of 64 x 32 (2 x 1 v_mfma_f32_32x32x16_f16; a group's
-// own accumulators and the result's fit 2 waves per SIMD), K in stages of 32
-// through a ring of four LDS buffers: a stage's tiles are stored two stages
-// ahead of its MFMAs and its fragments read one stage ahead, so neither the
-// stores nor the fragment reads sit between a barrier and the MFMAs that
-// follow it (2% faster than two buffers).  X goes to LDS as it is; the codes are
+// compute-bound and dequantization is extra work).  Block tile 256 tokens x
+// 128 outputs, 8 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_f16), or for at
+// most 128 tokens 128 x 128 with 8 waves of 64 x 32; a group's own
+// accumulators and the result's fit 2 waves per SIMD.  K goes in stages of 32
+// through a ring of four LDS buffers, a stage's tiles stored two stages ahead
+// of its MFMAs.  The larger tile does twice the matrix-core work per
+// dequantized code and per barrier (1.27x faster at 2048 tokens).  X goes to
+// LDS as it is; the codes are
 // dequantized on their way to LDS into exact fp16 (u - z): two K rows at a
 // time, one byte permute puts the same byte of both rows side by side, one
 // and-or makes 1024 + u (even nibbles) or 1024 + 16 u (odd nibbles) and one
@@ -251,9 +252,8 @@ int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 // a dequantized weight.  16-byte K-chunks of an LDS tile row are swizzled by
 // the row so that fragment reads are conflict-free.
 // ---------------------------------------------------------------------------
-constexpr int kQBM = 128, kQBN = 128, kQBK = 32;
+constexpr int kQBN = 128, kQBK = 32;
 constexpr int kQThreads = 512;
-constexpr int kQDepth = 8;           // stages of loads in flight (a register ring)
 constexpr int kQBufs = 4;            // LDS stage buffers: stores run two stages ahead of the MFMAs
 // from 9 tokens on, one 128-token tile (split over K when the tile grid is small)
 // costs less than the three or more passes of the 4-token GEMV
@@ -265,17 +265,21 @@ constexpr int kGemmMinTokens = 9;
 __device__ __forceinline__ int qoff_a(int row, int kc) { return row * kQBK + ((kc ^ ((row >> 2) & 3)) << 3); }
 __device__ __forceinline__ int qoff_b(int row, int kc) { return row * kQBK + ((kc ^ ((row >> 3) & 3)) << 3); }
 
-template <bool Y16>
+template <bool Y16, int BM>
 __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ld_x, int64_t M, int64_t d_in, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros, int64_t d_out, int group_size,
     void* __restrict__ Y, int64_t ld_y, int split_stages, float* __restrict__ part) {
-  __shared__ __align__(16) uint16_t sA[kQBufs][kQBM * kQBK];
+  constexpr int WM = BM / 64, WN = 8 / WM;  // waves along tokens and outputs
+  constexpr int NC = kQBN / WN / 32;         // 32-column tiles per wave (1 or 2)
+  constexpr int XC = BM / 128;               // X chunks per thread and stage
+  constexpr int kQDepth = BM == 128 ? 8 : 4;  // stages of loads in flight: the register ring fits 2 waves per SIMD
+  __shared__ __align__(16) uint16_t sA[kQBufs][BM * kQBK];
   __shared__ __align__(16) uint16_t sB[kQBufs][kQBN * kQBK];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;  // wave tile rows 64 wm.., columns 32 wn..
-  const int64_t n0 = (int64_t)blockIdx.x * kQBN, m0 = (int64_t)blockIdx.y * kQBM;
+  const int wm = wave / WN, wn = wave % WN;  // wave tile rows 64 wm.., columns 32 NC wn..
+  const int64_t n0 = (int64_t)blockIdx.x * kQBN, m0 = (int64_t)blockIdx.y * BM;
   const uint32_t n_words = (uint32_t)(d_out / 8);
   // K split z covers stages [z * split_stages, ...): a multiple of every group's stage count
   const int ks0 = (int)blockIdx.z * split_stages;
@@ -285,10 +289,15 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
   const uint32_t kLoMask = 0x000F000Fu, kHiMask = 0x00F000F0u, kMagic = 0x64006400u;
   constexpr int kOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 
-  // X: one 16-byte chunk per thread (rows past M read row 0 and store zeros)
+  // X: XC 16-byte chunks per thread, rows arow + 128 x (rows past M read row 0 and store zeros)
   const int arow = tid >> 2, akc = tid & 3;
-  const bool alive = m0 + arow < M;
-  const uint16_t* xrow = X + (alive ? (m0 + arow) : 0) * ld_x + akc * 8 + (int64_t)ks0 * kQBK;
+  bool alive[XC];
+  const uint16_t* xrow[XC];
+#pragma unroll
+  for (int x = 0; x < XC; ++x) {
+    alive[x] = m0 + arow + 128 * x < M;
+    xrow[x] = X + (alive[x] ? (m0 + arow + 128 * x) : 0) * ld_x + akc * 8 + (int64_t)ks0 * kQBK;
+  }
   // codes: word column bm, K rows 2 bp and 2 bp + 1 of the stage; threads 0..255 expand bytes
   // 0-1 of the two words, threads 256..511 bytes 2-3 (both halves load the same words); a
   // column past d_out re-reads the last one: its outputs are never stored
@@ -301,29 +310,38 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
   const bool has_z = qzeros != nullptr;
   const uint32_t* zp = has_z ? qzeros + (uint64_t)g0 * n_words + wc : qweight + wc;
   const uint32_t zstride = has_z ? n_words : 0u;
-  // scale of this lane's output column (1/16 for odd-nibble outputs); past d_out: column 0, unused
-  const int64_t my_col = n0 + wn * 32 + (lane & 31);
-  const bool col_live = my_col < d_out;
-  const float sc_mul = (my_col & 2) ? 0.0625f : 1.0f;
-  const uint16_t* sp = scales + g0 * d_out + (col_live ? my_col : 0);
+  // scales of this lane's NC output columns (32 apart, so alike in taking 1/16 for the
+  // odd-nibble outputs); past d_out: column 0, unused
+  int64_t my_col[NC];
+  const uint16_t* sp[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    my_col[c] = n0 + wn * 32 * NC + c * 32 + (lane & 31);
+    sp[c] = scales + g0 * d_out + (my_col[c] < d_out ? my_col[c] : 0);
+  }
+  const float sc_mul = (my_col[0] & 2) ? 0.0625f : 1.0f;
 
   // register ring: slot i holds the global data of stage kt with kt % kQDepth == i.  Every
-  // thread issues the same five loads per stage (stages past the end re-load the last one).
-  uint4 ra[kQDepth];
+  // thread issues the same loads per stage (stages past the end re-load the last one).
+  uint4 ra[kQDepth][XC];
   uint32_t rwa[kQDepth], rwb[kQDepth], rz[kQDepth];
-  uint16_t rs[kQDepth];
+  uint16_t rs[kQDepth][NC];
   auto issue = [&](int slot, int kt) {
     const int ktc = kt < nk ? kt : nk - 1;
     const uint32_t k0 = (uint32_t)ktc * kQBK;
     const uint32_t g = (uint32_t)(ktc / spg);
-    ra[slot] = *(const uint4*)(xrow + k0);
+#pragma unroll
+    for (int x = 0; x < XC; ++x) ra[slot][x] = *(const uint4*)(xrow[x] + k0);
     rwa[slot] = qw0[k0 * n_words];
     rwb[slot] = qw0[(k0 + 1) * n_words];
     rz[slot] = zp[g * zstride];
-    rs[slot] = sp[(uint64_t)g * d_out];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) rs[slot][c] = sp[c][(uint64_t)g * d_out];
   };
   auto store = [&](int slot, int buf) {
-    *(uint4*)&sA[buf][qoff_a(arow, akc)] = alive ? ra[slot] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < XC; ++x)
+      *(uint4*)&sA[buf][qoff_a(arow + 128 * x, akc)] = alive[x] ? ra[slot][x] : make_uint4(0, 0, 0, 0);
     const uint32_t zw = has_z ? rz[slot] : 0x77777777u;
     const int k2 = 2 * bp;  // the pair's first K row within the stage
 #pragma unroll
@@ -341,56 +359,54 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
     }
   };
 
-  f32x16 acc[2], accg[2];
+  f32x16 acc[2][NC], accg[2][NC];  // [32-row tile][32-column tile]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = accg[i][e] = 0.0f;
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[r][c][e] = accg[r][c][e] = 0.0f;
 
 #pragma unroll
   for (int i = 0; i < kQDepth; ++i) issue(i, i);
-  // fragments of one stage: per 16-deep K step, two X rows blocks and one code block
-  struct Frags {
-    uint4 a[2][2], b[2];
-  };
-  auto load_frags = [&](Frags& f, int buf) {
-#pragma unroll
-    for (int ks = 0; ks < kQBK / 16; ++ks) {
-      const int kc = 2 * ks + (lane >> 5);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) f.a[ks][r] = *(const uint4*)&sA[buf][qoff_a(wm * 64 + r * 32 + (lane & 31), kc)];
-      f.b[ks] = *(const uint4*)&sB[buf][qoff_b(wn * 32 + (lane & 31), kc)];
-    }
-  };
   store(0, 0);
   if (nk > 1) store(1, 1);
   __syncthreads();
-  Frags fr[2];
-  load_frags(fr[0], 0);
-  // stage kt (ring slot i = kt % kQDepth, LDS buffer kt % kQBufs, fragments fr[kt % 2]):
-  // loads of stage kt + depth into slot i; fragment reads of stage kt + 1 (stored two
-  // stages back, visible since the last barrier); MFMAs of stage kt; stage kt + 2 from
-  // its slot into its buffer, whose last reads (stage kt - 2) ended before the last barrier
+  // stage kt (ring slot i = kt % kQDepth, LDS buffer kt % kQBufs): loads of stage
+  // kt + depth into slot i; fragment reads and MFMAs of stage kt; stage kt + 2 from its
+  // slot into its buffer, whose last reads (stage kt - 2) ended before the last barrier
   int kt = 0;
-  auto run_stage = [&](const int i, const bool has_next, const bool has_next2) {
-    const float scv = h2f(rs[i]) * sc_mul;  // this stage's group scale, before the slot is reused
-    issue(i, kt + kQDepth);
-    if (has_next) load_frags(fr[(i + 1) & 1], (i + 1) % kQBufs);
-    const Frags& f = fr[i & 1];
+  auto run_stage = [&](const int i, const bool has_next2) {
+    float scv[NC];  // this stage's group scales, before the slot is reused
 #pragma unroll
-    for (int ks = 0; ks < kQBK / 16; ++ks)
+    for (int c = 0; c < NC; ++c) scv[c] = h2f(rs[i][c]) * sc_mul;
+    issue(i, kt + kQDepth);
+#pragma unroll
+    for (int ks = 0; ks < kQBK / 16; ++ks) {
+      const int kc = 2 * ks + (lane >> 5);
+      uint4 a[2], b[NC];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) a[r] = *(const uint4*)&sA[i % kQBufs][qoff_a(wm * 64 + r * 32 + (lane & 31), kc)];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        b[c] = *(const uint4*)&sB[i % kQBufs][qoff_b(wn * 32 * NC + c * 32 + (lane & 31), kc)];
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        accg[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, f.a[ks][r]),
-                                                         __builtin_bit_cast(f16x8, f.b[ks]), accg[r], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          accg[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[r]),
+                                                              __builtin_bit_cast(f16x8, b[c]), accg[r][c], 0, 0, 0);
+    }
     if ((kt + 1) % spg == 0) {  // the group is complete: scale it into the result
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          acc[r][e] = __builtin_fmaf(accg[r][e], scv, acc[r][e]);
-          accg[r][e] = 0.0f;
-        }
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            acc[r][c][e] = __builtin_fmaf(accg[r][c][e], scv[c], acc[r][c][e]);
+            accg[r][c][e] = 0.0f;
+          }
     }
     if (has_next2) store((i + 2) % kQDepth, (i + 2) % kQBufs);
     __syncthreads();
@@ -399,28 +415,36 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
   // full trips of kQDepth stages, each with two successors: no branch around the
   // ring's loads, so its registers stay put across trips and the compiler's
   // in-order waits leave the later stages in flight (kQDepth is a multiple of
-  // kQBufs and of 2, so slot, buffer and fragment set follow i)
+  // kQBufs, so slot and buffer follow i)
   for (; kt + kQDepth + 1 < nk;) {
 #pragma unroll
-    for (int i = 0; i < kQDepth; ++i) run_stage(i, true, true);
+    for (int i = 0; i < kQDepth; ++i) run_stage(i, true);
   }
 #pragma unroll
   for (int i = 0; i < kQDepth + 1; ++i) {  // the last 2..kQDepth + 1 stages
-    if (kt < nk) run_stage(i % kQDepth, kt + 1 < nk, kt + 2 < nk);
+    if (kt < nk) run_stage(i % kQDepth, kt + 2 < nk);
   }
   // lane l holds rows 8 (e / 4) + 4 (l / 32) + e % 4 of column l % 32 of each 32 x 32 tile
-  if (!col_live) return;
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int c = 0; c < NC; ++c) {
+    if (my_col[c] >= d_out) continue;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t row = m0 + wm * 64 + r * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (row >= M) continue;
-      if (part != nullptr) part[((int64_t)blockIdx.z * M + row) * d_out + my_col] = acc[r][e];
-      else if constexpr (Y16) ((uint16_t*)Y)[row * ld_y + my_col] = f2h_bits(acc[r][e]);
-      else ((float*)Y)[row * ld_y + my_col] = acc[r][e];
-    }
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 64 + r * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row >= M) continue;
+        if (part != nullptr) part[((int64_t)blockIdx.z * M + row) * d_out + my_col[c]] = acc[r][c][e];
+        else if constexpr (Y16) ((uint16_t*)Y)[row * ld_y + my_col[c]] = f2h_bits(acc[r][c][e]);
+        else ((float*)Y)[row * ld_y + my_col[c]] = acc[r][c][e];
+      }
+  }
 }
+
+// token tile of the GEMM: 256 rows (8 waves of 64 x 64: twice the matrix-core work per
+// dequantized code of the 128-row tile, 1.27x faster at 2048 tokens) once there are more
+// than 128 tokens, else 128 rows (8 waves of 64 x 32), which wastes less of the tile
+static int gemm_bm(int64_t M) { return M > 128 ? 256 : 128; }
 
 // K splits of the GEMM, so that a small tile grid still gives every compute
 // unit a block (one block per CU): split boundaries fall on multiples of 128
@@ -429,7 +453,8 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
 // are added in split order by the reduction kernel.
 static int gemm_split_stages(int64_t M, int64_t d_out, int64_t d_in) {
   const int nk = (int)(d_in / kQBK);
-  const int64_t tiles = ((d_out + kQBN - 1) / kQBN) * ((M + kQBM - 1) / kQBM);
+  const int64_t bmr = gemm_bm(M);
+  const int64_t tiles = ((d_out + kQBN - 1) / kQBN) * ((M + bmr - 1) / bmr);
   const int units = (nk + 3) / 4;  // 128-input units, the last one possibly partial
   int64_t s = (256 + tiles - 1) / tiles;
   s = s < 8 ? s : 8;
@@ -456,13 +481,23 @@ hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32
     const int nk = (int)(d_in / kQBK), ss = gemm_split_stages(M, d_out, d_in);
     const int n_split = (nk + ss - 1) / ss;
     float* gp = n_split > 1 ? part : nullptr;
-    const dim3 g((unsigned)((d_out + kQBN - 1) / kQBN), (unsigned)((M + kQBM - 1) / kQBM), (unsigned)n_split);
-    if (y_f16)
-      w4a16_gemm_kernel<true><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
-                                                            group_size, Y, ld_y, ss, gp);
-    else
-      w4a16_gemm_kernel<false><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
-                                                             group_size, Y, ld_y, ss, gp);
+    const int bmr = gemm_bm(M);
+    const dim3 g((unsigned)((d_out + kQBN - 1) / kQBN), (unsigned)((M + bmr - 1) / bmr), (unsigned)n_split);
+    if (bmr == 256) {
+      if (y_f16)
+        w4a16_gemm_kernel<true, 256><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
+                                                                   group_size, Y, ld_y, ss, gp);
+      else
+        w4a16_gemm_kernel<false, 256><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros,
+                                                                    d_out, group_size, Y, ld_y, ss, gp);
+    } else {
+      if (y_f16)
+        w4a16_gemm_kernel<true, 128><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros, d_out,
+                                                                   group_size, Y, ld_y, ss, gp);
+      else
+        w4a16_gemm_kernel<false, 128><<<g, kQThreads, 0, stream>>>(X, ld_x, M, d_in, qweight, scales, qzeros,
+                                                                    d_out, group_size, Y, ld_y, ss, gp);
+    }
     if (n_split > 1) {
       const dim3 rgrid((unsigned)((d_out / 4 + kRdCols - 1) / kRdCols), (unsigned)M);
       w4a16_reduce_kernel<<<rgrid, kRdCols * kRdSplit, 0, stream>>>(part, n_split, (int)M, d_out, Y, ld_y,

@@ -242,9 +242,9 @@ def test_w4a16_validation(A):
     assert need % (4096 * 4) == 0
     assert L.awq_w4a16_workspace(3, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 4 * need
     assert L.awq_w4a16_workspace(-1, 8, 128, ctypes.byref(n)) == A.AWQ_EINVAL
-    # prefill GEMM: 256 tokens x 4096 outputs is 64 tiles of 128 x 128, split 4 ways over K
-    # (fp32 partials [4][256][4096]); 2048 tokens give 512 tiles and run unsplit
-    assert L.awq_w4a16_workspace(256, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 4 * 256 * 4096 * 4
+    # prefill GEMM: 256 tokens x 4096 outputs is 32 tiles of 256 x 128, split 8 ways over K
+    # (fp32 partials [8][256][4096]); 2048 tokens give 256 tiles and run unsplit
+    assert L.awq_w4a16_workspace(256, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 8 * 256 * 4096 * 4
     assert L.awq_w4a16_workspace(2048, 4096, 4096, ctypes.byref(n)) == A.AWQ_OK and n.value == 4 * need
     # at most 8 splits, each at least two 128-input units: 32 tokens x 1024 outputs x 512 inputs -> 2
     assert L.awq_w4a16_workspace(32, 1024, 512, ctypes.byref(n)) == A.AWQ_OK and n.value == 2 * 32 * 1024 * 4
