@@ -228,6 +228,24 @@ def bench_weight(args, wl_name: str):
         k_ms["search_weight"] += ev.ms(6 * i + 2, 6 * i + 3) / K
         k_ms["quantize_pack"] += ev.ms(6 * i + 4, 6 * i + 5) / K
     ev.close()
+    # unpack + dequantize (verification path, not part of the step): the first member's
+    # packed output back to fp16 W, K calls between two events on torch's stream
+    qw0, sc0, qz0 = packs[0]
+    d0 = Ws[0].shape[0]
+    w_back = torch.empty((d0, d_in), dtype=torch.float16, device=dev)
+    unpack_args = (qw0.data_ptr(), sc0.data_ptr(), qz0.data_ptr(), d0, d_in, G, res.best_s.data_ptr(),
+                   w_back.data_ptr(), A.AWQ_F16, torch.cuda.current_stream().cuda_stream)
+    unpack_ms = []
+    for a in (unpack_args, unpack_args[:6] + (None,) + unpack_args[7:]):  # W domain (/ s), scaled domain
+        A._check(A.lib().awq_unpack_dequant(*a))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            A.lib().awq_unpack_dequant(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        unpack_ms.append(e0.elapsed_time(e1) / K)
+    unpack_bytes = d0 * d_in // 2 + 2 * d0 * (d_in // G) + d0 * (d_in // G) // 2 + 4 * d_in + 2 * d0 * d_in
 
     elem_pts = n_w * 20
     t_search = k_ms["search_weight"] * 1e-3
@@ -250,6 +268,8 @@ def bench_weight(args, wl_name: str):
         "pack_GBps": pk_bytes / (k_ms["quantize_pack"] * 1e-3) / 1e9,
         "act_stats_GBps": (2 * T * d_in + 4 * d_in) / (k_ms["act_stats"] * 1e-3) / 1e9,
         "kernel_us": {k: v * 1e3 for k, v in k_ms.items()},
+        "unpack_us": unpack_ms[0] * 1e3, "unpack_GBps": unpack_bytes / (unpack_ms[0] * 1e-3) / 1e9,
+        "unpack_scaled_domain_us": unpack_ms[1] * 1e3,
         "roofline": {"bound": "alu", "achieved": achieved_ops, "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s",
                      "frac": achieved_ops / VALU_LANE_OPS_PEAK_T,
                      "traffic": pmc_traffic("search_weight_kernel", wl_name, args),

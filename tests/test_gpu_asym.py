@@ -83,11 +83,12 @@ def test_pack_asym_grid_values(A):
     assert np.array_equal(host(out), W.astype(F32))
 
 
+@pytest.mark.parametrize("d_out", [136, 256])
 @pytest.mark.parametrize("G,with_s", [(128, True), (64, False), (32, True)])
-def test_unpack_asym(A, G, with_s):
+def test_unpack_asym(A, G, with_s, d_out):
     import torch
-    say(f"unpack asym G={G} s={with_s}")
-    d_out, d_in = 136, 512
+    say(f"unpack asym G={G} s={with_s} d_out={d_out}")
+    d_in = 512
     W = _special_rows(WL.make_weight(41 + G, d_out, d_in), G)
     s = (np.exp(np.random.default_rng(G).standard_normal(d_in) * 0.5)).astype(F32)
     qw, sc, qz = _pack_compare(A, W, G, s, None)

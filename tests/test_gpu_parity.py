@@ -192,11 +192,12 @@ def test_pack_worked_example_codes(A):
         assert np.all(u[:, 4:] == 7)
 
 
+@pytest.mark.parametrize("d_out", [136, 256])   # one word per thread; four (d_out % 32 == 0)
 @pytest.mark.parametrize("G,out_f16,with_s", [(128, False, True), (64, True, False), (32, False, False)])
-def test_unpack_roundtrip(A, G, out_f16, with_s):
+def test_unpack_roundtrip(A, G, out_f16, with_s, d_out):
     import torch
-    say(f"unpack G={G} f16={out_f16} s={with_s}")
-    d_out, d_in = 136, 512
+    say(f"unpack G={G} f16={out_f16} s={with_s} d_out={d_out}")
+    d_in = 512
     W = WL.make_weight(31 + G, d_out, d_in)
     s = (np.exp(np.random.default_rng(G).standard_normal(d_in) * 0.5)).astype(F32)
     qw, sc, qz, rq, rstep = _pack_compare(A, W, G, s)
