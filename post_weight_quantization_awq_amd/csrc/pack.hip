@@ -243,9 +243,71 @@ __global__ __launch_bounds__(256) void unpack_dequant_kernel(
   }
 }
 
+// Tiled form for d_out % 32 == 0 and 16-byte aligned qweight / qzeros: a block
+// takes 64 input rows x 16 words (128 outputs).  Thread t loads words
+// 4 (t % 4) .. + 3 of input row t / 4 as one 16-byte load (a wave reads 16
+// rows x 64 contiguous bytes), decodes its 32 values with the same arithmetic
+// as above into an LDS tile [128 outputs][64 inputs], and after a barrier the
+// block writes each output row's 64 inputs as contiguous 16-byte stores.
+constexpr int kUnpI = 64, kUnpW = 16;
+template <bool F16>
+__global__ __launch_bounds__(256) void unpack_dequant_tile_kernel(
+    const int32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const int32_t* __restrict__ qzeros, int64_t d_out, int64_t d_in, int group_size,
+    const float* __restrict__ s, void* __restrict__ out) {
+  typedef typename std::conditional<F16, uint16_t, float>::type T;
+  constexpr int kPad = 16 / sizeof(T);  // row padding (one 16-byte chunk) against bank conflicts
+  __shared__ __align__(16) T tile[kUnpW * 8][kUnpI + kPad];
+  const int64_t wpc = d_out / 8;
+  const int64_t i0 = (int64_t)blockIdx.x * kUnpI, m0 = (int64_t)blockIdx.y * kUnpW;
+  const int t = threadIdx.x, il = t >> 2, wq = t & 3;
+  const int64_t i = i0 + il, m = m0 + 4 * wq;
+  if (i < d_in && m < wpc) {
+    const int64_t g = i / group_size;
+    const uint4 wv4 = *(const uint4*)(qweight + i * wpc + m);
+    const uint4 zv4 = qzeros != nullptr ? *(const uint4*)(qzeros + g * wpc + m)
+                                        : make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+    const float sdiv = s != nullptr ? s[i] : 1.0f;
+    const uint32_t wv[4] = {wv4.x, wv4.y, wv4.z, wv4.w}, zv[4] = {zv4.x, zv4.y, zv4.z, zv4.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ol = 8 * (4 * wq + q) + ((j < 4) ? 2 * j : 2 * (j - 4) + 1);
+        const int u = (int)((wv[q] >> (4 * j)) & 0xFu);
+        const int z = (int)((zv[q] >> (4 * j)) & 0xFu);
+        float val = (float)(u - z) * h2f(scales[g * d_out + 8 * m0 + ol]);
+        if (s != nullptr) val = val / sdiv;
+        if constexpr (F16) tile[ol][il] = f2h_bits(val);
+        else tile[ol][il] = val;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int kChunks = kUnpI * (int)sizeof(T) / 16;  // 16-byte chunks per output row of the tile
+  constexpr int kPer = 16 / (int)sizeof(T);             // values per chunk
+  for (int c = t; c < kUnpW * 8 * kChunks; c += 256) {
+    const int ol = c / kChunks, ch = c % kChunks;
+    const int64_t o = 8 * m0 + ol, ii = i0 + (int64_t)ch * kPer;
+    if (o >= d_out || ii >= d_in) continue;  // d_in is a multiple of 8, so a chunk is whole or out
+    *(uint4*)((T*)out + o * d_in + ii) = *(const uint4*)&tile[ol][ch * kPer];
+  }
+}
+
 hipError_t launch_unpack_dequant(const int32_t* qweight, const uint16_t* scales,
                                  const int32_t* qzeros, int64_t d_out, int64_t d_in, int group_size,
                                  const float* s, void* out, bool out_f16, hipStream_t stream) {
+  if (d_out % 32 == 0 && d_in % 8 == 0 && (uintptr_t)qweight % 16 == 0 && (uintptr_t)qzeros % 16 == 0 &&
+      (uintptr_t)out % 16 == 0) {
+    const dim3 grid((unsigned)((d_in + kUnpI - 1) / kUnpI), (unsigned)((d_out / 8 + kUnpW - 1) / kUnpW));
+    if (out_f16)
+      unpack_dequant_tile_kernel<true><<<grid, 256, 0, stream>>>(qweight, scales, qzeros, d_out, d_in, group_size,
+                                                                 s, out);
+    else
+      unpack_dequant_tile_kernel<false><<<grid, 256, 0, stream>>>(qweight, scales, qzeros, d_out, d_in, group_size,
+                                                                  s, out);
+    return hipGetLastError();
+  }
   const int64_t n = d_in * (d_out / 8);
   unpack_dequant_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
       qweight, scales, qzeros, d_out, d_in, group_size, s, out, out_f16 ? 1 : 0);

@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kQThreads, 1) void w4a16_gemm_kernel(
   // ring's loads, so its registers stay put across trips and the compiler's
   // in-order waits leave the later stages in flight (kQDepth is a multiple of
   // kQBufs, so slot and buffer follow i)
-  for (; kt + kQDepth + 1 < nk;) {
+  while (kt + kQDepth + 1 < nk) {  // run_stage advances kt
 #pragma unroll
     for (int i = 0; i < kQDepth; ++i) run_stage(i, true);
   }
