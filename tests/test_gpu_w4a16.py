@@ -147,7 +147,7 @@ def test_w4a16_deterministic(A):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("M", [9, 32, 100, 257, 1024])
+@pytest.mark.parametrize("M", [9, 32, 100, 128, 129, 257, 1024])   # 128 | 129: the token tile grows to 256
 @pytest.mark.parametrize("d_out,d_in,G,out_dtype,zeros", [(1032, 384, 64, "f16", True), (520, 256, 32, "f32", False),
                                                           (4096, 4096, 128, "f16", True)])
 def test_w4a16_prefill_gemm(A, M, d_out, d_in, G, out_dtype, zeros):
