@@ -1,24 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the AWQ per-layer hot path on one MI355X.
 
-One step = the whole path on one linear group with its inputs resident in HBM:
-activation statistics -> candidate scales -> grid search over alpha (20
-points) -> selection -> INT4 quantize + pack of the winner.  The default
-workload is a Qwen3-8B q_proj-shaped linear (W 4096 x 4096 fp16, X 4096
-tokens x 4096 bf16, group size 128, weight-domain activation-weighted error).
+One step = the whole path on every linear group of the workload, inputs
+resident in HBM: activation statistics -> candidate scales -> grid search over
+alpha (20 points) -> selection -> INT4 quantize + pack of the winner.  The
+default workload is the full Qwen3-8B-shaped sweep: 36 blocks x 4
+input-sharing groups (QKV 6144 x 4096, o 4096 x 4096, gate/up 24576 x 4096,
+down 4096 x 12288; 6.95 G fp16 weights), every group with its own calibration
+input of 65536 bf16 tokens, weight-domain activation-weighted error, group
+size 128 (the line also reports group size 64).
 
 Prints ONE JSON line.  `value` is weight-elements x grid-points per second of
-the whole step, timed over K steps with nothing else on the stream; per-kernel
+the whole step, timed over K steps with nothing else on the streams; per-kernel
 times come from a second pass over the same K steps in which the library
 records HIP events around its main kernels on the stream they run on (an event
 record costs microseconds of GPU timeline, so it stays out of the step time);
 `roofline` describes the dominant kernel (traffic from committed counter runs,
 null once its sources change); `cpu_baseline` times the CPU oracle on a
-bounded sample.
+bounded sample over the host's cores.
 
-Other workloads (--workload) measure the remaining rows: the output-score
-search on the matrix cores (fused QKV, MLP with clip search) and the full
-Qwen3-8B-shaped sweep of 144 linear groups.
+Other workloads (--workload) measure the remaining rows: a single q_proj-shaped
+linear, the output-score search on the matrix cores (fused QKV, MLP with clip
+search), the norm-group export and the W4A16 product on the packed layout.
 """
 from __future__ import annotations
 
@@ -123,36 +126,193 @@ def pack_bytes(d_out: int, d_in: int, G: int) -> int:
     return 2 * n + n // 2 + 2 * n // G + n // (2 * G) + 4 * d_in
 
 
-def cpu_baseline_weight(W, X, G, budget_s: float, duo: bool = False, asym: bool = False):
-    """Times the CPU oracle on the same group: statistics over all tokens, then
-    search (20 points) + pack on consecutive row chunks until the time budget
-    or the rows run out; the step time is scaled to all rows."""
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_workers() -> int:
+    """Worker processes for the oracle baseline: the host's CPU share (the
+    OMP_NUM_THREADS the machine sets for a job, else every CPU this process
+    may run on)."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
+# Oracle tasks for the worker pool (top-level so that spawned workers can run them).
+def _oracle_stats_task(X):
     from oracle import awq_oracle as O
+    return O.act_stats(X), X.shape[0]
+
+
+def _oracle_search_task(W, S, xm, G, asym):
+    """Candidate errors of a row chunk of a group (the group's candidate table S)."""
+    import numpy as np
+    from oracle import awq_oracle as O
+    return np.array([O.weight_error(W, S[k], xm, G, asym=asym) for k in range(S.shape[0])])
+
+
+def _oracle_pack_task(W, s, G, asym):
+    from oracle import awq_oracle as O
+    out = O.quantize_pack_asym(W, s, G) if asym else O.quantize_pack(W, s, G)
+    return out[0].shape
+
+
+def _noop_task(i):
+    return i
+
+
+class OraclePool:
+    """The CPU oracle, unchanged, spread over a pool of worker processes: the
+    activation statistics over token chunks, the search over row chunks (a
+    group's candidate errors are sums over its rows, so the chunks' errors add
+    up to the group's), and the packing over row chunks."""
+
+    def __init__(self, n: int):
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        self.n = n
+        # single-threaded numpy in every worker: the pool is the parallelism
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+        for k in saved:
+            os.environ[k] = "1"
+        try:
+            self.ex = cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"))
+            list(self.ex.map(_noop_task, range(4 * n)))     # start every worker before any timing
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+
+    def act_stats(self, X, chunk_rows: int):
+        """x_mean of X from per-chunk means weighted by their token counts."""
+        import numpy as np
+        futs = [self.ex.submit(_oracle_stats_task, X[t:t + chunk_rows]) for t in range(0, X.shape[0], chunk_rows)]
+        tot = np.zeros(X.shape[1], dtype=np.float64)
+        for f in futs:
+            m, t = f.result()
+            tot += m.astype(np.float64) * t
+        return (tot / X.shape[0]).astype(np.float32)
+
+    def search(self, groups, G, duo=False, asym=False, chunk_rows=256):
+        """groups: list of (W [d_out, d_in] fp16, x_mean).  Returns per group (errors, best index, best s)."""
+        import numpy as np
+        from oracle import awq_oracle as O
+        tables = [O.candidate_scales(xm, 20, w_mean=O.weight_channel_mean([W]) if duo else None)
+                  for W, xm in groups]
+        futs = [[self.ex.submit(_oracle_search_task, W[r:r + chunk_rows], S, xm, G, asym)
+                 for r in range(0, W.shape[0], chunk_rows)] for (W, xm), S in zip(groups, tables)]
+        out = []
+        for S, fs in zip(tables, futs):
+            errs = np.zeros(S.shape[0], dtype=np.float64)
+            for f in fs:
+                errs += f.result()
+            k = O.first_argmin(errs)
+            out.append((errs, k, S[k]))
+        return out
+
+    def pack(self, jobs, G, asym=False, chunk_rows=256):
+        """jobs: list of (W part, s)."""
+        futs = [self.ex.submit(_oracle_pack_task, W[r:r + chunk_rows], s, G, asym)
+                for W, s in jobs for r in range(0, W.shape[0], chunk_rows)]
+        for f in futs:
+            f.result()
+
+    def close(self):
+        self.ex.shutdown(wait=True)
+
+
+def cpu_baseline_weight(W_parts, X, G, budget_s: float, duo: bool = False, asym: bool = False):
+    """Times the CPU oracle on the same group on the host's cores: statistics
+    over all tokens, then search (20 points) + pack of row chunks (the whole
+    group when it fits the budget, else as many 256-row chunks as fit, the
+    step time scaled to all rows)."""
+    import numpy as np
+    W = np.concatenate(W_parts, axis=0)
     d_out, d_in = W.shape
-    t0, c0 = time.perf_counter(), time.process_time()
-    xm = O.act_stats(X)
-    t_stats = time.perf_counter() - t0
-    done, t_rows, chunk = 0, 0.0, 256
-    while done < d_out and t_stats + t_rows < budget_s:
-        Wr = W[done:done + chunk]
-        t1 = time.perf_counter()
-        _, _, s = O.search_scales([Wr], xm, G, 20, duo=duo, asym=asym)
-        if asym:
-            O.quantize_pack_asym(Wr, s, G)
-        else:
-            O.quantize_pack(Wr, s, G)
-        t_rows += time.perf_counter() - t1
-        done += Wr.shape[0]
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
+    pool = OraclePool(oracle_workers())
+    try:
+        t0 = time.perf_counter()
+        xm = pool.act_stats(X, max(64, -(-X.shape[0] // pool.n)))
+        t_stats = time.perf_counter() - t0
+        # rows in rounds of one 256-row chunk per worker until the budget runs out
+        done, t_rows, rnd = 0, 0.0, 256 * pool.n
+        while done < d_out and t_stats + t_rows < budget_s:
+            Wr = W[done:done + rnd]
+            t1 = time.perf_counter()
+            (errs, k, s), = pool.search([(Wr, xm)], G, duo, asym)
+            pool.pack([(Wr, s)], G, asym)
+            t_rows += time.perf_counter() - t1
+            done += Wr.shape[0]
+        wall = time.perf_counter() - t0
+    finally:
+        pool.close()
     step_s = t_stats + t_rows * d_out / done
     return {
         "value": d_out * d_in * 20 / step_s,
         "unit": "weight-elem*grid-pt/s",
-        "cores": max(1, round(cpu / wall)),
+        "cores": pool.n, "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"act_stats over all {X.shape[0]} tokens, search (20 points) + pack of {done} of {d_out} "
-                  f"rows, step time scaled to all rows ({wall:.1f} s wall)",
+                  f"rows in 256-row chunks over {pool.n} worker processes, step time scaled to all rows "
+                  f"({wall:.1f} s wall)",
+    }
+
+
+def cpu_baseline_sweep(host_blocks, T_full: int, G: int, budget_s: float, duo: bool = False, asym: bool = False,
+                       n_blocks: int = 36):
+    """Times the CPU oracle on blocks of the sweep (host copies of the same
+    device tensors), on the host's cores, block after block until the budget
+    runs out: statistics on a token sample of every group's input (scaled to
+    all tokens), then the search of every group over all its rows and the
+    packing of every part; the per-block time is scaled to all blocks.
+    host_blocks: list over blocks of list over groups of (parts, X token sample)."""
+    pool = OraclePool(oracle_workers())
+    t_stats = t_search = t_pack = 0.0
+    done, t_tok = 0, 0
+    try:
+        t0 = time.perf_counter()
+        for groups in host_blocks:
+            t1 = time.perf_counter()
+            xms = [pool.act_stats(X, max(64, -(-X.shape[0] // pool.n))) for _, X in groups]
+            t2 = time.perf_counter()
+            res = pool.search([(__import__("numpy").concatenate(parts, axis=0), xm)
+                               for (parts, _), xm in zip(groups, xms)], G, duo, asym)
+            t3 = time.perf_counter()
+            pool.pack([(p, s) for (parts, _), (_, _, s) in zip(groups, res) for p in parts], G, asym)
+            t4 = time.perf_counter()
+            t_stats += t2 - t1
+            t_search += t3 - t2
+            t_pack += t4 - t3
+            t_tok = groups[0][1].shape[0]
+            done += 1
+            if t4 - t0 > budget_s:
+                break
+        wall = time.perf_counter() - t0
+    finally:
+        pool.close()
+    per_block = t_stats * (T_full / t_tok) / done + (t_search + t_pack) / done
+    n_w = sum(p.shape[0] * p.shape[1] for parts, _ in host_blocks[0] for p in parts)
+    return {
+        "value": n_blocks * n_w * 20 / (n_blocks * per_block),
+        "unit": "weight-elem*grid-pt/s",
+        "cores": pool.n, "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{done} of {n_blocks} blocks at G = {G}: act_stats on {t_tok} of {T_full} tokens per group "
+                  f"(scaled to all tokens), search (20 points) of every group and pack of every part in 256-row "
+                  f"chunks over {pool.n} worker processes; per-block time scaled to {n_blocks} blocks "
+                  f"({wall:.1f} s wall: stats {t_stats:.1f}, search {t_search:.1f}, pack {t_pack:.1f})",
     }
 
 
@@ -277,7 +437,7 @@ def bench_weight(args, wl_name: str):
                      "ops_per_elem_pt": ops},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_weight(W_h, X_h, G, args.cpu_seconds, args.duo, args.asym)
+        out["cpu_baseline"] = cpu_baseline_weight(parts_h, X_h, G, args.cpu_seconds, args.duo, args.asym)
     return out
 
 
@@ -375,6 +535,12 @@ def bench_output(args, wl_name: str):
 
 
 def bench_sweep(args):
+    """The full Qwen3-8B-shaped sweep: 36 blocks x 4 input-sharing groups (QKV
+    6144 x 4096, o 4096 x 4096, gate/up 24576 x 4096, down 4096 x 12288), each
+    block with its own calibration input per group (65536 tokens, bf16), at
+    G = 128 and then G = 64.  One step = per group: statistics, candidates,
+    search, select, pack of every part."""
+    import numpy as np
     import torch
     import post_weight_quantization_awq_amd as A
     import workloads as WL
@@ -382,12 +548,13 @@ def bench_sweep(args):
     wl = WL.WORKLOADS["qwen3_8b_sweep"]
     dev = torch.device("cuda:0")
     blocks = args.blocks
-    # one calibration input per group kind (the 36 blocks share their statistics' shape)
-    Xs = [WL.torch_activations(wl.seed(0, gi, 2), g.T, g.d_in, dev) for gi, g in enumerate(wl.groups)]
-    Ws = []
-    for b in range(blocks):
-        Ws.append([[WL.torch_weight(wl.seed(b, gi, 1 + 1000 * p), r, g.d_in, dev) for p, r in enumerate(g.parts)]
-                   for gi, g in enumerate(wl.groups)])
+    ng = len(wl.groups)
+    # every block has its own weights and its own calibration inputs (108 GiB of
+    # bf16 activations for 36 blocks, resident in HBM with the 13.9 GB of weights)
+    Xs = [[WL.torch_activations(wl.seed(b, gi, 2), g.T, g.d_in, dev) for gi, g in enumerate(wl.groups)]
+          for b in range(blocks)]
+    Ws = [[[WL.torch_weight(wl.seed(b, gi, 1 + 1000 * p), r, g.d_in, dev) for p, r in enumerate(g.parts)]
+           for gi, g in enumerate(wl.groups)] for b in range(blocks)]
     torch.cuda.synchronize()
     out_all = {}
     for G in wl.group_sizes:
@@ -402,9 +569,8 @@ def bench_sweep(args):
                    torch.empty((g.d_in // G, r // 8), dtype=torch.int32, device=dev)) for r in g.parts]
                  for g in wl.groups]
         K = args.steps
-        per = 6 * 4 * blocks
+        per = 6 * ng * blocks
         ev = HipEvents(per * K)
-        ng = len(wl.groups)
         # The groups of a block are independent chains (own statistics, search and
         # packing; own workspaces and outputs): the timed steps put each group
         # kind on a stream of its own, joined to the main stream at both ends.
@@ -413,7 +579,8 @@ def bench_sweep(args):
         streams = [torch.cuda.Stream() for _ in range(args.streams)]
 
         def plans(stream_of):
-            st = [A.ActStatsPlan(Xs[gi], x_mean=xms[gi], ws=ws_stats[gi], stream=stream_of(gi)) for gi in range(ng)]
+            st = [[A.ActStatsPlan(Xs[b][gi], x_mean=xms[gi], ws=ws_stats[gi], stream=stream_of(gi))
+                   for gi in range(ng)] for b in range(blocks)]
             se = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi], stream=stream_of(gi),
                                  duo=args.duo, asym=args.asym)
                    for gi in range(ng)] for b in range(blocks)]
@@ -432,7 +599,7 @@ def bench_sweep(args):
                 for gi in range(ng):
                     if k >= 0:
                         A.set_timing_events(ev.h(n), ev.h(n + 1))
-                    st_plans[gi].launch()
+                    st_plans[b][gi].launch()
                     if k >= 0:
                         A.set_timing_events(ev.h(n + 2), ev.h(n + 3))
                     se_plans[b][gi].launch()
@@ -475,30 +642,59 @@ def bench_sweep(args):
         sums = [s / args.steps for s in sums]
         n_w = blocks * sum(g.d_out * g.d_in for g in wl.groups)
         pk = blocks * sum(pack_bytes(r, g.d_in, G) for g in wl.groups for r in g.parts)
-        xb = blocks * sum(2 * g.T * g.d_in for g in wl.groups)
+        xb = blocks * sum(2 * g.T * g.d_in + 4 * g.d_in for g in wl.groups)
+        ops = SEARCH_OPS_PER_ELEM_PT_ASYM if args.asym else SEARCH_OPS_PER_ELEM_PT
         out_all[f"G{G}"] = {
             "ms_per_step": ms_step, "elem_pts_per_s": n_w * 20 / (ms_step * 1e-3),
             "search_ms": sums[1], "search_elem_pts_per_s": n_w * 20 / (sums[1] * 1e-3),
             "search_hbm_equiv_GBps": 2.0 * n_w * 20 / (sums[1] * 1e-3) / 1e9,
-            "search_alu_frac": (SEARCH_OPS_PER_ELEM_PT_ASYM if args.asym else SEARCH_OPS_PER_ELEM_PT)
-            * n_w * 20 / (sums[1] * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T,
+            "search_alu_frac": ops * n_w * 20 / (sums[1] * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T,
             "pack_ms": sums[2], "pack_GBps": pk / (sums[2] * 1e-3) / 1e9,
+            "pack_hbm_frac": pk / (sums[2] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "act_stats_ms": sums[0], "act_stats_GBps": xb / (sums[0] * 1e-3) / 1e9,
+            "act_stats_hbm_frac": xb / (sums[0] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         }
+        del par, ser
     n_w = blocks * sum(g.d_out * g.d_in for g in wl.groups)
-    first = out_all[f"G{wl.group_sizes[0]}"]
-    return {
+    G0 = wl.group_sizes[0]
+    first = out_all[f"G{G0}"]
+    ops = SEARCH_OPS_PER_ELEM_PT_ASYM if args.asym else SEARCH_OPS_PER_ELEM_PT
+    wl_key = "qwen3_8b_sweep" if blocks == 36 else f"qwen3_8b_sweep_{blocks}_blocks"
+    out = {
         "metric": METRIC, "value": first["elem_pts_per_s"], "unit": "weight-elem*grid-pt/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": first["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "qwen3_8b_sweep", "blocks": blocks, "weights": n_w, "n_grid": 20,
-                   "group_sizes": list(wl.group_sizes), "score": "weight", "streams": args.streams,
-                   "duo": args.duo, "asym": args.asym},
+        "config": {"workload": wl_key, "blocks": blocks, "weights": n_w, "n_grid": 20,
+                   "group_size": G0, "group_sizes": list(wl.group_sizes), "score": "weight",
+                   "calibration_tokens_per_group": wl.groups[0].T, "x_per_block": True,
+                   "x_dtype": "bf16", "streams": args.streams, "duo": args.duo, "asym": args.asym},
         "per_group_size": out_all,
+        "pack_GBps": first["pack_GBps"], "pack_hbm_frac": first["pack_hbm_frac"],
+        "act_stats_GBps": first["act_stats_GBps"], "act_stats_hbm_frac": first["act_stats_hbm_frac"],
         "roofline": {"bound": "alu", "achieved": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T,
                      "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s", "frac": first["search_alu_frac"],
-                     "traffic": None, "kernel": "search_weight_kernel"},
+                     "traffic": pmc_traffic("search_weight_kernel", wl_key, args),
+                     "kernel": "search_weight_kernel", "ops_per_elem_pt": ops,
+                     "per": "achieved over all 144 launches of one step at G = %d; traffic per launch, "
+                            "mean over the 144" % G0},
     }
+    if not args.no_cpu_baseline:
+        # host copies of the first blocks (weights, and a 4096-token sample of every group's input)
+        n_cpu = min(blocks, args.cpu_blocks)
+        T_s = min(4096, wl.groups[0].T)
+        host_blocks = []
+        for b in range(n_cpu):
+            gs = []
+            for gi in range(ng):
+                parts = [w.cpu().numpy() for w in Ws[b][gi]]
+                X = Xs[b][gi][:T_s].view(torch.int16).cpu().numpy().view(np.uint16)
+                gs.append((parts, X))
+            host_blocks.append(gs)
+        del Xs, Ws
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline_sweep(host_blocks, wl.groups[0].T, G0, args.cpu_seconds, args.duo,
+                                                 args.asym, n_blocks=blocks)
+    return out
 
 
 def bench_export(args):
@@ -808,7 +1004,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="q_proj_4096x4096",
+    ap.add_argument("--workload", default="qwen3_8b_sweep",
                     choices=["single_linear_256x512", "q_proj_4096x4096", "qkv_6144x4096_output",
                              "mlp_output_clip", "qwen3_8b_sweep", "qwen3_8b_export", "qwen3_8b_decode_w4a16",
                              "copy_512MiB"])
@@ -822,7 +1018,10 @@ def main() -> int:
                     help="asymmetric INT4 (zero point per group) in the search and pack of the search workloads")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per decode step of the W4A16 workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-time budget of the CPU oracle baseline")
+    ap.add_argument("--cpu-blocks", type=int, default=4,
+                    help="most sweep blocks the CPU oracle baseline runs (it stops earlier at --cpu-seconds)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the AWQ search and pack run per linear group on a single device; "

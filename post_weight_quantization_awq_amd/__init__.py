@@ -131,6 +131,37 @@ def _dev(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _tensor(t: Optional[torch.Tensor], name: str, dtype, shape=None, *, contiguous: bool = True,
+            unit_col_stride: bool = False, min_numel: Optional[int] = None, like: Optional[torch.Tensor] = None,
+            optional: bool = False) -> None:
+    """Checks a tensor the library will read or write before anything is launched:
+    dtype, shape (a tuple, entries None = any), layout (contiguous, or 2-D with
+    unit column stride), size, and that it lives where `like` does.  That the
+    tensors are on the device is checked once all of them passed (_dev).
+    Raises ValueError."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and g != w for g, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+            raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
+    if unit_col_stride:
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1) or (t.shape[0] > 1 and t.stride(0) < t.shape[1]):
+            raise ValueError(f"{name} must be 2-D with unit column stride and rows at least a row apart")
+    elif contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {min_numel}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, not on {like.device}")
+
+
 def _x_dtype(X: torch.Tensor) -> int:
     if X.dtype == torch.bfloat16:
         return AWQ_BF16
@@ -140,9 +171,11 @@ def _x_dtype(X: torch.Tensor) -> int:
 
 
 def _rows_view(X: torch.Tensor, name: str):
-    if X.dim() != 2 or X.stride(1) != 1:
+    if X.dim() != 2 or (X.shape[1] > 1 and X.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit column stride")
-    return X.shape[0], X.shape[1], X.stride(0)
+    # a tensor of at most one row may report any row stride; its rows are never stepped over
+    ld = X.stride(0) if X.shape[0] > 1 else max(X.stride(0), X.shape[1])
+    return X.shape[0], X.shape[1], ld
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -177,8 +210,11 @@ class ActStatsPlan(_Prepared):
 
     def __init__(self, X: torch.Tensor, x_mean: Optional[torch.Tensor] = None, inv_count: Optional[float] = None,
                  accumulate: bool = False, ws: Optional[torch.Tensor] = None, stream=None):
-        _dev(X, "X")
+        _tensor(X, "X", (torch.bfloat16, torch.float16), (None, None), unit_col_stride=True)
         T, d_in, ld = _rows_view(X, "X")
+        _tensor(x_mean, "x_mean", torch.float32, (d_in,), like=X, optional=True)
+        _tensor(ws, "ws", torch.uint8, (None,), like=X, optional=True)
+        _dev(X, "X")
         self.x_mean = torch.empty(d_in, dtype=torch.float32, device=X.device) if x_mean is None else x_mean
         if inv_count is None:
             inv_count = 1.0 / T if T > 0 else 0.0
@@ -200,6 +236,7 @@ def act_stats(X: torch.Tensor, x_mean: Optional[torch.Tensor] = None, inv_count:
 
 
 def candidate_scales(x_mean: torch.Tensor, n_grid: int = 20, s_min: float = 1e-4, stream=None) -> torch.Tensor:
+    _tensor(x_mean, "x_mean", torch.float32, (None,))
     _dev(x_mean, "x_mean")
     d_in = x_mean.numel()
     S = torch.empty((n_grid, d_in), dtype=torch.float32, device=x_mean.device)
@@ -240,8 +277,9 @@ def weight_channel_mean(W_parts: Sequence[torch.Tensor], stream=None) -> torch.T
 def candidate_scales_duo(x_mean: torch.Tensor, w_mean: torch.Tensor, n_grid: int = 20, s_min: float = 1e-4,
                          stream=None) -> torch.Tensor:
     """Duo-scaling candidate table S [n_grid, d_in]."""
+    _tensor(x_mean, "x_mean", torch.float32, (None,))
+    _tensor(w_mean, "w_mean", torch.float32, (x_mean.numel(),), like=x_mean)
     _dev(x_mean, "x_mean")
-    _dev(w_mean, "w_mean")
     d_in = x_mean.numel()
     S = torch.empty((n_grid, d_in), dtype=torch.float32, device=x_mean.device)
     n = ctypes.c_size_t()
@@ -290,19 +328,28 @@ class SearchPlan(_Prepared):
             raise ValueError("empty weight group")
         d_in = parts[0].shape[1]
         for p in parts:
-            _dev(p, "W")
             if p.dtype != torch.float16 or p.dim() != 2 or not p.is_contiguous() or p.shape[1] != d_in:
                 raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
         dev = parts[0].device
+        for p in parts[1:]:
+            if p.device != dev:
+                raise ValueError("the parts of a group must live on one device")
         d_out = sum(p.shape[0] for p in parts)
+        _tensor(x_mean, "x_mean", torch.float32, (d_in,), like=parts[0])
         self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo, asym)
         T, ld, xdt = 0, 0, AWQ_BF16
         if X is not None:
-            _dev(X, "X")
+            _tensor(X, "X", (torch.bfloat16, torch.float16), (None, d_in), unit_col_stride=True, like=parts[0])
             T, dx, ld = _rows_view(X, "X")
-            if dx != d_in:
-                raise ValueError("X and W disagree on d_in")
             xdt = _x_dtype(X)
+        if out is not None:
+            _tensor(out.err, "out.err", torch.float32, (n_grid,), like=parts[0])
+            _tensor(out.best_idx, "out.best_idx", torch.int32, (1,), like=parts[0])
+            _tensor(out.best_s, "out.best_s", torch.float32, (d_in,), like=parts[0])
+            _tensor(out.clip, "out.clip", torch.float32, (d_out,), like=parts[0], optional=not n_clip)
+            _tensor(out.clip_err, "out.clip_err", torch.float32, (d_out, n_clip), like=parts[0], optional=True)
+        _tensor(ws, "ws", torch.uint8, (None,), like=parts[0], optional=True)
+        _dev(parts[0], "W")
         n = ctypes.c_size_t()
         _check(lib().awq_search_workspace(ctypes.byref(self.cfg), d_out, d_in, max(T, 1), ctypes.byref(n)))
         self.ws = workspace(n.value, dev) if (ws is None or ws.numel() < n.value) else ws
@@ -345,10 +392,19 @@ class PackPlan(_Prepared):
         if asym:
             self._fn = "awq_quantize_pack_asym"
             with_zeros = True
-        _dev(W, "W")
-        if W.dtype != torch.float16 or W.dim() != 2 or not W.is_contiguous():
-            raise ValueError("W must be contiguous fp16 [d_out, d_in]")
+        _tensor(W, "W", torch.float16, (None, None))
         d_out, d_in = W.shape
+        if group_size not in (32, 64, 128) or d_in % group_size or d_out % 8:
+            raise ValueError(f"W [{d_out}, {d_in}]: need d_out % 8 == 0 and d_in a multiple of "
+                             f"group_size in {{32, 64, 128}}, got {group_size}")
+        _tensor(s, "s", torch.float32, (d_in,), like=W, optional=True)
+        _tensor(clip, "clip", torch.float32, (d_out,), like=W, optional=True)
+        if out is not None:
+            qweight, scales, qzeros = out
+            _tensor(qweight, "qweight", torch.int32, (d_in, d_out // 8), like=W)
+            _tensor(scales, "scales", torch.float16, (d_in // group_size, d_out), like=W)
+            _tensor(qzeros, "qzeros", torch.int32, (d_in // group_size, d_out // 8), like=W, optional=not asym)
+        _dev(W, "W")
         if out is None:
             qweight = torch.empty((d_in, d_out // 8), dtype=torch.int32, device=W.device)
             scales = torch.empty((d_in // group_size, d_out), dtype=torch.float16, device=W.device)
@@ -382,13 +438,18 @@ class W4A16Plan(_Prepared):
     def __init__(self, X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
                  qzeros: Optional[torch.Tensor], d_out: int, group_size: int = 128, out_dtype=torch.float16,
                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
-        _dev(X, "X")
-        _dev(qweight, "qweight")
-        if X.dtype != torch.float16:
-            raise ValueError("X must be fp16")
+        _tensor(X, "X", torch.float16, (None, None), unit_col_stride=True)
         M, d_in, ld = _rows_view(X, "X")
-        if qweight.shape != (d_in, d_out // 8):
-            raise ValueError("qweight must be [d_in, d_out/8]")
+        if group_size not in (32, 64, 128) or d_in % group_size or d_out % 8:
+            raise ValueError(f"need d_out % 8 == 0 and d_in ({d_in}) a multiple of group_size in "
+                             f"{{32, 64, 128}}, got d_out {d_out}, group_size {group_size}")
+        _tensor(qweight, "qweight", torch.int32, (d_in, d_out // 8), like=X)
+        _tensor(scales, "scales", torch.float16, (d_in // group_size, d_out), like=X)
+        _tensor(qzeros, "qzeros", torch.int32, (d_in // group_size, d_out // 8), like=X, optional=True)
+        if out is not None:
+            _tensor(out, "out", (torch.float16, torch.float32), (M, d_out), unit_col_stride=True, like=X)
+        _tensor(ws, "ws", torch.uint8, (None,), like=X, optional=True)
+        _dev(X, "X")
         n = ctypes.c_size_t()
         _check(lib().awq_w4a16_workspace(M, d_out, d_in, ctypes.byref(n)))
         self.ws = workspace(n.value, X.device) if (ws is None or ws.numel() < n.value) else ws
@@ -412,8 +473,15 @@ def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, q
 def unpack_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], d_out: int,
                    group_size: int = 128, s: Optional[torch.Tensor] = None, out_dtype=torch.float32,
                    stream=None) -> torch.Tensor:
-    _dev(qweight, "qweight")
+    _tensor(qweight, "qweight", torch.int32, (None, d_out // 8))
     d_in = qweight.shape[0]
+    if group_size not in (32, 64, 128) or d_in % group_size or d_out % 8:
+        raise ValueError(f"need d_out % 8 == 0 and d_in ({d_in}) a multiple of group_size in "
+                         f"{{32, 64, 128}}, got d_out {d_out}, group_size {group_size}")
+    _tensor(scales, "scales", torch.float16, (d_in // group_size, d_out), like=qweight)
+    _tensor(qzeros, "qzeros", torch.int32, (d_in // group_size, d_out // 8), like=qweight, optional=True)
+    _tensor(s, "s", torch.float32, (d_in,), like=qweight, optional=True)
+    _dev(qweight, "qweight")
     out = torch.empty((d_out, d_in), dtype=out_dtype, device=qweight.device)
     odt = {torch.float32: AWQ_F32, torch.float16: AWQ_F16}[out_dtype]
     _check(lib().awq_unpack_dequant(_ptr(qweight), _ptr(scales), _ptr(qzeros), d_out, d_in, group_size, _ptr(s),

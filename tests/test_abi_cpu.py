@@ -65,12 +65,14 @@ def st_pack(A, W=FAKE, d_out=64, d_in=256, G=128, s=None, clip=None, qw=FAKE, sc
 def test_pack_validation(A):
     assert st_pack(A, G=96) == A.AWQ_EINVAL
     assert st_pack(A, d_out=60) == A.AWQ_ESHAPE
+    assert "d_out 60 not a multiple of 8" in A.lib().awq_last_error().decode()
     assert st_pack(A, d_in=200) == A.AWQ_ESHAPE
+    assert "multiple of group_size 128" in A.lib().awq_last_error().decode()
     assert st_pack(A, W=None) == A.AWQ_EINVAL
     assert st_pack(A, W=FAKE_MIS) == A.AWQ_EALIGN
     assert st_pack(A, s=FAKE_MIS) == A.AWQ_EALIGN
     assert st_pack(A, d_out=-8) == A.AWQ_EINVAL
-    assert "multiple of 8" in A.lib().awq_last_error().decode() or True
+    assert "negative size" in A.lib().awq_last_error().decode()
     # empty inputs: nothing to do, no launch, NULL pointers allowed
     assert st_pack(A, W=None, d_out=0, qw=None, sc=None) == A.AWQ_OK
     assert st_pack(A, W=None, d_in=0, qw=None, sc=None) == A.AWQ_OK

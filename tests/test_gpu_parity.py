@@ -5,7 +5,9 @@ Bars: packed words, codes and fp16 scales bit-exact given the same fp32
 scale vector; candidate errors within 1e-3 relative; chosen alpha index equal
 unless the oracle's errors tie within 1e-4 relative; x_mean within 1e-6
 relative; candidate scales within 2 ulp (fp64 pow may differ in its last bit
-before the single rounding to fp32).
+before the single rounding to fp32); per-row clip errors within 1e-3
+relative and the chosen clip ratio equal unless the oracle's errors tie within
+1e-4 relative.
 """
 import numpy as np
 import pytest
@@ -215,6 +217,26 @@ def test_unpack_roundtrip(A, G, out_f16, with_s, d_out):
                           got.view(np.uint16 if out_f16 else np.uint32))
 
 
+@pytest.mark.parametrize("d_in,G,d_out", [(96, 32, 160), (192, 64, 288), (384, 128, 160)])
+@pytest.mark.parametrize("out_f16,with_s", [(False, True), (True, False), (True, True)])
+def test_unpack_partial_tiles(A, d_in, G, d_out, out_f16, with_s):
+    """The tiled unpack (64 inputs x 128 outputs through LDS, for d_out % 32 == 0)
+    on its ragged edges: d_in not a multiple of 64 and d_out not a multiple of 128."""
+    import torch
+    say(f"unpack partial tiles d_in={d_in} G={G} d_out={d_out} f16={out_f16} s={with_s}")
+    W = WL.make_weight(61 + d_in + d_out, d_out, d_in)
+    s = (np.exp(np.random.default_rng(d_in + G).standard_normal(d_in) * 0.5)).astype(F32)
+    qw, sc, qz, rq, rstep = _pack_compare(A, W, G, s)
+    sdev = dev_f32(s) if with_s else None
+    odt = torch.float16 if out_f16 else torch.float32
+    got = host(A.unpack_dequant(qw, sc, qz, d_out, G, sdev, odt))
+    ref = O.unpack_dequant(host(qw), host(sc), host(qz), d_out, G, s if with_s else None)
+    if out_f16:
+        assert np.array_equal(got.view(np.uint16), ref.astype(np.float16).view(np.uint16))
+    else:
+        assert np.array_equal(got, ref)
+
+
 # ---------------------------------------------------------------------------
 # A4 output score, A6 clip search (matrix cores)
 # ---------------------------------------------------------------------------
@@ -250,17 +272,19 @@ def test_clip_search(A, parts, d_in, T, G):
     xm = O.act_stats(X)
     res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
                           n_clip=20, want_clip_err=True)
-    _, k, s = O.search_scales([W], xm, G, 20, "output", X=X)
-    assert ulp_dist(host(res.best_s), s) <= 2 or int(host(res.best_idx)[0]) != k
+    errs, k, _ = O.search_scales([W], xm, G, 20, "output", X=X)
+    g_k = int(host(res.best_idx)[0])
+    assert argmin_ok(g_k, errs, k)
+    s = O.candidate_scales(xm, 20)[g_k]          # the clip search runs on the chosen row
+    assert ulp_dist(host(res.best_s), s) <= 2
     E, c = O.clip_search(W, s, X, G, 20, 0.5)
     g_E = host(res.clip_err).astype(np.float64)
-    # per-row errors: one row's (w_hat - W) in fp16 (2^-12 relative rounding) -> 2e-3 bound
-    np.testing.assert_allclose(g_E, E, rtol=2e-3)
+    np.testing.assert_allclose(g_E, E, rtol=1e-3)
     g_c = host(res.clip)
     ratios = O.clip_ratios(20, 0.5)
     for o in range(d_out):
         gj = int(np.nonzero(ratios == g_c[o])[0][0])
-        assert argmin_ok(gj, E[o], O.first_argmin(E[o]), rel=2e-3), o
+        assert argmin_ok(gj, E[o], O.first_argmin(E[o]), rel=1e-4), o
     # the oracle's scale and clip choice pack bit-exactly
     _pack_compare(A, W, G, s, c)
 
