@@ -67,6 +67,12 @@ PMC_TRAFFIC = {
         "fetch_kib": 16758.4, "write_kib": 640.0,
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
         "sha256": "defe0c2e9940a8e54a9e9e972d928a3348712ea21d6d59d02dfc4e145d6bede3"},
+    # the 36-block sweep at G = 128: mean over the 144 search launches of a step
+    # (the four group shapes, 36 times each); profiles/sweep_qwen3_8b_36_blocks.md
+    ("search_weight_kernel", "qwen3_8b_sweep"): {
+        "fetch_kib": 47659.7, "write_kib": 1840.0,
+        "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
+        "sha256": "defe0c2e9940a8e54a9e9e972d928a3348712ea21d6d59d02dfc4e145d6bede3"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
         "fetch_kib": 11797680.2, "write_kib": 30720.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
@@ -558,39 +564,60 @@ def bench_sweep(args):
     torch.cuda.synchronize()
     out_all = {}
     for G in wl.group_sizes:
-        xms = [torch.empty(g.d_in, device=dev) for g in wl.groups]
-        ws_stats = [A.workspace(A.act_stats_workspace_bytes(g.T, g.d_in), dev) for g in wl.groups]
-        ws = [A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G, duo=args.duo, asym=args.asym), dev)
-              for g in wl.groups]
-        res = [A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
-                              torch.empty(g.d_in, device=dev), None, None) for g in wl.groups]
-        packs = [[(torch.empty((g.d_in, r // 8), dtype=torch.int32, device=dev),
-                   torch.empty((g.d_in // G, r), dtype=torch.float16, device=dev),
-                   torch.empty((g.d_in // G, r // 8), dtype=torch.int32, device=dev)) for r in g.parts]
-                 for g in wl.groups]
+        # one x_mean per block and group: the statistics of later blocks may be
+        # taken while earlier blocks are still being searched
+        xmb = [[torch.empty(g.d_in, device=dev) for g in wl.groups] for _ in range(blocks)]
+        # workspaces and results per lane (a stream of the "blocks" schedule) and group kind
+        n_lane = args.streams if args.schedule == "blocks" else 1
+        ws_stats = [[A.workspace(A.act_stats_workspace_bytes(g.T, g.d_in), dev) for g in wl.groups]
+                    for _ in range(n_lane)]
+        ws = [[A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G, duo=args.duo, asym=args.asym),
+                           dev) for g in wl.groups] for _ in range(n_lane)]
+        res = [[A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+                               torch.empty(g.d_in, device=dev), None, None) for g in wl.groups]
+               for _ in range(n_lane)]
+        packs = [[[(torch.empty((g.d_in, r // 8), dtype=torch.int32, device=dev),
+                    torch.empty((g.d_in // G, r), dtype=torch.float16, device=dev),
+                    torch.empty((g.d_in // G, r // 8), dtype=torch.int32, device=dev)) for r in g.parts]
+                  for g in wl.groups] for _ in range(n_lane)]
         K = args.steps
         per = 6 * ng * blocks
         ev = HipEvents(per * K)
-        # The groups of a block are independent chains (own statistics, search and
-        # packing; own workspaces and outputs): the timed steps put each group
-        # kind on a stream of its own, joined to the main stream at both ends.
-        # Kernel durations come from the same steps on the main stream alone.
+        # Schedules of the timed steps (kernel durations come from the same steps
+        # on the main stream alone, events around each kernel).  Every group's
+        # chain (statistics, candidates, search, select, pack) is in order on one
+        # stream; the streams are joined to the main stream at both ends of a step:
+        # * "blocks": block b on stream b % streams, so that at any moment some
+        #   streams stream calibration inputs (HBM-bound statistics) while others
+        #   search (VALU-bound); the statistics and selection kernels are sized to
+        #   fit on a compute unit beside the search kernel's three waves per SIMD;
+        # * "groups": group kind g on stream g % streams;
+        # * "pipeline": all statistics on one stream, running ahead, every search
+        #   waiting for its statistics through an event (the searches on a second
+        #   stream).
         main = torch.cuda.current_stream()
-        streams = [torch.cuda.Stream() for _ in range(args.streams)]
+        n_side = 2 if args.schedule == "pipeline" else args.streams
+        streams = [torch.cuda.Stream() for _ in range(n_side)]
+        ready = [[torch.cuda.Event() for _ in range(ng)] for _ in range(blocks)]
 
-        def plans(stream_of):
-            st = [[A.ActStatsPlan(Xs[b][gi], x_mean=xms[gi], ws=ws_stats[gi], stream=stream_of(gi))
+        def plans(stats_stream, work_stream, lane_of):
+            st = [[A.ActStatsPlan(Xs[b][gi], x_mean=xmb[b][gi], ws=ws_stats[lane_of(b)][gi], stream=stats_stream(b, gi))
                    for gi in range(ng)] for b in range(blocks)]
-            se = [[A.SearchPlan(Ws[b][gi], xms[gi], group_size=G, ws=ws[gi], out=res[gi], stream=stream_of(gi),
-                                 duo=args.duo, asym=args.asym)
+            se = [[A.SearchPlan(Ws[b][gi], xmb[b][gi], group_size=G, ws=ws[lane_of(b)][gi], out=res[lane_of(b)][gi],
+                                 stream=work_stream(b, gi), duo=args.duo, asym=args.asym)
                    for gi in range(ng)] for b in range(blocks)]
-            pk = [[[A.PackPlan(p, G, res[gi].best_s, out=o, stream=stream_of(gi), asym=args.asym)
-                    for p, o in zip(Ws[b][gi], packs[gi])]
+            pk = [[[A.PackPlan(p, G, res[lane_of(b)][gi].best_s, out=o, stream=work_stream(b, gi), asym=args.asym)
+                    for p, o in zip(Ws[b][gi], packs[lane_of(b)][gi])]
                    for gi in range(ng)] for b in range(blocks)]
             return st, se, pk
 
-        par = plans(lambda gi: streams[gi % len(streams)])
-        ser = plans(lambda gi: main)
+        if args.schedule == "pipeline":
+            par = plans(lambda b, gi: streams[0], lambda b, gi: streams[1], lambda b: 0)
+        elif args.schedule == "blocks":
+            par = plans(lambda b, gi: streams[b % n_side], lambda b, gi: streams[b % n_side], lambda b: b % n_side)
+        else:
+            par = plans(lambda b, gi: streams[gi % n_side], lambda b, gi: streams[gi % n_side], lambda b: 0)
+        ser = plans(lambda b, gi: main, lambda b, gi: main, lambda b: 0)
 
         def step(pl, k=-1):
             st_plans, se_plans, pk_plans = pl
@@ -611,7 +638,31 @@ def bench_sweep(args):
             if k >= 0:
                 A.set_timing_events(None, None)
 
+        def step_pipeline():
+            st_plans, se_plans, pk_plans = par
+            start = torch.cuda.Event()
+            start.record(main)
+            for s_ in streams:
+                s_.wait_event(start)
+            for b in range(blocks):
+                for gi in range(ng):
+                    st_plans[b][gi].launch()
+                    ready[b][gi].record(streams[0])
+            for b in range(blocks):
+                for gi in range(ng):
+                    streams[1].wait_event(ready[b][gi])
+                    se_plans[b][gi].launch()
+                    for pp in pk_plans[b][gi]:
+                        pp.launch()
+            for s_ in streams:
+                done = torch.cuda.Event()
+                done.record(s_)
+                main.wait_event(done)
+
         def step_streams():
+            if args.schedule == "pipeline":
+                step_pipeline()
+                return
             start = torch.cuda.Event()
             start.record(main)
             for s_ in streams:
@@ -667,7 +718,8 @@ def bench_sweep(args):
         "config": {"workload": wl_key, "blocks": blocks, "weights": n_w, "n_grid": 20,
                    "group_size": G0, "group_sizes": list(wl.group_sizes), "score": "weight",
                    "calibration_tokens_per_group": wl.groups[0].T, "x_per_block": True,
-                   "x_dtype": "bf16", "streams": args.streams, "duo": args.duo, "asym": args.asym},
+                   "x_dtype": "bf16", "schedule": args.schedule,
+                   "streams": 2 if args.schedule == "pipeline" else args.streams, "duo": args.duo, "asym": args.asym},
         "per_group_size": out_all,
         "pack_GBps": first["pack_GBps"], "pack_hbm_frac": first["pack_hbm_frac"],
         "act_stats_GBps": first["act_stats_GBps"], "act_stats_hbm_frac": first["act_stats_hbm_frac"],
@@ -979,6 +1031,58 @@ def bench_w4a16(args):
     return out
 
 
+PROBE_KINDS = ["v_fma_f32", "v_mul_f32", "v_add_f32", "v_max3_f32", "v_rndne_f32", "v_fmac_f32",
+               "v_cvt_f32_f16", "v_max_u32 (DPP row_half_mirror)", "v_fma_f32 + v_rndne_f32",
+               "v_fma_f32 + v_mul_f32", "v_fma_f32 + v_max3_f32",
+               "search element mix (mul, mul, max3, fma, fma, add, add, fma x4)"]
+
+
+def bench_valu_probe(args):
+    """VALU issue rate by instruction class (the probe library): for 1, 2, 3, 4
+    and 8 waves per SIMD, wave64 instructions per second, as fp32 lane
+    operations per second over the whole chip and as wave instructions per
+    clock per SIMD at the published 2.4 GHz."""
+    import torch
+    from post_weight_quantization_awq_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        B.build_probe()
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.awq_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.awq_probe_valu.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4000
+    s = torch.cuda.current_stream()
+    res = {}
+    best = 0.0
+    for kind in range(lib.awq_probe_valu_kinds()):
+        ipt = lib.awq_probe_valu_insts_per_trip(kind)
+        row = {}
+        for w in (1, 2, 3, 4, 8):
+            blocks = n_cu * w                         # 4 waves per block: w waves per SIMD
+            out = torch.empty(blocks * 256, device="cuda")
+            for _ in range(2):
+                assert lib.awq_probe_valu(kind, blocks, iters, out.data_ptr(), s.cuda_stream) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                assert lib.awq_probe_valu(kind, blocks, iters, out.data_ptr(), s.cuda_stream) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / args.steps
+            wave_insts = blocks * 4 * iters * ipt
+            lane_ops = wave_insts * 64 / t / 1e12
+            row[f"{w}_waves_per_simd"] = {"lane_ops_T_per_s": lane_ops, "us": t * 1e6,
+                                          "wave_insts_per_clk_per_simd_at_2.4GHz": wave_insts / t / (n_cu * 4 * 2.4e9)}
+            best = max(best, lane_ops)
+        res[PROBE_KINDS[kind]] = row
+    return {"metric": "VALU issue rate (probe)", "value": best, "unit": "T fp32 lane-ops/s (best kind and occupancy)",
+            "n_gpus": 1, "steps": args.steps, "warmup": 2, "ms_per_step": None, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "valu_issue_probe", "compute_units": n_cu, "iters": iters,
+                       "chains_per_lane": 8, "threads_per_block": 256},
+            "derived_peak_T": VALU_LANE_OPS_PEAK_T, "kinds": res}
+
+
 def bench_copy(args):
     """Plain device copy of 512 MiB (torch), the calibration of the HBM byte counters."""
     import torch
@@ -1007,11 +1111,15 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_8b_sweep",
                     choices=["single_linear_256x512", "q_proj_4096x4096", "qkv_6144x4096_output",
                              "mlp_output_clip", "qwen3_8b_sweep", "qwen3_8b_export", "qwen3_8b_decode_w4a16",
-                             "copy_512MiB"])
+                             "copy_512MiB", "valu_issue_probe"])
     ap.add_argument("--group-size", type=int, default=None)
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
-    ap.add_argument("--streams", type=int, default=4,
-                    help="streams the sweep's group kinds are spread over in the timed steps")
+    ap.add_argument("--streams", type=int, default=8,
+                    help="streams of the sweep's timed steps (--schedule blocks or groups)")
+    ap.add_argument("--schedule", default="blocks", choices=["blocks", "groups", "pipeline"],
+                    help="sweep schedule: blocks round-robin over the streams (blocks), one stream per group "
+                         "kind (groups), or the statistics on a stream of their own running ahead of the "
+                         "searches (pipeline)")
     ap.add_argument("--duo", action="store_true",
                     help="duo-scaling candidates (x_mean^r / (w_mean^(1-r) + 1e-4)) in the search workloads")
     ap.add_argument("--asym", action="store_true",
@@ -1046,6 +1154,8 @@ def main() -> int:
         out = bench_w4a16(args)
     elif args.workload == "copy_512MiB":
         out = bench_copy(args)
+    elif args.workload == "valu_issue_probe":
+        out = bench_valu_probe(args)
     else:
         out = bench_output(args, args.workload)
     print(json.dumps(out), flush=True)

@@ -15,6 +15,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq.so")
+# the VALU issue-rate probe behind the search kernel's ALU peak (bench.py
+# --workload valu_issue_probe): a library of its own, not part of libawq
+PROBE_SRC = os.path.join(PKG, "probe", "valu_issue.hip")
+PROBE_LIB = os.path.join(PKG, "libawq_probe.so")
 ARCH = os.environ.get("AWQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -59,7 +63,18 @@ def build(jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *CFLAGS, "-shared", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{errs}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -40,6 +40,8 @@ def A():
     (53, 515, "f16", 0),        # d_in not a multiple of 8 (scalar path)
     (77, 256, "bf16", 40),      # leading dimension > d_in (strided rows)
     (1, 64, "bf16", 0),
+    (16400, 4096, "bf16", 0),   # 128-row splits (>= 1024 blocks) + a 16-row tail
+    (32831, 2048, "f16", 0),    # 128-row splits on 4 column strips, a 63-row tail
 ])
 def test_act_stats(A, T, d_in, dtype, pad):
     import torch

@@ -73,7 +73,7 @@ def test_pack_half_way_ties(A, G, with_s):
     assert np.array_equal(host(qz), rqz)
     # the page's rounding at the ties themselves: half to the even neighbour
     u = O.unpack_codes(host(qw), d_out).astype(np.int64) - 7
-    v = W.astype(np.float64) * (1.0 if s is None else s.astype(np.float64))[None, :]
+    v = W.astype(np.float64) * (np.ones(d_in) if s is None else s.astype(np.float64))[None, :]
     r = v / np.repeat(rstep.astype(np.float64), G, axis=1)
     tie = np.abs(r - np.floor(r)) == 0.5
     assert np.all(u[tie] % 2 == 0)
