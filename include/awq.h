@@ -216,6 +216,31 @@ awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_w
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * awq_search_scales_noalloc -- awq_search_scales (weight score) for callers
+ * that cannot allocate device memory: code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc.
+ *
+ * Same computation, arguments and results as awq_search_scales with
+ * cfg->score = AWQ_SCORE_WEIGHT, cfg->n_clip = 0 (X, clip, clip_err absent),
+ * duo and asymmetric flags allowed.  The scratch (candidate table, (x/s)^2,
+ * per-block partial errors, and the duo statistic) is a 16 MiB array inside
+ * the library, one per GPU, held until the process ends; the call uses the
+ * copy of the current device (hipGetDevice), which must be the device of
+ * `stream` and of every pointer.  The first call on a device looks up that
+ * copy's address; no call allocates or frees memory.  Searches that need more
+ * than 16 MiB of scratch (d_in x n_grid x 8 bytes of tables plus 4 bytes per
+ * block and candidate: every Qwen3-8B-shaped group fits at n_grid = 20) are
+ * rejected with AWQ_EWORKSPACE before anything is enqueued; the output score
+ * and the clip search are rejected with AWQ_EINVAL (they need gigabytes).
+ * Every kernel writes the scratch it reads before reading it, so nothing in it
+ * needs clearing, but all calls on one GPU share it: calls that overlap on one
+ * GPU (two streams, two host threads) race and must be serialized by the caller.
+ * ------------------------------------------------------------------------- */
+awq_status awq_search_scales_noalloc(const awq_search_cfg* cfg /* [host] */, const awq_wgroup* W /* [host] */,
+                                     int64_t d_in, const float* x_mean, float* err, int32_t* best_idx,
+                                     float* best_s, void* stream);
+
+/* ---------------------------------------------------------------------------
  * awq_quantize_pack -- quantize W*s and pack into the AutoAWQ GEMM layout.
  * [konic] Group-wise symmetric INT4; AutoAWQ / HF-AWQ GEMM on-disk format
  * (unsigned codes, 8 per int32, pack order [0,2,4,6,1,3,5,7]); exporter step 4

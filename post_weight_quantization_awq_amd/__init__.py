@@ -40,7 +40,7 @@ EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales_wo
             "awq_search_workspace", "awq_search_scales", "awq_quantize_pack", "awq_quantize_pack_asym",
             "awq_unpack_dequant", "awq_norm_group_fold", "awq_weight_channel_mean_workspace",
             "awq_weight_channel_mean", "awq_candidate_scales_duo_workspace", "awq_candidate_scales_duo",
-            "awq_w4a16_workspace", "awq_w4a16_matmul",
+            "awq_w4a16_workspace", "awq_w4a16_matmul", "awq_search_scales_noalloc",
             "awq_last_error", "awq_abi_version", "awq_set_timing_events")
 
 
@@ -88,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "awq_w4a16_workspace": [I64, I64, I64, PSZ],
         "awq_w4a16_matmul": [P, I64, I64, P, P, P, I64, I64, I32, P, I64, I32, P, SZ, P],
         "awq_set_timing_events": [P, P],
+        "awq_search_scales_noalloc": [ctypes.POINTER(SearchCfg), ctypes.POINTER(WGroup), I64, P, P, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -376,6 +377,33 @@ class SearchPlan(_Prepared):
         return self.out
 
 
+def search_scales_noalloc(W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, out: SearchResult, *,
+                          group_size: int = 128, n_grid: int = 20, s_min: float = 1e-4, duo: bool = False,
+                          asym: bool = False, stream=None) -> SearchResult:
+    """Weight-score search through awq_search_scales_noalloc: the library's own
+    per-GPU scratch, no workspace, nothing allocated (the caller passes `out`).
+    Calls that overlap on one GPU share that scratch and must not run concurrently."""
+    parts: List[torch.Tensor] = list(W_parts)
+    if not parts:
+        raise ValueError("empty weight group")
+    d_in = parts[0].shape[1]
+    for p in parts:
+        if p.dtype != torch.float16 or p.dim() != 2 or not p.is_contiguous() or p.shape[1] != d_in:
+            raise ValueError("weights must be contiguous fp16 [rows, d_in] with one d_in")
+        if p.device != parts[0].device:
+            raise ValueError("the parts of a group must live on one device")
+    _tensor(x_mean, "x_mean", torch.float32, (d_in,), like=parts[0])
+    _tensor(out.err, "out.err", torch.float32, (n_grid,), like=parts[0])
+    _tensor(out.best_idx, "out.best_idx", torch.int32, (1,), like=parts[0])
+    _tensor(out.best_s, "out.best_s", torch.float32, (d_in,), like=parts[0])
+    _dev(parts[0], "W")
+    cfg = _cfg(group_size, n_grid, "weight", 0, 0.5, s_min, duo, asym)
+    grp, keep = _wgroup(parts)
+    _check(lib().awq_search_scales_noalloc(ctypes.byref(cfg), ctypes.byref(grp), d_in, _ptr(x_mean), _ptr(out.err),
+                                           _ptr(out.best_idx), _ptr(out.best_s), _stream(stream)))
+    return out
+
+
 def search_scales(W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, **kw) -> SearchResult:
     """Grid search of alpha for one group of linears sharing an input (rows concatenated)."""
     return SearchPlan(W_parts, x_mean, **kw).run()
@@ -537,6 +565,6 @@ def set_timing_events(before: Optional[int], after: Optional[int]) -> None:
     _check(lib().awq_set_timing_events(before, after))
 
 
-__all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "PackPlan", "FoldPlan", "norm_group_fold",
+__all__ = ["set_timing_events", "ActStatsPlan", "SearchPlan", "search_scales_noalloc", "PackPlan", "FoldPlan", "norm_group_fold",
            "weight_channel_mean", "candidate_scales_duo", "W4A16Plan", "w4a16_matmul", "AwqError", "act_stats", "candidate_scales", "search_scales", "quantize_pack", "unpack_dequant",
            "search_workspace_bytes", "act_stats_workspace_bytes", "SearchResult", "lib", "LIB_PATH"]

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/awq.h"
 #include "awq_device.h"
 #include "awq_launch.h"
@@ -440,6 +442,62 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
       return hip_status(e, "clip_select");
   }
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Weight-score search without a caller workspace: the scratch lives in a
+// file-scope device array (one copy per GPU, kept until the process ends).
+// Host code never uses the array's name as an address: the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's scratch (set up on first use)
+awq_status device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AWQ_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(AWQ_EINVAL, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(AWQ_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return AWQ_OK;
+}
+}  // namespace
+
+extern "C" awq_status awq_search_scales_noalloc(const awq_search_cfg* cfg, const awq_wgroup* W, int64_t d_in,
+                                                const float* x_mean, float* err, int32_t* best_idx, float* best_s,
+                                                void* stream) {
+  awq_status st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->score != AWQ_SCORE_WEIGHT || cfg->n_clip != 0)
+    return fail(AWQ_EINVAL, "awq_search_scales_noalloc: weight score only (no output score, no clip search)");
+  WParts parts;
+  int64_t d_out = 0;
+  if ((st = read_group(W, &parts, &d_out))) return st;
+  if (d_in < cfg->group_size || d_in % cfg->group_size)
+    return fail(AWQ_ESHAPE, "d_in %lld not a positive multiple of group_size %d", (long long)d_in, cfg->group_size);
+  const size_t need = plan_search(*cfg, d_out, d_in, 0).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(AWQ_EWORKSPACE, "awq_search_scales_noalloc: this search needs %zu bytes of scratch, more than the "
+                "library's %zu", need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((st = device_scratch(&ws))) return st;
+  return awq_search_scales(cfg, W, d_in, x_mean, nullptr, AWQ_BF16, 0, 0, err, best_idx, best_s, nullptr, nullptr,
+                           ws, kNoAllocScratchBytes, stream);
 }
 
 // ---------------------------------------------------------------------------
