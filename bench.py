@@ -101,17 +101,30 @@ def pmc_traffic(kernel: str, workload: str, args=None):
 class HipEvents:
     """Raw hipEvent_t pairs through the HIP runtime already loaded by torch."""
 
-    def __init__(self, n: int):
+    def __init__(self, n: int, timing: bool = True):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            if timing:
+                assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            else:   # hipEventDisableTiming: a plain dependency marker
+                assert self.hip.hipEventCreateWithFlags(ctypes.byref(e), 2) == 0
             self.ev.append(e)
+
+    def record(self, i: int, stream) -> None:
+        assert self.hip.hipEventRecord(self.ev[i], stream.cuda_stream) == 0
+
+    def wait(self, stream, i: int) -> None:
+        """`stream` waits for event i (enqueued; the host does not wait)."""
+        assert self.hip.hipStreamWaitEvent(stream.cuda_stream, self.ev[i], 0) == 0
 
     def ms(self, a: int, b: int) -> float:
         assert self.hip.hipEventSynchronize(self.ev[b]) == 0
@@ -568,7 +581,7 @@ def bench_sweep(args):
         # taken while earlier blocks are still being searched
         xmb = [[torch.empty(g.d_in, device=dev) for g in wl.groups] for _ in range(blocks)]
         # workspaces and results per lane (a stream of the "blocks" schedule) and group kind
-        n_lane = args.streams if args.schedule == "blocks" else 1
+        n_lane = args.streams if args.schedule == "blocks" else (2 if args.schedule == "pipeline" else 1)
         ws_stats = [[A.workspace(A.act_stats_workspace_bytes(g.T, g.d_in), dev) for g in wl.groups]
                     for _ in range(n_lane)]
         ws = [[A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G, duo=args.duo, asym=args.asym),
@@ -584,21 +597,21 @@ def bench_sweep(args):
         per = 6 * ng * blocks
         ev = HipEvents(per * K)
         # Schedules of the timed steps (kernel durations come from the same steps
-        # on the main stream alone, events around each kernel).  Every group's
-        # chain (statistics, candidates, search, select, pack) is in order on one
-        # stream; the streams are joined to the main stream at both ends of a step:
-        # * "blocks": block b on stream b % streams, so that at any moment some
-        #   streams stream calibration inputs (HBM-bound statistics) while others
-        #   search (VALU-bound); the statistics and selection kernels are sized to
-        #   fit on a compute unit beside the search kernel's three waves per SIMD;
-        # * "groups": group kind g on stream g % streams;
-        # * "pipeline": all statistics on one stream, running ahead, every search
-        #   waiting for its statistics through an event (the searches on a second
-        #   stream).
+        # on the main stream alone, events around each kernel).  The side
+        # streams are forked from and joined to the main stream at both ends of
+        # a step with HIP events:
+        # * "pipeline": all statistics on one stream, running ahead; the
+        #   searches (with select and pack) on two streams, alternating blocks,
+        #   each waiting for its group's statistics through an event; the
+        #   HBM-bound statistics of later groups stream while the VALU-bound
+        #   searches of earlier ones compute;
+        # * "blocks": block b's whole chain on stream b % streams;
+        # * "groups": group kind g's chain on stream g % streams.
         main = torch.cuda.current_stream()
-        n_side = 2 if args.schedule == "pipeline" else args.streams
+        n_side = 3 if args.schedule == "pipeline" else args.streams
         streams = [torch.cuda.Stream() for _ in range(n_side)]
-        ready = [[torch.cuda.Event() for _ in range(ng)] for _ in range(blocks)]
+        sync = HipEvents(blocks * ng + n_side + 1, timing=False)   # per-group readiness, fork, joins
+        E_FORK = blocks * ng
 
         def plans(stats_stream, work_stream, lane_of):
             st = [[A.ActStatsPlan(Xs[b][gi], x_mean=xmb[b][gi], ws=ws_stats[lane_of(b)][gi], stream=stats_stream(b, gi))
@@ -612,7 +625,7 @@ def bench_sweep(args):
             return st, se, pk
 
         if args.schedule == "pipeline":
-            par = plans(lambda b, gi: streams[0], lambda b, gi: streams[1], lambda b: 0)
+            par = plans(lambda b, gi: streams[0], lambda b, gi: streams[1 + b % 2], lambda b: b % 2)
         elif args.schedule == "blocks":
             par = plans(lambda b, gi: streams[b % n_side], lambda b, gi: streams[b % n_side], lambda b: b % n_side)
         else:
@@ -638,40 +651,36 @@ def bench_sweep(args):
             if k >= 0:
                 A.set_timing_events(None, None)
 
+        def fork():
+            sync.record(E_FORK, main)
+            for s_ in streams:
+                sync.wait(s_, E_FORK)
+
+        def join():
+            for j, s_ in enumerate(streams):
+                sync.record(E_FORK + 1 + j, s_)
+                sync.wait(main, E_FORK + 1 + j)
+
         def step_pipeline():
             st_plans, se_plans, pk_plans = par
-            start = torch.cuda.Event()
-            start.record(main)
-            for s_ in streams:
-                s_.wait_event(start)
             for b in range(blocks):
                 for gi in range(ng):
                     st_plans[b][gi].launch()
-                    ready[b][gi].record(streams[0])
+                    sync.record(b * ng + gi, streams[0])
             for b in range(blocks):
                 for gi in range(ng):
-                    streams[1].wait_event(ready[b][gi])
+                    sync.wait(streams[1 + b % 2], b * ng + gi)
                     se_plans[b][gi].launch()
                     for pp in pk_plans[b][gi]:
                         pp.launch()
-            for s_ in streams:
-                done = torch.cuda.Event()
-                done.record(s_)
-                main.wait_event(done)
 
         def step_streams():
+            fork()
             if args.schedule == "pipeline":
                 step_pipeline()
-                return
-            start = torch.cuda.Event()
-            start.record(main)
-            for s_ in streams:
-                s_.wait_event(start)
-            step(par)
-            for s_ in streams:
-                done = torch.cuda.Event()
-                done.record(s_)
-                main.wait_event(done)
+            else:
+                step(par)
+            join()
 
         for _ in range(args.warmup):
             step_streams()
@@ -690,6 +699,7 @@ def bench_sweep(args):
             sums[1] += ev.ms(n + 2, n + 3)
             sums[2] += ev.ms(n + 4, n + 5)
         ev.close()
+        sync.close()
         sums = [s / args.steps for s in sums]
         n_w = blocks * sum(g.d_out * g.d_in for g in wl.groups)
         pk = blocks * sum(pack_bytes(r, g.d_in, G) for g in wl.groups for r in g.parts)
@@ -719,7 +729,7 @@ def bench_sweep(args):
                    "group_size": G0, "group_sizes": list(wl.group_sizes), "score": "weight",
                    "calibration_tokens_per_group": wl.groups[0].T, "x_per_block": True,
                    "x_dtype": "bf16", "schedule": args.schedule,
-                   "streams": 2 if args.schedule == "pipeline" else args.streams, "duo": args.duo, "asym": args.asym},
+                   "streams": 3 if args.schedule == "pipeline" else args.streams, "duo": args.duo, "asym": args.asym},
         "per_group_size": out_all,
         "pack_GBps": first["pack_GBps"], "pack_hbm_frac": first["pack_hbm_frac"],
         "act_stats_GBps": first["act_stats_GBps"], "act_stats_hbm_frac": first["act_stats_hbm_frac"],
@@ -1116,10 +1126,10 @@ def main() -> int:
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
     ap.add_argument("--streams", type=int, default=8,
                     help="streams of the sweep's timed steps (--schedule blocks or groups)")
-    ap.add_argument("--schedule", default="blocks", choices=["blocks", "groups", "pipeline"],
-                    help="sweep schedule: blocks round-robin over the streams (blocks), one stream per group "
-                         "kind (groups), or the statistics on a stream of their own running ahead of the "
-                         "searches (pipeline)")
+    ap.add_argument("--schedule", default="pipeline", choices=["pipeline", "blocks", "groups"],
+                    help="sweep schedule: the statistics on a stream of their own running ahead of the searches "
+                         "on two streams (pipeline), blocks round-robin over the streams (blocks), or one "
+                         "stream per group kind (groups)")
     ap.add_argument("--duo", action="store_true",
                     help="duo-scaling candidates (x_mean^r / (w_mean^(1-r) + 1e-4)) in the search workloads")
     ap.add_argument("--asym", action="store_true",
