@@ -1048,10 +1048,11 @@ PROBE_KINDS = ["v_fma_f32", "v_mul_f32", "v_add_f32", "v_max3_f32", "v_rndne_f32
 
 
 def bench_valu_probe(args):
-    """VALU issue rate by instruction class (the probe library): for 1, 2, 3, 4
-    and 8 waves per SIMD, wave64 instructions per second, as fp32 lane
+    """Issue rates (the probe library).  VALU by instruction class: for 1, 2, 3,
+    4 and 8 waves per SIMD, wave64 instructions per second, as fp32 lane
     operations per second over the whole chip and as wave instructions per
-    clock per SIMD at the published 2.4 GHz."""
+    clock per SIMD at the published 2.4 GHz.  Matrix cores: 32x32x16 fp16
+    products back to back on register operands, zero and random data."""
     import torch
     from post_weight_quantization_awq_amd import build as B
     if not os.path.exists(B.PROBE_LIB):
@@ -1085,12 +1086,37 @@ def bench_valu_probe(args):
                                           "wave_insts_per_clk_per_simd_at_2.4GHz": wave_insts / t / (n_cu * 4 * 2.4e9)}
             best = max(best, lane_ops)
         res[PROBE_KINDS[kind]] = row
+    # matrix cores: back-to-back 32x32x16 fp16 products on register operands,
+    # 2 waves per SIMD, on all-zero and on random operands
+    lib.awq_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.awq_probe_mfma.restype = ctypes.c_int
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    mfma = {}
+    blocks, m_iters = n_cu * 2, 2000
+    out = torch.empty(blocks * 256, device="cuda")
+    for name, fill in (("zero operands", lambda n: torch.zeros(n, dtype=torch.float16, device="cuda")),
+                       ("random operands N(0,1) fp16", lambda n: torch.randn(n, generator=g, device="cuda").half())):
+        Ab, Bb = fill(4 * 64 * 8), fill(2 * 64 * 8)
+        for _ in range(2):
+            assert lib.awq_probe_mfma(blocks, m_iters, Ab.data_ptr(), Bb.data_ptr(), out.data_ptr(), s.cuda_stream) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            assert lib.awq_probe_mfma(blocks, m_iters, Ab.data_ptr(), Bb.data_ptr(), out.data_ptr(), s.cuda_stream) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / args.steps
+        tf = blocks * 4 * m_iters * 8 * 2 * 32 * 32 * 16 / t / 1e12
+        mfma[name] = {"TFLOP_per_s": tf, "frac_of_2500": tf / MFMA_FP16_PEAK_TFLOPS, "us": t * 1e6}
     return {"metric": "VALU issue rate (probe)", "value": best, "unit": "T fp32 lane-ops/s (best kind and occupancy)",
             "n_gpus": 1, "steps": args.steps, "warmup": 2, "ms_per_step": None, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "valu_issue_probe", "compute_units": n_cu, "iters": iters,
                        "chains_per_lane": 8, "threads_per_block": 256},
-            "derived_peak_T": VALU_LANE_OPS_PEAK_T, "kinds": res}
+            "derived_peak_T": VALU_LANE_OPS_PEAK_T, "kinds": res,
+            "mfma_f32_32x32x16_f16_2_waves_per_simd": mfma}
 
 
 def bench_copy(args):

@@ -26,15 +26,20 @@
  *     sized by the matching *_workspace query.
  *   - Matrices are row-major.  Weights are fp16 [rows, d_in]; activations are
  *     fp16 or bf16 [T, d_in] with a leading dimension `ld_x` >= d_in (elements).
- *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
- *     call validates its arguments synchronously on the host, then enqueues its
- *     kernels asynchronously on `stream`; results are ready when the stream is.
+ *   - `stream` is a hipStream_t (NULL = the null stream); the header declares
+ *     the handle type itself, identically to HIP's own declaration, so that it
+ *     needs no HIP header.  Every call validates its arguments synchronously on
+ *     the host, then enqueues its kernels asynchronously on `stream`; results
+ *     are ready when the stream is.
  *   - Inputs are never modified.  On any argument error nothing is launched and
  *     outputs are untouched; the call returns a nonzero status and
  *     awq_last_error() describes it.  A launch failure returns AWQ_EHIP.
- *   - No global mutable device state: calls on distinct streams may run
- *     concurrently if their buffers are distinct.  Results are deterministic
- *     (fixed-order reductions, no floating-point atomics).
+ *   - No global mutable device state, except the scratch array of
+ *     awq_search_scales_noalloc (see there): other calls on distinct streams may
+ *     run concurrently if their buffers are distinct.  Results are
+ *     deterministic (fixed-order reductions, no floating-point atomics).  The
+ *     only host-side state is per host thread: the last error message and the
+ *     benchmark hook awq_set_timing_events.
  */
 #ifndef AWQ_H
 #define AWQ_H
@@ -45,6 +50,8 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+typedef struct ihipStream_t* hipStream_t;   /* identical to HIP's declaration */
 
 typedef int32_t awq_status;
 #define AWQ_OK 0
@@ -111,7 +118,7 @@ typedef struct {
 awq_status awq_act_stats_workspace(int64_t T, int64_t d_in, size_t* bytes /* [host] */);
 awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in, int64_t ld_x,
                          float inv_count, int32_t accumulate, float* x_mean,
-                         void* ws, size_t ws_bytes, void* stream);
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_candidate_scales -- the candidate scale table of the grid search.
@@ -127,7 +134,7 @@ awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in
  * ------------------------------------------------------------------------- */
 awq_status awq_candidate_scales_workspace(int64_t d_in, int32_t n_grid, size_t* bytes /* [host] */);
 awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_grid, double s_min,
-                                float* S, void* ws, size_t ws_bytes, void* stream);
+                                float* S, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_weight_channel_mean -- duo scaling's weight statistic.
@@ -144,7 +151,7 @@ awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_gri
  * ------------------------------------------------------------------------- */
 awq_status awq_weight_channel_mean_workspace(int64_t d_out_total, int64_t d_in, size_t* bytes /* [host] */);
 awq_status awq_weight_channel_mean(const awq_wgroup* W /* [host] */, int64_t d_in, float* w_mean, void* ws,
-                                   size_t ws_bytes, void* stream);
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_candidate_scales_duo -- the duo-scaling candidate table.
@@ -160,7 +167,7 @@ awq_status awq_weight_channel_mean(const awq_wgroup* W /* [host] */, int64_t d_i
  * ------------------------------------------------------------------------- */
 awq_status awq_candidate_scales_duo_workspace(int64_t d_in, int32_t n_grid, size_t* bytes /* [host] */);
 awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, int64_t d_in, int32_t n_grid,
-                                    double s_min, float* S, void* ws, size_t ws_bytes, void* stream);
+                                    double s_min, float* S, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_search_scales -- grid search of alpha for one input-sharing group.
@@ -213,7 +220,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_w
                              const void* X, int32_t x_dtype, int64_t T, int64_t ld_x,
                              float* err, int32_t* best_idx, float* best_s,
                              float* clip, float* clip_err,
-                             void* ws, size_t ws_bytes, void* stream);
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_search_scales_noalloc -- awq_search_scales (weight score) for callers
@@ -238,7 +245,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_w
  * ------------------------------------------------------------------------- */
 awq_status awq_search_scales_noalloc(const awq_search_cfg* cfg /* [host] */, const awq_wgroup* W /* [host] */,
                                      int64_t d_in, const float* x_mean, float* err, int32_t* best_idx,
-                                     float* best_s, void* stream);
+                                     float* best_s, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_quantize_pack -- quantize W*s and pack into the AutoAWQ GEMM layout.
@@ -261,7 +268,7 @@ awq_status awq_search_scales_noalloc(const awq_search_cfg* cfg /* [host] */, con
  * ------------------------------------------------------------------------- */
 awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size,
                              const float* s, const float* clip,
-                             int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
+                             int32_t* qweight, uint16_t* scales, int32_t* qzeros, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_quantize_pack_asym -- asymmetric INT4 codes in the same layout.
@@ -284,7 +291,7 @@ awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t
  * ------------------------------------------------------------------------- */
 awq_status awq_quantize_pack_asym(const void* W, int64_t d_out, int64_t d_in, int32_t group_size,
                                   const float* s, const float* clip,
-                                  int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
+                                  int32_t* qweight, uint16_t* scales, int32_t* qzeros, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_norm_group_fold -- shared scale of a norm group and the folded norm.
@@ -309,7 +316,7 @@ awq_status awq_quantize_pack_asym(const void* W, int64_t d_out, int64_t d_in, in
  * ------------------------------------------------------------------------- */
 awq_status awq_norm_group_fold(const float* const* s /* [host] */, int32_t n_members, int64_t d_in,
                                const void* norm, int32_t norm_dtype, void* norm_out, float* s_shared,
-                               void* stream);
+                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_unpack_dequant -- inverse of awq_quantize_pack, for verification.
@@ -322,7 +329,7 @@ awq_status awq_norm_group_fold(const float* const* s /* [host] */, int32_t n_mem
  * ------------------------------------------------------------------------- */
 awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                               int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
-                              void* out, int32_t out_dtype, void* stream);
+                              void* out, int32_t out_dtype, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_w4a16_matmul -- the W4A16 product on the packed layout (decode GEMV).
@@ -357,7 +364,7 @@ awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, co
 awq_status awq_w4a16_workspace(int64_t M, int64_t d_out, int64_t d_in, size_t* bytes /* [host] */);
 awq_status awq_w4a16_matmul(const void* X, int64_t M, int64_t ld_x, const int32_t* qweight, const uint16_t* scales,
                             const int32_t* qzeros, int64_t d_out, int64_t d_in, int32_t group_size, void* Y,
-                            int64_t ld_y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+                            int64_t ld_y, int32_t y_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * awq_set_timing_events -- benchmark hook.  While set, every later call on

@@ -182,7 +182,7 @@ awq_status awq_act_stats_workspace(int64_t T, int64_t d_in, size_t* bytes) {
 
 awq_status awq_act_stats(const void* X, int32_t x_dtype, int64_t T, int64_t d_in, int64_t ld_x,
                          float inv_count, int32_t accumulate, float* x_mean, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         size_t ws_bytes, hipStream_t stream) {
   if (x_dtype != AWQ_F16 && x_dtype != AWQ_BF16) return fail(AWQ_EDTYPE, "x_dtype %d: need AWQ_F16 or AWQ_BF16", x_dtype);
   if (T < 0 || d_in < 1) return fail(AWQ_EINVAL, "need T >= 0 and d_in >= 1");
   if (ld_x < d_in) return fail(AWQ_ESHAPE, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
@@ -211,7 +211,7 @@ awq_status awq_candidate_scales_workspace(int64_t d_in, int32_t n_grid, size_t* 
 }
 
 awq_status awq_candidate_scales(const float* x_mean, int64_t d_in, int32_t n_grid, double s_min,
-                                float* S, void* ws, size_t ws_bytes, void* stream) {
+                                float* S, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!x_mean || !S) return fail(AWQ_EINVAL, "x_mean / S is NULL");
   if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
   if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
@@ -257,7 +257,7 @@ awq_status awq_weight_channel_mean_workspace(int64_t d_out_total, int64_t d_in, 
 }
 
 awq_status awq_weight_channel_mean(const awq_wgroup* W, int64_t d_in, float* w_mean, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   hipStream_t stream) {
   WParts parts;
   int64_t d_out = 0;
   awq_status st = read_group(W, &parts, &d_out);
@@ -288,7 +288,7 @@ awq_status awq_candidate_scales_duo_workspace(int64_t d_in, int32_t n_grid, size
 }
 
 awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, int64_t d_in, int32_t n_grid,
-                                    double s_min, float* S, void* ws, size_t ws_bytes, void* stream) {
+                                    double s_min, float* S, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!x_mean || !w_mean || !S) return fail(AWQ_EINVAL, "x_mean / w_mean / S is NULL");
   if (d_in < 1) return fail(AWQ_EINVAL, "d_in must be >= 1");
   if (n_grid < 1 || n_grid > kMaxGrid) return fail(AWQ_EINVAL, "n_grid %d not in [1,%d]", n_grid, kMaxGrid);
@@ -319,7 +319,7 @@ awq_status awq_search_workspace(const awq_search_cfg* cfg, int64_t d_out_total, 
 awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int64_t d_in,
                              const float* x_mean, const void* X, int32_t x_dtype, int64_t T,
                              int64_t ld_x, float* err, int32_t* best_idx, float* best_s, float* clip,
-                             float* clip_err, void* ws, size_t ws_bytes, void* stream) {
+                             float* clip_err, void* ws, size_t ws_bytes, hipStream_t stream) {
   awq_status st = check_cfg(cfg);
   if (st) return st;
   if (!W || !W->w || !W->rows) return fail(AWQ_EINVAL, "weight group is NULL");
@@ -480,7 +480,7 @@ awq_status device_scratch(void** out) {
 
 extern "C" awq_status awq_search_scales_noalloc(const awq_search_cfg* cfg, const awq_wgroup* W, int64_t d_in,
                                                 const float* x_mean, float* err, int32_t* best_idx, float* best_s,
-                                                void* stream) {
+                                                hipStream_t stream) {
   awq_status st = check_cfg(cfg);
   if (st) return st;
   if (cfg->score != AWQ_SCORE_WEIGHT || cfg->n_clip != 0)
@@ -503,7 +503,7 @@ extern "C" awq_status awq_search_scales_noalloc(const awq_search_cfg* cfg, const
 // ---------------------------------------------------------------------------
 static awq_status quantize_pack_impl(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, bool asym,
                                      const float* s, const float* clip, int32_t* qweight, uint16_t* scales,
-                                     int32_t* qzeros, void* stream, const char* name) {
+                                     int32_t* qzeros, hipStream_t stream, const char* name) {
   if (!valid_group(group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", group_size);
   if (d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
   if (d_out % 8) return fail(AWQ_ESHAPE, "d_out %lld not a multiple of 8", (long long)d_out);
@@ -524,14 +524,14 @@ static awq_status quantize_pack_impl(const void* W, int64_t d_out, int64_t d_in,
 
 awq_status awq_quantize_pack(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
                              const float* clip, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
-                             void* stream) {
+                             hipStream_t stream) {
   return quantize_pack_impl(W, d_out, d_in, group_size, false, s, clip, qweight, scales, qzeros, stream,
                             "awq_quantize_pack");
 }
 
 awq_status awq_quantize_pack_asym(const void* W, int64_t d_out, int64_t d_in, int32_t group_size, const float* s,
                                   const float* clip, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
-                                  void* stream) {
+                                  hipStream_t stream) {
   return quantize_pack_impl(W, d_out, d_in, group_size, true, s, clip, qweight, scales, qzeros, stream,
                             "awq_quantize_pack_asym");
 }
@@ -550,7 +550,7 @@ awq_status awq_w4a16_workspace(int64_t M, int64_t d_out, int64_t d_in, size_t* b
 
 awq_status awq_w4a16_matmul(const void* X, int64_t M, int64_t ld_x, const int32_t* qweight, const uint16_t* scales,
                             const int32_t* qzeros, int64_t d_out, int64_t d_in, int32_t group_size, void* Y,
-                            int64_t ld_y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream) {
+                            int64_t ld_y, int32_t y_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_group(group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", group_size);
   if (M < 0 || d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");
   if (d_out % 8) return fail(AWQ_ESHAPE, "d_out %lld not a multiple of 8", (long long)d_out);
@@ -577,7 +577,7 @@ awq_status awq_w4a16_matmul(const void* X, int64_t M, int64_t ld_x, const int32_
 }
 
 awq_status awq_norm_group_fold(const float* const* s, int32_t n_members, int64_t d_in, const void* norm,
-                               int32_t norm_dtype, void* norm_out, float* s_shared, void* stream) {
+                               int32_t norm_dtype, void* norm_out, float* s_shared, hipStream_t stream) {
   if (!s) return fail(AWQ_EINVAL, "s is NULL");
   if (n_members < 1 || n_members > kMaxParts)
     return fail(AWQ_EINVAL, "n_members %d not in [1,%d]", n_members, kMaxParts);
@@ -607,7 +607,7 @@ awq_status awq_norm_group_fold(const float* const* s, int32_t n_members, int64_t
 
 awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, int64_t d_out,
                               int64_t d_in, int32_t group_size, const float* s, void* out, int32_t out_dtype,
-                              void* stream) {
+                              hipStream_t stream) {
   if (!valid_group(group_size)) return fail(AWQ_EINVAL, "group_size %d not in {32,64,128}", group_size);
   if (out_dtype != AWQ_F32 && out_dtype != AWQ_F16) return fail(AWQ_EDTYPE, "out_dtype %d: need AWQ_F32 or AWQ_F16", out_dtype);
   if (d_out < 0 || d_in < 0) return fail(AWQ_EINVAL, "negative size");

@@ -1,7 +1,9 @@
-// VALU issue-rate probe for gfx950: how many wave64 VALU instructions a SIMD
-// issues per second, by instruction class and for pairs of classes, with
-// W waves per SIMD.  This grounds the peak that the weight-score search
-// kernel is measured against (it is bound by VALU issue, not by HBM).
+// Issue-rate probes for gfx950.  VALU: how many wave64 VALU instructions a
+// SIMD issues per second, by instruction class and for pairs of classes, with
+// W waves per SIMD; this grounds the peak that the weight-score search kernel
+// is measured against (it is bound by VALU issue, not by HBM).  Matrix cores:
+// the rate of back-to-back 32x32x16 fp16 products on register operands, on
+// zero and on random data (the output-score GEMM's ceiling on this machine).
 //
 // Each lane runs 8 independent chains (no chain waits on its own previous
 // result for 8 instructions), unrolled 4 times per loop trip, so the loop's
@@ -127,9 +129,56 @@ hipError_t launch(int blocks, int iters, float* out, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Matrix-core issue probe: each wave loads 8 fragments of v_mfma_f32_32x32x16_f16
+// operands (4 of A, 2 of B, from the given buffers) once, then runs `iters`
+// rounds of the 8 independent 32x32x16 products (4 x 2 accumulator tiles, as
+// the output-score GEMM's wave tile) with no memory traffic.  The operand
+// values set the power the matrix cores draw, and with it the clock: the host
+// runs it on all-zero and on random fp16 operands.
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256, 2) void mfma_issue_kernel(const uint4* __restrict__ A, const uint4* __restrict__ B,
+                                                            float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  h8v a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(h8v, A[i * 64 + lane]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b[j] = __builtin_bit_cast(h8v, B[j * 64 + lane]);
+  f16v acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) r += acc[i][j][e];
+  if (r == 123.456f) out[blockIdx.x * blockDim.x + threadIdx.x] = r;  // keeps the products live
+}
+
 }  // namespace
 
 extern "C" {
+
+// Launches `blocks` blocks of 256 threads (4 waves) of the matrix-core probe:
+// A holds 4 x 64 and B 2 x 64 16-byte fragments (fp16), out blocks * 256 floats.
+// Flops per launch: blocks * 4 waves * iters * 8 * 2 * 32 * 32 * 16.
+int awq_probe_mfma(int blocks, int iters, const void* A, const void* B, float* out, void* stream) {
+  mfma_issue_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const uint4*)A, (const uint4*)B, out, iters);
+  return (int)hipGetLastError();
+}
 
 // Number of kinds, and VALU instructions per lane and loop trip of a kind.
 int awq_probe_valu_kinds(void) { return kSearchMix + 1; }
