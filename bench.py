@@ -1001,8 +1001,10 @@ def bench_w4a16(args):
 
     tot_b = sum(alg_bytes(d_out, d_in) for *_, d_out, d_in in layers)
     achieved = tot_b / (sum(call_ms) * 1e-3) / 1e9
-    # 9 tokens or more run the matrix-core GEMM: quoted against the fp16 MFMA peak
-    gemm = M >= 9
+    # 17 tokens or more run the matrix-core GEMM: quoted against the fp16 MFMA peak;
+    # 2..16 tokens the few-token matrix-core path, which reads every packed word
+    # once for all tokens and is quoted against HBM like the one-token GEMV
+    gemm = M >= 17
     tflops = 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (sum(call_ms) * 1e-3) / 1e12
     kinds = {}
     for (qw, sc, qz, x, y, d_out, d_in), t in zip(layers, call_ms):
@@ -1028,7 +1030,8 @@ def bench_w4a16(args):
                      if gemm else
                      {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                      "kernel": "w4a16_gemv_kernel + w4a16_reduce_kernel (per call)"}),
+                      "kernel": ("w4a16_gemv_kernel + w4a16_reduce_kernel (per call)" if M == 1 else
+                                 "w4a16_skinny_kernel (+ w4a16_reduce_kernel where the inputs are split; per call)")}),
         "step_TFLOPs": 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (ms * 1e-3) / 1e12,
         "fp16_step_TFLOPs": 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (ms16 * 1e-3) / 1e12,
     }

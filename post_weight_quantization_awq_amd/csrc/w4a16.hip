@@ -232,6 +232,222 @@ __global__ __launch_bounds__(kRdCols * kRdSplit) void w4a16_reduce_kernel(const 
 int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 
 // ---------------------------------------------------------------------------
+// Few tokens (2..16): one read of every packed word for all tokens, products on
+// the matrix cores (v_mfma_f32_16x16x32_f16).  Per wave: 16 word columns (128
+// outputs) of the packed rows; A = weights (16 outputs x 32 inputs), B = the
+// activations (32 inputs x 16 tokens, zero past the last token).  Lane l loads
+// the words of column c0 + (l & 15) in rows k + 8 (l >> 4) + 0..7 (two 64-byte
+// runs of a row per load instruction); the code of output 8c + order[j] is
+// nibble j of a word, so nibble position j of the lane's 8 words is exactly
+// lane l's part of the A fragment of the 16 outputs {8 (c0 + i) + order[j]}:
+// no data moves between lanes.  One v_perm_b32 puts byte b of two rows side by
+// side; an and-or with 0x6400 makes fp16 1024 + u (low nibble, j = 2b) or
+// 1024 + 16 u (high nibble, j = 2b + 1), and a packed fp16 subtract of
+// 1024 + z (or 1024 + 16 z) leaves the exact (u - z) or 16 (u - z): 1.25 VALU
+// operations per weight, so the kernel stays bound by reading the codes.  The
+// products of a group accumulate alone in fp32 and are added to the result
+// times the group's fp32 scale (over 16 for the odd nibbles), so no rounding
+// touches a dequantized weight.  Each of the 4 waves of a block takes one
+// 128-row chunk of the block's 512-row input range, all its loads in flight at
+// once; the waves are added in LDS in a fixed order, and the reduction kernel
+// adds the ranges' fp32 results in order (a single range writes Y directly).
+// ---------------------------------------------------------------------------
+constexpr int kSkTokens = 16;
+constexpr int kSkWords = 16;                   // word columns per wave (and per block)
+constexpr int kSkCols = kSkWords * 8;          // outputs per block
+constexpr int kSkWaves = 4;
+
+typedef _Float16 h8s __attribute__((ext_vector_type(8)));
+typedef float f4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_sub_f16(uint32_t a, uint32_t b) {
+  const h2 r = __builtin_bit_cast(h2, a) - __builtin_bit_cast(h2, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Work unit: a chunk of 128 input rows (4 steps of 32; the last chunk may be
+// shorter), every word and activation load of it issued at once.
+constexpr int kSkChunk = 128;
+constexpr int kSkSteps = kSkChunk / 32;
+
+template <bool Y_F16>
+__global__ __launch_bounds__(kSkWaves * kWave) void w4a16_skinny_kernel(
+    const uint16_t* __restrict__ X, int64_t ld_x, int m_valid, int64_t d_in, const uint32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros, int64_t d_out, int group_size,
+    int chunks_per_block, int n_strips, void* __restrict__ Y, int64_t ld_y, float* __restrict__ part) {
+  __shared__ __align__(16) float red[kSkWaves][kSkTokens][kSkCols];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n_words = d_out / 8;
+  // blocks go round-robin to the 8 XCDs: tile t of XCD x takes the x-th eighth of
+  // the (strip, range) tiles, strips fastest, so the two strips sharing each
+  // 128-byte line of a packed row are read through the same L2
+  const uint32_t nblk = gridDim.x, bid = blockIdx.x;
+  const uint32_t xcd = bid % 8, q = nblk / 8, rmd = nblk % 8;
+  const uint32_t tile = xcd * q + (xcd < rmd ? xcd : rmd) + bid / 8;
+  const uint32_t strip = tile % (uint32_t)n_strips, range = tile / (uint32_t)n_strips;
+  const int64_t c0 = (int64_t)strip * kSkWords;
+  const int li = lane & 15, lh = lane >> 4;               // row of the A / B fragment, 8-input run
+  const int64_t col = c0 + li < n_words ? c0 + li : n_words - 1;
+  const int64_t n_chunks = (d_in + kSkChunk - 1) / kSkChunk;
+  const int64_t ch_begin = (int64_t)range * chunks_per_block;
+  const int64_t ch_end = ch_begin + chunks_per_block < n_chunks ? ch_begin + chunks_per_block : n_chunks;
+  const int steps_per_group = group_size / 32;
+  const bool tok = li < m_valid;
+  const uint16_t* xrow = X + (int64_t)(tok ? li : m_valid - 1) * ld_x + 8 * lh;
+
+  f4s tot[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tot[j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
+  // this wave's chunks: ch_begin + wv, ch_begin + wv + 4, ...
+  for (int64_t ch = ch_begin + wv; ch < ch_end; ch += kSkWaves) {
+    const int64_t r0 = ch * kSkChunk;
+    const int n_steps = (int)((d_in - r0) / 32 < kSkSteps ? (d_in - r0) / 32 : kSkSteps);  // wave-uniform
+    // the first group's zero points and scales, then every code word and
+    // activation of the chunk, all in flight at once (a step past d_in repeats
+    // the chunk's first rows and is never used; a lane past the last token
+    // reads that token and zeroes it)
+    uint32_t zw = qzeros != nullptr ? qzeros[(r0 / group_size) * n_words + col] : 0x77777777u;
+    uint4 sr[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t ci = c0 + 4 * lh + v < n_words ? c0 + 4 * lh + v : n_words - 1;
+      sr[v] = *(const uint4*)(scales + (r0 / group_size) * d_out + 8 * ci);
+    }
+    uint32_t w[kSkSteps][8];
+    uint4 xv[kSkSteps];
+#pragma unroll
+    for (int st = 0; st < kSkSteps; ++st) {
+      const int64_t k = r0 + 32 * (st < n_steps ? st : 0);
+      const uint32_t* wp = qweight + (k + 8 * lh) * n_words + col;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) w[st][r] = __builtin_nontemporal_load(wp + r * n_words);
+      xv[st] = *(const uint4*)(xrow + k);
+    }
+#pragma unroll
+    for (int st = 0; st < kSkSteps; ++st) {
+      if (!tok) xv[st] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    f4s acc[8];
+    uint32_t zc[8];
+#pragma unroll
+    for (int st = 0; st < kSkSteps; ++st) {
+      if (st < n_steps) {
+        const int64_t k = r0 + 32 * st;
+        const int64_t g = k / group_size;
+        if (st % steps_per_group == 0) {   // a group starts: its zero points and scales, fresh sums
+          if (st > 0) {
+            zw = qzeros != nullptr ? qzeros[g * n_words + col] : 0x77777777u;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int64_t ci = c0 + 4 * lh + v < n_words ? c0 + 4 * lh + v : n_words - 1;
+              sr[v] = *(const uint4*)(scales + g * d_out + 8 * ci);
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t zl = (zw >> (8 * b)) & 0xFu, zh = (zw >> (8 * b + 4)) & 0xFu;
+            zc[2 * b] = (0x6400u | zl) * 0x10001u;                 // 1024 + z in both halves
+            zc[2 * b + 1] = (0x6400u | (zh << 4)) * 0x10001u;      // 1024 + 16 z
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        const h8s bx = __builtin_bit_cast(h8s, xv[st]);
+        uint32_t a[8][4];   // a[j][p]: fp16 pair (rows 2p, 2p + 1) of nibble j
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t sel = (uint32_t)b | (12u << 8) | ((uint32_t)(4 + b) << 16) | (12u << 24);
+            const uint32_t x2 = __builtin_amdgcn_perm(w[st][2 * p + 1], w[st][2 * p], sel);
+            a[2 * b][p] = pk_sub_f16(and_or(x2, 0x000F000Fu, 0x64006400u), zc[2 * b]);
+            a[2 * b + 1][p] = pk_sub_f16(and_or(x2, 0x00F000F0u, 0x64006400u), zc[2 * b + 1]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint4 av = make_uint4(a[j][0], a[j][1], a[j][2], a[j][3]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8s, av), bx, acc[j], 0, 0, 0);
+        }
+        if ((st + 1) % steps_per_group == 0) {   // the group ends: fold its sums with its scales
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t sw[4] = {sr[v].x, sr[v].y, sr[v].z, sr[v].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              constexpr int kOrd[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+              const int o = kOrd[j];
+              float sc = h2f((uint16_t)((sw[o >> 1] >> (16 * (o & 1))) & 0xFFFFu));
+              if (j & 1) sc *= 0.0625f;   // the odd nibbles carry 16 (u - z)
+              tot[j][v] = __builtin_fmaf(acc[j][v], sc, tot[j][v]);
+            }
+          }
+        }
+      }
+    }
+  }
+  // the waves' results into LDS: token li, outputs 8 (4 lh + v) + order[j]
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      constexpr int kOrd[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+      red[wv][li][8 * (4 * lh + v) + kOrd[j]] = tot[j][v];
+    }
+  }
+  __syncthreads();
+  // 8 consecutive outputs of one token per thread, waves added in order 0..3
+  const int t = tid / (kSkCols / 8), oc = (tid % (kSkCols / 8)) * 8;
+  const int64_t o = c0 * 8 + oc;
+  if (t >= m_valid || o >= d_out) return;
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float acc_w = red[0][t][oc + e];
+#pragma unroll
+    for (int q = 1; q < kSkWaves; ++q) acc_w += red[q][t][oc + e];
+    r[e] = acc_w;
+  }
+  if (part != nullptr) {
+    float* dst = part + ((int64_t)range * m_valid + t) * d_out + o;
+    *(float4*)dst = make_float4(r[0], r[1], r[2], r[3]);
+    *(float4*)(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
+  } else if (Y_F16) {
+    uint16_t* dst = (uint16_t*)Y + t * ld_y + o;
+    *(uint2*)dst = make_uint2((uint32_t)f2h_bits(r[0]) | ((uint32_t)f2h_bits(r[1]) << 16),
+                              (uint32_t)f2h_bits(r[2]) | ((uint32_t)f2h_bits(r[3]) << 16));
+    *(uint2*)(dst + 4) = make_uint2((uint32_t)f2h_bits(r[4]) | ((uint32_t)f2h_bits(r[5]) << 16),
+                                    (uint32_t)f2h_bits(r[6]) | ((uint32_t)f2h_bits(r[7]) << 16));
+  } else {
+    float* dst = (float*)Y + t * ld_y + o;
+    *(float4*)dst = make_float4(r[0], r[1], r[2], r[3]);
+    *(float4*)(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
+  }
+}
+
+// Input ranges of the few-token kernel: one 128-row chunk per wave (4 per
+// block), so that every wave's loads go out at once and the grid holds many
+// waves; the ranges' fp32 results (M x d_out each) cost 2 M / 128 bytes per
+// weight against its 0.5 + 2.5 / G bytes of codes, scales and zero points.
+static int64_t skinny_chunks_per_block(int64_t d_out, int64_t d_in) {
+  (void)d_out;
+  (void)d_in;
+  return kSkWaves;
+}
+static int64_t skinny_splits(int64_t d_out, int64_t d_in) {
+  const int64_t cpb = skinny_chunks_per_block(d_out, d_in);
+  return ((d_in + kSkChunk - 1) / kSkChunk + cpb - 1) / cpb;
+}
+int64_t w4a16_skinny_part_floats(int64_t M, int64_t d_out, int64_t d_in) {
+  const int64_t s = skinny_splits(d_out, d_in);
+  return s > 1 ? s * M * d_out : 0;
+}
+bool w4a16_uses_skinny(const void* X, int64_t M, int64_t ld_x) {
+  return M >= 2 && M <= kSkTokens && ((uintptr_t)X & 15u) == 0 && ld_x % 8 == 0;
+}
+
+// ---------------------------------------------------------------------------
 // Prefill: the W4A16 GEMM on the matrix cores ("AWQ architecture, in depth",
 // "Kernels: why W4A16 is fast at decode": at prefill sizes the product is
 // compute-bound and dequantization is extra work).  Block tile 256 tokens x
@@ -257,7 +473,7 @@ constexpr int kQThreads = 512;
 constexpr int kQBufs = 4;            // LDS stage buffers: stores run two stages ahead of the MFMAs
 // from 9 tokens on, one 128-token tile (split over K when the tile grid is small)
 // costs less than the three or more passes of the 4-token GEMV
-constexpr int kGemmMinTokens = 9;
+constexpr int kGemmMinTokens = 17;
 
 // 16-byte K-chunk kc (0..3) of an LDS tile row.  X rows are swizzled by bits
 // 2-3 of the row, code rows by bits 3-4: the codes are written as 4-byte
@@ -477,6 +693,26 @@ bool w4a16_uses_gemm(const void* X, int64_t M, int64_t ld_x, int64_t d_in) {
 hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* qzeros, int64_t d_out, int64_t d_in, int group_size, void* Y, int64_t ld_y,
                         bool y_f16, float* part, hipStream_t stream) {
+  if (w4a16_uses_skinny(X, M, ld_x)) {
+    const int64_t cpb = skinny_chunks_per_block(d_out, d_in);
+    const int64_t n_split = skinny_splits(d_out, d_in);
+    const int n_strips = (int)((d_out / 8 + kSkWords - 1) / kSkWords);
+    const unsigned g = (unsigned)(n_strips * n_split);
+    float* sp = n_split > 1 ? part : nullptr;
+    if (y_f16)
+      w4a16_skinny_kernel<true><<<g, kSkWaves * kWave, 0, stream>>>(X, ld_x, (int)M, d_in, qweight, scales, qzeros,
+                                                                   d_out, group_size, (int)cpb, n_strips, Y, ld_y, sp);
+    else
+      w4a16_skinny_kernel<false><<<g, kSkWaves * kWave, 0, stream>>>(X, ld_x, (int)M, d_in, qweight, scales, qzeros,
+                                                                    d_out, group_size, (int)cpb, n_strips, Y, ld_y,
+                                                                    sp);
+    if (n_split > 1) {
+      const dim3 rgrid((unsigned)((d_out / 4 + kRdCols - 1) / kRdCols), (unsigned)M);
+      w4a16_reduce_kernel<<<rgrid, kRdCols * kRdSplit, 0, stream>>>(part, n_split, (int)M, d_out, Y, ld_y,
+                                                                    y_f16 ? 1 : 0);
+    }
+    return hipGetLastError();
+  }
   if (w4a16_uses_gemm(X, M, ld_x, d_in)) {
     const int nk = (int)(d_in / kQBK), ss = gemm_split_stages(M, d_out, d_in);
     const int n_split = (nk + ss - 1) / ss;

@@ -7,7 +7,12 @@ HIP path).  Tolerance, from the arithmetic, with B = sum_i |x_i| (u_i + z) scale
   are exact in fp32; a wave adds 32 of them and the 32 activations in fp32,
   folds the zero point and the scale (3 roundings), then 8 waves and n_slices
   row slices are added in fp32: within 2^-24 (32 + 8 + 8 + n_slices) B;
-* prefill GEMM (9 tokens or more): the matrix cores add G exact products
+* few tokens (2 to 16, X 16-byte aligned rows): the matrix cores add the G
+  exact products (u - z) x (or 16 (u - z) x) of a group in fp32, one fma
+  applies the scale per group, a wave adds its groups, the block adds its 4
+  waves in LDS (3 roundings), and at most d_in / (4 G) input ranges are added
+  by the reduction: within 2^-24 (G + 5 + d_in / G + d_in / (4 G)) B;
+* prefill GEMM (17 tokens or more): the matrix cores add G exact products
   (u - z) x of a group in fp32, one fma applies the scale, d_in / G groups are
   added: within 2^-24 (G + 2 + d_in / G) B.  Split over K into S ranges of
   at least two 128-input units, a range adds at most d_in / G / S + 1 groups
@@ -48,7 +53,7 @@ def _dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
 
 
-def _bound(X, qw, sc, qz, d_out, G, n_slices, gemm=False):
+def _bound(X, qw, sc, qz, d_out, G, n_slices, kind="gemv"):
     u = O.unpack_codes(qw, d_out).astype(F64)                         # [d_out, d_in]
     z = (O.unpack_codes(qz, d_out).astype(F64) if qz is not None
          else np.full((d_out, qw.shape[0] // G), 7.0))
@@ -56,11 +61,14 @@ def _bound(X, qw, sc, qz, d_out, G, n_slices, gemm=False):
     ss = np.repeat(sc.astype(F64).T, G, axis=1)
     B = np.abs(O.decode_activations(X)) @ ((u + zz) * ss).T
     d_in = qw.shape[0]
-    return 2.0 ** -24 * ((G + 2 + d_in // G) if gemm else (32 + 8 + 8 + n_slices)) * B
+    count = {"gemv": 32 + 8 + 8 + n_slices, "gemm": G + 2 + d_in // G,
+             "few": G + 5 + d_in // G + d_in // (4 * G)}[kind]
+    return 2.0 ** -24 * count * B
 
 
 def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
-    """The kernel is the GEMM at 9 tokens or more when X rows are 16-byte aligned, else the GEMV."""
+    """With X rows 16-byte aligned the kernel is the few-token matrix-core path at
+    2 to 16 tokens and the GEMM from 17; else (and at one token) the GEMV."""
     import torch
     M, d_in = X.shape
     Xp = X if ld_x is None else np.pad(X, ((0, 0), (0, ld_x - d_in)))
@@ -73,8 +81,8 @@ def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
     Y = host(plan.run()).astype(F64)
     ref = O.w4a16_matmul(X, qw, sc, qz, d_out, G)
     ldx = d_in if ld_x is None else ld_x
-    gemm = M >= 9 and ldx % 8 == 0
-    tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 255) // 256, gemm)
+    kind = "gemv" if (ldx % 8 or M == 1) else ("few" if M <= 16 else "gemm")
+    tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 255) // 256, kind)
     if out_dtype == "f16":
         tol = tol + np.spacing(np.abs(ref).astype(np.float16) * np.float16(1.002)).astype(F64)
     err = np.abs(Y - ref)
@@ -97,7 +105,7 @@ def test_w4a16_decode_full_size(A, name, d_out, d_in, G, zeros):
     _check(A, X, qw, sc, qz, d_out, G)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 16])
 @pytest.mark.parametrize("d_out,d_in,G,out_dtype", [(1032, 384, 64, "f16"), (520, 96, 32, "f32"),
                                                     (16, 256, 128, "f32")])
 def test_w4a16_tokens_and_ragged_shapes(A, M, d_out, d_in, G, out_dtype):
@@ -107,12 +115,27 @@ def test_w4a16_tokens_and_ragged_shapes(A, M, d_out, d_in, G, out_dtype):
     _check(A, X, qw, sc, qz, d_out, G, out_dtype)
 
 
+@pytest.mark.parametrize("M", [2, 8, 16])
+@pytest.mark.parametrize("name,d_out,d_in,G,zeros,out_dtype", [
+    ("qkv_6144x4096", 6144, 4096, 128, True, "f16"),
+    ("gate_up_24576x4096", 24576, 4096, 128, False, "f32"),
+    ("down_4096x12288_g64", 4096, 12288, 64, True, "f16"),
+])
+def test_w4a16_few_tokens_full_size(A, M, name, d_out, d_in, G, zeros, out_dtype):
+    """2 to 16 tokens at Qwen3-8B linear sizes: the few-token matrix-core path,
+    its inputs split into ranges whose results the reduction adds."""
+    say(f"w4a16 few tokens {name} M={M}")
+    qw, sc, qz = _random_packed(3 * M + d_out + d_in, d_out, d_in, G, zeros)
+    X = (np.random.default_rng(5 * M + d_in).standard_normal((M, d_in))).astype(np.float16)
+    _check(A, X, qw, sc, qz, d_out, G, out_dtype)
+
+
 def test_w4a16_strides(A):
     say("w4a16 strided X and Y")
     qw, sc, qz = _random_packed(11, 264, 256, 64, True)
     X = (np.random.default_rng(12).standard_normal((3, 256))).astype(np.float16)
-    _check(A, X, qw, sc, qz, 264, 64, "f16", ld_x=264, ld_y=272)
-    _check(A, X, qw, sc, qz, 264, 64, "f32", ld_x=300, ld_y=268)
+    _check(A, X, qw, sc, qz, 264, 64, "f16", ld_x=264, ld_y=272)   # few-token path, padded rows
+    _check(A, X, qw, sc, qz, 264, 64, "f32", ld_x=300, ld_y=268)   # rows not 16-byte aligned: GEMV
 
 
 @pytest.mark.parametrize("asym", [False, True])
