@@ -91,7 +91,7 @@ int64_t w4a16_slices(int64_t d_in);
 int64_t w4a16_gemm_part_floats(int64_t M, int64_t d_out, int64_t d_in);
 // the few-token (2..16) matrix-core path: fp32 partials of its input ranges, and whether it runs
 int64_t w4a16_skinny_part_floats(int64_t M, int64_t d_out, int64_t d_in);
-bool w4a16_uses_skinny(const void* X, int64_t M, int64_t ld_x);
+bool w4a16_uses_skinny(const void* X, int64_t M, int64_t ld_x, const void* qweight, int64_t d_out);
 int64_t w4a16_cols(int64_t d_out);
 hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* qzeros, int64_t d_out, int64_t d_in, int group_size, void* Y, int64_t ld_y,

@@ -233,218 +233,237 @@ int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 
 // ---------------------------------------------------------------------------
 // Few tokens (2..16): one read of every packed word for all tokens, products on
-// the matrix cores (v_mfma_f32_16x16x32_f16).  Per wave: 16 word columns (128
-// outputs) of the packed rows; A = weights (16 outputs x 32 inputs), B = the
-// activations (32 inputs x 16 tokens, zero past the last token).  Lane l loads
-// the words of column c0 + (l & 15) in rows k + 8 (l >> 4) + 0..7 (two 64-byte
-// runs of a row per load instruction); the code of output 8c + order[j] is
-// nibble j of a word, so nibble position j of the lane's 8 words is exactly
-// lane l's part of the A fragment of the 16 outputs {8 (c0 + i) + order[j]}:
-// no data moves between lanes.  One v_perm_b32 puts byte b of two rows side by
-// side; an and-or with 0x6400 makes fp16 1024 + u (low nibble, j = 2b) or
-// 1024 + 16 u (high nibble, j = 2b + 1), and a packed fp16 subtract of
-// 1024 + z (or 1024 + 16 z) leaves the exact (u - z) or 16 (u - z): 1.25 VALU
-// operations per weight, so the kernel stays bound by reading the codes.  The
-// products of a group accumulate alone in fp32 and are added to the result
-// times the group's fp32 scale (over 16 for the odd nibbles), so no rounding
-// touches a dequantized weight.  Each of the 4 waves of a block takes one
-// 128-row chunk of the block's 512-row input range, all its loads in flight at
-// once; the waves are added in LDS in a fixed order, and the reduction kernel
-// adds the ranges' fp32 results in order (a single range writes Y directly).
+// the matrix cores (v_mfma_f32_16x16x32_f16).  A = weights (16 outputs x 32
+// inputs), B = the activations (32 inputs x 16 tokens, zero past the last
+// token).  A wave owns 32 word columns (256 outputs) of a 128-row chunk; lane
+// l loads the word pair of columns c0 + 2 (l & 15) + {0, 1} in rows
+// k + 8 (l >> 4) + 0..7 of each 32-row step with one 8-byte load per row, so a
+// load instruction reads four whole 128-byte runs of packed rows (a strip of
+// 16 columns, 64-byte runs, measured 35% slower on the same bytes).  The code
+// of output 8c + order[j] is nibble j of a word, so nibble position j of the
+// lane's 8 words of one column is exactly lane l's part of the A fragment of
+// the 16 outputs {8 (c0 + 2i + h) + order[j]}: no data moves between lanes.
+// One v_perm_b32 puts byte b of two rows side by side; an and-or with 0x6400
+// makes fp16 1024 + u (low nibble, j = 2b) or 1024 + 16 u (high nibble,
+// j = 2b + 1), and a packed fp16 subtract of 1024 + z (or 1024 + 16 z) leaves
+// the exact (u - z) or 16 (u - z): 1.25 VALU operations per weight.  The
+// products of a group accumulate alone in fp32; at the group's end they are
+// multiplied by the group's fp32 scale (over 16 for the odd nibbles) and added
+// into the wave's slot in LDS, so no rounding touches a dequantized weight and
+// no second set of accumulators is held in registers.  The 4 waves of a block
+// take the 4 chunks of the block's 512-row input range, all loads of a chunk
+// in flight at once (two waves per SIMD); their slots are added in a fixed
+// order, and the reduction kernel adds the ranges' fp32 results in order (a
+// single range writes Y directly).
 // ---------------------------------------------------------------------------
 constexpr int kSkTokens = 16;
-constexpr int kSkWords = 16;                   // word columns per wave (and per block)
-constexpr int kSkCols = kSkWords * 8;          // outputs per block
+constexpr int kSkWords = 32;                   // word columns per block (and per wave)
 constexpr int kSkWaves = 4;
+constexpr int kSkChunk = 128;                  // input rows per wave
+constexpr int kSkSteps = kSkChunk / 32;
+constexpr int kSkSlot = 68;                    // floats per lane in LDS (64 results, padded)
 
 typedef _Float16 h8s __attribute__((ext_vector_type(8)));
 typedef float f4s __attribute__((ext_vector_type(4)));
+typedef uint32_t u2s __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pk_sub_f16(uint32_t a, uint32_t b) {
   const h2 r = __builtin_bit_cast(h2, a) - __builtin_bit_cast(h2, b);
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Work unit: a chunk of 128 input rows (4 steps of 32; the last chunk may be
-// shorter), every word and activation load of it issued at once.
-constexpr int kSkChunk = 128;
-constexpr int kSkSteps = kSkChunk / 32;
+// fp16 1024 + z (low nibbles) and 1024 + 16 z (high nibbles) in both halves,
+// for the 8 nibbles of a packed zero-point word
+__device__ __forceinline__ void zero_consts(uint32_t zw, uint32_t* zc) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t zl = (zw >> (8 * b)) & 0xFu, zh = (zw >> (8 * b + 4)) & 0xFu;
+    zc[2 * b] = (0x6400u | zl) * 0x10001u;
+    zc[2 * b + 1] = (0x6400u | (zh << 4)) * 0x10001u;
+  }
+}
 
-template <bool Y_F16>
-__global__ __launch_bounds__(kSkWaves * kWave) void w4a16_skinny_kernel(
+template <int G, bool Y_F16>
+__global__ __launch_bounds__(kSkWaves * kWave, 2) void w4a16_skinny_kernel(
     const uint16_t* __restrict__ X, int64_t ld_x, int m_valid, int64_t d_in, const uint32_t* __restrict__ qweight,
-    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros, int64_t d_out, int group_size,
-    int chunks_per_block, int n_strips, void* __restrict__ Y, int64_t ld_y, float* __restrict__ part) {
-  __shared__ __align__(16) float red[kSkWaves][kSkTokens][kSkCols];
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros, int64_t d_out, int n_strips,
+    void* __restrict__ Y, int64_t ld_y, float* __restrict__ part) {
+  constexpr int kSpg = G / 32;   // steps per quantization group
+  // slot[w][lane][(h * 4 + v) * 8 + e]: wave w's sum for the lane's token and
+  // output 8 (c0 + 8 (lane >> 4) + 2 v + h) + e
+  __shared__ __align__(16) float slot[kSkWaves][kWave][kSkSlot];
+  __shared__ __align__(16) uint16_t scl[kSkWaves][kSkSteps][kSkWords * 8];   // each wave's group scales
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t n_words = d_out / 8;
+  const int64_t n_words = d_out / 8;   // even
   // blocks go round-robin to the 8 XCDs: tile t of XCD x takes the x-th eighth of
-  // the (strip, range) tiles, strips fastest, so the two strips sharing each
-  // 128-byte line of a packed row are read through the same L2
+  // the (strip, range) tiles, strips fastest, so neighbouring strips of a packed
+  // row are read through the same L2
   const uint32_t nblk = gridDim.x, bid = blockIdx.x;
   const uint32_t xcd = bid % 8, q = nblk / 8, rmd = nblk % 8;
   const uint32_t tile = xcd * q + (xcd < rmd ? xcd : rmd) + bid / 8;
   const uint32_t strip = tile % (uint32_t)n_strips, range = tile / (uint32_t)n_strips;
   const int64_t c0 = (int64_t)strip * kSkWords;
   const int li = lane & 15, lh = lane >> 4;               // row of the A / B fragment, 8-input run
-  const int64_t col = c0 + li < n_words ? c0 + li : n_words - 1;
-  const int64_t n_chunks = (d_in + kSkChunk - 1) / kSkChunk;
-  const int64_t ch_begin = (int64_t)range * chunks_per_block;
-  const int64_t ch_end = ch_begin + chunks_per_block < n_chunks ? ch_begin + chunks_per_block : n_chunks;
-  const int steps_per_group = group_size / 32;
+  // this lane's word pair (a pair past the last column re-reads the last pair;
+  // its outputs are never stored)
+  const int64_t cp = c0 + 2 * li + 2 <= n_words ? c0 + 2 * li : n_words - 2;
+  const int64_t r0 = ((int64_t)range * kSkWaves + wv) * kSkChunk;
   const bool tok = li < m_valid;
   const uint16_t* xrow = X + (int64_t)(tok ? li : m_valid - 1) * ld_x + 8 * lh;
+  float* my = &slot[wv][lane][0];
 
-  f4s tot[8];
+  // Every step of the chunk runs, with no branch, so that all loads go out at
+  // once in step order and each step waits only for its own: a step past d_in
+  // (the last range only) reads the last 32 rows again and multiplies them by
+  // zero activations, which adds exact zeros.
+  int64_t ks[kSkSteps];
+  bool live[kSkSteps];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) tot[j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
-  // this wave's chunks: ch_begin + wv, ch_begin + wv + 4, ...
-  for (int64_t ch = ch_begin + wv; ch < ch_end; ch += kSkWaves) {
-    const int64_t r0 = ch * kSkChunk;
-    const int n_steps = (int)((d_in - r0) / 32 < kSkSteps ? (d_in - r0) / 32 : kSkSteps);  // wave-uniform
-    // the first group's zero points and scales, then every code word and
-    // activation of the chunk, all in flight at once (a step past d_in repeats
-    // the chunk's first rows and is never used; a lane past the last token
-    // reads that token and zeroes it)
-    uint32_t zw = qzeros != nullptr ? qzeros[(r0 / group_size) * n_words + col] : 0x77777777u;
-    uint4 sr[4];
+  for (int st = 0; st < kSkSteps; ++st) {
+    live[st] = r0 + 32 * st < d_in;
+    ks[st] = live[st] ? r0 + 32 * st : d_in - 32;
+  }
+  // The zero points and scales of every group of the chunk first (the scales
+  // of the strip's 256 outputs, 8 bytes a lane, staged through LDS; a lane past
+  // d_out re-reads the last 4), then the code words and activations of every
+  // step, so that no wait for a later group's constants drains the loads.
+  constexpr int kGroups = kSkSteps / kSpg;
+  uint32_t zw[kGroups][2];
+  u2s sg[kGroups];
+  const int64_t so = 8 * c0 + 4 * lane + 4 <= d_out ? 8 * c0 + 4 * lane : d_out - 4;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t ci = c0 + 4 * lh + v < n_words ? c0 + 4 * lh + v : n_words - 1;
-      sr[v] = *(const uint4*)(scales + (r0 / group_size) * d_out + 8 * ci);
-    }
-    uint32_t w[kSkSteps][8];
-    uint4 xv[kSkSteps];
+  for (int gi = 0; gi < kGroups; ++gi) {
+    const int64_t g = ks[gi * kSpg] / G;
+    zw[gi][0] = qzeros != nullptr ? qzeros[g * n_words + cp] : 0x77777777u;
+    zw[gi][1] = qzeros != nullptr ? qzeros[g * n_words + cp + 1] : 0x77777777u;
+    sg[gi] = *(const u2s*)(scales + g * d_out + so);
+  }
+  u2s w[kSkSteps][8];
+  uint4 xv[kSkSteps];
 #pragma unroll
-    for (int st = 0; st < kSkSteps; ++st) {
-      const int64_t k = r0 + 32 * (st < n_steps ? st : 0);
-      const uint32_t* wp = qweight + (k + 8 * lh) * n_words + col;
+  for (int st = 0; st < kSkSteps; ++st) {
+    const uint32_t* wp = qweight + (ks[st] + 8 * lh) * n_words + cp;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) w[st][r] = __builtin_nontemporal_load(wp + r * n_words);
-      xv[st] = *(const uint4*)(xrow + k);
-    }
+    for (int r = 0; r < 8; ++r) w[st][r] = __builtin_nontemporal_load((const u2s*)(wp + r * n_words));
+    xv[st] = *(const uint4*)(xrow + ks[st]);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any arithmetic below
+  uint16_t* ssc = &scl[wv][0][0];
 #pragma unroll
-    for (int st = 0; st < kSkSteps; ++st) {
-      if (!tok) xv[st] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    f4s acc[8];
-    uint32_t zc[8];
+  for (int gi = 0; gi < kGroups; ++gi) *(u2s*)(ssc + gi * kSkWords * 8 + 4 * lane) = sg[gi];
+  f4s acc[2][8];
+  uint32_t zc[2][8];
 #pragma unroll
-    for (int st = 0; st < kSkSteps; ++st) {
-      if (st < n_steps) {
-        const int64_t k = r0 + 32 * st;
-        const int64_t g = k / group_size;
-        if (st % steps_per_group == 0) {   // a group starts: its zero points and scales, fresh sums
-          if (st > 0) {
-            zw = qzeros != nullptr ? qzeros[g * n_words + col] : 0x77777777u;
+  for (int st = 0; st < kSkSteps; ++st) {
+    {
+      if (st % kSpg == 0) {   // a group starts: its zero points, fresh sums
+        zero_consts(zw[st / kSpg][0], zc[0]);
+        zero_consts(zw[st / kSpg][1], zc[1]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int64_t ci = c0 + 4 * lh + v < n_words ? c0 + 4 * lh + v : n_words - 1;
-              sr[v] = *(const uint4*)(scales + g * d_out + 8 * ci);
-            }
-          }
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t zl = (zw >> (8 * b)) & 0xFu, zh = (zw >> (8 * b + 4)) & 0xFu;
-            zc[2 * b] = (0x6400u | zl) * 0x10001u;                 // 1024 + z in both halves
-            zc[2 * b + 1] = (0x6400u | (zh << 4)) * 0x10001u;      // 1024 + 16 z
-          }
+          for (int j = 0; j < 8; ++j) acc[h][j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      // masked where used, so that a step waits only for its own loads
+      const h8s bx = __builtin_bit_cast(h8s, (tok && live[st]) ? xv[st] : make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        const h8s bx = __builtin_bit_cast(h8s, xv[st]);
+      for (int h = 0; h < 2; ++h) {
         uint32_t a[8][4];   // a[j][p]: fp16 pair (rows 2p, 2p + 1) of nibble j
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const uint32_t sel = (uint32_t)b | (12u << 8) | ((uint32_t)(4 + b) << 16) | (12u << 24);
-            const uint32_t x2 = __builtin_amdgcn_perm(w[st][2 * p + 1], w[st][2 * p], sel);
-            a[2 * b][p] = pk_sub_f16(and_or(x2, 0x000F000Fu, 0x64006400u), zc[2 * b]);
-            a[2 * b + 1][p] = pk_sub_f16(and_or(x2, 0x00F000F0u, 0x64006400u), zc[2 * b + 1]);
+            const uint32_t x2 = __builtin_amdgcn_perm(w[st][2 * p + 1][h], w[st][2 * p][h], sel);
+            a[2 * b][p] = pk_sub_f16(and_or(x2, 0x000F000Fu, 0x64006400u), zc[h][2 * b]);
+            a[2 * b + 1][p] = pk_sub_f16(and_or(x2, 0x00F000F0u, 0x64006400u), zc[h][2 * b + 1]);
           }
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint4 av = make_uint4(a[j][0], a[j][1], a[j][2], a[j][3]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8s, av), bx, acc[j], 0, 0, 0);
+          acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8s, av), bx, acc[h][j], 0, 0, 0);
         }
-        if ((st + 1) % steps_per_group == 0) {   // the group ends: fold its sums with its scales
+      }
+      if ((st + 1) % kSpg == 0) {   // the group ends: its sums times its scales into the slot
+        const bool first = st + 1 == kSpg;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const uint32_t sw[4] = {sr[v].x, sr[v].y, sr[v].z, sr[v].w};
+            // scales of word column c0 + 8 lh + 2 v + h of this group
+            const uint4 sv = *(const uint4*)(ssc + (st / kSpg) * kSkWords * 8 + 8 * (8 * lh + 2 * v + h));
+            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+            float val[8];   // the 8 outputs of word column c0 + 8 lh + 2 v + h, in output order
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               constexpr int kOrd[8] = {0, 2, 4, 6, 1, 3, 5, 7};
               const int o = kOrd[j];
               float sc = h2f((uint16_t)((sw[o >> 1] >> (16 * (o & 1))) & 0xFFFFu));
               if (j & 1) sc *= 0.0625f;   // the odd nibbles carry 16 (u - z)
-              tot[j][v] = __builtin_fmaf(acc[j][v], sc, tot[j][v]);
+              val[o] = acc[h][j][v] * sc;
+            }
+            f4s* dst = (f4s*)(my + (h * 4 + v) * 8);
+            const f4s lo = {val[0], val[1], val[2], val[3]}, hi = {val[4], val[5], val[6], val[7]};
+            if (first) {
+              dst[0] = lo;
+              dst[1] = hi;
+            } else {
+              dst[0] = dst[0] + lo;
+              dst[1] = dst[1] + hi;
             }
           }
         }
       }
     }
   }
-  // the waves' results into LDS: token li, outputs 8 (4 lh + v) + order[j]
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      constexpr int kOrd[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-      red[wv][li][8 * (4 * lh + v) + kOrd[j]] = tot[j][v];
-    }
-  }
   __syncthreads();
-  // 8 consecutive outputs of one token per thread, waves added in order 0..3
-  const int t = tid / (kSkCols / 8), oc = (tid % (kSkCols / 8)) * 8;
-  const int64_t o = c0 * 8 + oc;
-  if (t >= m_valid || o >= d_out) return;
-  float r[8];
+  // 8 consecutive outputs (one word column) of one token per work item, the
+  // waves added in order 0..3
+  for (int idx = tid; idx < kSkTokens * kSkWords; idx += kSkWaves * kWave) {
+    const int t = idx / kSkWords, q8 = idx % kSkWords;   // token, word column in the strip
+    const int64_t o = (c0 + q8) * 8;
+    if (t >= m_valid || o >= d_out) continue;
+    const int ln = t + 16 * (q8 >> 3), off = ((q8 & 1) * 4 + ((q8 >> 1) & 3)) * 8;
+    f4s lo = *(const f4s*)&slot[0][ln][off], hi = *(const f4s*)&slot[0][ln][off + 4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float acc_w = red[0][t][oc + e];
-#pragma unroll
-    for (int q = 1; q < kSkWaves; ++q) acc_w += red[q][t][oc + e];
-    r[e] = acc_w;
-  }
-  if (part != nullptr) {
-    float* dst = part + ((int64_t)range * m_valid + t) * d_out + o;
-    *(float4*)dst = make_float4(r[0], r[1], r[2], r[3]);
-    *(float4*)(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
-  } else if (Y_F16) {
-    uint16_t* dst = (uint16_t*)Y + t * ld_y + o;
-    *(uint2*)dst = make_uint2((uint32_t)f2h_bits(r[0]) | ((uint32_t)f2h_bits(r[1]) << 16),
-                              (uint32_t)f2h_bits(r[2]) | ((uint32_t)f2h_bits(r[3]) << 16));
-    *(uint2*)(dst + 4) = make_uint2((uint32_t)f2h_bits(r[4]) | ((uint32_t)f2h_bits(r[5]) << 16),
-                                    (uint32_t)f2h_bits(r[6]) | ((uint32_t)f2h_bits(r[7]) << 16));
-  } else {
-    float* dst = (float*)Y + t * ld_y + o;
-    *(float4*)dst = make_float4(r[0], r[1], r[2], r[3]);
-    *(float4*)(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
+    for (int w2 = 1; w2 < kSkWaves; ++w2) {
+      lo = lo + *(const f4s*)&slot[w2][ln][off];
+      hi = hi + *(const f4s*)&slot[w2][ln][off + 4];
+    }
+    const float r[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (part != nullptr) {
+      float* dst = part + ((int64_t)range * m_valid + t) * d_out + o;
+      *(float4*)dst = make_float4(r[0], r[1], r[2], r[3]);
+      *(float4*)(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
+    } else if (Y_F16) {
+      uint16_t* dst = (uint16_t*)Y + t * ld_y + o;
+      *(uint2*)dst = make_uint2((uint32_t)f2h_bits(r[0]) | ((uint32_t)f2h_bits(r[1]) << 16),
+                                (uint32_t)f2h_bits(r[2]) | ((uint32_t)f2h_bits(r[3]) << 16));
+      *(uint2*)(dst + 4) = make_uint2((uint32_t)f2h_bits(r[4]) | ((uint32_t)f2h_bits(r[5]) << 16),
+                                      (uint32_t)f2h_bits(r[6]) | ((uint32_t)f2h_bits(r[7]) << 16));
+    } else {
+      float* dst = (float*)Y + t * ld_y + o;
+      *(float4*)dst = make_float4(r[0], r[1], r[2], r[3]);
+      *(float4*)(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
+    }
   }
 }
 
-// Input ranges of the few-token kernel: one 128-row chunk per wave (4 per
-// block), so that every wave's loads go out at once and the grid holds many
-// waves; the ranges' fp32 results (M x d_out each) cost 2 M / 128 bytes per
-// weight against its 0.5 + 2.5 / G bytes of codes, scales and zero points.
-static int64_t skinny_chunks_per_block(int64_t d_out, int64_t d_in) {
-  (void)d_out;
-  (void)d_in;
-  return kSkWaves;
-}
-static int64_t skinny_splits(int64_t d_out, int64_t d_in) {
-  const int64_t cpb = skinny_chunks_per_block(d_out, d_in);
-  return ((d_in + kSkChunk - 1) / kSkChunk + cpb - 1) / cpb;
+// Input ranges of the few-token kernel: 512 rows each (one 128-row chunk per
+// wave); their fp32 results (M x d_out each) cost 2 M / 512 bytes per weight
+// and input row, against 0.5 + 2.5 / G bytes of codes, scales and zero points.
+static int64_t skinny_splits(int64_t d_in) {
+  return (d_in + kSkWaves * kSkChunk - 1) / (kSkWaves * kSkChunk);
 }
 int64_t w4a16_skinny_part_floats(int64_t M, int64_t d_out, int64_t d_in) {
-  const int64_t s = skinny_splits(d_out, d_in);
+  const int64_t s = skinny_splits(d_in);
   return s > 1 ? s * M * d_out : 0;
 }
-bool w4a16_uses_skinny(const void* X, int64_t M, int64_t ld_x) {
-  return M >= 2 && M <= kSkTokens && ((uintptr_t)X & 15u) == 0 && ld_x % 8 == 0;
+bool w4a16_uses_skinny(const void* X, int64_t M, int64_t ld_x, const void* qweight, int64_t d_out) {
+  return M >= 2 && M <= kSkTokens && ((uintptr_t)X & 15u) == 0 && ld_x % 8 == 0 && ((uintptr_t)qweight & 7u) == 0 &&
+         (d_out / 8) % 2 == 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -693,19 +712,22 @@ bool w4a16_uses_gemm(const void* X, int64_t M, int64_t ld_x, int64_t d_in) {
 hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* qzeros, int64_t d_out, int64_t d_in, int group_size, void* Y, int64_t ld_y,
                         bool y_f16, float* part, hipStream_t stream) {
-  if (w4a16_uses_skinny(X, M, ld_x)) {
-    const int64_t cpb = skinny_chunks_per_block(d_out, d_in);
-    const int64_t n_split = skinny_splits(d_out, d_in);
+  if (w4a16_uses_skinny(X, M, ld_x, qweight, d_out)) {
+    const int64_t n_split = skinny_splits(d_in);
     const int n_strips = (int)((d_out / 8 + kSkWords - 1) / kSkWords);
     const unsigned g = (unsigned)(n_strips * n_split);
     float* sp = n_split > 1 ? part : nullptr;
-    if (y_f16)
-      w4a16_skinny_kernel<true><<<g, kSkWaves * kWave, 0, stream>>>(X, ld_x, (int)M, d_in, qweight, scales, qzeros,
-                                                                   d_out, group_size, (int)cpb, n_strips, Y, ld_y, sp);
-    else
-      w4a16_skinny_kernel<false><<<g, kSkWaves * kWave, 0, stream>>>(X, ld_x, (int)M, d_in, qweight, scales, qzeros,
-                                                                    d_out, group_size, (int)cpb, n_strips, Y, ld_y,
-                                                                    sp);
+#define AWQ_SKINNY(GG, YF)                                                                                \
+  w4a16_skinny_kernel<GG, YF><<<g, kSkWaves * kWave, 0, stream>>>(X, ld_x, (int)M, d_in, qweight, scales, qzeros, \
+                                                                  d_out, n_strips, Y, ld_y, sp)
+    if (group_size == 128) {
+      if (y_f16) AWQ_SKINNY(128, true); else AWQ_SKINNY(128, false);
+    } else if (group_size == 64) {
+      if (y_f16) AWQ_SKINNY(64, true); else AWQ_SKINNY(64, false);
+    } else {
+      if (y_f16) AWQ_SKINNY(32, true); else AWQ_SKINNY(32, false);
+    }
+#undef AWQ_SKINNY
     if (n_split > 1) {
       const dim3 rgrid((unsigned)((d_out / 4 + kRdCols - 1) / kRdCols), (unsigned)M);
       w4a16_reduce_kernel<<<rgrid, kRdCols * kRdSplit, 0, stream>>>(part, n_split, (int)M, d_out, Y, ld_y,

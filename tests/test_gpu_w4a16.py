@@ -68,7 +68,8 @@ def _bound(X, qw, sc, qz, d_out, G, n_slices, kind="gemv"):
 
 def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
     """With X rows 16-byte aligned the kernel is the few-token matrix-core path at
-    2 to 16 tokens and the GEMM from 17; else (and at one token) the GEMV."""
+    2 to 16 tokens (d_out a multiple of 16) and the GEMM from 17; else (and at
+    one token) the GEMV."""
     import torch
     M, d_in = X.shape
     Xp = X if ld_x is None else np.pad(X, ((0, 0), (0, ld_x - d_in)))
@@ -81,7 +82,8 @@ def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
     Y = host(plan.run()).astype(F64)
     ref = O.w4a16_matmul(X, qw, sc, qz, d_out, G)
     ldx = d_in if ld_x is None else ld_x
-    kind = "gemv" if (ldx % 8 or M == 1) else ("few" if M <= 16 else "gemm")
+    few = M <= 16 and (d_out // 8) % 2 == 0          # the few-token path reads word pairs
+    kind = "gemv" if (ldx % 8 or M == 1 or (M <= 16 and not few)) else ("few" if M <= 16 else "gemm")
     tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 255) // 256, kind)
     if out_dtype == "f16":
         tol = tol + np.spacing(np.abs(ref).astype(np.float16) * np.float16(1.002)).astype(F64)
@@ -106,8 +108,14 @@ def test_w4a16_decode_full_size(A, name, d_out, d_in, G, zeros):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 16])
-@pytest.mark.parametrize("d_out,d_in,G,out_dtype", [(1032, 384, 64, "f16"), (520, 96, 32, "f32"),
-                                                    (16, 256, 128, "f32")])
+@pytest.mark.parametrize("d_out,d_in,G,out_dtype", [
+    (1032, 384, 64, "f16"),    # odd word count: the GEMV below 17 tokens
+    (520, 96, 32, "f32"),      # odd word count
+    (1040, 384, 64, "f16"),    # 4 strips of 32 words + 2; one input range, its last wave past d_in
+    (560, 672, 32, "f32"),     # 2 ranges, the second 160 rows (one wave of 4 steps, one of 1)
+    (2064, 1088, 64, "f16"),   # 3 ranges, the last 64 rows
+    (16, 256, 128, "f32"),     # one strip of 2 words
+])
 def test_w4a16_tokens_and_ragged_shapes(A, M, d_out, d_in, G, out_dtype):
     say(f"w4a16 M={M} d_out={d_out} d_in={d_in} G={G} {out_dtype}")
     qw, sc, qz = _random_packed(7 * M + d_out, d_out, d_in, G, True)
@@ -132,10 +140,10 @@ def test_w4a16_few_tokens_full_size(A, M, name, d_out, d_in, G, zeros, out_dtype
 
 def test_w4a16_strides(A):
     say("w4a16 strided X and Y")
-    qw, sc, qz = _random_packed(11, 264, 256, 64, True)
+    qw, sc, qz = _random_packed(11, 272, 256, 64, True)
     X = (np.random.default_rng(12).standard_normal((3, 256))).astype(np.float16)
-    _check(A, X, qw, sc, qz, 264, 64, "f16", ld_x=264, ld_y=272)   # few-token path, padded rows
-    _check(A, X, qw, sc, qz, 264, 64, "f32", ld_x=300, ld_y=268)   # rows not 16-byte aligned: GEMV
+    _check(A, X, qw, sc, qz, 272, 64, "f16", ld_x=264, ld_y=280)   # few-token path, padded rows
+    _check(A, X, qw, sc, qz, 272, 64, "f32", ld_x=300, ld_y=276)   # rows not 16-byte aligned: GEMV
 
 
 @pytest.mark.parametrize("asym", [False, True])
