@@ -1001,10 +1001,10 @@ def bench_w4a16(args):
 
     tot_b = sum(alg_bytes(d_out, d_in) for *_, d_out, d_in in layers)
     achieved = tot_b / (sum(call_ms) * 1e-3) / 1e9
-    # 17 tokens or more run the matrix-core GEMM: quoted against the fp16 MFMA peak;
-    # 2..16 tokens the few-token matrix-core path, which reads every packed word
+    # 65 tokens or more run the matrix-core GEMM: quoted against the fp16 MFMA peak;
+    # 2..64 tokens the few-token matrix-core path, which reads every packed word
     # once for all tokens and is quoted against HBM like the one-token GEMV
-    gemm = M >= 17
+    gemm = M >= 65
     tflops = 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (sum(call_ms) * 1e-3) / 1e12
     kinds = {}
     for (qw, sc, qz, x, y, d_out, d_in), t in zip(layers, call_ms):
@@ -1122,6 +1122,147 @@ def bench_valu_probe(args):
             "mfma_f32_32x32x16_f16_2_waves_per_simd": mfma}
 
 
+def bench_floor_probe(args):
+    """Floors of the W4A16 decode step (the probe library).  For the packed
+    linears of the 36 Qwen3-8B-shaped blocks, in the step's order: one launch of
+    the read probe per linear over as many bytes as its codes, scales and zero
+    points (a fresh buffer each, 3.6 GB in all, so nothing is served from a
+    cache); the same followed by an empty one-block launch per linear (where a
+    split's reduction would go); and empty launches of the read probe's grids.
+    Each sequence is captured as a HIP graph and replayed like the W4A16 step;
+    each read launch is also timed alone with HIP events around it."""
+    import torch
+    import workloads as WL
+    from post_weight_quantization_awq_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        B.build_probe()
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.awq_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.awq_probe_empty.restype = ctypes.c_int
+    lib.awq_probe_read_blocks.argtypes = [ctypes.c_int64]
+    lib.awq_probe_read_blocks.restype = ctypes.c_int64
+    lib.awq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.awq_probe_read.restype = ctypes.c_int
+    wl = WL.WORKLOADS["qwen3_8b_decode_w4a16"]
+    G = args.group_size or wl.group_sizes[0]
+    dev = torch.device("cuda:0")
+    shapes = []
+    for g in wl.groups:
+        nb = g.d_out * g.d_in // 2 + 2 * g.d_out * (g.d_in // G) + g.d_out * (g.d_in // G) // 2
+        shapes.append((f"{g.d_out}x{g.d_in}", (nb + 15) // 16 * 16))
+    calls = []
+    for b in range(args.blocks):
+        for key, nb in shapes:
+            buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+            buf.fill_(0x5A)
+            calls.append((key, nb, buf))
+    n_out = max(lib.awq_probe_read_blocks(nb) for _, nb, _ in calls)
+    out = torch.zeros(n_out, dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    K = args.steps
+
+    def read(nb, buf):
+        assert lib.awq_probe_read(buf.data_ptr(), nb, out.data_ptr(), s.cuda_stream) == 0
+
+    def step_read():
+        for _, nb, buf in calls:
+            read(nb, buf)
+
+    def step_read_empty():
+        for _, nb, buf in calls:
+            read(nb, buf)
+            assert lib.awq_probe_empty(1, 256, s.cuda_stream) == 0
+
+    def step_empty():
+        for _, nb, _ in calls:
+            assert lib.awq_probe_empty(int(lib.awq_probe_read_blocks(nb)), 256, s.cuda_stream) == 0
+
+    def timed(fn):
+        s.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            fn()
+        s.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+
+    res = {}
+    with torch.cuda.stream(s):
+        for name, fn in (("read", step_read), ("read_then_empty", step_read_empty), ("empty", step_empty)):
+            for _ in range(args.warmup):
+                fn()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+            for _ in range(args.warmup):
+                g.replay()
+            res[name] = {"graph_ms_per_step": timed(g.replay), "eager_ms_per_step": timed(fn)}
+    n = len(calls)
+
+    def per_call(launch):
+        ev = HipEvents(2 * n * K)
+        with torch.cuda.stream(s):
+            for k in range(K):
+                for i, c in enumerate(calls):
+                    ev.record(2 * (k * n + i), s)
+                    launch(c)
+                    ev.record(2 * (k * n + i) + 1, s)
+        s.synchronize()
+        ms_ = [sum(ev.ms(2 * (k * n + i), 2 * (k * n + i) + 1) for k in range(K)) / K for i in range(n)]
+        ev.close()
+        return ms_
+
+    call_ms = per_call(lambda c: read(c[1], c[2]))
+    kinds = {}
+    for (key, nb, _), t in zip(calls, call_ms):
+        kb = kinds.setdefault(key, [0.0, 0, 0])
+        kb[0] += t
+        kb[1] += nb
+        kb[2] += 1
+    tot = sum(nb for _, nb, _ in calls)
+    # the few-token kernel's load pattern over each linear's codes, no arithmetic
+    lib.awq_probe_strip_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.awq_probe_strip_read.restype = ctypes.c_int
+    lib.awq_probe_strip_read_blocks.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    lib.awq_probe_strip_read_blocks.restype = ctypes.c_int64
+    dims = {f"{g.d_out}x{g.d_in}": (g.d_out, g.d_in) for g in wl.groups}
+    strips = {}
+    for wpl, spw in ((1, 4), (2, 4), (1, 8)):
+        nb_out = max(lib.awq_probe_strip_read_blocks(dims[k][1], dims[k][0] // 8, wpl, spw) for k, _, _ in calls)
+        o2 = torch.zeros(int(nb_out), dtype=torch.int32, device=dev)
+
+        def sl(c, wpl=wpl, spw=spw, o2=o2):
+            d_out, d_in = dims[c[0]]
+            assert lib.awq_probe_strip_read(c[2].data_ptr(), d_in, d_out // 8, wpl, spw, o2.data_ptr(),
+                                            s.cuda_stream) == 0
+        with torch.cuda.stream(s):
+            for c in calls:
+                sl(c)
+        ms_ = per_call(sl)
+        kb = {}
+        for c, t in zip(calls, ms_):
+            e = kb.setdefault(c[0], [0.0, 0, 0])
+            e[0] += t
+            e[1] += dims[c[0]][0] * dims[c[0]][1] // 2
+            e[2] += 1
+        strips[f"{16 * wpl}_words_per_strip_{32 * spw}_rows_per_wave"] = {
+            k: {"us": 1e3 * v[0] / v[2], "GBps": v[1] / (v[0] * 1e-3) / 1e9} for k, v in kb.items()}
+    ms = res["read"]["graph_ms_per_step"]
+    return {"metric": "W4A16 decode step floors (probe)", "value": tot / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "decode_floor_probe", "blocks": args.blocks, "group_size": G,
+                       "launches_per_step": n, "bytes_per_step": tot},
+            "steps_ms": res,
+            "empty_launch_us_in_graph": 1e3 * res["empty"]["graph_ms_per_step"] / n,
+            "second_launch_us_in_graph": 1e3 * (res["read_then_empty"]["graph_ms_per_step"] - ms) / n,
+            "per_shape_us": {k: 1e3 * v[0] / v[2] for k, v in kinds.items()},
+            "per_shape_GBps": {k: v[1] / (v[0] * 1e-3) / 1e9 for k, v in kinds.items()},
+            "per_call_GBps": tot / (sum(call_ms) * 1e-3) / 1e9,
+            "strip_reads_codes_only": strips}
+
+
 def bench_copy(args):
     """Plain device copy of 512 MiB (torch), the calibration of the HBM byte counters."""
     import torch
@@ -1150,7 +1291,7 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_8b_sweep",
                     choices=["single_linear_256x512", "q_proj_4096x4096", "qkv_6144x4096_output",
                              "mlp_output_clip", "qwen3_8b_sweep", "qwen3_8b_export", "qwen3_8b_decode_w4a16",
-                             "copy_512MiB", "valu_issue_probe"])
+                             "copy_512MiB", "valu_issue_probe", "decode_floor_probe"])
     ap.add_argument("--group-size", type=int, default=None)
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
     ap.add_argument("--streams", type=int, default=8,
@@ -1195,6 +1336,8 @@ def main() -> int:
         out = bench_copy(args)
     elif args.workload == "valu_issue_probe":
         out = bench_valu_probe(args)
+    elif args.workload == "decode_floor_probe":
+        out = bench_floor_probe(args)
     else:
         out = bench_output(args, args.workload)
     print(json.dumps(out), flush=True)

@@ -545,7 +545,7 @@ awq_status awq_w4a16_workspace(int64_t M, int64_t d_out, int64_t d_in, size_t* b
   const size_t gemv = (size_t)w4a16_slices(d_in) * (size_t)w4a16_mt(M) * (size_t)d_out;
   const size_t gemm = (size_t)w4a16_gemm_part_floats(M, d_out, d_in);
   const size_t skinny =   // the few-token path's input ranges
-      (M >= 2 && M <= 16 && d_out > 0 && d_in > 0) ? (size_t)w4a16_skinny_part_floats(M, d_out, d_in) : 0;
+      (d_out > 0 && d_in > 0) ? (size_t)w4a16_skinny_part_floats(M, d_out, d_in) : 0;
   size_t need = gemv > gemm ? gemv : gemm;
   need = need > skinny ? need : skinny;
   *bytes = align256(need * sizeof(float));

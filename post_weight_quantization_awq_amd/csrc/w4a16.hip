@@ -232,10 +232,10 @@ __global__ __launch_bounds__(kRdCols * kRdSplit) void w4a16_reduce_kernel(const 
 int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 
 // ---------------------------------------------------------------------------
-// Few tokens (2..16): one read of every packed word for all tokens, products on
+// Few tokens (2..64): one read of every packed word for all tokens, products on
 // the matrix cores (v_mfma_f32_16x16x32_f16).  A = weights (16 outputs x 32
-// inputs), B = the activations (32 inputs x 16 tokens, zero past the last
-// token).  A wave owns 32 word columns (256 outputs) of a 128-row chunk; lane
+// inputs), B = the activations (32 inputs x a tile of 16 tokens, zero past the
+// last token; the code words are dequantized again for every tile).  A wave owns 32 word columns (256 outputs) of a 128-row chunk; lane
 // l loads the word pair of columns c0 + 2 (l & 15) + {0, 1} in rows
 // k + 8 (l >> 4) + 0..7 of each 32-row step with one 8-byte load per row, so a
 // load instruction reads four whole 128-byte runs of packed rows (a strip of
@@ -256,7 +256,8 @@ int64_t w4a16_cols(int64_t d_out) { return (d_out / 8 + kWave - 1) / kWave; }
 // order, and the reduction kernel adds the ranges' fp32 results in order (a
 // single range writes Y directly).
 // ---------------------------------------------------------------------------
-constexpr int kSkTokens = 16;
+constexpr int kSkTile = 16;                   // tokens per B operand
+constexpr int kSkMaxTokens = 64;
 constexpr int kSkWords = 32;                   // word columns per block (and per wave)
 constexpr int kSkWaves = 4;
 constexpr int kSkChunk = 128;                  // input rows per wave
@@ -283,7 +284,62 @@ __device__ __forceinline__ void zero_consts(uint32_t zw, uint32_t* zc) {
   }
 }
 
-template <int G, bool Y_F16>
+// One 32-row step of word column h of the lane's pair: the 8 codes of the
+// lane's rows dequantized to exact fp16 (u - z) (or 16 (u - z), odd nibbles)
+// and multiplied with the activations, one product per nibble position j.
+__device__ __forceinline__ void skinny_mma(const u2s (&ws)[8], int h, const uint32_t (&zc)[8], h8s bx,
+                                           f4s (&acc)[8]) {
+  uint32_t a[8][4];   // a[j][p]: fp16 pair (rows 2p, 2p + 1) of nibble j
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t sel = (uint32_t)b | (12u << 8) | ((uint32_t)(4 + b) << 16) | (12u << 24);
+      const uint32_t x2 = __builtin_amdgcn_perm(ws[2 * p + 1][h], ws[2 * p][h], sel);
+      a[2 * b][p] = pk_sub_f16(and_or(x2, 0x000F000Fu, 0x64006400u), zc[2 * b]);
+      a[2 * b + 1][p] = pk_sub_f16(and_or(x2, 0x00F000F0u, 0x64006400u), zc[2 * b + 1]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 av = make_uint4(a[j][0], a[j][1], a[j][2], a[j][3]);
+    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8s, av), bx, acc[j], 0, 0, 0);
+  }
+}
+
+// A group's sums of word column h times the group's scales (sg: the strip's
+// 256 scales of the group, in LDS) into half hs of the lane's slot: written by
+// the first group of the chunk, added by the others.
+__device__ __forceinline__ void skinny_fold(const f4s (&acc)[8], const uint16_t* sg, int lh, int h, int hs,
+                                            float* my, bool first) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    // scales of word column c0 + 8 lh + 2 v + h
+    const uint4 sv = *(const uint4*)(sg + 8 * (8 * lh + 2 * v + h));
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    float val[8];   // the 8 outputs of the word column, in output order
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      constexpr int kOrd[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+      const int o = kOrd[j];
+      float sc = h2f((uint16_t)((sw[o >> 1] >> (16 * (o & 1))) & 0xFFFFu));
+      if (j & 1) sc *= 0.0625f;   // the odd nibbles carry 16 (u - z)
+      val[o] = acc[j][v] * sc;
+    }
+    f4s* dst = (f4s*)(my + (hs * 4 + v) * 8);
+    const f4s lo = {val[0], val[1], val[2], val[3]}, hi = {val[4], val[5], val[6], val[7]};
+    if (first) {
+      dst[0] = lo;
+      dst[1] = hi;
+    } else {
+      dst[0] = dst[0] + lo;
+      dst[1] = dst[1] + hi;
+    }
+  }
+}
+
+// MULTI: more than 16 tokens, in tiles of 16 (the B operand's columns).
+template <int G, bool Y_F16, bool MULTI>
 __global__ __launch_bounds__(kSkWaves * kWave, 2) void w4a16_skinny_kernel(
     const uint16_t* __restrict__ X, int64_t ld_x, int m_valid, int64_t d_in, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros, int64_t d_out, int n_strips,
@@ -309,8 +365,7 @@ __global__ __launch_bounds__(kSkWaves * kWave, 2) void w4a16_skinny_kernel(
   // its outputs are never stored)
   const int64_t cp = c0 + 2 * li + 2 <= n_words ? c0 + 2 * li : n_words - 2;
   const int64_t r0 = ((int64_t)range * kSkWaves + wv) * kSkChunk;
-  const bool tok = li < m_valid;
-  const uint16_t* xrow = X + (int64_t)(tok ? li : m_valid - 1) * ld_x + 8 * lh;
+  const uint16_t* xrow = X + (int64_t)(li < m_valid ? li : m_valid - 1) * ld_x + 8 * lh;   // tile 0
   float* my = &slot[wv][lane][0];
 
   // Every step of the chunk runs, with no branch, so that all loads go out at
@@ -330,14 +385,14 @@ __global__ __launch_bounds__(kSkWaves * kWave, 2) void w4a16_skinny_kernel(
   // step, so that no wait for a later group's constants drains the loads.
   constexpr int kGroups = kSkSteps / kSpg;
   uint32_t zw[kGroups][2];
-  u2s sg[kGroups];
+  u2s sgr[kGroups];
   const int64_t so = 8 * c0 + 4 * lane + 4 <= d_out ? 8 * c0 + 4 * lane : d_out - 4;
 #pragma unroll
   for (int gi = 0; gi < kGroups; ++gi) {
     const int64_t g = ks[gi * kSpg] / G;
     zw[gi][0] = qzeros != nullptr ? qzeros[g * n_words + cp] : 0x77777777u;
     zw[gi][1] = qzeros != nullptr ? qzeros[g * n_words + cp + 1] : 0x77777777u;
-    sg[gi] = *(const u2s*)(scales + g * d_out + so);
+    sgr[gi] = *(const u2s*)(scales + g * d_out + so);
   }
   u2s w[kSkSteps][8];
   uint4 xv[kSkSteps];
@@ -351,81 +406,15 @@ __global__ __launch_bounds__(kSkWaves * kWave, 2) void w4a16_skinny_kernel(
   __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any arithmetic below
   uint16_t* ssc = &scl[wv][0][0];
 #pragma unroll
-  for (int gi = 0; gi < kGroups; ++gi) *(u2s*)(ssc + gi * kSkWords * 8 + 4 * lane) = sg[gi];
-  f4s acc[2][8];
-  uint32_t zc[2][8];
-#pragma unroll
-  for (int st = 0; st < kSkSteps; ++st) {
-    {
-      if (st % kSpg == 0) {   // a group starts: its zero points, fresh sums
-        zero_consts(zw[st / kSpg][0], zc[0]);
-        zero_consts(zw[st / kSpg][1], zc[1]);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[h][j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
-      }
-      // masked where used, so that a step waits only for its own loads
-      const h8s bx = __builtin_bit_cast(h8s, (tok && live[st]) ? xv[st] : make_uint4(0u, 0u, 0u, 0u));
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t a[8][4];   // a[j][p]: fp16 pair (rows 2p, 2p + 1) of nibble j
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t sel = (uint32_t)b | (12u << 8) | ((uint32_t)(4 + b) << 16) | (12u << 24);
-            const uint32_t x2 = __builtin_amdgcn_perm(w[st][2 * p + 1][h], w[st][2 * p][h], sel);
-            a[2 * b][p] = pk_sub_f16(and_or(x2, 0x000F000Fu, 0x64006400u), zc[h][2 * b]);
-            a[2 * b + 1][p] = pk_sub_f16(and_or(x2, 0x00F000F0u, 0x64006400u), zc[h][2 * b + 1]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint4 av = make_uint4(a[j][0], a[j][1], a[j][2], a[j][3]);
-          acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8s, av), bx, acc[h][j], 0, 0, 0);
-        }
-      }
-      if ((st + 1) % kSpg == 0) {   // the group ends: its sums times its scales into the slot
-        const bool first = st + 1 == kSpg;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            // scales of word column c0 + 8 lh + 2 v + h of this group
-            const uint4 sv = *(const uint4*)(ssc + (st / kSpg) * kSkWords * 8 + 8 * (8 * lh + 2 * v + h));
-            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-            float val[8];   // the 8 outputs of word column c0 + 8 lh + 2 v + h, in output order
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              constexpr int kOrd[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-              const int o = kOrd[j];
-              float sc = h2f((uint16_t)((sw[o >> 1] >> (16 * (o & 1))) & 0xFFFFu));
-              if (j & 1) sc *= 0.0625f;   // the odd nibbles carry 16 (u - z)
-              val[o] = acc[h][j][v] * sc;
-            }
-            f4s* dst = (f4s*)(my + (h * 4 + v) * 8);
-            const f4s lo = {val[0], val[1], val[2], val[3]}, hi = {val[4], val[5], val[6], val[7]};
-            if (first) {
-              dst[0] = lo;
-              dst[1] = hi;
-            } else {
-              dst[0] = dst[0] + lo;
-              dst[1] = dst[1] + hi;
-            }
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // 8 consecutive outputs (one word column) of one token per work item, the
-  // waves added in order 0..3
-  for (int idx = tid; idx < kSkTokens * kSkWords; idx += kSkWaves * kWave) {
-    const int t = idx / kSkWords, q8 = idx % kSkWords;   // token, word column in the strip
+  for (int gi = 0; gi < kGroups; ++gi) *(u2s*)(ssc + gi * kSkWords * 8 + 4 * lane) = sgr[gi];
+
+  // the results of one token tile of the slots: 8 consecutive outputs (word
+  // column c0 + q8) of token t, half hs of lane ln's slot, the waves added in
+  // order 0..3
+  auto store8 = [&](int t, int q8, int ln, int hs) {
     const int64_t o = (c0 + q8) * 8;
-    if (t >= m_valid || o >= d_out) continue;
-    const int ln = t + 16 * (q8 >> 3), off = ((q8 & 1) * 4 + ((q8 >> 1) & 3)) * 8;
+    if (t >= m_valid || o >= d_out) return;
+    const int off = (hs * 4 + ((q8 >> 1) & 3)) * 8;
     f4s lo = *(const f4s*)&slot[0][ln][off], hi = *(const f4s*)&slot[0][ln][off + 4];
 #pragma unroll
     for (int w2 = 1; w2 < kSkWaves; ++w2) {
@@ -448,6 +437,137 @@ __global__ __launch_bounds__(kSkWaves * kWave, 2) void w4a16_skinny_kernel(
       *(float4*)dst = make_float4(r[0], r[1], r[2], r[3]);
       *(float4*)(dst + 4) = make_float4(r[4], r[5], r[6], r[7]);
     }
+  };
+
+  if constexpr (!MULTI) {
+    // one tile: both word columns of the pair per step
+    const bool tok = li < m_valid;
+    f4s acc[2][8];
+    uint32_t zc[2][8];
+#pragma unroll
+    for (int st = 0; st < kSkSteps; ++st) {
+      if (st % kSpg == 0) {   // a group starts: its zero points, fresh sums
+        zero_consts(zw[st / kSpg][0], zc[0]);
+        zero_consts(zw[st / kSpg][1], zc[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[h][j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      // masked where used, so that a step waits only for its own loads
+      const h8s bx = __builtin_bit_cast(h8s, (tok && live[st]) ? xv[st] : make_uint4(0u, 0u, 0u, 0u));
+      skinny_mma(w[st], 0, zc[0], bx, acc[0]);
+      skinny_mma(w[st], 1, zc[1], bx, acc[1]);
+      if ((st + 1) % kSpg == 0) {   // the group ends: its sums times its scales into the slot
+        skinny_fold(acc[0], ssc + (st / kSpg) * kSkWords * 8, lh, 0, 0, my, st + 1 == kSpg);
+        skinny_fold(acc[1], ssc + (st / kSpg) * kSkWords * 8, lh, 1, 1, my, st + 1 == kSpg);
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kSkTile * kSkWords; idx += kSkWaves * kWave) {
+      const int t = idx / kSkWords, q8 = idx % kSkWords;   // token, word column in the strip
+      store8(t, q8, t + 16 * (q8 >> 3), q8 & 1);
+    }
+  } else {
+    // Passes of NT tiles (NT = 2 at G = 128: each dequantized fragment feeds
+    // the products of both tiles; 1 at smaller groups, whose extra folds leave
+    // no registers for a second set of sums).  Per pass, word column h = 0 of
+    // every lane's pair, then h = 1, each through the slots (half hs = the
+    // tile of the pass) and stored before the next.
+    constexpr int NT = G == 128 ? 2 : 1;
+    uint4 xt[NT][kSkSteps];   // activations of the pass's tiles
+#pragma unroll
+    for (int st = 0; st < kSkSteps; ++st) xt[0][st] = xv[st];
+#pragma unroll
+    for (int ti = 1; ti < NT; ++ti) {
+      const int tn = kSkTile * ti + li;
+      const uint16_t* xr = X + (int64_t)(tn < m_valid ? tn : m_valid - 1) * ld_x + 8 * lh;
+#pragma unroll
+      for (int st = 0; st < kSkSteps; ++st) xt[ti][st] = *(const uint4*)(xr + ks[st]);
+    }
+    const int n_pass = (m_valid + NT * kSkTile - 1) / (NT * kSkTile);
+    for (int ps = 0; ps < n_pass; ++ps) {
+      bool tok[NT];
+#pragma unroll
+      for (int ti = 0; ti < NT; ++ti) tok[ti] = NT * kSkTile * ps + kSkTile * ti + li < m_valid;
+      // The code words pass through an empty asm each pass, so the compiler
+      // cannot hoist the (token-independent) dequantization out of the pass
+      // loop, which would hold every step's fp16 operands in registers.
+#pragma unroll
+      for (int st = 0; st < kSkSteps; ++st)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          uint32_t lo = w[st][r][0], hi = w[st][r][1];
+          asm volatile("" : "+v"(lo), "+v"(hi));
+          w[st][r] = (u2s){lo, hi};
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f4s acc[NT][8];
+        uint32_t zc[8];
+#pragma unroll
+        for (int st = 0; st < kSkSteps; ++st) {
+          if (st % kSpg == 0) {
+            zero_consts(zw[st / kSpg][h], zc);
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) acc[ti][j] = (f4s){0.0f, 0.0f, 0.0f, 0.0f};
+          }
+          h8s bt[NT];
+#pragma unroll
+          for (int ti = 0; ti < NT; ++ti)
+            bt[ti] = __builtin_bit_cast(h8s, (tok[ti] && live[st]) ? xt[ti][st] : make_uint4(0u, 0u, 0u, 0u));
+          // byte b of the lane's 8 rows: nibble positions 2b and 2b + 1, the
+          // products of every tile, before the next byte (few fragment
+          // registers live)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            uint32_t al[4], ah[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const uint32_t sel = (uint32_t)b | (12u << 8) | ((uint32_t)(4 + b) << 16) | (12u << 24);
+              const uint32_t x2 = __builtin_amdgcn_perm(w[st][2 * p + 1][h], w[st][2 * p][h], sel);
+              al[p] = pk_sub_f16(and_or(x2, 0x000F000Fu, 0x64006400u), zc[2 * b]);
+              ah[p] = pk_sub_f16(and_or(x2, 0x00F000F0u, 0x64006400u), zc[2 * b + 1]);
+            }
+            const h8s avl = __builtin_bit_cast(h8s, make_uint4(al[0], al[1], al[2], al[3]));
+            const h8s avh = __builtin_bit_cast(h8s, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+              acc[ti][2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(avl, bt[ti], acc[ti][2 * b], 0, 0, 0);
+              acc[ti][2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(avh, bt[ti], acc[ti][2 * b + 1], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if ((st + 1) % kSpg == 0) {
+            const uint16_t* sg = ssc + (st / kSpg) * kSkWords * 8;
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+              skinny_fold(acc[ti], sg, lh, h, ti, my, st + 1 == kSpg);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+        if (h == 1 && ps + 1 < n_pass) {   // the next pass's activations, loading while this one is stored
+#pragma unroll
+          for (int ti = 0; ti < NT; ++ti) {
+            const int tn = NT * kSkTile * (ps + 1) + kSkTile * ti + li;
+            const uint16_t* xr = X + (int64_t)(tn < m_valid ? tn : m_valid - 1) * ld_x + 8 * lh;
+#pragma unroll
+            for (int st = 0; st < kSkSteps; ++st) xt[ti][st] = *(const uint4*)(xr + ks[st]);
+          }
+        }
+        __syncthreads();
+        // word columns of parity h of the pass's tiles: NT x 16 tokens x 16 columns
+        for (int idx = tid; idx < NT * kSkTile * (kSkWords / 2); idx += kSkWaves * kWave) {
+          const int ti = idx / (kSkTile * kSkWords / 2), rem = idx % (kSkTile * kSkWords / 2);
+          const int tl = rem / (kSkWords / 2), q8 = 2 * (rem % (kSkWords / 2)) + h;
+          store8(NT * kSkTile * ps + kSkTile * ti + tl, q8, tl + 16 * (q8 >> 3), ti);
+        }
+        __syncthreads();   // the slots are read before the next pass writes them
+      }
+    }
   }
 }
 
@@ -458,12 +578,13 @@ static int64_t skinny_splits(int64_t d_in) {
   return (d_in + kSkWaves * kSkChunk - 1) / (kSkWaves * kSkChunk);
 }
 int64_t w4a16_skinny_part_floats(int64_t M, int64_t d_out, int64_t d_in) {
+  if (M < 2 || M > kSkMaxTokens) return 0;
   const int64_t s = skinny_splits(d_in);
   return s > 1 ? s * M * d_out : 0;
 }
 bool w4a16_uses_skinny(const void* X, int64_t M, int64_t ld_x, const void* qweight, int64_t d_out) {
-  return M >= 2 && M <= kSkTokens && ((uintptr_t)X & 15u) == 0 && ld_x % 8 == 0 && ((uintptr_t)qweight & 7u) == 0 &&
-         (d_out / 8) % 2 == 0;
+  return M >= 2 && M <= kSkMaxTokens && ((uintptr_t)X & 15u) == 0 && ld_x % 8 == 0 &&
+         ((uintptr_t)qweight & 7u) == 0 && (d_out / 8) % 2 == 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -717,16 +838,26 @@ hipError_t launch_w4a16(const uint16_t* X, int64_t M, int64_t ld_x, const uint32
     const int n_strips = (int)((d_out / 8 + kSkWords - 1) / kSkWords);
     const unsigned g = (unsigned)(n_strips * n_split);
     float* sp = n_split > 1 ? part : nullptr;
-#define AWQ_SKINNY(GG, YF)                                                                                \
-  w4a16_skinny_kernel<GG, YF><<<g, kSkWaves * kWave, 0, stream>>>(X, ld_x, (int)M, d_in, qweight, scales, qzeros, \
-                                                                  d_out, n_strips, Y, ld_y, sp)
-    if (group_size == 128) {
-      if (y_f16) AWQ_SKINNY(128, true); else AWQ_SKINNY(128, false);
-    } else if (group_size == 64) {
-      if (y_f16) AWQ_SKINNY(64, true); else AWQ_SKINNY(64, false);
+#define AWQ_SKINNY(GG, YF, MU)                                                                          \
+  w4a16_skinny_kernel<GG, YF, MU><<<g, kSkWaves * kWave, 0, stream>>>(X, ld_x, (int)M, d_in, qweight, scales, \
+                                                                      qzeros, d_out, n_strips, Y, ld_y, sp)
+#define AWQ_SKINNY_Y(GG, MU) \
+  if (y_f16) AWQ_SKINNY(GG, true, MU); else AWQ_SKINNY(GG, false, MU)
+#define AWQ_SKINNY_G(MU)                  \
+  if (group_size == 128) {                \
+    AWQ_SKINNY_Y(128, MU);                \
+  } else if (group_size == 64) {          \
+    AWQ_SKINNY_Y(64, MU);                 \
+  } else {                                \
+    AWQ_SKINNY_Y(32, MU);                 \
+  }
+    if (M <= kSkTile) {
+      AWQ_SKINNY_G(false)
     } else {
-      if (y_f16) AWQ_SKINNY(32, true); else AWQ_SKINNY(32, false);
+      AWQ_SKINNY_G(true)
     }
+#undef AWQ_SKINNY_G
+#undef AWQ_SKINNY_Y
 #undef AWQ_SKINNY
     if (n_split > 1) {
       const dim3 rgrid((unsigned)((d_out / 4 + kRdCols - 1) / kRdCols), (unsigned)M);

@@ -68,8 +68,8 @@ def _bound(X, qw, sc, qz, d_out, G, n_slices, kind="gemv"):
 
 def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
     """With X rows 16-byte aligned the kernel is the few-token matrix-core path at
-    2 to 16 tokens (d_out a multiple of 16) and the GEMM from 17; else (and at
-    one token) the GEMV."""
+    2 to 64 tokens (d_out a multiple of 16), else the GEMM from 17 tokens; else
+    (and at one token) the GEMV."""
     import torch
     M, d_in = X.shape
     Xp = X if ld_x is None else np.pad(X, ((0, 0), (0, ld_x - d_in)))
@@ -82,8 +82,9 @@ def _check(A, X, qw, sc, qz, d_out, G, out_dtype="f16", ld_x=None, ld_y=None):
     Y = host(plan.run()).astype(F64)
     ref = O.w4a16_matmul(X, qw, sc, qz, d_out, G)
     ldx = d_in if ld_x is None else ld_x
-    few = M <= 16 and (d_out // 8) % 2 == 0          # the few-token path reads word pairs
-    kind = "gemv" if (ldx % 8 or M == 1 or (M <= 16 and not few)) else ("few" if M <= 16 else "gemm")
+    aligned = ldx % 8 == 0
+    few = aligned and 2 <= M <= 64 and (d_out // 8) % 2 == 0   # the few-token path reads word pairs
+    kind = "few" if few else ("gemm" if aligned and M >= 17 else "gemv")
     tol = _bound(X, qw, sc, qz, d_out, G, (d_in + 255) // 256, kind)
     if out_dtype == "f16":
         tol = tol + np.spacing(np.abs(ref).astype(np.float16) * np.float16(1.002)).astype(F64)
@@ -107,7 +108,7 @@ def test_w4a16_decode_full_size(A, name, d_out, d_in, G, zeros):
     _check(A, X, qw, sc, qz, d_out, G)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 31, 33, 48, 64])
 @pytest.mark.parametrize("d_out,d_in,G,out_dtype", [
     (1032, 384, 64, "f16"),    # odd word count: the GEMV below 17 tokens
     (520, 96, 32, "f32"),      # odd word count
@@ -123,15 +124,16 @@ def test_w4a16_tokens_and_ragged_shapes(A, M, d_out, d_in, G, out_dtype):
     _check(A, X, qw, sc, qz, d_out, G, out_dtype)
 
 
-@pytest.mark.parametrize("M", [2, 8, 16])
+@pytest.mark.parametrize("M", [2, 8, 16, 40, 64])
 @pytest.mark.parametrize("name,d_out,d_in,G,zeros,out_dtype", [
     ("qkv_6144x4096", 6144, 4096, 128, True, "f16"),
     ("gate_up_24576x4096", 24576, 4096, 128, False, "f32"),
     ("down_4096x12288_g64", 4096, 12288, 64, True, "f16"),
 ])
 def test_w4a16_few_tokens_full_size(A, M, name, d_out, d_in, G, zeros, out_dtype):
-    """2 to 16 tokens at Qwen3-8B linear sizes: the few-token matrix-core path,
-    its inputs split into ranges whose results the reduction adds."""
+    """2 to 64 tokens at Qwen3-8B linear sizes: the few-token matrix-core path
+    (one or several 16-token tiles), its inputs split into ranges whose
+    results the reduction adds."""
     say(f"w4a16 few tokens {name} M={M}")
     qw, sc, qz = _random_packed(3 * M + d_out + d_in, d_out, d_in, G, zeros)
     X = (np.random.default_rng(5 * M + d_in).standard_normal((M, d_in))).astype(np.float16)
