@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq.so")
 # the VALU issue-rate probe behind the search kernel's ALU peak (bench.py
 # --workload valu_issue_probe): a library of its own, not part of libawq
-PROBE_SRC = os.path.join(PKG, "probe", "valu_issue.hip")
+PROBE_SRCS = [os.path.join(PKG, "probe", "valu_issue.hip"), os.path.join(PKG, "probe", "stream_read.hip")]
 PROBE_LIB = os.path.join(PKG, "libawq_probe.so")
 ARCH = os.environ.get("AWQ_OFFLOAD_ARCH", "gfx950")
 
@@ -69,10 +69,10 @@ def build(jobs: int = 8) -> str:
 
 def build_probe() -> str:
     tmp = PROBE_LIB + ".tmp"
-    r = subprocess.run([HIPCC, *CFLAGS, "-shared", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    r = subprocess.run([HIPCC, *CFLAGS, "-shared", *PROBE_SRCS, "-o", tmp], capture_output=True, text=True)
     if r.returncode != 0:
         errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
-        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{errs}")
+        raise RuntimeError(f"hipcc failed on {PROBE_SRCS}:\n{errs}")
     os.replace(tmp, PROBE_LIB)
     return PROBE_LIB
 
