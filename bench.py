@@ -906,6 +906,44 @@ def cpu_baseline_w4a16(layers_h, M, budget_s: float):
                       f"{wall:.1f} s wall)"}
 
 
+def read_floor_per_call(sizes, K):
+    """Per-call time (ms, HIP events around each eager launch, K rounds) of the
+    read probe over a fresh buffer of each of `sizes` bytes (multiples of 16),
+    launched in order on one stream: the floor of a kernel that reads those
+    bytes once and does nothing else, timed like the W4A16 calls."""
+    import torch
+    from post_weight_quantization_awq_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        B.build_probe()
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.awq_probe_read_blocks.argtypes = [ctypes.c_int64]
+    lib.awq_probe_read_blocks.restype = ctypes.c_int64
+    lib.awq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.awq_probe_read.restype = ctypes.c_int
+    bufs = []
+    for nb in sizes:
+        b = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        b.fill_(0x5A)
+        bufs.append(b)
+    out = torch.zeros(int(max(lib.awq_probe_read_blocks(nb) for nb in sizes)), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    n = len(sizes)
+    ev = HipEvents(2 * n * K)
+    with torch.cuda.stream(s):
+        for nb, b in zip(sizes, bufs):   # warm-up round
+            assert lib.awq_probe_read(b.data_ptr(), nb, out.data_ptr(), s.cuda_stream) == 0
+        for k in range(K):
+            for i, (nb, b) in enumerate(zip(sizes, bufs)):
+                ev.record(2 * (k * n + i), s)
+                assert lib.awq_probe_read(b.data_ptr(), nb, out.data_ptr(), s.cuda_stream) == 0
+                ev.record(2 * (k * n + i) + 1, s)
+    s.synchronize()
+    ms = [sum(ev.ms(2 * (k * n + i), 2 * (k * n + i) + 1) for k in range(K)) / K for i in range(n)]
+    ev.close()
+    del bufs
+    return ms
+
+
 def bench_w4a16(args):
     import numpy as np
     import torch
@@ -1035,6 +1073,15 @@ def bench_w4a16(args):
         "step_TFLOPs": 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (ms * 1e-3) / 1e12,
         "fp16_step_TFLOPs": 2.0 * M * sum(d_out * d_in for *_, d_out, d_in in layers) / (ms16 * 1e-3) / 1e12,
     }
+    if not gemm:   # the same bytes read by a kernel that does nothing else, timed the same way
+        sizes = [(d_out * d_in // 2 + 2 * d_out * (d_in // G) + d_out * (d_in // G) // 2 + 15) // 16 * 16
+                 for *_, d_out, d_in in layers]
+        fl = read_floor_per_call(sizes, K)
+        floor = sum(sizes) / (sum(fl) * 1e-3) / 1e9
+        out["read_floor"] = {"per_call_GBps": floor, "us_per_step": 1e3 * sum(fl),
+                             "frac_of_floor": sum(fl) / sum(call_ms),   # floor time / W4A16 time
+                             "kernel": "stream_read_kernel (probe library): one read of each linear's packed "
+                                       "bytes per launch, HIP events around each call"}
     if not args.no_cpu_baseline:
         hl = []
         for qw, sc, qz, x, y, d_out, d_in in layers[:8]:

@@ -332,7 +332,7 @@ awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, co
                               void* out, int32_t out_dtype, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * awq_w4a16_matmul -- the W4A16 product on the packed layout (decode GEMV).
+ * awq_w4a16_matmul -- the W4A16 product on the packed layout (decode and prefill).
  * [cassindra] Kernels: why W4A16 is fast at decode (packed 4-bit weights
  * dequantized in registers with the group's scale and zero point, multiplied
  * with 16-bit activations; bound by reading the weights at a few tokens);
@@ -348,16 +348,25 @@ awq_status awq_unpack_dequant(const int32_t* qweight, const uint16_t* scales, co
  * 16-byte aligned.  Y: [M, ld_y] of y_dtype (AWQ_F16, rounded to nearest even
  * once, or AWQ_F32), ld_y >= d_out and a multiple of 4, 8-byte (fp16) or
  * 16-byte (fp32) aligned.  d_out % 8 == 0, d_in % group_size == 0.
- * Arithmetic: fewer than 9 tokens (or X rows not 16-byte aligned, ld_x not a
- * multiple of 8, or d_in not a multiple of 32): the decode GEMV -- u * x
- * exact in fp32, fp32 sums over 32 input rows, then the zero point and scale,
- * then fixed-order fp32 sums, tokens 4 at a time (the weights are read once
- * per 4 tokens).  9 tokens or more: the matrix-core GEMM -- exact fp16
- * (u - z) times X accumulated in fp32 per quantization group, times the fp32
- * scale, groups added in order; when the output tiles (256 tokens x 128
- * outputs, or 128 x 128 for at most 128 tokens) are fewer than the compute
- * units, K is cut at multiples of 128 inputs into up to 8 ranges whose fp32
- * results are added in range order.  Both are deterministic.
+ * Arithmetic, by token count M (X rows 16-byte aligned and ld_x a multiple
+ * of 8 unless said otherwise):
+ *   M = 1, or X rows not so aligned: the decode GEMV -- u * x exact in fp32,
+ *     fp32 sums over 32 input rows, then the zero point and scale, then
+ *     fixed-order fp32 sums over 256-row slices; tokens 4 at a time (the
+ *     weights are read once per 4 tokens).
+ *   2 <= M <= 64, d_out a multiple of 16 and qweight 8-byte aligned: the
+ *     few-token matrix-core kernel -- every packed word read once for all
+ *     tokens, exact fp16 (u - z) times X accumulated in fp32 per
+ *     quantization group, times the fp32 scale, groups and the 4 waves of a
+ *     512-row range added in order, the ranges' fp32 results added in range
+ *     order.
+ *   M >= 17 otherwise: the matrix-core GEMM -- exact fp16 (u - z) times X
+ *     accumulated in fp32 per group, times the fp32 scale, groups added in
+ *     order; when the output tiles (256 tokens x 128 outputs, or 128 x 128
+ *     for at most 128 tokens) are fewer than the compute units, K is cut at
+ *     multiples of 128 inputs into up to 8 ranges whose fp32 results are
+ *     added in range order.
+ *   All are deterministic.
  * ws: awq_w4a16_workspace(M, d_out, d_in) bytes, 256-byte aligned.  M = 0 or
  * d_out = 0 returns AWQ_OK at once.
  * ------------------------------------------------------------------------- */
