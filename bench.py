@@ -1094,7 +1094,8 @@ def bench_w4a16(args):
 PROBE_KINDS = ["v_fma_f32", "v_mul_f32", "v_add_f32", "v_max3_f32", "v_rndne_f32", "v_fmac_f32",
                "v_cvt_f32_f16", "v_max_u32 (DPP row_half_mirror)", "v_fma_f32 + v_rndne_f32",
                "v_fma_f32 + v_mul_f32", "v_fma_f32 + v_max3_f32",
-               "search element mix (mul, mul, max3, fma, fma, add, add, fma x4)"]
+               "search element mix (mul, mul, max3, fma, fma, add, add, fma x4)",
+               "v_fma_mix_f32 (fp16 a widened in the multiply)"]
 
 
 def bench_valu_probe(args):

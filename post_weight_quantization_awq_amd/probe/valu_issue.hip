@@ -29,7 +29,8 @@ enum Kind : int {
   kFmaRndne = 8,  // alternating v_fma_f32 / v_rndne_f32
   kFmaMul = 9,    // alternating v_fma_f32 / v_mul_f32
   kFmaMax3 = 10,  // alternating v_fma_f32 / v_max3_f32
-  kSearchMix = 11 // the weight-score element loop's mix: mul, max3 (half), fma, add, fma, fma
+  kSearchMix = 11, // the weight-score element loop's mix: mul, max3 (half), fma, add, fma, fma
+  kFmaMix = 12     // v_fma_mix_f32 d, a.f16, b, d (an fp16 operand widened in the multiply)
 };
 
 #define OP8(INS)                                                                         \
@@ -101,6 +102,10 @@ __global__ __launch_bounds__(256) void valu_issue_kernel(float* __restrict__ out
         asm volatile("v_max3_f32 %0, %1, %2, %0" : "+v"(x5) : "v"(a), "v"(b));
         asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x6) : "v"(a), "v"(b));
         asm volatile("v_max3_f32 %0, %1, %2, %0" : "+v"(x7) : "v"(a), "v"(b));
+      } else if constexpr (K == kFmaMix) {
+#define I(x) asm volatile("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,0,0]" : "+v"(x) : "v"(a), "v"(b));
+        OP8(I)
+#undef I
       } else {  // kSearchMix: per pair of elements mul, mul, max3, fma, fma, add, add, fma, fma, fma, fma (11 for 2)
         asm volatile("v_mul_f32 %0, %1, %0" : "+v"(x0) : "v"(a));
         asm volatile("v_mul_f32 %0, %1, %0" : "+v"(x1) : "v"(a));
@@ -181,7 +186,7 @@ int awq_probe_mfma(int blocks, int iters, const void* A, const void* B, float* o
 }
 
 // Number of kinds, and VALU instructions per lane and loop trip of a kind.
-int awq_probe_valu_kinds(void) { return kSearchMix + 1; }
+int awq_probe_valu_kinds(void) { return kFmaMix + 1; }
 int awq_probe_valu_insts_per_trip(int kind) { return insts_per_trip(kind); }
 
 // Launches `blocks` blocks of 256 threads running `iters` loop trips of `kind`
@@ -202,6 +207,7 @@ int awq_probe_valu(int kind, int blocks, int iters, float* out, void* stream) {
     case kFmaMul: return launch<kFmaMul>(blocks, iters, out, s);
     case kFmaMax3: return launch<kFmaMax3>(blocks, iters, out, s);
     case kSearchMix: return launch<kSearchMix>(blocks, iters, out, s);
+    case kFmaMix: return launch<kFmaMix>(blocks, iters, out, s);
     default: return 1;
   }
 }
