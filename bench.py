@@ -610,8 +610,10 @@ def bench_sweep(args):
         main = torch.cuda.current_stream()
         n_side = 3 if args.schedule == "pipeline" else args.streams
         streams = [torch.cuda.Stream() for _ in range(n_side)]
-        sync = HipEvents(blocks * ng + n_side + 1, timing=False)   # per-group readiness, fork, joins
+        # per-group readiness, fork, joins, per-block search completion
+        sync = HipEvents(blocks * ng + n_side + 1 + blocks, timing=False)
         E_FORK = blocks * ng
+        E_DONE = blocks * ng + n_side + 1
 
         def plans(stats_stream, work_stream, lane_of):
             st = [[A.ActStatsPlan(Xs[b][gi], x_mean=xmb[b][gi], ws=ws_stats[lane_of(b)][gi], stream=stats_stream(b, gi))
@@ -662,17 +664,31 @@ def bench_sweep(args):
                 sync.wait(main, E_FORK + 1 + j)
 
         def step_pipeline():
+            # The statistics of block b + D start once the searches of block
+            # b - 1 are done, so they stream from HBM while the searches of
+            # blocks b and b + 1 compute, instead of all running first.
             st_plans, se_plans, pk_plans = par
-            for b in range(blocks):
+            D = max(1, args.lookahead)
+
+            def stats(b):
                 for gi in range(ng):
                     st_plans[b][gi].launch()
                     sync.record(b * ng + gi, streams[0])
+
+            for b in range(min(D, blocks)):
+                stats(b)
             for b in range(blocks):
+                if b + D < blocks:
+                    if b >= 1:
+                        sync.wait(streams[0], E_DONE + b - 1)
+                    stats(b + D)
+                ws_ = streams[1 + b % 2]
                 for gi in range(ng):
-                    sync.wait(streams[1 + b % 2], b * ng + gi)
+                    sync.wait(ws_, b * ng + gi)
                     se_plans[b][gi].launch()
                     for pp in pk_plans[b][gi]:
                         pp.launch()
+                sync.record(E_DONE + b, ws_)
 
         def step_streams():
             fork()
@@ -728,7 +744,7 @@ def bench_sweep(args):
         "config": {"workload": wl_key, "blocks": blocks, "weights": n_w, "n_grid": 20,
                    "group_size": G0, "group_sizes": list(wl.group_sizes), "score": "weight",
                    "calibration_tokens_per_group": wl.groups[0].T, "x_per_block": True,
-                   "x_dtype": "bf16", "schedule": args.schedule,
+                   "x_dtype": "bf16", "schedule": args.schedule, "lookahead": args.lookahead,
                    "streams": 3 if args.schedule == "pipeline" else args.streams, "duo": args.duo, "asym": args.asym},
         "per_group_size": out_all,
         "pack_GBps": first["pack_GBps"], "pack_hbm_frac": first["pack_hbm_frac"],
@@ -1344,6 +1360,8 @@ def main() -> int:
     ap.add_argument("--blocks", type=int, default=36, help="blocks of the sweep workload")
     ap.add_argument("--streams", type=int, default=8,
                     help="streams of the sweep's timed steps (--schedule blocks or groups)")
+    ap.add_argument("--lookahead", type=int, default=2,
+                    help="pipeline schedule: blocks whose statistics may run ahead of the searches")
     ap.add_argument("--schedule", default="pipeline", choices=["pipeline", "blocks", "groups"],
                     help="sweep schedule: the statistics on a stream of their own running ahead of the searches "
                          "on two streams (pipeline), blocks round-robin over the streams (blocks), or one "
