@@ -42,9 +42,13 @@ METRIC = "scale-search weight-elems×grid-pts/s + pack GB/s; % of HBM roofline, 
 HBM_PEAK_GBPS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 # fp32 vector: 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 32 lane-ops per clock x 2 flops
-# (FMA) x 2.4 GHz, i.e. 78.6 T lane-operations/s; a SIMD issues up to two
-# wave64 VALU instructions per 4 clocks when they come from different classes
+# (FMA) x 2.4 GHz, i.e. 78.6 T lane-operations/s: one wave64 instruction of the
+# full-rate class (fma, mul, add) per 2 clocks per SIMD, no dual issue
 VALU_LANE_OPS_PEAK_T = 256 * 4 * 32 * 2.4e9 / 1e12   # 78.64 T fp32 lane-ops/s
+# The same class as measured on the machine by the issue-rate probe
+# (`--workload valu_issue_probe`: v_fma / v_mul / v_add at 8 waves per SIMD,
+# one wave64 instruction per 2 clocks at the ~2.1 GHz the chip holds under it)
+VALU_LANE_OPS_MEASURED_T = 68.4
 # fp32 lane operations that one element x candidate needs in the weight score:
 # scale (mul), group max (max), v / step (mul by reciprocal), round (rndne),
 # residual v - q*step (fma), square-accumulate (fma)
@@ -450,7 +454,8 @@ def bench_weight(args, wl_name: str):
         "unpack_us": unpack_ms[0] * 1e3, "unpack_GBps": unpack_bytes / (unpack_ms[0] * 1e-3) / 1e9,
         "unpack_scaled_domain_us": unpack_ms[1] * 1e3,
         "roofline": {"bound": "alu", "achieved": achieved_ops, "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s",
-                     "frac": achieved_ops / VALU_LANE_OPS_PEAK_T,
+                     "frac": achieved_ops / VALU_LANE_OPS_PEAK_T, "measured_peak": VALU_LANE_OPS_MEASURED_T,
+                     "frac_of_measured_peak": achieved_ops / VALU_LANE_OPS_MEASURED_T,
                      "traffic": pmc_traffic("search_weight_kernel", wl_name, args),
                      "kernel": "search_weight_kernel",
                      "ops_per_elem_pt": ops},
@@ -751,6 +756,8 @@ def bench_sweep(args):
         "act_stats_GBps": first["act_stats_GBps"], "act_stats_hbm_frac": first["act_stats_hbm_frac"],
         "roofline": {"bound": "alu", "achieved": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T,
                      "peak": VALU_LANE_OPS_PEAK_T, "unit": "TOP/s", "frac": first["search_alu_frac"],
+                     "measured_peak": VALU_LANE_OPS_MEASURED_T,
+                     "frac_of_measured_peak": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T / VALU_LANE_OPS_MEASURED_T,
                      "traffic": pmc_traffic("search_weight_kernel", wl_key, args),
                      "kernel": "search_weight_kernel", "ops_per_elem_pt": ops,
                      "per": "achieved over all 144 launches of one step at G = %d; traffic per launch, "
@@ -898,7 +905,9 @@ def bench_export(args):
         "fold_us_per_call": sums["fold"] / counts["fold"] * 1e3,
         "pack_GBps": pk / (per_step["pack"] * 1e-3) / 1e9,
         "roofline": {"bound": "alu", "achieved": frac * VALU_LANE_OPS_PEAK_T, "peak": VALU_LANE_OPS_PEAK_T,
-                     "unit": "TOP/s", "frac": frac, "traffic": None, "kernel": "search_weight_kernel"},
+                     "unit": "TOP/s", "frac": frac, "measured_peak": VALU_LANE_OPS_MEASURED_T,
+                     "frac_of_measured_peak": frac * VALU_LANE_OPS_PEAK_T / VALU_LANE_OPS_MEASURED_T,
+                     "traffic": None, "kernel": "search_weight_kernel"},
     }
 
 
