@@ -42,6 +42,10 @@ def A():
     (1, 64, "bf16", 0),
     (16400, 4096, "bf16", 0),   # 128-row splits (>= 1024 blocks) + a 16-row tail
     (32831, 2048, "f16", 0),    # 128-row splits on 4 column strips, a 63-row tail
+    # the persistent lean kernel (128-row splits): blocks loop over several
+    # splits, the last column block ragged (lanes past d_in), rows strided
+    (65613, 1000, "bf16", 0),   # 512 splits on 2 column blocks (128 per block row), a 77-row tail
+    (20480, 3080, "f16", 8),    # 160 splits on 7 column blocks, ld = 3088
 ])
 def test_act_stats(A, T, d_in, dtype, pad):
     import torch
