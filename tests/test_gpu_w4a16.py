@@ -116,6 +116,7 @@ def test_w4a16_decode_full_size(A, name, d_out, d_in, G, zeros):
     (560, 672, 32, "f32"),     # 2 ranges, the second 160 rows (one wave of 4 steps, one of 1)
     (2064, 1088, 64, "f16"),   # 3 ranges, the last 64 rows
     (16, 256, 128, "f32"),     # one strip of 2 words
+    (32, 32, 32, "f32"),       # one 32-row step (three past d_in in each wave's chunk), 4 words
 ])
 def test_w4a16_tokens_and_ragged_shapes(A, M, d_out, d_in, G, out_dtype):
     say(f"w4a16 M={M} d_out={d_out} d_in={d_in} G={G} {out_dtype}")
