@@ -78,9 +78,9 @@ PMC_TRAFFIC = {
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
         "sha256": "defe0c2e9940a8e54a9e9e972d928a3348712ea21d6d59d02dfc4e145d6bede3"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11797680.2, "write_kib": 30720.0,
+        "fetch_kib": 12140610.5, "write_kib": 20640.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "694cb7a3b501509768c9ce468c13db421cf19ad44e50f1b2f92caf9c141469fb"},
+        "sha256": "46b1011635aceb00849ba2e9da3dd555eb2886d2ac4b800e656ba1e2fa5706c4"},
 }
 
 

@@ -95,7 +95,7 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     off += align256((size_t)p.n_blocks * cfg.n_grid * sizeof(float));
   } else {
     gemm_sq_pad(T, d_out, d_in, &p.T_pad, &p.d_out_pad, &p.K_pad);
-    p.n_mt = p.T_pad / 256;
+    p.n_mt = p.T_pad / gemm_sq_tile_rows();
     p.n_x = absmax_blocks(T);
     p.n_db = build_dw_blocks(cfg.group_size, d_out, d_in);
     const int max_c = cfg.n_grid > cfg.n_clip ? cfg.n_grid : cfg.n_clip;

@@ -47,7 +47,8 @@ hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 // scales: xs from the X partial maxima, ds[c] and inv[c] from the dW partial maxima dmax [n_cand, n_d]
 hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
                              OutScales* sc, hipStream_t stream);
-// padded GEMM shapes: T_pad, d_out_pad multiples of 256, K_pad of 64
+// padded GEMM shapes: T_pad a multiple of the token tile, d_out_pad of 256, K_pad of 64
+int64_t gemm_sq_tile_rows();
 void gemm_sq_pad(int64_t T, int64_t d_out, int64_t d_in, int64_t* T_pad, int64_t* d_out_pad, int64_t* K_pad);
 // X16 [T_pad, K_pad] = fp16(X * xs), zero padded
 hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,
@@ -61,7 +62,7 @@ hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64
                            int n_clip, float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
                            hipStream_t stream);
 // gemm of squares on fp16 operands: Y = X16 [T_pad, K_pad] dw^T (dw: [n_cols, K_pad]);
-// colpart[mt * ldc + n] = sum over the 256 tokens of tile mt of Y[t, n]^2
+// colpart[mt * ldc + n] = sum over the 384 tokens of tile mt of Y[t, n]^2
 hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                           float* colpart, int64_t ldc, hipStream_t stream);
 // chunk_sum[c, ch] = sum_mt sum_{o in chunk ch, o < d_out} colpart[mt * ldc + c * d_out_pad + o]

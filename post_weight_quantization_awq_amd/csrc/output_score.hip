@@ -302,32 +302,32 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 // 2. GEMM of squares: Y = X16 dW^T over the concatenated candidates
 //    (N_total = n_cand * d_out_pad columns, each candidate padded to a multiple
 //    of the tile with zero rows; M and K padded likewise with zeros), and per
-//    column the sum over the block's 256 tokens of Y^2 -> colpart[mt][n].
+//    column the sum over the block's 384 tokens of Y^2 -> colpart[mt][n].
 //
-//    Block tile 256 x 256, 8 waves (2 x 4), wave tile 128 x 64 = 4 x 2 MFMA
-//    32x32x16 f16 tiles; 128 fp32 accumulators per lane, 168 registers in
-//    all, so two waves share a SIMD and one issues MFMAs while the other
-//    waits (measured 4-5% faster than 4 waves of 128 x 128 tiles with one
-//    wave per SIMD, 1.5% faster than 16 waves of 64 x 64).  A wave reads 6
-//    fragments (6 KiB of LDS) per 8 MFMAs.  K advances in stages of 32 through a ring of 4 LDS slots, one
-//    distinct array per slot and operand: the operands go from global memory
-//    straight into LDS (buffer loads with the LDS bit, 16 bytes per lane, no
-//    staging registers and no LDS store instructions), three stages ahead of
-//    the MFMAs.  At the end of a stage each wave waits until its loads of the
-//    next stage have landed (two younger stages stay in flight) and the
-//    block meets at a barrier without a memory fence, which would wait for
-//    every load.  The separate slot arrays let the compiler see that fragment
-//    reads never alias the loads in flight.  16-byte K-chunks are
-//    XOR-swizzled by row so that fragment reads are free of bank conflicts;
-//    since a direct load places lane i at byte 16 i of its 1 KiB, the swizzle
-//    is applied on the global side (each lane fetches the chunk its LDS slot
-//    holds).  Measured: 6-7% faster than staging the operands through
-//    registers with LDS stores, identical results.
+//    Block tile 384 x 256, 8 waves (4 x 2), wave tile 96 x 128 = 3 x 4 MFMA
+//    32x32x16 f16 tiles: 192 fp32 accumulators per lane, 240 registers in
+//    all, so two waves still share a SIMD and one issues MFMAs while the
+//    other waits.  Per 16-deep K step a wave reads 7 fragments (7 KiB of LDS)
+//    for 12 MFMAs, and the block writes 20 KiB of operands per 96 MFMAs; LDS
+//    bandwidth co-limits the matrix cores, so the larger wave tile is what
+//    pays (4% over 8 waves of 128 x 64 at K = 4096).  K advances in stages
+//    of 32 through a ring of 3 LDS slots of 40 KiB, one distinct array per
+//    slot and operand: the operands go from global memory straight into LDS
+//    (buffer loads with the LDS bit, 16 bytes per lane, no staging registers
+//    and no LDS store instructions), two stages ahead of the MFMAs.  At the
+//    end of a stage each wave waits until its loads of the next stage have
+//    landed (the younger stage stays in flight) and the block meets at a
+//    barrier without a memory fence, which would wait for every load.  The
+//    separate slot arrays let the compiler see that fragment reads never
+//    alias the loads in flight.  16-byte K-chunks are XOR-swizzled by row so
+//    that fragment reads are free of bank conflicts; since a direct load
+//    places lane i at byte 16 i of its 1 KiB, the swizzle is applied on the
+//    global side (each lane fetches the chunk its LDS slot holds).
 //    The block order is remapped so that each XCD owns a contiguous range of
 //    tiles, walked in groups of up to 8 M-tiles: concurrent blocks of one XCD
 //    share A and B tiles in its L2.
 // ---------------------------------------------------------------------------
-constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kBM = 384, kBN = 256, kBK = 32;
 constexpr int kGemmThreads = 512;
 constexpr int kXcds = 8;
 
@@ -349,46 +349,45 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
 __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
 __shared__ __attribute__((aligned(1024))) uint16_t sA2[kBM * kBK];
-__shared__ __attribute__((aligned(1024))) uint16_t sA3[kBM * kBK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB0[kBN * kBK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB1[kBN * kBK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB2[kBN * kBK];
-__shared__ __attribute__((aligned(1024))) uint16_t sB3[kBN * kBK];
 
-// one operand tile (256 rows x 32 K) straight into LDS: wave w fetches rows
-// 32w .. 32w+31 in 2 loads of 16 rows; lane i lands in row 32w + 16n + i/4,
-// slot i%4, and fetches chunk (i%4) ^ swz(row) = (i%4) ^ ((i/16) & 3)
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* dst, int wave, uint32_t vo,
+// NL loads of 16 rows x 32 K straight into LDS rows row0 .. row0 + 16 NL - 1;
+// lane i lands in row row0 + 16 n + i/4, slot i%4, and fetches chunk
+// (i%4) ^ swz(row) = (i%4) ^ ((i/16) & 3) (row0 is a multiple of 16)
+template <int NL>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, uint16_t* dst, int row0, uint32_t vo,
                                          uint32_t soff, uint32_t row16_bytes) {
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (32 * wave + 16 * n) * kBK), 16, vo,
+  for (int n = 0; n < NL; ++n)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (row0 + 16 * n) * kBK), 16, vo,
                                              soff + (uint32_t)n * row16_bytes, 0, 0);
 }
 
 __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane,
-                                           f32x16 (&acc)[4][2]) {
+                                           f32x16 (&acc)[3][4]) {
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
     const int kc = 2 * ks + (lane >> 5);
-    uint4 a[4], b[2];
+    uint4 a[3], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = frag(As, wm * 128 + i * 32 + (lane & 31), kc);
+    for (int i = 0; i < 3; ++i) a[i] = frag(As, wm * 96 + i * 32 + (lane & 31), kc);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = frag(Bs, wn * 64 + j * 32 + (lane & 31), kc);
+    for (int j = 0; j < 4; ++j) b[j] = frag(Bs, wn * 128 + j * 32 + (lane & 31), kc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
   }
 }
 
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                               uint32_t a_bytes, const uint16_t* __restrict__ B,
                                                               int64_t ldb, uint32_t b_bytes, int64_t K, int64_t n_mt,
                                                               int64_t n_nt, float* __restrict__ colpart, int64_t ldc,
                                                               int group_m) {
-  __shared__ float red[2][kBN];
+  __shared__ float red[4][kBN];
   const int64_t nblk = (int64_t)gridDim.x;
   const int64_t bid = blockIdx.x;
   const int64_t xcd = bid % kXcds, pos = bid / kXcds;
@@ -403,83 +402,80 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_sq_kernel(const uint16_t
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 96 x 128
 
-  f32x16 acc[4][2];
+  f32x16 acc[3][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nk = (int)(K / kBK);  // even (K is a multiple of 64)
+  const int nk = (int)(K / kBK);
   const uint32_t ld2 = (uint32_t)(lda * 2);
   const uint32_t vo = (uint32_t)((lane >> 2) * ld2 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
   const uint32_t row16 = 16 * ld2;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, a_bytes);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, b_bytes);
-  const uint32_t sA = (uint32_t)((m0 + 32 * wave) * lda * 2), sB = (uint32_t)((n0 + 32 * wave) * ldb * 2);
-  // k-tile t (clamped: past the end the ring re-fetches the last tile into a free buffer)
+  // wave w fetches A rows 48 w .. 48 w + 47 (3 loads) and B rows 32 w .. 32 w + 31 (2 loads)
+  const uint32_t sA = (uint32_t)((m0 + 48 * wave) * lda * 2), sB = (uint32_t)((n0 + 32 * wave) * ldb * 2);
+  // k-tile t (clamped: past the end the ring re-fetches the last tile into a free slot)
   auto koff = [&](int t) { return (uint32_t)((t < nk ? t : nk - 1) * kBK * 2); };
 
-  // prologue: stages 0, 1, 2 in flight; wait for stage 0
-  dma_tile(rsA, sA0, wave, vo, sA + koff(0), row16);
-  dma_tile(rsB, sB0, wave, vo, sB + koff(0), row16);
-  dma_tile(rsA, sA1, wave, vo, sA + koff(1), row16);
-  dma_tile(rsB, sB1, wave, vo, sB + koff(1), row16);
-  dma_tile(rsA, sA2, wave, vo, sA + koff(2), row16);
-  dma_tile(rsB, sB2, wave, vo, sB + koff(2), row16);
-  __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): this wave's stage-0 loads are in LDS
+  // prologue: stages 0 and 1 in flight; wait for stage 0 (5 loads per stage and wave)
+  dma_rows<3>(rsA, sA0, 48 * wave, vo, sA + koff(0), row16);
+  dma_rows<2>(rsB, sB0, 32 * wave, vo, sB + koff(0), row16);
+  dma_rows<3>(rsA, sA1, 48 * wave, vo, sA + koff(1), row16);
+  dma_rows<2>(rsB, sB1, 32 * wave, vo, sB + koff(1), row16);
+  __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0): this wave's stage-0 loads are in LDS
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // stage kt on ring slot S: fetch stage kt + 3 into slot S + 3 (freed by the
+  // stage kt on ring slot S: fetch stage kt + 2 into slot SN (freed by the
   // previous barrier), MFMAs on slot S, then wait until stage kt + 1 is in
-  // LDS (stages kt + 2 and kt + 3 may still be in flight) and all reads of
-  // slot S are done, barrier
-#define AWQ_STAGE4(S, SN)                                                       \
+  // LDS (stage kt + 2 may still be in flight) and all reads of slot S are
+  // done, barrier
+#define AWQ_STAGE3(S, SN)                                                       \
   {                                                                             \
-    dma_tile(rsA, sA##SN, wave, vo, sA + koff(kt + 3), row16);                  \
-    dma_tile(rsB, sB##SN, wave, vo, sB + koff(kt + 3), row16);                  \
+    dma_rows<3>(rsA, sA##SN, 48 * wave, vo, sA + koff(kt + 2), row16);          \
+    dma_rows<2>(rsB, sB##SN, 32 * wave, vo, sB + koff(kt + 2), row16);          \
     mfma_stage(sA##S, sB##S, wm, wn, lane, acc);                                \
-    __builtin_amdgcn_s_waitcnt(0x0078);                                         \
+    __builtin_amdgcn_s_waitcnt(0x0075);                                         \
     asm volatile("" ::: "memory");                                              \
     __builtin_amdgcn_s_barrier();                                               \
     asm volatile("" ::: "memory");                                              \
     ++kt;                                                                       \
   }
   int kt = 0;
-  for (; kt + 4 <= nk;) {
-    AWQ_STAGE4(0, 3)
-    AWQ_STAGE4(1, 0)
-    AWQ_STAGE4(2, 1)
-    AWQ_STAGE4(3, 2)
+  for (; kt + 3 <= nk;) {
+    AWQ_STAGE3(0, 2)
+    AWQ_STAGE3(1, 0)
+    AWQ_STAGE3(2, 1)
   }
-  if (kt < nk) {  // nk % 4 == 2
-    AWQ_STAGE4(0, 3)
-    AWQ_STAGE4(1, 0)
-  }
-#undef AWQ_STAGE4
+  if (kt < nk) AWQ_STAGE3(0, 2)
+  if (kt < nk) AWQ_STAGE3(1, 0)
+#undef AWQ_STAGE3
   __builtin_amdgcn_s_waitcnt(0x0070);  // no load in flight past this point
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 4; ++j) {
     float cs = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
     cs += __shfl_xor(cs, 32, kWave);
-    if (lane < 32) red[wm][wn * 64 + j * 32 + lane] = cs;
+    if (lane < 32) red[wm][wn * 128 + j * 32 + lane] = cs;
   }
   __syncthreads();
-  if (tid < kBN) colpart[mt * ldc + n0 + tid] = red[0][tid] + red[1][tid];
+  if (tid < kBN) colpart[mt * ldc + n0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
-// K is padded to a multiple of 64 = two ring stages: the stage count is even,
-// so the 4-slot ring ends with zero or one pair of stages after its loop
+int64_t gemm_sq_tile_rows() { return kBM; }
+
+// M padded to the block's 384 rows, N to 256, K to a multiple of 64
 void gemm_sq_pad(int64_t T, int64_t d_out, int64_t d_in, int64_t* T_pad, int64_t* d_out_pad, int64_t* K_pad) {
   *T_pad = (T + kBM - 1) / kBM * kBM;
   *d_out_pad = (d_out + kBN - 1) / kBN * kBN;
@@ -487,12 +483,13 @@ void gemm_sq_pad(int64_t T, int64_t d_out, int64_t d_in, int64_t* T_pad, int64_t
 }
 
 // M-tiles per tile group: each XCD walks its tiles in groups of group_m
-// M-tiles, so the 8 XCDs keep 8 * group_m A panels (256 rows x K each) in
-// use.  The largest group (up to 8) whose panels fit in ~224 MiB of the
-// 256 MB MALL is taken, so that A re-reads across rounds of tiles stay there:
-// 8 at K = 4096, 4 at K = 12288 (measured 6% faster there than 8).
+// M-tiles, so the 8 XCDs keep 8 * group_m A panels (384 rows x K each) in
+// use.  The largest group (up to 8) whose panels stay within 320 MiB is
+// taken: 8 at K = 4096 (2% faster than 4), 4 at K = 12288 (5% faster than 2,
+// 18% than 1), where A re-reads across rounds of tiles mostly hit the 256 MB
+// MALL.
 static int gemm_group_m(int64_t K_pad) {
-  const double budget = 224.0 * 1024 * 1024;
+  const double budget = 320.0 * 1024 * 1024;
   int g = 8;
   while (g > 1 && 8.0 * g * kBM * (double)K_pad * 2.0 > budget) g /= 2;
   return g;
