@@ -80,14 +80,19 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
   const int64_t k0 = (int64_t)blockIdx.y * kGvSlice;
   const int64_t r0 = k0 + (int64_t)wv * kGvRows;
 
-  // activations of the slice first (issued before the codes)
+  // activations of the slice first, issued before the codes and
+  // unconditionally (the compiler waits for a load under a branch inside the
+  // branch, before the codes are requested); out-of-range entries read X[0]
+  // and are masked when staged
   uint16_t xr[kXPer];
+  bool xok[kXPer];
 #pragma unroll
   for (int q = 0; q < kXPer; ++q) {
     const int idx = q * kGvThreads + tid;
     const int t = idx / kGvSlice, c = idx % kGvSlice;
     const int64_t row = k0 + c;
-    xr[q] = (idx < MT * kGvSlice && t < m_valid && row < d_in) ? X[t * ld_x + row] : (uint16_t)0;
+    xok[q] = idx < MT * kGvSlice && t < m_valid && row < d_in;
+    xr[q] = X[xok[q] ? t * ld_x + row : 0];
   }
   // codes: this lane's word in the wave's 32 rows (a partial last slice
   // re-reads row d_in - 1; its activations are zero)
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
 #pragma unroll
   for (int q = 0; q < kXPer; ++q) {
     const int idx = q * kGvThreads + tid;
-    if (idx < MT * kGvSlice) xs[idx / kGvSlice][idx % kGvSlice] = h2f(xr[q]);
+    if (idx < MT * kGvSlice) xs[idx / kGvSlice][idx % kGvSlice] = xok[q] ? h2f(xr[q]) : 0.0f;
   }
   __syncthreads();
 
