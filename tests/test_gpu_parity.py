@@ -254,6 +254,9 @@ def test_unpack_partial_tiles(A, d_in, G, d_out, out_f16, with_s):
     ([40], 96, 70, 32, "bf16"),            # K padded to the 64-wide GEMM step
     ([300, 220], 512, 600, 128, "bf16"),   # several token and row tiles, ragged edges
     ([40, 0, 24, 8, 16, 33, 7, 16], 256, 90, 64, "bf16"),  # eight parts, one empty
+    ([300], 256, 384, 128, "bf16"),        # exactly one 384-token tile
+    ([64, 200], 128, 385, 64, "f16"),      # one token past it: a second tile of one row
+    ([260], 192, 769, 64, "bf16"),         # three token tiles, one row in the last
 ])
 def test_search_output(A, parts, d_in, T, G, xdt):
     say(f"search output parts={parts} d_in={d_in} T={T} G={G} {xdt}")
@@ -268,7 +271,7 @@ def test_search_output(A, parts, d_in, T, G, xdt):
 
 
 @pytest.mark.parametrize("parts,d_in,T,G", [([64], 256, 150, 128), ([136], 384, 70, 64),
-                                            ([24, 0, 40], 256, 60, 128)])
+                                            ([24, 0, 40], 256, 60, 128), ([272], 128, 385, 64)])
 def test_clip_search(A, parts, d_in, T, G):
     d_out = sum(parts)
     say(f"clip search parts={parts} d_in={d_in} T={T} G={G}")
