@@ -558,6 +558,19 @@ def bench_output(args, wl_name: str):
     }
 
 
+def _sweep_outputs(xmb, res_lane, packs_lane):
+    """Copies of a step's outputs: x_mean of every block and group, and the
+    search results and packed tensors held by one lane (its last block)."""
+    return ([x.clone() for row in xmb for x in row],
+            [t.clone() for r in res_lane for t in (r.err, r.best_idx, r.best_s)],
+            [t.clone() for grp in packs_lane for o in grp for t in o])
+
+
+def _same_outputs(a, b) -> bool:
+    import torch
+    return all(len(x) == len(y) and all(torch.equal(u, v) for u, v in zip(x, y)) for x, y in zip(a, b))
+
+
 def bench_sweep(args):
     """The full Qwen3-8B-shaped sweep: 36 blocks x 4 input-sharing groups (QKV
     6144 x 4096, o 4096 x 4096, gate/up 24576 x 4096, down 4096 x 12288), each
@@ -711,9 +724,16 @@ def bench_sweep(args):
             step_streams()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t1) * 1e3 / K
+        # the multi-stream step must give exactly the one-stream results: every
+        # block's statistics and the last block's search results and packed tensors
+        last = blocks - 1
+        lane_last = {"pipeline": last % 2, "blocks": last % n_side}.get(args.schedule, 0)
+        snap = _sweep_outputs(xmb, res[lane_last], packs[lane_last])
         for k in range(K):  # kernel durations: same steps again, one stream, events around each kernel
             step(ser, k)
         torch.cuda.synchronize()
+        if not _same_outputs(snap, _sweep_outputs(xmb, res[0], packs[0])):
+            raise RuntimeError("the multi-stream sweep step differs from the one-stream step")
         sums = [0.0, 0.0, 0.0]
         for n in range(0, per * K, 6):
             sums[0] += ev.ms(n, n + 1)
@@ -752,6 +772,7 @@ def bench_sweep(args):
                    "x_dtype": "bf16", "schedule": args.schedule, "lookahead": args.lookahead,
                    "streams": 3 if args.schedule == "pipeline" else args.streams, "duo": args.duo, "asym": args.asym},
         "per_group_size": out_all,
+        "streams_match_one_stream": True,
         "pack_GBps": first["pack_GBps"], "pack_hbm_frac": first["pack_hbm_frac"],
         "act_stats_GBps": first["act_stats_GBps"], "act_stats_hbm_frac": first["act_stats_hbm_frac"],
         "roofline": {"bound": "alu", "achieved": first["search_alu_frac"] * VALU_LANE_OPS_PEAK_T,
@@ -879,10 +900,17 @@ def bench_export(args):
         step_streams()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t1) * 1e3 / K
+
+    def outputs():  # the last block's export: packed tensors, folded norms, shared and searched scales
+        return ([t.clone() for o in packs.values() for t in o], [t.clone() for t in n_out.values()],
+                [t.clone() for t in s_sh.values()] + [t.clone() for r in res.values() for t in (r.err, r.best_s)])
+    snap = outputs()
     tagged = []
     for k in range(K):  # kernel durations: the same steps on one stream, events around each call's main kernel
         tagged += step(ser, k)
     torch.cuda.synchronize()
+    if not _same_outputs(snap, outputs()):
+        raise RuntimeError("the multi-stream export step differs from the one-stream step")
     sums, counts = {}, {}
     for kind, n in tagged:
         sums[kind] = sums.get(kind, 0.0) + ev.ms(n, n + 1)
@@ -901,6 +929,7 @@ def bench_export(args):
                    "exported_weights": n_all, "n_grid": 20, "group_size": G, "score": "weight",
                    "streams": args.streams},
         "weights_exported_per_s": n_all / (ms_step * 1e-3),
+        "streams_match_one_stream": True,
         "kernel_ms_per_step": per_step,
         "fold_us_per_call": sums["fold"] / counts["fold"] * 1e3,
         "pack_GBps": pk / (per_step["pack"] * 1e-3) / 1e9,
