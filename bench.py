@@ -80,7 +80,7 @@ PMC_TRAFFIC = {
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
         "fetch_kib": 12140610.5, "write_kib": 20640.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "46b1011635aceb00849ba2e9da3dd555eb2886d2ac4b800e656ba1e2fa5706c4"},
+        "sha256": "9ccdd3e1c3eec37d7ea3f2b49e30a9569904755b641e5721fc5bcee14ca3b045"},
 }
 
 

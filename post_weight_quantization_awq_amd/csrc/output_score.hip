@@ -230,10 +230,10 @@ __device__ float block_max256(const float* __restrict__ a, int64_t n, float* red
   return r;
 }
 
-// xmax: [n_x] partial maxima of |X|; dmax: [n_cand, n_d].  Block c sets ds[c]
-// and inv[c] (every block derives the same xs from the X partials).
+// xmax: [n_x] partial maxima of |X|; dmax: [n_cand, n_d].  Block c (one per
+// candidate) sets ds[c] and inv[c] (every block derives the same xs from the X partials).
 __global__ __launch_bounds__(256) void out_scales_kernel(const float* __restrict__ xmax, int64_t n_x,
-                                                        const float* __restrict__ dmax, int64_t n_d, int n_cand,
+                                                        const float* __restrict__ dmax, int64_t n_d,
                                                         OutScales* __restrict__ sc) {
   __shared__ float red[256];
   const int c = blockIdx.x;
@@ -284,7 +284,7 @@ hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 
 hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
                              OutScales* sc, hipStream_t stream) {
-  out_scales_kernel<<<n_cand, 256, 0, stream>>>(xmax_part, n_x, dmax, n_d, n_cand, sc);
+  out_scales_kernel<<<n_cand, 256, 0, stream>>>(xmax_part, n_x, dmax, n_d, sc);
   return hipGetLastError();
 }
 
