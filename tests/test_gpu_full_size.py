@@ -1,8 +1,13 @@
 """Parity at the workloads' full sizes, in the launch shapes the benchmark
-times.  Where the oracle cannot evaluate every output at that size it checks
-sampled outputs (per-row clip errors, one row block) and the rest is checked
-through properties that hold at any size (errors are sums over rows; the
-chosen candidate is the first minimum of the reported errors)."""
+times.  The output-score errors of the fused QKV and MLP gate/up groups are
+compared with the oracle's over every row and token, stored by
+tests/golden/make_output_score_full_size.py (the oracle needs minutes there);
+elsewhere the oracle checks sampled outputs (per-row clip errors, one row
+block) and the rest through properties that hold at any size (errors are sums
+over rows; the chosen candidate is the first minimum of the reported errors)."""
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -18,6 +23,16 @@ def A():
     import post_weight_quantization_awq_amd as A
     A.lib()
     return A
+
+
+def _golden_errors(wl_name, gi):
+    """The oracle's full-size alpha errors and first minimum, or None."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "output_score_full_size.json")
+    with open(path) as f:
+        for c in json.load(f)["cases"]:
+            if c["workload"] == wl_name and c["group"] == gi:
+                return np.array(c["errors"], dtype=np.float64), int(c["best_idx"])
+    return None
 
 
 def _sample_rows(part_rows, seed, n_inner=2):
@@ -45,6 +60,10 @@ def _output_clip_full(A, wl_name, gi, G, T_limit=None):
     # never worse than plain RTN (candidate 0), s* is the oracle's candidate row k
     assert np.all(np.isfinite(g_err)) and np.all(g_err >= 0)
     assert k == O.first_argmin(g_err) and g_err[k] <= g_err[0]
+    gold = _golden_errors(wl_name, gi) if T_limit is None else None
+    if gold is not None:   # every row and token against the oracle
+        np.testing.assert_allclose(g_err, gold[0], rtol=1e-3)
+        assert argmin_ok(k, gold[0], gold[1])
     S = O.candidate_scales(xm, 20)
     assert ulp_dist(host(res.best_s), S[k]) <= 2
     # per-row clip errors of sampled rows against the oracle (given the oracle's s_k)
@@ -71,7 +90,8 @@ def _output_clip_full(A, wl_name, gi, G, T_limit=None):
 
 def test_qkv_output_full_size_rows(A):
     """Fused QKV, 6144 x 4096, 16384 tokens: the alpha-search GEMM launches
-    [16384 x 4096] x [4096 x 122880] as in the benchmark."""
+    [16384 x 4096] x [4096 x 122880] as in the benchmark; the 20 errors
+    against the oracle's over the whole group."""
     _output_clip_full(A, "qkv_6144x4096_output", 0, 128)
 
 

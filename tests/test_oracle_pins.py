@@ -231,6 +231,16 @@ class TestQuantizer:
 # errors and search
 # ---------------------------------------------------------------------------
 class TestErrorsAndSearch:
+    def test_full_size_output_fixture(self):
+        # the stored full-size oracle errors (GPU parity at calibration size):
+        # 20 finite errors per group, the first minimum stored, never worse than
+        # plain RTN (alpha = 0, candidate 0)
+        for c in load("output_score_full_size.json")["cases"]:
+            e = np.array(c["errors"])
+            assert e.shape == (20,) and np.all(np.isfinite(e)) and np.all(e > 0)
+            assert c["best_idx"] == O.first_argmin(e) and e[c["best_idx"]] <= e[0]
+            assert c["tokens"] == 16384 and c["group_size"] == 128
+
     def test_act_stats_closed_form(self):
         X = np.array([[1.0, -2.0, 0.0], [-3.0, 2.0, 0.5]], dtype=np.float16)
         assert O.act_stats(X).tolist() == [2.0, 2.0, 0.25]
