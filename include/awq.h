@@ -112,8 +112,9 @@ typedef struct {
  * X: fp16/bf16 [T, ld_x] (x_dtype = AWQ_F16 | AWQ_BF16); T >= 0, d_in >= 1.
  * Sums: per channel, |x| of four consecutive rows added in fp32 (in row
  * order; all terms non-negative, so within 3 * 2^-24 of their exact sum),
- * those sums added in fp64 over fixed token splits, the splits added in a
- * fixed order, rounded once to fp32: deterministic.
+ * those sums added in fp64 over token splits, each partial covering a fixed
+ * set of splits in a fixed order, the partials added in a fixed order,
+ * rounded once to fp32: deterministic.
  * Pass inv_count = 1/T for one chunk; to stream tokens in chunks, call with
  * accumulate = 1 and inv_count = 1/T_total for every chunk after the first.
  * ws: awq_act_stats_workspace(T, d_in) bytes, 256-byte aligned.

@@ -127,11 +127,14 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_main_kernel(const uin
   store_partials<4>(acc, wv, lane, blockIdx.y, d_in, part);
 }
 
-// Lean main kernel, used for 128-row splits: the same rows, splits and sums
-// as act_stats_main_kernel<BF16, 32> would give (bit-identical partials), with the
-// wave's 32 rows in batches of 8 loads, so that a wave fits in 80 registers,
-// and a persistent grid of about one block per compute unit that loops over
-// the splits.  One statistics block then runs on each compute unit beside
+// Lean main kernel, used for 128-row splits: the rows of
+// act_stats_main_kernel<BF16, 32>, with the wave's 32 rows in batches of 8
+// loads, so that a wave fits in 80 registers, and a persistent grid of about
+// one block per compute unit that loops over the splits.  A block keeps its
+// fp64 channel sums across all its splits (y, y + gridDim.y, ... in order) and
+// writes one partial per block row, so its waves never meet at a barrier
+// inside the loop and the final kernel adds gridDim.y partials instead of one
+// per split.  One statistics block then runs on each compute unit beside
 // three blocks of the weight-score search (3 x 144 registers of each SIMD's
 // 512), and the statistics of the next linears stream from HBM while the
 // search computes, instead of taking every free slot of the machine and
@@ -154,11 +157,11 @@ __global__ __launch_bounds__(kStatsThreads, 6) void act_stats_lean_kernel(const 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t col0 = ((int64_t)blockIdx.x * 64 + lane) * 8;
-  for (int64_t y = blockIdx.y; y < n_split; y += gridDim.y) {   // persistent over the splits
-    double acc[8];
+  double acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-    if (col0 < d_in) {
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+  if (col0 < d_in) {
+    for (int64_t y = blockIdx.y; y < n_split; y += gridDim.y) {   // persistent over the splits
       const uint16_t* p = X + (y * (4 * ROWS) + wv * ROWS) * ld + col0;
 #pragma unroll
       for (int b0 = 0; b0 < ROWS; b0 += BATCH) {
@@ -170,9 +173,8 @@ __global__ __launch_bounds__(kStatsThreads, 6) void act_stats_lean_kernel(const 
         for (int q = 0; q < BATCH; q += 4) acc8_rows4<BF16>(&u[q], acc);
       }
     }
-    store_partials<4>(acc, wv, lane, y, d_in, part);
-    __syncthreads();
   }
+  store_partials<4>(acc, wv, lane, blockIdx.y, d_in, part);
 }
 
 // Generic kernel: split y covers rows [row0 + y * rps, min(T, ... + rps)) and
@@ -281,30 +283,36 @@ void act_stats_plan(int64_t T, int64_t d_in, int64_t* n_split, int64_t* rows_per
   *n_split = n_main + n_tail;
 }
 
+// Launches the partial kernels; returns the number of partial rows written
+// (at most the plan's n_split: the lean kernel writes one per block row).
 template <bool BF16>
-static void launch_stats_t(const uint16_t* x, int64_t T, int64_t d_in, int64_t ld, double* part,
-                           hipStream_t stream) {
+static int64_t launch_stats_t(const uint16_t* x, int64_t T, int64_t d_in, int64_t ld, double* part,
+                              hipStream_t stream) {
   int64_t rps, n_main, n_tail;
   stats_split(T, d_in, &rps, &n_main, &n_tail);
   const unsigned n_cb = (unsigned)((d_in + kStatsCols - 1) / kStatsCols);
   const bool vec = ((uintptr_t)x % 16 == 0) && (ld % 8 == 0);
   if (vec) {
+    int64_t n_written = n_main;
     if (n_main > 0) {
       const dim3 grid(n_cb, (unsigned)n_main);
       if (d_in % 8 == 0) {
-        if (rps == kStepRows)
+        if (rps == kStepRows) {
           act_stats_main_kernel<BF16, 16><<<grid, kStatsThreads, 0, stream>>>(x, d_in, ld, part);
-        else
-          act_stats_lean_kernel<BF16>
-              <<<dim3(n_cb, (unsigned)std::max<int64_t>(1, std::min<int64_t>(n_main, kLeanBlocks / n_cb))),
-                 kStatsThreads, 0, stream>>>(x, d_in, ld, n_main, part);
-      } else
+        } else {
+          n_written = std::max<int64_t>(1, std::min<int64_t>(n_main, kLeanBlocks / n_cb));
+          act_stats_lean_kernel<BF16><<<dim3(n_cb, (unsigned)n_written), kStatsThreads, 0, stream>>>(
+              x, d_in, ld, n_main, part);
+        }
+      } else {
         act_stats_partial_kernel<BF16, true><<<dim3(n_cb, (unsigned)n_main), kStatsThreads, 0, stream>>>(
             x, T, d_in, ld, 0, rps, 0, part);
+      }
     }
     if (n_tail > 0)
       act_stats_partial_kernel<BF16, true><<<dim3(n_cb, (unsigned)n_tail), kStatsThreads, 0, stream>>>(
-          x, T, d_in, ld, n_main * rps, kStepRows, n_main, part);
+          x, T, d_in, ld, n_main * rps, kStepRows, n_written, part);
+    return n_written + n_tail;
   } else {
     if (n_main > 0)
       act_stats_partial_kernel<BF16, false><<<dim3(n_cb, (unsigned)n_main), kStatsThreads, 0, stream>>>(
@@ -312,6 +320,7 @@ static void launch_stats_t(const uint16_t* x, int64_t T, int64_t d_in, int64_t l
     if (n_tail > 0)
       act_stats_partial_kernel<BF16, false><<<dim3(n_cb, (unsigned)n_tail), kStatsThreads, 0, stream>>>(
           x, T, d_in, ld, n_main * rps, kStepRows, n_main, part);
+    return n_main + n_tail;
   }
 }
 
@@ -321,10 +330,9 @@ hipError_t launch_act_stats(const void* X, bool bf16, int64_t T, int64_t d_in, i
   int64_t n_split, rps;
   act_stats_plan(T, d_in, &n_split, &rps);
   double* part = (double*)ws;
-  if (n_split > 0) {
-    if (bf16) launch_stats_t<true>((const uint16_t*)X, T, d_in, ld, part, stream);
-    else launch_stats_t<false>((const uint16_t*)X, T, d_in, ld, part, stream);
-  }
+  if (n_split > 0)
+    n_split = bf16 ? launch_stats_t<true>((const uint16_t*)X, T, d_in, ld, part, stream)
+                   : launch_stats_t<false>((const uint16_t*)X, T, d_in, ld, part, stream);
   act_stats_final_kernel<<<(unsigned)((d_in + 31) / 32), 256, 0, stream>>>(
       part, n_split, d_in, (double)inv_count, accumulate, x_mean);
   return hipGetLastError();
