@@ -599,7 +599,7 @@ def bench_sweep(args):
         # taken while earlier blocks are still being searched
         xmb = [[torch.empty(g.d_in, device=dev) for g in wl.groups] for _ in range(blocks)]
         # workspaces and results per lane (a stream of the "blocks" schedule) and group kind
-        n_lane = args.streams if args.schedule == "blocks" else (2 if args.schedule == "pipeline" else 1)
+        n_lane = args.streams if args.schedule == "blocks" else (args.search_streams if args.schedule == "pipeline" else 1)
         ws_stats = [[A.workspace(A.act_stats_workspace_bytes(g.T, g.d_in), dev) for g in wl.groups]
                     for _ in range(n_lane)]
         ws = [[A.workspace(A.search_workspace_bytes(g.d_out, g.d_in, 1, group_size=G, duo=args.duo, asym=args.asym),
@@ -626,7 +626,7 @@ def bench_sweep(args):
         # * "blocks": block b's whole chain on stream b % streams;
         # * "groups": group kind g's chain on stream g % streams.
         main = torch.cuda.current_stream()
-        n_side = 3 if args.schedule == "pipeline" else args.streams
+        n_side = 1 + args.search_streams if args.schedule == "pipeline" else args.streams
         streams = [torch.cuda.Stream() for _ in range(n_side)]
         # per-group readiness, fork, joins, per-block search completion
         sync = HipEvents(blocks * ng + n_side + 1 + blocks, timing=False)
@@ -645,7 +645,8 @@ def bench_sweep(args):
             return st, se, pk
 
         if args.schedule == "pipeline":
-            par = plans(lambda b, gi: streams[0], lambda b, gi: streams[1 + b % 2], lambda b: b % 2)
+            ns = args.search_streams
+            par = plans(lambda b, gi: streams[0], lambda b, gi: streams[1 + b % ns], lambda b: b % ns)
         elif args.schedule == "blocks":
             par = plans(lambda b, gi: streams[b % n_side], lambda b, gi: streams[b % n_side], lambda b: b % n_side)
         else:
@@ -700,7 +701,7 @@ def bench_sweep(args):
                     if b >= 1:
                         sync.wait(streams[0], E_DONE + b - 1)
                     stats(b + D)
-                ws_ = streams[1 + b % 2]
+                ws_ = streams[1 + b % args.search_streams]
                 for gi in range(ng):
                     sync.wait(ws_, b * ng + gi)
                     se_plans[b][gi].launch()
@@ -727,7 +728,7 @@ def bench_sweep(args):
         # the multi-stream step must give exactly the one-stream results: every
         # block's statistics and the last block's search results and packed tensors
         last = blocks - 1
-        lane_last = {"pipeline": last % 2, "blocks": last % n_side}.get(args.schedule, 0)
+        lane_last = {"pipeline": last % args.search_streams, "blocks": last % n_side}.get(args.schedule, 0)
         snap = _sweep_outputs(xmb, res[lane_last], packs[lane_last])
         for k in range(K):  # kernel durations: same steps again, one stream, events around each kernel
             step(ser, k)
@@ -770,7 +771,8 @@ def bench_sweep(args):
                    "group_size": G0, "group_sizes": list(wl.group_sizes), "score": "weight",
                    "calibration_tokens_per_group": wl.groups[0].T, "x_per_block": True,
                    "x_dtype": "bf16", "schedule": args.schedule, "lookahead": args.lookahead,
-                   "streams": 3 if args.schedule == "pipeline" else args.streams, "duo": args.duo, "asym": args.asym},
+                   "streams": 1 + args.search_streams if args.schedule == "pipeline" else args.streams,
+                   "duo": args.duo, "asym": args.asym},
         "per_group_size": out_all,
         "streams_match_one_stream": True,
         "pack_GBps": first["pack_GBps"], "pack_hbm_frac": first["pack_hbm_frac"],
@@ -1400,6 +1402,8 @@ def main() -> int:
                     help="streams of the sweep's timed steps (--schedule blocks or groups)")
     ap.add_argument("--lookahead", type=int, default=2,
                     help="pipeline schedule: blocks whose statistics may run ahead of the searches")
+    ap.add_argument("--search-streams", type=int, default=2,
+                    help="pipeline schedule: streams the searches, selections and packs alternate over")
     ap.add_argument("--schedule", default="pipeline", choices=["pipeline", "blocks", "groups"],
                     help="sweep schedule: the statistics on a stream of their own running ahead of the searches "
                          "on two streams (pipeline), blocks round-robin over the streams (blocks), or one "
