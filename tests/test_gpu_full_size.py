@@ -25,12 +25,12 @@ def A():
     return A
 
 
-def _golden_errors(wl_name, gi):
+def _golden_errors(wl_name, gi, duo=False, asym=False):
     """The oracle's full-size alpha errors and first minimum, or None."""
     path = os.path.join(os.path.dirname(__file__), "golden", "output_score_full_size.json")
     with open(path) as f:
         for c in json.load(f)["cases"]:
-            if c["workload"] == wl_name and c["group"] == gi:
+            if (c["workload"], c["group"], c.get("duo", False), c.get("asym", False)) == (wl_name, gi, duo, asym):
                 return np.array(c["errors"], dtype=np.float64), int(c["best_idx"])
     return None
 
@@ -93,6 +93,26 @@ def test_qkv_output_full_size_rows(A):
     [16384 x 4096] x [4096 x 122880] as in the benchmark; the 20 errors
     against the oracle's over the whole group."""
     _output_clip_full(A, "qkv_6144x4096_output", 0, 128)
+
+
+@pytest.mark.parametrize("duo,asym", [(True, False), (False, True)])
+def test_qkv_output_full_size_duo_asym(A, duo, asym):
+    """Fused QKV at 16384 tokens with duo scaling or asymmetric INT4: the 20
+    output-score errors against the oracle's over the whole group."""
+    wl = WL.WORKLOADS["qkv_6144x4096_output"]
+    say(f"full size output qkv duo={duo} asym={asym}: generating inputs")
+    parts, X = WL.host_group_inputs(wl, 0, 0)
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in parts], dev_f32(xm), group_size=128, score="output", X=dev_x(X),
+                          duo=duo, asym=asym)
+    g_err = host(res.err).astype(np.float64)
+    k = int(host(res.best_idx)[0])
+    gold = _golden_errors("qkv_6144x4096_output", 0, duo, asym)
+    assert gold is not None
+    np.testing.assert_allclose(g_err, gold[0], rtol=1e-3)
+    assert argmin_ok(k, gold[0], gold[1])
+    S = O.candidate_scales(xm, 20, O.S_MIN, O.weight_channel_mean(parts) if duo else None)
+    assert ulp_dist(host(res.best_s), S[k]) <= 2
 
 
 def test_mlp_gate_up_output_clip_full_size_rows(A):
