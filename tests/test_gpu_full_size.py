@@ -135,7 +135,8 @@ def test_mlp_down_output_clip_rows(A):
 def test_sweep_weight_search_row_blocks(A, rows, d_in, G, n_blk):
     """Weight score at sweep shapes.  The error is a sum over rows, so the
     full launch must equal the sum of launches over row blocks (the same
-    candidate scales), and the oracle checks the first block exactly."""
+    candidate scales); the full launch matches the oracle's stored errors over
+    every row, and the oracle checks the first block here as well."""
     say(f"sweep-shape weight search rows={rows} d_in={d_in} G={G}")
     parts = [WL.make_weight(9100 + 31 * i + d_in, r, d_in) for i, r in enumerate(rows)]
     X = WL.make_activations(9200 + d_in, 2048, d_in, "bf16")
@@ -150,6 +151,12 @@ def test_sweep_weight_search_row_blocks(A, rows, d_in, G, n_blk):
         blocks.append(host(r.err).astype(np.float64))
     np.testing.assert_allclose(g_full, np.sum(blocks, axis=0), rtol=1e-5)
     assert int(host(full.best_idx)[0]) == O.first_argmin(g_full)
+    # every row against the oracle's errors (tests/golden/make_weight_score_full_size.py)
+    with open(os.path.join(os.path.dirname(__file__), "golden", "weight_score_full_size.json")) as f:
+        gold = [c for c in json.load(f)["cases"] if (c["rows"], c["d_in"], c["group_size"]) == (rows, d_in, G)]
+    assert len(gold) == 1
+    np.testing.assert_allclose(g_full, gold[0]["errors"], rtol=1e-3)
+    assert argmin_ok(int(host(full.best_idx)[0]), np.array(gold[0]["errors"]), gold[0]["best_idx"])
     say("  oracle on the first row block")
     errs, k, _ = O.search_scales([W[:nb]], xm, G, 20)
     np.testing.assert_allclose(blocks[0], errs, rtol=1e-3)

@@ -240,6 +240,10 @@ class TestErrorsAndSearch:
             assert e.shape == (20,) and np.all(np.isfinite(e)) and np.all(e > 0)
             assert c["best_idx"] == O.first_argmin(e) and e[c["best_idx"]] <= e[0]
             assert c["tokens"] == 16384 and c["group_size"] == 128
+        for c in load("weight_score_full_size.json")["cases"]:
+            e = np.array(c["errors"])
+            assert e.shape == (20,) and np.all(np.isfinite(e)) and np.all(e > 0)
+            assert c["best_idx"] == O.first_argmin(e) and e[c["best_idx"]] <= e[0]
 
     def test_act_stats_closed_form(self):
         X = np.array([[1.0, -2.0, 0.0], [-3.0, 2.0, 0.5]], dtype=np.float16)
