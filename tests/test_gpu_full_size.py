@@ -5,6 +5,7 @@ tests/golden/make_output_score_full_size.py (the oracle needs minutes there);
 elsewhere the oracle checks sampled outputs (per-row clip errors, one row
 block) and the rest through properties that hold at any size (errors are sums
 over rows; the chosen candidate is the first minimum of the reported errors)."""
+import hashlib
 import json
 import os
 
@@ -160,3 +161,27 @@ def test_sweep_weight_search_row_blocks(A, rows, d_in, G, n_blk):
     say("  oracle on the first row block")
     errs, k, _ = O.search_scales([W[:nb]], xm, G, 20)
     np.testing.assert_allclose(blocks[0], errs, rtol=1e-3)
+
+
+def _pack_cases():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "pack_full_size.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _pack_cases(), ids=lambda c: f"{c['rows']}-{c['d_in']}-G{c['group_size']}"
+                         + ("-asym" if c["asym"] else ""))
+def test_pack_full_size_digests(A, case):
+    """Whole sweep-shaped groups packed with the oracle's chosen scale row: the
+    qweight, scales and qzeros bytes hash to the oracle's (every code, fp16
+    scale and zero point bit-exact)."""
+    rows, d_in, G = case["rows"], case["d_in"], case["group_size"]
+    say(f"full-size pack rows={rows} d_in={d_in} G={G} asym={case['asym']}")
+    parts = [WL.make_weight(9100 + 31 * i + d_in, r, d_in) for i, r in enumerate(rows)]
+    X = WL.make_activations(9200 + d_in, 2048, d_in, "bf16")
+    s = O.candidate_scales(O.act_stats(X), 20)[case["best_idx"]]
+    W = np.concatenate(parts, axis=0)
+    qw, sc, qz = A.quantize_pack(dev_f16(W), G, dev_f32(s), asym=case["asym"])
+    dig = lambda a: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+    assert dig(host(qw).view(np.uint32).astype("<u4")) == case["qweight"]
+    assert dig(host(sc).view(np.uint16).view("<f2")) == case["scales"]
+    assert dig(host(qz).view(np.uint32).astype("<u4")) == case["qzeros"]

@@ -244,6 +244,12 @@ class TestErrorsAndSearch:
             e = np.array(c["errors"])
             assert e.shape == (20,) and np.all(np.isfinite(e)) and np.all(e > 0)
             assert c["best_idx"] == O.first_argmin(e) and e[c["best_idx"]] <= e[0]
+        ws = {(tuple(c["rows"]), c["d_in"], c["group_size"]): c["best_idx"]
+              for c in load("weight_score_full_size.json")["cases"]}
+        for c in load("pack_full_size.json")["cases"]:
+            # the packs use the weight-score fixture's chosen candidate; three sha256 digests each
+            assert ws[(tuple(c["rows"]), c["d_in"], c["group_size"])] == c["best_idx"]
+            assert all(len(c[k]) == 64 and int(c[k], 16) >= 0 for k in ("qweight", "scales", "qzeros"))
 
     def test_act_stats_closed_form(self):
         X = np.array([[1.0, -2.0, 0.0], [-3.0, 2.0, 0.5]], dtype=np.float16)
