@@ -185,3 +185,15 @@ def test_pack_full_size_digests(A, case):
     assert dig(host(qw).view(np.uint32).astype("<u4")) == case["qweight"]
     assert dig(host(sc).view(np.uint16).view("<f2")) == case["scales"]
     assert dig(host(qz).view(np.uint32).astype("<u4")) == case["qzeros"]
+
+
+@pytest.mark.parametrize("d_in", [4096, 12288])
+def test_act_stats_sweep_shape(A, d_in):
+    """Activation statistics at the sweep's calibration size (65536 bf16 tokens;
+    the persistent kernel with each block's sums kept across its 128-row
+    splits, 32 or 10 block rows over 512 splits): every channel against the
+    oracle's token-order fp64 sum."""
+    say(f"act_stats 65536 x {d_in} bf16")
+    X = WL.make_activations(9300 + d_in, 65536, d_in, "bf16")
+    g = host(A.act_stats(dev_x(X)))
+    np.testing.assert_allclose(g, O.act_stats(X), rtol=1e-6)
