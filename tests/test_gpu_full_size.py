@@ -154,7 +154,8 @@ def test_sweep_weight_search_row_blocks(A, rows, d_in, G, n_blk):
     assert int(host(full.best_idx)[0]) == O.first_argmin(g_full)
     # every row against the oracle's errors (tests/golden/make_weight_score_full_size.py)
     with open(os.path.join(os.path.dirname(__file__), "golden", "weight_score_full_size.json")) as f:
-        gold = [c for c in json.load(f)["cases"] if (c["rows"], c["d_in"], c["group_size"]) == (rows, d_in, G)]
+        gold = [c for c in json.load(f)["cases"] if (c["rows"], c["d_in"], c["group_size"]) == (rows, d_in, G)
+                and not c.get("duo") and not c.get("asym")]
     assert len(gold) == 1
     np.testing.assert_allclose(g_full, gold[0]["errors"], rtol=1e-3)
     assert argmin_ok(int(host(full.best_idx)[0]), np.array(gold[0]["errors"]), gold[0]["best_idx"])
@@ -197,3 +198,25 @@ def test_act_stats_sweep_shape(A, d_in):
     X = WL.make_activations(9300 + d_in, 65536, d_in, "bf16")
     g = host(A.act_stats(dev_x(X)))
     np.testing.assert_allclose(g, O.act_stats(X), rtol=1e-6)
+
+
+@pytest.mark.parametrize("duo,asym", [(True, False), (False, True)])
+def test_sweep_weight_search_duo_asym(A, duo, asym):
+    """The gate/up sweep shape (24576 x 4096, G = 128) with duo scaling or the
+    asymmetric quantizer: every row against the oracle's stored errors."""
+    rows, d_in, G = [12288, 12288], 4096, 128
+    say(f"sweep-shape weight search duo={duo} asym={asym}")
+    parts = [WL.make_weight(9100 + 31 * i + d_in, r, d_in) for i, r in enumerate(rows)]
+    X = WL.make_activations(9200 + d_in, 2048, d_in, "bf16")
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in parts], dev_f32(xm), group_size=G, duo=duo, asym=asym)
+    g_err = host(res.err).astype(np.float64)
+    with open(os.path.join(os.path.dirname(__file__), "golden", "weight_score_full_size.json")) as f:
+        gold = [c for c in json.load(f)["cases"] if (c["rows"], c["d_in"], c["group_size"]) == (rows, d_in, G)
+                and c.get("duo", False) == duo and c.get("asym", False) == asym]
+    assert len(gold) == 1
+    np.testing.assert_allclose(g_err, gold[0]["errors"], rtol=1e-3)
+    k = int(host(res.best_idx)[0])
+    assert argmin_ok(k, np.array(gold[0]["errors"]), gold[0]["best_idx"])
+    S = O.candidate_scales(xm, 20, O.S_MIN, O.weight_channel_mean(parts) if duo else None)
+    assert ulp_dist(host(res.best_s), S[k]) <= 2

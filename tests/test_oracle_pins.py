@@ -245,7 +245,7 @@ class TestErrorsAndSearch:
             assert e.shape == (20,) and np.all(np.isfinite(e)) and np.all(e > 0)
             assert c["best_idx"] == O.first_argmin(e) and e[c["best_idx"]] <= e[0]
         ws = {(tuple(c["rows"]), c["d_in"], c["group_size"]): c["best_idx"]
-              for c in load("weight_score_full_size.json")["cases"]}
+              for c in load("weight_score_full_size.json")["cases"] if not c.get("duo") and not c.get("asym")}
         for c in load("pack_full_size.json")["cases"]:
             # the packs use the weight-score fixture's chosen candidate; three sha256 digests each
             assert ws[(tuple(c["rows"]), c["d_in"], c["group_size"])] == c["best_idx"]
