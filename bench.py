@@ -78,9 +78,9 @@ PMC_TRAFFIC = {
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
         "sha256": "defe0c2e9940a8e54a9e9e972d928a3348712ea21d6d59d02dfc4e145d6bede3"},
     ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 12140610.5, "write_kib": 20640.0,
+        "fetch_kib": 11893939.4, "write_kib": 20640.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "9ccdd3e1c3eec37d7ea3f2b49e30a9569904755b641e5721fc5bcee14ca3b045"},
+        "sha256": "d4cb58e5ba2e367f0c9864a86ca3112000757f3ef4cab0790e475b593b0372ed"},
 }
 
 

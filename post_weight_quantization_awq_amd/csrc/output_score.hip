@@ -46,15 +46,16 @@ __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_lo) {
 //   point and codes; the signed code clamp(n, -z, 15 - z) times the step)
 //   dW16 rows are d_out_pad apart per candidate and K_pad elements long; rows
 //   d_out .. d_out_pad-1 and columns d_in .. K_pad-1 are written as zeros.
+// A block loads its tile of W once and takes the launch's candidates
+// cand0 + blockIdx.y, + gridDim.y, ... in turn, so W is read once per
+// candidate slice instead of once per candidate.
 template <int G, bool WRITE, bool ASYM>
 __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int64_t d_out_pad, int64_t K_pad, int mode,
-    const float* __restrict__ S, const float* __restrict__ s_best, int n_clip, float clip_lo, int cand0,
+    const float* __restrict__ S, const float* __restrict__ s_best, int n_clip, float clip_lo, int cand0, int n_cand,
     const OutScales* __restrict__ sc, float* __restrict__ dmax, uint16_t* __restrict__ dw) {
   constexpr int LPG = G / 16;
   constexpr int RS = kDwThreads / LPG;
-  const int c = cand0 + blockIdx.y;
-  const float* s = (mode == 0) ? S + (int64_t)c * d_in : s_best;
   const int64_t n_gcol = d_in / G;
   const int64_t gcol = blockIdx.x % n_gcol;
   const int64_t rblk = blockIdx.x / n_gcol;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
   __shared__ float red[kDwThreads / 64];
   const int64_t col = gcol * G + lg * 16;
 
-  float w[16], sv[16], v[16];
+  float w[16];
   if (valid) {
     const uint4* p = (const uint4*)(row_ptr(P, row, d_in) + col);
     unpack8_f16(p[0], w);
@@ -76,82 +77,89 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) w[j] = 0.0f;
   }
+  for (int ci = blockIdx.y; ci < n_cand; ci += gridDim.y) {
+    const int c = cand0 + ci;
+    const float* s = (mode == 0) ? S + (int64_t)c * d_in : s_best;
+    float sv[16], v[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float4 t = ((const float4*)(s + col))[j];
-    sv[4 * j] = t.x; sv[4 * j + 1] = t.y; sv[4 * j + 2] = t.z; sv[4 * j + 3] = t.w;
-  }
-  float m = 0.0f, mn = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const float4 t = ((const float4*)(s + col))[j];
+      sv[4 * j] = t.x; sv[4 * j + 1] = t.y; sv[4 * j + 2] = t.z; sv[4 * j + 3] = t.w;
+    }
+    float m = 0.0f, mn = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    v[j] = w[j] * sv[j];
-    if constexpr (ASYM) {
-      m = __builtin_fmaxf(m, v[j]);
-      mn = __builtin_fmaxf(mn, -v[j]);
-    } else {
-      m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
-    }
-  }
-  m = group_max<LPG>(m);
-  float a = m, an = 0.0f;
-  if constexpr (ASYM) an = group_max<LPG>(mn);
-  if (mode == 1) {
-    const float cr = clip_ratio(c, n_clip, clip_lo);
-    a = cr * a;
-    an = cr * an;
-  }
-  const float step = ASYM ? div15(a + an) : div7(a);
-  const float inv = __builtin_amdgcn_rcpf(step);
-  float qlo = -7.0f, qhi = 7.0f;
-  if constexpr (ASYM) {
-    const float z = step > 0.0f ? __builtin_amdgcn_fmed3f(code_exact(an, step, inv), 0.0f, (float)kUMax) : 0.0f;
-    qlo = -z;
-    qhi = (float)kUMax - z;
-  }
-  const float dsc = WRITE ? sc->ds[c] : 1.0f;
-  uint32_t outw[8];
-  float mx = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    float n = step > 0.0f ? code_exact(v[j], step, inv) : 0.0f;
-    n = __builtin_fminf(__builtin_fmaxf(n, qlo), qhi);
-    // w_hat - w = (q * step - w * s) / s, formed in the scaled domain with one
-    // fma and the hardware reciprocal of s: within a few fp32 ulp of
-    // RN(RN(q * step) / s) - w, far below the fp16 rounding of the operand
-    // (the codes q themselves are exact)
-    const float d = __builtin_fmaf(n, step, -v[j]) * __builtin_amdgcn_rcpf(sv[j]);
-    if constexpr (WRITE) {
-      const uint32_t b = f2h_bits(d * dsc);       // exact scaling by 2^e, one rounding
-      if (j & 1) outw[j >> 1] |= b << 16;
-      else outw[j >> 1] = b;
-    } else {
-      mx = __builtin_fmaxf(mx, __builtin_fabsf(d));
-    }
-  }
-  if constexpr (WRITE) {
-    if (row >= d_out_pad) return;
-    uint16_t* rowp = dw + (int64_t)blockIdx.y * d_out_pad * K_pad + row * K_pad;
-    uint4* dst = (uint4*)(rowp + col);
-    if (!valid) {
-      for (int j = 0; j < 8; ++j) outw[j] = 0u;
-    }
-    dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-    dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
-    if (K_pad > d_in && gcol == n_gcol - 1) {  // zero K padding (at most one group wide)
-      uint4* pad = (uint4*)(rowp + col + G);
-      if (col + G < K_pad) {
-        pad[0] = make_uint4(0u, 0u, 0u, 0u);
-        pad[1] = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < 16; ++j) {
+      v[j] = w[j] * sv[j];
+      if constexpr (ASYM) {
+        m = __builtin_fmaxf(m, v[j]);
+        mn = __builtin_fmaxf(mn, -v[j]);
+      } else {
+        m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
       }
     }
-  } else {
-    mx = wave_max(mx);
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
-    __syncthreads();
-    if (tid == 0) {
-      float b = red[0];
-      for (int w = 1; w < kDwThreads / 64; ++w) b = __builtin_fmaxf(b, red[w]);
-      dmax[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = b;
+    m = group_max<LPG>(m);
+    float a = m, an = 0.0f;
+    if constexpr (ASYM) an = group_max<LPG>(mn);
+    if (mode == 1) {
+      const float cr = clip_ratio(c, n_clip, clip_lo);
+      a = cr * a;
+      an = cr * an;
+    }
+    const float step = ASYM ? div15(a + an) : div7(a);
+    const float inv = __builtin_amdgcn_rcpf(step);
+    float qlo = -7.0f, qhi = 7.0f;
+    if constexpr (ASYM) {
+      const float z = step > 0.0f ? __builtin_amdgcn_fmed3f(code_exact(an, step, inv), 0.0f, (float)kUMax) : 0.0f;
+      qlo = -z;
+      qhi = (float)kUMax - z;
+    }
+    const float dsc = WRITE ? sc->ds[c] : 1.0f;
+    uint32_t outw[8];
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float n = step > 0.0f ? code_exact(v[j], step, inv) : 0.0f;
+      n = __builtin_fminf(__builtin_fmaxf(n, qlo), qhi);
+      // w_hat - w = (q * step - w * s) / s, formed in the scaled domain with one
+      // fma and the hardware reciprocal of s: within a few fp32 ulp of
+      // RN(RN(q * step) / s) - w, far below the fp16 rounding of the operand
+      // (the codes q themselves are exact)
+      const float d = __builtin_fmaf(n, step, -v[j]) * __builtin_amdgcn_rcpf(sv[j]);
+      if constexpr (WRITE) {
+        const uint32_t b = f2h_bits(d * dsc);       // exact scaling by 2^e, one rounding
+        if (j & 1) outw[j >> 1] |= b << 16;
+        else outw[j >> 1] = b;
+      } else {
+        mx = __builtin_fmaxf(mx, __builtin_fabsf(d));
+      }
+    }
+    if constexpr (WRITE) {
+      if (row < d_out_pad) {
+        uint16_t* rowp = dw + (int64_t)ci * d_out_pad * K_pad + row * K_pad;
+        uint4* dst = (uint4*)(rowp + col);
+        if (!valid) {
+          for (int j = 0; j < 8; ++j) outw[j] = 0u;
+        }
+        dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+        dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+        if (K_pad > d_in && gcol == n_gcol - 1) {  // zero K padding (at most one group wide)
+          uint4* pad = (uint4*)(rowp + col + G);
+          if (col + G < K_pad) {
+            pad[0] = make_uint4(0u, 0u, 0u, 0u);
+            pad[1] = make_uint4(0u, 0u, 0u, 0u);
+          }
+        }
+      }
+    } else {
+      mx = wave_max(mx);
+      if ((tid & 63) == 0) red[tid >> 6] = mx;
+      __syncthreads();
+      if (tid == 0) {
+        float b = red[0];
+        for (int w = 1; w < kDwThreads / 64; ++w) b = __builtin_fmaxf(b, red[w]);
+        dmax[(int64_t)ci * gridDim.x + blockIdx.x] = b;
+      }
+      __syncthreads();  // red is written again by the next candidate
     }
   }
 }
@@ -165,13 +173,16 @@ hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64
                            int64_t d_out_pad, int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best,
                            int n_clip, float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
                            hipStream_t stream) {
-  // max pass: d_out rows; write pass: d_out_pad rows (zeros past d_out)
-  dim3 grid((unsigned)build_dw_blocks(group_size, dw == nullptr ? d_out : d_out_pad, d_in), (unsigned)n_cand);
-#define AWQ_DW2(G, A)                                                                         \
-  if (dw == nullptr) build_dw_kernel<G, false, A><<<grid, kDwThreads, 0, stream>>>(             \
-      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw); \
-  else build_dw_kernel<G, true, A><<<grid, kDwThreads, 0, stream>>>(                            \
-      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, sc, dmax, dw);
+  // max pass: d_out rows; write pass: d_out_pad rows (zeros past d_out).  One
+  // block per W tile takes all of the launch's candidates: measured 1.2%
+  // faster on the fused-QKV output-score step than one block per tile and
+  // candidate (W read once instead of n_cand times), 0.9% than four slices
+  dim3 grid((unsigned)build_dw_blocks(group_size, dw == nullptr ? d_out : d_out_pad, d_in), 1u);
+#define AWQ_DW2(G, A)                                                                                  \
+  if (dw == nullptr) build_dw_kernel<G, false, A><<<grid, kDwThreads, 0, stream>>>(                      \
+      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, dmax, dw); \
+  else build_dw_kernel<G, true, A><<<grid, kDwThreads, 0, stream>>>(                                     \
+      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, dmax, dw);
 #define AWQ_DW(G) \
   if (asym) { AWQ_DW2(G, true) } else { AWQ_DW2(G, false) }
   switch (group_size) {
