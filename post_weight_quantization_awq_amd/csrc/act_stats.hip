@@ -130,19 +130,23 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_main_kernel(const uin
 // Lean main kernel, used for 128-row splits: the rows of
 // act_stats_main_kernel<BF16, 32>, with the wave's 32 rows in batches of 8
 // loads, so that a wave fits in 80 registers, and a persistent grid of about
-// one block per compute unit that loops over the splits.  A block keeps its
+// three blocks per four compute units that loops over the splits.  A block keeps its
 // fp64 channel sums across all its splits (y, y + gridDim.y, ... in order) and
 // writes one partial per block row, so its waves never meet at a barrier
 // inside the loop and the final kernel adds gridDim.y partials instead of one
-// per split.  One statistics block then runs on each compute unit beside
-// three blocks of the weight-score search (3 x 144 registers of each SIMD's
-// 512), and the statistics of the next linears stream from HBM while the
-// search computes, instead of taking every free slot of the machine and
-// stalling it: on the 36-block Qwen3-8B sweep the step measured 33.8 ms
-// against 35.6 with act_stats_main_kernel<BF16, 32> (alone, this kernel
-// streams ~5% slower: 20.4 against 19.3 ms of statistics per step; 128 or
-// 512 blocks measured 38.6 and 34.5 ms per step, 192 the same as 256).
-constexpr int64_t kLeanBlocks = 256;   // blocks of the persistent grid (~one per compute unit)
+// per split.  A statistics block then runs on a compute unit beside three
+// blocks of the weight-score search (3 x 144 registers of each SIMD's 512),
+// and the statistics of the next linears stream from HBM while the search
+// computes, instead of taking every free slot of the machine and stalling it.
+//
+// Grid size: the search alone already holds the chip at its sustained power
+// limit (~1.34 kW at a ~2.2 GHz shader clock on the 36-block Qwen3-8B sweep;
+// the statistics alone draw ~1.08 kW), and with both running the clock drops
+// to ~2.0 GHz, so the stream rate that suits the pair is below this kernel's
+// best alone.  On that sweep 192 blocks (6.3 TB/s alone) measured 30.7-31.0
+// ms per step against 31.8-32.1 with 256 (6.9 TB/s alone), 31.2-31.3 with
+// 160 and 31.4 with 224, in interleaved runs on one machine.
+constexpr int64_t kLeanBlocks = 192;   // blocks of the persistent grid
 
 template <bool BF16>
 __global__ __launch_bounds__(kStatsThreads, 6) void act_stats_lean_kernel(const uint16_t* __restrict__ X,
