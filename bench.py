@@ -30,7 +30,11 @@ import ctypes
 import hashlib
 import json
 import os
+import re
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -142,6 +146,70 @@ class HipEvents:
     def close(self):
         for e in self.ev:
             self.hip.hipEventDestroy(e)
+
+
+class PowerSampler:
+    """Socket power and shader clock while the timed steps run (``--power``):
+    a thread calls ``amd-smi metric --clock --power`` back to back (about one
+    sample per 0.1 s) between start() and stop(); stop() returns the means, or
+    None when the option is off or amd-smi is not there.  Use enough steps for
+    the timed region to hold a few tens of samples."""
+
+    def __init__(self, enabled: bool, device: int = 0):
+        self.cmd = ["amd-smi", "metric", "-g", str(device), "--clock", "--power"]
+        self.enabled = enabled and shutil.which("amd-smi") is not None
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    @staticmethod
+    def parse(text: str):
+        watts, clocks, in_gfx = None, [], False
+        for line in text.splitlines():
+            f = line.strip()
+            if f.startswith("SOCKET_POWER:"):
+                try:
+                    watts = float(f.split()[1])
+                except (IndexError, ValueError):
+                    pass
+            elif re.fullmatch(r"GFX_\d+:", f):
+                in_gfx = True
+            elif f.startswith("CLK:") and in_gfx:
+                try:
+                    clocks.append(float(f.split()[1]))
+                except (IndexError, ValueError):
+                    pass
+                in_gfx = False
+            elif f.endswith(":"):
+                in_gfx = False
+        return (watts, sum(clocks) / len(clocks)) if watts is not None and clocks else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(self.cmd, capture_output=True, text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            v = self.parse(r.stdout)
+            if v is not None and not self._stop.is_set():
+                self.samples.append(v)
+
+    def start(self):
+        if self.enabled:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is None:
+            return None
+        self._stop.set()
+        self._thread.join()
+        if not self.samples:
+            return None
+        n = len(self.samples)
+        return {"socket_W": sum(w for w, _ in self.samples) / n, "gfx_MHz": sum(c for _, c in self.samples) / n,
+                "gfx_MHz_min": min(c for _, c in self.samples), "samples": n,
+                "source": " ".join(self.cmd) + ", sampled during the timed steps"}
 
 
 def pack_bytes(d_out: int, d_in: int, G: int) -> int:
@@ -524,11 +592,14 @@ def bench_output(args, wl_name: str):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    pw = PowerSampler(args.power)
+    pw.start()
     t1 = time.perf_counter()
     for _ in range(K):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t1) * 1e3 / K
+    power = pw.stop()
     for k in range(K):  # GEMM durations: same steps again with events around the GEMMs
         step(k)
     torch.cuda.synchronize()
@@ -540,7 +611,7 @@ def bench_output(args, wl_name: str):
     tflops = sum(flops_alpha) / (sum(gemm_ms) * 1e-3) / 1e12
     n_gemm = 20 + (wl.n_clip or 0)
     total_flops = sum(2.0 * X.shape[0] * g.d_out * g.d_in * n_gemm for _, X, g, *_ in plans)
-    return {
+    out = {
         "metric": METRIC,
         "value": n_elem_pts / (ms_step * 1e-3),
         "unit": "weight-elem*grid-pt/s",
@@ -556,6 +627,9 @@ def bench_output(args, wl_name: str):
                      "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": pmc_traffic("gemm_sq_kernel", wl_name, args),
                      "kernel": "gemm_sq_kernel"},
     }
+    if power is not None:
+        out["power"] = power
+    return out
 
 
 def _sweep_outputs(xmb, res_lane, packs_lane):
@@ -720,11 +794,14 @@ def bench_sweep(args):
         for _ in range(args.warmup):
             step_streams()
         torch.cuda.synchronize()
+        pw = PowerSampler(args.power)
+        pw.start()
         t1 = time.perf_counter()
         for _ in range(K):
             step_streams()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t1) * 1e3 / K
+        power = pw.stop()
         # the multi-stream step must give exactly the one-stream results: every
         # block's statistics and the last block's search results and packed tensors
         last = blocks - 1
@@ -757,6 +834,8 @@ def bench_sweep(args):
             "act_stats_ms": sums[0], "act_stats_GBps": xb / (sums[0] * 1e-3) / 1e9,
             "act_stats_hbm_frac": xb / (sums[0] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         }
+        if power is not None:
+            out_all[f"G{G}"]["power"] = power
         del par, ser
     n_w = blocks * sum(g.d_out * g.d_in for g in wl.groups)
     G0 = wl.group_sizes[0]
@@ -897,11 +976,14 @@ def bench_export(args):
     for _ in range(args.warmup):
         step_streams()
     torch.cuda.synchronize()
+    pw = PowerSampler(args.power)
+    pw.start()
     t1 = time.perf_counter()
     for _ in range(K):
         step_streams()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t1) * 1e3 / K
+    power = pw.stop()
 
     def outputs():  # the last block's export: packed tensors, folded norms, shared and searched scales
         return ([t.clone() for o in packs.values() for t in o], [t.clone() for t in n_out.values()],
@@ -923,7 +1005,7 @@ def bench_export(args):
     n_all = blocks * sum(g.d_out * g.d_in for g in grp)
     pk = blocks * sum(pack_bytes(r, g.d_in, G) for g in grp for r in g.parts)
     frac = SEARCH_OPS_PER_ELEM_PT * n_search * 20 / (per_step["search"] * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T
-    return {
+    out = {
         "metric": METRIC, "value": n_search * 20 / (ms_step * 1e-3), "unit": "weight-elem*grid-pt/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -940,6 +1022,9 @@ def bench_export(args):
                      "frac_of_measured_peak": frac * VALU_LANE_OPS_PEAK_T / VALU_LANE_OPS_MEASURED_T,
                      "traffic": None, "kernel": "search_weight_kernel"},
     }
+    if power is not None:
+        out["power"] = power
+    return out
 
 
 def cpu_baseline_w4a16(layers_h, M, budget_s: float):
@@ -1414,6 +1499,9 @@ def main() -> int:
                     help="asymmetric INT4 (zero point per group) in the search and pack of the search workloads")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per decode step of the W4A16 workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power", action="store_true",
+                    help="sample socket power and shader clock (amd-smi) during the timed steps of the sweep, "
+                         "export and output-score workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the CPU oracle baseline")
     ap.add_argument("--cpu-blocks", type=int, default=4,
