@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kStatsThreads) void act_stats_main_kernel(const uin
 // limit (~1.34 kW at a ~2.2 GHz shader clock on the 36-block Qwen3-8B sweep;
 // the statistics alone draw ~1.08 kW), and with both running the clock drops
 // to ~2.0 GHz, so the stream rate that suits the pair is below this kernel's
-// best alone.  On that sweep 192 blocks (6.3 TB/s alone) measured 30.7-31.0
+// best alone.  On that sweep 192 blocks (6.4 TB/s alone) measured 30.7-31.0
 // ms per step against 31.8-32.1 with 256 (6.9 TB/s alone), 31.2-31.3 with
 // 160 and 31.4 with 224, in interleaved runs on one machine.
 constexpr int64_t kLeanBlocks = 192;   // blocks of the persistent grid
