@@ -79,7 +79,7 @@ typedef struct {
   int32_t n_clip;     /* 0 = no clip search; else >= 2 ratios (output score only) */
   double s_min;       /* lower clamp of x_mean^alpha before normalising (1e-4)    */
   float clip_lo;      /* smallest clip ratio, in (0, 1]; ratios 1.0 .. clip_lo     */
-  int32_t flags;      /* AWQ_FLAG_DUO | AWQ_FLAG_ASYM; other bits 0                 */
+  int32_t flags;      /* AWQ_FLAG_DUO | AWQ_FLAG_ASYM | AWQ_FLAG_OUT_*; others 0   */
 } awq_search_cfg;
 
 /* [cassindra] The scale search as code, duo_scaling=True: the candidates are
@@ -93,6 +93,19 @@ typedef struct {
  * per group and output channel; the recipe's W4A16_ASYM): score the
  * asymmetric grid of awq_quantize_pack_asym instead of the symmetric one. */
 #define AWQ_FLAG_ASYM 2
+
+/* Output score only: how the sum of squares of X (W_hat - W)^T is formed.
+ * Both give the same quantity ([cassindra] The scale search as code); by
+ * default the library takes the one with less matrix-core work.
+ *   direct:        each candidate contracts X with dW = W_hat - W
+ *                  (2 T d_in d_out flops per candidate);
+ *   second moment: per row o, sum_t (X dW^T)[t,o]^2 = dW_o H dW_o^T with
+ *                  H = X^T X formed once (2 T d_in^2 flops), then
+ *                  2 d_in^2 d_out flops per candidate: the lighter form when
+ *                  the calibration set has more tokens than d_in.
+ * Setting both is AWQ_EINVAL; with neither the library chooses. */
+#define AWQ_FLAG_OUT_DIRECT 4
+#define AWQ_FLAG_OUT_GRAM 8
 
 /* One group of linears sharing an input ([cassindra] torch.cat of the group's
  * weights): part p is an fp16 device matrix [rows[p], d_in], 16-byte aligned.
@@ -215,6 +228,11 @@ awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, in
  * two chosen from its maximum (exact, overflow-free), fp32 accumulation, fp64
  * final sums; the fp16 rounding of (w_hat - W) bounds the relative error of
  * err[k] near 1e-4 on small inputs and far below it at calibration sizes.
+ * In the second-moment form (AWQ_FLAG_OUT_GRAM, or chosen by the library)
+ * H = X^T X is accumulated in fp32 from the same fp16 X, normalised to unit
+ * diagonal (R H R, R = diag(H_ii^-1/2)) and rounded to fp16, and the columns
+ * of dW carry sqrt(H_ii) instead: the extra rounding of H perturbs each
+ * row's quadratic form by random-signed terms far below 1e-4 of it.
  * ws: awq_search_workspace(...) bytes, 256-byte aligned.
  * ------------------------------------------------------------------------- */
 awq_status awq_search_workspace(const awq_search_cfg* cfg /* [host] */, int64_t d_out_total,

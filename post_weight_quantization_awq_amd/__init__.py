@@ -33,6 +33,9 @@ AWQ_F16, AWQ_BF16, AWQ_F32 = 0, 1, 2
 AWQ_SCORE_WEIGHT, AWQ_SCORE_OUTPUT = 0, 1
 AWQ_FLAG_DUO = 1
 AWQ_FLAG_ASYM = 2
+AWQ_FLAG_OUT_DIRECT = 4
+AWQ_FLAG_OUT_GRAM = 8
+_OUT_FORM = {"auto": 0, "direct": AWQ_FLAG_OUT_DIRECT, "gram": AWQ_FLAG_OUT_GRAM}
 STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_EINVAL", 2: "AWQ_ESHAPE", 3: "AWQ_EDTYPE",
                 4: "AWQ_EWORKSPACE", 5: "AWQ_EALIGN", 6: "AWQ_EHIP"}
 
@@ -300,30 +303,34 @@ class SearchResult:
     clip_err: Optional[torch.Tensor]  # fp32 [d_out, n_clip] or None
 
 
-def _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo=False, asym=False) -> SearchCfg:
+def _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo=False, asym=False, out_form="auto") -> SearchCfg:
     sc = {"weight": AWQ_SCORE_WEIGHT, "output": AWQ_SCORE_OUTPUT}[score] if isinstance(score, str) else score
-    flags = (AWQ_FLAG_DUO if duo else 0) | (AWQ_FLAG_ASYM if asym else 0)
+    if out_form not in _OUT_FORM:
+        raise ValueError(f"out_form {out_form!r} not in {sorted(_OUT_FORM)}")
+    flags = (AWQ_FLAG_DUO if duo else 0) | (AWQ_FLAG_ASYM if asym else 0) | _OUT_FORM[out_form]
     return SearchCfg(group_size, n_grid, sc, n_clip, s_min, clip_lo, flags)
 
 
 def search_workspace_bytes(d_out: int, d_in: int, T: int = 0, *, group_size: int = 128, n_grid: int = 20,
                            score="weight", n_clip: int = 0, clip_lo: float = 0.5, s_min: float = 1e-4,
-                           duo: bool = False, asym: bool = False) -> int:
-    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo, asym)
+                           duo: bool = False, asym: bool = False, out_form: str = "auto") -> int:
+    cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo, asym, out_form)
     n = ctypes.c_size_t()
     _check(lib().awq_search_workspace(ctypes.byref(cfg), d_out, d_in, T, ctypes.byref(n)))
     return n.value
 
 
 class SearchPlan(_Prepared):
-    """Grid search of alpha for one group of linears sharing an input (rows concatenated)."""
+    """Grid search of alpha for one group of linears sharing an input (rows concatenated).
+    out_form (output score): "auto" (the library picks), "direct" (X times each candidate's
+    dW) or "gram" (the second-moment form dW H dW^T with H = X^T X)."""
     _fn = "awq_search_scales"
 
     def __init__(self, W_parts: Sequence[torch.Tensor], x_mean: torch.Tensor, *, group_size: int = 128,
                  n_grid: int = 20, score="weight", X: Optional[torch.Tensor] = None, n_clip: int = 0,
                  clip_lo: float = 0.5, s_min: float = 1e-4, want_clip_err: bool = False,
                  ws: Optional[torch.Tensor] = None, out: Optional[SearchResult] = None, stream=None,
-                 duo: bool = False, asym: bool = False):
+                 duo: bool = False, asym: bool = False, out_form: str = "auto"):
         parts: List[torch.Tensor] = list(W_parts)
         if not parts:
             raise ValueError("empty weight group")
@@ -337,7 +344,7 @@ class SearchPlan(_Prepared):
                 raise ValueError("the parts of a group must live on one device")
         d_out = sum(p.shape[0] for p in parts)
         _tensor(x_mean, "x_mean", torch.float32, (d_in,), like=parts[0])
-        self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo, asym)
+        self.cfg = _cfg(group_size, n_grid, score, n_clip, clip_lo, s_min, duo, asym, out_form)
         T, ld, xdt = 0, 0, AWQ_BF16
         if X is not None:
             _tensor(X, "X", (torch.bfloat16, torch.float16), (None, d_in), unit_col_stride=True, like=parts[0])

@@ -57,7 +57,10 @@ struct SearchPlan {
   int64_t T_pad, d_out_pad, K_pad, n_mt, ldc;  // output score: padded GEMM shapes, token tiles, partial ld
   int64_t n_x, n_db;    // output score: X max partials, dW max partials per candidate
   int cand_chunk;       // output score: candidates per dW chunk
+  bool gram;            // output score in the second-moment form (H = X^T X)
+  int64_t g_T_pad, g_xt_rows, g_h_rows;  // second-moment form: token padding, Xt rows, H16 rows
   size_t off_S, off_C2, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
+  size_t off_h32, off_h16, off_hc, off_hr;
   bool duo;                   // duo-scaling candidates: w_mean, its scratch, the fp64 table
   size_t off_wmean, off_rmax, off_wpart, off_T, off_ext;
 };
@@ -79,6 +82,30 @@ size_t plan_duo(SearchPlan& p, int64_t d_out, int64_t d_in, int n_grid, size_t o
 
 constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
 
+// Output score in the second-moment form?  Forced by a flag, else taken when
+// its matrix-core work (H = X^T X once, then d_in^2 per scored row) is below
+// 0.8 of the direct form's (T d_in per scored row); the margin covers its
+// extra passes (transpose of X, H to fp16).
+// Its fp32 H and fp16 operands are addressed with 32-bit offsets.
+bool gram_fits(const SearchPlan& p) {
+  const double k = (double)p.K_pad;
+  return k * k < 2147483648.0 && (double)p.g_h_rows * k * 2.0 < 4294967296.0 &&
+         (double)p.g_xt_rows * (double)p.g_T_pad * 2.0 < 4294967296.0;
+}
+
+bool use_gram(const awq_search_cfg& cfg, const SearchPlan& p, int64_t T) {
+  (void)T;
+  if (cfg.flags & AWQ_FLAG_OUT_DIRECT) return false;
+  if (cfg.flags & AWQ_FLAG_OUT_GRAM) return true;
+  if (!gram_fits(p)) return false;
+  const double rows = (double)(cfg.n_grid + (cfg.n_clip >= 2 ? cfg.n_clip : 0)) * (double)p.d_out_pad;
+  const double k = (double)p.K_pad;
+  const double direct = (double)p.T_pad * k * rows;
+  const double gram = (double)p.g_T_pad * (double)p.g_h_rows * (double)((p.K_pad + 255) / 256 * 256) +
+                      (double)p.g_h_rows * k * rows;
+  return gram < 0.8 * direct;
+}
+
 SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, int64_t T) {
   SearchPlan p{};
   p.output = cfg.score == AWQ_SCORE_OUTPUT;
@@ -95,7 +122,9 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     off += align256((size_t)p.n_blocks * cfg.n_grid * sizeof(float));
   } else {
     gemm_sq_pad(T, d_out, d_in, &p.T_pad, &p.d_out_pad, &p.K_pad);
-    p.n_mt = p.T_pad / gemm_sq_tile_rows();
+    gram_pad(T, p.K_pad, &p.g_T_pad, &p.g_xt_rows, &p.g_h_rows);
+    p.gram = use_gram(cfg, p, T);
+    p.n_mt = (p.gram ? p.g_h_rows : p.T_pad) / gemm_sq_tile_rows();
     p.n_x = absmax_blocks(T);
     p.n_db = build_dw_blocks(cfg.group_size, d_out, d_in);
     const int max_c = cfg.n_grid > cfg.n_clip ? cfg.n_grid : cfg.n_clip;
@@ -105,8 +134,19 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     if (chunk > max_c) chunk = max_c;
     if (chunk < 1) chunk = 1;
     p.cand_chunk = (int)chunk;
-    p.off_x16 = off;
-    off += align256((size_t)p.T_pad * p.K_pad * sizeof(uint16_t));
+    p.off_x16 = off;  // X16 [T_pad, K_pad], or Xt [g_xt_rows, g_T_pad] in the second-moment form
+    off += align256(p.gram ? (size_t)p.g_xt_rows * p.g_T_pad * sizeof(uint16_t)
+                           : (size_t)p.T_pad * p.K_pad * sizeof(uint16_t));
+    if (p.gram) {
+      p.off_h32 = off;
+      off += align256((size_t)p.K_pad * p.K_pad * sizeof(float));
+      p.off_h16 = off;
+      off += align256((size_t)p.g_h_rows * p.K_pad * sizeof(uint16_t));
+      p.off_hc = off;
+      off += align256((size_t)p.K_pad * sizeof(float));
+      p.off_hr = off;
+      off += align256((size_t)p.K_pad * sizeof(float));
+    }
     p.off_dw = off;
     off += align256(per_cand * chunk);
     p.off_part = off;
@@ -150,8 +190,10 @@ awq_status check_cfg(const awq_search_cfg* cfg) {
     if (!(cfg->clip_lo > 0.0f && cfg->clip_lo <= 1.0f)) return fail(AWQ_EINVAL, "clip_lo %g not in (0,1]", (double)cfg->clip_lo);
   }
   if (!(cfg->s_min > 0.0 && isfinite(cfg->s_min))) return fail(AWQ_EINVAL, "s_min must be positive and finite");
-  if (cfg->flags & ~(AWQ_FLAG_DUO | AWQ_FLAG_ASYM))
+  if (cfg->flags & ~(AWQ_FLAG_DUO | AWQ_FLAG_ASYM | AWQ_FLAG_OUT_DIRECT | AWQ_FLAG_OUT_GRAM))
     return fail(AWQ_EINVAL, "flags 0x%x: unknown bits", (unsigned)cfg->flags);
+  if ((cfg->flags & AWQ_FLAG_OUT_DIRECT) && (cfg->flags & AWQ_FLAG_OUT_GRAM))
+    return fail(AWQ_EINVAL, "AWQ_FLAG_OUT_DIRECT and AWQ_FLAG_OUT_GRAM exclude each other");
   return AWQ_OK;
 }
 
@@ -357,6 +399,8 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   }
   if (cfg->n_clip >= 2 && !clip) return fail(AWQ_EINVAL, "clip is NULL but n_clip >= 2");
   const SearchPlan plan = plan_search(*cfg, d_out, d_in, T);
+  if (plan.output && plan.gram && !gram_fits(plan))
+    return fail(AWQ_ESHAPE, "second-moment output score needs d_in^2 and T*d_in below 2^31 elements");
   if (!ws || ws_bytes < plan.total) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, plan.total);
   if ((uintptr_t)ws & 255u) return fail(AWQ_EALIGN, "ws not 256-byte aligned");
 
@@ -391,25 +435,43 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   OutScales* sc_c = (OutScales*)(base + plan.off_sc + align256(sizeof(OutScales)));
   const int G = cfg->group_size;
   const int64_t dop = plan.d_out_pad, kp = plan.K_pad;
+  // second-moment form: H = X^T X once, dW columns scaled by hc = sqrt(diag H)
+  const float* hc = plan.gram ? (const float*)(base + plan.off_hc) : nullptr;
+  const uint16_t* h16 = plan.gram ? (const uint16_t*)(base + plan.off_h16) : nullptr;
+  auto product = [&](int64_t n_cols, float* part) -> hipError_t {
+    return plan.gram ? launch_gemm_gram(h16, plan.g_h_rows, kp, dw, n_cols, part, plan.ldc, s)
+                     : launch_gemm_sq(x16, plan.T_pad, kp, dw, n_cols, part, plan.ldc, s);
+  };
   if ((e = launch_cands(*cfg, plan, parts, d_out, d_in, x_mean, base, S, nullptr, s)) != hipSuccess)
     return hip_status(e, "candidates");
   if ((e = launch_prepare_x(X, bf16, T, d_in, ld_x, xmax, s)) != hipSuccess) return hip_status(e, "absmax(X)");
-  if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, dmax,
-                           nullptr, s)) != hipSuccess)
+  if (plan.gram) {
+    if ((e = launch_out_scales(xmax, plan.n_x, nullptr, 0, 1, sc_a, s)) != hipSuccess)
+      return hip_status(e, "out_scales(X)");
+    if ((e = launch_transpose_x(X, bf16, T, d_in, ld_x, plan.g_T_pad, plan.g_xt_rows, sc_a, x16, s)) != hipSuccess)
+      return hip_status(e, "transpose_x");
+    float* h32 = (float*)(base + plan.off_h32);
+    if ((e = launch_gemm_gram_h(x16, plan.g_T_pad, kp, h32, s)) != hipSuccess) return hip_status(e, "gemm(H)");
+    if ((e = launch_gram_scale(h32, kp, plan.g_h_rows, (float*)(base + plan.off_hc), (float*)(base + plan.off_hr),
+                               (uint16_t*)h16, s)) != hipSuccess)
+      return hip_status(e, "gram_scale");
+  }
+  if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, hc,
+                           dmax, nullptr, s)) != hipSuccess)
     return hip_status(e, "build_dw(max)");
   if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, cfg->n_grid, sc_a, s)) != hipSuccess)
     return hip_status(e, "out_scales");
-  if ((e = launch_convert_x(X, bf16, T, d_in, ld_x, plan.T_pad, kp, sc_a, x16, s)) != hipSuccess)
+  if (!plan.gram && (e = launch_convert_x(X, bf16, T, d_in, ld_x, plan.T_pad, kp, sc_a, x16, s)) != hipSuccess)
     return hip_status(e, "convert_x");
   const bool one_chunk = plan.cand_chunk >= cfg->n_grid;
   if (!one_chunk) mark(true, s);
   for (int c0 = 0; c0 < cfg->n_grid; c0 += plan.cand_chunk) {
     const int nc = (cfg->n_grid - c0) < plan.cand_chunk ? (cfg->n_grid - c0) : plan.cand_chunk;
-    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, nullptr, dw, s)) !=
-        hipSuccess)
+    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, hc, nullptr,
+                             dw, s)) != hipSuccess)
       return hip_status(e, "build_dw");
     if (one_chunk) mark(true, s);
-    e = launch_gemm_sq(x16, plan.T_pad, kp, dw, (int64_t)nc * dop, colpart + (int64_t)c0 * dop, plan.ldc, s);
+    e = product((int64_t)nc * dop, colpart + (int64_t)c0 * dop);
     if (one_chunk) mark(false, s);
     if (e != hipSuccess) return hip_status(e, "gemm_sq");
   }
@@ -424,17 +486,16 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   if (cfg->n_clip >= 2) {
     const int nclip = cfg->n_clip;
     if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0,
-                             nullptr, dmax, nullptr, s)) != hipSuccess)
+                             nullptr, hc, dmax, nullptr, s)) != hipSuccess)
       return hip_status(e, "build_dw(clip max)");
     if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, nclip, sc_c, s)) != hipSuccess)
       return hip_status(e, "out_scales(clip)");
     for (int c0 = 0; c0 < nclip; c0 += plan.cand_chunk) {
       const int nc = (nclip - c0) < plan.cand_chunk ? (nclip - c0) : plan.cand_chunk;
-      if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0, sc_c,
-                               nullptr, dw, s)) != hipSuccess)
+      if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0,
+                               sc_c, hc, nullptr, dw, s)) != hipSuccess)
         return hip_status(e, "build_dw(clip)");
-      if ((e = launch_gemm_sq(x16, plan.T_pad, kp, dw, (int64_t)nc * dop, colpart + (int64_t)c0 * dop, plan.ldc, s)) !=
-          hipSuccess)
+      if ((e = product((int64_t)nc * dop, colpart + (int64_t)c0 * dop)) != hipSuccess)
         return hip_status(e, "gemm_sq(clip)");
     }
     if ((e = launch_clip_select(colpart, plan.n_mt, plan.ldc, d_out, dop, nclip, cfg->clip_lo, sc_c, clip, clip_err,

@@ -57,14 +57,27 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 //   dw == nullptr: per-block max |dW_c| -> dmax [n_cand, build_dw_blocks(G, d_out, d_in)]
 //   dw != nullptr: dw[c - cand0] = fp16(dW_c * sc->ds[c]), [d_out_pad, K_pad] each, zero padded
 int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in);
+//   cs != nullptr: column i of every dW_c is multiplied by cs[i] first (second-moment form)
 hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
                            int64_t d_out_pad, int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best,
-                           int n_clip, float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
-                           hipStream_t stream);
+                           int n_clip, float clip_lo, int cand0, const OutScales* sc, const float* cs, float* dmax,
+                           uint16_t* dw, hipStream_t stream);
 // gemm of squares on fp16 operands: Y = X16 [T_pad, K_pad] dw^T (dw: [n_cols, K_pad]);
 // colpart[mt * ldc + n] = sum over the 384 tokens of tile mt of Y[t, n]^2
 hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                           float* colpart, int64_t ldc, hipStream_t stream);
+// second-moment form: Xt [xt_rows, T_pad] = fp16(X^T xs); H32 = Xt Xt^T [K_pad, K_pad];
+// c = sqrt(diag H), r = 1 / c; H16 [h_rows, K_pad] = fp16(r_i H_ij r_j);
+// colpart[mt * ldc + n] = tile mt's share of dw_n H16 dw_n^T (dw built with cs = c)
+void gram_pad(int64_t T, int64_t K_pad, int64_t* T_pad, int64_t* xt_rows, int64_t* h_rows);
+hipError_t launch_transpose_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,
+                              int64_t rows_pad, const OutScales* sc, uint16_t* Xt, hipStream_t stream);
+hipError_t launch_gemm_gram_h(const uint16_t* Xt, int64_t T_pad, int64_t K_pad, float* H32, hipStream_t stream);
+hipError_t launch_gram_scale(const float* H32, int64_t K_pad, int64_t h_rows, float* c, float* r, uint16_t* H16,
+                             hipStream_t stream);
+hipError_t launch_gemm_gram(const uint16_t* H16, int64_t h_rows, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
+                            float* colpart, int64_t ldc, hipStream_t stream);
+// scales: with dmax == nullptr only sc->xs is set
 // chunk_sum[c, ch] = sum_mt sum_{o in chunk ch, o < d_out} colpart[mt * ldc + c * d_out_pad + o]
 // (fp64, fixed order), [n_cand, reduce_cols_chunks(d_out)]
 int64_t reduce_cols_chunks(int64_t d_out);

@@ -49,11 +49,14 @@ __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_lo) {
 // A block loads its tile of W once and takes the launch's candidates
 // cand0 + blockIdx.y, + gridDim.y, ... in turn, so W is read once per
 // candidate slice instead of once per candidate.
-template <int G, bool WRITE, bool ASYM>
+// COLS: every column i of dW_c is multiplied by cs[i] before the maximum and
+//   the fp16 rounding (the second-moment form's sqrt(H_ii), see section 2b).
+template <int G, bool WRITE, bool ASYM, bool COLS>
 __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int64_t d_out_pad, int64_t K_pad, int mode,
     const float* __restrict__ S, const float* __restrict__ s_best, int n_clip, float clip_lo, int cand0, int n_cand,
-    const OutScales* __restrict__ sc, float* __restrict__ dmax, uint16_t* __restrict__ dw) {
+    const OutScales* __restrict__ sc, const float* __restrict__ cs, float* __restrict__ dmax,
+    uint16_t* __restrict__ dw) {
   constexpr int LPG = G / 16;
   constexpr int RS = kDwThreads / LPG;
   const int64_t n_gcol = d_in / G;
@@ -76,6 +79,14 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) w[j] = 0.0f;
+  }
+  float cv[16];
+  if constexpr (COLS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 t = ((const float4*)(cs + col))[j];
+      cv[4 * j] = t.x; cv[4 * j + 1] = t.y; cv[4 * j + 2] = t.z; cv[4 * j + 3] = t.w;
+    }
   }
   for (int ci = blockIdx.y; ci < n_cand; ci += gridDim.y) {
     const int c = cand0 + ci;
@@ -124,7 +135,8 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
       // fma and the hardware reciprocal of s: within a few fp32 ulp of
       // RN(RN(q * step) / s) - w, far below the fp16 rounding of the operand
       // (the codes q themselves are exact)
-      const float d = __builtin_fmaf(n, step, -v[j]) * __builtin_amdgcn_rcpf(sv[j]);
+      float d = __builtin_fmaf(n, step, -v[j]) * __builtin_amdgcn_rcpf(sv[j]);
+      if constexpr (COLS) d *= cv[j];
       if constexpr (WRITE) {
         const uint32_t b = f2h_bits(d * dsc);       // exact scaling by 2^e, one rounding
         if (j & 1) outw[j >> 1] |= b << 16;
@@ -171,18 +183,20 @@ int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in) {
 
 hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
                            int64_t d_out_pad, int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best,
-                           int n_clip, float clip_lo, int cand0, const OutScales* sc, float* dmax, uint16_t* dw,
-                           hipStream_t stream) {
+                           int n_clip, float clip_lo, int cand0, const OutScales* sc, const float* cs, float* dmax,
+                           uint16_t* dw, hipStream_t stream) {
   // max pass: d_out rows; write pass: d_out_pad rows (zeros past d_out).  One
   // block per W tile takes all of the launch's candidates: measured 1.2%
   // faster on the fused-QKV output-score step than one block per tile and
   // candidate (W read once instead of n_cand times), 0.9% than four slices
   dim3 grid((unsigned)build_dw_blocks(group_size, dw == nullptr ? d_out : d_out_pad, d_in), 1u);
-#define AWQ_DW2(G, A)                                                                                  \
-  if (dw == nullptr) build_dw_kernel<G, false, A><<<grid, kDwThreads, 0, stream>>>(                      \
-      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, dmax, dw); \
-  else build_dw_kernel<G, true, A><<<grid, kDwThreads, 0, stream>>>(                                     \
-      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, dmax, dw);
+#define AWQ_DW3(G, A, C)                                                                                   \
+  if (dw == nullptr) build_dw_kernel<G, false, A, C><<<grid, kDwThreads, 0, stream>>>(                       \
+      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, cs, dmax, dw); \
+  else build_dw_kernel<G, true, A, C><<<grid, kDwThreads, 0, stream>>>(                                      \
+      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, cs, dmax, dw);
+#define AWQ_DW2(G, A) \
+  if (cs != nullptr) { AWQ_DW3(G, A, true) } else { AWQ_DW3(G, A, false) }
 #define AWQ_DW(G) \
   if (asym) { AWQ_DW2(G, true) } else { AWQ_DW2(G, false) }
   switch (group_size) {
@@ -192,6 +206,7 @@ hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64
   }
 #undef AWQ_DW
 #undef AWQ_DW2
+#undef AWQ_DW3
   return hipGetLastError();
 }
 
@@ -249,6 +264,10 @@ __global__ __launch_bounds__(256) void out_scales_kernel(const float* __restrict
   __shared__ float red[256];
   const int c = blockIdx.x;
   const float xs = pow2_scale_for(block_max256(xmax, n_x, red));
+  if (dmax == nullptr) {  // xs alone (one block)
+    if (threadIdx.x == 0) sc->xs = xs;
+    return;
+  }
   const float ds = pow2_scale_for(block_max256(dmax + (int64_t)c * n_d, n_d, red));
   if (threadIdx.x == 0) {
     if (c == 0) sc->xs = xs;
@@ -295,7 +314,7 @@ hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
 
 hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
                              OutScales* sc, hipStream_t stream) {
-  out_scales_kernel<<<n_cand, 256, 0, stream>>>(xmax_part, n_x, dmax, n_d, sc);
+  out_scales_kernel<<<dmax == nullptr ? 1 : n_cand, 256, 0, stream>>>(xmax_part, n_x, dmax, n_d, sc);
   return hipGetLastError();
 }
 
@@ -306,6 +325,59 @@ hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, i
   if (nb > 8192) nb = 8192;
   if (bf16) convert_x_kernel<true><<<(unsigned)nb, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, T_pad, K_pad, sc, X16);
   else convert_x_kernel<false><<<(unsigned)nb, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, T_pad, K_pad, sc, X16);
+  return hipGetLastError();
+}
+
+// Xt [rows_pad, T_pad] = fp16(X^T * xs), zeros in rows >= cols (channels) and
+// columns >= rows (tokens): the token axis becomes the contraction axis of
+// H = X^T X.  64 x 64 tiles through LDS: coalesced 16-byte reads along the
+// channels, coalesced 16-byte writes along the tokens.
+template <bool BF16>
+__global__ __launch_bounds__(256) void transpose_x_kernel(const uint16_t* __restrict__ X, int64_t rows, int64_t cols,
+                                                         int64_t ld, int64_t T_pad, const OutScales* __restrict__ sc,
+                                                         uint16_t* __restrict__ Xt) {
+  __shared__ uint16_t tile[64][64 + 2];  // [token][channel]; odd word stride spreads the column reads
+  const float xs = sc->xs;
+  const int64_t t0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const int rr = tid >> 3, cc = (tid & 7) * 8;  // 32 rows x 8 chunks of 8 per pass
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t t = t0 + rr + 32 * h, c = c0 + cc;
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (t < rows && c < cols) {  // cols is a multiple of 8
+      const uint4 u = ld_nt(X + t * ld + c);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = BF16 ? bf2f((uint16_t)(w[j] & 0xFFFFu)) : h2f((uint16_t)(w[j] & 0xFFFFu));
+        const float hi = BF16 ? bf2f((uint16_t)(w[j] >> 16)) : h2f((uint16_t)(w[j] >> 16));
+        o[j] = (uint32_t)f2h_bits(lo * xs) | ((uint32_t)f2h_bits(hi * xs) << 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[rr + 32 * h][cc + 2 * j] = (uint16_t)(o[j] & 0xFFFFu);
+      tile[rr + 32 * h][cc + 2 * j + 1] = (uint16_t)(o[j] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ch = rr + 32 * h, tt = cc;  // output row = channel, 8 tokens from tt
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = (uint32_t)tile[tt + 2 * j][ch] | ((uint32_t)tile[tt + 2 * j + 1][ch] << 16);
+    *(uint4*)(Xt + (c0 + ch) * T_pad + t0 + tt) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_transpose_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,
+                              int64_t rows_pad, const OutScales* sc, uint16_t* Xt, hipStream_t stream) {
+  const dim3 grid((unsigned)(T_pad / 64), (unsigned)(rows_pad / 64));
+  if (bf16) transpose_x_kernel<true><<<grid, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, T_pad, sc, Xt);
+  else transpose_x_kernel<false><<<grid, 256, 0, stream>>>((const uint16_t*)X, T, d_in, ld_x, T_pad, sc, Xt);
   return hipGetLastError();
 }
 
@@ -393,11 +465,20 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* B
   }
 }
 
+// Epilogues of the block's 384 x 256 product C (rows m of A, columns n of B):
+//   kEpiSq:    colpart[mt * ldc + n] = sum over the tile's rows of C[m, n]^2
+//   kEpiGram:  colpart[mt * ldc + n] = sum over the tile's rows m < lim of
+//              C[m, n] * B[n, m]  (A = H' symmetric, B = dW': the row's
+//              quadratic form dW'_n H' dW'_n^T, one tile's share)
+//   kEpiStore: out[m * ldc + n] = C[m, n] for m, n < lim (H = Xt Xt^T in fp32)
+constexpr int kEpiSq = 0, kEpiGram = 1, kEpiStore = 2;
+
+template <int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                               uint32_t a_bytes, const uint16_t* __restrict__ B,
                                                               int64_t ldb, uint32_t b_bytes, int64_t K, int64_t n_mt,
                                                               int64_t n_nt, float* __restrict__ colpart, int64_t ldc,
-                                                              int group_m) {
+                                                              int group_m, int64_t lim) {
   __shared__ float red[4][kBN];
   const int64_t nblk = (int64_t)gridDim.x;
   const int64_t bid = blockIdx.x;
@@ -470,13 +551,54 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
 #undef AWQ_STAGE3
   __builtin_amdgcn_s_waitcnt(0x0070);  // no load in flight past this point
 
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float cs = 0.0f;
+  // accumulator element e of MFMA tile (i, j) holds C[m, n] with
+  // n = n0 + 128 wn + 32 j + lane % 32 and m = mrow(i) + 8 (e / 4) + e % 4
+  const int64_t mlane = m0 + wm * 96 + 4 * (lane >> 5);
+  if constexpr (EPI == kEpiStore) {
+    // 32-bit element offsets (the launcher keeps lim * ldc below 2^31)
+    const uint32_t ldo = (uint32_t)ldc;
+    const uint32_t nl = (uint32_t)(n0 + wn * 128 + (lane & 31));
 #pragma unroll
     for (int i = 0; i < 3; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t mb = (uint32_t)(mlane + i * 32 + 8 * g);  // a multiple of 4, lim a multiple of 64
+        if (mb >= (uint32_t)lim) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (nl + 32 * j >= (uint32_t)lim) continue;
+          float* p = colpart + (mb * ldo + nl + 32 * j);
+          p[0] = acc[i][j][4 * g];
+          p[ldo] = acc[i][j][4 * g + 1];
+          p[2 * ldo] = acc[i][j][4 * g + 2];
+          p[3 * ldo] = acc[i][j][4 * g + 3];
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float cs = 0.0f;
+    if constexpr (EPI == kEpiSq) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
+    } else {
+      const uint16_t* brow = B + (n0 + wn * 128 + j * 32 + (lane & 31)) * ldb;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t m = mlane + i * 32 + 8 * g;  // a multiple of 4, lim a multiple of 64
+          uint2 u = make_uint2(0u, 0u);
+          if (m < lim) u = *(const uint2*)(brow + m);
+          cs = __builtin_fmaf(acc[i][j][4 * g], h2f((uint16_t)(u.x & 0xFFFFu)), cs);
+          cs = __builtin_fmaf(acc[i][j][4 * g + 1], h2f((uint16_t)(u.x >> 16)), cs);
+          cs = __builtin_fmaf(acc[i][j][4 * g + 2], h2f((uint16_t)(u.y & 0xFFFFu)), cs);
+          cs = __builtin_fmaf(acc[i][j][4 * g + 3], h2f((uint16_t)(u.y >> 16)), cs);
+        }
+    }
     cs += __shfl_xor(cs, 32, kWave);
     if (lane < 32) red[wm][wn * 128 + j * 32 + lane] = cs;
   }
@@ -510,8 +632,90 @@ hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, con
                           float* colpart, int64_t ldc, hipStream_t stream) {
   const int64_t n_mt = T_pad / kBM, n_nt = n_cols / kBN;
   const uint32_t a_bytes = (uint32_t)(T_pad * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
-  gemm_sq_kernel<<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(X16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad,
-                                                                      n_mt, n_nt, colpart, ldc, gemm_group_m(K_pad));
+  gemm_sq_kernel<kEpiSq><<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(
+      X16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad, n_mt, n_nt, colpart, ldc, gemm_group_m(K_pad), 0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 2b. Second-moment form of the output score.  For one row o of the group,
+//   sum_t (X (W_hat - W)^T)[t, o]^2 = dW_o H dW_o^T,  H = X^T X  [d_in, d_in],
+// so H is formed once (2 T d_in^2 flops) and each candidate costs
+// 2 d_in^2 d_out instead of 2 T d_in d_out: fewer flops whenever
+// d_in (T + n d_out) < T n d_out for n scored candidates.  In fp16 on the
+// matrix cores H is taken as H' = R H R, R = diag(1 / sqrt(H_ii)) (entries in
+// [-1, 1], unit diagonal), and dW as dW' = ds dW diag(sqrt(H_ii)), so that
+// dW' H' dW'^T = ds^2 dW H dW^T exactly up to the roundings of the operands.
+// ---------------------------------------------------------------------------
+
+// Xt rows (channels) cover both operand tiles of the H product; H' rows cover
+// the 384-row tiles of the candidate product; the token axis is padded to 64
+void gram_pad(int64_t T, int64_t K_pad, int64_t* T_pad, int64_t* xt_rows, int64_t* h_rows) {
+  *T_pad = (T + 63) / 64 * 64;
+  const int64_t m = (K_pad + kBM - 1) / kBM * kBM, n = (K_pad + kBN - 1) / kBN * kBN;
+  *xt_rows = m > n ? m : n;
+  *h_rows = m;
+}
+
+// H32 [K_pad, K_pad] = Xt Xt^T (fp32, rows and columns < K_pad)
+hipError_t launch_gemm_gram_h(const uint16_t* Xt, int64_t T_pad, int64_t K_pad, float* H32, hipStream_t stream) {
+  int64_t tp, xr, hr;
+  gram_pad(T_pad, K_pad, &tp, &xr, &hr);
+  const int64_t n_mt = hr / kBM, n_nt = (K_pad + kBN - 1) / kBN;
+  const uint32_t bytes = (uint32_t)(xr * T_pad * 2);
+  gemm_sq_kernel<kEpiStore><<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(
+      Xt, T_pad, bytes, Xt, T_pad, bytes, T_pad, n_mt, n_nt, H32, K_pad, gemm_group_m(T_pad), K_pad);
+  return hipGetLastError();
+}
+
+// c[i] = sqrt(H_ii), r[i] = 1 / c[i] (0 for a channel that is zero in every token)
+__global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict__ H32, int64_t K_pad,
+                                                       float* __restrict__ c, float* __restrict__ r) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= K_pad) return;
+  const float h = H32[i * K_pad + i];
+  const float ci = h > 0.0f ? __builtin_sqrtf(h) : 0.0f;
+  c[i] = ci;
+  r[i] = ci > 0.0f ? 1.0f / ci : 0.0f;
+}
+
+// H16 [h_rows, K_pad] = fp16(H_ij r_i r_j), zero rows from K_pad on
+__global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict__ H32, int64_t K_pad, int64_t h_rows,
+                                                       const float* __restrict__ r, uint16_t* __restrict__ H16) {
+  const int64_t chunks = K_pad / 8, n = h_rows * chunks;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
+    const int64_t i = idx / chunks, j = (idx % chunks) * 8;
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (i < K_pad) {
+      const float ri = r[i];
+      const float4 h0 = *(const float4*)(H32 + i * K_pad + j), h1 = *(const float4*)(H32 + i * K_pad + j + 4);
+      const float4 r0 = *(const float4*)(r + j), r1 = *(const float4*)(r + j + 4);
+      const float v[8] = {h0.x * ri * r0.x, h0.y * ri * r0.y, h0.z * ri * r0.z, h0.w * ri * r0.w,
+                          h1.x * ri * r1.x, h1.y * ri * r1.y, h1.z * ri * r1.z, h1.w * ri * r1.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = (uint32_t)f2h_bits(v[2 * q]) | ((uint32_t)f2h_bits(v[2 * q + 1]) << 16);
+    }
+    *(uint4*)(H16 + i * K_pad + j) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_gram_scale(const float* H32, int64_t K_pad, int64_t h_rows, float* c, float* r, uint16_t* H16,
+                             hipStream_t stream) {
+  gram_diag_kernel<<<(unsigned)((K_pad + 255) / 256), 256, 0, stream>>>(H32, K_pad, c, r);
+  const int64_t n = h_rows * (K_pad / 8);
+  int64_t nb = (n + 255) / 256;
+  if (nb > 8192) nb = 8192;
+  gram_half_kernel<<<(unsigned)nb, 256, 0, stream>>>(H32, K_pad, h_rows, r, H16);
+  return hipGetLastError();
+}
+
+// colpart[mt * ldc + n] = the tile-mt share of dW'_n H' dW'_n^T over the n_cols stacked dW' rows
+hipError_t launch_gemm_gram(const uint16_t* H16, int64_t h_rows, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
+                            float* colpart, int64_t ldc, hipStream_t stream) {
+  const int64_t n_mt = h_rows / kBM, n_nt = n_cols / kBN;
+  const uint32_t a_bytes = (uint32_t)(h_rows * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
+  gemm_sq_kernel<kEpiGram><<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(
+      H16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad, n_mt, n_nt, colpart, ldc, gemm_group_m(K_pad), K_pad);
   return hipGetLastError();
 }
 

@@ -141,8 +141,11 @@ def test_search_validation(A):
     for c in bad:
         assert st_search(A, c, grp, X=FAKE, T=16, ld=256, clip=FAKE) == A.AWQ_EINVAL
     c = A._cfg(128, 20, "weight", 0, 0.5, 1e-4)
-    c.flags = 4
+    c.flags = 16                                   # no such flag
     assert st_search(A, c, grp) == A.AWQ_EINVAL
+    c.flags = A.AWQ_FLAG_OUT_DIRECT | A.AWQ_FLAG_OUT_GRAM
+    assert st_search(A, c, grp) == A.AWQ_EINVAL
+    assert "exclude" in A.lib().awq_last_error().decode()
     assert st_search(A, good, grp, d_in=200) == A.AWQ_ESHAPE
     assert st_search(A, good, grp, d_in=64) == A.AWQ_ESHAPE
     assert st_search(A, good, _group(A, [FAKE_MIS], [64])) == A.AWQ_EALIGN
@@ -186,6 +189,16 @@ def test_workspace_sizes(A):
     assert big < (3 << 30)                        # dW built in chunks of <= 2 GiB
     with pytest.raises(A.AwqError):
         A.search_workspace_bytes(4096, 4000)
+    # output score forms: the second-moment form holds X^T (as the direct form
+    # holds X), H in fp32 and fp16, and the same dW chunk
+    direct = A.search_workspace_bytes(6144, 4096, 16384, score="output", out_form="direct")
+    gram = A.search_workspace_bytes(6144, 4096, 16384, score="output", out_form="gram")
+    assert gram > direct + 4096 * 4096 * 4
+    assert A.search_workspace_bytes(6144, 4096, 16384, score="output") == gram   # the default choice here
+    assert A.search_workspace_bytes(6144, 4096, 64, score="output") == \
+        A.search_workspace_bytes(6144, 4096, 64, score="output", out_form="direct")
+    with pytest.raises(ValueError):
+        A.search_workspace_bytes(6144, 4096, 64, score="output", out_form="hessian")
 
 
 def test_norm_group_fold_validation(A):

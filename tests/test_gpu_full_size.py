@@ -46,15 +46,15 @@ def _sample_rows(part_rows, seed, n_inner=2):
     return np.array(sorted(set(int(x) for x in rows)))
 
 
-def _output_clip_full(A, wl_name, gi, G, T_limit=None):
+def _output_clip_full(A, wl_name, gi, G, T_limit=None, out_form="auto"):
     wl = WL.WORKLOADS[wl_name]
     grp = wl.groups[gi]
-    say(f"full size output+clip {wl_name} group {grp.name}: generating inputs")
+    say(f"full size output+clip {wl_name} group {grp.name} ({out_form} form): generating inputs")
     parts, X = WL.host_group_inputs(wl, 0, gi, T_limit=T_limit)
     xm = O.act_stats(X)
     say(f"  GPU search: rows {sum(p.shape[0] for p in parts)}, d_in {grp.d_in}, T {X.shape[0]}")
     res = A.search_scales([dev_f16(p) for p in parts], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
-                          n_clip=20, want_clip_err=True)
+                          n_clip=20, want_clip_err=True, out_form=out_form)
     g_err = host(res.err).astype(np.float64)
     k = int(host(res.best_idx)[0])
     # alpha search at full size: finite non-negative errors, first minimum taken,
@@ -89,11 +89,13 @@ def _output_clip_full(A, wl_name, gi, G, T_limit=None):
     assert np.array_equal(host(sc).view(np.uint16), rsc.view(np.uint16))
 
 
-def test_qkv_output_full_size_rows(A):
-    """Fused QKV, 6144 x 4096, 16384 tokens: the alpha-search GEMM launches
-    [16384 x 4096] x [4096 x 122880] as in the benchmark; the 20 errors
-    against the oracle's over the whole group."""
-    _output_clip_full(A, "qkv_6144x4096_output", 0, 128)
+@pytest.mark.parametrize("out_form", ["gram", "direct"])
+def test_qkv_output_full_size_rows(A, out_form):
+    """Fused QKV, 6144 x 4096, 16384 tokens, in both forms of the output score:
+    direct ([16384 x 4096] x [4096 x 122880]) and second-moment (H = X^T X,
+    then [4096 x 4096] x [4096 x 122880], the form the benchmark's default
+    choice takes here); the 20 errors against the oracle's over the whole group."""
+    _output_clip_full(A, "qkv_6144x4096_output", 0, 128, out_form=out_form)
 
 
 @pytest.mark.parametrize("duo,asym", [(True, False), (False, True)])
@@ -116,17 +118,20 @@ def test_qkv_output_full_size_duo_asym(A, duo, asym):
     assert ulp_dist(host(res.best_s), S[k]) <= 2
 
 
-def test_mlp_gate_up_output_clip_full_size_rows(A):
+@pytest.mark.parametrize("out_form", ["gram", "direct"])
+def test_mlp_gate_up_output_clip_full_size_rows(A, out_form):
     """MLP gate/up, 2 x 12288 x 4096, 16384 tokens, with the clip search: the dW
-    of the 20 candidates (4 GB) is built and multiplied in two chunks."""
-    _output_clip_full(A, "mlp_output_clip", 0, 128)
+    of the 20 candidates (4 GB) is built and multiplied in two chunks, in both
+    forms of the output score."""
+    _output_clip_full(A, "mlp_output_clip", 0, 128, out_form=out_form)
 
 
-def test_mlp_down_output_clip_rows(A):
-    """MLP down_proj, 4096 x 12288 (the K = 12288 GEMM), on the first 512
-    tokens of its synthetic input (the host oracle builds that input with two
-    fp32 matrix products)."""
-    _output_clip_full(A, "mlp_output_clip", 1, 128, T_limit=512)
+@pytest.mark.parametrize("out_form", ["direct", "gram"])
+def test_mlp_down_output_clip_rows(A, out_form):
+    """MLP down_proj, 4096 x 12288 (the K = 12288 GEMM; a 12288 x 12288 H in the
+    second-moment form), on the first 512 tokens of its synthetic input (the
+    host oracle builds that input with two fp32 matrix products)."""
+    _output_clip_full(A, "mlp_output_clip", 1, 128, T_limit=512, out_form=out_form)
 
 
 @pytest.mark.parametrize("rows,d_in,G,n_blk", [

@@ -1,0 +1,128 @@
+"""GPU parity of the output score in its second-moment form.
+
+For one output row o the output error of a candidate is
+sum_t (X (W_hat - W)^T)[t, o]^2 = dW_o (X^T X) dW_o^T, so the device may form
+H = X^T X once and score every candidate against H instead of against X
+("AWQ architecture, in depth", The scale search as code: the group's output
+error; the identity is the expansion of the sum of squares).  The form is
+forced here with out_form="gram" on shapes that span several tiles of H and a
+ragged tail (d_in not a multiple of the 384-row tile, token counts not a
+multiple of 64), and each result is compared with the oracle's plain
+definition at the output-score bars: errors within 1e-3 relative, the chosen
+index equal unless the oracle's errors tie within 1e-4 relative; per-row clip
+errors within 1e-3 and the clip choice under the same tie rule.
+"""
+import numpy as np
+import pytest
+
+from oracle import awq_oracle as O
+import workloads as WL
+from tests._util import argmin_ok, dev_f16, dev_f32, dev_x, host, say, ulp_dist
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import post_weight_quantization_awq_amd as A
+    A.lib()
+    return A
+
+
+@pytest.mark.parametrize("parts,d_in,T,G,xdt", [
+    ([64], 256, 150, 128, "bf16"),         # one H tile, ragged tokens
+    ([136], 384, 70, 64, "f16"),           # d_in equal to the 384-row tile
+    ([24, 0, 40], 256, 60, 128, "bf16"),   # parts with an empty one
+    ([272], 96, 385, 32, "bf16"),          # d_in padded 96 -> 128, 385 tokens
+    ([520], 1024, 1000, 128, "bf16"),      # three H row tiles, the last ragged
+    ([300, 212], 2048, 700, 64, "f16"),    # six H row tiles
+])
+def test_search_output_gram(A, parts, d_in, T, G, xdt):
+    say(f"search output (second-moment form) parts={parts} d_in={d_in} T={T} G={G} {xdt}")
+    Ws = [WL.make_weight(900 + 5 * i + T, r, d_in) for i, r in enumerate(parts)]
+    X = WL.make_activations(950 + T, T, d_in, xdt)
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          out_form="gram")
+    errs, k, _ = O.search_scales(Ws, xm, G, 20, "output", X=X)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
+
+
+@pytest.mark.parametrize("duo,asym", [(True, False), (False, True), (True, True)])
+def test_search_output_gram_duo_asym(A, duo, asym):
+    parts, d_in, T, G = [200, 56], 512, 333, 128
+    say(f"search output (second-moment form) duo={duo} asym={asym}")
+    Ws = [WL.make_weight(1100 + i, r, d_in) for i, r in enumerate(parts)]
+    X = WL.make_activations(1150, T, d_in, "bf16")
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          duo=duo, asym=asym, out_form="gram")
+    errs, k, _ = O.search_scales(Ws, xm, G, 20, "output", X=X, duo=duo, asym=asym)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
+
+
+@pytest.mark.parametrize("parts,d_in,T,G,asym", [([64], 256, 150, 128, False), ([272], 128, 385, 64, False),
+                                                 ([136], 384, 70, 64, True)])
+def test_clip_search_gram(A, parts, d_in, T, G, asym):
+    d_out = sum(parts)
+    say(f"clip search (second-moment form) parts={parts} d_in={d_in} T={T} G={G} asym={asym}")
+    Ws = [WL.make_weight(1200 + d_out + 3 * i, r, d_in) for i, r in enumerate(parts)]
+    W = np.concatenate(Ws, axis=0)
+    X = WL.make_activations(1250 + d_out, T, d_in, "bf16")
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          n_clip=20, want_clip_err=True, asym=asym, out_form="gram")
+    errs, k, _ = O.search_scales([W], xm, G, 20, "output", X=X, asym=asym)
+    g_k = int(host(res.best_idx)[0])
+    assert argmin_ok(g_k, errs, k)
+    s = O.candidate_scales(xm, 20)[g_k]
+    assert ulp_dist(host(res.best_s), s) <= 2
+    E, _ = O.clip_search(W, s, X, G, 20, 0.5, asym=asym)
+    np.testing.assert_allclose(host(res.clip_err).astype(np.float64), E, rtol=1e-3)
+    g_c = host(res.clip)
+    ratios = O.clip_ratios(20, 0.5)
+    for o in range(d_out):
+        gj = int(np.nonzero(ratios == g_c[o])[0][0])
+        assert argmin_ok(gj, E[o], O.first_argmin(E[o]), rel=1e-4), o
+
+
+def test_output_forms_agree_and_auto(A):
+    """4096 tokens over 256 inputs: the library's own choice is the
+    second-moment form there (its work is a fraction of the direct form's),
+    so the default call and out_form="gram" return the same bits; the direct
+    form agrees with both at the output-score bar, and all three with the oracle."""
+    d_out, d_in, T, G = 512, 256, 4096, 128
+    say("output forms: auto vs gram vs direct")
+    W = WL.make_weight(1301, d_out, d_in)
+    X = WL.make_activations(1302, T, d_in, "bf16")
+    xm = O.act_stats(X)
+    args = ([dev_f16(W)], dev_f32(xm))
+    kw = dict(group_size=G, score="output", X=dev_x(X))
+    r_auto = A.search_scales(*args, **kw)
+    r_gram = A.search_scales(*args, out_form="gram", **kw)
+    r_dir = A.search_scales(*args, out_form="direct", **kw)
+    assert np.array_equal(host(r_auto.err), host(r_gram.err))
+    errs, k, _ = O.search_scales([W], xm, G, 20, "output", X=X)
+    for r in (r_gram, r_dir):
+        np.testing.assert_allclose(host(r.err).astype(np.float64), errs, rtol=1e-3)
+        assert argmin_ok(int(host(r.best_idx)[0]), errs, k)
+
+
+def test_gram_dead_channel(A):
+    """An input channel that is zero in every token has H_ii = 0: its column of
+    dW and its row and column of H drop out (scale 0), as they do from X dW^T."""
+    d_out, d_in, T, G = 128, 256, 200, 128
+    say("second-moment form with a dead input channel")
+    W = WL.make_weight(1401, d_out, d_in)
+    X = WL.make_activations(1402, T, d_in, "f16")
+    X[:, 7] = 0
+    X[:, 200] = 0
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(W)], dev_f32(xm), group_size=G, score="output", X=dev_x(X), out_form="gram")
+    errs, k, _ = O.search_scales([W], xm, G, 20, "output", X=X)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
