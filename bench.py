@@ -558,7 +558,8 @@ def bench_output(args, wl_name: str):
         xm = torch.empty(grp.d_in, dtype=torch.float32, device=dev)
         ws_stats = A.workspace(A.act_stats_workspace_bytes(X.shape[0], grp.d_in), dev)
         ws = A.workspace(A.search_workspace_bytes(d_out, grp.d_in, X.shape[0], group_size=G, score="output",
-                                                  n_clip=wl.n_clip, duo=args.duo, asym=args.asym), dev)
+                                                  n_clip=wl.n_clip, duo=args.duo, asym=args.asym,
+                                                  out_form=args.out_form), dev)
         res = A.SearchResult(torch.empty(20, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                              torch.empty(grp.d_in, device=dev),
                              torch.empty(d_out, device=dev) if wl.n_clip else None, None)
@@ -567,7 +568,7 @@ def bench_output(args, wl_name: str):
                   torch.empty((grp.d_in // G, p.shape[0] // 8), dtype=torch.int32, device=dev)) for p in parts]
         sp = A.ActStatsPlan(X, x_mean=xm, ws=ws_stats)
         qp = A.SearchPlan(parts, xm, group_size=G, score="output", X=X, n_clip=wl.n_clip, ws=ws, out=res,
-                          duo=args.duo, asym=args.asym)
+                          duo=args.duo, asym=args.asym, out_form=args.out_form)
         pps, off = [], 0
         for p, o in zip(parts, packs):
             clip = res.clip[off:off + p.shape[0]] if res.clip is not None else None
@@ -606,11 +607,27 @@ def bench_output(args, wl_name: str):
     gemm_ms = [sum(ev.ms(2 * (k * n_pl + i), 2 * (k * n_pl + i) + 1) for k in range(K)) / K for i in range(n_pl)]
     ev.close()
     n_elem_pts = sum(g.d_out * g.d_in for _, _, g, *_ in plans) * 20
-    flops_alpha = [2.0 * X.shape[0] * g.d_out * g.d_in * 20 for _, X, g, *_ in plans]
-    # the events bracket the alpha-search GEMMs (with their dW builds when chunked)
-    tflops = sum(flops_alpha) / (sum(gemm_ms) * 1e-3) / 1e12
+    # the form the library takes per group: "direct" contracts X with each
+    # candidate's dW (2 T d_in flops per scored row); "gram" forms H = X^T X once
+    # and scores each row against it, both on and right of H's diagonal
+    # 384-blocks only (H is symmetric): 2 tri(d_in) flops per scored row and
+    # 2 T tri(d_in) for H, tri(d) = sum over blocks I of rows(I) (d - 384 I)
+    forms = [A.search_output_form(g.d_out, g.d_in, X.shape[0], group_size=G, n_clip=wl.n_clip, duo=args.duo,
+                                  asym=args.asym, out_form=args.out_form) for _, X, g, *_ in plans]
     n_gemm = 20 + (wl.n_clip or 0)
-    total_flops = sum(2.0 * X.shape[0] * g.d_out * g.d_in * n_gemm for _, X, g, *_ in plans)
+
+    def tri(d):
+        return float(sum(min(384, d - b) * (d - b) for b in range(0, d, 384)))
+
+    def row_flops(X, g, form):  # per scored output row
+        return 2.0 * (tri(g.d_in) if form == "gram" else X.shape[0] * g.d_in)
+
+    # the events bracket the alpha-search products (with their dW builds when chunked)
+    flops_alpha = [row_flops(X, g, f) * g.d_out * 20 for (_, X, g, *_), f in zip(plans, forms)]
+    tflops = sum(flops_alpha) / (sum(gemm_ms) * 1e-3) / 1e12
+    total_flops = sum(row_flops(X, g, f) * g.d_out * n_gemm + (2.0 * X.shape[0] * tri(g.d_in) if f == "gram" else 0.0)
+                      for (_, X, g, *_), f in zip(plans, forms))
+    direct_flops = sum(2.0 * X.shape[0] * g.d_out * g.d_in * n_gemm for _, X, g, *_ in plans)
     out = {
         "metric": METRIC,
         "value": n_elem_pts / (ms_step * 1e-3),
@@ -620,12 +637,15 @@ def bench_output(args, wl_name: str):
         "dtype": "f16-mfma/f32", "data": "synthetic",
         "config": {"workload": wl_name, "groups": [[g.name, g.d_out, g.d_in, X.shape[0]] for _, X, g, *_ in plans],
                    "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip, "duo": args.duo,
-                   "asym": args.asym},
-        "step_TFLOPs_algorithmic": total_flops / (ms_step * 1e-3) / 1e12,
+                   "asym": args.asym, "out_form": args.out_form},
+        "output_forms": forms,
+        "step_TFLOPs_performed": total_flops / (ms_step * 1e-3) / 1e12,
+        "step_TFLOPs_direct_equivalent": direct_flops / (ms_step * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_FP16_PEAK_TFLOPS, "traffic": pmc_traffic("gemm_sq_kernel", wl_name, args),
-                     "kernel": "gemm_sq_kernel"},
+                     "frac": tflops / MFMA_FP16_PEAK_TFLOPS,
+                     "traffic": pmc_traffic("gemm_sq_kernel", wl_name, args) if set(forms) == {"direct"} else None,
+                     "kernel": "gemm_sq_kernel<" + ",".join("1" if f == "gram" else "0" for f in forms) + ">"},
     }
     if power is not None:
         out["power"] = power
@@ -1493,6 +1513,9 @@ def main() -> int:
                     help="sweep schedule: the statistics on a stream of their own running ahead of the searches "
                          "on two streams (pipeline), blocks round-robin over the streams (blocks), or one "
                          "stream per group kind (groups)")
+    ap.add_argument("--out-form", choices=["auto", "direct", "gram"], default="auto",
+                    help="output-score form: the library's choice, X times each candidate's dW, or the "
+                         "second-moment form dW (X^T X) dW^T")
     ap.add_argument("--duo", action="store_true",
                     help="duo-scaling candidates (x_mean^r / (w_mean^(1-r) + 1e-4)) in the search workloads")
     ap.add_argument("--asym", action="store_true",

@@ -237,6 +237,14 @@ awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, in
  * ------------------------------------------------------------------------- */
 awq_status awq_search_workspace(const awq_search_cfg* cfg /* [host] */, int64_t d_out_total,
                                 int64_t d_in, int64_t T, size_t* bytes /* [host] */);
+/* Which form awq_search_scales takes for the output score with these
+ * arguments: *form = AWQ_OUT_FORM_DIRECT or AWQ_OUT_FORM_GRAM (see
+ * AWQ_FLAG_OUT_*).  Host only, enqueues nothing; AWQ_EINVAL unless
+ * cfg->score = AWQ_SCORE_OUTPUT, shape errors as awq_search_workspace. */
+#define AWQ_OUT_FORM_DIRECT 0
+#define AWQ_OUT_FORM_GRAM 1
+awq_status awq_search_output_form(const awq_search_cfg* cfg /* [host] */, int64_t d_out_total, int64_t d_in,
+                                  int64_t T, int32_t* form /* [host] */);
 awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_wgroup* W /* [host] */,
                              int64_t d_in, const float* x_mean,
                              const void* X, int32_t x_dtype, int64_t T, int64_t ld_x,

@@ -40,7 +40,7 @@ STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_EINVAL", 2: "AWQ_ESHAPE", 3: "AWQ_EDTYPE",
                 4: "AWQ_EWORKSPACE", 5: "AWQ_EALIGN", 6: "AWQ_EHIP"}
 
 EXPORTED = ("awq_act_stats_workspace", "awq_act_stats", "awq_candidate_scales_workspace", "awq_candidate_scales",
-            "awq_search_workspace", "awq_search_scales", "awq_quantize_pack", "awq_quantize_pack_asym",
+            "awq_search_workspace", "awq_search_output_form", "awq_search_scales", "awq_quantize_pack", "awq_quantize_pack_asym",
             "awq_unpack_dequant", "awq_norm_group_fold", "awq_weight_channel_mean_workspace",
             "awq_weight_channel_mean", "awq_candidate_scales_duo_workspace", "awq_candidate_scales_duo",
             "awq_w4a16_workspace", "awq_w4a16_matmul", "awq_search_scales_noalloc",
@@ -78,6 +78,7 @@ def _load() -> ctypes.CDLL:
         "awq_candidate_scales_workspace": [I64, I32, PSZ],
         "awq_candidate_scales": [P, I64, I32, F64, P, P, SZ, P],
         "awq_search_workspace": [ctypes.POINTER(SearchCfg), I64, I64, I64, PSZ],
+        "awq_search_output_form": [ctypes.POINTER(SearchCfg), I64, I64, I64, ctypes.POINTER(I32)],
         "awq_search_scales": [ctypes.POINTER(SearchCfg), ctypes.POINTER(WGroup), I64, P, P, I32, I64, I64,
                               P, P, P, P, P, P, SZ, P],
         "awq_quantize_pack": [P, I64, I64, I32, P, P, P, P, P, P],
@@ -318,6 +319,16 @@ def search_workspace_bytes(d_out: int, d_in: int, T: int = 0, *, group_size: int
     n = ctypes.c_size_t()
     _check(lib().awq_search_workspace(ctypes.byref(cfg), d_out, d_in, T, ctypes.byref(n)))
     return n.value
+
+
+def search_output_form(d_out: int, d_in: int, T: int, *, group_size: int = 128, n_grid: int = 20, n_clip: int = 0,
+                       clip_lo: float = 0.5, s_min: float = 1e-4, duo: bool = False, asym: bool = False,
+                       out_form: str = "auto") -> str:
+    """The form the output-score search takes for these arguments: "direct" or "gram"."""
+    cfg = _cfg(group_size, n_grid, "output", n_clip, clip_lo, s_min, duo, asym, out_form)
+    f = ctypes.c_int32()
+    _check(lib().awq_search_output_form(ctypes.byref(cfg), d_out, d_in, T, ctypes.byref(f)))
+    return "gram" if f.value == 1 else "direct"
 
 
 class SearchPlan(_Prepared):

@@ -99,10 +99,16 @@ bool use_gram(const awq_search_cfg& cfg, const SearchPlan& p, int64_t T) {
   if (cfg.flags & AWQ_FLAG_OUT_GRAM) return true;
   if (!gram_fits(p)) return false;
   const double rows = (double)(cfg.n_grid + (cfg.n_clip >= 2 ? cfg.n_clip : 0)) * (double)p.d_out_pad;
-  const double k = (double)p.K_pad;
-  const double direct = (double)p.T_pad * k * rows;
-  const double gram = (double)p.g_T_pad * (double)p.g_h_rows * (double)((p.K_pad + 255) / 256 * 256) +
-                      (double)p.g_h_rows * k * rows;
+  const int64_t bm = gemm_sq_tile_rows(), bn = 256;
+  const double direct = (double)p.T_pad * (double)p.K_pad * rows;
+  // both products of the second-moment form run on and right of the diagonal
+  // blocks only: H's 384 x 256 tiles with n0 + 256 > m0, and K from m0 on
+  double h_tiles = 0.0, k_cols = 0.0;
+  for (int64_t m0 = 0; m0 < p.g_h_rows; m0 += bm) {
+    for (int64_t n0 = 0; n0 < p.K_pad; n0 += bn) h_tiles += (n0 + bn > m0) ? 1.0 : 0.0;
+    k_cols += (double)(p.K_pad - m0);
+  }
+  const double gram = h_tiles * (double)(bm * bn) * (double)p.g_T_pad + (double)bm * k_cols * rows;
   return gram < 0.8 * direct;
 }
 
@@ -124,7 +130,7 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     gemm_sq_pad(T, d_out, d_in, &p.T_pad, &p.d_out_pad, &p.K_pad);
     gram_pad(T, p.K_pad, &p.g_T_pad, &p.g_xt_rows, &p.g_h_rows);
     p.gram = use_gram(cfg, p, T);
-    p.n_mt = (p.gram ? p.g_h_rows : p.T_pad) / gemm_sq_tile_rows();
+    p.n_mt = p.gram ? gram_units(p.g_h_rows) : p.T_pad / gemm_sq_tile_rows();  // rows of column partials
     p.n_x = absmax_blocks(T);
     p.n_db = build_dw_blocks(cfg.group_size, d_out, d_in);
     const int max_c = cfg.n_grid > cfg.n_clip ? cfg.n_grid : cfg.n_clip;
@@ -138,8 +144,11 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     off += align256(p.gram ? (size_t)p.g_xt_rows * p.g_T_pad * sizeof(uint16_t)
                            : (size_t)p.T_pad * p.K_pad * sizeof(uint16_t));
     if (p.gram) {
+      int ns;
+      int64_t slice;
+      gram_slices(p.g_T_pad, p.K_pad, &ns, &slice);
       p.off_h32 = off;
-      off += align256((size_t)p.K_pad * p.K_pad * sizeof(float));
+      off += align256((size_t)ns * p.K_pad * p.K_pad * sizeof(float));
       p.off_h16 = off;
       off += align256((size_t)p.g_h_rows * p.K_pad * sizeof(uint16_t));
       p.off_hc = off;
@@ -358,6 +367,19 @@ awq_status awq_search_workspace(const awq_search_cfg* cfg, int64_t d_out_total, 
   return ok();
 }
 
+awq_status awq_search_output_form(const awq_search_cfg* cfg, int64_t d_out_total, int64_t d_in, int64_t T,
+                                  int32_t* form) {
+  awq_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!form) return fail(AWQ_EINVAL, "form is NULL");
+  if (cfg->score != AWQ_SCORE_OUTPUT) return fail(AWQ_EINVAL, "the form applies to the output score only");
+  if (d_out_total < 1 || d_in < 1) return fail(AWQ_EINVAL, "need d_out_total >= 1 and d_in >= 1");
+  if (d_in % cfg->group_size) return fail(AWQ_ESHAPE, "d_in %lld not a multiple of group_size %d", (long long)d_in, cfg->group_size);
+  if (T < 1) return fail(AWQ_EINVAL, "output score needs T >= 1");
+  *form = plan_search(*cfg, d_out_total, d_in, T).gram ? AWQ_OUT_FORM_GRAM : AWQ_OUT_FORM_DIRECT;
+  return ok();
+}
+
 awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int64_t d_in,
                              const float* x_mean, const void* X, int32_t x_dtype, int64_t T,
                              int64_t ld_x, float* err, int32_t* best_idx, float* best_s, float* clip,
@@ -452,8 +474,8 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
       return hip_status(e, "transpose_x");
     float* h32 = (float*)(base + plan.off_h32);
     if ((e = launch_gemm_gram_h(x16, plan.g_T_pad, kp, h32, s)) != hipSuccess) return hip_status(e, "gemm(H)");
-    if ((e = launch_gram_scale(h32, kp, plan.g_h_rows, (float*)(base + plan.off_hc), (float*)(base + plan.off_hr),
-                               (uint16_t*)h16, s)) != hipSuccess)
+    if ((e = launch_gram_scale(h32, plan.g_T_pad, kp, plan.g_h_rows, (float*)(base + plan.off_hc),
+                               (float*)(base + plan.off_hr), (uint16_t*)h16, s)) != hipSuccess)
       return hip_status(e, "gram_scale");
   }
   if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, hc,

@@ -72,9 +72,13 @@ hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, con
 void gram_pad(int64_t T, int64_t K_pad, int64_t* T_pad, int64_t* xt_rows, int64_t* h_rows);
 hipError_t launch_transpose_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,
                               int64_t rows_pad, const OutScales* sc, uint16_t* Xt, hipStream_t stream);
+// H is formed in n_slices partial copies over token slices (summed in order by gram_scale)
+void gram_slices(int64_t T_pad, int64_t K_pad, int* n_slices, int64_t* slice);
 hipError_t launch_gemm_gram_h(const uint16_t* Xt, int64_t T_pad, int64_t K_pad, float* H32, hipStream_t stream);
-hipError_t launch_gram_scale(const float* H32, int64_t K_pad, int64_t h_rows, float* c, float* r, uint16_t* H16,
-                             hipStream_t stream);
+hipError_t launch_gram_scale(const float* H32, int64_t T_pad, int64_t K_pad, int64_t h_rows, float* c, float* r,
+                             uint16_t* H16, hipStream_t stream);
+// rows of colpart written by launch_gemm_gram (pairs of 384-row tiles of H16)
+int64_t gram_units(int64_t h_rows);
 hipError_t launch_gemm_gram(const uint16_t* H16, int64_t h_rows, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                             float* colpart, int64_t ldc, hipStream_t stream);
 // scales: with dmax == nullptr only sc->xs is set

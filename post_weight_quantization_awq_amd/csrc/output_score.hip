@@ -467,18 +467,27 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* B
 
 // Epilogues of the block's 384 x 256 product C (rows m of A, columns n of B):
 //   kEpiSq:    colpart[mt * ldc + n] = sum over the tile's rows of C[m, n]^2
-//   kEpiGram:  colpart[mt * ldc + n] = sum over the tile's rows m < lim of
-//              C[m, n] * B[n, m]  (A = H' symmetric, B = dW': the row's
-//              quadratic form dW'_n H' dW'_n^T, one tile's share)
-//   kEpiStore: out[m * ldc + n] = C[m, n] for m, n < lim (H = Xt Xt^T in fp32)
+//   kEpiGram:  colpart[u * ldc + n] = sum over the rows m < lim of the
+//              unit's two tiles of C[m, n] * B[n, m]  (A = H'', B = dW': one
+//              unit's share of the row's quadratic form dW'_n H' dW'_n^T).  H' is symmetric,
+//              so with 384-wide blocks I, J the form is
+//              sum_I a_I H'_II a_I + 2 sum_{J > I} a_I H'_IJ a_J: A holds
+//              H'' (diagonal blocks as they are, blocks right of the diagonal
+//              doubled) and the K loop of row tile mt starts at its diagonal
+//              block, column 384 mt.
+//   kEpiStore: out[m * ldc + n] = C[m, n] for m, n < lim (H = Xt Xt^T in
+//              fp32); tiles wholly left of their rows' diagonal block
+//              (n0 + 256 <= m0) are not needed and exit at once.
 constexpr int kEpiSq = 0, kEpiGram = 1, kEpiStore = 2;
 
+// kEpiStore splits K over blockIdx.y: slice y takes K columns [y kslice,
+// (y + 1) kslice) and stores its partial product at out + y lim ldc.
 template <int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                               uint32_t a_bytes, const uint16_t* __restrict__ B,
                                                               int64_t ldb, uint32_t b_bytes, int64_t K, int64_t n_mt,
                                                               int64_t n_nt, float* __restrict__ colpart, int64_t ldc,
-                                                              int group_m, int64_t lim) {
+                                                              int group_m, int64_t lim, int64_t kslice) {
   __shared__ float red[4][kBN];
   const int64_t nblk = (int64_t)gridDim.x;
   const int64_t bid = blockIdx.x;
@@ -488,47 +497,75 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
   const int64_t per_group = (int64_t)group_m * n_nt;
   const int64_t first_m = (id / per_group) * group_m;
   const int64_t gsz = (n_mt - first_m) < group_m ? (n_mt - first_m) : group_m;
-  const int64_t mt = first_m + (id % per_group) % gsz;
+  const int64_t mu = first_m + (id % per_group) % gsz;  // row unit: a tile, or a pair of tiles
   const int64_t nt = (id % per_group) / gsz;
-  const int64_t m0 = mt * kBM, n0 = nt * kBN;
+  const int64_t n0 = nt * kBN;
+  // kEpiGram: unit mu holds row tiles mu and kslice - 1 - mu (kslice = the
+  // number of row tiles, n_mt = ceil(kslice / 2) units): their K ranges from
+  // the diagonal block on sum to the same length for every unit, so all
+  // blocks carry the same work; the middle tile of an odd count is alone
+  int64_t mts[2] = {mu, mu};
+  int ntile = 1;
+  if constexpr (EPI == kEpiGram) {
+    mts[1] = kslice - 1 - mu;
+    ntile = mts[1] != mu ? 2 : 1;
+  }
+  if constexpr (EPI == kEpiStore) {
+    if (n0 + kBN <= mu * kBM) return;  // the whole block: no barrier reached yet
+    colpart += (int64_t)blockIdx.y * lim * ldc;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 96 x 128
-
-  f32x16 acc[3][4];
-#pragma unroll
-  for (int i = 0; i < 3; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int nk = (int)(K / kBK);
   const uint32_t ld2 = (uint32_t)(lda * 2);
   const uint32_t vo = (uint32_t)((lane >> 2) * ld2 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
   const uint32_t row16 = 16 * ld2;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, a_bytes);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, b_bytes);
-  // wave w fetches A rows 48 w .. 48 w + 47 (3 loads) and B rows 32 w .. 32 w + 31 (2 loads)
-  const uint32_t sA = (uint32_t)((m0 + 48 * wave) * lda * 2), sB = (uint32_t)((n0 + 32 * wave) * ldb * 2);
-  // k-tile t (clamped: past the end the ring re-fetches the last tile into a free slot)
-  auto koff = [&](int t) { return (uint32_t)((t < nk ? t : nk - 1) * kBK * 2); };
+  float csum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this lane's column sums over the unit's tiles
 
-  // prologue: stages 0 and 1 in flight; wait for stage 0 (5 loads per stage and wave)
-  dma_rows<3>(rsA, sA0, 48 * wave, vo, sA + koff(0), row16);
-  dma_rows<2>(rsB, sB0, 32 * wave, vo, sB + koff(0), row16);
-  dma_rows<3>(rsA, sA1, 48 * wave, vo, sA + koff(1), row16);
-  dma_rows<2>(rsB, sB1, 32 * wave, vo, sB + koff(1), row16);
-  __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0): this wave's stage-0 loads are in LDS
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  for (int ti = 0; ti < ntile; ++ti) {
+    const int64_t m0 = mts[ti] * kBM;
+    // K range: from the diagonal block on for the triangular quadratic form,
+    // the block's slice for the split product
+    int64_t kbeg = EPI == kEpiGram ? m0 : 0, kend = K;
+    if constexpr (EPI == kEpiStore) {
+      kbeg = (int64_t)blockIdx.y * kslice;
+      kend = kbeg + kslice < K ? kbeg + kslice : K;
+    }
 
-  // stage kt on ring slot S: fetch stage kt + 2 into slot SN (freed by the
-  // previous barrier), MFMAs on slot S, then wait until stage kt + 1 is in
-  // LDS (stage kt + 2 may still be in flight) and all reads of slot S are
-  // done, barrier
+    f32x16 acc[3][4];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int nk = (int)((kend - kbeg) / kBK);
+    // wave w fetches A rows 48 w .. 48 w + 47 (3 loads) and B rows 32 w .. 32 w + 31 (2 loads)
+    const uint32_t sA = (uint32_t)(((m0 + 48 * wave) * lda + kbeg) * 2),
+                   sB = (uint32_t)(((n0 + 32 * wave) * ldb + kbeg) * 2);
+    // k-tile t (clamped: past the end the ring re-fetches the last tile into a free slot)
+    auto koff = [&](int t) { return (uint32_t)((t < nk ? t : nk - 1) * kBK * 2); };
+
+    // prologue: stages 0 and 1 in flight; wait for stage 0 (5 loads per stage
+    // and wave).  On a unit's second tile every wave has passed the last
+    // stage's barrier, so no fragment read of the ring is outstanding.
+    dma_rows<3>(rsA, sA0, 48 * wave, vo, sA + koff(0), row16);
+    dma_rows<2>(rsB, sB0, 32 * wave, vo, sB + koff(0), row16);
+    dma_rows<3>(rsA, sA1, 48 * wave, vo, sA + koff(1), row16);
+    dma_rows<2>(rsB, sB1, 32 * wave, vo, sB + koff(1), row16);
+    __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0): this wave's stage-0 loads are in LDS
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    // stage kt on ring slot S: fetch stage kt + 2 into slot SN (freed by the
+    // previous barrier), MFMAs on slot S, then wait until stage kt + 1 is in
+    // LDS (stage kt + 2 may still be in flight) and all reads of slot S are
+    // done, barrier
 #define AWQ_STAGE3(S, SN)                                                       \
   {                                                                             \
     dma_rows<3>(rsA, sA##SN, 48 * wave, vo, sA + koff(kt + 2), row16);          \
@@ -540,70 +577,91 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     asm volatile("" ::: "memory");                                              \
     ++kt;                                                                       \
   }
-  int kt = 0;
-  for (; kt + 3 <= nk;) {
-    AWQ_STAGE3(0, 2)
-    AWQ_STAGE3(1, 0)
-    AWQ_STAGE3(2, 1)
-  }
-  if (kt < nk) AWQ_STAGE3(0, 2)
-  if (kt < nk) AWQ_STAGE3(1, 0)
+    int kt = 0;
+    for (; kt + 3 <= nk;) {
+      AWQ_STAGE3(0, 2)
+      AWQ_STAGE3(1, 0)
+      AWQ_STAGE3(2, 1)
+    }
+    if (kt < nk) AWQ_STAGE3(0, 2)
+    if (kt < nk) AWQ_STAGE3(1, 0)
 #undef AWQ_STAGE3
-  __builtin_amdgcn_s_waitcnt(0x0070);  // no load in flight past this point
+    __builtin_amdgcn_s_waitcnt(0x0070);  // no load in flight past this point
 
-  // accumulator element e of MFMA tile (i, j) holds C[m, n] with
-  // n = n0 + 128 wn + 32 j + lane % 32 and m = mrow(i) + 8 (e / 4) + e % 4
-  const int64_t mlane = m0 + wm * 96 + 4 * (lane >> 5);
-  if constexpr (EPI == kEpiStore) {
-    // 32-bit element offsets (the launcher keeps lim * ldc below 2^31)
-    const uint32_t ldo = (uint32_t)ldc;
-    const uint32_t nl = (uint32_t)(n0 + wn * 128 + (lane & 31));
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t mb = (uint32_t)(mlane + i * 32 + 8 * g);  // a multiple of 4, lim a multiple of 64
-        if (mb >= (uint32_t)lim) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (nl + 32 * j >= (uint32_t)lim) continue;
-          float* p = colpart + (mb * ldo + nl + 32 * j);
-          p[0] = acc[i][j][4 * g];
-          p[ldo] = acc[i][j][4 * g + 1];
-          p[2 * ldo] = acc[i][j][4 * g + 2];
-          p[3 * ldo] = acc[i][j][4 * g + 3];
-        }
-      }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float cs = 0.0f;
-    if constexpr (EPI == kEpiSq) {
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
-    } else {
-      const uint16_t* brow = B + (n0 + wn * 128 + j * 32 + (lane & 31)) * ldb;
+    // accumulator element e of MFMA tile (i, j) holds C[m, n] with
+    // n = n0 + 128 wn + 32 j + lane % 32 and m = mrow(i) + 8 (e / 4) + e % 4
+    const int64_t mlane = m0 + wm * 96 + 4 * (lane >> 5);
+    if constexpr (EPI == kEpiStore) {
+      // 32-bit element offsets (the launcher keeps lim * ldc below 2^31)
+      const uint32_t ldo = (uint32_t)ldc;
+      const uint32_t nl = (uint32_t)(n0 + wn * 128 + (lane & 31));
 #pragma unroll
       for (int i = 0; i < 3; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t m = mlane + i * 32 + 8 * g;  // a multiple of 4, lim a multiple of 64
-          uint2 u = make_uint2(0u, 0u);
-          if (m < lim) u = *(const uint2*)(brow + m);
-          cs = __builtin_fmaf(acc[i][j][4 * g], h2f((uint16_t)(u.x & 0xFFFFu)), cs);
-          cs = __builtin_fmaf(acc[i][j][4 * g + 1], h2f((uint16_t)(u.x >> 16)), cs);
-          cs = __builtin_fmaf(acc[i][j][4 * g + 2], h2f((uint16_t)(u.y & 0xFFFFu)), cs);
-          cs = __builtin_fmaf(acc[i][j][4 * g + 3], h2f((uint16_t)(u.y >> 16)), cs);
+          const uint32_t mb = (uint32_t)(mlane + i * 32 + 8 * g);  // a multiple of 4, lim a multiple of 64
+          if (mb >= (uint32_t)lim) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (nl + 32 * j >= (uint32_t)lim) continue;
+            float* p = colpart + (mb * ldo + nl + 32 * j);
+            p[0] = acc[i][j][4 * g];
+            p[ldo] = acc[i][j][4 * g + 1];
+            p[2 * ldo] = acc[i][j][4 * g + 2];
+            p[3 * ldo] = acc[i][j][4 * g + 3];
+          }
         }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float cs = 0.0f;
+        if constexpr (EPI == kEpiSq) {
+#pragma unroll
+          for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) cs = __builtin_fmaf(acc[i][j][e], acc[i][j][e], cs);
+        } else {
+          // the 12 four-element pieces of dW'[n, m] this lane needs, loads
+          // issued in two batches of six before their use (rows m >= lim
+          // read a valid clamped address and are masked out; m is a multiple
+          // of 4, lim of 64)
+          const uint16_t* brow = B + (n0 + wn * 128 + j * 32 + (lane & 31)) * ldb;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint2 u[3][2];
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                const int64_t m = mlane + i * 32 + 8 * (2 * h + g);
+                u[i][g] = *(const uint2*)(brow + (m < lim ? m : lim - 4));
+              }
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                const int e = 4 * (2 * h + g);
+                float t = acc[i][j][e] * h2f((uint16_t)(u[i][g].x & 0xFFFFu));
+                t = __builtin_fmaf(acc[i][j][e + 1], h2f((uint16_t)(u[i][g].x >> 16)), t);
+                t = __builtin_fmaf(acc[i][j][e + 2], h2f((uint16_t)(u[i][g].y & 0xFFFFu)), t);
+                t = __builtin_fmaf(acc[i][j][e + 3], h2f((uint16_t)(u[i][g].y >> 16)), t);
+                cs += mlane + i * 32 + 8 * (2 * h + g) < lim ? t : 0.0f;
+              }
+          }
+        }
+        csum[j] += cs;
+      }
     }
-    cs += __shfl_xor(cs, 32, kWave);
-    if (lane < 32) red[wm][wn * 128 + j * 32 + lane] = cs;
   }
-  __syncthreads();
-  if (tid < kBN) colpart[mt * ldc + n0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if constexpr (EPI != kEpiStore) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float cs = csum[j] + __shfl_xor(csum[j], 32, kWave);
+      if (lane < 32) red[wm][wn * 128 + j * 32 + lane] = cs;
+    }
+    __syncthreads();
+    if (tid < kBN) colpart[mu * ldc + n0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  }
 }
 
 int64_t gemm_sq_tile_rows() { return kBM; }
@@ -633,7 +691,7 @@ hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, con
   const int64_t n_mt = T_pad / kBM, n_nt = n_cols / kBN;
   const uint32_t a_bytes = (uint32_t)(T_pad * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
   gemm_sq_kernel<kEpiSq><<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(
-      X16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad, n_mt, n_nt, colpart, ldc, gemm_group_m(K_pad), 0);
+      X16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad, n_mt, n_nt, colpart, ldc, gemm_group_m(K_pad), 0, 0);
   return hipGetLastError();
 }
 
@@ -657,38 +715,82 @@ void gram_pad(int64_t T, int64_t K_pad, int64_t* T_pad, int64_t* xt_rows, int64_
   *h_rows = m;
 }
 
-// H32 [K_pad, K_pad] = Xt Xt^T (fp32, rows and columns < K_pad)
+// Token slices of the H product: enough blocks with work (tiles on or right
+// of the diagonal block) for about two per compute unit, slices of at least
+// 1024 tokens, at most 8 partial copies of H.
+static int64_t gram_tiles_needed(int64_t K_pad) {
+  int64_t n = 0;
+  for (int64_t m0 = 0; m0 < K_pad; m0 += kBM)
+    for (int64_t n0 = 0; n0 < K_pad; n0 += kBN) n += (n0 + kBN > m0) ? 1 : 0;
+  return n;
+}
+
+void gram_slices(int64_t T_pad, int64_t K_pad, int* n_slices, int64_t* slice) {
+  // s slices take about ceil(a s / 256) / s of the unsplit product's time (a
+  // blocks with work, one per compute unit at a time): the s in 1..8 that
+  // minimises it, with slices of at least 512 tokens and the partial copies
+  // of H within 2 GiB
+  const int64_t a = gram_tiles_needed(K_pad);
+  const double bytes = 4.0 * (double)K_pad * (double)K_pad;
+  int64_t s = 1;
+  double best = (double)((a + 255) / 256);
+  for (int64_t c = 2; c <= 8; ++c) {
+    if (T_pad / c < 512 || c * bytes > 2147483648.0) break;
+    const double t = (double)((a * c + 255) / 256) / (double)c;
+    if (t < best - 1e-9) { best = t; s = c; }
+  }
+  const int64_t len = ((T_pad + s - 1) / s + 63) / 64 * 64;
+  *slice = len;
+  *n_slices = (int)((T_pad + len - 1) / len);
+}
+
+// H32 slices [n_slices][K_pad, K_pad] = Xt Xt^T over each token slice (fp32,
+// on and right of the diagonal blocks, rows and columns < K_pad)
 hipError_t launch_gemm_gram_h(const uint16_t* Xt, int64_t T_pad, int64_t K_pad, float* H32, hipStream_t stream) {
-  int64_t tp, xr, hr;
+  int64_t tp, xr, hr, slice;
+  int ns;
   gram_pad(T_pad, K_pad, &tp, &xr, &hr);
+  gram_slices(T_pad, K_pad, &ns, &slice);
   const int64_t n_mt = hr / kBM, n_nt = (K_pad + kBN - 1) / kBN;
   const uint32_t bytes = (uint32_t)(xr * T_pad * 2);
-  gemm_sq_kernel<kEpiStore><<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(
-      Xt, T_pad, bytes, Xt, T_pad, bytes, T_pad, n_mt, n_nt, H32, K_pad, gemm_group_m(T_pad), K_pad);
+  gemm_sq_kernel<kEpiStore><<<dim3((unsigned)(n_mt * n_nt), (unsigned)ns), kGemmThreads, 0, stream>>>(
+      Xt, T_pad, bytes, Xt, T_pad, bytes, T_pad, n_mt, n_nt, H32, K_pad, gemm_group_m(slice), K_pad, slice);
   return hipGetLastError();
 }
 
-// c[i] = sqrt(H_ii), r[i] = 1 / c[i] (0 for a channel that is zero in every token)
-__global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict__ H32, int64_t K_pad,
+// c[i] = sqrt(H_ii), r[i] = 1 / c[i] (0 for a channel that is zero in every
+// token); H_ii summed over the token slices in order
+__global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict__ H32, int64_t K_pad, int ns,
                                                        float* __restrict__ c, float* __restrict__ r) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= K_pad) return;
-  const float h = H32[i * K_pad + i];
+  float h = H32[i * K_pad + i];
+  for (int q = 1; q < ns; ++q) h += H32[(int64_t)q * K_pad * K_pad + i * K_pad + i];
   const float ci = h > 0.0f ? __builtin_sqrtf(h) : 0.0f;
   c[i] = ci;
   r[i] = ci > 0.0f ? 1.0f / ci : 0.0f;
 }
 
-// H16 [h_rows, K_pad] = fp16(H_ij r_i r_j), zero rows from K_pad on
-__global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict__ H32, int64_t K_pad, int64_t h_rows,
-                                                       const float* __restrict__ r, uint16_t* __restrict__ H16) {
+// H16 [h_rows, K_pad] = H'' of the triangular form: fp16(H_ij r_i r_j) in the
+// diagonal 384-block of row i, twice that right of it (exact), zeros left of
+// it (never read; H32 is not formed there) and in rows from K_pad on
+__global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict__ H32, int64_t K_pad, int ns,
+                                                       int64_t h_rows, const float* __restrict__ r,
+                                                       uint16_t* __restrict__ H16) {
   const int64_t chunks = K_pad / 8, n = h_rows * chunks;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
     const int64_t i = idx / chunks, j = (idx % chunks) * 8;
+    const int64_t dblk = i / kBM * kBM;  // first column of row i's diagonal block
     uint32_t o[4] = {0u, 0u, 0u, 0u};
-    if (i < K_pad) {
-      const float ri = r[i];
-      const float4 h0 = *(const float4*)(H32 + i * K_pad + j), h1 = *(const float4*)(H32 + i * K_pad + j + 4);
+    if (i < K_pad && j >= dblk) {
+      const float ri = j >= dblk + kBM ? 2.0f * r[i] : r[i];
+      float4 h0 = *(const float4*)(H32 + i * K_pad + j), h1 = *(const float4*)(H32 + i * K_pad + j + 4);
+      for (int q = 1; q < ns; ++q) {  // token slices in order
+        const float* hq = H32 + (int64_t)q * K_pad * K_pad + i * K_pad + j;
+        const float4 a = *(const float4*)hq, b = *(const float4*)(hq + 4);
+        h0.x += a.x; h0.y += a.y; h0.z += a.z; h0.w += a.w;
+        h1.x += b.x; h1.y += b.y; h1.z += b.z; h1.w += b.w;
+      }
       const float4 r0 = *(const float4*)(r + j), r1 = *(const float4*)(r + j + 4);
       const float v[8] = {h0.x * ri * r0.x, h0.y * ri * r0.y, h0.z * ri * r0.z, h0.w * ri * r0.w,
                           h1.x * ri * r1.x, h1.y * ri * r1.y, h1.z * ri * r1.z, h1.w * ri * r1.w};
@@ -699,23 +801,31 @@ __global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict_
   }
 }
 
-hipError_t launch_gram_scale(const float* H32, int64_t K_pad, int64_t h_rows, float* c, float* r, uint16_t* H16,
-                             hipStream_t stream) {
-  gram_diag_kernel<<<(unsigned)((K_pad + 255) / 256), 256, 0, stream>>>(H32, K_pad, c, r);
+hipError_t launch_gram_scale(const float* H32, int64_t T_pad, int64_t K_pad, int64_t h_rows, float* c, float* r,
+                             uint16_t* H16, hipStream_t stream) {
+  int ns;
+  int64_t slice;
+  gram_slices(T_pad, K_pad, &ns, &slice);
+  gram_diag_kernel<<<(unsigned)((K_pad + 255) / 256), 256, 0, stream>>>(H32, K_pad, ns, c, r);
   const int64_t n = h_rows * (K_pad / 8);
   int64_t nb = (n + 255) / 256;
   if (nb > 8192) nb = 8192;
-  gram_half_kernel<<<(unsigned)nb, 256, 0, stream>>>(H32, K_pad, h_rows, r, H16);
+  gram_half_kernel<<<(unsigned)nb, 256, 0, stream>>>(H32, K_pad, ns, h_rows, r, H16);
   return hipGetLastError();
 }
 
-// colpart[mt * ldc + n] = the tile-mt share of dW'_n H' dW'_n^T over the n_cols stacked dW' rows
+// colpart[u * ldc + n] = row unit u's share (tiles u and n_tiles - 1 - u) of
+// dW'_n H' dW'_n^T over the n_cols stacked dW' rows, u < gram_units(h_rows)
+// (K from each tile's diagonal block on: about half the products of the full form)
+int64_t gram_units(int64_t h_rows) { return (h_rows / kBM + 1) / 2; }
+
 hipError_t launch_gemm_gram(const uint16_t* H16, int64_t h_rows, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                             float* colpart, int64_t ldc, hipStream_t stream) {
-  const int64_t n_mt = h_rows / kBM, n_nt = n_cols / kBN;
+  const int64_t n_tiles = h_rows / kBM, n_units = gram_units(h_rows), n_nt = n_cols / kBN;
   const uint32_t a_bytes = (uint32_t)(h_rows * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
-  gemm_sq_kernel<kEpiGram><<<(unsigned)(n_mt * n_nt), kGemmThreads, 0, stream>>>(
-      H16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad, n_mt, n_nt, colpart, ldc, gemm_group_m(K_pad), K_pad);
+  gemm_sq_kernel<kEpiGram><<<(unsigned)(n_units * n_nt), kGemmThreads, 0, stream>>>(
+      H16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad, n_units, n_nt, colpart, ldc, gemm_group_m(K_pad), K_pad,
+      n_tiles);
   return hipGetLastError();
 }
 

@@ -201,6 +201,29 @@ def test_workspace_sizes(A):
         A.search_workspace_bytes(6144, 4096, 64, score="output", out_form="hessian")
 
 
+def test_output_form_choice(A):
+    """The output score's form: the second-moment form where the calibration set
+    has several times more tokens than inputs, the direct form where it has few;
+    the flags force either; weight score and bad shapes are rejected."""
+    assert A.search_output_form(6144, 4096, 16384) == "gram"            # fused QKV, 16384 tokens
+    assert A.search_output_form(24576, 4096, 16384, n_clip=20) == "gram"  # MLP gate/up with the clip search
+    assert A.search_output_form(4096, 12288, 16384, n_clip=20) == "gram"  # down_proj: triangular H products
+    assert A.search_output_form(4096, 12288, 512, n_clip=20) == "direct"
+    assert A.search_output_form(6144, 4096, 2048) == "direct"             # T near d_in
+    assert A.search_output_form(6144, 4096, 512) == "direct"
+    assert A.search_output_form(256, 512, 64) == "direct"
+    assert A.search_output_form(6144, 4096, 16384, out_form="direct") == "direct"
+    assert A.search_output_form(256, 512, 64, out_form="gram") == "gram"
+    L = A.lib()
+    f = ctypes.c_int32()
+    w = A._cfg(128, 20, "weight", 0, 0.5, 1e-4)
+    assert L.awq_search_output_form(ctypes.byref(w), 256, 512, 64, ctypes.byref(f)) == A.AWQ_EINVAL
+    o = A._cfg(128, 20, "output", 0, 0.5, 1e-4)
+    assert L.awq_search_output_form(ctypes.byref(o), 256, 500, 64, ctypes.byref(f)) == A.AWQ_ESHAPE
+    assert L.awq_search_output_form(ctypes.byref(o), 256, 512, 0, ctypes.byref(f)) == A.AWQ_EINVAL
+    assert L.awq_search_output_form(ctypes.byref(o), 256, 512, 64, None) == A.AWQ_EINVAL
+
+
 def test_norm_group_fold_validation(A):
     L = A.lib()
     ptrs = lambda *p: ctypes.cast((ctypes.c_void_p * len(p))(*p), ctypes.POINTER(ctypes.c_void_p))

@@ -100,6 +100,7 @@ def test_output_forms_agree_and_auto(A):
     W = WL.make_weight(1301, d_out, d_in)
     X = WL.make_activations(1302, T, d_in, "bf16")
     xm = O.act_stats(X)
+    assert A.search_output_form(d_out, d_in, T, group_size=G) == "gram"
     args = ([dev_f16(W)], dev_f32(xm))
     kw = dict(group_size=G, score="output", X=dev_x(X))
     r_auto = A.search_scales(*args, **kw)
