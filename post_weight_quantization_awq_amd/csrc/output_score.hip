@@ -477,7 +477,7 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* B
 //              block, column 384 mt.
 //   kEpiStore: out[m * ldc + n] = C[m, n] for m, n < lim (H = Xt Xt^T in
 //              fp32); tiles wholly left of their rows' diagonal block
-//              (n0 + 256 <= m0) are not needed and exit at once.
+//              (n0 + 256 <= m0) are not needed and not launched.
 constexpr int kEpiSq = 0, kEpiGram = 1, kEpiStore = 2;
 
 // kEpiStore splits K over blockIdx.y: slice y takes K columns [y kslice,
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
   const int64_t gsz = (n_mt - first_m) < group_m ? (n_mt - first_m) : group_m;
   const int64_t mu = first_m + (id % per_group) % gsz;  // row unit: a tile, or a pair of tiles
   const int64_t nt = (id % per_group) / gsz;
-  const int64_t n0 = nt * kBN;
+  int64_t n0 = nt * kBN;
   // kEpiGram: unit mu holds row tiles mu and kslice - 1 - mu (kslice = the
   // number of row tiles, n_mt = ceil(kslice / 2) units): their K ranges from
   // the diagonal block on sum to the same length for every unit, so all
@@ -511,7 +511,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     ntile = mts[1] != mu ? 2 : 1;
   }
   if constexpr (EPI == kEpiStore) {
-    if (n0 + kBN <= mu * kBM) return;  // the whole block: no barrier reached yet
+    // blockIdx.x enumerates only the tiles on or right of their rows'
+    // diagonal block (n0 + 256 > m0, i.e. nt >= m0 / 256), row by row: equal
+    // work per block, spread over the XCDs by the dispatch order itself
+    int64_t rem = bid, m = 0;
+    for (; m < n_mt; ++m) {
+      const int64_t cnt = n_nt - m * kBM / kBN;
+      if (rem < cnt) break;
+      rem -= cnt;
+    }
+    mts[0] = mts[1] = m;
+    n0 = (m * kBM / kBN + rem) * kBN;
     colpart += (int64_t)blockIdx.y * lim * ldc;
   }
 
@@ -753,7 +763,7 @@ hipError_t launch_gemm_gram_h(const uint16_t* Xt, int64_t T_pad, int64_t K_pad, 
   gram_slices(T_pad, K_pad, &ns, &slice);
   const int64_t n_mt = hr / kBM, n_nt = (K_pad + kBN - 1) / kBN;
   const uint32_t bytes = (uint32_t)(xr * T_pad * 2);
-  gemm_sq_kernel<kEpiStore><<<dim3((unsigned)(n_mt * n_nt), (unsigned)ns), kGemmThreads, 0, stream>>>(
+  gemm_sq_kernel<kEpiStore><<<dim3((unsigned)gram_tiles_needed(K_pad), (unsigned)ns), kGemmThreads, 0, stream>>>(
       Xt, T_pad, bytes, Xt, T_pad, bytes, T_pad, n_mt, n_nt, H32, K_pad, gemm_group_m(slice), K_pad, slice);
   return hipGetLastError();
 }
