@@ -55,12 +55,12 @@ struct SearchPlan {
   bool output;
   int64_t n_blocks;     // weight score: search blocks
   int64_t T_pad, d_out_pad, K_pad, n_mt, ldc;  // output score: padded GEMM shapes, token tiles, partial ld
-  int64_t n_x, n_db;    // output score: X max partials, dW max partials per candidate
+  int64_t n_x, n_db;    // output score: X max partials, dW bounds per candidate (1)
   int cand_chunk;       // output score: candidates per dW chunk
   bool gram;            // output score in the second-moment form (H = X^T X)
   int64_t g_T_pad, g_xt_rows, g_h_rows;  // second-moment form: token padding, Xt rows, H16 rows
   size_t off_S, off_C2, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
-  size_t off_h32, off_h16, off_hc, off_hr;
+  size_t off_h32, off_h16, off_hc, off_hr, off_cpart, off_cmax;
   bool duo;                   // duo-scaling candidates: w_mean, its scratch, the fp64 table
   size_t off_wmean, off_rmax, off_wpart, off_T, off_ext;
 };
@@ -132,7 +132,7 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     p.gram = use_gram(cfg, p, T);
     p.n_mt = p.gram ? gram_units(p.g_h_rows) : p.T_pad / gemm_sq_tile_rows();  // rows of column partials
     p.n_x = absmax_blocks(T);
-    p.n_db = build_dw_blocks(cfg.group_size, d_out, d_in);
+    p.n_db = 1;  // one bound on max |dW| per candidate
     const int max_c = cfg.n_grid > cfg.n_clip ? cfg.n_grid : cfg.n_clip;
     p.ldc = (int64_t)max_c * p.d_out_pad;
     const size_t per_cand = (size_t)p.d_out_pad * p.K_pad * sizeof(uint16_t);
@@ -168,6 +168,10 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     off += 2 * align256(sizeof(OutScales));
     p.off_chunk = off;
     off += align256((size_t)max_c * reduce_cols_chunks(d_out) * sizeof(double));
+    p.off_cpart = off;
+    off += align256((size_t)colmax_part_floats(d_in) * sizeof(float));
+    p.off_cmax = off;
+    off += align256((size_t)d_in * sizeof(float));
   }
   p.duo = (cfg.flags & AWQ_FLAG_DUO) != 0;
   if (p.duo) off = plan_duo(p, d_out, d_in, cfg.n_grid, off);
@@ -478,9 +482,11 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
                                (float*)(base + plan.off_hr), (uint16_t*)h16, s)) != hipSuccess)
       return hip_status(e, "gram_scale");
   }
-  if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, cfg->n_grid, 0, S, nullptr, 0, 1.0f, 0, nullptr, hc,
-                           dmax, nullptr, s)) != hipSuccess)
-    return hip_status(e, "build_dw(max)");
+  float* cmax = (float*)(base + plan.off_cmax);
+  if ((e = launch_colmax(parts, d_out, d_in, (float*)(base + plan.off_cpart), cmax, s)) != hipSuccess)
+    return hip_status(e, "colmax");
+  if ((e = launch_dw_bound(asym, cmax, d_in, cfg->n_grid, 0, S, nullptr, 0, 1.0f, hc, dmax, s)) != hipSuccess)
+    return hip_status(e, "dw_bound");
   if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, cfg->n_grid, sc_a, s)) != hipSuccess)
     return hip_status(e, "out_scales");
   if (!plan.gram && (e = launch_convert_x(X, bf16, T, d_in, ld_x, plan.T_pad, kp, sc_a, x16, s)) != hipSuccess)
@@ -489,8 +495,8 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   if (!one_chunk) mark(true, s);
   for (int c0 = 0; c0 < cfg->n_grid; c0 += plan.cand_chunk) {
     const int nc = (cfg->n_grid - c0) < plan.cand_chunk ? (cfg->n_grid - c0) : plan.cand_chunk;
-    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, hc, nullptr,
-                             dw, s)) != hipSuccess)
+    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, hc, dw, s)) !=
+        hipSuccess)
       return hip_status(e, "build_dw");
     if (one_chunk) mark(true, s);
     e = product((int64_t)nc * dop, colpart + (int64_t)c0 * dop);
@@ -507,15 +513,15 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
     return hip_status(e, "select");
   if (cfg->n_clip >= 2) {
     const int nclip = cfg->n_clip;
-    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, 0,
-                             nullptr, hc, dmax, nullptr, s)) != hipSuccess)
-      return hip_status(e, "build_dw(clip max)");
+    if ((e = launch_dw_bound(asym, cmax, d_in, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, hc, dmax, s)) !=
+        hipSuccess)
+      return hip_status(e, "dw_bound(clip)");
     if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, nclip, sc_c, s)) != hipSuccess)
       return hip_status(e, "out_scales(clip)");
     for (int c0 = 0; c0 < nclip; c0 += plan.cand_chunk) {
       const int nc = (nclip - c0) < plan.cand_chunk ? (nclip - c0) : plan.cand_chunk;
       if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0,
-                               sc_c, hc, nullptr, dw, s)) != hipSuccess)
+                               sc_c, hc, dw, s)) != hipSuccess)
         return hip_status(e, "build_dw(clip)");
       if ((e = product((int64_t)nc * dop, colpart + (int64_t)c0 * dop)) != hipSuccess)
         return hip_status(e, "gemm_sq(clip)");

@@ -44,7 +44,7 @@ hipError_t launch_select(const double* partials, int64_t n_blocks, int n_cand, d
 int64_t absmax_blocks(int64_t rows);
 hipError_t launch_prepare_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, float* xmax_part,
                             hipStream_t stream);
-// scales: xs from the X partial maxima, ds[c] and inv[c] from the dW partial maxima dmax [n_cand, n_d]
+// scales: xs from the X partial maxima, ds[c] and inv[c] from the dW bounds dmax [n_cand, n_d]
 hipError_t launch_out_scales(const float* xmax_part, int64_t n_x, const float* dmax, int64_t n_d, int n_cand,
                              OutScales* sc, hipStream_t stream);
 // padded GEMM shapes: T_pad a multiple of the token tile, d_out_pad of 256, K_pad of 64
@@ -54,14 +54,21 @@ void gemm_sq_pad(int64_t T, int64_t d_out, int64_t d_in, int64_t* T_pad, int64_t
 hipError_t launch_convert_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,
                             int64_t K_pad, const OutScales* sc, uint16_t* X16, hipStream_t stream);
 // dW of candidates c = cand0 .. cand0+n_cand-1 (mode 0: s = S[c]; mode 1: s = s_best, clip ratio c):
-//   dw == nullptr: per-block max |dW_c| -> dmax [n_cand, build_dw_blocks(G, d_out, d_in)]
-//   dw != nullptr: dw[c - cand0] = fp16(dW_c * sc->ds[c]), [d_out_pad, K_pad] each, zero padded
-int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in);
+//   dw[c - cand0] = fp16(dW_c * sc->ds[c]), [d_out_pad, K_pad] each, zero padded;
 //   cs != nullptr: column i of every dW_c is multiplied by cs[i] first (second-moment form)
+int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in);
 hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
                            int64_t d_out_pad, int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best,
-                           int n_clip, float clip_lo, int cand0, const OutScales* sc, const float* cs, float* dmax,
-                           uint16_t* dw, hipStream_t stream);
+                           int n_clip, float clip_lo, int cand0, const OutScales* sc, const float* cs, uint16_t* dw,
+                           hipStream_t stream);
+// colmax[i] = max_o |W[o, i]| (part: colmax_part_floats(d_in) floats of scratch)
+int64_t colmax_part_floats(int64_t d_in);
+hipError_t launch_colmax(const WParts& parts, int64_t d_out, int64_t d_in, float* part, float* colmax,
+                         hipStream_t stream);
+// bound[c] >= max |dW_c| (times cs) for c = 0 .. n_cand-1, from the column maxima (same modes as build_dw)
+hipError_t launch_dw_bound(bool asym, const float* colmax, int64_t d_in, int n_cand, int mode, const float* S,
+                           const float* s_best, int n_clip, float clip_lo, const float* cs, float* bound,
+                           hipStream_t stream);
 // gemm of squares on fp16 operands: Y = X16 [T_pad, K_pad] dw^T (dw: [n_cols, K_pad]);
 // colpart[mt * ldc + n] = sum over the 384 tokens of tile mt of Y[t, n]^2
 hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,

@@ -39,8 +39,8 @@ __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_lo) {
   return (float)(1.0 - (double)j * (1.0 - (double)clip_lo) / (double)(n_clip - 1));
 }
 
-// WRITE = false: per-block max |dW_c| -> dmax[(c - cand0) * gridDim.x + block]
-// WRITE = true:  dW16[c - cand0] = fp16(dW_c * ds[c])
+// dW16[c - cand0] = fp16(dW_c * ds[c]), ds[c] a power of two from a bound on
+// max |dW_c| (dw_bound_kernel below)
 // ASYM: codes of the asymmetric grid (range [min(0, min v), max(0, max v)],
 //   both ends times the clip ratio in mode 1, step RN(range / 15), exact zero
 //   point and codes; the signed code clamp(n, -z, 15 - z) times the step)
@@ -49,14 +49,13 @@ __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_lo) {
 // A block loads its tile of W once and takes the launch's candidates
 // cand0 + blockIdx.y, + gridDim.y, ... in turn, so W is read once per
 // candidate slice instead of once per candidate.
-// COLS: every column i of dW_c is multiplied by cs[i] before the maximum and
-//   the fp16 rounding (the second-moment form's sqrt(H_ii), see section 2b).
-template <int G, bool WRITE, bool ASYM, bool COLS>
+// COLS: every column i of dW_c is multiplied by cs[i] before the fp16
+//   rounding (the second-moment form's sqrt(H_ii), see section 2b).
+template <int G, bool ASYM, bool COLS>
 __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
     const WParts P, int64_t d_out, int64_t d_in, int64_t d_out_pad, int64_t K_pad, int mode,
     const float* __restrict__ S, const float* __restrict__ s_best, int n_clip, float clip_lo, int cand0, int n_cand,
-    const OutScales* __restrict__ sc, const float* __restrict__ cs, float* __restrict__ dmax,
-    uint16_t* __restrict__ dw) {
+    const OutScales* __restrict__ sc, const float* __restrict__ cs, uint16_t* __restrict__ dw) {
   constexpr int LPG = G / 16;
   constexpr int RS = kDwThreads / LPG;
   const int64_t n_gcol = d_in / G;
@@ -65,10 +64,9 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
   const int tid = threadIdx.x;
   const int lg = tid % LPG, slot = tid / LPG;
   const int64_t row = rblk * RS + slot;
-  // rows past d_out run the same code on zeros (dW = 0) so that every thread
-  // reaches the block reduction below; only the loads and stores are skipped
+  // rows past d_out run the same code on zeros (dW = 0) so that every lane
+  // takes part in the cross-lane group maxima; only the loads are skipped
   const bool valid = row < d_out;
-  __shared__ float red[kDwThreads / 64];
   const int64_t col = gcol * G + lg * 16;
 
   float w[16];
@@ -124,9 +122,8 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
       qlo = -z;
       qhi = (float)kUMax - z;
     }
-    const float dsc = WRITE ? sc->ds[c] : 1.0f;
+    const float dsc = sc->ds[c];
     uint32_t outw[8];
-    float mx = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       float n = step > 0.0f ? code_exact(v[j], step, inv) : 0.0f;
@@ -137,15 +134,11 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
       // (the codes q themselves are exact)
       float d = __builtin_fmaf(n, step, -v[j]) * __builtin_amdgcn_rcpf(sv[j]);
       if constexpr (COLS) d *= cv[j];
-      if constexpr (WRITE) {
-        const uint32_t b = f2h_bits(d * dsc);       // exact scaling by 2^e, one rounding
-        if (j & 1) outw[j >> 1] |= b << 16;
-        else outw[j >> 1] = b;
-      } else {
-        mx = __builtin_fmaxf(mx, __builtin_fabsf(d));
-      }
+      const uint32_t b = f2h_bits(d * dsc);       // exact scaling by 2^e, one rounding
+      if (j & 1) outw[j >> 1] |= b << 16;
+      else outw[j >> 1] = b;
     }
-    if constexpr (WRITE) {
+    {
       if (row < d_out_pad) {
         uint16_t* rowp = dw + (int64_t)ci * d_out_pad * K_pad + row * K_pad;
         uint4* dst = (uint4*)(rowp + col);
@@ -162,16 +155,6 @@ __global__ __launch_bounds__(kDwThreads) void build_dw_kernel(
           }
         }
       }
-    } else {
-      mx = wave_max(mx);
-      if ((tid & 63) == 0) red[tid >> 6] = mx;
-      __syncthreads();
-      if (tid == 0) {
-        float b = red[0];
-        for (int w = 1; w < kDwThreads / 64; ++w) b = __builtin_fmaxf(b, red[w]);
-        dmax[(int64_t)ci * gridDim.x + blockIdx.x] = b;
-      }
-      __syncthreads();  // red is written again by the next candidate
     }
   }
 }
@@ -183,18 +166,16 @@ int64_t build_dw_blocks(int group_size, int64_t d_out, int64_t d_in) {
 
 hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64_t d_out, int64_t d_in,
                            int64_t d_out_pad, int64_t K_pad, int n_cand, int mode, const float* S, const float* s_best,
-                           int n_clip, float clip_lo, int cand0, const OutScales* sc, const float* cs, float* dmax,
-                           uint16_t* dw, hipStream_t stream) {
-  // max pass: d_out rows; write pass: d_out_pad rows (zeros past d_out).  One
-  // block per W tile takes all of the launch's candidates: measured 1.2%
-  // faster on the fused-QKV output-score step than one block per tile and
-  // candidate (W read once instead of n_cand times), 0.9% than four slices
-  dim3 grid((unsigned)build_dw_blocks(group_size, dw == nullptr ? d_out : d_out_pad, d_in), 1u);
-#define AWQ_DW3(G, A, C)                                                                                   \
-  if (dw == nullptr) build_dw_kernel<G, false, A, C><<<grid, kDwThreads, 0, stream>>>(                       \
-      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, cs, dmax, dw); \
-  else build_dw_kernel<G, true, A, C><<<grid, kDwThreads, 0, stream>>>(                                      \
-      parts, d_out, d_in, d_out_pad, K_pad, mode, S, s_best, n_clip, clip_lo, cand0, n_cand, sc, cs, dmax, dw);
+                           int n_clip, float clip_lo, int cand0, const OutScales* sc, const float* cs, uint16_t* dw,
+                           hipStream_t stream) {
+  // d_out_pad rows (zeros past d_out).  One block per W tile takes all of the
+  // launch's candidates: measured 1.2% faster on the fused-QKV output-score
+  // step than one block per tile and candidate (W read once instead of
+  // n_cand times), 0.9% than four slices
+  dim3 grid((unsigned)build_dw_blocks(group_size, d_out_pad, d_in), 1u);
+#define AWQ_DW3(G, A, C)                                                     \
+  build_dw_kernel<G, A, C><<<grid, kDwThreads, 0, stream>>>(parts, d_out, d_in, d_out_pad, K_pad, mode, S, \
+                                                            s_best, n_clip, clip_lo, cand0, n_cand, sc, cs, dw);
 #define AWQ_DW2(G, A) \
   if (cs != nullptr) { AWQ_DW3(G, A, true) } else { AWQ_DW3(G, A, false) }
 #define AWQ_DW(G) \
@@ -207,6 +188,107 @@ hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64
 #undef AWQ_DW
 #undef AWQ_DW2
 #undef AWQ_DW3
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Bound on max |dW_c| (times cs) for the power-of-two operand scale ds[c].
+// With v = w s and the chosen grid point q step, |q step - v| <= |v| (0 is on
+// every grid, and the code is the nearest grid point, clamped toward 0's side
+// of the range), and |q step - v| <= F a with a the group's max |v|:
+//   symmetric:  step = rho a / 7, unclamped error <= step / 2, a clamped value
+//               exceeds 7 step by at most (1 - rho) a:  F = (1 - rho) + rho / 14
+//   asymmetric: step <= 2 rho a / 15, error <= step unclamped and
+//               (1 - rho) a + step clamped:             F = (1 - rho) + 2 rho / 15
+// (rho the clip ratio, 1 in the alpha search).  So
+//   |dW_c[o, i]| cs_i <= cs_i min(F A_c / s_i, colmax_i),  A_c = max_i colmax_i s_i,
+// which needs only the column maxima of |W|, not the codes of every candidate.
+// Scaled by the power of two of this bound the largest element lands at most
+// a few octaves below 2^14, far from fp16's subnormals.
+// ---------------------------------------------------------------------------
+constexpr int kColSplits = 64;   // row slices of the column-max pass
+
+// part[r][i] = max |W[o, i]| over the rows o of slice r, 8 columns per thread
+__global__ __launch_bounds__(256) void colmax_part_kernel(const WParts P, int64_t d_out, int64_t d_in,
+                                                         float* __restrict__ part) {
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c >= d_in) return;
+  const int64_t per = (d_out + kColSplits - 1) / kColSplits;
+  const int64_t r0 = blockIdx.y * per, r1 = r0 + per < d_out ? r0 + per : d_out;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t row = r0; row < r1; ++row) {
+    float w[8];
+    unpack8_f16(*(const uint4*)(row_ptr(P, row, d_in) + c), w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = __builtin_fmaxf(m[j], __builtin_fabsf(w[j]));
+  }
+  float* o = part + (int64_t)blockIdx.y * d_in + c;
+  *(float4*)o = make_float4(m[0], m[1], m[2], m[3]);
+  *(float4*)(o + 4) = make_float4(m[4], m[5], m[6], m[7]);
+}
+
+__global__ __launch_bounds__(256) void colmax_final_kernel(const float* __restrict__ part, int64_t d_in,
+                                                          float* __restrict__ colmax) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= d_in) return;
+  float m = 0.0f;
+  for (int r = 0; r < kColSplits; ++r) m = __builtin_fmaxf(m, part[(int64_t)r * d_in + i]);
+  colmax[i] = m;
+}
+
+__device__ float block_max256_v(float m, float* red) {
+  const int tid = threadIdx.x;
+  red[tid] = m;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] = __builtin_fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// bound[blockIdx.x] for candidate c = cand0 + blockIdx.x (mode 0: s = S[c];
+// mode 1: s = s_best and clip ratio c); 1% above the bound for the roundings
+// of v, the step, the reciprocal of s and the bound's own arithmetic
+__global__ __launch_bounds__(256) void dw_bound_kernel(const float* __restrict__ colmax, int64_t d_in, int mode,
+                                                      const float* __restrict__ S, const float* __restrict__ s_best,
+                                                      int n_clip, float clip_lo, int cand0, int asym,
+                                                      const float* __restrict__ cs, float* __restrict__ bound) {
+  __shared__ float red[256];
+  const int c = cand0 + blockIdx.x;
+  const float* s = mode == 0 ? S + (int64_t)c * d_in : s_best;
+  float a = 0.0f;
+  for (int64_t i = threadIdx.x; i < d_in; i += 256) a = __builtin_fmaxf(a, colmax[i] * s[i]);
+  const float A = block_max256_v(a, red);
+  const float rho = mode == 1 ? clip_ratio(c, n_clip, clip_lo) : 1.0f;
+  const float F = (1.0f - rho) + rho * (asym ? 2.0f / 15.0f : 1.0f / 14.0f);
+  float u = 0.0f;
+  for (int64_t i = threadIdx.x; i < d_in; i += 256) {
+    float t = __builtin_fminf(F * A / s[i], colmax[i]);
+    if (cs != nullptr) t *= cs[i];
+    u = __builtin_fmaxf(u, t);
+  }
+  const float U = block_max256_v(u, red);
+  if (threadIdx.x == 0) bound[blockIdx.x] = 1.01f * U;
+}
+
+hipError_t launch_colmax(const WParts& parts, int64_t d_out, int64_t d_in, float* part, float* colmax,
+                         hipStream_t stream) {
+  colmax_part_kernel<<<dim3((unsigned)((d_in + 2047) / 2048), kColSplits), 256, 0, stream>>>(parts, d_out, d_in,
+                                                                                               part);
+  colmax_final_kernel<<<(unsigned)((d_in + 255) / 256), 256, 0, stream>>>(part, d_in, colmax);
+  return hipGetLastError();
+}
+
+int64_t colmax_part_floats(int64_t d_in) { return (int64_t)kColSplits * d_in; }
+
+hipError_t launch_dw_bound(bool asym, const float* colmax, int64_t d_in, int n_cand, int mode, const float* S,
+                           const float* s_best, int n_clip, float clip_lo, const float* cs, float* bound,
+                           hipStream_t stream) {
+  dw_bound_kernel<<<(unsigned)n_cand, 256, 0, stream>>>(colmax, d_in, mode, S, s_best, n_clip, clip_lo, 0,
+                                                        asym ? 1 : 0, cs, bound);
   return hipGetLastError();
 }
 
