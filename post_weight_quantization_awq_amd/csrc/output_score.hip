@@ -639,8 +639,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     // wave w fetches A rows 48 w .. 48 w + 47 (3 loads) and B rows 32 w .. 32 w + 31 (2 loads)
     const uint32_t sA = (uint32_t)(((m0 + 48 * wave) * lda + kbeg) * 2),
                    sB = (uint32_t)(((n0 + 32 * wave) * ldb + kbeg) * 2);
+    // kEpiGram: a unit's first (long) tile runs K downwards from K_pad, its
+    // second (short) tile upwards to K_pad.  At step t every unit of an N-tile
+    // then reads B at K_pad - 32 t (first tiles) or at 32 t + 384 (n - 1) - K_pad
+    // (second tiles), whatever u is, so the units sharing a B panel fetch the
+    // same few chunks at the same time
+    const bool desc = EPI == kEpiGram && ti == 0;
     // k-tile t (clamped: past the end the ring re-fetches the last tile into a free slot)
-    auto koff = [&](int t) { return (uint32_t)((t < nk ? t : nk - 1) * kBK * 2); };
+    auto koff = [&](int t) {
+      const int tc = t < nk ? t : nk - 1;
+      return (uint32_t)((desc ? nk - 1 - tc : tc) * kBK * 2);
+    };
 
     // prologue: stages 0 and 1 in flight; wait for stage 0 (5 loads per stage
     // and wave).  On a unit's second tile every wave has passed the last
