@@ -206,9 +206,10 @@ hipError_t launch_build_dw(int group_size, bool asym, const WParts& parts, int64
 // Scaled by the power of two of this bound the largest element lands at most
 // a few octaves below 2^14, far from fp16's subnormals.
 // ---------------------------------------------------------------------------
-constexpr int kColSplits = 64;   // row slices of the column-max pass
+constexpr int kColSplits = 256;  // row slices of the column-max pass (enough blocks to fill the chip)
 
-// part[r][i] = max |W[o, i]| over the rows o of slice r, 8 columns per thread
+// part[r][i] = max |W[o, i]| over the rows o of slice r, 8 columns per thread,
+// four rows' loads in flight at a time
 __global__ __launch_bounds__(256) void colmax_part_kernel(const WParts P, int64_t d_out, int64_t d_in,
                                                          float* __restrict__ part) {
   const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
@@ -216,7 +217,20 @@ __global__ __launch_bounds__(256) void colmax_part_kernel(const WParts P, int64_
   const int64_t per = (d_out + kColSplits - 1) / kColSplits;
   const int64_t r0 = blockIdx.y * per, r1 = r0 + per < d_out ? r0 + per : d_out;
   float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t row = r0; row < r1; ++row) {
+  int64_t row = r0;
+  for (; row + 4 <= r1; row += 4) {
+    uint4 u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = *(const uint4*)(row_ptr(P, row + q, d_in) + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float w[8];
+      unpack8_f16(u[q], w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = __builtin_fmaxf(m[j], __builtin_fabsf(w[j]));
+    }
+  }
+  for (; row < r1; ++row) {
     float w[8];
     unpack8_f16(*(const uint4*)(row_ptr(P, row, d_in) + c), w);
 #pragma unroll
