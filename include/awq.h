@@ -225,7 +225,9 @@ awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, in
  * ulp of a half-integer); partial sums in fp32, final sums in fp64.  Output
  * score uses the bit-exact codes of awq_quantize_pack and contracts X with
  * (w_hat - W) on the matrix cores in fp16, each operand scaled by a power of
- * two chosen from its maximum (exact, overflow-free), fp32 accumulation, fp64
+ * two chosen from its maximum (X) or from a bound on it (dW: the column
+ * maxima of |W| and the step, never below the true maximum), so the scaling
+ * is exact and overflow-free, fp32 accumulation, fp64
  * final sums; the fp16 rounding of (w_hat - W) bounds the relative error of
  * err[k] near 1e-4 on small inputs and far below it at calibration sizes.
  * In the second-moment form (AWQ_FLAG_OUT_GRAM, or chosen by the library)

@@ -12,13 +12,15 @@
 //   1. absmax + convert_x: X is copied once to fp16 scaled by a power of two
 //      (exact for bf16 inputs in range, overflow-free), padded with zeros to
 //      whole GEMM tiles;
-//   2. build_dw (max pass, then write pass): dW_c with the same bit-exact codes
-//      as the pack kernel, scaled by a power of two from its exact maximum and
-//      rounded to fp16 -- 3 more mantissa bits than bf16 at the same matrix-core
-//      rate, which keeps the relative error of the errors near 1e-4 even for
-//      a few tokens and rows (one pass over W per candidate, negligible next to
-//      the GEMM);
-//   3. gemm_sq: fp16 MFMA 32x32x16 GEMM over all candidates of a chunk at once
+//   2. colmax + dw_bound, then build_dw: dW_c with the same bit-exact codes
+//      as the pack kernel, scaled by a power of two from a bound on its
+//      largest element (column maxima of |W|, see the bound below) and
+//      rounded to fp16 -- 3 more mantissa bits than bf16 at the same
+//      matrix-core rate, which keeps the relative error of the errors near
+//      1e-4 even for a few tokens and rows (one pass over W per candidate
+//      slice, small next to the GEMM);
+//   3. gemm_sq (direct form; section 2b holds the second-moment form):
+//      fp16 MFMA 32x32x16 GEMM over all candidates of a chunk at once
 //      (their dW stacked along N), fp32 accumulation; the epilogue squares the
 //      tile and sums each column over the tile's tokens, so the T x d_out
 //      product never reaches memory;
