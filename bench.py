@@ -64,7 +64,7 @@ SEARCH_OPS_PER_ELEM_PT_ASYM = 7
 # HBM bytes per launch of the dominant kernels, from `rocprofv3 --pmc FETCH_SIZE`
 # and `--pmc WRITE_SIZE` runs of this script (commands and tables in
 # profiles/search_weight_q_proj_4096x4096.md and
-# profiles/gemm_sq_qkv_6144x4096_output.md): KiB per dispatch, scaled by what
+# profiles/gemm_gram_qkv_mlp_output.md): KiB per dispatch, scaled by what
 # the same counters read for a plain copy of known size
 # (profiles/copy_512MiB_calibration.md).  Each entry records the sha256 of the
 # sources its kernel is built from; once those change, the counters describe
@@ -81,10 +81,17 @@ PMC_TRAFFIC = {
         "fetch_kib": 47659.7, "write_kib": 1840.0,
         "sources": ("csrc/search_weight.hip", "csrc/awq_device.h"),
         "sha256": "defe0c2e9940a8e54a9e9e972d928a3348712ea21d6d59d02dfc4e145d6bede3"},
-    ("gemm_sq_kernel", "qkv_6144x4096_output"): {
-        "fetch_kib": 11893939.4, "write_kib": 20640.0,
+    # the fused QKV output score at 16384 tokens in either form: the
+    # second-moment product (gemm_sq_kernel<1>, the default here) and the direct
+    # GEMM (gemm_sq_kernel<0>, --out-form direct); profiles/gemm_gram_qkv_mlp_output.md
+    ("gemm_sq_kernel<1>", "qkv_6144x4096_output"): {
+        "fetch_kib": 1953131.1, "write_kib": 2880.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "d4cb58e5ba2e367f0c9864a86ca3112000757f3ef4cab0790e475b593b0372ed"},
+        "sha256": "39b69e860c1dda075a2189eb3c1ee8ea4fe52b88cc9a23216bbea650fda78527"},
+    ("gemm_sq_kernel<0>", "qkv_6144x4096_output"): {
+        "fetch_kib": 11771219.3, "write_kib": 20640.0,
+        "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
+        "sha256": "39b69e860c1dda075a2189eb3c1ee8ea4fe52b88cc9a23216bbea650fda78527"},
 }
 
 
@@ -644,7 +651,8 @@ def bench_output(args, wl_name: str):
         "gemm_ms": gemm_ms,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_FP16_PEAK_TFLOPS,
-                     "traffic": pmc_traffic("gemm_sq_kernel", wl_name, args) if set(forms) == {"direct"} else None,
+                     "traffic": pmc_traffic("gemm_sq_kernel<%d>" % (forms[0] == "gram"), wl_name, args)
+                     if len(set(forms)) == 1 else None,
                      "kernel": "gemm_sq_kernel<" + ",".join("1" if f == "gram" else "0" for f in forms) + ">"},
     }
     if power is not None:
