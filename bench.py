@@ -632,7 +632,11 @@ def bench_output(args, wl_name: str):
     # the events bracket the alpha-search products (with their dW builds when chunked)
     flops_alpha = [row_flops(X, g, f) * g.d_out * 20 for (_, X, g, *_), f in zip(plans, forms)]
     tflops = sum(flops_alpha) / (sum(gemm_ms) * 1e-3) / 1e12
-    total_flops = sum(row_flops(X, g, f) * g.d_out * n_gemm + (2.0 * X.shape[0] * tri(g.d_in) if f == "gram" else 0.0)
+    # the clip search takes the direct form unless the second-moment form is forced
+    clip_form = "gram" if args.out_form == "gram" else "direct"
+    n_clip = wl.n_clip or 0
+    total_flops = sum(row_flops(X, g, f) * g.d_out * 20 + row_flops(X, g, clip_form) * g.d_out * n_clip
+                      + (2.0 * X.shape[0] * tri(g.d_in) if "gram" in (f, clip_form if n_clip else f) else 0.0)
                       for (_, X, g, *_), f in zip(plans, forms))
     direct_flops = sum(2.0 * X.shape[0] * g.d_out * g.d_in * n_gemm for _, X, g, *_ in plans)
     out = {
@@ -645,7 +649,7 @@ def bench_output(args, wl_name: str):
         "config": {"workload": wl_name, "groups": [[g.name, g.d_out, g.d_in, X.shape[0]] for _, X, g, *_ in plans],
                    "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip, "duo": args.duo,
                    "asym": args.asym, "out_form": args.out_form},
-        "output_forms": forms,
+        "output_forms": forms, "clip_form": clip_form if wl.n_clip else None,
         "step_TFLOPs_performed": total_flops / (ms_step * 1e-3) / 1e12,
         "step_TFLOPs_direct_equivalent": direct_flops / (ms_step * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,

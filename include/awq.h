@@ -103,7 +103,12 @@ typedef struct {
  *                  H = X^T X formed once (2 T d_in^2 flops), then
  *                  2 d_in^2 d_out flops per candidate: the lighter form when
  *                  the calibration set has more tokens than d_in.
- * Setting both is AWQ_EINVAL; with neither the library chooses. */
+ * Setting both is AWQ_EINVAL; with neither the library chooses the form of
+ * the alpha search by its matrix-core work and runs the clip search in the
+ * direct form: the error of a single row's form over the fp16 H grows with
+ * the conditioning of X^T X, and the clip search decides per row (the alpha
+ * search's sums over rows are carried by the well-measured rows).
+ * AWQ_FLAG_OUT_GRAM puts both searches in the second-moment form. */
 #define AWQ_FLAG_OUT_DIRECT 4
 #define AWQ_FLAG_OUT_GRAM 8
 
@@ -239,9 +244,9 @@ awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, in
  * ------------------------------------------------------------------------- */
 awq_status awq_search_workspace(const awq_search_cfg* cfg /* [host] */, int64_t d_out_total,
                                 int64_t d_in, int64_t T, size_t* bytes /* [host] */);
-/* Which form awq_search_scales takes for the output score with these
- * arguments: *form = AWQ_OUT_FORM_DIRECT or AWQ_OUT_FORM_GRAM (see
- * AWQ_FLAG_OUT_*).  Host only, enqueues nothing; AWQ_EINVAL unless
+/* Which form awq_search_scales takes for the output score's alpha search with
+ * these arguments: *form = AWQ_OUT_FORM_DIRECT or AWQ_OUT_FORM_GRAM (see
+ * AWQ_FLAG_OUT_*; the clip search is direct unless AWQ_FLAG_OUT_GRAM).  Host only, enqueues nothing; AWQ_EINVAL unless
  * cfg->score = AWQ_SCORE_OUTPUT, shape errors as awq_search_workspace. */
 #define AWQ_OUT_FORM_DIRECT 0
 #define AWQ_OUT_FORM_GRAM 1

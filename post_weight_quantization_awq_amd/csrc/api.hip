@@ -57,9 +57,12 @@ struct SearchPlan {
   int64_t T_pad, d_out_pad, K_pad, n_mt, ldc;  // output score: padded GEMM shapes, token tiles, partial ld
   int64_t n_x, n_db;    // output score: X max partials, dW bounds per candidate (1)
   int cand_chunk;       // output score: candidates per dW chunk
-  bool gram;            // output score in the second-moment form (H = X^T X)
+  bool gram;            // alpha search in the second-moment form (H = X^T X)
+  bool clip_gram;       // clip search in the second-moment form (only when forced)
+  bool need_x16, need_h;  // operands of the direct form / of the second-moment form
+  int64_t n_mt_a, n_mt_c;  // rows of column partials: alpha search, clip search
   int64_t g_T_pad, g_xt_rows, g_h_rows;  // second-moment form: token padding, Xt rows, H16 rows
-  size_t off_S, off_C2, off_tot, off_part, off_x16, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
+  size_t off_S, off_C2, off_tot, off_part, off_x16, off_xt, off_dw, off_xmax, off_dmax, off_sc, off_chunk, total;
   size_t off_h32, off_h16, off_hc, off_hr, off_cpart, off_cmax;
   bool duo;                   // duo-scaling candidates: w_mean, its scratch, the fp64 table
   size_t off_wmean, off_rmax, off_wpart, off_T, off_ext;
@@ -82,10 +85,14 @@ size_t plan_duo(SearchPlan& p, int64_t d_out, int64_t d_in, int n_grid, size_t o
 
 constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
 
-// Output score in the second-moment form?  Forced by a flag, else taken when
-// its matrix-core work (H = X^T X once, then d_in^2 per scored row) is below
-// 0.8 of the direct form's (T d_in per scored row); the margin covers its
-// extra passes (transpose of X, H to fp16).
+// Alpha search of the output score in the second-moment form?  Forced by a
+// flag, else taken when its matrix-core work (H = X^T X once, then d_in^2 per
+// scored row) is below 0.8 of the direct form's (T d_in per scored row); the
+// margin covers its extra passes (transpose of X, H to fp16).  The clip search
+// takes the direct form unless AWQ_FLAG_OUT_GRAM forces the other: it decides
+// per row, and the error of one row's quadratic form over an fp16 H grows with
+// the conditioning of X^T X (linearly; the direct form's with its square root),
+// where the alpha search's sums over rows are carried by the well-measured rows.
 // Its fp32 H and fp16 operands are addressed with 32-bit offsets.
 bool gram_fits(const SearchPlan& p) {
   const double k = (double)p.K_pad;
@@ -98,7 +105,7 @@ bool use_gram(const awq_search_cfg& cfg, const SearchPlan& p, int64_t T) {
   if (cfg.flags & AWQ_FLAG_OUT_DIRECT) return false;
   if (cfg.flags & AWQ_FLAG_OUT_GRAM) return true;
   if (!gram_fits(p)) return false;
-  const double rows = (double)(cfg.n_grid + (cfg.n_clip >= 2 ? cfg.n_clip : 0)) * (double)p.d_out_pad;
+  const double rows = (double)cfg.n_grid * (double)p.d_out_pad;
   const int64_t bm = gemm_sq_tile_rows(), bn = 256;
   const double direct = (double)p.T_pad * (double)p.K_pad * rows;
   // both products of the second-moment form run on and right of the diagonal
@@ -130,7 +137,12 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     gemm_sq_pad(T, d_out, d_in, &p.T_pad, &p.d_out_pad, &p.K_pad);
     gram_pad(T, p.K_pad, &p.g_T_pad, &p.g_xt_rows, &p.g_h_rows);
     p.gram = use_gram(cfg, p, T);
-    p.n_mt = p.gram ? gram_units(p.g_h_rows) : p.T_pad / gemm_sq_tile_rows();  // rows of column partials
+    p.clip_gram = cfg.n_clip >= 2 && (cfg.flags & AWQ_FLAG_OUT_GRAM) != 0;
+    p.need_x16 = !p.gram || (cfg.n_clip >= 2 && !p.clip_gram);
+    p.need_h = p.gram || p.clip_gram;
+    p.n_mt_a = p.gram ? gram_units(p.g_h_rows) : p.T_pad / gemm_sq_tile_rows();
+    p.n_mt_c = p.clip_gram ? gram_units(p.g_h_rows) : p.T_pad / gemm_sq_tile_rows();
+    p.n_mt = cfg.n_clip >= 2 && p.n_mt_c > p.n_mt_a ? p.n_mt_c : p.n_mt_a;  // rows of column partials
     p.n_x = absmax_blocks(T);
     p.n_db = 1;  // one bound on max |dW| per candidate
     const int max_c = cfg.n_grid > cfg.n_clip ? cfg.n_grid : cfg.n_clip;
@@ -140,10 +152,11 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     if (chunk > max_c) chunk = max_c;
     if (chunk < 1) chunk = 1;
     p.cand_chunk = (int)chunk;
-    p.off_x16 = off;  // X16 [T_pad, K_pad], or Xt [g_xt_rows, g_T_pad] in the second-moment form
-    off += align256(p.gram ? (size_t)p.g_xt_rows * p.g_T_pad * sizeof(uint16_t)
-                           : (size_t)p.T_pad * p.K_pad * sizeof(uint16_t));
-    if (p.gram) {
+    p.off_x16 = off;  // X16 [T_pad, K_pad] (direct form)
+    if (p.need_x16) off += align256((size_t)p.T_pad * p.K_pad * sizeof(uint16_t));
+    p.off_xt = off;   // Xt [g_xt_rows, g_T_pad] (second-moment form)
+    if (p.need_h) off += align256((size_t)p.g_xt_rows * p.g_T_pad * sizeof(uint16_t));
+    if (p.need_h) {
       int ns;
       int64_t slice;
       gram_slices(p.g_T_pad, p.K_pad, &ns, &slice);
@@ -425,7 +438,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   }
   if (cfg->n_clip >= 2 && !clip) return fail(AWQ_EINVAL, "clip is NULL but n_clip >= 2");
   const SearchPlan plan = plan_search(*cfg, d_out, d_in, T);
-  if (plan.output && plan.gram && !gram_fits(plan))
+  if (plan.output && plan.need_h && !gram_fits(plan))
     return fail(AWQ_ESHAPE, "second-moment output score needs d_in^2 and T*d_in below 2^31 elements");
   if (!ws || ws_bytes < plan.total) return fail(AWQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, plan.total);
   if ((uintptr_t)ws & 255u) return fail(AWQ_EALIGN, "ws not 256-byte aligned");
@@ -462,22 +475,25 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   const int G = cfg->group_size;
   const int64_t dop = plan.d_out_pad, kp = plan.K_pad;
   // second-moment form: H = X^T X once, dW columns scaled by hc = sqrt(diag H)
-  const float* hc = plan.gram ? (const float*)(base + plan.off_hc) : nullptr;
-  const uint16_t* h16 = plan.gram ? (const uint16_t*)(base + plan.off_h16) : nullptr;
-  auto product = [&](int64_t n_cols, float* part) -> hipError_t {
-    return plan.gram ? launch_gemm_gram(h16, plan.g_h_rows, kp, dw, n_cols, part, plan.ldc, s)
-                     : launch_gemm_sq(x16, plan.T_pad, kp, dw, n_cols, part, plan.ldc, s);
+  const float* hc = plan.need_h ? (const float*)(base + plan.off_hc) : nullptr;
+  const uint16_t* h16 = plan.need_h ? (const uint16_t*)(base + plan.off_h16) : nullptr;
+  auto product = [&](bool gram, int64_t n_cols, float* part) -> hipError_t {
+    return gram ? launch_gemm_gram(h16, plan.g_h_rows, kp, dw, n_cols, part, plan.ldc, s)
+                : launch_gemm_sq(x16, plan.T_pad, kp, dw, n_cols, part, plan.ldc, s);
   };
+  const float* hc_a = plan.gram ? hc : nullptr;
+  const float* hc_c = plan.clip_gram ? hc : nullptr;
   if ((e = launch_cands(*cfg, plan, parts, d_out, d_in, x_mean, base, S, nullptr, s)) != hipSuccess)
     return hip_status(e, "candidates");
   if ((e = launch_prepare_x(X, bf16, T, d_in, ld_x, xmax, s)) != hipSuccess) return hip_status(e, "absmax(X)");
-  if (plan.gram) {
+  if (plan.need_h) {
+    uint16_t* xt = (uint16_t*)(base + plan.off_xt);
     if ((e = launch_out_scales(xmax, plan.n_x, nullptr, 0, 1, sc_a, s)) != hipSuccess)
       return hip_status(e, "out_scales(X)");
-    if ((e = launch_transpose_x(X, bf16, T, d_in, ld_x, plan.g_T_pad, plan.g_xt_rows, sc_a, x16, s)) != hipSuccess)
+    if ((e = launch_transpose_x(X, bf16, T, d_in, ld_x, plan.g_T_pad, plan.g_xt_rows, sc_a, xt, s)) != hipSuccess)
       return hip_status(e, "transpose_x");
     float* h32 = (float*)(base + plan.off_h32);
-    if ((e = launch_gemm_gram_h(x16, plan.g_T_pad, kp, h32, s)) != hipSuccess) return hip_status(e, "gemm(H)");
+    if ((e = launch_gemm_gram_h(xt, plan.g_T_pad, kp, h32, s)) != hipSuccess) return hip_status(e, "gemm(H)");
     if ((e = launch_gram_scale(h32, plan.g_T_pad, kp, plan.g_h_rows, (float*)(base + plan.off_hc),
                                (float*)(base + plan.off_hr), (uint16_t*)h16, s)) != hipSuccess)
       return hip_status(e, "gram_scale");
@@ -485,35 +501,35 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   float* cmax = (float*)(base + plan.off_cmax);
   if ((e = launch_colmax(parts, d_out, d_in, (float*)(base + plan.off_cpart), cmax, s)) != hipSuccess)
     return hip_status(e, "colmax");
-  if ((e = launch_dw_bound(asym, cmax, d_in, cfg->n_grid, 0, S, nullptr, 0, 1.0f, hc, dmax, s)) != hipSuccess)
+  if ((e = launch_dw_bound(asym, cmax, d_in, cfg->n_grid, 0, S, nullptr, 0, 1.0f, hc_a, dmax, s)) != hipSuccess)
     return hip_status(e, "dw_bound");
   if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, cfg->n_grid, sc_a, s)) != hipSuccess)
     return hip_status(e, "out_scales");
-  if (!plan.gram && (e = launch_convert_x(X, bf16, T, d_in, ld_x, plan.T_pad, kp, sc_a, x16, s)) != hipSuccess)
+  if (plan.need_x16 && (e = launch_convert_x(X, bf16, T, d_in, ld_x, plan.T_pad, kp, sc_a, x16, s)) != hipSuccess)
     return hip_status(e, "convert_x");
   const bool one_chunk = plan.cand_chunk >= cfg->n_grid;
   if (!one_chunk) mark(true, s);
   for (int c0 = 0; c0 < cfg->n_grid; c0 += plan.cand_chunk) {
     const int nc = (cfg->n_grid - c0) < plan.cand_chunk ? (cfg->n_grid - c0) : plan.cand_chunk;
-    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, hc, dw, s)) !=
+    if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 0, S, nullptr, 0, 1.0f, c0, sc_a, hc_a, dw, s)) !=
         hipSuccess)
       return hip_status(e, "build_dw");
     if (one_chunk) mark(true, s);
-    e = product((int64_t)nc * dop, colpart + (int64_t)c0 * dop);
+    e = product(plan.gram, (int64_t)nc * dop, colpart + (int64_t)c0 * dop);
     if (one_chunk) mark(false, s);
     if (e != hipSuccess) return hip_status(e, "gemm_sq");
   }
   if (!one_chunk) mark(false, s);
   double* chunk_sum = (double*)(base + plan.off_chunk);
   const int64_t nch = reduce_cols_chunks(d_out);
-  if ((e = launch_reduce_cols(colpart, plan.n_mt, plan.ldc, d_out, dop, cfg->n_grid, chunk_sum, s)) != hipSuccess)
+  if ((e = launch_reduce_cols(colpart, plan.n_mt_a, plan.ldc, d_out, dop, cfg->n_grid, chunk_sum, s)) != hipSuccess)
     return hip_status(e, "reduce_cols");
   if ((e = launch_select(chunk_sum, nch, cfg->n_grid, 1.0 / ((double)T * (double)d_out), sc_a->inv, tot, err,
                          best_idx, S, d_in, best_s, s)) != hipSuccess)
     return hip_status(e, "select");
   if (cfg->n_clip >= 2) {
     const int nclip = cfg->n_clip;
-    if ((e = launch_dw_bound(asym, cmax, d_in, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, hc, dmax, s)) !=
+    if ((e = launch_dw_bound(asym, cmax, d_in, nclip, 1, nullptr, best_s, nclip, cfg->clip_lo, hc_c, dmax, s)) !=
         hipSuccess)
       return hip_status(e, "dw_bound(clip)");
     if ((e = launch_out_scales(xmax, plan.n_x, dmax, plan.n_db, nclip, sc_c, s)) != hipSuccess)
@@ -521,12 +537,12 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
     for (int c0 = 0; c0 < nclip; c0 += plan.cand_chunk) {
       const int nc = (nclip - c0) < plan.cand_chunk ? (nclip - c0) : plan.cand_chunk;
       if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0,
-                               sc_c, hc, dw, s)) != hipSuccess)
+                               sc_c, hc_c, dw, s)) != hipSuccess)
         return hip_status(e, "build_dw(clip)");
-      if ((e = product((int64_t)nc * dop, colpart + (int64_t)c0 * dop)) != hipSuccess)
+      if ((e = product(plan.clip_gram, (int64_t)nc * dop, colpart + (int64_t)c0 * dop)) != hipSuccess)
         return hip_status(e, "gemm_sq(clip)");
     }
-    if ((e = launch_clip_select(colpart, plan.n_mt, plan.ldc, d_out, dop, nclip, cfg->clip_lo, sc_c, clip, clip_err,
+    if ((e = launch_clip_select(colpart, plan.n_mt_c, plan.ldc, d_out, dop, nclip, cfg->clip_lo, sc_c, clip, clip_err,
                                 s)) != hipSuccess)
       return hip_status(e, "clip_select");
   }

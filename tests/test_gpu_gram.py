@@ -113,6 +113,55 @@ def test_output_forms_agree_and_auto(A):
         assert argmin_ok(int(host(r.best_idx)[0]), errs, k)
 
 
+@pytest.mark.parametrize("out_form", ["auto", "direct"])
+@pytest.mark.parametrize("rank,noise", [(16, 0.05), (64, 0.1)])
+def test_output_correlated_channels(A, out_form, rank, noise):
+    """Correlated input channels (a rank-r mix plus noise, so H = X^T X is far
+    from diagonal): the library's default (the alpha search in the
+    second-moment form at this shape, the clip search in the direct form) and
+    the direct form throughout, against the oracle at the output-score bars,
+    per-row clip errors included."""
+    parts, d_in, T, G = [160, 96], 768, 1024, 128
+    say(f"output score, correlated channels rank={rank} noise={noise} ({out_form} form)")
+    if out_form == "auto":
+        assert A.search_output_form(sum(parts), d_in, T, group_size=G, n_clip=20) == "gram"
+    Ws = [WL.make_weight(1500 + i, r, d_in) for i, r in enumerate(parts)]
+    W = np.concatenate(Ws, axis=0)
+    X = WL.make_correlated_activations(1550 + rank, T, d_in, rank, noise)
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          n_clip=20, want_clip_err=True, out_form=out_form)
+    errs, k, _ = O.search_scales(Ws, xm, G, 20, "output", X=X)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    g_k = int(host(res.best_idx)[0])
+    assert argmin_ok(g_k, errs, k)
+    s = O.candidate_scales(xm, 20)[g_k]
+    E, _ = O.clip_search(W, s, X, G, 20, 0.5)
+    np.testing.assert_allclose(host(res.clip_err).astype(np.float64), E, rtol=1e-3)
+    g_c = host(res.clip)
+    ratios = O.clip_ratios(20, 0.5)
+    for o in range(W.shape[0]):
+        gj = int(np.nonzero(ratios == g_c[o])[0][0])
+        assert argmin_ok(gj, E[o], O.first_argmin(E[o]), rel=1e-4), o
+
+
+def test_gram_alpha_errors_ill_conditioned(A):
+    """A rank-4 mix with 1% noise (X^T X conditioned ~10^4): one row's quadratic
+    form over the fp16 H loses accuracy with the conditioning (why the clip
+    search stays in the direct form by default), but the alpha search's errors,
+    sums over all rows, stay within the bar in the forced second-moment form."""
+    parts, d_in, T, G = [160, 96], 768, 1024, 128
+    say("alpha errors, second-moment form forced, rank-4 activations")
+    Ws = [WL.make_weight(1500 + i, r, d_in) for i, r in enumerate(parts)]
+    X = WL.make_correlated_activations(1554, T, d_in, 4, 0.01)
+    xm = O.act_stats(X)
+    res = A.search_scales([dev_f16(p) for p in Ws], dev_f32(xm), group_size=G, score="output", X=dev_x(X),
+                          out_form="gram")
+    errs, k, _ = O.search_scales(Ws, xm, G, 20, "output", X=X)
+    np.testing.assert_allclose(host(res.err).astype(np.float64), errs, rtol=1e-3)
+    assert argmin_ok(int(host(res.best_idx)[0]), errs, k)
+
+
 def test_gram_dead_channel(A):
     """An input channel that is zero in every token has H_ii = 0: its column of
     dW and its row and column of H drop out (scale 0), as they do from X dW^T."""

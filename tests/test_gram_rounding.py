@@ -75,3 +75,20 @@ def test_second_moment_identity_exact():
     tri = np.where(blk[None, :] > blk[:, None], 2.0, 1.0) * (blk[None, :] >= blk[:, None])
     rows = np.einsum("oi,ij,oj->o", dW, H * tri, dW)
     np.testing.assert_allclose(rows, ((X @ dW.T) ** 2).sum(axis=0), rtol=1e-10)
+
+
+def test_second_moment_form_roundings_correlated_channels():
+    """Activations whose channels are strongly correlated (a rank-4 mix plus 1%
+    noise: H far from diagonal, off-diagonal entries as large as the diagonal
+    ones): the fp16 rounding of H'' still leaves the 20 errors -- sums over all
+    rows -- within the bar (single rows are not: the clip search, which
+    decides per row, stays in the direct form by default)."""
+    d_out, d_in, T, G = 160, 768, 1024, 128
+    W = WL.make_weight(41, d_out, d_in)
+    X = WL.make_correlated_activations(42, T, d_in, rank=4, noise=0.01)
+    xm = O.act_stats(X)
+    errs, k, _ = O.search_scales([W], xm, G, 20, "output", X=X)
+    got = _device_form_errors(W, X, O.candidate_scales(xm, 20), G)
+    np.testing.assert_allclose(got, errs, rtol=1e-3)
+    gk = int(np.argmin(got))
+    assert gk == k or errs[gk] <= errs[k] * (1 + 1e-4)

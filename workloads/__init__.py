@@ -80,6 +80,23 @@ def make_activations(seed: int, T: int, d_in: int, dtype: str = "bf16",
     raise ValueError(dtype)
 
 
+def make_correlated_activations(seed: int, T: int, d_in: int, rank: int, noise: float,
+                                dtype: str = "bf16") -> np.ndarray:
+    """X[T, d_in] with strongly correlated channels: a rank-`rank` mix Z M
+    (Z [T, rank] ~ N(0, 1), M [rank, d_in] ~ N(0, 1) times the per-channel
+    magnitudes, outliers included) plus `noise` times independent N(0, 1);
+    bf16 bits (uint16) or float16."""
+    g = rng(seed)
+    z = g.standard_normal((T, rank), dtype=np.float32)
+    m = g.standard_normal((rank, d_in), dtype=np.float32) * make_magnitudes(seed + 7, d_in)[None, :]
+    x = z @ m + np.float32(noise) * g.standard_normal((T, d_in), dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    raise ValueError(dtype)
+
+
 def activations_to_f32(X: np.ndarray) -> np.ndarray:
     if X.dtype == np.uint16:
         return bf16_bits_to_f32(X)
