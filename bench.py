@@ -619,25 +619,26 @@ def bench_output(args, wl_name: str):
     # and scores each row against it, both on and right of H's diagonal
     # 384-blocks only (H is symmetric): 2 tri(d_in) flops per scored row and
     # 2 T tri(d_in) for H, tri(d) = sum over blocks I of rows(I) (d - 384 I)
-    forms = [A.search_output_form(g.d_out, g.d_in, X.shape[0], group_size=G, n_clip=wl.n_clip, duo=args.duo,
+    both = [A.search_output_forms(g.d_out, g.d_in, X.shape[0], group_size=G, n_clip=wl.n_clip, duo=args.duo,
                                   asym=args.asym, out_form=args.out_form) for _, X, g, *_ in plans]
+    forms = [a for a, _ in both]
+    clip_forms = [c for _, c in both]
     n_gemm = 20 + (wl.n_clip or 0)
 
     def tri(d):
         return float(sum(min(384, d - b) * (d - b) for b in range(0, d, 384)))
 
-    def row_flops(X, g, form):  # per scored output row
-        return 2.0 * (tri(g.d_in) if form == "gram" else X.shape[0] * g.d_in)
+    def row_flops(X, g, form, parts=1):  # per scored output row (the clip search's H in `parts` fp16 parts)
+        return 2.0 * (parts * tri(g.d_in) if form == "gram" else X.shape[0] * g.d_in)
 
     # the events bracket the alpha-search products (with their dW builds when chunked)
     flops_alpha = [row_flops(X, g, f) * g.d_out * 20 for (_, X, g, *_), f in zip(plans, forms)]
     tflops = sum(flops_alpha) / (sum(gemm_ms) * 1e-3) / 1e12
-    # the clip search takes the direct form unless the second-moment form is forced
-    clip_form = "gram" if args.out_form == "gram" else "direct"
     n_clip = wl.n_clip or 0
-    total_flops = sum(row_flops(X, g, f) * g.d_out * 20 + row_flops(X, g, clip_form) * g.d_out * n_clip
-                      + (2.0 * X.shape[0] * tri(g.d_in) if "gram" in (f, clip_form if n_clip else f) else 0.0)
-                      for (_, X, g, *_), f in zip(plans, forms))
+    total_flops = sum(row_flops(X, g, f) * g.d_out * 20
+                      + (row_flops(X, g, cf, 2) * g.d_out * n_clip if n_clip else 0.0)
+                      + (2.0 * X.shape[0] * tri(g.d_in) if "gram" in (f, cf) else 0.0)
+                      for (_, X, g, *_), f, cf in zip(plans, forms, clip_forms))
     direct_flops = sum(2.0 * X.shape[0] * g.d_out * g.d_in * n_gemm for _, X, g, *_ in plans)
     out = {
         "metric": METRIC,
@@ -649,7 +650,7 @@ def bench_output(args, wl_name: str):
         "config": {"workload": wl_name, "groups": [[g.name, g.d_out, g.d_in, X.shape[0]] for _, X, g, *_ in plans],
                    "group_size": G, "n_grid": 20, "score": "output", "n_clip": wl.n_clip, "duo": args.duo,
                    "asym": args.asym, "out_form": args.out_form},
-        "output_forms": forms, "clip_form": clip_form if wl.n_clip else None,
+        "output_forms": forms, "clip_forms": clip_forms if wl.n_clip else None,
         "step_TFLOPs_performed": total_flops / (ms_step * 1e-3) / 1e12,
         "step_TFLOPs_direct_equivalent": direct_flops / (ms_step * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,

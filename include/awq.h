@@ -103,12 +103,13 @@ typedef struct {
  *                  H = X^T X formed once (2 T d_in^2 flops), then
  *                  2 d_in^2 d_out flops per candidate: the lighter form when
  *                  the calibration set has more tokens than d_in.
- * Setting both is AWQ_EINVAL; with neither the library chooses the form of
- * the alpha search by its matrix-core work and runs the clip search in the
- * direct form: the error of a single row's form over the fp16 H grows with
- * the conditioning of X^T X, and the clip search decides per row (the alpha
- * search's sums over rows are carried by the well-measured rows).
- * AWQ_FLAG_OUT_GRAM puts both searches in the second-moment form. */
+ * Setting both is AWQ_EINVAL; with neither the library chooses each search's
+ * form by its matrix-core work.  The alpha search compares sums over rows,
+ * which the well-measured rows carry, and takes H (normalised) in fp16; the
+ * clip search decides per row, and the error of a single row's form over H
+ * grows with the conditioning of X^T X, so it takes H as two fp16 parts
+ * (hi + lo, twice the products).  AWQ_FLAG_OUT_GRAM puts both searches in the
+ * second-moment form. */
 #define AWQ_FLAG_OUT_DIRECT 4
 #define AWQ_FLAG_OUT_GRAM 8
 
@@ -244,12 +245,15 @@ awq_status awq_candidate_scales_duo(const float* x_mean, const float* w_mean, in
  * ------------------------------------------------------------------------- */
 awq_status awq_search_workspace(const awq_search_cfg* cfg /* [host] */, int64_t d_out_total,
                                 int64_t d_in, int64_t T, size_t* bytes /* [host] */);
-/* Which form awq_search_scales takes for the output score's alpha search with
- * these arguments: *form = AWQ_OUT_FORM_DIRECT or AWQ_OUT_FORM_GRAM (see
- * AWQ_FLAG_OUT_*; the clip search is direct unless AWQ_FLAG_OUT_GRAM).  Host only, enqueues nothing; AWQ_EINVAL unless
- * cfg->score = AWQ_SCORE_OUTPUT, shape errors as awq_search_workspace. */
+/* Which forms awq_search_scales takes for the output score with these
+ * arguments (see AWQ_FLAG_OUT_*): *form = AWQ_OUT_FORM_GRAM if the alpha
+ * search is in the second-moment form (else AWQ_OUT_FORM_DIRECT), plus
+ * AWQ_OUT_FORM_CLIP_GRAM if the clip search (n_clip >= 2) is.  Host only,
+ * enqueues nothing; AWQ_EINVAL unless cfg->score = AWQ_SCORE_OUTPUT, shape
+ * errors as awq_search_workspace. */
 #define AWQ_OUT_FORM_DIRECT 0
 #define AWQ_OUT_FORM_GRAM 1
+#define AWQ_OUT_FORM_CLIP_GRAM 2
 awq_status awq_search_output_form(const awq_search_cfg* cfg /* [host] */, int64_t d_out_total, int64_t d_in,
                                   int64_t T, int32_t* form /* [host] */);
 awq_status awq_search_scales(const awq_search_cfg* cfg /* [host] */, const awq_wgroup* W /* [host] */,

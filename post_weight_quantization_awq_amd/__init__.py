@@ -324,11 +324,20 @@ def search_workspace_bytes(d_out: int, d_in: int, T: int = 0, *, group_size: int
 def search_output_form(d_out: int, d_in: int, T: int, *, group_size: int = 128, n_grid: int = 20, n_clip: int = 0,
                        clip_lo: float = 0.5, s_min: float = 1e-4, duo: bool = False, asym: bool = False,
                        out_form: str = "auto") -> str:
-    """The form the output-score search takes for these arguments: "direct" or "gram"."""
+    """The form the output-score alpha search takes for these arguments: "direct" or "gram"."""
+    return search_output_forms(d_out, d_in, T, group_size=group_size, n_grid=n_grid, n_clip=n_clip,
+                               clip_lo=clip_lo, s_min=s_min, duo=duo, asym=asym, out_form=out_form)[0]
+
+
+def search_output_forms(d_out: int, d_in: int, T: int, *, group_size: int = 128, n_grid: int = 20, n_clip: int = 0,
+                        clip_lo: float = 0.5, s_min: float = 1e-4, duo: bool = False, asym: bool = False,
+                        out_form: str = "auto"):
+    """(alpha search form, clip search form or None): "direct" or "gram" each."""
     cfg = _cfg(group_size, n_grid, "output", n_clip, clip_lo, s_min, duo, asym, out_form)
     f = ctypes.c_int32()
     _check(lib().awq_search_output_form(ctypes.byref(cfg), d_out, d_in, T, ctypes.byref(f)))
-    return "gram" if f.value == 1 else "direct"
+    return ("gram" if f.value & 1 else "direct",
+            ("gram" if f.value & 2 else "direct") if n_clip >= 2 else None)
 
 
 class SearchPlan(_Prepared):

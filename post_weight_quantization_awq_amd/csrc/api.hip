@@ -89,15 +89,30 @@ constexpr size_t kDwBudget = (size_t)2 << 30;  // bytes of dW per chunk (2 GiB)
 // flag, else taken when its matrix-core work (H = X^T X once, then d_in^2 per
 // scored row) is below 0.8 of the direct form's (T d_in per scored row); the
 // margin covers its extra passes (transpose of X, H to fp16).  The clip search
-// takes the direct form unless AWQ_FLAG_OUT_GRAM forces the other: it decides
-// per row, and the error of one row's quadratic form over an fp16 H grows with
-// the conditioning of X^T X (linearly; the direct form's with its square root),
-// where the alpha search's sums over rows are carried by the well-measured rows.
+// decides per row, and the error of one row's quadratic form over an fp16 H''
+// grows with the conditioning of X^T X (linearly; the direct form's with its
+// square root), where the alpha search's sums over rows are carried by the
+// well-measured rows: in the second-moment form the clip search takes H'' as
+// hi + lo parts (use_gram_clip).
 // Its fp32 H and fp16 operands are addressed with 32-bit offsets.
 bool gram_fits(const SearchPlan& p) {
   const double k = (double)p.K_pad;
-  return k * k < 2147483648.0 && (double)p.g_h_rows * k * 2.0 < 4294967296.0 &&
+  return k * k < 2147483648.0 && (double)p.g_h_rows * k * 4.0 < 4294967296.0 &&
          (double)p.g_xt_rows * (double)p.g_T_pad * 2.0 < 4294967296.0;
+}
+
+// Matrix-core work (multiply-adds) of the second-moment form for `rows` scored
+// rows: H's tiles on and right of the diagonal blocks (once per search, when
+// `with_h`), then K from each row tile's diagonal block on, `parts` times
+// (1: H'' in fp16; 2: hi + lo)
+double gram_work(const SearchPlan& p, double rows, int parts, bool with_h) {
+  const int64_t bm = gemm_sq_tile_rows(), bn = 256;
+  double h_tiles = 0.0, k_cols = 0.0;
+  for (int64_t m0 = 0; m0 < p.g_h_rows; m0 += bm) {
+    for (int64_t n0 = 0; n0 < p.K_pad; n0 += bn) h_tiles += (n0 + bn > m0) ? 1.0 : 0.0;
+    k_cols += (double)(p.K_pad - m0);
+  }
+  return (with_h ? h_tiles * (double)(bm * bn) * (double)p.g_T_pad : 0.0) + parts * (double)bm * k_cols * rows;
 }
 
 bool use_gram(const awq_search_cfg& cfg, const SearchPlan& p, int64_t T) {
@@ -106,17 +121,19 @@ bool use_gram(const awq_search_cfg& cfg, const SearchPlan& p, int64_t T) {
   if (cfg.flags & AWQ_FLAG_OUT_GRAM) return true;
   if (!gram_fits(p)) return false;
   const double rows = (double)cfg.n_grid * (double)p.d_out_pad;
-  const int64_t bm = gemm_sq_tile_rows(), bn = 256;
-  const double direct = (double)p.T_pad * (double)p.K_pad * rows;
-  // both products of the second-moment form run on and right of the diagonal
-  // blocks only: H's 384 x 256 tiles with n0 + 256 > m0, and K from m0 on
-  double h_tiles = 0.0, k_cols = 0.0;
-  for (int64_t m0 = 0; m0 < p.g_h_rows; m0 += bm) {
-    for (int64_t n0 = 0; n0 < p.K_pad; n0 += bn) h_tiles += (n0 + bn > m0) ? 1.0 : 0.0;
-    k_cols += (double)(p.K_pad - m0);
-  }
-  const double gram = h_tiles * (double)(bm * bn) * (double)p.g_T_pad + (double)bm * k_cols * rows;
-  return gram < 0.8 * direct;
+  return gram_work(p, rows, 1, true) < 0.8 * (double)p.T_pad * (double)p.K_pad * rows;
+}
+
+// The clip search in the second-moment form takes H'' as hi + lo (twice the
+// products of the alpha search's form): taken when that is below 0.6 of the
+// direct form's work (its product runs at a lower fraction of the matrix-core
+// peak than the direct GEMM), H counted only if the alpha search did not form it.
+bool use_gram_clip(const awq_search_cfg& cfg, const SearchPlan& p) {
+  if (cfg.n_clip < 2 || (cfg.flags & AWQ_FLAG_OUT_DIRECT)) return false;
+  if (cfg.flags & AWQ_FLAG_OUT_GRAM) return true;
+  if (!gram_fits(p)) return false;
+  const double rows = (double)cfg.n_clip * (double)p.d_out_pad;
+  return gram_work(p, rows, 2, !p.gram) < 0.6 * (double)p.T_pad * (double)p.K_pad * rows;
 }
 
 SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, int64_t T) {
@@ -137,7 +154,7 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
     gemm_sq_pad(T, d_out, d_in, &p.T_pad, &p.d_out_pad, &p.K_pad);
     gram_pad(T, p.K_pad, &p.g_T_pad, &p.g_xt_rows, &p.g_h_rows);
     p.gram = use_gram(cfg, p, T);
-    p.clip_gram = cfg.n_clip >= 2 && (cfg.flags & AWQ_FLAG_OUT_GRAM) != 0;
+    p.clip_gram = use_gram_clip(cfg, p);
     p.need_x16 = !p.gram || (cfg.n_clip >= 2 && !p.clip_gram);
     p.need_h = p.gram || p.clip_gram;
     p.n_mt_a = p.gram ? gram_units(p.g_h_rows) : p.T_pad / gemm_sq_tile_rows();
@@ -162,8 +179,8 @@ SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, i
       gram_slices(p.g_T_pad, p.K_pad, &ns, &slice);
       p.off_h32 = off;
       off += align256((size_t)ns * p.K_pad * p.K_pad * sizeof(float));
-      p.off_h16 = off;
-      off += align256((size_t)p.g_h_rows * p.K_pad * sizeof(uint16_t));
+      p.off_h16 = off;  // hi and lo parts
+      off += align256((size_t)p.g_h_rows * 2 * p.K_pad * sizeof(uint16_t));
       p.off_hc = off;
       off += align256((size_t)p.K_pad * sizeof(float));
       p.off_hr = off;
@@ -393,7 +410,8 @@ awq_status awq_search_output_form(const awq_search_cfg* cfg, int64_t d_out_total
   if (d_out_total < 1 || d_in < 1) return fail(AWQ_EINVAL, "need d_out_total >= 1 and d_in >= 1");
   if (d_in % cfg->group_size) return fail(AWQ_ESHAPE, "d_in %lld not a multiple of group_size %d", (long long)d_in, cfg->group_size);
   if (T < 1) return fail(AWQ_EINVAL, "output score needs T >= 1");
-  *form = plan_search(*cfg, d_out_total, d_in, T).gram ? AWQ_OUT_FORM_GRAM : AWQ_OUT_FORM_DIRECT;
+  const SearchPlan p = plan_search(*cfg, d_out_total, d_in, T);
+  *form = (p.gram ? AWQ_OUT_FORM_GRAM : AWQ_OUT_FORM_DIRECT) | (p.clip_gram ? AWQ_OUT_FORM_CLIP_GRAM : 0);
   return ok();
 }
 
@@ -477,8 +495,10 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
   // second-moment form: H = X^T X once, dW columns scaled by hc = sqrt(diag H)
   const float* hc = plan.need_h ? (const float*)(base + plan.off_hc) : nullptr;
   const uint16_t* h16 = plan.need_h ? (const uint16_t*)(base + plan.off_h16) : nullptr;
-  auto product = [&](bool gram, int64_t n_cols, float* part) -> hipError_t {
-    return gram ? launch_gemm_gram(h16, plan.g_h_rows, kp, dw, n_cols, part, plan.ldc, s)
+  // the alpha search's sums over rows take H'' in fp16; the clip search's
+  // per-row forms take it as hi + lo
+  auto product = [&](bool gram, bool split, int64_t n_cols, float* part) -> hipError_t {
+    return gram ? launch_gemm_gram(h16, plan.g_h_rows, kp, dw, n_cols, part, plan.ldc, split, s)
                 : launch_gemm_sq(x16, plan.T_pad, kp, dw, n_cols, part, plan.ldc, s);
   };
   const float* hc_a = plan.gram ? hc : nullptr;
@@ -515,7 +535,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
         hipSuccess)
       return hip_status(e, "build_dw");
     if (one_chunk) mark(true, s);
-    e = product(plan.gram, (int64_t)nc * dop, colpart + (int64_t)c0 * dop);
+    e = product(plan.gram, false, (int64_t)nc * dop, colpart + (int64_t)c0 * dop);
     if (one_chunk) mark(false, s);
     if (e != hipSuccess) return hip_status(e, "gemm_sq");
   }
@@ -539,7 +559,7 @@ awq_status awq_search_scales(const awq_search_cfg* cfg, const awq_wgroup* W, int
       if ((e = launch_build_dw(G, asym, parts, d_out, d_in, dop, kp, nc, 1, nullptr, best_s, nclip, cfg->clip_lo, c0,
                                sc_c, hc_c, dw, s)) != hipSuccess)
         return hip_status(e, "build_dw(clip)");
-      if ((e = product(plan.clip_gram, (int64_t)nc * dop, colpart + (int64_t)c0 * dop)) != hipSuccess)
+      if ((e = product(plan.clip_gram, true, (int64_t)nc * dop, colpart + (int64_t)c0 * dop)) != hipSuccess)
         return hip_status(e, "gemm_sq(clip)");
     }
     if ((e = launch_clip_select(colpart, plan.n_mt_c, plan.ldc, d_out, dop, nclip, cfg->clip_lo, sc_c, clip, clip_err,

@@ -576,7 +576,14 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* B
 //   kEpiStore: out[m * ldc + n] = C[m, n] for m, n < lim (H = Xt Xt^T in
 //              fp32); tiles wholly left of their rows' diagonal block
 //              (n0 + 256 <= m0) are not needed and not launched.
-constexpr int kEpiSq = 0, kEpiGram = 1, kEpiStore = 2;
+//   kEpiGram2: kEpiGram with H'' in two fp16 parts, hi + lo (row m of A holds
+//              hi in columns 0 .. K-1 and lo in K .. 2K-1): the stages
+//              alternate hi and lo over the same dW' chunk, so the product is
+//              exact to about 2^-22 of H'' instead of 2^-11 -- the accuracy
+//              of single rows' forms, which the per-row clip search needs.
+// The kEpiGram forms read A rows lda = 2 K apart (the same H'' buffer; kEpiGram
+// uses the hi part only).
+constexpr int kEpiSq = 0, kEpiGram = 1, kEpiStore = 2, kEpiGram2 = 3;
 
 // kEpiStore splits K over blockIdx.y: slice y takes K columns [y kslice,
 // (y + 1) kslice) and stores its partial product at out + y lim ldc.
@@ -602,9 +609,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
   // number of row tiles, n_mt = ceil(kslice / 2) units): their K ranges from
   // the diagonal block on sum to the same length for every unit, so all
   // blocks carry the same work; the middle tile of an odd count is alone
+  constexpr bool kGram = EPI == kEpiGram || EPI == kEpiGram2;
   int64_t mts[2] = {mu, mu};
   int ntile = 1;
-  if constexpr (EPI == kEpiGram) {
+  if constexpr (kGram) {
     mts[1] = kslice - 1 - mu;
     ntile = mts[1] != mu ? 2 : 1;
   }
@@ -626,9 +634,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 96 x 128
-  const uint32_t ld2 = (uint32_t)(lda * 2);
-  const uint32_t vo = (uint32_t)((lane >> 2) * ld2 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
-  const uint32_t row16 = 16 * ld2;
+  // per-lane byte offset and 16-row stride of the DMA loads, for A and for B
+  // (the second-moment product's A rows are 2 K apart, its B rows K apart)
+  const uint32_t ld2 = (uint32_t)(lda * 2), ldb2 = (uint32_t)(ldb * 2);
+  const uint32_t swz_off = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  const uint32_t vo = (uint32_t)(lane >> 2) * ld2 + swz_off, voB = (uint32_t)(lane >> 2) * ldb2 + swz_off;
+  const uint32_t row16 = 16 * ld2, row16B = 16 * ldb2;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, a_bytes);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, b_bytes);
   float csum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this lane's column sums over the unit's tiles
@@ -637,7 +648,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     const int64_t m0 = mts[ti] * kBM;
     // K range: from the diagonal block on for the triangular quadratic form,
     // the block's slice for the split product
-    int64_t kbeg = EPI == kEpiGram ? m0 : 0, kend = K;
+    int64_t kbeg = kGram ? m0 : 0, kend = K;
     if constexpr (EPI == kEpiStore) {
       kbeg = (int64_t)blockIdx.y * kslice;
       kend = kbeg + kslice < K ? kbeg + kslice : K;
@@ -651,7 +662,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nk = (int)((kend - kbeg) / kBK);
+    const int nk = (int)((kend - kbeg) / kBK);         // K chunks
+    const int nks = (EPI == kEpiGram2 ? 2 : 1) * nk;     // stages (hi and lo per chunk)
     // wave w fetches A rows 48 w .. 48 w + 47 (3 loads) and B rows 32 w .. 32 w + 31 (2 loads)
     const uint32_t sA = (uint32_t)(((m0 + 48 * wave) * lda + kbeg) * 2),
                    sB = (uint32_t)(((n0 + 32 * wave) * ldb + kbeg) * 2);
@@ -660,20 +672,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     // then reads B at K_pad - 32 t (first tiles) or at 32 t + 384 (n - 1) - K_pad
     // (second tiles), whatever u is, so the units sharing a B panel fetch the
     // same few chunks at the same time
-    const bool desc = EPI == kEpiGram && ti == 0;
-    // k-tile t (clamped: past the end the ring re-fetches the last tile into a free slot)
-    auto koff = [&](int t) {
-      const int tc = t < nk ? t : nk - 1;
-      return (uint32_t)((desc ? nk - 1 - tc : tc) * kBK * 2);
+    const bool desc = kGram && ti == 0;
+    // stage t (clamped: past the end the ring re-fetches the last stage into
+    // a free slot): its K chunk, the same for A and B, and for kEpiGram2 the
+    // part of A (hi on even stages, lo on odd ones, K columns further)
+    auto koffB = [&](int t) {
+      const int tc = t < nks ? t : nks - 1;
+      const int c = EPI == kEpiGram2 ? (tc >> 1) : tc;
+      return (uint32_t)((desc ? nk - 1 - c : c) * kBK * 2);
+    };
+    auto koffA = [&](int t) {
+      const int tc = t < nks ? t : nks - 1;
+      return koffB(t) + ((EPI == kEpiGram2 && (tc & 1)) ? (uint32_t)(K * 2) : 0u);
     };
 
     // prologue: stages 0 and 1 in flight; wait for stage 0 (5 loads per stage
     // and wave).  On a unit's second tile every wave has passed the last
     // stage's barrier, so no fragment read of the ring is outstanding.
-    dma_rows<3>(rsA, sA0, 48 * wave, vo, sA + koff(0), row16);
-    dma_rows<2>(rsB, sB0, 32 * wave, vo, sB + koff(0), row16);
-    dma_rows<3>(rsA, sA1, 48 * wave, vo, sA + koff(1), row16);
-    dma_rows<2>(rsB, sB1, 32 * wave, vo, sB + koff(1), row16);
+    dma_rows<3>(rsA, sA0, 48 * wave, vo, sA + koffA(0), row16);
+    dma_rows<2>(rsB, sB0, 32 * wave, voB, sB + koffB(0), row16B);
+    dma_rows<3>(rsA, sA1, 48 * wave, vo, sA + koffA(1), row16);
+    dma_rows<2>(rsB, sB1, 32 * wave, voB, sB + koffB(1), row16B);
     __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0): this wave's stage-0 loads are in LDS
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -685,8 +704,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     // done, barrier
 #define AWQ_STAGE3(S, SN)                                                       \
   {                                                                             \
-    dma_rows<3>(rsA, sA##SN, 48 * wave, vo, sA + koff(kt + 2), row16);          \
-    dma_rows<2>(rsB, sB##SN, 32 * wave, vo, sB + koff(kt + 2), row16);          \
+    dma_rows<3>(rsA, sA##SN, 48 * wave, vo, sA + koffA(kt + 2), row16);         \
+    dma_rows<2>(rsB, sB##SN, 32 * wave, voB, sB + koffB(kt + 2), row16B);       \
     mfma_stage(sA##S, sB##S, wm, wn, lane, acc);                                \
     __builtin_amdgcn_s_waitcnt(0x0075);                                         \
     asm volatile("" ::: "memory");                                              \
@@ -695,13 +714,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     ++kt;                                                                       \
   }
     int kt = 0;
-    for (; kt + 3 <= nk;) {
+    for (; kt + 3 <= nks;) {
       AWQ_STAGE3(0, 2)
       AWQ_STAGE3(1, 0)
       AWQ_STAGE3(2, 1)
     }
-    if (kt < nk) AWQ_STAGE3(0, 2)
-    if (kt < nk) AWQ_STAGE3(1, 0)
+    if (kt < nks) AWQ_STAGE3(0, 2)
+    if (kt < nks) AWQ_STAGE3(1, 0)
 #undef AWQ_STAGE3
     __builtin_amdgcn_s_waitcnt(0x0070);  // no load in flight past this point
 
@@ -888,9 +907,11 @@ __global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict_
   r[i] = ci > 0.0f ? 1.0f / ci : 0.0f;
 }
 
-// H16 [h_rows, K_pad] = H'' of the triangular form: fp16(H_ij r_i r_j) in the
-// diagonal 384-block of row i, twice that right of it (exact), zeros left of
-// it (never read; H32 is not formed there) and in rows from K_pad on
+// H16 [h_rows, 2 K_pad] = H'' of the triangular form in two fp16 parts: with
+// x = H_ij r_i r_j in the diagonal 384-block of row i and twice that right of
+// it (exact), hi = fp16(x) in column j and lo = fp16(x - hi) in column K_pad + j
+// (x - hi is exact in fp32); zeros left of the diagonal block (never read; H32
+// is not formed there) and in rows from K_pad on
 __global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict__ H32, int64_t K_pad, int ns,
                                                        int64_t h_rows, const float* __restrict__ r,
                                                        uint16_t* __restrict__ H16) {
@@ -898,7 +919,7 @@ __global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict_
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
     const int64_t i = idx / chunks, j = (idx % chunks) * 8;
     const int64_t dblk = i / kBM * kBM;  // first column of row i's diagonal block
-    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    uint32_t o[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
     if (i < K_pad && j >= dblk) {
       const float ri = j >= dblk + kBM ? 2.0f * r[i] : r[i];
       float4 h0 = *(const float4*)(H32 + i * K_pad + j), h1 = *(const float4*)(H32 + i * K_pad + j + 4);
@@ -912,9 +933,14 @@ __global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict_
       const float v[8] = {h0.x * ri * r0.x, h0.y * ri * r0.y, h0.z * ri * r0.z, h0.w * ri * r0.w,
                           h1.x * ri * r1.x, h1.y * ri * r1.y, h1.z * ri * r1.z, h1.w * ri * r1.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = (uint32_t)f2h_bits(v[2 * q]) | ((uint32_t)f2h_bits(v[2 * q + 1]) << 16);
+      for (int q = 0; q < 4; ++q) {
+        const uint16_t a = f2h_bits(v[2 * q]), b = f2h_bits(v[2 * q + 1]);
+        o[q] = (uint32_t)a | ((uint32_t)b << 16);
+        lo[q] = (uint32_t)f2h_bits(v[2 * q] - h2f(a)) | ((uint32_t)f2h_bits(v[2 * q + 1] - h2f(b)) << 16);
+      }
     }
-    *(uint4*)(H16 + i * K_pad + j) = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)(H16 + i * 2 * K_pad + j) = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)(H16 + i * 2 * K_pad + K_pad + j) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
 }
 
@@ -933,16 +959,23 @@ hipError_t launch_gram_scale(const float* H32, int64_t T_pad, int64_t K_pad, int
 
 // colpart[u * ldc + n] = row unit u's share (tiles u and n_tiles - 1 - u) of
 // dW'_n H' dW'_n^T over the n_cols stacked dW' rows, u < gram_units(h_rows)
-// (K from each tile's diagonal block on: about half the products of the full form)
+// (K from each tile's diagonal block on: about half the products of the full
+// form); split: H'' as hi + lo (twice the products, per-row accuracy)
 int64_t gram_units(int64_t h_rows) { return (h_rows / kBM + 1) / 2; }
 
 hipError_t launch_gemm_gram(const uint16_t* H16, int64_t h_rows, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
-                            float* colpart, int64_t ldc, hipStream_t stream) {
+                            float* colpart, int64_t ldc, bool split, hipStream_t stream) {
   const int64_t n_tiles = h_rows / kBM, n_units = gram_units(h_rows), n_nt = n_cols / kBN;
-  const uint32_t a_bytes = (uint32_t)(h_rows * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
-  gemm_sq_kernel<kEpiGram><<<(unsigned)(n_units * n_nt), kGemmThreads, 0, stream>>>(
-      H16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad, n_units, n_nt, colpart, ldc, gemm_group_m(K_pad), K_pad,
-      n_tiles);
+  const uint32_t a_bytes = (uint32_t)(h_rows * 2 * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
+  const dim3 grid((unsigned)(n_units * n_nt));
+  if (split)
+    gemm_sq_kernel<kEpiGram2><<<grid, kGemmThreads, 0, stream>>>(H16, 2 * K_pad, a_bytes, dw, K_pad, b_bytes, K_pad,
+                                                                 n_units, n_nt, colpart, ldc, gemm_group_m(K_pad),
+                                                                 K_pad, n_tiles);
+  else
+    gemm_sq_kernel<kEpiGram><<<grid, kGemmThreads, 0, stream>>>(H16, 2 * K_pad, a_bytes, dw, K_pad, b_bytes, K_pad,
+                                                                n_units, n_nt, colpart, ldc, gemm_group_m(K_pad),
+                                                                K_pad, n_tiles);
   return hipGetLastError();
 }
 

@@ -214,6 +214,12 @@ def test_output_form_choice(A):
     assert A.search_output_form(256, 512, 64) == "direct"
     assert A.search_output_form(6144, 4096, 16384, out_form="direct") == "direct"
     assert A.search_output_form(256, 512, 64, out_form="gram") == "gram"
+    # the clip search (hi + lo parts of H in the second-moment form)
+    assert A.search_output_forms(24576, 4096, 16384, n_clip=20) == ("gram", "gram")
+    assert A.search_output_forms(6144, 4096, 16384) == ("gram", None)
+    assert A.search_output_forms(6144, 4096, 2048, n_clip=20) == ("direct", "direct")
+    assert A.search_output_forms(6144, 4096, 16384, n_clip=20, out_form="direct") == ("direct", "direct")
+    assert A.search_output_forms(256, 512, 64, n_clip=20, out_form="gram") == ("gram", "gram")
     L = A.lib()
     f = ctypes.c_int32()
     w = A._cfg(128, 20, "weight", 0, 0.5, 1e-4)

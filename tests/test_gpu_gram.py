@@ -113,14 +113,15 @@ def test_output_forms_agree_and_auto(A):
         assert argmin_ok(int(host(r.best_idx)[0]), errs, k)
 
 
-@pytest.mark.parametrize("out_form", ["auto", "direct"])
+@pytest.mark.parametrize("out_form", ["gram", "auto", "direct"])
 @pytest.mark.parametrize("rank,noise", [(16, 0.05), (64, 0.1)])
 def test_output_correlated_channels(A, out_form, rank, noise):
     """Correlated input channels (a rank-r mix plus noise, so H = X^T X is far
-    from diagonal): the library's default (the alpha search in the
-    second-moment form at this shape, the clip search in the direct form) and
-    the direct form throughout, against the oracle at the output-score bars,
-    per-row clip errors included."""
+    from diagonal): the second-moment form throughout (the clip search's H in
+    hi + lo parts), the library's default (at this shape the alpha search in
+    the second-moment form, the clip search direct) and the direct form
+    throughout, against the oracle at the output-score bars, per-row clip
+    errors included."""
     parts, d_in, T, G = [160, 96], 768, 1024, 128
     say(f"output score, correlated channels rank={rank} noise={noise} ({out_form} form)")
     if out_form == "auto":
