@@ -74,7 +74,7 @@ hipError_t launch_dw_bound(bool asym, const float* colmax, int64_t d_in, int n_c
 hipError_t launch_gemm_sq(const uint16_t* X16, int64_t T_pad, int64_t K_pad, const uint16_t* dw, int64_t n_cols,
                           float* colpart, int64_t ldc, hipStream_t stream);
 // second-moment form: Xt [xt_rows, T_pad] = fp16(X^T xs); H32 = Xt Xt^T [K_pad, K_pad];
-// c = sqrt(diag H), r = 1 / c; H16 [h_rows, 2 K_pad] = r_i H_ij r_j as fp16 hi | lo parts;
+// c = sqrt(diag H), r = 1 / c; H16 = r_i H_ij r_j as fp16 hi then lo matrices [h_rows, K_pad];
 // colpart[mt * ldc + n] = tile mt's share of dw_n H16 dw_n^T (dw built with cs = c)
 void gram_pad(int64_t T, int64_t K_pad, int64_t* T_pad, int64_t* xt_rows, int64_t* h_rows);
 hipError_t launch_transpose_x(const void* X, bool bf16, int64_t T, int64_t d_in, int64_t ld_x, int64_t T_pad,

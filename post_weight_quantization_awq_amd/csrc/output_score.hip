@@ -576,13 +576,12 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* B
 //   kEpiStore: out[m * ldc + n] = C[m, n] for m, n < lim (H = Xt Xt^T in
 //              fp32); tiles wholly left of their rows' diagonal block
 //              (n0 + 256 <= m0) are not needed and not launched.
-//   kEpiGram2: kEpiGram with H'' in two fp16 parts, hi + lo (row m of A holds
-//              hi in columns 0 .. K-1 and lo in K .. 2K-1): the stages
+//   kEpiGram2: kEpiGram with H'' in two fp16 parts, hi + lo (the lo matrix
+//              follows the hi one, kslice * 384 rows further): the stages
 //              alternate hi and lo over the same dW' chunk, so the product is
 //              exact to about 2^-22 of H'' instead of 2^-11 -- the accuracy
 //              of single rows' forms, which the per-row clip search needs.
-// The kEpiGram forms read A rows lda = 2 K apart (the same H'' buffer; kEpiGram
-// uses the hi part only).
+//              kEpiGram reads the hi matrix only.
 constexpr int kEpiSq = 0, kEpiGram = 1, kEpiStore = 2, kEpiGram2 = 3;
 
 // kEpiStore splits K over blockIdx.y: slice y takes K columns [y kslice,
@@ -683,7 +682,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
     };
     auto koffA = [&](int t) {
       const int tc = t < nks ? t : nks - 1;
-      return koffB(t) + ((EPI == kEpiGram2 && (tc & 1)) ? (uint32_t)(K * 2) : 0u);
+      return koffB(t) + ((EPI == kEpiGram2 && (tc & 1)) ? (uint32_t)(kslice * kBM * lda * 2) : 0u);
     };
 
     // prologue: stages 0 and 1 in flight; wait for stage 0 (5 loads per stage
@@ -907,11 +906,11 @@ __global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict_
   r[i] = ci > 0.0f ? 1.0f / ci : 0.0f;
 }
 
-// H16 [h_rows, 2 K_pad] = H'' of the triangular form in two fp16 parts: with
-// x = H_ij r_i r_j in the diagonal 384-block of row i and twice that right of
-// it (exact), hi = fp16(x) in column j and lo = fp16(x - hi) in column K_pad + j
-// (x - hi is exact in fp32); zeros left of the diagonal block (never read; H32
-// is not formed there) and in rows from K_pad on
+// H16 = H'' of the triangular form in two fp16 matrices [h_rows, K_pad], hi
+// then lo: with x = H_ij r_i r_j in the diagonal 384-block of row i and twice
+// that right of it (exact), hi = fp16(x) and lo = fp16(x - hi) (x - hi is
+// exact in fp32); zeros left of the diagonal block (never read; H32 is not
+// formed there) and in rows from K_pad on
 __global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict__ H32, int64_t K_pad, int ns,
                                                        int64_t h_rows, const float* __restrict__ r,
                                                        uint16_t* __restrict__ H16) {
@@ -939,8 +938,8 @@ __global__ __launch_bounds__(256) void gram_half_kernel(const float* __restrict_
         lo[q] = (uint32_t)f2h_bits(v[2 * q] - h2f(a)) | ((uint32_t)f2h_bits(v[2 * q + 1] - h2f(b)) << 16);
       }
     }
-    *(uint4*)(H16 + i * 2 * K_pad + j) = make_uint4(o[0], o[1], o[2], o[3]);
-    *(uint4*)(H16 + i * 2 * K_pad + K_pad + j) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *(uint4*)(H16 + i * K_pad + j) = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)(H16 + (h_rows + i) * K_pad + j) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
 }
 
@@ -969,11 +968,11 @@ hipError_t launch_gemm_gram(const uint16_t* H16, int64_t h_rows, int64_t K_pad, 
   const uint32_t a_bytes = (uint32_t)(h_rows * 2 * K_pad * 2), b_bytes = (uint32_t)(n_cols * K_pad * 2);
   const dim3 grid((unsigned)(n_units * n_nt));
   if (split)
-    gemm_sq_kernel<kEpiGram2><<<grid, kGemmThreads, 0, stream>>>(H16, 2 * K_pad, a_bytes, dw, K_pad, b_bytes, K_pad,
+    gemm_sq_kernel<kEpiGram2><<<grid, kGemmThreads, 0, stream>>>(H16, K_pad, a_bytes, dw, K_pad, b_bytes, K_pad,
                                                                  n_units, n_nt, colpart, ldc, gemm_group_m(K_pad),
                                                                  K_pad, n_tiles);
   else
-    gemm_sq_kernel<kEpiGram><<<grid, kGemmThreads, 0, stream>>>(H16, 2 * K_pad, a_bytes, dw, K_pad, b_bytes, K_pad,
+    gemm_sq_kernel<kEpiGram><<<grid, kGemmThreads, 0, stream>>>(H16, K_pad, a_bytes / 2, dw, K_pad, b_bytes, K_pad,
                                                                 n_units, n_nt, colpart, ldc, gemm_group_m(K_pad),
                                                                 K_pad, n_tiles);
   return hipGetLastError();
