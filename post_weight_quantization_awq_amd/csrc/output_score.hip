@@ -634,7 +634,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_sq_kernel(const uint16_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 96 x 128
   // per-lane byte offset and 16-row stride of the DMA loads, for A and for B
-  // (the second-moment product's A rows are 2 K apart, its B rows K apart)
+  // (each with its own row stride)
   const uint32_t ld2 = (uint32_t)(lda * 2), ldb2 = (uint32_t)(ldb * 2);
   const uint32_t swz_off = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
   const uint32_t vo = (uint32_t)(lane >> 2) * ld2 + swz_off, voB = (uint32_t)(lane >> 2) * ldb2 + swz_off;
