@@ -85,13 +85,13 @@ PMC_TRAFFIC = {
     # second-moment product (gemm_sq_kernel<1>, the default here) and the direct
     # GEMM (gemm_sq_kernel<0>, --out-form direct); profiles/gemm_gram_qkv_mlp_output.md
     ("gemm_sq_kernel<1>", "qkv_6144x4096_output"): {
-        "fetch_kib": 2164584.7, "write_kib": 2880.0,
+        "fetch_kib": 1958292.6, "write_kib": 2880.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "dde298d872065ed8d6b032b78dcb59cfdaef3abbc65f1f3717bf996a2b7c3736"},
+        "sha256": "533cb816d98cc45e5f4eda807c2acf4ed616753e493111d3ed9eaa027d8f3369"},
     ("gemm_sq_kernel<0>", "qkv_6144x4096_output"): {
-        "fetch_kib": 11450074.8, "write_kib": 20640.0,
+        "fetch_kib": 11891109.2, "write_kib": 20640.0,
         "sources": ("csrc/output_score.hip", "csrc/awq_device.h"),
-        "sha256": "dde298d872065ed8d6b032b78dcb59cfdaef3abbc65f1f3717bf996a2b7c3736"},
+        "sha256": "533cb816d98cc45e5f4eda807c2acf4ed616753e493111d3ed9eaa027d8f3369"},
 }
 
 

@@ -125,15 +125,16 @@ bool use_gram(const awq_search_cfg& cfg, const SearchPlan& p, int64_t T) {
 }
 
 // The clip search in the second-moment form takes H'' as hi + lo (twice the
-// products of the alpha search's form): taken when that is below 0.6 of the
-// direct form's work (its product runs at a lower fraction of the matrix-core
-// peak than the direct GEMM), H counted only if the alpha search did not form it.
+// products of the alpha search's form): taken when that is below 0.85 of the
+// direct form's work (the split product, with twice the K per block, runs at
+// the direct GEMM's fraction of the matrix-core peak: 0.47 of it on MLP
+// gate/up and down), H counted only if the alpha search did not form it.
 bool use_gram_clip(const awq_search_cfg& cfg, const SearchPlan& p) {
   if (cfg.n_clip < 2 || (cfg.flags & AWQ_FLAG_OUT_DIRECT)) return false;
   if (cfg.flags & AWQ_FLAG_OUT_GRAM) return true;
   if (!gram_fits(p)) return false;
   const double rows = (double)cfg.n_clip * (double)p.d_out_pad;
-  return gram_work(p, rows, 2, !p.gram) < 0.6 * (double)p.T_pad * (double)p.K_pad * rows;
+  return gram_work(p, rows, 2, !p.gram) < 0.85 * (double)p.T_pad * (double)p.K_pad * rows;
 }
 
 SearchPlan plan_search(const awq_search_cfg& cfg, int64_t d_out, int64_t d_in, int64_t T) {
