@@ -164,6 +164,13 @@ def test_search_validation(A):
     assert st_search(A, out, grp, X=FAKE, T=16, ld=256, xdt=2) == A.AWQ_EDTYPE
     clipc = A._cfg(128, 20, "output", 20, 0.5, 1e-4)
     assert st_search(A, clipc, grp, X=FAKE, T=16, ld=256, clip=None) == A.AWQ_EINVAL
+    # the second-moment form addresses H with 32-bit offsets: forced at
+    # d_in^2 >= 2^31 it is refused before anything is enqueued, and the
+    # library's own choice falls back to the direct form there
+    assert A.search_output_form(96, 49152, 1 << 20) == "direct"
+    gram = A._cfg(128, 20, "output", 0, 0.5, 1e-4, out_form="gram")
+    assert st_search(A, gram, grp, d_in=49152, X=FAKE, T=16, ld=49152) == A.AWQ_ESHAPE
+    assert "second-moment" in A.lib().awq_last_error().decode()
     assert A.lib().awq_last_error().decode() != ""
 
 

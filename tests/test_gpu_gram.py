@@ -38,6 +38,7 @@ def A():
     ([272], 96, 385, 32, "bf16"),          # d_in padded 96 -> 128, 385 tokens
     ([520], 1024, 1000, 128, "bf16"),      # three H row tiles, the last ragged
     ([300, 212], 2048, 700, 64, "f16"),    # six H row tiles
+    ([200], 256, 3000, 128, "bf16"),       # H over two token slices, the last one shorter
 ])
 def test_search_output_gram(A, parts, d_in, T, G, xdt):
     say(f"search output (second-moment form) parts={parts} d_in={d_in} T={T} G={G} {xdt}")
